@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X log-mel front end (one GPU).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+A step is one whole pass of the transform over one batch: for the default
+workload, lm_from_pcm on 64 clips x 480000 int16 samples (30 s at 16 kHz),
+n_fft 400, hop 160, 128 Slaney mels, float32 out -- the main kernel plus the
+per-clip clamp fix-up.  Inputs are generated on the host, copied to HBM once
+and stay resident; several input/output buffer sets are cycled so that every
+step reads its input from HBM rather than from the 256 MB last-level cache.
+
+Prints ONE JSON line: frames/s for the batch, the main kernel's achieved HBM
+bandwidth against MI355X's 8 TB/s (event-timed on the stream it runs on),
+and the fp64 oracle timed on this host's cores on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+FP32_VALU_PEAK_TFLOPS = 157.3     # published fp32 vector peak
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash(entry: str) -> str:
+    files = ["lm_device.h", "lm_pcm.hip" if entry == "pcm" else "lm_stft.hip"]
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "stft_log_mel_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload: str, entry: str):
+    """HBM bytes per launch of the main kernel from committed rocprofv3 counter
+    runs, if they were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash(entry):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def flops_per_frame(w) -> float:
+    """Nominal arithmetic per frame (real FFT 2.5 N log2 N, window, power,
+    packed mel FMAs): used for the FFT-rate context figure only."""
+    import math
+    if w.entry == "stft":
+        return 3.0 * w.NF + 2.0 * 2 * w.NF
+    N = w.n_fft
+    return 2.5 * N * math.log2(N) + N + 3.0 * (N // 2 + 1) + 2.0 * 2 * (N // 2 + 1)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="pcm_i16_b64")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (clips shard across "
+              "GPUs with no communication; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import lm_synth
+    import stft_log_mel_amd as lm
+
+    w = lm_synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
+    t0 = time.time()
+    if w.entry == "stft":
+        host_in, host_filters = lm_synth.make_inputs(w)
+    else:
+        host_in = lm_synth.make_inputs(w)
+    print(f"[bench] inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    per_step_bytes = w.essential_bytes()
+    nbuf = max(1, min(8, -(-1_000_000_000 // per_step_bytes) + 1))   # cycle >= ~1 GB of buffers
+    ins = [torch.from_numpy(host_in).to(dev) for _ in range(nbuf)]
+    out_dt = torch.float16 if w.out_dtype == "f16" else torch.float32
+    outs = [torch.empty(w.out_shape, dtype=out_dt, device=dev) for _ in range(nbuf)]
+    if w.entry == "stft":
+        filt = torch.from_numpy(host_filters).to(dev)
+        plan = lm.Plan(400, 160, w.NM)
+
+        def step(i):
+            plan.from_stft(ins[i % nbuf], filt, out=outs[i % nbuf])
+    else:
+        plan = lm.Plan(w.n_fft, w.hop, w.n_mels, w.center, w.pad_mode, w.power, w.out_dtype)
+        plan.set_mel(w.sample_rate, w.f_min, w.f_max)
+
+        def step(i):
+            plan.from_pcm(ins[i % nbuf], out=outs[i % nbuf])
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps, {nbuf} buffer sets)", file=sys.stderr, flush=True)
+
+    plan.profile(True)
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    plan.profile(False)
+    ms_total = ev0.elapsed_time(ev1)
+    prof = plan.profile_read()
+    ms_per_step = ms_total / args.steps
+    frames = w.B * w.n_frames
+    value = frames / (ms_per_step / 1e3)
+    main_ms = prof["main"]["ms"] / max(1, prof["main"]["count"])
+    fix_ms = prof["fixup"]["ms"] / max(1, prof["fixup"]["count"])
+    achieved = per_step_bytes / (main_ms / 1e3) / 1e9
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step (wall {wall:.3f}s), "
+          f"main kernel {main_ms:.4f} ms, fixup {fix_ms:.4f} ms", file=sys.stderr, flush=True)
+
+    # parity spot check of the timed output against the first clip's oracle
+    parity = None
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+        if w.entry == "stft":
+            W = host_filters
+            run_clip = lambda b: oracle.from_stft(host_in[b:b + 1], W)     # noqa: E731
+        else:
+            W = oracle.mel_filterbank(w.sample_rate, w.n_fft, w.n_mels, w.f_min, w.f_max)
+            run_clip = lambda b: oracle.from_pcm(host_in[b:b + 1], w.n_fft, w.hop, W,    # noqa: E731
+                                                 center=w.center, pad_mode=w.pad_mode, power=w.power)
+        got = outs[(args.steps - 1) % nbuf].float().cpu().numpy()
+        t_cpu = time.perf_counter()
+        done = 0
+        errs = []
+        while done < w.B:
+            ref = run_clip(done)
+            errs.append(float(np.abs(got[done] - ref[0]).max()))
+            done += 1
+            if time.perf_counter() - t_cpu >= args.cpu_seconds:
+                break
+        dt = time.perf_counter() - t_cpu
+        cpu = {"value": round(done * w.n_frames / dt, 1), "unit": "frames/s", "cores": int(threads),
+               "kind": "oracle",
+               "sample": f"{done} of {w.B} clips ({done * w.n_frames} frames) of the same workload, "
+                         f"fp64 numpy oracle, {dt:.1f}s"}
+        parity = {"clips_checked": done, "max_abs_err": max(errs),
+                  "tol": 2e-3 if w.out_dtype == "f16" else 1e-4}
+        print(f"[bench] oracle: {done} clips in {dt:.1f}s, max |err| {max(errs):.2e}", file=sys.stderr,
+              flush=True)
+
+    fpf = flops_per_frame(w)
+    line = {
+        "metric": "log-mel frames/sec (B=64x30 s, n_fft=400, 128 mels) + HBM GB/s % of peak",
+        "value": round(value, 1),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded speech-like int16 PCM)" if w.entry == "pcm" else "synthetic (seeded STFT)",
+        "config": {
+            "workload": w.name, "entry": f"lm_from_{w.entry}", "B": w.B,
+            **({"T": w.T, "sample_rate": w.sample_rate, "n_fft": w.n_fft, "hop": w.hop, "n_mels": w.n_mels,
+                "center": w.center, "pad_mode": w.pad_mode, "power": w.power, "in": w.in_dtype,
+                "mel": "slaney/slaney-norm", "f_min": w.f_min, "f_max": w.f_max}
+               if w.entry == "pcm" else {"F": w.F, "NF": w.NF, "NM": w.NM, "in": "complex64",
+                                         "filters": "linear triangles (fp32)"}),
+            "out": w.out_dtype, "frames_per_step": frames, "essential_bytes_per_step": per_step_bytes,
+            "buffer_sets": nbuf,
+        },
+        "hbm_gbs_step": round(per_step_bytes / (ms_per_step / 1e3) / 1e9, 1),
+        "hbm_frac_step": round(per_step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": counter_traffic(w.name, w.entry),
+            "kernel": "pcm_logmel_kernel" if w.entry == "pcm" else "stft_logmel_kernel",
+            "kernel_ms": round(main_ms, 5),
+            "algorithmic_bytes_per_launch": per_step_bytes,
+        },
+        "alu_context": {
+            "nominal_flop_per_frame": round(fpf, 1),
+            "tflops": round(frames * fpf / (main_ms / 1e3) / 1e12, 2),
+            "fp32_vector_peak_tflops": FP32_VALU_PEAK_TFLOPS,
+        },
+        "fixup_ms": round(fix_ms, 5),
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,197 @@
+/*
+ * lm.h -- C ABI of the MI355X log-mel front end.
+ *
+ * The library turns raw PCM (float32 or int16) or a given complex64 STFT
+ * into the normalised log-mel spectrogram used by speech encoders:
+ *
+ *   frames (center padding by index arithmetic) -> periodic Hann window
+ *   -> one-sided real FFT -> |X|^power -> triangular mel projection
+ *   -> log10(max(mel, 1e-10)) -> max(., clip max - 8) -> (. + 4) / 4
+ *
+ * Definitions follow two pages:
+ *  - KBench task page "audio-mel-spectrogram-fused": the STFT -> log-mel
+ *    chain (section "spec_md"), its tensor contract ("contract_md") and its
+ *    float32-everywhere precision rule ("precision_md").
+ *  - flashmel project page (PyPI): the PCM front half and its arguments
+ *    (sections "Usage" and "How it works").
+ *
+ * Conventions for every entry point
+ *  - Return value: LM_OK (0) or a negative lm_status code.  No call aborts
+ *    the process.  lm_last_error() gives a thread-local message for the
+ *    most recent failure on the calling thread.
+ *  - Device pointers are plain HIP device addresses on the device that is
+ *    current when the call is made (normally torch tensors' data_ptr()).
+ *    The caller owns them.  Inputs are only read; outputs must not alias
+ *    inputs.  Arrays are dense and row-major (C order).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    The lm_from_* calls only enqueue work on it; they never synchronise
+ *    with the host, except the first call on a plan (or the first after
+ *    its filters change), which uploads the plan's tables with a blocking
+ *    copy.
+ *  - A plan binds to the device current at its first lm_from_* call and
+ *    must only be used on that device, by one stream at a time (its
+ *    workspace is shared between calls).  Do not change or destroy a plan
+ *    while work that uses it is in flight.
+ */
+#ifndef LM_H
+#define LM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct lm_plan lm_plan;   /* opaque, owned by the library */
+
+/* Status codes. */
+enum {
+  LM_OK = 0,
+  LM_ERR_INVALID_ARG = -1,  /* a value outside what the call accepts     */
+  LM_ERR_UNSUPPORTED = -2,  /* valid in principle, not built (e.g. size) */
+  LM_ERR_NO_FILTERS = -3,   /* the plan has no filterbank yet            */
+  LM_ERR_HIP = -4,          /* a HIP runtime call or launch failed       */
+  LM_ERR_OOM = -5           /* device or host allocation failed          */
+};
+
+/* Padding modes for center=1 (flashmel page, "How it works": all four
+ * modes are index arithmetic on the unpadded signal).
+ *  CONSTANT  zeros outside the signal
+ *  REFLECT   mirror about the edge sample, edge not repeated
+ *  REPLICATE repeat the edge sample
+ *  CIRCULAR  wrap around                                             */
+enum { LM_PAD_CONSTANT = 0, LM_PAD_REFLECT = 1, LM_PAD_REPLICATE = 2, LM_PAD_CIRCULAR = 3 };
+
+/* Element types.  LM_I16 is raw PCM scaled by 1/32768 (flashmel page,
+ * "Usage").  Outputs are LM_F32 or LM_F16 (cast at the final store).  */
+enum { LM_F32 = 0, LM_F16 = 1, LM_I16 = 2 };
+
+/* Mel scale and filter normalisation for lm_plan_set_mel. */
+enum { LM_MEL_SLANEY = 0, LM_MEL_HTK = 1 };
+enum { LM_NORM_SLANEY = 0, LM_NORM_NONE = 1 };
+
+/*
+ * lm_plan_create -- validate the transform's shape and build a plan.
+ *
+ *  n_fft     FFT size: 400, or a power of two in [64, 16384] (flashmel
+ *            page, "Usage", constraints).
+ *  hop       frame step in samples, >= 1.
+ *  n_mels    number of mel bands, 1..256.
+ *  center    1: pad n_fft/2 samples on both sides with `pad_mode`;
+ *            0: no padding (frames start at sample 0).
+ *  pad_mode  one of LM_PAD_*.
+ *  power     exponent p of |X|^p, finite and > 0 (2 = power spectrum).
+ *  out_dtype LM_F32 or LM_F16.
+ *
+ * Host-only: makes no HIP call.  *plan receives a new plan on LM_OK and is
+ * left untouched otherwise.  The plan has no filterbank until
+ * lm_plan_set_mel or lm_plan_set_filters succeeds.
+ */
+int lm_plan_create(lm_plan **plan, int n_fft, int hop, int n_mels, int center, int pad_mode,
+                   float power, int out_dtype);
+
+/*
+ * lm_plan_set_mel -- build the plan's triangular mel filterbank.
+ *
+ * n_mels + 2 corner frequencies evenly spaced in mel between f_min and
+ * f_max (Slaney: linear below 1 kHz, logarithmic above; HTK:
+ * 2595 log10(1 + f/700)); bin k sits at k * sample_rate / n_fft; row m is
+ * the triangle on corners m, m+1, m+2; LM_NORM_SLANEY scales each row to
+ * unit area (2 / (f[m+2] - f[m])).  Computed in float64 on the host and
+ * rounded once to float32.  Requires 0 <= f_min < f_max <= sample_rate/2.
+ * Host-only; the device copy is refreshed at the next lm_from_* call.
+ */
+int lm_plan_set_mel(lm_plan *plan, double sample_rate, double f_min, double f_max, int mel_scale,
+                    int norm);
+
+/*
+ * lm_plan_set_filters -- use a caller-supplied dense filterbank.
+ *
+ * host_dense: host array (n_mels, n_bins) float32, row-major, with
+ * n_mels == the plan's n_mels and n_bins == n_fft/2 + 1.  Copied; each row
+ * is packed to its [first, last] non-zero range (interior zeros kept, so
+ * the sparse sum is exact for any input).  Host-only.
+ */
+int lm_plan_set_filters(lm_plan *plan, const float *host_dense, int n_mels, int n_bins);
+
+/*
+ * lm_plan_get_filters -- copy the plan's filterbank (as used, float32) into
+ * host_dense (n_mels, n_bins), zero outside each row's packed range.
+ */
+int lm_plan_get_filters(const lm_plan *plan, float *host_dense, int n_mels, int n_bins);
+
+/*
+ * lm_plan_num_frames -- frames produced for a clip of n_samples:
+ * 1 + floor((n_samples + 2*pad - n_fft) / hop), pad = n_fft/2 if center
+ * else 0.  Returns a negative lm_status if no frame fits.
+ */
+int64_t lm_plan_num_frames(const lm_plan *plan, int64_t n_samples);
+
+/*
+ * lm_from_pcm -- PCM clips -> log-mel (flashmel page, "Usage": input
+ * (..., time) -> output (..., n_mels, n_frames); then the log / per-clip
+ * clamp / rescale tail of the KBench page's "spec_md").
+ *
+ *  pcm       device array (n_clips, n_samples) of LM_F32 or LM_I16, 4- or
+ *            2-byte aligned.
+ *  in_dtype  LM_F32 or LM_I16.
+ *  out       device array (n_clips, n_mels, F) of the plan's out_dtype,
+ *            F = lm_plan_num_frames(plan, n_samples).  Mel-major: each
+ *            band's F frames are contiguous.
+ *  Each clip is floored at its own maximum: out = (max(L, hi_b - 8) + 4)/4
+ *  with L = log10(max(mel, 1e-10)) and hi_b the clip's largest L.
+ *
+ * Needs n_samples > n_fft/2 for reflect, >= n_fft/2 for circular and
+ * >= n_fft for center=0.  n_clips == 0 is a no-op.  Returns
+ * LM_ERR_NO_FILTERS before any filterbank is set.
+ */
+int lm_from_pcm(lm_plan *plan, const void *pcm, int in_dtype, int64_t n_clips, int64_t n_samples,
+                void *out, void *stream);
+
+/*
+ * lm_from_stft -- complex STFT -> log-mel (KBench page, "reference_src",
+ * "spec_md" and "contract_md").
+ *
+ *  stft        device array (n_clips, n_frames, n_bins) complex64, real and
+ *              imaginary parts interleaved, 8-byte aligned.
+ *  mel_filters device array (n_mels, n_bins) float32, row-major; or NULL
+ *              to use the plan's own filterbank (then n_bins must be
+ *              n_fft/2 + 1 and n_mels the plan's n_mels).  A device
+ *              filterbank is packed on the device on every call (rows to
+ *              their [first, last] non-zero range; exact for any input).
+ *  out         device array (n_clips, n_frames, n_mels) of the plan's
+ *              out_dtype.  Frame-major, as the contract fixes.
+ *  power = re^2 + im^2 always (the plan's `power`, framing and padding do
+ *  not apply to this path).  1 <= n_bins <= 8193, 1 <= n_mels <= 256.
+ *  n_clips == 0 or n_frames == 0 is a no-op.
+ */
+int lm_from_stft(lm_plan *plan, const void *stft, const float *mel_filters, int64_t n_clips,
+                 int64_t n_frames, int64_t n_bins, int n_mels, void *out, void *stream);
+
+/*
+ * lm_plan_profile -- per-kernel timing for measurement.
+ *
+ * enable != 0 makes later lm_from_* calls bracket each kernel they launch
+ * with HIP events on the same stream; enable == 0 stops it.
+ * lm_plan_profile_read waits for the recorded events, writes the summed
+ * milliseconds and launch counts of the main kernel (index 0: the
+ * PCM or STFT kernel), the clamp fix-up kernel (1) and the filter-packing
+ * kernel (2) into ms[3] / counts[3], and clears the record.
+ */
+int lm_plan_profile(lm_plan *plan, int enable);
+int lm_plan_profile_read(lm_plan *plan, double *ms, int64_t *counts);
+
+/* lm_plan_destroy -- free the plan and its device memory (NULL is a no-op). */
+void lm_plan_destroy(lm_plan *plan);
+
+/* Static text for a status code. */
+const char *lm_status_string(int status);
+
+/* Thread-local text describing the last failure on this thread ("" if none). */
+const char *lm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LM_H */

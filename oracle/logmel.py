@@ -124,16 +124,19 @@ def hann_periodic(N: int) -> np.ndarray:
     return 0.5 - 0.5 * np.cos(2.0 * np.pi * n / N)
 
 
-def rdft_direct(y: np.ndarray, chunk: int = 1024) -> np.ndarray:
+def rdft_direct(y: np.ndarray, chunk: int | None = None) -> np.ndarray:
     """One-sided DFT by its definition: X[k] = sum_n y[n] exp(-2 pi i k n / N).
 
     k = 0..N/2.  The angle uses the exact integer residue (k n) mod N before
     scaling, so no large-argument cos/sin is taken.  Evaluated as float64
     matrix products over chunks of bins (a library matmul is one step; the
-    sum itself is the plain O(N^2) definition).
+    sum itself is the plain O(N^2) definition).  The default chunk keeps each
+    temporary near 16 MB.
     """
     y = np.asarray(y, dtype=np.float64)
     N = y.shape[-1]
+    if chunk is None:
+        chunk = max(1, (1 << 21) // N)
     K = N // 2 + 1
     lead = y.shape[:-1]
     y2 = y.reshape(-1, N)

@@ -1,0 +1,299 @@
+// C-ABI entry points: per-call validation, device tables and workspace,
+// and the launch sequence (main kernel, then the per-clip clamp fix-up) on
+// the caller's stream.
+#include <cstring>
+
+#include "lm_internal.h"
+
+namespace lm {
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int ensure_device(lm_plan *p) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (p->device < 0) p->device = dev;
+  else if (p->device != dev) return fail(LM_ERR_INVALID_ARG, "plan is bound to another device");
+  return LM_OK;
+}
+
+int upload_tables(lm_plan *p) {
+  if (!p->tables_dirty && p->dt.base) return LM_OK;
+  const int N = p->n_fft, M = N / 2, NM = p->n_mels;
+  const int nnz = (int)p->csr.w.size();
+  size_t o_win = 0;
+  size_t o_tw = align256(o_win + sizeof(float) * N);
+  size_t o_ut = align256(o_tw + sizeof(float) * 2 * M);
+  size_t o_st = align256(o_ut + sizeof(float) * 2 * (M / 2 + 1));
+  size_t o_wd = align256(o_st + sizeof(int32_t) * NM);
+  size_t o_of = align256(o_wd + sizeof(int32_t) * NM);
+  size_t o_w = align256(o_of + sizeof(int32_t) * NM);
+  size_t total = align256(o_w + sizeof(float) * (nnz > 0 ? nnz : 1));
+  std::vector<unsigned char> host(total, 0);
+  std::memcpy(host.data() + o_win, p->window.data(), sizeof(float) * N);
+  std::memcpy(host.data() + o_tw, p->twiddle.data(), sizeof(float) * 2 * M);
+  std::memcpy(host.data() + o_ut, p->untangle.data(), sizeof(float) * 2 * (M / 2 + 1));
+  if (p->have_filters) {
+    std::memcpy(host.data() + o_st, p->csr.start.data(), sizeof(int32_t) * NM);
+    std::memcpy(host.data() + o_wd, p->csr.width.data(), sizeof(int32_t) * NM);
+    std::memcpy(host.data() + o_of, p->csr.off.data(), sizeof(int32_t) * NM);
+    if (nnz) std::memcpy(host.data() + o_w, p->csr.w.data(), sizeof(float) * nnz);
+  }
+  if (p->dt.base) {
+    hipError_t e = hipFree(p->dt.base);
+    p->dt.base = nullptr;
+    if (e != hipSuccess) return hip_fail(e, "hipFree(tables)");
+  }
+  void *d = nullptr;
+  hipError_t e = hipMalloc(&d, total);
+  if (e != hipSuccess) return hip_fail(e, "hipMalloc(tables)");
+  e = hipMemcpy(d, host.data(), total, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(d);
+    return hip_fail(e, "hipMemcpy(tables)");
+  }
+  unsigned char *c = static_cast<unsigned char *>(d);
+  p->dt.base = d;
+  p->dt.bytes = total;
+  p->dt.window = reinterpret_cast<const float *>(c + o_win);
+  p->dt.twiddle = reinterpret_cast<const float2 *>(c + o_tw);
+  p->dt.untangle = reinterpret_cast<const float2 *>(c + o_ut);
+  p->dt.csr_start = reinterpret_cast<const int32_t *>(c + o_st);
+  p->dt.csr_width = reinterpret_cast<const int32_t *>(c + o_wd);
+  p->dt.csr_off = reinterpret_cast<const int32_t *>(c + o_of);
+  p->dt.csr_w = reinterpret_cast<const float *>(c + o_w);
+  p->dt.nnz = nnz;
+  p->tables_dirty = false;
+  return LM_OK;
+}
+
+// hi_bits must be zero when a call starts; the fix-up kernel clears it at
+// the end of every call, and a fresh (or previously failed) buffer is
+// cleared here on the caller's stream.
+int ensure_workspace(lm_plan *p, int64_t n_clips, int64_t n_tiles, hipStream_t s) {
+  hipError_t e;
+  if ((size_t)n_clips > p->hi_cap) {
+    if (p->d_hi) {
+      e = hipFree(p->d_hi);
+      p->d_hi = nullptr;
+      p->hi_cap = 0;
+      if (e != hipSuccess) return hip_fail(e, "hipFree(workspace)");
+    }
+    e = hipMalloc(reinterpret_cast<void **>(&p->d_hi), sizeof(uint32_t) * n_clips);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
+    p->hi_cap = n_clips;
+    p->ws_dirty = true;
+  }
+  if (p->ws_dirty) {
+    e = hipMemsetAsync(p->d_hi, 0, sizeof(uint32_t) * p->hi_cap, s);
+    if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync(workspace)");
+    p->ws_dirty = false;
+  }
+  if ((size_t)n_tiles > p->tile_cap) {
+    if (p->d_tile_min) {
+      e = hipFree(p->d_tile_min);
+      p->d_tile_min = nullptr;
+      p->tile_cap = 0;
+      if (e != hipSuccess) return hip_fail(e, "hipFree(workspace)");
+    }
+    e = hipMalloc(reinterpret_cast<void **>(&p->d_tile_min), sizeof(float) * n_tiles);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
+    p->tile_cap = n_tiles;
+  }
+  return LM_OK;
+}
+
+static int prof_begin(lm_plan *p, hipStream_t s, hipEvent_t *beg) {
+  if (!p->profiling) return LM_OK;
+  hipError_t e = hipEventCreate(beg);
+  if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+  e = hipEventRecord(*beg, s);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  return LM_OK;
+}
+
+static int prof_end(lm_plan *p, hipStream_t s, hipEvent_t beg, int kind) {
+  if (!p->profiling) return LM_OK;
+  hipEvent_t end;
+  hipError_t e = hipEventCreate(&end);
+  if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+  e = hipEventRecord(end, s);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  p->prof.push_back(ProfileRec{beg, end, kind});
+  return LM_OK;
+}
+
+// Launch `fn` bracketed by profiling events when enabled.
+template <typename Fn>
+static int timed_launch(lm_plan *p, hipStream_t s, int kind, const char *what, Fn fn) {
+  hipEvent_t beg{};
+  int rc = prof_begin(p, s, &beg);
+  if (rc != LM_OK) return rc;
+  hipError_t e = fn();
+  if (e != hipSuccess) {
+    if (p->profiling) (void)hipEventDestroy(beg);
+    return hip_fail(e, what);
+  }
+  return prof_end(p, s, beg, kind);
+}
+
+}  // namespace lm
+
+using namespace lm;
+
+extern "C" {
+
+int lm_from_pcm(lm_plan *p, const void *pcm, int in_dtype, int64_t n_clips, int64_t n_samples, void *out,
+                void *stream) {
+  if (!p) return fail(LM_ERR_INVALID_ARG, "plan is NULL");
+  if (!p->have_filters) return fail(LM_ERR_NO_FILTERS, "call lm_plan_set_mel or lm_plan_set_filters first");
+  if (in_dtype != LM_F32 && in_dtype != LM_I16) return fail(LM_ERR_INVALID_ARG, "in_dtype must be LM_F32 or LM_I16");
+  if (n_clips < 0) return fail(LM_ERR_INVALID_ARG, "n_clips < 0");
+  if (n_samples < 1) return fail(LM_ERR_INVALID_ARG, "n_samples < 1");
+  const int64_t half = p->n_fft / 2;
+  if (!p->center && n_samples < p->n_fft) return fail(LM_ERR_INVALID_ARG, "center=0 needs n_samples >= n_fft");
+  if (p->center && p->pad_mode == LM_PAD_REFLECT && n_samples <= half)
+    return fail(LM_ERR_INVALID_ARG, "reflect padding needs n_samples > n_fft/2");
+  if (p->center && p->pad_mode == LM_PAD_CIRCULAR && n_samples < half)
+    return fail(LM_ERR_INVALID_ARG, "circular padding needs n_samples >= n_fft/2");
+  if (n_clips == 0) return LM_OK;
+  if (!pcm || !out) return fail(LM_ERR_INVALID_ARG, "pcm and out must be device pointers");
+  const size_t in_align = in_dtype == LM_I16 ? 2 : 4, out_align = p->out_dtype == LM_F16 ? 2 : 4;
+  if ((reinterpret_cast<uintptr_t>(pcm) % in_align) || (reinterpret_cast<uintptr_t>(out) % out_align))
+    return fail(LM_ERR_INVALID_ARG, "misaligned pcm or out pointer");
+  const int64_t F = lm_plan_num_frames(p, n_samples);
+  if (F < 1) return (int)F;
+  const int fpb = pcm_frames_per_tile(p->n_fft);
+  const int64_t tiles = (F + fpb - 1) / fpb;
+  if (tiles > INT32_MAX || n_clips * tiles > INT32_MAX) return fail(LM_ERR_UNSUPPORTED, "input too large");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int rc = ensure_device(p);
+  if (rc == LM_OK) rc = upload_tables(p);
+  if (rc == LM_OK) rc = ensure_workspace(p, n_clips, n_clips * tiles, s);
+  if (rc != LM_OK) return rc;
+
+  PcmArgs a{pcm, in_dtype == LM_I16, n_clips, n_samples, F, (int)tiles, out, p->d_hi, p->d_tile_min};
+  rc = timed_launch(p, s, 0, "launch(pcm kernel)", [&] { return launch_pcm(p, a, s); });
+  if (rc != LM_OK) {
+    p->ws_dirty = true;
+    return rc;
+  }
+  FixupArgs fx{out, p->out_dtype == LM_F16, p->d_hi, p->d_tile_min, n_clips, F, p->n_mels, fpb, (int)tiles, 1};
+  rc = timed_launch(p, s, 1, "launch(clamp fix-up)", [&] { return launch_fixup(fx, s); });
+  if (rc != LM_OK) p->ws_dirty = true;
+  return rc;
+}
+
+int lm_from_stft(lm_plan *p, const void *stft, const float *mel_filters, int64_t n_clips, int64_t n_frames,
+                 int64_t n_bins, int n_mels, void *out, void *stream) {
+  if (!p) return fail(LM_ERR_INVALID_ARG, "plan is NULL");
+  if (n_clips < 0 || n_frames < 0) return fail(LM_ERR_INVALID_ARG, "negative size");
+  if (n_bins < 1 || n_bins > 8193) return fail(LM_ERR_INVALID_ARG, "n_bins must be in [1, 8193]");
+  if (n_mels < 1 || n_mels > 256) return fail(LM_ERR_INVALID_ARG, "n_mels must be in [1, 256]");
+  if (!mel_filters) {
+    if (!p->have_filters) return fail(LM_ERR_NO_FILTERS, "no mel_filters given and the plan has none");
+    if (n_bins != p->n_bins || n_mels != p->n_mels)
+      return fail(LM_ERR_INVALID_ARG, "n_bins / n_mels do not match the plan's filterbank");
+  } else if (reinterpret_cast<uintptr_t>(mel_filters) % 4) {
+    return fail(LM_ERR_INVALID_ARG, "misaligned mel_filters pointer");
+  }
+  if (n_clips == 0 || n_frames == 0) return LM_OK;
+  if (!stft || !out) return fail(LM_ERR_INVALID_ARG, "stft and out must be device pointers");
+  const size_t out_align = p->out_dtype == LM_F16 ? 2 : 4;
+  if ((reinterpret_cast<uintptr_t>(stft) % 8) || (reinterpret_cast<uintptr_t>(out) % out_align))
+    return fail(LM_ERR_INVALID_ARG, "misaligned stft or out pointer");
+  const int tf = stft_frames_per_tile((int)n_bins, n_mels);
+  const int64_t tiles = (n_frames + tf - 1) / tf;
+  if (tiles > INT32_MAX || n_clips * tiles > INT32_MAX) return fail(LM_ERR_UNSUPPORTED, "input too large");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int rc = ensure_device(p);
+  if (rc == LM_OK && !mel_filters) rc = upload_tables(p);
+  if (rc == LM_OK) rc = ensure_workspace(p, n_clips, n_clips * tiles, s);
+  if (rc != LM_OK) return rc;
+
+  const int32_t *cs, *cw, *co;
+  const float *w;
+  if (mel_filters) {
+    const size_t need = sizeof(int32_t) * 3 * n_mels + sizeof(float) * (size_t)n_mels * n_bins;
+    if (need > p->pack_cap) {
+      if (p->d_pack) {
+        hipError_t e = hipFree(p->d_pack);
+        p->d_pack = nullptr;
+        p->pack_cap = 0;
+        if (e != hipSuccess) return hip_fail(e, "hipFree(pack)");
+      }
+      hipError_t e = hipMalloc(&p->d_pack, need);
+      if (e != hipSuccess) return hip_fail(e, "hipMalloc(pack)");
+      p->pack_cap = need;
+    }
+    rc = timed_launch(p, s, 2, "launch(filter pack)",
+                      [&] { return launch_pack(mel_filters, n_mels, (int)n_bins, p->d_pack, s); });
+    if (rc != LM_OK) return rc;
+    cs = reinterpret_cast<const int32_t *>(p->d_pack);
+    cw = cs + n_mels;
+    co = cw + n_mels;
+    w = reinterpret_cast<const float *>(co + n_mels);
+  } else {
+    cs = p->dt.csr_start;
+    cw = p->dt.csr_width;
+    co = p->dt.csr_off;
+    w = p->dt.csr_w;
+  }
+  StftArgs a{reinterpret_cast<const float2 *>(stft), n_clips, n_frames, (int)n_bins, n_mels, tf, (int)tiles,
+             cs, cw, co, w, n_mels * (int)n_bins, out, p->out_dtype == LM_F16, p->d_hi, p->d_tile_min};
+  rc = timed_launch(p, s, 0, "launch(stft kernel)", [&] { return launch_stft(a, s); });
+  if (rc != LM_OK) {
+    p->ws_dirty = true;
+    return rc;
+  }
+  FixupArgs fx{out, p->out_dtype == LM_F16, p->d_hi, p->d_tile_min, n_clips, n_frames, n_mels, tf,
+               (int)tiles, 0};
+  rc = timed_launch(p, s, 1, "launch(clamp fix-up)", [&] { return launch_fixup(fx, s); });
+  if (rc != LM_OK) p->ws_dirty = true;
+  return rc;
+}
+
+int lm_plan_profile(lm_plan *p, int enable) {
+  if (!p) return fail(LM_ERR_INVALID_ARG, "plan is NULL");
+  p->profiling = enable != 0;
+  return LM_OK;
+}
+
+int lm_plan_profile_read(lm_plan *p, double *ms, int64_t *counts) {
+  if (!p || !ms || !counts) return fail(LM_ERR_INVALID_ARG, "NULL argument");
+  for (int i = 0; i < 3; ++i) {
+    ms[i] = 0.0;
+    counts[i] = 0;
+  }
+  int rc = LM_OK;
+  for (auto &r : p->prof) {
+    float t = 0.0f;
+    hipError_t e = hipEventSynchronize(r.end);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, r.beg, r.end);
+    if (e != hipSuccess && rc == LM_OK) rc = hip_fail(e, "profile events");
+    if (r.kind >= 0 && r.kind < 3) {
+      ms[r.kind] += t;
+      counts[r.kind] += 1;
+    }
+    (void)hipEventDestroy(r.beg);
+    (void)hipEventDestroy(r.end);
+  }
+  p->prof.clear();
+  return rc;
+}
+
+void lm_plan_destroy(lm_plan *p) {
+  if (!p) return;
+  for (auto &r : p->prof) {
+    (void)hipEventDestroy(r.beg);
+    (void)hipEventDestroy(r.end);
+  }
+  if (p->dt.base) (void)hipFree(p->dt.base);
+  if (p->d_hi) (void)hipFree(p->d_hi);
+  if (p->d_tile_min) (void)hipFree(p->d_tile_min);
+  if (p->d_pack) (void)hipFree(p->d_pack);
+  delete p;
+}
+
+}  // extern "C"

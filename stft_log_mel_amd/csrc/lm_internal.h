@@ -1,0 +1,137 @@
+// Internal declarations shared by the host plan, the entry points and the
+// kernel launchers.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/lm.h"
+
+namespace lm {
+
+// Set the thread-local error text and return `status`.
+int fail(int status, const std::string &msg);
+int hip_fail(hipError_t err, const char *what);
+
+// Packed triangular filterbank: row m covers bins [start[m], start[m] +
+// width[m]) with weights w[off[m] + j].  Rows are contiguous in w.
+struct Csr {
+  std::vector<int32_t> start, width, off;
+  std::vector<float> w;
+  int n_rows = 0, n_bins = 0;
+  int max_width() const;
+};
+
+// Device copy of the tables one PCM launch reads.  One allocation:
+//   [window n_fft f32][fft twiddles M f32x2][untangle twiddles M/2+1 f32x2]
+//   [csr start n_mels i32][csr width n_mels i32][csr off n_mels i32][csr w nnz f32]
+struct DeviceTables {
+  void *base = nullptr;
+  size_t bytes = 0;
+  const float *window = nullptr;
+  const float2 *twiddle = nullptr;    // exp(-2 pi i j / M), j < M
+  const float2 *untangle = nullptr;   // exp(-2 pi i k / n_fft), k <= M/2
+  const int32_t *csr_start = nullptr, *csr_width = nullptr, *csr_off = nullptr;
+  const float *csr_w = nullptr;
+  int nnz = 0;
+};
+
+struct ProfileRec {
+  hipEvent_t beg, end;
+  int kind;
+};
+
+}  // namespace lm
+
+struct lm_plan {
+  int n_fft = 0, hop = 0, n_mels = 0, center = 0, pad_mode = 0, out_dtype = 0;
+  float power = 2.0f;
+  int n_bins = 0;  // n_fft / 2 + 1
+
+  bool have_filters = false;
+  lm::Csr csr;
+  std::vector<float> window;      // n_fft
+  std::vector<float> twiddle;     // 2 * M
+  std::vector<float> untangle;    // 2 * (M/2 + 1)
+
+  int device = -1;                // bound at first launch
+  bool tables_dirty = true;
+  lm::DeviceTables dt;
+
+  // workspace: per-clip max bits and per-tile minimum log value
+  uint32_t *d_hi = nullptr;
+  size_t hi_cap = 0;
+  float *d_tile_min = nullptr;
+  size_t tile_cap = 0;
+  // per-call packed copy of a device filterbank (STFT path)
+  void *d_pack = nullptr;
+  size_t pack_cap = 0;
+
+  bool ws_dirty = false;         // hi_bits must be cleared before the next call
+
+  bool profiling = false;
+  std::vector<lm::ProfileRec> prof;
+};
+
+namespace lm {
+
+// Workspace helpers (lm_api.cpp)
+int ensure_device(lm_plan *p);
+int ensure_workspace(lm_plan *p, int64_t n_clips, int64_t n_tiles_total, hipStream_t s);
+int upload_tables(lm_plan *p);
+
+// Host table builders (lm_plan.cpp)
+void build_window(lm_plan *p);
+void build_twiddles(lm_plan *p);
+Csr pack_dense(const float *dense, int n_rows, int n_bins);
+
+// Kernel launchers.  Each returns hipSuccess or the launch error.
+struct PcmArgs {
+  const void *pcm;
+  bool in_i16;
+  int64_t n_clips, n_samples, n_frames;
+  int tiles_per_clip;
+  void *out;
+  uint32_t *hi_bits;
+  float *tile_min;
+};
+// Frames per workgroup tile the PCM kernel uses for this n_fft.
+int pcm_frames_per_tile(int n_fft);
+hipError_t launch_pcm(const lm_plan *p, const PcmArgs &a, hipStream_t s);
+
+struct StftArgs {
+  const float2 *stft;
+  int64_t n_clips, n_frames;
+  int n_bins, n_mels;
+  int frames_per_tile, tiles_per_clip;
+  const int32_t *csr_start, *csr_width, *csr_off;
+  const float *csr_w;
+  int nnz_cap;          // upper bound of the packed weight count
+  void *out;
+  int out_f16;
+  uint32_t *hi_bits;
+  float *tile_min;
+};
+int stft_frames_per_tile(int n_bins, int n_mels);
+hipError_t launch_stft(const StftArgs &a, hipStream_t s);
+
+// Pack a device dense (n_mels, n_bins) filterbank into CSR arrays laid out
+// in `ws` as [start n_mels][width n_mels][off n_mels][w n_mels*n_bins].
+hipError_t launch_pack(const float *dense, int n_mels, int n_bins, void *ws, hipStream_t s);
+
+struct FixupArgs {
+  void *out;
+  int out_f16;
+  uint32_t *hi_bits;
+  const float *tile_min;
+  int64_t n_clips, n_frames;
+  int n_mels;
+  int frames_per_tile, tiles_per_clip;
+  int mel_major;  // 1: (B, NM, F); 0: (B, F, NM)
+};
+hipError_t launch_fixup(const FixupArgs &a, hipStream_t s);
+
+}  // namespace lm

@@ -1,0 +1,336 @@
+// PCM -> log-mel, one fused kernel per (n_fft, input type, output type).
+//
+// A workgroup owns a tile of FPB consecutive frames of one clip and runs
+// the whole chain on it in LDS (flashmel page, "How it works"):
+//   1. frame samples are read straight from the clip with the center
+//      padding done as index arithmetic (nothing padded is stored), paired
+//      as z[n] = w[2n] x[2n] + i w[2n+1] x[2n+1] (periodic Hann);
+//   2. an M = n_fft/2 point complex FFT of z, as Stockham autosort passes
+//      of radix 16/8/5/4/2 through one LDS buffer;
+//   3. the split into the n_fft-point real spectrum,
+//        2 X[k] = (Z[k] + Z*[M-k]) - i e^{-2 pi i k/n_fft} (Z[k] - Z*[M-k]),
+//      and |X|^p written back over the same buffer as a power tile with an
+//      odd row stride M+1;
+//   4. the packed triangular mel sum per (band, frame), log10 after the
+//      1e-10 floor (KBench task page, "spec_md"), the (L+4)/4 rescale and a
+//      mel-major store (flashmel page, "Usage": (..., n_mels, n_frames));
+//   5. the tile's largest mel value goes to the clip's maximum with one
+//      atomicMax on its float bits (positive floats order like unsigned
+//      integers), its smallest log value to a per-tile slot.  The clamp
+//      fix-up kernel finishes the per-clip floor.
+// int16 input is converted to float without its 1/32768 scale; the mel
+// values are scaled by 2^-30 instead (exact), together with the 1/4 of
+// the split above.
+#include "lm_device.h"
+#include "lm_internal.h"
+
+namespace lm {
+
+template <int... R>
+struct Radices {};
+
+template <int NFFT>
+struct PcmCfg;
+// FPB frames per tile, THREADS per workgroup, radix sequence of M = NFFT/2.
+template <> struct PcmCfg<400>   { static constexpr int FPB = 16,  THREADS = 256; using Rad = Radices<8, 5, 5>; };
+template <> struct PcmCfg<64>    { static constexpr int FPB = 128, THREADS = 256; using Rad = Radices<16, 2>; };
+template <> struct PcmCfg<128>   { static constexpr int FPB = 64,  THREADS = 256; using Rad = Radices<16, 4>; };
+template <> struct PcmCfg<256>   { static constexpr int FPB = 32,  THREADS = 256; using Rad = Radices<16, 8>; };
+template <> struct PcmCfg<512>   { static constexpr int FPB = 16,  THREADS = 256; using Rad = Radices<16, 16>; };
+template <> struct PcmCfg<1024>  { static constexpr int FPB = 8,   THREADS = 256; using Rad = Radices<8, 8, 8>; };
+template <> struct PcmCfg<2048>  { static constexpr int FPB = 4,   THREADS = 256; using Rad = Radices<16, 16, 4>; };
+template <> struct PcmCfg<4096>  { static constexpr int FPB = 2,   THREADS = 256; using Rad = Radices<16, 16, 8>; };
+template <> struct PcmCfg<8192>  { static constexpr int FPB = 1,   THREADS = 256; using Rad = Radices<16, 16, 16>; };
+template <> struct PcmCfg<16384> { static constexpr int FPB = 1,   THREADS = 512; using Rad = Radices<16, 16, 16, 2>; };
+
+__device__ __forceinline__ float to_f(float v) { return v; }
+__device__ __forceinline__ float to_f(int16_t v) { return (float)(int)v; }
+
+// Sample j of a clip of T samples, with center padding resolved by index.
+template <typename IN>
+__device__ __forceinline__ float padded_sample(const IN *__restrict__ x, int64_t j, int64_t T, int mode) {
+  if (j < 0 || j >= T) {
+    if (mode == LM_PAD_CONSTANT) return 0.0f;
+    if (mode == LM_PAD_REFLECT) j = j < 0 ? -j : 2 * (T - 1) - j;
+    else if (mode == LM_PAD_REPLICATE) j = j < 0 ? 0 : T - 1;
+    else j = ((j % T) + T) % T;
+  }
+  return to_f(x[j]);
+}
+
+// One Stockham radix-R pass over FPB frames of M points held in `buf`.
+// Butterfly j of a frame (j < M/R, k = j mod Ns) reads a[t] = in[j + t M/R],
+// multiplies a[t] by exp(-2 pi i t k / (Ns R)), transforms, and writes
+// b[s] to ((j / Ns) Ns R + k + s Ns).  After the last pass the frame holds
+// its DFT in natural order.
+template <int R, int M, int FPB, int THREADS, int Ns>
+__device__ __forceinline__ void fft_pass(float2 *buf, const float2 *__restrict__ tw) {
+  constexpr int NBF = M / R;                 // butterflies per frame
+  constexpr int NB = FPB * NBF;
+  constexpr int BPT = (NB + THREADS - 1) / THREADS;
+  constexpr int TW_STEP = M / (Ns * R);
+  float2 v[BPT][R];
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) {
+    const int q = threadIdx.x + i * THREADS;
+    if (NB % THREADS == 0 || q < NB) {
+      const int f = q / NBF, j = q - f * NBF;
+      const float2 *fb = buf + f * M;
+#pragma unroll
+      for (int t = 0; t < R; ++t) v[i][t] = fb[j + t * NBF];
+      if (Ns > 1) {
+        const int k = j % Ns;
+#pragma unroll
+        for (int t = 1; t < R; ++t) v[i][t] = cmul(v[i][t], tw[t * k * TW_STEP]);
+      }
+      dft<R>(v[i]);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) {
+    const int q = threadIdx.x + i * THREADS;
+    if (NB % THREADS == 0 || q < NB) {
+      const int f = q / NBF, j = q - f * NBF;
+      const int k = j % Ns;
+      float2 *fb = buf + f * M + (j / Ns) * Ns * R + k;
+#pragma unroll
+      for (int s = 0; s < R; ++s) fb[s * Ns] = v[i][s];
+    }
+  }
+  __syncthreads();
+}
+
+template <int M, int FPB, int THREADS, int Ns, int R, int... Rest>
+__device__ __forceinline__ void fft_passes(float2 *buf, const float2 *__restrict__ tw) {
+  fft_pass<R, M, FPB, THREADS, Ns>(buf, tw);
+  if constexpr (sizeof...(Rest) > 0) fft_passes<M, FPB, THREADS, Ns * R, Rest...>(buf, tw);
+}
+
+template <int M, int FPB, int THREADS, int... R>
+__device__ __forceinline__ void run_fft(float2 *buf, const float2 *__restrict__ tw, Radices<R...>) {
+  fft_passes<M, FPB, THREADS, 1, R...>(buf, tw);
+}
+
+struct PcmKernelArgs {
+  const void *pcm;
+  int64_t T, F;
+  int tiles_per_clip;
+  int hop, pad, pad_mode;
+  float power;          // exponent p; 2 takes the fast path
+  float mel_scale;      // exact power-of-two scale of the mel sums
+  float pre_scale;      // scale of |2X|^2 before a general power
+  int n_mels;
+  const float *window;
+  const float2 *twiddle, *untangle;
+  const int32_t *csr_start, *csr_width, *csr_off;
+  const float *csr_w;
+  int nnz;
+  void *out;
+  uint32_t *hi_bits;
+  float *tile_min;
+};
+
+// Packed filter weights are staged in LDS when they fit this many floats.
+constexpr int kCsrLdsMax = 4096;
+
+template <int NFFT, typename IN, typename OUT>
+__global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKernelArgs a) {
+  constexpr int M = NFFT / 2;
+  constexpr int FPB = PcmCfg<NFFT>::FPB;
+  constexpr int THREADS = PcmCfg<NFFT>::THREADS;
+  constexpr int NW = THREADS / 64;
+  __shared__ float2 s_buf[FPB * M];
+  __shared__ int32_t s_start[256], s_width[256], s_off[256];
+  __shared__ float s_w[kCsrLdsMax];
+  __shared__ float s_red[2 * NW];
+
+  const int tid = threadIdx.x;
+  const int64_t tile = blockIdx.x;
+  const int64_t b = tile / a.tiles_per_clip;
+  const int t = (int)(tile - b * a.tiles_per_clip);
+  const int64_t f0 = (int64_t)t * FPB;
+  const int64_t T = a.T, F = a.F;
+  const IN *__restrict__ x = reinterpret_cast<const IN *>(a.pcm) + b * T;
+
+  // packed filterbank -> LDS
+  const int NM = a.n_mels;
+  const bool w_in_lds = a.nnz <= kCsrLdsMax;
+  for (int m = tid; m < NM; m += THREADS) {
+    s_start[m] = a.csr_start[m];
+    s_width[m] = a.csr_width[m];
+    s_off[m] = a.csr_off[m];
+  }
+  if (w_in_lds)
+    for (int i = tid; i < a.nnz; i += THREADS) s_w[i] = a.csr_w[i];
+
+  // 1. windowed, padded frame samples as M complex points per frame
+  const float2 *__restrict__ win2 = reinterpret_cast<const float2 *>(a.window);
+  for (int i = tid; i < FPB * M; i += THREADS) {
+    const int fl = i / M, n = i - fl * M;
+    const int64_t fr = f0 + fl;
+    float2 z = make_float2(0.0f, 0.0f);
+    if (fr < F) {
+      const int64_t s0 = fr * a.hop - a.pad;
+      const int64_t j = s0 + 2 * n;
+      float x0, x1;
+      if (s0 >= 0 && s0 + NFFT <= T) {
+        x0 = to_f(x[j]);
+        x1 = to_f(x[j + 1]);
+      } else {
+        x0 = padded_sample(x, j, T, a.pad_mode);
+        x1 = padded_sample(x, j + 1, T, a.pad_mode);
+      }
+      const float2 w = win2[n];
+      z = make_float2(x0 * w.x, x1 * w.y);
+    }
+    s_buf[i] = z;
+  }
+  __syncthreads();
+
+  // 2. M-point complex FFT per frame
+  run_fft<M, FPB, THREADS>(s_buf, a.twiddle, typename PcmCfg<NFFT>::Rad{});
+
+  // 3. split into the real spectrum; power tile over the same LDS
+  constexpr int NU = M / 2 + 1;              // pairs (k, M-k), k = 0..M/2
+  constexpr int UPT = (FPB * NU + THREADS - 1) / THREADS;
+  float pk[UPT], pmk[UPT];
+#pragma unroll
+  for (int u = 0; u < UPT; ++u) {
+    const int q = tid + u * THREADS;
+    pk[u] = pmk[u] = 0.0f;
+    if (q < FPB * NU) {
+      const int fl = q / NU, k = q - fl * NU;
+      const float2 zk = s_buf[fl * M + k];
+      const float2 zc = cconj(s_buf[fl * M + (k == 0 ? 0 : M - k)]);
+      const float2 Y = cadd(zk, zc), D = csub(zk, zc);
+      const float2 V = cmul(a.untangle[k], D);
+      float p0 = (Y.x + V.y) * (Y.x + V.y) + (Y.y - V.x) * (Y.y - V.x);
+      float p1 = (Y.x - V.y) * (Y.x - V.y) + (Y.y + V.x) * (Y.y + V.x);
+      if (a.power != 2.0f) {
+        const float e = 0.5f * a.power;
+        p0 = powf(p0 * a.pre_scale, e);
+        p1 = powf(p1 * a.pre_scale, e);
+      }
+      pk[u] = p0;
+      pmk[u] = p1;
+    }
+  }
+  __syncthreads();
+  float *P = reinterpret_cast<float *>(s_buf);
+#pragma unroll
+  for (int u = 0; u < UPT; ++u) {
+    const int q = tid + u * THREADS;
+    if (q < FPB * NU) {
+      const int fl = q / NU, k = q - fl * NU;
+      P[fl * (M + 1) + k] = pk[u];
+      if (k != M / 2) P[fl * (M + 1) + M - k] = pmk[u];
+    }
+  }
+  __syncthreads();
+
+  // 4. mel sums, log10, rescale, mel-major store
+  float vmax = 0.0f, lmin = __builtin_huge_valf();
+  OUT *__restrict__ out = reinterpret_cast<OUT *>(a.out) + b * (int64_t)NM * F;
+  for (int o = tid; o < NM * FPB; o += THREADS) {
+    const int fl = o % FPB, m = o / FPB;
+    const int64_t fr = f0 + fl;
+    if (fr >= F) continue;
+    const int st = s_start[m], wd = s_width[m], of = s_off[m];
+    const float *pr = P + fl * (M + 1) + st;
+    float acc = 0.0f;
+    if (w_in_lds)
+      for (int j = 0; j < wd; ++j) acc = __builtin_fmaf(s_w[of + j], pr[j], acc);
+    else
+      for (int j = 0; j < wd; ++j) acc = __builtin_fmaf(a.csr_w[of + j], pr[j], acc);
+    const float v = fmaxf(acc * a.mel_scale, 1e-10f);
+    const float L = log10_pos(v);
+    vmax = fmaxf(vmax, v);
+    lmin = fminf(lmin, L);
+    store_out(out + (int64_t)m * F + fr, rescale(L));
+  }
+
+  // 5. tile statistics
+  block_maxmin<THREADS>(vmax, lmin, s_red);
+  if (tid == 0) {
+    atomicMax(a.hi_bits + b, __float_as_uint(vmax));
+    a.tile_min[tile] = lmin;
+  }
+}
+
+template <int NFFT>
+static hipError_t launch_n(const PcmKernelArgs &k, bool i16, bool f16, int64_t n_tiles, hipStream_t s) {
+  constexpr int THREADS = PcmCfg<NFFT>::THREADS;
+  const dim3 grid((unsigned)n_tiles), block(THREADS);
+  if (!i16 && !f16) hipLaunchKernelGGL((pcm_logmel_kernel<NFFT, float, float>), grid, block, 0, s, k);
+  else if (!i16 && f16) hipLaunchKernelGGL((pcm_logmel_kernel<NFFT, float, __half>), grid, block, 0, s, k);
+  else if (i16 && !f16) hipLaunchKernelGGL((pcm_logmel_kernel<NFFT, int16_t, float>), grid, block, 0, s, k);
+  else hipLaunchKernelGGL((pcm_logmel_kernel<NFFT, int16_t, __half>), grid, block, 0, s, k);
+  return hipGetLastError();
+}
+
+int pcm_frames_per_tile(int n_fft) {
+  switch (n_fft) {
+    case 400: return PcmCfg<400>::FPB;
+    case 64: return PcmCfg<64>::FPB;
+    case 128: return PcmCfg<128>::FPB;
+    case 256: return PcmCfg<256>::FPB;
+    case 512: return PcmCfg<512>::FPB;
+    case 1024: return PcmCfg<1024>::FPB;
+    case 2048: return PcmCfg<2048>::FPB;
+    case 4096: return PcmCfg<4096>::FPB;
+    case 8192: return PcmCfg<8192>::FPB;
+    case 16384: return PcmCfg<16384>::FPB;
+    default: return 0;
+  }
+}
+
+hipError_t launch_pcm(const lm_plan *p, const PcmArgs &a, hipStream_t s) {
+  PcmKernelArgs k;
+  k.pcm = a.pcm;
+  k.T = a.n_samples;
+  k.F = a.n_frames;
+  k.tiles_per_clip = a.tiles_per_clip;
+  k.hop = p->hop;
+  k.pad = p->center ? p->n_fft / 2 : 0;
+  k.pad_mode = p->pad_mode;
+  k.power = p->power;
+  // |2X|^2 = 4 |X|^2; int16 samples carry a 2^15 factor per |X|
+  const float in_scale2 = a.in_i16 ? 1.0f / 1073741824.0f : 1.0f;   // 2^-30
+  if (p->power == 2.0f) {
+    k.mel_scale = 0.25f * in_scale2;
+    k.pre_scale = 1.0f;
+  } else {
+    k.mel_scale = 1.0f;
+    k.pre_scale = 0.25f * in_scale2;
+  }
+  k.n_mels = p->n_mels;
+  k.window = p->dt.window;
+  k.twiddle = p->dt.twiddle;
+  k.untangle = p->dt.untangle;
+  k.csr_start = p->dt.csr_start;
+  k.csr_width = p->dt.csr_width;
+  k.csr_off = p->dt.csr_off;
+  k.csr_w = p->dt.csr_w;
+  k.nnz = p->dt.nnz;
+  k.out = a.out;
+  k.hi_bits = a.hi_bits;
+  k.tile_min = a.tile_min;
+  const int64_t n_tiles = a.n_clips * a.tiles_per_clip;
+  const bool f16 = p->out_dtype == LM_F16;
+  switch (p->n_fft) {
+    case 400: return launch_n<400>(k, a.in_i16, f16, n_tiles, s);
+    case 64: return launch_n<64>(k, a.in_i16, f16, n_tiles, s);
+    case 128: return launch_n<128>(k, a.in_i16, f16, n_tiles, s);
+    case 256: return launch_n<256>(k, a.in_i16, f16, n_tiles, s);
+    case 512: return launch_n<512>(k, a.in_i16, f16, n_tiles, s);
+    case 1024: return launch_n<1024>(k, a.in_i16, f16, n_tiles, s);
+    case 2048: return launch_n<2048>(k, a.in_i16, f16, n_tiles, s);
+    case 4096: return launch_n<4096>(k, a.in_i16, f16, n_tiles, s);
+    case 8192: return launch_n<8192>(k, a.in_i16, f16, n_tiles, s);
+    case 16384: return launch_n<16384>(k, a.in_i16, f16, n_tiles, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace lm

@@ -1,0 +1,225 @@
+// Host side of a plan: argument validation and the tables a launch reads
+// (window, FFT twiddles, packed mel filterbank).  Everything here runs on
+// the host in float64 and rounds once to float32; no HIP call is made.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "lm_internal.h"
+
+namespace lm {
+
+static thread_local std::string g_last_error;
+
+int fail(int status, const std::string &msg) {
+  g_last_error = msg;
+  return status;
+}
+
+int hip_fail(hipError_t err, const char *what) {
+  char buf[256];
+  std::snprintf(buf, sizeof buf, "%s: %s", what, hipGetErrorString(err));
+  g_last_error = buf;
+  return err == hipErrorOutOfMemory ? LM_ERR_OOM : LM_ERR_HIP;
+}
+
+int Csr::max_width() const {
+  int m = 0;
+  for (int v : width) m = v > m ? v : m;
+  return m;
+}
+
+static bool is_supported_nfft(int n) {
+  if (n == 400) return true;
+  if (n < 64 || n > 16384) return false;
+  return (n & (n - 1)) == 0;
+}
+
+// Periodic Hann: 0.5 - 0.5 cos(2 pi n / N), n = 0..N-1 (flashmel page,
+// "Usage": the window is always the periodic Hann).
+void build_window(lm_plan *p) {
+  const int N = p->n_fft;
+  p->window.resize(N);
+  for (int n = 0; n < N; ++n)
+    p->window[n] = (float)(0.5 - 0.5 * std::cos(2.0 * M_PI * (double)n / (double)N));
+}
+
+// exp(-2 pi i j / M) for the M-point complex FFT, and exp(-2 pi i k / N)
+// for k = 0..M/2 to split its result into the N-point real transform.
+void build_twiddles(lm_plan *p) {
+  const int N = p->n_fft, M = N / 2;
+  p->twiddle.resize(2 * (size_t)M);
+  for (int j = 0; j < M; ++j) {
+    const double a = 2.0 * M_PI * (double)j / (double)M;
+    p->twiddle[2 * j] = (float)std::cos(a);
+    p->twiddle[2 * j + 1] = (float)-std::sin(a);
+  }
+  p->untangle.resize(2 * (size_t)(M / 2 + 1));
+  for (int k = 0; k <= M / 2; ++k) {
+    const double a = 2.0 * M_PI * (double)k / (double)N;
+    p->untangle[2 * k] = (float)std::cos(a);
+    p->untangle[2 * k + 1] = (float)-std::sin(a);
+  }
+}
+
+Csr pack_dense(const float *dense, int n_rows, int n_bins) {
+  Csr c;
+  c.n_rows = n_rows;
+  c.n_bins = n_bins;
+  c.start.assign(n_rows, 0);
+  c.width.assign(n_rows, 0);
+  c.off.assign(n_rows, 0);
+  int off = 0;
+  for (int m = 0; m < n_rows; ++m) {
+    const float *row = dense + (size_t)m * n_bins;
+    int first = -1, last = -1;
+    for (int k = 0; k < n_bins; ++k)
+      if (row[k] != 0.0f) {
+        if (first < 0) first = k;
+        last = k;
+      }
+    c.off[m] = off;
+    if (first >= 0) {
+      c.start[m] = first;
+      c.width[m] = last - first + 1;
+      for (int k = first; k <= last; ++k) c.w.push_back(row[k]);
+      off += last - first + 1;
+    }
+  }
+  return c;
+}
+
+// Mel scales.  Slaney: 3f/200 below 1 kHz, then 27 mels per factor 6.4.
+static double hz_to_mel(double f, int scale) {
+  if (scale == LM_MEL_HTK) return 2595.0 * std::log10(1.0 + f / 700.0);
+  const double f_sp = 200.0 / 3.0, brk = 1000.0, step = std::log(6.4) / 27.0;
+  return f < brk ? f / f_sp : brk / f_sp + std::log(f / brk) / step;
+}
+
+static double mel_to_hz(double m, int scale) {
+  if (scale == LM_MEL_HTK) return 700.0 * (std::pow(10.0, m / 2595.0) - 1.0);
+  const double f_sp = 200.0 / 3.0, brk = 1000.0, step = std::log(6.4) / 27.0;
+  const double brk_mel = brk / f_sp;
+  return m < brk_mel ? f_sp * m : brk * std::exp(step * (m - brk_mel));
+}
+
+}  // namespace lm
+
+using namespace lm;
+
+extern "C" {
+
+const char *lm_last_error(void) { return g_last_error.c_str(); }
+
+const char *lm_status_string(int s) {
+  switch (s) {
+    case LM_OK: return "ok";
+    case LM_ERR_INVALID_ARG: return "invalid argument";
+    case LM_ERR_UNSUPPORTED: return "unsupported configuration";
+    case LM_ERR_NO_FILTERS: return "plan has no filterbank";
+    case LM_ERR_HIP: return "HIP runtime error";
+    case LM_ERR_OOM: return "out of memory";
+    default: return "unknown status";
+  }
+}
+
+int lm_plan_create(lm_plan **plan, int n_fft, int hop, int n_mels, int center, int pad_mode,
+                   float power, int out_dtype) {
+  g_last_error.clear();
+  if (!plan) return fail(LM_ERR_INVALID_ARG, "plan out-pointer is NULL");
+  if (!is_supported_nfft(n_fft))
+    return fail(LM_ERR_UNSUPPORTED, "n_fft must be 400 or a power of two in [64, 16384]");
+  if (hop < 1) return fail(LM_ERR_INVALID_ARG, "hop must be >= 1");
+  if (n_mels < 1 || n_mels > 256) return fail(LM_ERR_INVALID_ARG, "n_mels must be in [1, 256]");
+  if (center != 0 && center != 1) return fail(LM_ERR_INVALID_ARG, "center must be 0 or 1");
+  if (pad_mode < LM_PAD_CONSTANT || pad_mode > LM_PAD_CIRCULAR)
+    return fail(LM_ERR_INVALID_ARG, "unknown pad_mode");
+  if (!(power > 0.0f) || !std::isfinite(power))
+    return fail(LM_ERR_INVALID_ARG, "power must be finite and > 0");
+  if (out_dtype != LM_F32 && out_dtype != LM_F16)
+    return fail(LM_ERR_INVALID_ARG, "out_dtype must be LM_F32 or LM_F16");
+  lm_plan *p = new (std::nothrow) lm_plan();
+  if (!p) return fail(LM_ERR_OOM, "host allocation failed");
+  p->n_fft = n_fft;
+  p->hop = hop;
+  p->n_mels = n_mels;
+  p->center = center;
+  p->pad_mode = pad_mode;
+  p->power = power;
+  p->out_dtype = out_dtype;
+  p->n_bins = n_fft / 2 + 1;
+  build_window(p);
+  build_twiddles(p);
+  *plan = p;
+  return LM_OK;
+}
+
+int lm_plan_set_mel(lm_plan *p, double sr, double f_min, double f_max, int scale, int norm) {
+  g_last_error.clear();
+  if (!p) return fail(LM_ERR_INVALID_ARG, "plan is NULL");
+  if (!(sr > 0.0) || !std::isfinite(sr)) return fail(LM_ERR_INVALID_ARG, "sample_rate must be > 0");
+  if (!(f_min >= 0.0) || !(f_max > f_min) || !(f_max <= sr / 2.0))
+    return fail(LM_ERR_INVALID_ARG, "need 0 <= f_min < f_max <= sample_rate / 2");
+  if (scale != LM_MEL_SLANEY && scale != LM_MEL_HTK) return fail(LM_ERR_INVALID_ARG, "mel_scale");
+  if (norm != LM_NORM_SLANEY && norm != LM_NORM_NONE) return fail(LM_ERR_INVALID_ARG, "norm");
+  const int NM = p->n_mels, K = p->n_bins;
+  std::vector<double> fpts(NM + 2);
+  const double m_lo = hz_to_mel(f_min, scale), m_hi = hz_to_mel(f_max, scale);
+  for (int i = 0; i < NM + 2; ++i) {
+    const double m = (i == NM + 1) ? m_hi : m_lo + (m_hi - m_lo) * (double)i / (double)(NM + 1);
+    fpts[i] = mel_to_hz(m, scale);
+  }
+  std::vector<float> dense((size_t)NM * K, 0.0f);
+  for (int m = 0; m < NM; ++m) {
+    const double lo = fpts[m], mid = fpts[m + 1], hi = fpts[m + 2];
+    const double g = (norm == LM_NORM_SLANEY) ? 2.0 / (hi - lo) : 1.0;
+    for (int k = 0; k < K; ++k) {
+      const double fk = (double)k * sr / (double)p->n_fft;
+      const double rise = (fk - lo) / (mid - lo), fall = (hi - fk) / (hi - mid);
+      const double w = std::fmax(0.0, std::fmin(rise, fall));
+      dense[(size_t)m * K + k] = (float)(w * g);
+    }
+  }
+  p->csr = pack_dense(dense.data(), NM, K);
+  p->have_filters = true;
+  p->tables_dirty = true;
+  return LM_OK;
+}
+
+int lm_plan_set_filters(lm_plan *p, const float *host_dense, int n_mels, int n_bins) {
+  g_last_error.clear();
+  if (!p) return fail(LM_ERR_INVALID_ARG, "plan is NULL");
+  if (!host_dense) return fail(LM_ERR_INVALID_ARG, "filters pointer is NULL");
+  if (n_mels != p->n_mels || n_bins != p->n_bins)
+    return fail(LM_ERR_INVALID_ARG, "filters must be (n_mels, n_fft/2 + 1)");
+  for (size_t i = 0; i < (size_t)n_mels * n_bins; ++i)
+    if (!std::isfinite(host_dense[i])) return fail(LM_ERR_INVALID_ARG, "filters hold a non-finite value");
+  p->csr = pack_dense(host_dense, n_mels, n_bins);
+  p->have_filters = true;
+  p->tables_dirty = true;
+  return LM_OK;
+}
+
+int lm_plan_get_filters(const lm_plan *p, float *out, int n_mels, int n_bins) {
+  g_last_error.clear();
+  if (!p || !out) return fail(LM_ERR_INVALID_ARG, "NULL argument");
+  if (!p->have_filters) return fail(LM_ERR_NO_FILTERS, "plan has no filterbank");
+  if (n_mels != p->n_mels || n_bins != p->n_bins)
+    return fail(LM_ERR_INVALID_ARG, "shape must be (n_mels, n_fft/2 + 1)");
+  std::memset(out, 0, sizeof(float) * (size_t)n_mels * n_bins);
+  for (int m = 0; m < n_mels; ++m)
+    for (int j = 0; j < p->csr.width[m]; ++j)
+      out[(size_t)m * n_bins + p->csr.start[m] + j] = p->csr.w[p->csr.off[m] + j];
+  return LM_OK;
+}
+
+int64_t lm_plan_num_frames(const lm_plan *p, int64_t n_samples) {
+  if (!p) return fail(LM_ERR_INVALID_ARG, "plan is NULL");
+  if (n_samples < 0) return fail(LM_ERR_INVALID_ARG, "n_samples < 0");
+  const int64_t t_pad = n_samples + (p->center ? 2 * (int64_t)(p->n_fft / 2) : 0);
+  if (t_pad < p->n_fft) return fail(LM_ERR_INVALID_ARG, "signal shorter than one frame");
+  return 1 + (t_pad - p->n_fft) / p->hop;
+}
+
+}  // extern "C"

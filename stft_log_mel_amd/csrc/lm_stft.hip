@@ -1,0 +1,228 @@
+// Complex STFT -> log-mel (KBench task page "audio-mel-spectrogram-fused",
+// sections "reference_src", "spec_md", "contract_md", "perf_md").
+//
+// The source is read exactly once.  A workgroup owns TF consecutive frames
+// of one clip; those frames are one contiguous run of TF*NF complex64
+// values, streamed with 16-byte non-temporal loads (two bins per load) and
+// turned into power re^2 + im^2 straight into an LDS tile.  Each (frame,
+// band) output is then the packed triangular mel sum over that tile, log10
+// after the 1e-10 floor, (L+4)/4, stored frame-major so a tile's outputs
+// are one contiguous run.  The tile's largest mel value joins its clip's
+// maximum by atomicMax on the float bits and its smallest log value goes
+// to a per-tile slot; the clamp fix-up kernel completes the per-clip floor.
+#include <climits>
+
+#include "lm_device.h"
+#include "lm_internal.h"
+
+namespace lm {
+
+constexpr int kStftThreads = 256;
+constexpr int kStftLoadUnroll = 8;
+constexpr int kStftCsrLds = 2048;   // packed weights staged in LDS up to this count
+
+struct StftKernelArgs {
+  const float2 *stft;
+  int64_t F;
+  int NF, NM, TF, tiles_per_clip;
+  const int32_t *csr_start, *csr_width, *csr_off;
+  const float *csr_w;
+  void *out;
+  uint32_t *hi_bits;
+  float *tile_min;
+};
+
+__device__ __forceinline__ float pw(float2 v) { return __builtin_fmaf(v.x, v.x, v.y * v.y); }
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+template <typename OUT, bool VEC16>
+__global__ void __launch_bounds__(kStftThreads) stft_logmel_kernel(StftKernelArgs a) {
+  extern __shared__ float s_dyn[];      // [TF*NF power tile][kStftCsrLds weights]
+  __shared__ int32_t s_start[256], s_width[256], s_off[256];
+  __shared__ float s_red[2 * kStftThreads / 64];
+
+  const int tid = threadIdx.x;
+  const int64_t tile = blockIdx.x;
+  const int64_t b = tile / a.tiles_per_clip;
+  const int t = (int)(tile - b * a.tiles_per_clip);
+  const int64_t f0 = (int64_t)t * a.TF;
+  const int nfr = (int)min((int64_t)a.TF, a.F - f0);
+  const int NF = a.NF, NM = a.NM;
+  float *P = s_dyn;
+  float *s_w = s_dyn + a.TF * NF;
+
+  // 1. power tile: elements [e0, e0 + n) of the flat complex array
+  const int64_t e0 = (b * a.F + f0) * NF;
+  const int n = nfr * NF;
+  if (VEC16) {
+    const int head = (int)(e0 & 1);                  // element e0 is 16-byte aligned iff even
+    const int npairs = (n - head) >> 1;
+    const v4f *src = reinterpret_cast<const v4f *>(a.stft + e0 + head);
+    for (int q0 = tid; q0 < npairs; q0 += kStftLoadUnroll * kStftThreads) {
+      v4f v[kStftLoadUnroll];
+#pragma unroll
+      for (int u = 0; u < kStftLoadUnroll; ++u) {
+        const int q = q0 + u * kStftThreads;
+        if (q < npairs) v[u] = __builtin_nontemporal_load(src + q);
+      }
+#pragma unroll
+      for (int u = 0; u < kStftLoadUnroll; ++u) {
+        const int q = q0 + u * kStftThreads;
+        if (q < npairs) {
+          P[head + 2 * q] = __builtin_fmaf(v[u].x, v[u].x, v[u].y * v[u].y);
+          P[head + 2 * q + 1] = __builtin_fmaf(v[u].z, v[u].z, v[u].w * v[u].w);
+        }
+      }
+    }
+    if (tid == 0 && head) P[0] = pw(a.stft[e0]);
+    if (tid == kStftThreads - 1 && ((n - head) & 1)) P[n - 1] = pw(a.stft[e0 + n - 1]);
+  } else {
+    for (int i = tid; i < n; i += kStftThreads) P[i] = pw(a.stft[e0 + i]);
+  }
+
+  // packed filterbank -> LDS
+  for (int m = tid; m < NM; m += kStftThreads) {
+    s_start[m] = a.csr_start[m];
+    s_width[m] = a.csr_width[m];
+    s_off[m] = a.csr_off[m];
+  }
+  const int nnz = a.csr_off[NM - 1] + a.csr_width[NM - 1];
+  const bool w_in_lds = nnz <= kStftCsrLds;
+  if (w_in_lds)
+    for (int i = tid; i < nnz; i += kStftThreads) s_w[i] = a.csr_w[i];
+  __syncthreads();
+
+  // 2. mel sums, log10, rescale, frame-major store
+  OUT *__restrict__ out = reinterpret_cast<OUT *>(a.out) + (b * a.F + f0) * NM;
+  float vmax = 0.0f, lmin = __builtin_huge_valf();
+  int m = tid % NM, f = tid / NM;
+  const int dm = kStftThreads % NM, df = kStftThreads / NM;
+  for (int o = tid; o < nfr * NM; o += kStftThreads) {
+    const int st = s_start[m], wd = s_width[m], of = s_off[m];
+    const float *pr = P + f * NF + st;
+    float acc = 0.0f;
+    if (w_in_lds)
+      for (int j = 0; j < wd; ++j) acc = __builtin_fmaf(s_w[of + j], pr[j], acc);
+    else
+      for (int j = 0; j < wd; ++j) acc = __builtin_fmaf(a.csr_w[of + j], pr[j], acc);
+    const float v = fmaxf(acc, 1e-10f);
+    const float L = log10_pos(v);
+    vmax = fmaxf(vmax, v);
+    lmin = fminf(lmin, L);
+    store_out(out + o, rescale(L));
+    m += dm;
+    f += df;
+    if (m >= NM) {
+      m -= NM;
+      f += 1;
+    }
+  }
+
+  // 3. tile statistics
+  block_maxmin<kStftThreads>(vmax, lmin, s_red);
+  if (tid == 0) {
+    atomicMax(a.hi_bits + b, __float_as_uint(vmax));
+    a.tile_min[tile] = lmin;
+  }
+}
+
+int stft_frames_per_tile(int n_bins, int n_mels) {
+  (void)n_mels;
+  int tf = 6144 / n_bins;
+  if (tf > 64) tf = 64;
+  if (tf < 1) tf = 1;
+  return tf;
+}
+
+hipError_t launch_stft(const StftArgs &a, hipStream_t s) {
+  StftKernelArgs k;
+  k.stft = a.stft;
+  k.F = a.n_frames;
+  k.NF = a.n_bins;
+  k.NM = a.n_mels;
+  k.TF = a.frames_per_tile;
+  k.tiles_per_clip = a.tiles_per_clip;
+  k.csr_start = a.csr_start;
+  k.csr_width = a.csr_width;
+  k.csr_off = a.csr_off;
+  k.csr_w = a.csr_w;
+  k.out = a.out;
+  k.hi_bits = a.hi_bits;
+  k.tile_min = a.tile_min;
+  const size_t lds = sizeof(float) * ((size_t)a.frames_per_tile * a.n_bins + kStftCsrLds);
+  const dim3 grid((unsigned)(a.n_clips * a.tiles_per_clip)), block(kStftThreads);
+  const bool vec16 = (reinterpret_cast<uintptr_t>(a.stft) & 15) == 0;
+  if (a.out_f16) {
+    if (vec16) hipLaunchKernelGGL((stft_logmel_kernel<__half, true>), grid, block, lds, s, k);
+    else hipLaunchKernelGGL((stft_logmel_kernel<__half, false>), grid, block, lds, s, k);
+  } else {
+    if (vec16) hipLaunchKernelGGL((stft_logmel_kernel<float, true>), grid, block, lds, s, k);
+    else hipLaunchKernelGGL((stft_logmel_kernel<float, false>), grid, block, lds, s, k);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Dense (NM, NF) device filterbank -> packed rows.  One workgroup: each wave
+// finds the first and last non-zero of its rows, one thread lays out the
+// row offsets, then the waves copy each row's [first, last] range.
+// ---------------------------------------------------------------------------
+
+constexpr int kPackThreads = 1024;
+
+__global__ void __launch_bounds__(kPackThreads)
+pack_filters_kernel(const float *__restrict__ dense, int NM, int NF, int32_t *start, int32_t *width,
+                    int32_t *off, float *w) {
+  __shared__ int s_first[256], s_last[256], s_off[256];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  constexpr int NWV = kPackThreads / 64;
+  for (int m = wv; m < NM; m += NWV) {
+    int first = INT_MAX, last = -1;
+    const float *row = dense + (size_t)m * NF;
+    for (int k = lane; k < NF; k += 64)
+      if (row[k] != 0.0f) {
+        first = min(first, k);
+        last = max(last, k);
+      }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      first = min(first, __shfl_xor(first, o, 64));
+      last = max(last, __shfl_xor(last, o, 64));
+    }
+    if (lane == 0) {
+      s_first[m] = first;
+      s_last[m] = last;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int o = 0;
+    for (int m = 0; m < NM; ++m) {
+      const int wd = s_last[m] >= 0 ? s_last[m] - s_first[m] + 1 : 0;
+      s_off[m] = o;
+      start[m] = wd ? s_first[m] : 0;
+      width[m] = wd;
+      off[m] = o;
+      o += wd;
+    }
+  }
+  __syncthreads();
+  for (int m = wv; m < NM; m += NWV) {
+    if (s_last[m] < 0) continue;
+    const int st = s_first[m], wd = s_last[m] - st + 1, o = s_off[m];
+    for (int j = lane; j < wd; j += 64) w[o + j] = dense[(size_t)m * NF + st + j];
+  }
+}
+
+hipError_t launch_pack(const float *dense, int n_mels, int n_bins, void *ws, hipStream_t s) {
+  int32_t *start = reinterpret_cast<int32_t *>(ws);
+  int32_t *width = start + n_mels;
+  int32_t *off = width + n_mels;
+  float *w = reinterpret_cast<float *>(off + n_mels);
+  hipLaunchKernelGGL(pack_filters_kernel, dim3(1), dim3(kPackThreads), 0, s, dense, n_mels, n_bins, start,
+                     width, off, w);
+  return hipGetLastError();
+}
+
+}  // namespace lm

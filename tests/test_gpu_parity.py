@@ -1,0 +1,305 @@
+"""HIP path vs the fp64 oracle, element by element, through the C ABI.
+
+Tolerances (fixed by the target, written here): max |GPU - oracle| <= 1e-4
+for float32 output and <= 2e-3 for float16 output.  Each case prints what it
+runs before launching anything.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import lm_synth
+import oracle
+from tests.golden_io import load_stft_worked
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+TOL32 = 1e-4
+TOL16 = 2e-3
+
+
+def lm():
+    import stft_log_mel_amd
+    return stft_log_mel_amd
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+
+
+def check(got, ref, tol, what):
+    got = got.detach().float().cpu().numpy().astype(np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.isfinite(got).all(), what
+    err = np.abs(got - ref)
+    i = np.unravel_index(np.argmax(err), err.shape)
+    assert err.max() <= tol, f"{what}: max |err| {err.max():.3e} at {i} (got {got[i]}, ref {ref[i]})"
+    return float(err.max())
+
+
+# ---------------------------------------------------------------------------
+# STFT path
+# ---------------------------------------------------------------------------
+
+def test_stft_worked_example():
+    stft, W, exp = load_stft_worked()
+    say("stft worked example", stft.shape)
+    out = lm().log_mel_spectrogram(to_dev(stft), to_dev(W))
+    torch.cuda.synchronize()
+    check(out, exp, 1e-6, "worked example")
+
+
+@pytest.mark.parametrize("B,F,NF,NM", [(1, 3000, 201, 80), (3, 301, 201, 128), (5, 128, 65, 40),
+                                       (2, 3000, 201, 128), (7, 97, 129, 80), (4, 1500, 401, 80),
+                                       (2, 33, 1, 3), (3, 5, 8193, 256)])
+def test_stft_shapes(B, F, NF, NM):
+    say("stft", B, F, NF, NM)
+    s = lm_synth.stft_speechlike(B, F, NF, seed=B * 7 + NF)
+    W = lm_synth.lintri_filters(NF, NM)
+    out = lm().log_mel_spectrogram(to_dev(s), to_dev(W))
+    torch.cuda.synchronize()
+    check(out, oracle.from_stft(s, W), TOL32, f"stft {B,F,NF,NM}")
+
+
+def test_stft_full_size_large_batch():
+    w = lm_synth.WORKLOADS["stft_b256"]
+    say("stft full size", w.B, w.F, w.NF, w.NM)
+    s, W = lm_synth.make_inputs(w)
+    s_d = to_dev(s)
+    out = lm().log_mel_spectrogram(s_d, to_dev(W))
+    torch.cuda.synchronize()
+    del s_d
+    check(out, oracle.from_stft(s, W), TOL32, "stft_b256")
+
+
+def test_stft_misaligned_and_plan_filters_and_f16():
+    B, F, NF, NM = 3, 77, 201, 80
+    s = lm_synth.stft_speechlike(B, F, NF, seed=3)
+    W = lm_synth.lintri_filters(NF, NM)
+    ref = oracle.from_stft(s, W)
+    flat = torch.zeros(B * F * NF + 1, dtype=torch.complex64, device=dev())
+    flat[1:] = to_dev(s.reshape(-1))
+    view = flat[1:].view(B, F, NF)                 # 8-byte but not 16-byte aligned
+    assert view.data_ptr() % 16 == 8
+    say("stft misaligned")
+    out = lm().log_mel_spectrogram(view, to_dev(W))
+    torch.cuda.synchronize()
+    check(out, ref, TOL32, "misaligned")
+    # the plan's own filterbank (filters passed as NULL)
+    p = lm().Plan(400, 160, NM).set_filters(W)
+    say("stft plan filters")
+    out2 = p.from_stft(to_dev(s))
+    torch.cuda.synchronize()
+    check(out2, ref, TOL32, "plan filters")
+    p16 = lm().Plan(400, 160, NM, out_dtype="f16").set_filters(W)
+    say("stft f16 out")
+    out3 = p16.from_stft(to_dev(s))
+    torch.cuda.synchronize()
+    assert out3.dtype == torch.float16
+    check(out3, ref, TOL16, "f16 out")
+
+
+def test_stft_clamp_engaged_per_clip():
+    """Silent frames and mixed gains: the hi-8 floor binds, per clip."""
+    B, F, NF, NM = 4, 200, 201, 128
+    s = lm_synth.stft_speechlike(B, F, NF, seed=11)
+    s[0, 50:150] = 0                      # digital silence inside a loud clip
+    s[1] *= 1e-6                          # quiet clip: its own floor
+    s[2, :, 100:] *= 1e-5                 # weak high band
+    s[3] = 0                              # all silent: -1.5 everywhere
+    W = lm_synth.lintri_filters(NF, NM)
+    ref = oracle.from_stft(s, W)
+    say("stft clamp engaged")
+    out = lm().log_mel_spectrogram(to_dev(s), to_dev(W))
+    torch.cuda.synchronize()
+    check(out, ref, TOL32, "clamp engaged")
+    hi0 = ref[0].max()
+    assert np.isclose(ref[0].min(), hi0 - 2.0)          # floor really binds
+    assert np.abs(out[3].cpu().numpy() + 1.5).max() <= 1e-6     # fp32 1e-10 floor, hardware log2
+
+
+def test_stft_repeat_calls_and_invariances():
+    B, F, NF, NM = 5, 300, 201, 80
+    s = lm_synth.stft_speechlike(B, F, NF, seed=21)
+    W = to_dev(lm_synth.lintri_filters(NF, NM))
+    sd = to_dev(s)
+    say("stft determinism / permutation / single clip")
+    a = lm().log_mel_spectrogram(sd, W)
+    b = lm().log_mel_spectrogram(sd, W)
+    perm = [3, 1, 4, 0, 2]
+    c = lm().log_mel_spectrogram(sd[perm].contiguous(), W)
+    d = lm().log_mel_spectrogram(sd[2:3].contiguous(), W)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert torch.equal(c, a[perm])
+    assert torch.equal(d[0], a[2])
+
+
+# ---------------------------------------------------------------------------
+# PCM path
+# ---------------------------------------------------------------------------
+
+def run_pcm(x, n_fft, hop, n_mels, sr, center=True, pad_mode="reflect", power=2.0, out_dtype="f32",
+            fmin=0.0, fmax=None, scale="slaney", norm="slaney"):
+    p = lm().Plan(n_fft, hop, n_mels, center, pad_mode, power, out_dtype).set_mel(sr, fmin, fmax, scale, norm)
+    out = p.from_pcm(to_dev(x))
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_pcm(x, n_fft, hop, n_mels, sr, center=True, pad_mode="reflect", power=2.0, fmin=0.0, fmax=None,
+               scale="slaney", norm="slaney"):
+    W = oracle.mel_filterbank(sr, n_fft, n_mels, fmin, fmax, scale=scale, norm=norm)
+    return oracle.from_pcm(x, n_fft, hop, W, center=center, pad_mode=pad_mode, power=power)
+
+
+@pytest.mark.parametrize("name", ["pcm_f32_b8", "pcm_i16_b64"])
+def test_pcm_full_size_n400(name):
+    w = lm_synth.WORKLOADS[name]
+    say("pcm full size", name)
+    x = lm_synth.make_inputs(w)
+    out = run_pcm(x, w.n_fft, w.hop, w.n_mels, w.sample_rate, out_dtype=w.out_dtype)
+    ref = oracle_pcm(x, w.n_fft, w.hop, w.n_mels, w.sample_rate)
+    check(out, ref, TOL32, name)
+
+
+def test_pcm_full_size_n16384_f16():
+    w = lm_synth.WORKLOADS["pcm_f32_nfft16384"]
+    say("pcm full size", w.name)
+    x = lm_synth.make_inputs(w)
+    out = run_pcm(x, w.n_fft, w.hop, w.n_mels, w.sample_rate, out_dtype="f16")
+    assert out.dtype == torch.float16 and tuple(out.shape) == w.out_shape
+    # the clip-level maximum makes whole clips the natural sample; three clips
+    clips = [0, 7, 15]
+    ref = oracle_pcm(x[clips], w.n_fft, w.hop, w.n_mels, w.sample_rate)
+    check(out[clips], ref, TOL16, w.name)
+
+
+@pytest.mark.parametrize("n_fft", [64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384, 400])
+def test_pcm_every_size_ragged(n_fft):
+    hop = max(1, n_fft // 4)
+    B, T = 3, 9 * n_fft + 123
+    sr = 16000.0
+    n_mels = min(128, n_fft // 4)
+    say("pcm size", n_fft, B, T)
+    x = lm_synth.speech_pcm(B, T, sr, seed=n_fft)
+    out = run_pcm(x, n_fft, hop, n_mels, sr)
+    check(out, oracle_pcm(x, n_fft, hop, n_mels, sr), TOL32, f"n_fft {n_fft}")
+
+
+@pytest.mark.parametrize("pad_mode", ["reflect", "constant", "replicate", "circular"])
+@pytest.mark.parametrize("center", [True, False])
+def test_pcm_pad_modes(pad_mode, center):
+    B, T = 2, 7001
+    say("pcm pad", pad_mode, center)
+    x = lm_synth.speech_pcm(B, T, 16000.0, seed=5)
+    out = run_pcm(x, 400, 160, 80, 16000.0, center=center, pad_mode=pad_mode)
+    ref = oracle_pcm(x, 400, 160, 80, 16000.0, center=center, pad_mode=pad_mode)
+    check(out, ref, TOL32, f"{pad_mode} center={center}")
+
+
+@pytest.mark.parametrize("T,center,pad_mode", [(201, True, "reflect"), (200, True, "circular"),
+                                               (400, False, "reflect"), (559, False, "reflect"),
+                                               (1, True, "constant"), (1, True, "replicate")])
+def test_pcm_short_clips(T, center, pad_mode):
+    say("pcm short", T, center, pad_mode)
+    rng = np.random.default_rng(T)
+    x = (0.3 * rng.standard_normal((2, T))).astype(np.float32)
+    out = run_pcm(x, 400, 160, 40, 16000.0, center=center, pad_mode=pad_mode)
+    ref = oracle_pcm(x, 400, 160, 40, 16000.0, center=center, pad_mode=pad_mode)
+    check(out, ref, TOL32, f"short T={T}")
+
+
+def test_pcm_int16_extremes_and_batch_sizes():
+    rng = np.random.default_rng(9)
+    for B in (1, 3, 7):
+        x = rng.integers(-32768, 32768, size=(B, 5000), dtype=np.int64).astype(np.int16)
+        x[0, :50] = 32767
+        x[0, 50:100] = -32768
+        say("pcm int16 extremes B", B)
+        out = run_pcm(x, 400, 160, 128, 16000.0)
+        check(out, oracle_pcm(x, 400, 160, 128, 16000.0), TOL32, f"int16 B={B}")
+
+
+@pytest.mark.parametrize("power", [1.0, 3.0])
+def test_pcm_general_power(power):
+    say("pcm power", power)
+    x = lm_synth.speech_pcm(2, 6000, 16000.0, seed=4)
+    out = run_pcm(x, 512, 128, 64, 16000.0, power=power)
+    check(out, oracle_pcm(x, 512, 128, 64, 16000.0, power=power), TOL32, f"power {power}")
+
+
+def test_pcm_htk_no_norm_and_user_filters():
+    x = lm_synth.speech_pcm(2, 8000, 16000.0, seed=8)
+    say("pcm htk / norm none")
+    out = run_pcm(x, 1024, 256, 96, 16000.0, fmin=30.0, fmax=7000.0, scale="htk", norm=None)
+    ref = oracle_pcm(x, 1024, 256, 96, 16000.0, fmin=30.0, fmax=7000.0, scale="htk", norm=None)
+    check(out, ref, TOL32, "htk")
+    rng = np.random.default_rng(3)
+    W = np.zeros((10, 201), dtype=np.float32)
+    for m in range(10):
+        W[m, 10 * m: 10 * m + 30] = rng.random(30)
+    p = lm().Plan(400, 160, 10).set_filters(W)
+    say("pcm user filters")
+    out2 = p.from_pcm(to_dev(x))
+    torch.cuda.synchronize()
+    check(out2, oracle.from_pcm(x, 400, 160, W), TOL32, "user filters")
+
+
+def test_pcm_clamp_engaged():
+    """Digital silence, a quiet clip and an all-zero clip in one batch."""
+    sr = 16000.0
+    x = lm_synth.speech_pcm(4, 32000, sr, seed=12)
+    x[0, 8000:24000] = 0.0               # loud clip with a silent middle: floor binds
+    x[1] *= 1e-4                          # quiet clip: its own floor, not the batch's
+    x[2] = 0.0                            # all zero: every value is -1.5
+    x[3] = 0.25                           # DC
+    say("pcm clamp engaged")
+    out = run_pcm(x, 400, 160, 80, sr)
+    ref = oracle_pcm(x, 400, 160, 80, sr)
+    check(out, ref, TOL32, "pcm clamp")
+    assert np.isclose(ref[0].min(), ref[0].max() - 2.0)
+    assert np.abs(out[2].cpu().numpy() + 1.5).max() <= 1e-6     # fp32 1e-10 floor, hardware log2
+
+
+def test_pcm_invariances():
+    sr = 16000.0
+    x = lm_synth.speech_pcm(4, 20000, sr, seed=13)
+    p = lm().Plan(400, 160, 80).set_mel(sr)
+    xd = to_dev(x)
+    say("pcm determinism / permutation / batch-vs-single / gain")
+    a = p.from_pcm(xd)
+    b = p.from_pcm(xd)
+    perm = [2, 0, 3, 1]
+    c = p.from_pcm(xd[perm].contiguous())
+    d = p.from_pcm(xd[1:2].contiguous())
+    g = p.from_pcm((xd * 10.0).contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert torch.equal(c, a[perm])
+    assert torch.equal(d[0], a[1])
+    assert float((g - a - 0.5).abs().max()) <= 2 * TOL32
+
+
+def test_melspectrogram_wrapper_shapes():
+    m = lm().MelSpectrogram(sample_rate=16000, n_fft=400, hop_length=160, n_mels=128)
+    x = lm_synth.speech_pcm(6, 16000, 16000.0, seed=2).reshape(2, 3, 16000)
+    say("MelSpectrogram wrapper (..., time)")
+    y = m(to_dev(x))
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (2, 3, 128, 101)
+    ref = oracle_pcm(x.reshape(6, 16000), 400, 160, 128, 16000.0).reshape(2, 3, 128, 101)
+    check(y, ref, TOL32, "wrapper")
+    with pytest.raises(RuntimeError):
+        m(to_dev(x[0]).requires_grad_(True))
