@@ -69,6 +69,8 @@ def main():
     ap.add_argument("--workload", default="pcm_i16_b64")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy (5 times), to scale HBM counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (clips shard across "
@@ -77,6 +79,17 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = 1 << 28                                   # 2^28 floats = 1 GiB read + 1 GiB written
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"bytes_read_per_copy": 4 * n, "bytes_written_per_copy": 4 * n,
+                                               "copies": 5}}), flush=True)
+        return
 
     import lm_synth
     import stft_log_mel_amd as lm
@@ -135,9 +148,10 @@ def main():
     value = frames / (ms_per_step / 1e3)
     main_ms = prof["main"]["ms"] / max(1, prof["main"]["count"])
     fix_ms = prof["fixup"]["ms"] / max(1, prof["fixup"]["count"])
+    pack_ms = prof["pack"]["ms"] / max(1, prof["pack"]["count"])
     achieved = per_step_bytes / (main_ms / 1e3) / 1e9
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step (wall {wall:.3f}s), "
-          f"main kernel {main_ms:.4f} ms, fixup {fix_ms:.4f} ms", file=sys.stderr, flush=True)
+          f"main kernel {main_ms:.4f} ms, fixup {fix_ms:.4f} ms, pack {pack_ms:.4f} ms", file=sys.stderr, flush=True)
 
     # parity spot check of the timed output against the first clip's oracle
     parity = None
@@ -213,6 +227,7 @@ def main():
             "fp32_vector_peak_tflops": FP32_VALU_PEAK_TFLOPS,
         },
         "fixup_ms": round(fix_ms, 5),
+        "pack_ms": round(pack_ms, 5),
         "cpu_baseline": cpu,
         "parity": parity,
     }

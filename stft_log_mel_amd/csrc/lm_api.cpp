@@ -29,7 +29,8 @@ int upload_tables(lm_plan *p) {
   size_t o_wd = align256(o_st + sizeof(int32_t) * NM);
   size_t o_of = align256(o_wd + sizeof(int32_t) * NM);
   size_t o_w = align256(o_of + sizeof(int32_t) * NM);
-  size_t total = align256(o_w + sizeof(float) * (nnz > 0 ? nnz : 1));
+  size_t o_mf = align256(o_w + sizeof(float) * (nnz > 0 ? nnz : 1));
+  size_t total = align256(o_mf + sizeof(float) * p->mfma400.size());
   std::vector<unsigned char> host(total, 0);
   std::memcpy(host.data() + o_win, p->window.data(), sizeof(float) * N);
   std::memcpy(host.data() + o_tw, p->twiddle.data(), sizeof(float) * 2 * M);
@@ -40,6 +41,8 @@ int upload_tables(lm_plan *p) {
     std::memcpy(host.data() + o_of, p->csr.off.data(), sizeof(int32_t) * NM);
     if (nnz) std::memcpy(host.data() + o_w, p->csr.w.data(), sizeof(float) * nnz);
   }
+  if (!p->mfma400.empty())
+    std::memcpy(host.data() + o_mf, p->mfma400.data(), sizeof(float) * p->mfma400.size());
   if (p->dt.base) {
     hipError_t e = hipFree(p->dt.base);
     p->dt.base = nullptr;
@@ -64,13 +67,15 @@ int upload_tables(lm_plan *p) {
   p->dt.csr_off = reinterpret_cast<const int32_t *>(c + o_of);
   p->dt.csr_w = reinterpret_cast<const float *>(c + o_w);
   p->dt.nnz = nnz;
+  p->dt.mfma400 = p->mfma400.empty() ? nullptr : reinterpret_cast<const float *>(c + o_mf);
   p->tables_dirty = false;
   return LM_OK;
 }
 
-// hi_bits must be zero when a call starts; the fix-up kernel clears it at
-// the end of every call, and a fresh (or previously failed) buffer is
-// cleared here on the caller's stream.
+// hi_bits and the fix-up counters (d_hi[hi_cap ..]) must be zero when a
+// call starts; the fix-up kernel clears both at the end of every call, and
+// a fresh (or previously failed) buffer is cleared here on the caller's
+// stream.
 int ensure_workspace(lm_plan *p, int64_t n_clips, int64_t n_tiles, hipStream_t s) {
   hipError_t e;
   if ((size_t)n_clips > p->hi_cap) {
@@ -80,13 +85,13 @@ int ensure_workspace(lm_plan *p, int64_t n_clips, int64_t n_tiles, hipStream_t s
       p->hi_cap = 0;
       if (e != hipSuccess) return hip_fail(e, "hipFree(workspace)");
     }
-    e = hipMalloc(reinterpret_cast<void **>(&p->d_hi), sizeof(uint32_t) * n_clips);
+    e = hipMalloc(reinterpret_cast<void **>(&p->d_hi), 2 * sizeof(uint32_t) * n_clips);
     if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
     p->hi_cap = n_clips;
     p->ws_dirty = true;
   }
   if (p->ws_dirty) {
-    e = hipMemsetAsync(p->d_hi, 0, sizeof(uint32_t) * p->hi_cap, s);
+    e = hipMemsetAsync(p->d_hi, 0, 2 * sizeof(uint32_t) * p->hi_cap, s);
     if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync(workspace)");
     p->ws_dirty = false;
   }
@@ -164,13 +169,15 @@ int lm_from_pcm(lm_plan *p, const void *pcm, int in_dtype, int64_t n_clips, int6
     return fail(LM_ERR_INVALID_ARG, "misaligned pcm or out pointer");
   const int64_t F = lm_plan_num_frames(p, n_samples);
   if (F < 1) return (int)F;
-  const int fpb = pcm_frames_per_tile(p->n_fft);
+  int rc = ensure_device(p);
+  if (rc == LM_OK) rc = upload_tables(p);
+  if (rc != LM_OK) return rc;
+  const int fpb = pcm_frames_per_tile(p, in_dtype == LM_I16);
+  const int rows = pcm_min_rows_per_tile(p, in_dtype == LM_I16);
   const int64_t tiles = (F + fpb - 1) / fpb;
   if (tiles > INT32_MAX || n_clips * tiles > INT32_MAX) return fail(LM_ERR_UNSUPPORTED, "input too large");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  int rc = ensure_device(p);
-  if (rc == LM_OK) rc = upload_tables(p);
-  if (rc == LM_OK) rc = ensure_workspace(p, n_clips, n_clips * tiles, s);
+  rc = ensure_workspace(p, n_clips, n_clips * tiles * rows, s);
   if (rc != LM_OK) return rc;
 
   PcmArgs a{pcm, in_dtype == LM_I16, n_clips, n_samples, F, (int)tiles, out, p->d_hi, p->d_tile_min};
@@ -179,7 +186,8 @@ int lm_from_pcm(lm_plan *p, const void *pcm, int in_dtype, int64_t n_clips, int6
     p->ws_dirty = true;
     return rc;
   }
-  FixupArgs fx{out, p->out_dtype == LM_F16, p->d_hi, p->d_tile_min, n_clips, F, p->n_mels, fpb, (int)tiles, 1};
+  FixupArgs fx{out, p->out_dtype == LM_F16, p->d_hi, p->d_hi + p->hi_cap, p->d_tile_min, n_clips, F,
+               p->n_mels, fpb, (int)tiles, 1, rows};
   rc = timed_launch(p, s, 1, "launch(clamp fix-up)", [&] { return launch_fixup(fx, s); });
   if (rc != LM_OK) p->ws_dirty = true;
   return rc;
@@ -214,6 +222,7 @@ int lm_from_stft(lm_plan *p, const void *stft, const float *mel_filters, int64_t
 
   const int32_t *cs, *cw, *co;
   const float *w;
+  int w_len;
   if (mel_filters) {
     const size_t need = sizeof(int32_t) * 3 * n_mels + sizeof(float) * (size_t)n_mels * n_bins;
     if (need > p->pack_cap) {
@@ -234,21 +243,23 @@ int lm_from_stft(lm_plan *p, const void *stft, const float *mel_filters, int64_t
     cw = cs + n_mels;
     co = cw + n_mels;
     w = reinterpret_cast<const float *>(co + n_mels);
+    w_len = n_mels * (int)n_bins;
   } else {
     cs = p->dt.csr_start;
     cw = p->dt.csr_width;
     co = p->dt.csr_off;
     w = p->dt.csr_w;
+    w_len = p->dt.nnz;
   }
   StftArgs a{reinterpret_cast<const float2 *>(stft), n_clips, n_frames, (int)n_bins, n_mels, tf, (int)tiles,
-             cs, cw, co, w, n_mels * (int)n_bins, out, p->out_dtype == LM_F16, p->d_hi, p->d_tile_min};
+             cs, cw, co, w, w_len, out, p->out_dtype == LM_F16, p->d_hi, p->d_tile_min};
   rc = timed_launch(p, s, 0, "launch(stft kernel)", [&] { return launch_stft(a, s); });
   if (rc != LM_OK) {
     p->ws_dirty = true;
     return rc;
   }
-  FixupArgs fx{out, p->out_dtype == LM_F16, p->d_hi, p->d_tile_min, n_clips, n_frames, n_mels, tf,
-               (int)tiles, 0};
+  FixupArgs fx{out, p->out_dtype == LM_F16, p->d_hi, p->d_hi + p->hi_cap, p->d_tile_min, n_clips, n_frames,
+               n_mels, tf, (int)tiles, 0, 1};
   rc = timed_launch(p, s, 1, "launch(clamp fix-up)", [&] { return launch_fixup(fx, s); });
   if (rc != LM_OK) p->ws_dirty = true;
   return rc;

@@ -204,4 +204,32 @@ __device__ __forceinline__ void block_maxmin(float &vmax, float &lmin, float *re
   }
 }
 
+// ---------------------------------------------------------------------------
+// Packed filterbank staging
+// ---------------------------------------------------------------------------
+
+// Row m of a packed filterbank covers bins [start[m], start[m] + width[m])
+// with weights w[off[m] + j]; rows are stored back to back, so the weight
+// count is off[NM-1] + width[NM-1] and `w` holds w_len >= that many floats.
+// All loads are independent (the first min(cap, w_len) weights are copied
+// whatever the count); one barrier.  Weights are read from LDS when the
+// returned count is <= cap, else from global memory.  NM <= 256.
+template <int THREADS>
+__device__ __forceinline__ int stage_filters(int NM, const int32_t *__restrict__ start,
+                                             const int32_t *__restrict__ width,
+                                             const int32_t *__restrict__ off, const float *__restrict__ w,
+                                             int w_len, int32_t *s_start, int32_t *s_width, int32_t *s_off,
+                                             float *s_w, int cap) {
+  const int tid = threadIdx.x;
+  for (int m = tid; m < NM; m += THREADS) {
+    s_start[m] = start[m];
+    s_width[m] = width[m];
+    s_off[m] = off[m];
+  }
+  const int n = min(cap, w_len);
+  for (int i = tid; i < n; i += THREADS) s_w[i] = w[i];
+  __syncthreads();
+  return s_off[NM - 1] + s_width[NM - 1];
+}
+
 }  // namespace lm

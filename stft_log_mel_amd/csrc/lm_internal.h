@@ -37,6 +37,7 @@ struct DeviceTables {
   const int32_t *csr_start = nullptr, *csr_width = nullptr, *csr_off = nullptr;
   const float *csr_w = nullptr;
   int nnz = 0;
+  const float *mfma400 = nullptr;   // n_fft = 400 only
 };
 
 struct ProfileRec {
@@ -56,13 +57,14 @@ struct lm_plan {
   std::vector<float> window;      // n_fft
   std::vector<float> twiddle;     // 2 * M
   std::vector<float> untangle;    // 2 * (M/2 + 1)
+  std::vector<float> mfma400;     // n_fft = 400 only: 25 x 64 x 4 matrix-core operands
 
   int device = -1;                // bound at first launch
   bool tables_dirty = true;
   lm::DeviceTables dt;
 
   // workspace: per-clip max bits and per-tile minimum log value
-  uint32_t *d_hi = nullptr;
+  uint32_t *d_hi = nullptr;       // [hi_cap] max bits, then [hi_cap] fix-up counters
   size_t hi_cap = 0;
   float *d_tile_min = nullptr;
   size_t tile_cap = 0;
@@ -71,6 +73,7 @@ struct lm_plan {
   size_t pack_cap = 0;
 
   bool ws_dirty = false;         // hi_bits must be cleared before the next call
+  bool force_generic = false;    // LM_FORCE_GENERIC=1: skip the specialised PCM kernels
 
   bool profiling = false;
   std::vector<lm::ProfileRec> prof;
@@ -86,6 +89,7 @@ int upload_tables(lm_plan *p);
 // Host table builders (lm_plan.cpp)
 void build_window(lm_plan *p);
 void build_twiddles(lm_plan *p);
+void build_mfma400(lm_plan *p);
 Csr pack_dense(const float *dense, int n_rows, int n_bins);
 
 // Kernel launchers.  Each returns hipSuccess or the launch error.
@@ -98,9 +102,17 @@ struct PcmArgs {
   uint32_t *hi_bits;
   float *tile_min;
 };
-// Frames per workgroup tile the PCM kernel uses for this n_fft.
-int pcm_frames_per_tile(int n_fft);
+// Frames per workgroup tile of the PCM kernel launch_pcm picks for this
+// plan and input type (the n_fft = 400 matrix-core kernel when it applies,
+// else the generic one).
+int pcm_frames_per_tile(const lm_plan *p, bool in_i16);
 hipError_t launch_pcm(const lm_plan *p, const PcmArgs &a, hipStream_t s);
+bool pcm400_supported(const lm_plan *p, bool in_i16);
+int pcm400_frames_per_tile();
+int pcm400_min_rows_per_tile(const lm_plan *p);
+// entries of tile_min per tile the PCM kernel launch_pcm picks writes
+int pcm_min_rows_per_tile(const lm_plan *p, bool in_i16);
+hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &a, hipStream_t s);
 
 struct StftArgs {
   const float2 *stft;
@@ -109,7 +121,7 @@ struct StftArgs {
   int frames_per_tile, tiles_per_clip;
   const int32_t *csr_start, *csr_width, *csr_off;
   const float *csr_w;
-  int nnz_cap;          // upper bound of the packed weight count
+  int w_len;            // floats allocated at csr_w (>= the packed weight count)
   void *out;
   int out_f16;
   uint32_t *hi_bits;
@@ -118,20 +130,24 @@ struct StftArgs {
 int stft_frames_per_tile(int n_bins, int n_mels);
 hipError_t launch_stft(const StftArgs &a, hipStream_t s);
 
-// Pack a device dense (n_mels, n_bins) filterbank into CSR arrays laid out
-// in `ws` as [start n_mels][width n_mels][off n_mels][w n_mels*n_bins].
+// Pack a device dense (n_mels, n_bins) filterbank into `ws` laid out as
+// [start n_mels][width n_mels][off n_mels] int32 then [w n_mels*n_bins] f32
+// (rows back to back, row m's weights at w[off[m] + j], j < width[m]).
 hipError_t launch_pack(const float *dense, int n_mels, int n_bins, void *ws, hipStream_t s);
 
 struct FixupArgs {
   void *out;
   int out_f16;
   uint32_t *hi_bits;
+  uint32_t *done;         // per-clip finished-workgroup counters (zero between calls)
   const float *tile_min;
   int64_t n_clips, n_frames;
   int n_mels;
   int frames_per_tile, tiles_per_clip;
   int mel_major;  // 1: (B, NM, F); 0: (B, F, NM)
+  int rows_per_tile;                              // entries of tile_min per tile: 1 or n_mels (mel-major)
+  int tiles_per_group = 0, groups_per_clip = 0;   // set by launch_fixup
 };
-hipError_t launch_fixup(const FixupArgs &a, hipStream_t s);
+hipError_t launch_fixup(FixupArgs a, hipStream_t s);
 
 }  // namespace lm

@@ -155,14 +155,9 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
 
   // packed filterbank -> LDS
   const int NM = a.n_mels;
-  const bool w_in_lds = a.nnz <= kCsrLdsMax;
-  for (int m = tid; m < NM; m += THREADS) {
-    s_start[m] = a.csr_start[m];
-    s_width[m] = a.csr_width[m];
-    s_off[m] = a.csr_off[m];
-  }
-  if (w_in_lds)
-    for (int i = tid; i < a.nnz; i += THREADS) s_w[i] = a.csr_w[i];
+  const int nnz = stage_filters<THREADS>(NM, a.csr_start, a.csr_width, a.csr_off, a.csr_w, a.nnz, s_start, s_width,
+                                         s_off, s_w, kCsrLdsMax);
+  const bool w_in_lds = nnz <= kCsrLdsMax;
 
   // 1. windowed, padded frame samples as M complex points per frame
   const float2 *__restrict__ win2 = reinterpret_cast<const float2 *>(a.window);
@@ -236,13 +231,11 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
     const int fl = o % FPB, m = o / FPB;
     const int64_t fr = f0 + fl;
     if (fr >= F) continue;
-    const int st = s_start[m], wd = s_width[m], of = s_off[m];
+    const int st = s_start[m], wd = s_width[m];
     const float *pr = P + fl * (M + 1) + st;
     float acc = 0.0f;
-    if (w_in_lds)
-      for (int j = 0; j < wd; ++j) acc = __builtin_fmaf(s_w[of + j], pr[j], acc);
-    else
-      for (int j = 0; j < wd; ++j) acc = __builtin_fmaf(a.csr_w[of + j], pr[j], acc);
+    const float *wr = (w_in_lds ? s_w : a.csr_w) + s_off[m];
+    for (int j = 0; j < wd; ++j) acc = __builtin_fmaf(wr[j], pr[j], acc);
     const float v = fmaxf(acc * a.mel_scale, 1e-10f);
     const float L = log10_pos(v);
     vmax = fmaxf(vmax, v);
@@ -269,7 +262,7 @@ static hipError_t launch_n(const PcmKernelArgs &k, bool i16, bool f16, int64_t n
   return hipGetLastError();
 }
 
-int pcm_frames_per_tile(int n_fft) {
+static int generic_frames_per_tile(int n_fft) {
   switch (n_fft) {
     case 400: return PcmCfg<400>::FPB;
     case 64: return PcmCfg<64>::FPB;
@@ -285,7 +278,18 @@ int pcm_frames_per_tile(int n_fft) {
   }
 }
 
+static bool use_pcm400(const lm_plan *p, bool in_i16) { return !p->force_generic && pcm400_supported(p, in_i16); }
+
+int pcm_frames_per_tile(const lm_plan *p, bool in_i16) {
+  return use_pcm400(p, in_i16) ? pcm400_frames_per_tile() : generic_frames_per_tile(p->n_fft);
+}
+
+int pcm_min_rows_per_tile(const lm_plan *p, bool in_i16) {
+  return use_pcm400(p, in_i16) ? pcm400_min_rows_per_tile(p) : 1;
+}
+
 hipError_t launch_pcm(const lm_plan *p, const PcmArgs &a, hipStream_t s) {
+  if (use_pcm400(p, a.in_i16)) return launch_pcm400(p, a, s);
   PcmKernelArgs k;
   k.pcm = a.pcm;
   k.T = a.n_samples;

@@ -3,6 +3,7 @@
 // the host in float64 and rounds once to float32; no HIP call is made.
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 
@@ -60,6 +61,48 @@ void build_twiddles(lm_plan *p) {
     const double a = 2.0 * M_PI * (double)k / (double)N;
     p->untangle[2 * k] = (float)std::cos(a);
     p->untangle[2 * k + 1] = (float)-std::sin(a);
+  }
+}
+
+// Operand tables of the n_fft = 400 kernel's matrix-core stage.  The frame
+// is folded to z[n] = w[2n] x[2n] + i w[2n+1] x[2n+1], n < 200 = 25 * 8, and
+// for each n1 < 25 the eight points z[n1 + 25 n2] go through one real 16x16
+// matrix that applies the window, the 8-point DFT over n2 and the twiddle
+// exp(-2 pi i k2 n1 / 200):
+//   out[k2] = sum_n2 z[n1 + 25 n2] exp(-2 pi i k2 (n1 + 25 n2) / 200).
+// Rows (outputs) are ordered so that lane group g = row / 4 holds the
+// classes (1,7), (2,6), (3,5), (0,4) as (re a, im a, re b, im b); columns
+// (inputs) are r = n2 + 8 e for sample x[2 (n1 + 25 n2) + e].  Stored per
+// n1 in matrix-core lane order: entry [n1][lane][j] = M_n1[lane % 16][4 j +
+// lane / 16].
+void build_mfma400(lm_plan *p) {
+  static const int kPairs[4][2] = {{1, 7}, {2, 6}, {3, 5}, {0, 4}};
+  p->mfma400.assign(25 * 64 * 4, 0.0f);
+  const double *w = nullptr;
+  std::vector<double> win(400);
+  for (int n = 0; n < 400; ++n) win[n] = 0.5 - 0.5 * std::cos(2.0 * M_PI * (double)n / 400.0);
+  w = win.data();
+  for (int n1 = 0; n1 < 25; ++n1) {
+    double M[16][16];
+    for (int m = 0; m < 16; ++m) {
+      const int g = m / 4, isb = (m / 2) & 1, part = m & 1;
+      const int k2 = kPairs[g][isb];
+      for (int r = 0; r < 16; ++r) {
+        const int n2 = r & 7, e = r >> 3;
+        const int n = n1 + 25 * n2;
+        const long ang = ((long)k2 * n) % 200;
+        const double th = 2.0 * M_PI * (double)ang / 200.0;
+        const double cr = std::cos(th), ci = -std::sin(th);
+        const double we = w[2 * n], wo = w[2 * n + 1];
+        double v;
+        if (part == 0) v = (e == 0) ? we * cr : -wo * ci;   // real part
+        else v = (e == 0) ? we * ci : wo * cr;              // imaginary part
+        M[m][r] = v;
+      }
+    }
+    for (int lane = 0; lane < 64; ++lane)
+      for (int j = 0; j < 4; ++j)
+        p->mfma400[((size_t)n1 * 64 + lane) * 4 + j] = (float)M[lane % 16][4 * j + lane / 16];
   }
 }
 
@@ -149,8 +192,11 @@ int lm_plan_create(lm_plan **plan, int n_fft, int hop, int n_mels, int center, i
   p->power = power;
   p->out_dtype = out_dtype;
   p->n_bins = n_fft / 2 + 1;
+  const char *fg = std::getenv("LM_FORCE_GENERIC");
+  p->force_generic = fg && fg[0] == '1';
   build_window(p);
   build_twiddles(p);
+  if (n_fft == 400) build_mfma400(p);
   *plan = p;
   return LM_OK;
 }

@@ -27,6 +27,7 @@ struct StftKernelArgs {
   int NF, NM, TF, tiles_per_clip;
   const int32_t *csr_start, *csr_width, *csr_off;
   const float *csr_w;
+  int w_len;
   void *out;
   uint32_t *hi_bits;
   float *tile_min;
@@ -81,17 +82,10 @@ __global__ void __launch_bounds__(kStftThreads) stft_logmel_kernel(StftKernelArg
     for (int i = tid; i < n; i += kStftThreads) P[i] = pw(a.stft[e0 + i]);
   }
 
-  // packed filterbank -> LDS
-  for (int m = tid; m < NM; m += kStftThreads) {
-    s_start[m] = a.csr_start[m];
-    s_width[m] = a.csr_width[m];
-    s_off[m] = a.csr_off[m];
-  }
-  const int nnz = a.csr_off[NM - 1] + a.csr_width[NM - 1];
+  // packed filterbank -> LDS (ends with a barrier, which also covers the power tile)
+  const int nnz = stage_filters<kStftThreads>(NM, a.csr_start, a.csr_width, a.csr_off, a.csr_w, a.w_len, s_start,
+                                              s_width, s_off, s_w, kStftCsrLds);
   const bool w_in_lds = nnz <= kStftCsrLds;
-  if (w_in_lds)
-    for (int i = tid; i < nnz; i += kStftThreads) s_w[i] = a.csr_w[i];
-  __syncthreads();
 
   // 2. mel sums, log10, rescale, frame-major store
   OUT *__restrict__ out = reinterpret_cast<OUT *>(a.out) + (b * a.F + f0) * NM;
@@ -99,13 +93,11 @@ __global__ void __launch_bounds__(kStftThreads) stft_logmel_kernel(StftKernelArg
   int m = tid % NM, f = tid / NM;
   const int dm = kStftThreads % NM, df = kStftThreads / NM;
   for (int o = tid; o < nfr * NM; o += kStftThreads) {
-    const int st = s_start[m], wd = s_width[m], of = s_off[m];
+    const int st = s_start[m], wd = s_width[m];
     const float *pr = P + f * NF + st;
     float acc = 0.0f;
-    if (w_in_lds)
-      for (int j = 0; j < wd; ++j) acc = __builtin_fmaf(s_w[of + j], pr[j], acc);
-    else
-      for (int j = 0; j < wd; ++j) acc = __builtin_fmaf(a.csr_w[of + j], pr[j], acc);
+    const float *wr = (w_in_lds ? s_w : a.csr_w) + s_off[m];
+    for (int j = 0; j < wd; ++j) acc = __builtin_fmaf(wr[j], pr[j], acc);
     const float v = fmaxf(acc, 1e-10f);
     const float L = log10_pos(v);
     vmax = fmaxf(vmax, v);
@@ -147,6 +139,7 @@ hipError_t launch_stft(const StftArgs &a, hipStream_t s) {
   k.csr_width = a.csr_width;
   k.csr_off = a.csr_off;
   k.csr_w = a.csr_w;
+  k.w_len = a.w_len;
   k.out = a.out;
   k.hi_bits = a.hi_bits;
   k.tile_min = a.tile_min;
@@ -164,51 +157,87 @@ hipError_t launch_stft(const StftArgs &a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Dense (NM, NF) device filterbank -> packed rows.  One workgroup: each wave
-// finds the first and last non-zero of its rows, one thread lays out the
-// row offsets, then the waves copy each row's [first, last] range.
+// Dense (NM, NF) device filterbank -> packed rows (start, width, off, w),
+// the same layout as a plan's own table.  One workgroup of 16 waves: each
+// wave issues the loads of all its rows at once and reduces each row's
+// first and last non-zero; wave 0 lays out the offsets; then each wave
+// copies its rows' [first, last] weights.
 // ---------------------------------------------------------------------------
 
 constexpr int kPackThreads = 1024;
+constexpr int kPackWaves = kPackThreads / 64;
+constexpr int kPackRowsPerWave = 256 / kPackWaves;   // NM <= 256
 
 __global__ void __launch_bounds__(kPackThreads)
 pack_filters_kernel(const float *__restrict__ dense, int NM, int NF, int32_t *start, int32_t *width,
                     int32_t *off, float *w) {
   __shared__ int s_first[256], s_last[256], s_off[256];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  constexpr int NWV = kPackThreads / 64;
-  for (int m = wv; m < NM; m += NWV) {
-    int first = INT_MAX, last = -1;
-    const float *row = dense + (size_t)m * NF;
-    for (int k = lane; k < NF; k += 64)
-      if (row[k] != 0.0f) {
-        first = min(first, k);
-        last = max(last, k);
+  int first[kPackRowsPerWave], last[kPackRowsPerWave];
+#pragma unroll
+  for (int r = 0; r < kPackRowsPerWave; ++r) {
+    first[r] = INT_MAX;
+    last[r] = -1;
+  }
+  for (int k0 = 0; k0 < NF; k0 += 64) {
+    const int k = k0 + lane;
+    float v[kPackRowsPerWave];
+#pragma unroll
+    for (int r = 0; r < kPackRowsPerWave; ++r) {
+      const int m = wv + r * kPackWaves;
+      v[r] = (m < NM && k < NF) ? dense[(size_t)m * NF + k] : 0.0f;
+    }
+#pragma unroll
+    for (int r = 0; r < kPackRowsPerWave; ++r)
+      if (v[r] != 0.0f) {
+        first[r] = min(first[r], k);
+        last[r] = max(last[r], k);
       }
+  }
+#pragma unroll
+  for (int r = 0; r < kPackRowsPerWave; ++r) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-      first = min(first, __shfl_xor(first, o, 64));
-      last = max(last, __shfl_xor(last, o, 64));
+      first[r] = min(first[r], __shfl_xor(first[r], o, 64));
+      last[r] = max(last[r], __shfl_xor(last[r], o, 64));
     }
-    if (lane == 0) {
-      s_first[m] = first;
-      s_last[m] = last;
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int o = 0;
-    for (int m = 0; m < NM; ++m) {
-      const int wd = s_last[m] >= 0 ? s_last[m] - s_first[m] + 1 : 0;
-      s_off[m] = o;
-      start[m] = wd ? s_first[m] : 0;
-      width[m] = wd;
-      off[m] = o;
-      o += wd;
+    const int m = wv + r * kPackWaves;
+    if (lane == 0 && m < NM) {
+      s_first[m] = first[r];
+      s_last[m] = last[r];
     }
   }
   __syncthreads();
-  for (int m = wv; m < NM; m += NWV) {
+  if (threadIdx.x < 64) {
+    const int tid = threadIdx.x;
+    int wd[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * tid + i;
+      wd[i] = (m < NM && s_last[m] >= 0) ? s_last[m] - s_first[m] + 1 : 0;
+      sum += wd[i];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o, 64);
+      if (tid >= o) incl += t;
+    }
+    int run = incl - sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * tid + i;
+      if (m < NM) {
+        s_off[m] = run;
+        start[m] = wd[i] ? s_first[m] : 0;
+        width[m] = wd[i];
+        off[m] = run;
+      }
+      run += wd[i];
+    }
+  }
+  __syncthreads();
+  for (int m = wv; m < NM; m += kPackWaves) {
     if (s_last[m] < 0) continue;
     const int st = s_first[m], wd = s_last[m] - st + 1, o = s_off[m];
     for (int j = lane; j < wd; j += 64) w[o + j] = dense[(size_t)m * NF + st + j];
@@ -220,8 +249,8 @@ hipError_t launch_pack(const float *dense, int n_mels, int n_bins, void *ws, hip
   int32_t *width = start + n_mels;
   int32_t *off = width + n_mels;
   float *w = reinterpret_cast<float *>(off + n_mels);
-  hipLaunchKernelGGL(pack_filters_kernel, dim3(1), dim3(kPackThreads), 0, s, dense, n_mels, n_bins, start,
-                     width, off, w);
+  hipLaunchKernelGGL(pack_filters_kernel, dim3(1), dim3(kPackThreads), 0, s, dense, n_mels, n_bins, start, width,
+                     off, w);
   return hipGetLastError();
 }
 

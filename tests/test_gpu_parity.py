@@ -303,3 +303,19 @@ def test_melspectrogram_wrapper_shapes():
     check(y, ref, TOL32, "wrapper")
     with pytest.raises(RuntimeError):
         m(to_dev(x[0]).requires_grad_(True))
+
+
+@pytest.mark.parametrize("hop,in_dtype", [(160, "f32"), (160, "i16"), (161, "f32"), (200, "f32"), (320, "i16")])
+def test_pcm400_fast_and_generic_paths(hop, in_dtype, monkeypatch):
+    """n_fft = 400 runs on the matrix-core kernel when the hop is even and the
+    tile's span fits in LDS, else on the generic kernel; LM_FORCE_GENERIC=1
+    selects the generic kernel.  Both must match the oracle."""
+    import os
+    B, T = 3, 24321
+    x = lm_synth.speech_pcm(B, T, 16000.0, seed=hop, as_int16=(in_dtype == "i16"))
+    ref = oracle_pcm(x, 400, hop, 128, 16000.0)
+    for force in ("0", "1"):
+        monkeypatch.setenv("LM_FORCE_GENERIC", force)
+        say("pcm400 path", hop, in_dtype, "force_generic", force)
+        out = run_pcm(x, 400, hop, 128, 16000.0)
+        check(out, ref, TOL32, f"hop {hop} {in_dtype} generic={force}")
