@@ -30,7 +30,9 @@ int upload_tables(lm_plan *p) {
   size_t o_of = align256(o_wd + sizeof(int32_t) * NM);
   size_t o_w = align256(o_of + sizeof(int32_t) * NM);
   size_t o_mf = align256(o_w + sizeof(float) * (nnz > 0 ? nnz : 1));
-  size_t total = align256(o_mf + sizeof(float) * p->mfma400.size());
+  size_t o_bm = align256(o_mf + sizeof(float) * p->mfma400.size());
+  size_t o_bw = align256(o_bm + sizeof(int32_t) * p->melblk_meta.size());
+  size_t total = align256(o_bw + sizeof(float) * p->melblk_w.size() + 16);
   std::vector<unsigned char> host(total, 0);
   std::memcpy(host.data() + o_win, p->window.data(), sizeof(float) * N);
   std::memcpy(host.data() + o_tw, p->twiddle.data(), sizeof(float) * 2 * M);
@@ -43,6 +45,10 @@ int upload_tables(lm_plan *p) {
   }
   if (!p->mfma400.empty())
     std::memcpy(host.data() + o_mf, p->mfma400.data(), sizeof(float) * p->mfma400.size());
+  if (p->have_filters) {
+    std::memcpy(host.data() + o_bm, p->melblk_meta.data(), sizeof(int32_t) * p->melblk_meta.size());
+    std::memcpy(host.data() + o_bw, p->melblk_w.data(), sizeof(float) * p->melblk_w.size());
+  }
   if (p->dt.base) {
     hipError_t e = hipFree(p->dt.base);
     p->dt.base = nullptr;
@@ -68,44 +74,26 @@ int upload_tables(lm_plan *p) {
   p->dt.csr_w = reinterpret_cast<const float *>(c + o_w);
   p->dt.nnz = nnz;
   p->dt.mfma400 = p->mfma400.empty() ? nullptr : reinterpret_cast<const float *>(c + o_mf);
+  p->dt.melblk_meta = reinterpret_cast<const int32_t *>(c + o_bm);
+  p->dt.melblk_w = reinterpret_cast<const float *>(c + o_bw);
+  p->dt.n_melblk = p->have_filters ? (int)(p->melblk_meta.size() / 3) : 0;
   p->tables_dirty = false;
   return LM_OK;
 }
 
-// hi_bits and the fix-up counters (d_hi[hi_cap ..]) must be zero when a
-// call starts; the fix-up kernel clears both at the end of every call, and
-// a fresh (or previously failed) buffer is cleared here on the caller's
-// stream.
-int ensure_workspace(lm_plan *p, int64_t n_clips, int64_t n_tiles, hipStream_t s) {
-  hipError_t e;
-  if ((size_t)n_clips > p->hi_cap) {
-    if (p->d_hi) {
-      e = hipFree(p->d_hi);
-      p->d_hi = nullptr;
-      p->hi_cap = 0;
-      if (e != hipSuccess) return hip_fail(e, "hipFree(workspace)");
-    }
-    e = hipMalloc(reinterpret_cast<void **>(&p->d_hi), 2 * sizeof(uint32_t) * n_clips);
-    if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
-    p->hi_cap = n_clips;
-    p->ws_dirty = true;
+// Per-(sub-)tile statistics: minima then maxima, each n_entries floats.
+// Every call overwrites all of its entries, so nothing needs clearing.
+int ensure_workspace(lm_plan *p, int64_t n_entries) {
+  if ((size_t)n_entries <= p->tile_cap) return LM_OK;
+  if (p->d_tile_min) {
+    hipError_t e = hipFree(p->d_tile_min);
+    p->d_tile_min = nullptr;
+    p->tile_cap = 0;
+    if (e != hipSuccess) return hip_fail(e, "hipFree(workspace)");
   }
-  if (p->ws_dirty) {
-    e = hipMemsetAsync(p->d_hi, 0, 2 * sizeof(uint32_t) * p->hi_cap, s);
-    if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync(workspace)");
-    p->ws_dirty = false;
-  }
-  if ((size_t)n_tiles > p->tile_cap) {
-    if (p->d_tile_min) {
-      e = hipFree(p->d_tile_min);
-      p->d_tile_min = nullptr;
-      p->tile_cap = 0;
-      if (e != hipSuccess) return hip_fail(e, "hipFree(workspace)");
-    }
-    e = hipMalloc(reinterpret_cast<void **>(&p->d_tile_min), sizeof(float) * n_tiles);
-    if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
-    p->tile_cap = n_tiles;
-  }
+  hipError_t e = hipMalloc(reinterpret_cast<void **>(&p->d_tile_min), 2 * sizeof(float) * n_entries);
+  if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
+  p->tile_cap = n_entries;
   return LM_OK;
 }
 
@@ -177,20 +165,15 @@ int lm_from_pcm(lm_plan *p, const void *pcm, int in_dtype, int64_t n_clips, int6
   const int64_t tiles = (F + fpb - 1) / fpb;
   if (tiles > INT32_MAX || n_clips * tiles > INT32_MAX) return fail(LM_ERR_UNSUPPORTED, "input too large");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  rc = ensure_workspace(p, n_clips, n_clips * tiles * rows, s);
+  rc = ensure_workspace(p, n_clips * tiles * rows);
   if (rc != LM_OK) return rc;
+  float *tmin = p->d_tile_min, *tmax = p->d_tile_min + p->tile_cap;
 
-  PcmArgs a{pcm, in_dtype == LM_I16, n_clips, n_samples, F, (int)tiles, out, p->d_hi, p->d_tile_min};
+  PcmArgs a{pcm, in_dtype == LM_I16, n_clips, n_samples, F, (int)tiles, out, tmin, tmax};
   rc = timed_launch(p, s, 0, "launch(pcm kernel)", [&] { return launch_pcm(p, a, s); });
-  if (rc != LM_OK) {
-    p->ws_dirty = true;
-    return rc;
-  }
-  FixupArgs fx{out, p->out_dtype == LM_F16, p->d_hi, p->d_hi + p->hi_cap, p->d_tile_min, n_clips, F,
-               p->n_mels, fpb, (int)tiles, 1, rows};
-  rc = timed_launch(p, s, 1, "launch(clamp fix-up)", [&] { return launch_fixup(fx, s); });
-  if (rc != LM_OK) p->ws_dirty = true;
-  return rc;
+  if (rc != LM_OK) return rc;
+  FixupArgs fx{out, p->out_dtype == LM_F16, tmin, tmax, n_clips, F, p->n_mels, fpb, (int)tiles, 1, rows};
+  return timed_launch(p, s, 1, "launch(clamp fix-up)", [&] { return launch_fixup(fx, s); });
 }
 
 int lm_from_stft(lm_plan *p, const void *stft, const float *mel_filters, int64_t n_clips, int64_t n_frames,
@@ -217,8 +200,9 @@ int lm_from_stft(lm_plan *p, const void *stft, const float *mel_filters, int64_t
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   int rc = ensure_device(p);
   if (rc == LM_OK && !mel_filters) rc = upload_tables(p);
-  if (rc == LM_OK) rc = ensure_workspace(p, n_clips, n_clips * tiles, s);
+  if (rc == LM_OK) rc = ensure_workspace(p, n_clips * tiles);
   if (rc != LM_OK) return rc;
+  float *tmin = p->d_tile_min, *tmax = p->d_tile_min + p->tile_cap;
 
   const int32_t *cs, *cw, *co;
   const float *w;
@@ -252,17 +236,11 @@ int lm_from_stft(lm_plan *p, const void *stft, const float *mel_filters, int64_t
     w_len = p->dt.nnz;
   }
   StftArgs a{reinterpret_cast<const float2 *>(stft), n_clips, n_frames, (int)n_bins, n_mels, tf, (int)tiles,
-             cs, cw, co, w, w_len, out, p->out_dtype == LM_F16, p->d_hi, p->d_tile_min};
+             cs, cw, co, w, w_len, out, p->out_dtype == LM_F16, tmin, tmax};
   rc = timed_launch(p, s, 0, "launch(stft kernel)", [&] { return launch_stft(a, s); });
-  if (rc != LM_OK) {
-    p->ws_dirty = true;
-    return rc;
-  }
-  FixupArgs fx{out, p->out_dtype == LM_F16, p->d_hi, p->d_hi + p->hi_cap, p->d_tile_min, n_clips, n_frames,
-               n_mels, tf, (int)tiles, 0, 1};
-  rc = timed_launch(p, s, 1, "launch(clamp fix-up)", [&] { return launch_fixup(fx, s); });
-  if (rc != LM_OK) p->ws_dirty = true;
-  return rc;
+  if (rc != LM_OK) return rc;
+  FixupArgs fx{out, p->out_dtype == LM_F16, tmin, tmax, n_clips, n_frames, n_mels, tf, (int)tiles, 0, 1};
+  return timed_launch(p, s, 1, "launch(clamp fix-up)", [&] { return launch_fixup(fx, s); });
 }
 
 int lm_plan_profile(lm_plan *p, int enable) {
@@ -301,7 +279,6 @@ void lm_plan_destroy(lm_plan *p) {
     (void)hipEventDestroy(r.end);
   }
   if (p->dt.base) (void)hipFree(p->dt.base);
-  if (p->d_hi) (void)hipFree(p->d_hi);
   if (p->d_tile_min) (void)hipFree(p->d_tile_min);
   if (p->d_pack) (void)hipFree(p->d_pack);
   delete p;

@@ -8,7 +8,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/lm.h"
+#include "lm.h"
 
 namespace lm {
 
@@ -38,6 +38,9 @@ struct DeviceTables {
   const float *csr_w = nullptr;
   int nnz = 0;
   const float *mfma400 = nullptr;   // n_fft = 400 only
+  const int32_t *melblk_meta = nullptr;
+  const float *melblk_w = nullptr;
+  int n_melblk = 0;
 };
 
 struct ProfileRec {
@@ -58,21 +61,20 @@ struct lm_plan {
   std::vector<float> twiddle;     // 2 * M
   std::vector<float> untangle;    // 2 * (M/2 + 1)
   std::vector<float> mfma400;     // n_fft = 400 only: 25 x 64 x 4 matrix-core operands
+  std::vector<int32_t> melblk_meta;  // per 16-band block: klo, chunks, offset
+  std::vector<float> melblk_w;       // blocked filter weights in matrix-core lane order
 
   int device = -1;                // bound at first launch
   bool tables_dirty = true;
   lm::DeviceTables dt;
 
-  // workspace: per-clip max bits and per-tile minimum log value
-  uint32_t *d_hi = nullptr;       // [hi_cap] max bits, then [hi_cap] fix-up counters
-  size_t hi_cap = 0;
-  float *d_tile_min = nullptr;
+  // workspace: per-(sub-)tile smallest log value and largest mel value
+  float *d_tile_min = nullptr;    // [tile_cap] minima, then [tile_cap] maxima
   size_t tile_cap = 0;
   // per-call packed copy of a device filterbank (STFT path)
   void *d_pack = nullptr;
   size_t pack_cap = 0;
 
-  bool ws_dirty = false;         // hi_bits must be cleared before the next call
   bool force_generic = false;    // LM_FORCE_GENERIC=1: skip the specialised PCM kernels
 
   bool profiling = false;
@@ -83,13 +85,14 @@ namespace lm {
 
 // Workspace helpers (lm_api.cpp)
 int ensure_device(lm_plan *p);
-int ensure_workspace(lm_plan *p, int64_t n_clips, int64_t n_tiles_total, hipStream_t s);
+int ensure_workspace(lm_plan *p, int64_t n_entries);
 int upload_tables(lm_plan *p);
 
 // Host table builders (lm_plan.cpp)
 void build_window(lm_plan *p);
 void build_twiddles(lm_plan *p);
 void build_mfma400(lm_plan *p);
+void build_mel_blocks(lm_plan *p);
 Csr pack_dense(const float *dense, int n_rows, int n_bins);
 
 // Kernel launchers.  Each returns hipSuccess or the launch error.
@@ -99,8 +102,8 @@ struct PcmArgs {
   int64_t n_clips, n_samples, n_frames;
   int tiles_per_clip;
   void *out;
-  uint32_t *hi_bits;
-  float *tile_min;
+  float *tile_min;   // per (sub-)tile smallest log value
+  float *tile_max;   // per (sub-)tile largest mel value (after the 1e-10 floor)
 };
 // Frames per workgroup tile of the PCM kernel launch_pcm picks for this
 // plan and input type (the n_fft = 400 matrix-core kernel when it applies,
@@ -124,8 +127,8 @@ struct StftArgs {
   int w_len;            // floats allocated at csr_w (>= the packed weight count)
   void *out;
   int out_f16;
-  uint32_t *hi_bits;
   float *tile_min;
+  float *tile_max;
 };
 int stft_frames_per_tile(int n_bins, int n_mels);
 hipError_t launch_stft(const StftArgs &a, hipStream_t s);
@@ -138,15 +141,14 @@ hipError_t launch_pack(const float *dense, int n_mels, int n_bins, void *ws, hip
 struct FixupArgs {
   void *out;
   int out_f16;
-  uint32_t *hi_bits;
-  uint32_t *done;         // per-clip finished-workgroup counters (zero between calls)
   const float *tile_min;
+  const float *tile_max;
   int64_t n_clips, n_frames;
   int n_mels;
   int frames_per_tile, tiles_per_clip;
   int mel_major;  // 1: (B, NM, F); 0: (B, F, NM)
-  int rows_per_tile;                              // entries of tile_min per tile: 1 or n_mels (mel-major)
-  int tiles_per_group = 0, groups_per_clip = 0;   // set by launch_fixup
+  int rows_per_tile;    // entries of tile_min per tile: R sub-tiles of frames_per_tile / R frames
+  int entries_per_group = 0, groups_per_clip = 0;   // set by launch_fixup
 };
 hipError_t launch_fixup(FixupArgs a, hipStream_t s);
 

@@ -14,10 +14,9 @@
 //   4. the packed triangular mel sum per (band, frame), log10 after the
 //      1e-10 floor (KBench task page, "spec_md"), the (L+4)/4 rescale and a
 //      mel-major store (flashmel page, "Usage": (..., n_mels, n_frames));
-//   5. the tile's largest mel value goes to the clip's maximum with one
-//      atomicMax on its float bits (positive floats order like unsigned
-//      integers), its smallest log value to a per-tile slot.  The clamp
-//      fix-up kernel finishes the per-clip floor.
+//   5. the tile's largest mel value and smallest log value go to per-tile
+//      slots; the clamp fix-up kernel reduces them per clip and finishes the
+//      per-clip floor.
 // int16 input is converted to float without its 1/32768 scale; the mel
 // values are scaled by 2^-30 instead (exact), together with the 1/4 of
 // the split above.
@@ -127,8 +126,7 @@ struct PcmKernelArgs {
   const float *csr_w;
   int nnz;
   void *out;
-  uint32_t *hi_bits;
-  float *tile_min;
+  float *tile_min, *tile_max;
 };
 
 // Packed filter weights are staged in LDS when they fit this many floats.
@@ -246,7 +244,7 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
   // 5. tile statistics
   block_maxmin<THREADS>(vmax, lmin, s_red);
   if (tid == 0) {
-    atomicMax(a.hi_bits + b, __float_as_uint(vmax));
+    a.tile_max[tile] = vmax;
     a.tile_min[tile] = lmin;
   }
 }
@@ -318,8 +316,8 @@ hipError_t launch_pcm(const lm_plan *p, const PcmArgs &a, hipStream_t s) {
   k.csr_w = p->dt.csr_w;
   k.nnz = p->dt.nnz;
   k.out = a.out;
-  k.hi_bits = a.hi_bits;
   k.tile_min = a.tile_min;
+  k.tile_max = a.tile_max;
   const int64_t n_tiles = a.n_clips * a.tiles_per_clip;
   const bool f16 = p->out_dtype == LM_F16;
   switch (p->n_fft) {

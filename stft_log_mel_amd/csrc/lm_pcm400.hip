@@ -19,9 +19,9 @@
 //   64 frames of the tile: packed filter weights are wave-uniform (scalar
 //   loads), 64 consecutive frames make one 256-byte store per band
 //   (mel-major output), log10 after the 1e-10 floor, (L+4)/4.
-// The tile's largest mel value joins its clip's maximum (atomicMax on float
-// bits), its smallest log value a per-tile slot; the clamp fix-up kernel
-// finishes the per-clip floor.
+// Each wave's largest mel value and smallest log value go to per-sub-tile
+// slots; the clamp fix-up kernel reduces them per clip and finishes the
+// per-clip floor.
 #include "lm_device.h"
 #include "lm_internal.h"
 
@@ -35,6 +35,7 @@ constexpr int kTileFrames = 64;               // frames per workgroup
 constexpr int kThreads = 256;                 // 4 waves, 16 frames each in the FFT
 constexpr int kRow = 201;                     // power-tile row stride (odd: no bank conflicts)
 constexpr int kLdsFloats = kTileFrames * kRow;
+constexpr int kMelWLds = 4096;                // blocked filter weights staged in LDS up to this count
 
 // compile-time cos/sin of 2 pi j / N for N a multiple of 8 (octant reduction
 // in integers, Taylor series on [0, pi/4]); evaluated in double, rounded once
@@ -126,14 +127,11 @@ struct Args {
   int tiles_per_clip;
   int hop, pad, pad_mode;
   float power, mel_scale, pre_scale;
-  int n_mels;
+  int n_mels, n_melblk;
   const v4f *amat;   // [25][64] operand table of the matrix-core stage
-  const int32_t *csr_start, *csr_width, *csr_off;
-  const float *csr_w;
-  int nnz;
   void *out;
-  uint32_t *hi_bits;
-  float *tile_min;
+  float *tile_max;
+  int melw_lds;   // blocked filter weights staged in LDS (count <= kMelWLds), else 0
 };
 
 __device__ __forceinline__ float to_f(float v) { return v; }
@@ -223,11 +221,12 @@ __device__ __forceinline__ void stage_span(const IN *__restrict__ x, int64_t T, 
 
 template <typename IN, typename OUT>
 __global__ void __launch_bounds__(kThreads, 2)
-pcm400_kernel(Args a, const int32_t *__restrict__ csr_start, const int32_t *__restrict__ csr_width,
-              const int32_t *__restrict__ csr_off, const float *__restrict__ csr_w, OUT *__restrict__ out_base,
-              float *__restrict__ tile_min) {
-  __shared__ __attribute__((aligned(16))) float s_lds[kLdsFloats];   // staged span, then the power tile
-  __shared__ float s_red[kThreads / 64];
+pcm400_kernel(Args a, const int32_t *__restrict__ melblk_meta, const float *__restrict__ melblk_w,
+              OUT *__restrict__ out_base, float *__restrict__ tile_min) {
+  // staged span, then the power tile; 4 zero floats after it are read (with
+  // weight 0) by a filter chunk that runs past the last frame's row
+  __shared__ __attribute__((aligned(16))) float s_lds[kLdsFloats + 4];
+  __shared__ float s_melw[kMelWLds];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
@@ -242,6 +241,8 @@ pcm400_kernel(Args a, const int32_t *__restrict__ csr_start, const int32_t *__re
   const int64_t s_begin = f0 * hop - a.pad;
   const int span = (kTileFrames - 1) * hop + 400;
   const int64_t s_limit = (F - 1) * (int64_t)hop - a.pad + 400;   // end of the last frame of the clip
+  if (tid < 4) s_lds[kLdsFloats + tid] = 0.0f;
+  for (int i = tid; i < a.melw_lds; i += kThreads) s_melw[i] = melblk_w[i];
   stage_span<IN>(x, T, s_begin, span, s_limit, a.pad_mode, reinterpret_cast<uint32_t *>(s_lds));
   __syncthreads();
 
@@ -330,44 +331,51 @@ pcm400_kernel(Args a, const int32_t *__restrict__ csr_start, const int32_t *__re
     if (gen_pow) p100 = powf(p100 * a.pre_scale, pe);
     P[100] = p100;
   }
-  __syncthreads();
+  __syncthreads();   // power rows complete (each wave reads its own frames' rows)
 
-  // 5. mel bands: wave wv takes bands wv, wv+4, ...; lane = frame of the
-  // tile.  Band descriptors and weights are wave-uniform (scalar loads).
-  // The wave's smallest log value over its bands and the tile's frames goes
-  // to tile_min[tile * 4 + wv]: the fix-up's unit is one such band class.
+  // 5. mel sums on the matrix cores, for the wave's own 16 frames: bands in
+  // blocks of 16, each block only over the 4-bin chunks its filters touch.
+  // A = blocked filter weights (lane order), B = P[frame c][bin klo+4ch+g],
+  // D = 16 bands x 16 frames; lane (c, g) gets bands 16j+4g .. 16j+4g+3 of
+  // frame c.  Then log10 after the 1e-10 floor, (L+4)/4, mel-major store.
   const int NM = a.n_mels;
-  const int64_t fr = f0 + lane;
+  const int64_t fr = f0 + fl;
   const bool valid = fr < F;
-  const float *Pl = s_lds + lane * kRow;
-  OUT *__restrict__ optr = out_base + (b * NM + wv) * F + fr;
-  const int64_t ostep = (int64_t)(kThreads / 64) * F;
+  const float *pb0 = s_lds + fl * kRow + g;
+  OUT *__restrict__ ocol = out_base + b * (int64_t)NM * F + fr;
   float vmax = 0.0f, lmin = __builtin_huge_valf();
-  for (int m = wv; m < NM; m += kThreads / 64, optr += ostep) {
-    const int st = csr_start[m], wd = csr_width[m];
-    const float *wr = csr_w + csr_off[m];
-    const float *pr = Pl + st;
-    float acc = 0.0f;
-    for (int jj = 0; jj < wd; ++jj) acc = __builtin_fmaf(wr[jj], pr[jj], acc);
-    const float v = fmaxf(acc * a.mel_scale, 1e-10f);
-    const float L = log10_pos(v);
-    vmax = fmaxf(vmax, v);
-    lmin = fminf(lmin, L);
-    if (valid) store_out(optr, rescale(L));
+  for (int j = 0; j < 16; ++j) {
+    if (j >= a.n_melblk) break;
+    const int klo = melblk_meta[3 * j], nch = melblk_meta[3 * j + 1], toff = melblk_meta[3 * j + 2];
+    const float *wt = (a.melw_lds ? s_melw : melblk_w) + toff + lane;
+    const float *pb = pb0 + klo;
+    v4f acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+    int ch = 0;
+    for (; ch + 1 < nch; ch += 2) {
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(wt[64 * ch], pb[4 * ch], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(wt[64 * ch + 64], pb[4 * ch + 4], acc1, 0, 0, 0);
+    }
+    if (ch < nch) acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(wt[64 * ch], pb[4 * ch], acc0, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 16 * j + 4 * g + r;
+      const float v = fmaxf((acc0[r] + acc1[r]) * a.mel_scale, 1e-10f);
+      const float L = log10_pos(v);
+      if (valid && m < NM) {
+        vmax = fmaxf(vmax, v);
+        lmin = fminf(lmin, L);
+        store_out(ocol + (int64_t)m * F, rescale(L));
+      }
+    }
   }
-  lmin = wave_min(valid ? lmin : __builtin_huge_valf());
-  vmax = wave_max(valid ? vmax : 0.0f);
+
+  // 6. statistics of the wave's 16-frame sub-tile: smallest log value and
+  // largest mel value to entry tile * 4 + wave
+  lmin = wave_min(lmin);
+  vmax = wave_max(vmax);
   if (lane == 0) {
     tile_min[tile * (kThreads / 64) + wv] = lmin;
-    s_red[wv] = vmax;
-  }
-
-  // 6. the tile's largest mel value joins the clip maximum
-  __syncthreads();
-  if (tid == 0) {
-#pragma unroll
-    for (int i = 1; i < kThreads / 64; ++i) vmax = fmaxf(vmax, s_red[i]);
-    atomicMax(a.hi_bits + b, __float_as_uint(vmax));
+    a.tile_max[tile * (kThreads / 64) + wv] = vmax;
   }
 }
 
@@ -376,14 +384,14 @@ pcm400_kernel(Args a, const int32_t *__restrict__ csr_start, const int32_t *__re
 // The n_fft = 400 path needs an even hop (sample pairs stay aligned) and a
 // staged span that fits the power tile's LDS.
 bool pcm400_supported(const lm_plan *p, bool in_i16) {
-  if (p->n_fft != 400 || (p->hop & 1) || !p->dt.mfma400) return false;
+  if (p->n_fft != 400 || (p->hop & 1) || !p->dt.mfma400 || p->n_mels > 256) return false;
   const int span = (kTileFrames - 1) * p->hop + 400;
   const int ndw = in_i16 ? span / 2 : span;
   return (in_i16 ? ndw + (ndw >> 5) : ndw + 2 * (ndw >> 6)) + 2 <= kLdsFloats;
 }
 
 int pcm400_frames_per_tile() { return kTileFrames; }
-int pcm400_min_rows_per_tile(const lm_plan *p) { return p->n_mels < kThreads / 64 ? p->n_mels : kThreads / 64; }
+int pcm400_min_rows_per_tile(const lm_plan *) { return kThreads / 64; }
 
 hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &pa, hipStream_t s) {
   Args k;
@@ -404,28 +412,24 @@ hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &pa, hipStream_t s) {
     k.pre_scale = 0.25f * in_scale2;
   }
   k.n_mels = p->n_mels;
+  k.n_melblk = p->dt.n_melblk;
   k.amat = reinterpret_cast<const v4f *>(p->dt.mfma400);
-  k.csr_start = p->dt.csr_start;
-  k.csr_width = p->dt.csr_width;
-  k.csr_off = p->dt.csr_off;
-  k.csr_w = p->dt.csr_w;
-  k.nnz = p->dt.nnz;
   k.out = pa.out;
-  k.hi_bits = pa.hi_bits;
-  k.tile_min = pa.tile_min;
+  k.tile_max = pa.tile_max;
+  k.melw_lds = p->melblk_w.size() <= (size_t)kMelWLds ? (int)p->melblk_w.size() : 0;
   const dim3 grid((unsigned)(pa.n_clips * pa.tiles_per_clip)), block(kThreads);
   const bool f16 = p->out_dtype == LM_F16;
-  const int32_t *cs = p->dt.csr_start, *cw = p->dt.csr_width, *co = p->dt.csr_off;
-  const float *w = p->dt.csr_w;
+  const int32_t *bm = p->dt.melblk_meta;
+  const float *bw = p->dt.melblk_w;
   float *tm = pa.tile_min;
   if (!pa.in_i16 && !f16)
-    hipLaunchKernelGGL((pcm400_kernel<float, float>), grid, block, 0, s, k, cs, cw, co, w, (float *)pa.out, tm);
+    hipLaunchKernelGGL((pcm400_kernel<float, float>), grid, block, 0, s, k, bm, bw, (float *)pa.out, tm);
   else if (!pa.in_i16 && f16)
-    hipLaunchKernelGGL((pcm400_kernel<float, __half>), grid, block, 0, s, k, cs, cw, co, w, (__half *)pa.out, tm);
+    hipLaunchKernelGGL((pcm400_kernel<float, __half>), grid, block, 0, s, k, bm, bw, (__half *)pa.out, tm);
   else if (pa.in_i16 && !f16)
-    hipLaunchKernelGGL((pcm400_kernel<int16_t, float>), grid, block, 0, s, k, cs, cw, co, w, (float *)pa.out, tm);
+    hipLaunchKernelGGL((pcm400_kernel<int16_t, float>), grid, block, 0, s, k, bm, bw, (float *)pa.out, tm);
   else
-    hipLaunchKernelGGL((pcm400_kernel<int16_t, __half>), grid, block, 0, s, k, cs, cw, co, w, (__half *)pa.out, tm);
+    hipLaunchKernelGGL((pcm400_kernel<int16_t, __half>), grid, block, 0, s, k, bm, bw, (__half *)pa.out, tm);
   return hipGetLastError();
 }
 

@@ -3,6 +3,7 @@
 // the host in float64 and rounds once to float32; no HIP call is made.
 #include <cmath>
 #include <cstdio>
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -103,6 +104,42 @@ void build_mfma400(lm_plan *p) {
     for (int lane = 0; lane < 64; ++lane)
       for (int j = 0; j < 4; ++j)
         p->mfma400[((size_t)n1 * 64 + lane) * 4 + j] = (float)M[lane % 16][4 * j + lane / 16];
+  }
+}
+
+// Blocked copy of a packed filterbank for the matrix-core mel sum:
+// bands in blocks of 16; block j covers bins [klo, klo + 4 nch) where
+// [klo, khi) is the union of its bands' supports; chunk c of block j is
+// stored in matrix-core lane order, entry [lane] = W[16 j + lane % 16][klo +
+// 4 c + lane / 16] (0 outside a band's support or past the last band).
+// meta holds (klo, nch, offset in floats) per block.
+void build_mel_blocks(lm_plan *p) {
+  const Csr &c = p->csr;
+  const int NM = c.n_rows, NB = (NM + 15) / 16;
+  p->melblk_meta.assign(3 * (size_t)NB, 0);
+  p->melblk_w.clear();
+  for (int j = 0; j < NB; ++j) {
+    int klo = 1 << 30, khi = 0;
+    for (int m = 16 * j; m < NM && m < 16 * j + 16; ++m)
+      if (c.width[m] > 0) {
+        klo = std::min(klo, c.start[m]);
+        khi = std::max(khi, c.start[m] + c.width[m]);
+      }
+    if (khi <= klo) {
+      klo = 0;
+      khi = 0;
+    }
+    const int nch = (khi - klo + 3) / 4;
+    p->melblk_meta[3 * j] = klo;
+    p->melblk_meta[3 * j + 1] = nch;
+    p->melblk_meta[3 * j + 2] = (int)p->melblk_w.size();
+    for (int ch = 0; ch < nch; ++ch)
+      for (int lane = 0; lane < 64; ++lane) {
+        const int m = 16 * j + lane % 16, k = klo + 4 * ch + lane / 16;
+        float v = 0.0f;
+        if (m < NM && k >= c.start[m] && k < c.start[m] + c.width[m]) v = c.w[c.off[m] + k - c.start[m]];
+        p->melblk_w.push_back(v);
+      }
   }
 }
 
@@ -228,6 +265,7 @@ int lm_plan_set_mel(lm_plan *p, double sr, double f_min, double f_max, int scale
     }
   }
   p->csr = pack_dense(dense.data(), NM, K);
+  build_mel_blocks(p);
   p->have_filters = true;
   p->tables_dirty = true;
   return LM_OK;
@@ -242,6 +280,7 @@ int lm_plan_set_filters(lm_plan *p, const float *host_dense, int n_mels, int n_b
   for (size_t i = 0; i < (size_t)n_mels * n_bins; ++i)
     if (!std::isfinite(host_dense[i])) return fail(LM_ERR_INVALID_ARG, "filters hold a non-finite value");
   p->csr = pack_dense(host_dense, n_mels, n_bins);
+  build_mel_blocks(p);
   p->have_filters = true;
   p->tables_dirty = true;
   return LM_OK;

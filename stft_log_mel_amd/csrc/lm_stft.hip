@@ -7,9 +7,9 @@
 // turned into power re^2 + im^2 straight into an LDS tile.  Each (frame,
 // band) output is then the packed triangular mel sum over that tile, log10
 // after the 1e-10 floor, (L+4)/4, stored frame-major so a tile's outputs
-// are one contiguous run.  The tile's largest mel value joins its clip's
-// maximum by atomicMax on the float bits and its smallest log value goes
-// to a per-tile slot; the clamp fix-up kernel completes the per-clip floor.
+// are one contiguous run.  The tile's largest mel value and smallest log
+// value go to per-tile slots; the clamp fix-up kernel reduces them per clip
+// and completes the per-clip floor.
 #include <climits>
 
 #include "lm_device.h"
@@ -29,8 +29,7 @@ struct StftKernelArgs {
   const float *csr_w;
   int w_len;
   void *out;
-  uint32_t *hi_bits;
-  float *tile_min;
+  float *tile_min, *tile_max;
 };
 
 __device__ __forceinline__ float pw(float2 v) { return __builtin_fmaf(v.x, v.x, v.y * v.y); }
@@ -114,7 +113,7 @@ __global__ void __launch_bounds__(kStftThreads) stft_logmel_kernel(StftKernelArg
   // 3. tile statistics
   block_maxmin<kStftThreads>(vmax, lmin, s_red);
   if (tid == 0) {
-    atomicMax(a.hi_bits + b, __float_as_uint(vmax));
+    a.tile_max[tile] = vmax;
     a.tile_min[tile] = lmin;
   }
 }
@@ -141,8 +140,8 @@ hipError_t launch_stft(const StftArgs &a, hipStream_t s) {
   k.csr_w = a.csr_w;
   k.w_len = a.w_len;
   k.out = a.out;
-  k.hi_bits = a.hi_bits;
   k.tile_min = a.tile_min;
+  k.tile_max = a.tile_max;
   const size_t lds = sizeof(float) * ((size_t)a.frames_per_tile * a.n_bins + kStftCsrLds);
   const dim3 grid((unsigned)(a.n_clips * a.tiles_per_clip)), block(kStftThreads);
   const bool vec16 = (reinterpret_cast<uintptr_t>(a.stft) & 15) == 0;
