@@ -29,16 +29,27 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_source_hash(entry: str) -> str:
-    files = ["lm_device.h", "lm_pcm.hip" if entry == "pcm" else "lm_stft.hip"]
+def kernel_source_hash() -> str:
+    """Hash of every library source: counter figures taken on other sources are stale."""
+    csrc = os.path.join(ROOT, "stft_log_mel_amd", "csrc")
     h = hashlib.sha256()
-    for f in files:
-        with open(os.path.join(ROOT, "stft_log_mel_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".cpp", ".h")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
-def counter_traffic(workload: str, entry: str):
+def main_kernel_name(w) -> str:
+    """The kernel lm_from_* launches for this workload (the library's own dispatch rule)."""
+    if w.entry == "stft":
+        return "stft_logmel_kernel"
+    if w.n_fft == 400 and w.hop % 2 == 0 and not os.environ.get("LM_FORCE_GENERIC"):
+        return "pcm400_kernel"
+    return "pcm_logmel_kernel"
+
+
+def counter_traffic(workload: str):
     """HBM bytes per launch of the main kernel from committed rocprofv3 counter
     runs, if they were taken on the current kernel source; else None."""
     try:
@@ -46,7 +57,7 @@ def counter_traffic(workload: str, entry: str):
             rec = json.load(fh).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_hash") != kernel_source_hash(entry):
+    if not rec or rec.get("source_hash") != kernel_source_hash():
         return None
     return rec.get("bytes_per_launch")
 
@@ -216,8 +227,8 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": counter_traffic(w.name, w.entry),
-            "kernel": "pcm_logmel_kernel" if w.entry == "pcm" else "stft_logmel_kernel",
+            "traffic": counter_traffic(w.name),
+            "kernel": main_kernel_name(w),
             "kernel_ms": round(main_ms, 5),
             "algorithmic_bytes_per_launch": per_step_bytes,
         },

@@ -26,6 +26,12 @@ __device__ __forceinline__ float rescale(float L) { return __builtin_fmaf(L, 0.2
 
 __device__ __forceinline__ void store_out(float *p, float v) { *p = v; }
 __device__ __forceinline__ void store_out(__half *p, float v) { *p = __float2half_rn(v); }
+// Streaming stores for the main kernels: every output is written once and
+// read again only by the fix-up's few flagged regions.
+__device__ __forceinline__ void store_out_nt(float *p, float v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store_out_nt(__half *p, float v) {
+  __builtin_nontemporal_store(__half_as_ushort(__float2half_rn(v)), reinterpret_cast<unsigned short *>(p));
+}
 __device__ __forceinline__ float load_out(const float *p) { return *p; }
 __device__ __forceinline__ float load_out(const __half *p) { return __half2float(*p); }
 

@@ -198,15 +198,8 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
       const float2 zc = cconj(s_buf[fl * M + (k == 0 ? 0 : M - k)]);
       const float2 Y = cadd(zk, zc), D = csub(zk, zc);
       const float2 V = cmul(a.untangle[k], D);
-      float p0 = (Y.x + V.y) * (Y.x + V.y) + (Y.y - V.x) * (Y.y - V.x);
-      float p1 = (Y.x - V.y) * (Y.x - V.y) + (Y.y + V.x) * (Y.y + V.x);
-      if (a.power != 2.0f) {
-        const float e = 0.5f * a.power;
-        p0 = powf(p0 * a.pre_scale, e);
-        p1 = powf(p1 * a.pre_scale, e);
-      }
-      pk[u] = p0;
-      pmk[u] = p1;
+      pk[u] = (Y.x + V.y) * (Y.x + V.y) + (Y.y - V.x) * (Y.y - V.x);
+      pmk[u] = (Y.x - V.y) * (Y.x - V.y) + (Y.y + V.x) * (Y.y + V.x);
     }
   }
   __syncthreads();
@@ -221,6 +214,12 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
     }
   }
   __syncthreads();
+  if (a.power != 2.0f) {
+    // |X|^p = (|X|^2)^(p/2) in place, outside the unrolled split above
+    const float e = 0.5f * a.power;
+    for (int i = tid; i < FPB * (M + 1); i += THREADS) P[i] = powf(P[i] * a.pre_scale, e);
+    __syncthreads();
+  }
 
   // 4. mel sums, log10, rescale, mel-major store
   float vmax = 0.0f, lmin = __builtin_huge_valf();
@@ -238,7 +237,7 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
     const float L = log10_pos(v);
     vmax = fmaxf(vmax, v);
     lmin = fminf(lmin, L);
-    store_out(out + (int64_t)m * F + fr, rescale(L));
+    store_out_nt(out + (int64_t)m * F + fr, rescale(L));
   }
 
   // 5. tile statistics

@@ -302,8 +302,6 @@ pcm400_kernel(Args a, const int32_t *__restrict__ melblk_meta, const float *__re
   const float2 c1 = g3 ? make_float2(1.0f, 0.0f) : wa;
   const float2 c2 = g3 ? make_float2(0.0f, 1.0f) : wa;
   float *P = s_lds + fl * kRow;
-  const bool gen_pow = a.power != 2.0f;
-  const float pe = 0.5f * a.power;
 #pragma unroll
   for (int i = 0; i < 25; ++i) {
     float2 zk = Za[i];
@@ -315,23 +313,24 @@ pcm400_kernel(Args a, const int32_t *__restrict__ melblk_meta, const float *__re
     const float2 Y = cadd(zk, zc), Dd = csub(zk, zc);
     const float2 W = cmul(w400(8 * i), i < 13 ? c1 : c2);
     const float2 V = cmul(W, Dd);
-    float pk = (Y.x + V.y) * (Y.x + V.y) + (Y.y - V.x) * (Y.y - V.x);
-    float pm = (Y.x - V.y) * (Y.x - V.y) + (Y.y + V.x) * (Y.y + V.x);
-    if (gen_pow) {
-      pk = powf(pk * a.pre_scale, pe);
-      pm = powf(pm * a.pre_scale, pe);
-    }
+    const float pk = (Y.x + V.y) * (Y.x + V.y) + (Y.y - V.x) * (Y.y - V.x);
+    const float pm = (Y.x - V.y) * (Y.x - V.y) + (Y.y + V.x) * (Y.y + V.x);
     const int k = 8 * i + (i < 13 ? d1 : d2);
     P[k] = pk;
     P[200 - k] = pm;
   }
   if (g3) {   // bin 100: 2 X[100] = 2 conj(Z[100]), |.|^2 = 4 |Z[100]|^2
     const float2 z = Zb[12];
-    float p100 = 4.0f * (z.x * z.x + z.y * z.y);
-    if (gen_pow) p100 = powf(p100 * a.pre_scale, pe);
-    P[100] = p100;
+    P[100] = 4.0f * (z.x * z.x + z.y * z.y);
   }
   __syncthreads();   // power rows complete (each wave reads its own frames' rows)
+  if (a.power != 2.0f) {
+    // |X|^p = (|X|^2)^(p/2), in place over the wave's own 16 rows (kept out
+    // of the unrolled split above so the power-2 path stays compact)
+    float *rows = s_lds + 16 * wv * kRow;
+    const float pe = 0.5f * a.power;
+    for (int i = lane; i < 16 * kRow; i += 64) rows[i] = powf(rows[i] * a.pre_scale, pe);
+  }
 
   // 5. mel sums on the matrix cores, for the wave's own 16 frames: bands in
   // blocks of 16, each block only over the 4-bin chunks its filters touch.
@@ -364,7 +363,7 @@ pcm400_kernel(Args a, const int32_t *__restrict__ melblk_meta, const float *__re
       if (valid && m < NM) {
         vmax = fmaxf(vmax, v);
         lmin = fminf(lmin, L);
-        store_out(ocol + (int64_t)m * F, rescale(L));
+        store_out_nt(ocol + (int64_t)m * F, rescale(L));
       }
     }
   }

@@ -101,7 +101,7 @@ __global__ void __launch_bounds__(kStftThreads) stft_logmel_kernel(StftKernelArg
     const float L = log10_pos(v);
     vmax = fmaxf(vmax, v);
     lmin = fminf(lmin, L);
-    store_out(out + o, rescale(L));
+    store_out_nt(out + o, rescale(L));
     m += dm;
     f += df;
     if (m >= NM) {

@@ -232,12 +232,13 @@ def test_pcm_int16_extremes_and_batch_sizes():
         check(out, oracle_pcm(x, 400, 160, 128, 16000.0), TOL32, f"int16 B={B}")
 
 
+@pytest.mark.parametrize("n_fft,hop,n_mels", [(512, 128, 64), (400, 160, 80)])
 @pytest.mark.parametrize("power", [1.0, 3.0])
-def test_pcm_general_power(power):
-    say("pcm power", power)
+def test_pcm_general_power(power, n_fft, hop, n_mels):
+    say("pcm power", power, "n_fft", n_fft)
     x = lm_synth.speech_pcm(2, 6000, 16000.0, seed=4)
-    out = run_pcm(x, 512, 128, 64, 16000.0, power=power)
-    check(out, oracle_pcm(x, 512, 128, 64, 16000.0, power=power), TOL32, f"power {power}")
+    out = run_pcm(x, n_fft, hop, n_mels, 16000.0, power=power)
+    check(out, oracle_pcm(x, n_fft, hop, n_mels, 16000.0, power=power), TOL32, f"power {power} n_fft {n_fft}")
 
 
 def test_pcm_htk_no_norm_and_user_filters():
