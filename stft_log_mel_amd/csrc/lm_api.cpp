@@ -13,8 +13,15 @@ int ensure_device(lm_plan *p) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  if (p->device < 0) p->device = dev;
-  else if (p->device != dev) return fail(LM_ERR_INVALID_ARG, "plan is bound to another device");
+  if (p->device < 0) {
+    int n_cu = 0;
+    e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    p->device = dev;
+    p->n_cu = n_cu > 0 ? n_cu : 1;
+  } else if (p->device != dev) {
+    return fail(LM_ERR_INVALID_ARG, "plan is bound to another device");
+  }
   return LM_OK;
 }
 
@@ -81,19 +88,19 @@ int upload_tables(lm_plan *p) {
   return LM_OK;
 }
 
-// Per-(sub-)tile statistics: minima then maxima, each n_entries floats.
-// Every call overwrites all of its entries, so nothing needs clearing.
-int ensure_workspace(lm_plan *p, int64_t n_entries) {
-  if ((size_t)n_entries <= p->tile_cap) return LM_OK;
-  if (p->d_tile_min) {
-    hipError_t e = hipFree(p->d_tile_min);
-    p->d_tile_min = nullptr;
-    p->tile_cap = 0;
+// Statistics workspace (minima, then maxima), grown on demand.  Every call
+// overwrites all of the entries it reads, so nothing needs clearing.
+int ensure_workspace(lm_plan *p, int64_t n_floats) {
+  if ((size_t)n_floats <= p->stats_cap) return LM_OK;
+  if (p->d_stats) {
+    hipError_t e = hipFree(p->d_stats);
+    p->d_stats = nullptr;
+    p->stats_cap = 0;
     if (e != hipSuccess) return hip_fail(e, "hipFree(workspace)");
   }
-  hipError_t e = hipMalloc(reinterpret_cast<void **>(&p->d_tile_min), 2 * sizeof(float) * n_entries);
+  hipError_t e = hipMalloc(reinterpret_cast<void **>(&p->d_stats), sizeof(float) * n_floats);
   if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
-  p->tile_cap = n_entries;
+  p->stats_cap = n_floats;
   return LM_OK;
 }
 
@@ -160,19 +167,19 @@ int lm_from_pcm(lm_plan *p, const void *pcm, int in_dtype, int64_t n_clips, int6
   int rc = ensure_device(p);
   if (rc == LM_OK) rc = upload_tables(p);
   if (rc != LM_OK) return rc;
-  const int fpb = pcm_frames_per_tile(p, in_dtype == LM_I16);
-  const int rows = pcm_min_rows_per_tile(p, in_dtype == LM_I16);
-  const int64_t tiles = (F + fpb - 1) / fpb;
+  const StatLayout st = pcm_stat_layout(p, in_dtype == LM_I16);
+  const int64_t tiles = (F + st.frames_per_tile - 1) / st.frames_per_tile;
   if (tiles > INT32_MAX || n_clips * tiles > INT32_MAX) return fail(LM_ERR_UNSUPPORTED, "input too large");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  rc = ensure_workspace(p, n_clips * tiles * rows);
+  const int64_t n_min = n_clips * tiles * st.min_per_tile(), n_max = n_clips * tiles * st.max_per_tile;
+  rc = ensure_workspace(p, n_min + n_max);
   if (rc != LM_OK) return rc;
-  float *tmin = p->d_tile_min, *tmax = p->d_tile_min + p->tile_cap;
+  float *tmin = p->d_stats, *tmax = p->d_stats + n_min;
 
   PcmArgs a{pcm, in_dtype == LM_I16, n_clips, n_samples, F, (int)tiles, out, tmin, tmax};
   rc = timed_launch(p, s, 0, "launch(pcm kernel)", [&] { return launch_pcm(p, a, s); });
   if (rc != LM_OK) return rc;
-  FixupArgs fx{out, p->out_dtype == LM_F16, tmin, tmax, n_clips, F, p->n_mels, fpb, (int)tiles, 1, rows};
+  FixupArgs fx{out, p->out_dtype == LM_F16, tmin, tmax, n_clips, F, p->n_mels, (int)tiles, st, 1};
   return timed_launch(p, s, 1, "launch(clamp fix-up)", [&] { return launch_fixup(fx, s); });
 }
 
@@ -200,9 +207,9 @@ int lm_from_stft(lm_plan *p, const void *stft, const float *mel_filters, int64_t
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   int rc = ensure_device(p);
   if (rc == LM_OK && !mel_filters) rc = upload_tables(p);
-  if (rc == LM_OK) rc = ensure_workspace(p, n_clips * tiles);
+  if (rc == LM_OK) rc = ensure_workspace(p, 2 * n_clips * tiles);
   if (rc != LM_OK) return rc;
-  float *tmin = p->d_tile_min, *tmax = p->d_tile_min + p->tile_cap;
+  float *tmin = p->d_stats, *tmax = p->d_stats + n_clips * tiles;
 
   const int32_t *cs, *cw, *co;
   const float *w;
@@ -239,7 +246,10 @@ int lm_from_stft(lm_plan *p, const void *stft, const float *mel_filters, int64_t
              cs, cw, co, w, w_len, out, p->out_dtype == LM_F16, tmin, tmax};
   rc = timed_launch(p, s, 0, "launch(stft kernel)", [&] { return launch_stft(a, s); });
   if (rc != LM_OK) return rc;
-  FixupArgs fx{out, p->out_dtype == LM_F16, tmin, tmax, n_clips, n_frames, n_mels, tf, (int)tiles, 0, 1};
+  StatLayout st;
+  st.frames_per_tile = tf;
+  st.band_h = n_mels;
+  FixupArgs fx{out, p->out_dtype == LM_F16, tmin, tmax, n_clips, n_frames, n_mels, (int)tiles, st, 0};
   return timed_launch(p, s, 1, "launch(clamp fix-up)", [&] { return launch_fixup(fx, s); });
 }
 
@@ -279,7 +289,7 @@ void lm_plan_destroy(lm_plan *p) {
     (void)hipEventDestroy(r.end);
   }
   if (p->dt.base) (void)hipFree(p->dt.base);
-  if (p->d_tile_min) (void)hipFree(p->d_tile_min);
+  if (p->d_stats) (void)hipFree(p->d_stats);
   if (p->d_pack) (void)hipFree(p->d_pack);
   delete p;
 }

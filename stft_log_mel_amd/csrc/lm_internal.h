@@ -60,17 +60,18 @@ struct lm_plan {
   std::vector<float> window;      // n_fft
   std::vector<float> twiddle;     // 2 * M
   std::vector<float> untangle;    // 2 * (M/2 + 1)
-  std::vector<float> mfma400;     // n_fft = 400 only: 25 x 64 x 4 matrix-core operands
+  std::vector<float> mfma400;     // n_fft = 400 only: first-stage matrix-core operands (4 x 7 x 64 x 4)
   std::vector<int32_t> melblk_meta;  // per 16-band block: klo, chunks, offset
   std::vector<float> melblk_w;       // blocked filter weights in matrix-core lane order
 
   int device = -1;                // bound at first launch
+  int n_cu = 0;                   // compute units of that device
   bool tables_dirty = true;
   lm::DeviceTables dt;
 
-  // workspace: per-(sub-)tile smallest log value and largest mel value
-  float *d_tile_min = nullptr;    // [tile_cap] minima, then [tile_cap] maxima
-  size_t tile_cap = 0;
+  // workspace: per-region smallest log value and per-tile largest mel value
+  float *d_stats = nullptr;       // [minima][maxima], laid out per call
+  size_t stats_cap = 0;           // floats
   // per-call packed copy of a device filterbank (STFT path)
   void *d_pack = nullptr;
   size_t pack_cap = 0;
@@ -85,7 +86,7 @@ namespace lm {
 
 // Workspace helpers (lm_api.cpp)
 int ensure_device(lm_plan *p);
-int ensure_workspace(lm_plan *p, int64_t n_entries);
+int ensure_workspace(lm_plan *p, int64_t n_floats);
 int upload_tables(lm_plan *p);
 
 // Host table builders (lm_plan.cpp)
@@ -96,25 +97,36 @@ void build_mel_blocks(lm_plan *p);
 Csr pack_dense(const float *dense, int n_rows, int n_bins);
 
 // Kernel launchers.  Each returns hipSuccess or the launch error.
+// Geometry of a main kernel's statistics for the clamp fix-up.  A tile is
+// frames_per_tile consecutive frames of one clip.  Per tile there are
+// sub_per_tile x blk_per_sub minimum entries: entry (sub, blk) holds the
+// smallest log value over frames [sub * frames_per_tile / sub_per_tile,
+// +frames_per_tile / sub_per_tile) of the tile and bands [blk * band_h,
+// (blk + 1) * band_h) (both clipped to the output), or +inf if that region
+// is empty; and max_per_tile maximum entries whose largest value is the
+// tile's largest mel value (after the 1e-10 floor).  Entries are stored
+// clip-major, tile-major.
+struct StatLayout {
+  int frames_per_tile = 1, sub_per_tile = 1, blk_per_sub = 1, band_h = 1, max_per_tile = 1;
+  __host__ __device__ int min_per_tile() const { return sub_per_tile * blk_per_sub; }
+};
+
 struct PcmArgs {
   const void *pcm;
   bool in_i16;
   int64_t n_clips, n_samples, n_frames;
   int tiles_per_clip;
   void *out;
-  float *tile_min;   // per (sub-)tile smallest log value
-  float *tile_max;   // per (sub-)tile largest mel value (after the 1e-10 floor)
+  float *tile_min;
+  float *tile_max;
 };
-// Frames per workgroup tile of the PCM kernel launch_pcm picks for this
-// plan and input type (the n_fft = 400 matrix-core kernel when it applies,
-// else the generic one).
-int pcm_frames_per_tile(const lm_plan *p, bool in_i16);
+// Statistics geometry of the PCM kernel launch_pcm picks for this plan and
+// input type (the n_fft = 400 matrix-core kernel when it applies, else the
+// generic one).
+StatLayout pcm_stat_layout(const lm_plan *p, bool in_i16);
 hipError_t launch_pcm(const lm_plan *p, const PcmArgs &a, hipStream_t s);
 bool pcm400_supported(const lm_plan *p, bool in_i16);
-int pcm400_frames_per_tile();
-int pcm400_min_rows_per_tile(const lm_plan *p);
-// entries of tile_min per tile the PCM kernel launch_pcm picks writes
-int pcm_min_rows_per_tile(const lm_plan *p, bool in_i16);
+StatLayout pcm400_stat_layout(const lm_plan *p);
 hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &a, hipStream_t s);
 
 struct StftArgs {
@@ -145,9 +157,9 @@ struct FixupArgs {
   const float *tile_max;
   int64_t n_clips, n_frames;
   int n_mels;
-  int frames_per_tile, tiles_per_clip;
+  int tiles_per_clip;
+  StatLayout st;
   int mel_major;  // 1: (B, NM, F); 0: (B, F, NM)
-  int rows_per_tile;    // entries of tile_min per tile: R sub-tiles of frames_per_tile / R frames
   int entries_per_group = 0, groups_per_clip = 0;   // set by launch_fixup
 };
 hipError_t launch_fixup(FixupArgs a, hipStream_t s);

@@ -277,12 +277,12 @@ static int generic_frames_per_tile(int n_fft) {
 
 static bool use_pcm400(const lm_plan *p, bool in_i16) { return !p->force_generic && pcm400_supported(p, in_i16); }
 
-int pcm_frames_per_tile(const lm_plan *p, bool in_i16) {
-  return use_pcm400(p, in_i16) ? pcm400_frames_per_tile() : generic_frames_per_tile(p->n_fft);
-}
-
-int pcm_min_rows_per_tile(const lm_plan *p, bool in_i16) {
-  return use_pcm400(p, in_i16) ? pcm400_min_rows_per_tile(p) : 1;
+StatLayout pcm_stat_layout(const lm_plan *p, bool in_i16) {
+  if (use_pcm400(p, in_i16)) return pcm400_stat_layout(p);
+  StatLayout st;   // one entry per tile over all bands
+  st.frames_per_tile = generic_frames_per_tile(p->n_fft);
+  st.band_h = p->n_mels;
+  return st;
 }
 
 hipError_t launch_pcm(const lm_plan *p, const PcmArgs &a, hipStream_t s) {

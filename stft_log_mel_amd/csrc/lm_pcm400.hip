@@ -2,26 +2,33 @@
 // 16 kHz), using the matrix cores for the first FFT stage.
 //
 // Chain per frame (flashmel page, "How it works"; KBench task page
-// "audio-mel-spectrogram-fused", "spec_md"):
-//   fold the 400 windowed samples to z[n] = w[2n]x[2n] + i w[2n+1]x[2n+1],
-//   n < 200; 200 = 25 * 8 with n = n1 + 25 n2 and bin k = 8 k1 + k2:
-//     Z[8 k1 + k2] = sum_n1 W25^(n1 k1) [ sum_n2 z[n1+25n2] W200^(k2 (n1+25n2)) ]
-//   The inner bracket (window, 8-point DFT and twiddle) is, for each n1, one
-//   real 16x16 matrix applied to 16 frames at once on the matrix cores
-//   (v_mfma_f32_16x16x4f32, four per n1).  Its output layout leaves lane
-//   (frame c, group g) with two whole frequency classes k2 over all n1, so
-//   the 25-point DFTs over n1 run in registers (5 x 5, Winograd 5-point
-//   modules).  The classes are paired (1,7), (2,6), (3,5), (0,4) so that
-//   the split into the real spectrum,
-//     2 X[k] = (Z[k] + Z*[200-k]) - i W400^k (Z[k] - Z*[200-k]),
-//   needs only the lane's own registers.  |X|^2 goes to an LDS power tile
-//   (row stride 201, odd), then each wave forms 1/4 of the mel bands for all
-//   64 frames of the tile: packed filter weights are wave-uniform (scalar
-//   loads), 64 consecutive frames make one 256-byte store per band
-//   (mel-major output), log10 after the 1e-10 floor, (L+4)/4.
-// Each wave's largest mel value and smallest log value go to per-sub-tile
-// slots; the clamp fix-up kernel reduces them per clip and finishes the
-// per-clip floor.
+// "audio-mel-spectrogram-fused", "spec_md"): the windowed frame y[n] =
+// w[n] x[n], n < 400, is split as n = n1 + 25 n2 (n1 < 25, n2 < 16) with bins
+// k = 16 k1 + k2, so that
+//   X[16 k1 + k2] = sum_n1 W25^(n1 k1) [ sum_n2 y[n1 + 25 n2] W400^(k2 (n1 + 25 n2)) ].
+// The bracket (window, 16-point DFT and twiddle) is, for each n1, one real
+// 16x16 matrix applied to 16 frames at once on the matrix cores
+// (v_mfma_f32_16x16x4f32, four per n1).  Since y is real, classes k2 and
+// 16 - k2 are conjugate mirrors, so the matrix rows hold classes 1..7
+// (real and imaginary parts) plus the two sums of y over even and over odd
+// n2 -- from which classes 0 and 8, the bins that are multiples of 8, are a
+// 50-point real DFT.  The output layout leaves lane (frame c, group g) with
+// whole classes over all n1: group g < 3 holds classes g + 1 and 7 - g,
+// group 3 holds class 4 and the even/odd sums.  The 25-point DFTs over n1
+// then run in registers (5 x 5, Winograd 5-point modules); the 50-point
+// real DFT is the 25-point complex DFT of z[m] = s[2m] + i s[2m+1] followed
+// by its split into real-input bins.  |X|^2 goes to the wave's own power
+// rows in LDS; the mel sums run on the matrix cores over blocks of 16 bands
+// and only the 4-bin chunks their filters touch; log10 after the 1e-10
+// floor, (L+4)/4, mel-major store (16 consecutive frames per band).
+//
+// One workgroup of 8 waves per compute unit walks a contiguous range of
+// 16-frame sub-tiles; its waves take every 8th one and never wait for each
+// other (one barrier after the operand tables are staged).  Each wave
+// fetches the next sub-tile's samples into registers while it computes the
+// current one.  Per sub-tile it records the largest mel value and, per
+// 4-band group of every band block, the smallest log value, for the clamp
+// fix-up kernel.
 #include "lm_device.h"
 #include "lm_internal.h"
 
@@ -30,12 +37,16 @@ namespace lm {
 namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-constexpr int kTileFrames = 64;               // frames per workgroup
-constexpr int kThreads = 256;                 // 4 waves, 16 frames each in the FFT
-constexpr int kRow = 201;                     // power-tile row stride (odd: no bank conflicts)
-constexpr int kLdsFloats = kTileFrames * kRow;
-constexpr int kMelWLds = 4096;                // blocked filter weights staged in LDS up to this count
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kSub = 16;                  // frames per wave step (the matrix-core N)
+constexpr int kRow = 204;                 // power row stride: 12 c mod 64 puts 16 rows on distinct bank quads
+constexpr int kRegion = kSub * kRow;      // floats of LDS per wave: staged samples, then power rows
+constexpr int kAmat = 4 * 7 * 64;         // first-stage operands (v4f): [j][n1 / 4][lane]
+constexpr int kMelWLds = 4096;            // blocked filter weights staged in LDS up to this count
+constexpr int kPfI16 = 6, kPfF32 = 11;    // 16-byte sample loads per lane held for the next sub-tile
 
 // compile-time cos/sin of 2 pi j / N for N a multiple of 8 (octant reduction
 // in integers, Taylor series on [0, pi/4]); evaluated in double, rounded once
@@ -121,17 +132,30 @@ __device__ __forceinline__ void dft25(float2 (&a)[25]) {
   }
 }
 
+// min over the 16 lanes of a DPP row (rotations by 1, 2, 4, 8)
+template <int N>
+__device__ __forceinline__ float ror_min(float v) {
+  const int r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + N, 0xf, 0xf, false);
+  return fminf(v, __builtin_bit_cast(float, r));
+}
+__device__ __forceinline__ float row_min16(float v) {
+  v = ror_min<1>(v);
+  v = ror_min<2>(v);
+  v = ror_min<4>(v);
+  return ror_min<8>(v);
+}
+
 struct Args {
   const void *pcm;
   int64_t T, F;
-  int tiles_per_clip;
+  int S;                 // 16-frame sub-tiles per clip
+  int64_t n_sub;         // sub-tiles of the whole call
+  int per_wg;            // sub-tiles per workgroup
   int hop, pad, pad_mode;
-  float power, mel_scale, pre_scale;
+  float power, pre_scale, mel_scale;
   int n_mels, n_melblk;
-  const v4f *amat;   // [25][64] operand table of the matrix-core stage
-  void *out;
+  int melw_n;            // blocked weights staged in LDS (count <= kMelWLds), else 0
   float *tile_max;
-  int melw_lds;   // blocked filter weights staged in LDS (count <= kMelWLds), else 0
 };
 
 __device__ __forceinline__ float to_f(float v) { return v; }
@@ -148,260 +172,296 @@ __device__ __forceinline__ float padded(const IN *__restrict__ x, int64_t j, int
   return to_f(x[j]);
 }
 
-// LDS layout of the staged span, in dwords: int16 sample pairs with one
-// pad dword after every 32, or float samples with two pad dwords after every
-// 64 (sample pairs stay 8-byte aligned).  Frame starts are multiples of
-// hop/2 (or hop) dwords, which would put the 16 frames a wave reads at once
-// on two banks; the padding spreads them over all of them.
 template <typename IN>
-__device__ __forceinline__ int skew(int d) {
-  return sizeof(IN) == 2 ? d + (d >> 5) : d + 2 * (d >> 6);
+struct Prefetch {
+  static constexpr int N = sizeof(IN) == 2 ? kPfI16 : kPfF32;
+  u4 v[N];
+};
+
+// Where sub-tile gs reads: clip b, samples [s_begin, s_begin + span) of it
+// (s_begin < 0 or past the end: padding).
+struct SubTile {
+  int64_t b, s;
+  int64_t s_begin;
+};
+__device__ __forceinline__ SubTile locate(const Args &a, int64_t gs) {
+  SubTile t;
+  t.b = gs / a.S;
+  t.s = gs - t.b * a.S;
+  t.s_begin = t.s * kSub * a.hop - a.pad;
+  return t;
 }
 
-constexpr int kStageUnroll = 4;
-
-// Stage samples [s_begin, s_begin + span) of the clip (padding resolved by
-// index; positions past the end of the clip's last frame read as 0) into
-// LDS as dwords.  Interior spans with a 16-byte aligned start are copied
-// with 16-byte loads, kStageUnroll in flight per thread.
+// Issue the 16-byte loads of an interior, 16-byte aligned span (the rounded
+// up span must lie inside the clip); false if the span needs the padded path.
 template <typename IN>
-__device__ __forceinline__ void stage_span(const IN *__restrict__ x, int64_t T, int64_t s_begin, int span,
-                                           int64_t s_limit, int mode, uint32_t *lds) {
-  const int tid = threadIdx.x;
-  constexpr int PER_DW = 4 / sizeof(IN);                 // samples per dword
-  const int ndw = span / PER_DW;                          // span is a multiple of PER_DW
-  const IN *src = x + s_begin;
-  const bool interior = s_begin >= 0 && s_begin + span <= T;
-  if (interior && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
-    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-    const u4 *s4 = reinterpret_cast<const u4 *>(src);
-    const int n4 = ndw >> 2;
-    for (int q0 = tid; q0 < n4; q0 += kStageUnroll * kThreads) {
-      u4 v[kStageUnroll];
+__device__ __forceinline__ bool prefetch(const Args &a, const IN *__restrict__ pcm, int64_t gs, int span,
+                                         Prefetch<IN> &pf) {
+  constexpr int PER = 16 / sizeof(IN);   // samples per load
+  const int n4 = (span + PER - 1) / PER;
+  const SubTile t = locate(a, gs);
+  const IN *src = pcm + t.b * a.T + t.s_begin;
+  if (n4 > 64 * Prefetch<IN>::N || t.s_begin < 0 || t.s_begin + (int64_t)n4 * PER > a.T ||
+      (reinterpret_cast<uintptr_t>(src) & 15))
+    return false;
+  const u4 *s4 = reinterpret_cast<const u4 *>(src);
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-      for (int u = 0; u < kStageUnroll; ++u)
-        if (q0 + u * kThreads < n4) v[u] = s4[q0 + u * kThreads];
+  for (int i = 0; i < Prefetch<IN>::N; ++i)
+    if (lane + 64 * i < n4) pf.v[i] = s4[lane + 64 * i];
+  return true;
+}
+
+template <typename IN>
+__device__ __forceinline__ void put_prefetch(const Prefetch<IN> &pf, int span, float *R) {
+  constexpr int PER = 16 / sizeof(IN);
+  const int n4 = (span + PER - 1) / PER;
+  const int lane = threadIdx.x & 63;
+  u4 *d4 = reinterpret_cast<u4 *>(R);
 #pragma unroll
-      for (int u = 0; u < kStageUnroll; ++u)
-        if (q0 + u * kThreads < n4) {
-          uint32_t *dst = lds + skew<IN>(4 * (q0 + u * kThreads));   // 4 dwords never straddle a pad
-          dst[0] = v[u].x;
-          dst[1] = v[u].y;
-          dst[2] = v[u].z;
-          dst[3] = v[u].w;
-        }
+  for (int i = 0; i < Prefetch<IN>::N; ++i)
+    if (lane + 64 * i < n4) d4[lane + 64 * i] = pf.v[i];
+}
+
+// Padded path: every dword of the span by index arithmetic (positions past
+// the end of the clip's last frame read as 0).
+template <typename IN>
+__device__ __forceinline__ void stage_padded(const Args &a, const IN *__restrict__ pcm, int64_t gs, int span,
+                                             float *R) {
+  constexpr int PER_DW = 4 / sizeof(IN);
+  const SubTile t = locate(a, gs);
+  const IN *x = pcm + t.b * a.T;
+  const int64_t s_limit = (a.F - 1) * (int64_t)a.hop - a.pad + 400;
+  uint32_t *d32 = reinterpret_cast<uint32_t *>(R);
+  const int lane = threadIdx.x & 63;
+  for (int d = lane; d < span / PER_DW; d += 64) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < PER_DW; ++e) {
+      const int64_t j = t.s_begin + (int64_t)d * PER_DW + e;
+      const float v = j < s_limit ? padded(x, j, a.T, a.pad_mode) : 0.0f;
+      if (sizeof(IN) == 2) w |= (uint32_t)(uint16_t)(int16_t)(int)v << (16 * e);
+      else w = __float_as_uint(v);
     }
-    const uint32_t *s32 = reinterpret_cast<const uint32_t *>(src);
-    for (int d = 4 * n4 + tid; d < ndw; d += kThreads) lds[skew<IN>(d)] = s32[d];
-  } else if (interior && (reinterpret_cast<uintptr_t>(src) & 3) == 0) {
-    const uint32_t *s32 = reinterpret_cast<const uint32_t *>(src);
-    for (int d0 = tid; d0 < ndw; d0 += kStageUnroll * kThreads) {
-      uint32_t v[kStageUnroll];
-#pragma unroll
-      for (int u = 0; u < kStageUnroll; ++u)
-        if (d0 + u * kThreads < ndw) v[u] = s32[d0 + u * kThreads];
-#pragma unroll
-      for (int u = 0; u < kStageUnroll; ++u)
-        if (d0 + u * kThreads < ndw) lds[skew<IN>(d0 + u * kThreads)] = v[u];
-    }
-  } else {
-    for (int d = tid; d < ndw; d += kThreads) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int e = 0; e < PER_DW; ++e) {
-        const int64_t j = s_begin + (int64_t)d * PER_DW + e;
-        const float v = j < s_limit ? padded(x, j, T, mode) : 0.0f;
-        if (sizeof(IN) == 2) w |= (uint32_t)(uint16_t)(int16_t)(int)v << (16 * e);
-        else w = __float_as_uint(v);
-      }
-      lds[skew<IN>(d)] = w;
-    }
+    d32[d] = w;
   }
 }
 
 template <typename IN, typename OUT>
-__global__ void __launch_bounds__(kThreads, 2)
-pcm400_kernel(Args a, const int32_t *__restrict__ melblk_meta, const float *__restrict__ melblk_w,
-              OUT *__restrict__ out_base, float *__restrict__ tile_min) {
-  // staged span, then the power tile; 4 zero floats after it are read (with
-  // weight 0) by a filter chunk that runs past the last frame's row
-  __shared__ __attribute__((aligned(16))) float s_lds[kLdsFloats + 4];
+__global__ void __launch_bounds__(kThreads, 1)
+pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ melblk_meta,
+              const float *__restrict__ melblk_w, OUT *__restrict__ out, float *__restrict__ tile_min) {
+  __shared__ v4f s_amat[kAmat];
   __shared__ float s_melw[kMelWLds];
+  __shared__ __attribute__((aligned(16))) float s_reg[kWaves * kRegion];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
-  const int64_t tile = blockIdx.x;
-  const int64_t b = tile / a.tiles_per_clip;
-  const int64_t f0 = (tile - b * a.tiles_per_clip) * (int64_t)kTileFrames;
-  const int64_t T = a.T, F = a.F;
-  const int hop = a.hop;
-  const IN *__restrict__ x = reinterpret_cast<const IN *>(a.pcm) + b * T;
-
-  // 1. the tile's sample span into LDS
-  const int64_t s_begin = f0 * hop - a.pad;
-  const int span = (kTileFrames - 1) * hop + 400;
-  const int64_t s_limit = (F - 1) * (int64_t)hop - a.pad + 400;   // end of the last frame of the clip
-  if (tid < 4) s_lds[kLdsFloats + tid] = 0.0f;
-  for (int i = tid; i < a.melw_lds; i += kThreads) s_melw[i] = melblk_w[i];
-  stage_span<IN>(x, T, s_begin, span, s_limit, a.pad_mode, reinterpret_cast<uint32_t *>(s_lds));
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  for (int i = tid; i < kAmat; i += kThreads) s_amat[i] = amat[i];
+  for (int i = tid; i < a.melw_n; i += kThreads) s_melw[i] = melblk_w[i] * a.mel_scale;
   __syncthreads();
 
-  // 2. window + 8-point DFT + twiddle on the matrix cores: D[n1] = M_n1 * B_n1
+  const IN *__restrict__ pcm = reinterpret_cast<const IN *>(a.pcm);
+  float *R = s_reg + wv * kRegion;
+  const int hop = a.hop;
+  const int span = (kSub - 1) * hop + 400;
   const int c = lane & 15, g = lane >> 4;
-  const int fl = 16 * wv + c;                   // frame within the tile
-  v4f D[25];
-#pragma unroll
-  for (int n1 = 0; n1 < 25; ++n1) {
-    const int s0 = fl * hop + 2 * n1 + 50 * g;  // samples s0, s0+1 (n2 = g) and s0+200, s0+201 (n2 = g+4)
-    float xe0, xo0, xe1, xo1;
-    if (sizeof(IN) == 2) {
-      const uint32_t *d32 = reinterpret_cast<const uint32_t *>(s_lds);
-      const uint32_t p0 = d32[skew<IN>(s0 >> 1)], p1 = d32[skew<IN>((s0 >> 1) + 100)];
-      xe0 = (float)(int16_t)(p0 & 0xffffu);
-      xo0 = (float)((int32_t)p0 >> 16);
-      xe1 = (float)(int16_t)(p1 & 0xffffu);
-      xo1 = (float)((int32_t)p1 >> 16);
-    } else {
-      const float2 q0 = *reinterpret_cast<const float2 *>(s_lds + skew<IN>(s0));
-      const float2 q1 = *reinterpret_cast<const float2 *>(s_lds + skew<IN>(s0 + 200));
-      xe0 = q0.x;
-      xo0 = q0.y;
-      xe1 = q1.x;
-      xo1 = q1.y;
-    }
-    const v4f m = a.amat[n1 * 64 + lane];
-    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(m[0], xe0, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(m[1], xe1, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(m[2], xo0, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(m[3], xo1, acc, 0, 0, 0);
-    D[n1] = acc;
-  }
-  __syncthreads();   // every wave is done with the span; the LDS becomes the power tile
-
-  // 3. two 25-point DFTs per lane: classes a (rows 4g, 4g+1) and b (4g+2, 4g+3)
-  float2 Za[25], Zb[25];
-#pragma unroll
-  for (int n1 = 0; n1 < 25; ++n1) {
-    Za[n1] = make_float2(D[n1][0], D[n1][1]);
-    Zb[n1] = make_float2(D[n1][2], D[n1][3]);
-  }
-  dft25(Za);
-  dft25(Zb);
-
-  // 4. split into the real spectrum and power.  Slot i pairs Z[k] with
-  // Z[200 - k]; for groups 0..2 (classes a, 8-a): k = 8i + a, partner
-  // Zb[24 - i].  Group 3 holds the self-paired classes 0 and 4, laid out
-  // into the same slot pattern: slots 0..12 are class 0 (k = 8i, partner
-  // Z0[(25 - i) mod 25]), slots 13..24 class 4 (k = 8i - 100, partner
-  // Z4[37 - i]); bin 100 (Z4[12] with itself) is one extra slot.
   const bool g3 = g == 3;
-  const int d1 = g3 ? 0 : g + 1, d2 = g3 ? -100 : g + 1;
-  // per-lane factor of the split twiddle W400^k = W400^(8i) * c
-  const float2 wa = g == 0 ? w400(1) : (g == 1 ? w400(2) : w400(3));
-  const float2 c1 = g3 ? make_float2(1.0f, 0.0f) : wa;
-  const float2 c2 = g3 ? make_float2(0.0f, 1.0f) : wa;
-  float *P = s_lds + fl * kRow;
-#pragma unroll
-  for (int i = 0; i < 25; ++i) {
-    float2 zk = Za[i];
-    if (i >= 13 && g3) zk = Zb[i - 13];
-    const int j = 24 - i;
-    float2 zm = Zb[j];
-    if (g3) zm = j < 12 ? Zb[13 + j] : (j < 24 ? Za[1 + j] : Za[0]);
-    const float2 zc = cconj(zm);
-    const float2 Y = cadd(zk, zc), Dd = csub(zk, zc);
-    const float2 W = cmul(w400(8 * i), i < 13 ? c1 : c2);
-    const float2 V = cmul(W, Dd);
-    const float pk = (Y.x + V.y) * (Y.x + V.y) + (Y.y - V.x) * (Y.y - V.x);
-    const float pm = (Y.x - V.y) * (Y.x - V.y) + (Y.y + V.x) * (Y.y + V.x);
-    const int k = 8 * i + (i < 13 ? d1 : d2);
-    P[k] = pk;
-    P[200 - k] = pm;
-  }
-  if (g3) {   // bin 100: 2 X[100] = 2 conj(Z[100]), |.|^2 = 4 |Z[100]|^2
-    const float2 z = Zb[12];
-    P[100] = 4.0f * (z.x * z.x + z.y * z.y);
-  }
-  __syncthreads();   // power rows complete (each wave reads its own frames' rows)
-  if (a.power != 2.0f) {
-    // |X|^p = (|X|^2)^(p/2), in place over the wave's own 16 rows (kept out
-    // of the unrolled split above so the power-2 path stays compact)
-    float *rows = s_lds + 16 * wv * kRow;
-    const float pe = 0.5f * a.power;
-    for (int i = lane; i < 16 * kRow; i += 64) rows[i] = powf(rows[i] * a.pre_scale, pe);
-  }
+  const int NM = a.n_mels, NB = a.n_melblk;
+  const int64_t F = a.F;
+  const float *wbase = a.melw_n ? s_melw : melblk_w;
 
-  // 5. mel sums on the matrix cores, for the wave's own 16 frames: bands in
-  // blocks of 16, each block only over the 4-bin chunks its filters touch.
-  // A = blocked filter weights (lane order), B = P[frame c][bin klo+4ch+g],
-  // D = 16 bands x 16 frames; lane (c, g) gets bands 16j+4g .. 16j+4g+3 of
-  // frame c.  Then log10 after the 1e-10 floor, (L+4)/4, mel-major store.
-  const int NM = a.n_mels;
-  const int64_t fr = f0 + fl;
-  const bool valid = fr < F;
-  const float *pb0 = s_lds + fl * kRow + g;
-  OUT *__restrict__ ocol = out_base + b * (int64_t)NM * F + fr;
-  float vmax = 0.0f, lmin = __builtin_huge_valf();
-  for (int j = 0; j < 16; ++j) {
-    if (j >= a.n_melblk) break;
-    const int klo = melblk_meta[3 * j], nch = melblk_meta[3 * j + 1], toff = melblk_meta[3 * j + 2];
-    const float *wt = (a.melw_lds ? s_melw : melblk_w) + toff + lane;
-    const float *pb = pb0 + klo;
-    v4f acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
-    int ch = 0;
-    for (; ch + 1 < nch; ch += 2) {
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(wt[64 * ch], pb[4 * ch], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(wt[64 * ch + 64], pb[4 * ch + 4], acc1, 0, 0, 0);
-    }
-    if (ch < nch) acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(wt[64 * ch], pb[4 * ch], acc0, 0, 0, 0);
+  const int64_t wg0 = (int64_t)blockIdx.x * a.per_wg;
+  const int64_t wg_end = min(wg0 + a.per_wg, a.n_sub);
+  int64_t gs = wg0 + wv;
+  Prefetch<IN> pf;
+  bool have = gs < wg_end && prefetch<IN>(a, pcm, gs, span, pf);
+
+  for (; gs < wg_end; gs += kWaves) {
+    // 1. this sub-tile's samples into the wave's region (LDS operations of
+    //    one wave complete in order, so no barrier is needed around them)
+    if (have) put_prefetch<IN>(pf, span, R);
+    else stage_padded<IN>(a, pcm, gs, span, R);
+    have = gs + kWaves < wg_end && prefetch<IN>(a, pcm, gs + kWaves, span, pf);
+
+    // 2. window + 16-point DFT + twiddle on the matrix cores: D[n1] += A[j][n1] x[j][n1].
+    //    Lane (c, g) supplies, for step j, the samples n1 + 25 (4 g + j) of frame c:
+    //    a run of 25 consecutive samples starting at c hop + 100 g + 25 j.
+    v4f D[25];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 16 * j + 4 * g + r;
-      const float v = fmaxf((acc0[r] + acc1[r]) * a.mel_scale, 1e-10f);
-      const float L = log10_pos(v);
-      if (valid && m < NM) {
-        vmax = fmaxf(vmax, v);
-        lmin = fminf(lmin, L);
-        store_out_nt(ocol + (int64_t)m * F, rescale(L));
+    for (int n1 = 0; n1 < 25; ++n1) D[n1] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v4f A[7];
+#pragma unroll
+      for (int q = 0; q < 7; ++q) A[q] = s_amat[(j * 7 + q) * 64 + lane];
+      const int r0 = c * hop + 100 * g + 25 * j;   // even hop: r0 has the parity of j
+      float x[25];
+      if (sizeof(IN) == 2) {
+        const uint32_t *rd = reinterpret_cast<const uint32_t *>(R) + (r0 >> 1);
+        uint32_t w[13];
+#pragma unroll
+        for (int i = 0; i < 13; ++i) w[i] = rd[i];
+#pragma unroll
+        for (int n1 = 0; n1 < 25; ++n1) {
+          const int s = n1 + (j & 1);
+          const uint32_t d = w[s >> 1];
+          x[n1] = (s & 1) ? (float)((int32_t)d >> 16) : (float)(int16_t)(d & 0xffffu);
+        }
+      } else {
+        const float2 *rf = reinterpret_cast<const float2 *>(R + (r0 & ~1));
+        float2 f[13];
+#pragma unroll
+        for (int i = 0; i < 13; ++i) f[i] = rf[i];
+#pragma unroll
+        for (int n1 = 0; n1 < 25; ++n1) {
+          const int s = n1 + (j & 1);
+          x[n1] = (s & 1) ? f[s >> 1].y : f[s >> 1].x;
+        }
+      }
+#pragma unroll
+      for (int n1 = 0; n1 < 25; ++n1)
+        D[n1] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[n1 >> 2][n1 & 3], x[n1], D[n1], 0, 0, 0);
+    }
+
+    // 3. 25-point DFTs over n1.  Za: class g + 1 (rows 4g, 4g+1).  Zb: class
+    //    7 - g (rows 4g+2, 4g+3) for g < 3; for g = 3, z[m] = s[2m] + i s[2m+1]
+    //    with s[n1 + 25 e] the sum over n2 of parity e (rows 14, 15).
+    float2 Za[25], Zb[25];
+#pragma unroll
+    for (int n1 = 0; n1 < 25; ++n1) Za[n1] = make_float2(D[n1][0], D[n1][1]);
+#pragma unroll
+    for (int m = 0; m < 25; ++m) {
+      const int e = 2 * m, o = 2 * m + 1;
+      const float se = e < 25 ? D[e][2] : D[e - 25][3];
+      const float so = o < 25 ? D[o][2] : D[o - 25][3];
+      Zb[m] = make_float2(g3 ? se : D[m][2], g3 ? so : D[m][3]);
+    }
+    dft25(Za);
+    dft25(Zb);
+
+    // 4. power rows (every value is 4 |X[k]|^2: the class rows are scaled by
+    //    2 in the matrix).  Za output k1 is bin 16 k1 + (g+1), or its mirror
+    //    400 - that for k1 > 12.  Zb outputs of groups 0..2 are bins 16 k1 +
+    //    7 - g and mirrors alike; they are taken in pairs (j, 25 - j), bins
+    //    16 j + 7 - g and 16 j - 7 + g, so that group 3 can share the loop:
+    //    there, with u = Zb[j], v = Zb[25 - j], A = u + v*, B = u - v* and W =
+    //    W50^j, the 50-point real DFT gives 2 S[j] = A - i W B (bin 8 j) and
+    //    conj(2 S[25 - j]) = A + i W B (bin 200 - 8 j).  The complex values
+    //    are formed before squaring, so a weak bin is not the difference of
+    //    two large squares.
+    float *Rc = R + c * kRow;
+    {
+      float *pa = Rc + (g + 1), *pb = Rc + (15 - g);
+#pragma unroll
+      for (int k1 = 0; k1 < 25; ++k1) {
+        const float p = __builtin_fmaf(Za[k1].x, Za[k1].x, Za[k1].y * Za[k1].y);
+        if (k1 <= 12) pa[16 * k1] = p;
+        else pb[16 * (24 - k1)] = p;
+      }
+      const int kb = 7 - g;
+      float *q1 = Rc + (g3 ? 0 : kb), *q2 = Rc + (g3 ? 200 : -kb);
+      const int st1 = g3 ? 8 : 16, st2 = g3 ? -8 : 16;
+#pragma unroll
+      for (int j = 0; j < 13; ++j) {
+        const float2 u = Zb[j], v = Zb[(25 - j) % 25];
+        const float2 A = make_float2(u.x + v.x, u.y - v.y), B = make_float2(u.x - v.x, u.y + v.y);
+        const float wx = kW400.c[8 * j], wy = kW400.s[8 * j];
+        const float p = __builtin_fmaf(wx, B.x, -wy * B.y), q = __builtin_fmaf(wx, B.y, wy * B.x);   // W B
+        const float2 X1 = g3 ? make_float2(A.x + q, A.y - p) : u;
+        const float2 X2 = g3 ? make_float2(A.x - q, A.y + p) : v;
+        q1[st1 * j] = __builtin_fmaf(X1.x, X1.x, X1.y * X1.y);
+        const float p2 = __builtin_fmaf(X2.x, X2.x, X2.y * X2.y);
+        if (j == 0) Rc[g3 ? 200 : kb] = p2;
+        else q2[st2 * j] = p2;
       }
     }
-  }
+    if (lane < 48) R[(lane / 3) * kRow + 201 + lane % 3] = 0.0f;   // pad columns read by the last chunks
+    if (a.power != 2.0f) {
+      // |X|^p = (|X|^2)^(p/2) in place over the wave's rows
+      const float pe = 0.5f * a.power;
+      for (int i = lane; i < kRegion; i += 64) R[i] = powf(R[i] * a.pre_scale, pe);
+    }
 
-  // 6. statistics of the wave's 16-frame sub-tile: smallest log value and
-  // largest mel value to entry tile * 4 + wave
-  lmin = wave_min(lmin);
-  vmax = wave_max(vmax);
-  if (lane == 0) {
-    tile_min[tile * (kThreads / 64) + wv] = lmin;
-    a.tile_max[tile * (kThreads / 64) + wv] = vmax;
+    // 5. mel sums on the matrix cores: bands in blocks of 16, each over the
+    //    4-bin chunks its filters touch.  A = blocked weights (lane order,
+    //    pre-scaled when staged), B = P[frame c][bin klo + 4 ch + g]; lane (c,
+    //    g) gets bands 16 jb + 4 g + r of frame c.
+    const SubTile t = locate(a, gs);
+    const int64_t fr = t.s * kSub + c;
+    const bool valid = fr < F;
+    OUT *__restrict__ ocol = out + t.b * (int64_t)NM * F + fr;
+    const float *pb0 = Rc + g;
+    const float sc = a.melw_n ? 1.0f : a.mel_scale;
+    float vmax = 0.0f;
+    for (int jb = 0; jb < 16; ++jb) {
+      if (jb >= NB) break;
+      const int klo = melblk_meta[3 * jb], nch = melblk_meta[3 * jb + 1], toff = melblk_meta[3 * jb + 2];
+      const float *wt = wbase + toff + lane;
+      const float *pb = pb0 + klo;
+      v4f acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+      int ch = 0;
+      for (; ch + 1 < nch; ch += 2) {
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(wt[64 * ch], pb[4 * ch], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(wt[64 * ch + 64], pb[4 * ch + 4], acc1, 0, 0, 0);
+      }
+      if (ch < nch) acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(wt[64 * ch], pb[4 * ch], acc0, 0, 0, 0);
+      float lmn = __builtin_huge_valf();
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 16 * jb + 4 * g + r;
+        const float v = fmaxf((acc0[r] + acc1[r]) * sc, 1e-10f);
+        const float L = log10_pos(v);
+        if (valid && m < NM) {
+          vmax = fmaxf(vmax, v);
+          lmn = fminf(lmn, L);
+          store_out_nt(ocol + (int64_t)m * F, rescale(L));
+        }
+      }
+      lmn = row_min16(lmn);
+      if (c == 0) tile_min[(gs * NB + jb) * 4 + g] = lmn;
+    }
+    vmax = wave_max(vmax);
+    if (lane == 0) a.tile_max[gs] = vmax;
   }
 }
 
 }  // namespace
 
-// The n_fft = 400 path needs an even hop (sample pairs stay aligned) and a
-// staged span that fits the power tile's LDS.
+// The n_fft = 400 path needs an even hop (runs of samples keep a parity
+// known at compile time) and a 16-frame span that fits the wave's region.
 bool pcm400_supported(const lm_plan *p, bool in_i16) {
-  if (p->n_fft != 400 || (p->hop & 1) || !p->dt.mfma400 || p->n_mels > 256) return false;
-  const int span = (kTileFrames - 1) * p->hop + 400;
+  if (p->n_fft != 400 || (p->hop & 1) || p->mfma400.empty() || p->n_mels > 256) return false;
+  const int span = (kSub - 1) * p->hop + 400;
   const int ndw = in_i16 ? span / 2 : span;
-  return (in_i16 ? ndw + (ndw >> 5) : ndw + 2 * (ndw >> 6)) + 2 <= kLdsFloats;
+  return ndw + 4 <= kRegion;
 }
 
-int pcm400_frames_per_tile() { return kTileFrames; }
-int pcm400_min_rows_per_tile(const lm_plan *) { return kThreads / 64; }
+StatLayout pcm400_stat_layout(const lm_plan *p) {
+  StatLayout st;
+  st.frames_per_tile = kSub;
+  st.sub_per_tile = 1;
+  st.blk_per_sub = 4 * ((p->n_mels + 15) / 16);
+  st.band_h = 4;
+  st.max_per_tile = 1;
+  return st;
+}
 
 hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &pa, hipStream_t s) {
   Args k;
   k.pcm = pa.pcm;
   k.T = pa.n_samples;
   k.F = pa.n_frames;
-  k.tiles_per_clip = pa.tiles_per_clip;
+  k.S = pa.tiles_per_clip;
+  k.n_sub = pa.n_clips * pa.tiles_per_clip;
+  const int64_t want = (k.n_sub + kWaves - 1) / kWaves;   // workgroups with >= 8 sub-tiles each
+  const int64_t n_wg = want < p->n_cu ? want : p->n_cu;
+  k.per_wg = (int)((k.n_sub + n_wg - 1) / n_wg);
   k.hop = p->hop;
   k.pad = p->center ? 200 : 0;
   k.pad_mode = p->pad_mode;
   k.power = p->power;
+  // every power value is 4 |X|^2; int16 samples carry 2^15 per |X|
   const float in_scale2 = pa.in_i16 ? 1.0f / 1073741824.0f : 1.0f;   // 2^-30
   if (p->power == 2.0f) {
     k.mel_scale = 0.25f * in_scale2;
@@ -412,23 +472,22 @@ hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &pa, hipStream_t s) {
   }
   k.n_mels = p->n_mels;
   k.n_melblk = p->dt.n_melblk;
-  k.amat = reinterpret_cast<const v4f *>(p->dt.mfma400);
-  k.out = pa.out;
+  k.melw_n = p->melblk_w.size() <= (size_t)kMelWLds ? (int)p->melblk_w.size() : 0;
   k.tile_max = pa.tile_max;
-  k.melw_lds = p->melblk_w.size() <= (size_t)kMelWLds ? (int)p->melblk_w.size() : 0;
-  const dim3 grid((unsigned)(pa.n_clips * pa.tiles_per_clip)), block(kThreads);
+  const dim3 grid((unsigned)n_wg), block(kThreads);
   const bool f16 = p->out_dtype == LM_F16;
+  const v4f *am = reinterpret_cast<const v4f *>(p->dt.mfma400);
   const int32_t *bm = p->dt.melblk_meta;
   const float *bw = p->dt.melblk_w;
   float *tm = pa.tile_min;
   if (!pa.in_i16 && !f16)
-    hipLaunchKernelGGL((pcm400_kernel<float, float>), grid, block, 0, s, k, bm, bw, (float *)pa.out, tm);
+    hipLaunchKernelGGL((pcm400_kernel<float, float>), grid, block, 0, s, k, am, bm, bw, (float *)pa.out, tm);
   else if (!pa.in_i16 && f16)
-    hipLaunchKernelGGL((pcm400_kernel<float, __half>), grid, block, 0, s, k, bm, bw, (__half *)pa.out, tm);
+    hipLaunchKernelGGL((pcm400_kernel<float, __half>), grid, block, 0, s, k, am, bm, bw, (__half *)pa.out, tm);
   else if (pa.in_i16 && !f16)
-    hipLaunchKernelGGL((pcm400_kernel<int16_t, float>), grid, block, 0, s, k, bm, bw, (float *)pa.out, tm);
+    hipLaunchKernelGGL((pcm400_kernel<int16_t, float>), grid, block, 0, s, k, am, bm, bw, (float *)pa.out, tm);
   else
-    hipLaunchKernelGGL((pcm400_kernel<int16_t, __half>), grid, block, 0, s, k, bm, bw, (__half *)pa.out, tm);
+    hipLaunchKernelGGL((pcm400_kernel<int16_t, __half>), grid, block, 0, s, k, am, bm, bw, (__half *)pa.out, tm);
   return hipGetLastError();
 }
 

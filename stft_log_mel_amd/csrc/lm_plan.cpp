@@ -77,34 +77,35 @@ void build_twiddles(lm_plan *p) {
 // n1 in matrix-core lane order: entry [n1][lane][j] = M_n1[lane % 16][4 j +
 // lane / 16].
 void build_mfma400(lm_plan *p) {
-  static const int kPairs[4][2] = {{1, 7}, {2, 6}, {3, 5}, {0, 4}};
-  p->mfma400.assign(25 * 64 * 4, 0.0f);
-  const double *w = nullptr;
+  // Matrix M_n1 (16 x 16) maps the samples y[n1 + 25 n2], n2 < 16, of 16
+  // frames to row m: group g = m / 4 holds classes g + 1 (rows 4g, 4g+1,
+  // real/imag) and 7 - g (rows 4g+2, 4g+3) for g < 3; group 3 holds class 4
+  // (rows 12, 13) and the sums over even / odd n2 (rows 14, 15).  Class rows
+  // are scaled by 2, so that every power value comes out as 4 |X|^2 like
+  // the even/odd split's |2 S|^2.  Class k row: w[n] (cos, -sin)(2 pi k n / 400), n = n1 +
+  // 25 n2 (angles reduced exactly in integers).  Operand for step j, lane l:
+  // M_n1[l % 16][4 (l / 16) + j]; stored as [j][n1 / 4][lane][n1 % 4], zero
+  // for n1 >= 25.
+  static const int kA[4] = {1, 2, 3, 4}, kB[3] = {7, 6, 5};
   std::vector<double> win(400);
   for (int n = 0; n < 400; ++n) win[n] = 0.5 - 0.5 * std::cos(2.0 * M_PI * (double)n / 400.0);
-  w = win.data();
-  for (int n1 = 0; n1 < 25; ++n1) {
-    double M[16][16];
-    for (int m = 0; m < 16; ++m) {
-      const int g = m / 4, isb = (m / 2) & 1, part = m & 1;
-      const int k2 = kPairs[g][isb];
-      for (int r = 0; r < 16; ++r) {
-        const int n2 = r & 7, e = r >> 3;
-        const int n = n1 + 25 * n2;
-        const long ang = ((long)k2 * n) % 200;
-        const double th = 2.0 * M_PI * (double)ang / 200.0;
-        const double cr = std::cos(th), ci = -std::sin(th);
-        const double we = w[2 * n], wo = w[2 * n + 1];
-        double v;
-        if (part == 0) v = (e == 0) ? we * cr : -wo * ci;   // real part
-        else v = (e == 0) ? we * ci : wo * cr;              // imaginary part
-        M[m][r] = v;
-      }
-    }
+  p->mfma400.assign(4 * 7 * 64 * 4, 0.0f);
+  for (int n1 = 0; n1 < 25; ++n1)
     for (int lane = 0; lane < 64; ++lane)
-      for (int j = 0; j < 4; ++j)
-        p->mfma400[((size_t)n1 * 64 + lane) * 4 + j] = (float)M[lane % 16][4 * j + lane / 16];
-  }
+      for (int j = 0; j < 4; ++j) {
+        const int m = lane % 16, n2 = 4 * (lane / 16) + j, n = n1 + 25 * n2;
+        const int g = m / 4, sub = m % 4;
+        double v;
+        if (g == 3 && sub >= 2) {
+          v = ((n2 & 1) == sub - 2) ? win[n] : 0.0;
+        } else {
+          const int k = sub < 2 ? kA[g] : kB[g];
+          const double sc = 2.0;
+          const double th = 2.0 * M_PI * (double)(((long)k * n) % 400) / 400.0;
+          v = sc * win[n] * ((sub & 1) == 0 ? std::cos(th) : -std::sin(th));
+        }
+        p->mfma400[(((size_t)j * 7 + n1 / 4) * 64 + lane) * 4 + n1 % 4] = (float)v;
+      }
 }
 
 // Blocked copy of a packed filterbank for the matrix-core mel sum:
