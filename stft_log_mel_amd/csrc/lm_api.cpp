@@ -1,6 +1,7 @@
 // C-ABI entry points: per-call validation, device tables and workspace,
 // and the launch sequence (main kernel, then the per-clip clamp fix-up) on
 // the caller's stream.
+#include <algorithm>
 #include <cstring>
 
 #include "lm_internal.h"
@@ -38,8 +39,11 @@ int upload_tables(lm_plan *p) {
   size_t o_w = align256(o_of + sizeof(int32_t) * NM);
   size_t o_mf = align256(o_w + sizeof(float) * (nnz > 0 ? nnz : 1));
   size_t o_bm = align256(o_mf + sizeof(float) * p->mfma400.size());
-  size_t o_bw = align256(o_bm + sizeof(int32_t) * p->melblk_meta.size());
-  size_t total = align256(o_bw + sizeof(float) * p->melblk_w.size() + 16);
+  // meta is read as 16 blocks' worth whatever the block count (zeros past it)
+  size_t o_bw = align256(o_bm + sizeof(int32_t) * std::max<size_t>(48, p->melblk_meta.size()));
+  // blocked weights are followed by one zero batch: the mel loop prefetches
+  // a batch past the last block
+  size_t total = align256(o_bw + sizeof(float) * (p->melblk_w.size() + 64 * kMelBatch) + 16);
   std::vector<unsigned char> host(total, 0);
   std::memcpy(host.data() + o_win, p->window.data(), sizeof(float) * N);
   std::memcpy(host.data() + o_tw, p->twiddle.data(), sizeof(float) * 2 * M);

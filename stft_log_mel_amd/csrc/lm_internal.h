@@ -12,6 +12,14 @@
 
 namespace lm {
 
+// Power row stride (floats) of the n_fft = 400 kernel: bins 0..200 plus
+// zeroed padding that chunked mel reads may touch (20 c mod 64 spreads 16
+// rows over distinct bank quads).
+constexpr int kPcm400Row = 212;
+// Chunks of 4 bins the n_fft = 400 mel loop takes per step; every band
+// block's chunk count is a multiple of it.
+constexpr int kMelBatch = 4;
+
 // Set the thread-local error text and return `status`.
 int fail(int status, const std::string &msg);
 int hip_fail(hipError_t err, const char *what);

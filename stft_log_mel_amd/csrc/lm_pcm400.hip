@@ -42,10 +42,10 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSub = 16;                  // frames per wave step (the matrix-core N)
-constexpr int kRow = 204;                 // power row stride: 12 c mod 64 puts 16 rows on distinct bank quads
+constexpr int kRow = kPcm400Row;          // power row stride
 constexpr int kRegion = kSub * kRow;      // floats of LDS per wave: staged samples, then power rows
 constexpr int kAmat = 4 * 7 * 64;         // first-stage operands (v4f): [j][n1 / 4][lane]
-constexpr int kMelWLds = 4096;            // blocked filter weights staged in LDS up to this count
+constexpr int kMelWLds = 6400;            // LDS floats for the blocked filter weights (and one zero batch)
 constexpr int kPfI16 = 6, kPfF32 = 11;    // 16-byte sample loads per lane held for the next sub-tile
 
 // compile-time cos/sin of 2 pi j / N for N a multiple of 8 (octant reduction
@@ -154,7 +154,7 @@ struct Args {
   int hop, pad, pad_mode;
   float power, pre_scale, mel_scale;
   int n_mels, n_melblk;
-  int melw_n;            // blocked weights staged in LDS (count <= kMelWLds), else 0
+  int melw_n;            // blocked weight count (plus 64 kMelBatch zeros fit kMelWLds)
   float *tile_max;
 };
 
@@ -254,11 +254,14 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
   __shared__ v4f s_amat[kAmat];
   __shared__ float s_melw[kMelWLds];
   __shared__ __attribute__((aligned(16))) float s_reg[kWaves * kRegion];
+  __shared__ int s_meta[3 * 16];   // per block: klo, chunks, weight offset
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   for (int i = tid; i < kAmat; i += kThreads) s_amat[i] = amat[i];
-  for (int i = tid; i < a.melw_n; i += kThreads) s_melw[i] = melblk_w[i] * a.mel_scale;
+  if (tid < 3 * 16) s_meta[tid] = melblk_meta[tid];   // the table holds 16 blocks' worth
+  for (int i = tid; i < a.melw_n + 64 * kMelBatch; i += kThreads)
+    s_melw[i] = i < a.melw_n ? melblk_w[i] * a.mel_scale : 0.0f;
   __syncthreads();
 
   const IN *__restrict__ pcm = reinterpret_cast<const IN *>(a.pcm);
@@ -269,7 +272,6 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
   const bool g3 = g == 3;
   const int NM = a.n_mels, NB = a.n_melblk;
   const int64_t F = a.F;
-  const float *wbase = a.melw_n ? s_melw : melblk_w;
 
   const int64_t wg0 = (int64_t)blockIdx.x * a.per_wg;
   const int64_t wg_end = min(wg0 + a.per_wg, a.n_sub);
@@ -376,7 +378,11 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
         else q2[st2 * j] = p2;
       }
     }
-    if (lane < 48) R[(lane / 3) * kRow + 201 + lane % 3] = 0.0f;   // pad columns read by the last chunks
+    // zero the pad columns 201..211 of the lane's row, which the last chunks read
+    static_assert(kRow == 212, "pad columns below assume 11 of them");
+    Rc[201 + g] = 0.0f;
+    Rc[205 + g] = 0.0f;
+    if (g < 3) Rc[209 + g] = 0.0f;
     if (a.power != 2.0f) {
       // |X|^p = (|X|^2)^(p/2) in place over the wave's rows
       const float pe = 0.5f * a.power;
@@ -384,38 +390,93 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
     }
 
     // 5. mel sums on the matrix cores: bands in blocks of 16, each over the
-    //    4-bin chunks its filters touch.  A = blocked weights (lane order,
-    //    pre-scaled when staged), B = P[frame c][bin klo + 4 ch + g]; lane (c,
-    //    g) gets bands 16 jb + 4 g + r of frame c.
+    //    4-bin chunks its filters touch (a multiple of kMelBatch chunks).  A =
+    //    blocked weights (lane order, pre-scaled, in LDS), B = P[frame c][bin
+    //    klo + 4 ch + g]; lane (c, g) gets bands 16 jb + 4 g + r of frame c.
+    //    Operands go through two register sets: the next batch (or the next
+    //    block's first) is loaded while the current one is multiplied.
     const SubTile t = locate(a, gs);
     const int64_t fr = t.s * kSub + c;
     const bool valid = fr < F;
     OUT *__restrict__ ocol = out + t.b * (int64_t)NM * F + fr;
     const float *pb0 = Rc + g;
-    const float sc = a.melw_n ? 1.0f : a.mel_scale;
     float vmax = 0.0f;
-    for (int jb = 0; jb < 16; ++jb) {
-      if (jb >= NB) break;
-      const int klo = melblk_meta[3 * jb], nch = melblk_meta[3 * jb + 1], toff = melblk_meta[3 * jb + 2];
-      const float *wt = wbase + toff + lane;
-      const float *pb = pb0 + klo;
+    float wA[kMelBatch], pA[kMelBatch], wB[kMelBatch], pB[kMelBatch];
+    const float *wt = s_melw + s_meta[2] + lane, *pp = pb0 + s_meta[0];
+    int nch = s_meta[1];
+#pragma unroll
+    for (int u = 0; u < kMelBatch; ++u) {
+      wA[u] = wt[64 * u];
+      pA[u] = pp[4 * u];
+    }
+    for (int jb = 0; jb < NB; ++jb) {
+      const int nb = nch / kMelBatch;
+      const int jn = jb + 1 < NB ? jb + 1 : jb;
+      const float *wn = s_melw + s_meta[3 * jn + 2] + lane, *pn = pb0 + s_meta[3 * jn];
+      const int nch_n = s_meta[3 * jn + 1];
       v4f acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
-      int ch = 0;
-      for (; ch + 1 < nch; ch += 2) {
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(wt[64 * ch], pb[4 * ch], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(wt[64 * ch + 64], pb[4 * ch + 4], acc1, 0, 0, 0);
+      if (nb == 0) {   // nothing to multiply; the held operands become the next block's
+#pragma unroll
+        for (int u = 0; u < kMelBatch; ++u) {
+          wA[u] = wn[64 * u];
+          pA[u] = pn[4 * u];
+        }
+      } else {
+        for (int k = 0;;) {
+          {
+            const bool in = k + 1 < nb;
+            const float *wq = in ? wt + 64 * kMelBatch * (k + 1) : wn;
+            const float *pq = in ? pp + 4 * kMelBatch * (k + 1) : pn;
+#pragma unroll
+            for (int u = 0; u < kMelBatch; ++u) {
+              wB[u] = wq[64 * u];
+              pB[u] = pq[4 * u];
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < kMelBatch; u += 2) {
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(wA[u], pA[u], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(wA[u + 1], pA[u + 1], acc1, 0, 0, 0);
+          }
+          if (++k >= nb) {
+#pragma unroll
+            for (int u = 0; u < kMelBatch; ++u) {
+              wA[u] = wB[u];
+              pA[u] = pB[u];
+            }
+            break;
+          }
+          {
+            const bool in = k + 1 < nb;
+            const float *wq = in ? wt + 64 * kMelBatch * (k + 1) : wn;
+            const float *pq = in ? pp + 4 * kMelBatch * (k + 1) : pn;
+#pragma unroll
+            for (int u = 0; u < kMelBatch; ++u) {
+              wA[u] = wq[64 * u];
+              pA[u] = pq[4 * u];
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < kMelBatch; u += 2) {
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(wB[u], pB[u], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(wB[u + 1], pB[u + 1], acc1, 0, 0, 0);
+          }
+          if (++k >= nb) break;
+        }
       }
-      if (ch < nch) acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(wt[64 * ch], pb[4 * ch], acc0, 0, 0, 0);
+      wt = wn;
+      pp = pn;
+      nch = nch_n;
       float lmn = __builtin_huge_valf();
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = 16 * jb + 4 * g + r;
-        const float v = fmaxf((acc0[r] + acc1[r]) * sc, 1e-10f);
+        const float v = fmaxf(acc0[r] + acc1[r], 1e-10f);
         const float L = log10_pos(v);
         if (valid && m < NM) {
           vmax = fmaxf(vmax, v);
           lmn = fminf(lmn, L);
-          store_out_nt(ocol + (int64_t)m * F, rescale(L));
+          store_out(ocol + (int64_t)m * F, rescale(L));
         }
       }
       lmn = row_min16(lmn);
@@ -429,9 +490,11 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
 }  // namespace
 
 // The n_fft = 400 path needs an even hop (runs of samples keep a parity
-// known at compile time) and a 16-frame span that fits the wave's region.
+// known at compile time), a 16-frame span that fits the wave's region and a
+// blocked filter table that fits its LDS share.
 bool pcm400_supported(const lm_plan *p, bool in_i16) {
   if (p->n_fft != 400 || (p->hop & 1) || p->mfma400.empty() || p->n_mels > 256) return false;
+  if (p->melblk_w.size() + 64 * kMelBatch > (size_t)kMelWLds) return false;
   const int span = (kSub - 1) * p->hop + 400;
   const int ndw = in_i16 ? span / 2 : span;
   return ndw + 4 <= kRegion;
@@ -472,7 +535,7 @@ hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &pa, hipStream_t s) {
   }
   k.n_mels = p->n_mels;
   k.n_melblk = p->dt.n_melblk;
-  k.melw_n = p->melblk_w.size() <= (size_t)kMelWLds ? (int)p->melblk_w.size() : 0;
+  k.melw_n = (int)p->melblk_w.size();
   k.tile_max = pa.tile_max;
   const dim3 grid((unsigned)n_wg), block(kThreads);
   const bool f16 = p->out_dtype == LM_F16;

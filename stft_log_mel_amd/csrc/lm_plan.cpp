@@ -108,13 +108,17 @@ void build_mfma400(lm_plan *p) {
       }
 }
 
-// Blocked copy of a packed filterbank for the matrix-core mel sum:
-// bands in blocks of 16; block j covers bins [klo, klo + 4 nch) where
-// [klo, khi) is the union of its bands' supports; chunk c of block j is
+// Blocked copy of a packed filterbank for the matrix-core mel sum (n_fft =
+// 400 only): bands in blocks of 16; block j covers bins [klo, klo + 4 nch)
+// which contains the union of its bands' supports, nch a multiple of
+// kMelBatch; chunk c of block j is
 // stored in matrix-core lane order, entry [lane] = W[16 j + lane % 16][klo +
 // 4 c + lane / 16] (0 outside a band's support or past the last band).
 // meta holds (klo, nch, offset in floats) per block.
 void build_mel_blocks(lm_plan *p) {
+  p->melblk_meta.clear();
+  p->melblk_w.clear();
+  if (p->n_fft != 400) return;
   const Csr &c = p->csr;
   const int NM = c.n_rows, NB = (NM + 15) / 16;
   p->melblk_meta.assign(3 * (size_t)NB, 0);
@@ -130,7 +134,10 @@ void build_mel_blocks(lm_plan *p) {
       klo = 0;
       khi = 0;
     }
-    const int nch = (khi - klo + 3) / 4;
+    // chunk count padded to whole batches; the padded range starts early
+    // enough to end inside the power row (its extra bins have zero weight)
+    const int nch = (khi - klo + 4 * kMelBatch - 1) / (4 * kMelBatch) * kMelBatch;
+    klo = std::min(klo, kPcm400Row - 4 * nch);
     p->melblk_meta[3 * j] = klo;
     p->melblk_meta[3 * j + 1] = nch;
     p->melblk_meta[3 * j + 2] = (int)p->melblk_w.size();
