@@ -215,11 +215,10 @@ int lm_from_stft(lm_plan *p, const void *stft, const float *mel_filters, int64_t
   if (rc != LM_OK) return rc;
   float *tmin = p->d_stats, *tmax = p->d_stats + n_clips * tiles;
 
-  const int32_t *cs, *cw, *co;
-  const float *w;
-  int w_len;
+  StftArgs a{reinterpret_cast<const float2 *>(stft), n_clips, n_frames, (int)n_bins, n_mels, tf, (int)tiles,
+             nullptr, nullptr, nullptr, nullptr, 0, out, p->out_dtype == LM_F16, tmin, tmax, p->n_cu};
   if (mel_filters) {
-    const size_t need = sizeof(int32_t) * 3 * n_mels + sizeof(float) * (size_t)n_mels * n_bins;
+    const size_t need = sizeof(int32_t) * 2 * n_mels;
     if (need > p->pack_cap) {
       if (p->d_pack) {
         hipError_t e = hipFree(p->d_pack);
@@ -231,23 +230,20 @@ int lm_from_stft(lm_plan *p, const void *stft, const float *mel_filters, int64_t
       if (e != hipSuccess) return hip_fail(e, "hipMalloc(pack)");
       p->pack_cap = need;
     }
-    rc = timed_launch(p, s, 2, "launch(filter pack)",
-                      [&] { return launch_pack(mel_filters, n_mels, (int)n_bins, p->d_pack, s); });
+    int32_t *sw = reinterpret_cast<int32_t *>(p->d_pack);
+    rc = timed_launch(p, s, 2, "launch(filter rows)",
+                      [&] { return launch_pack(mel_filters, n_mels, (int)n_bins, sw, s); });
     if (rc != LM_OK) return rc;
-    cs = reinterpret_cast<const int32_t *>(p->d_pack);
-    cw = cs + n_mels;
-    co = cw + n_mels;
-    w = reinterpret_cast<const float *>(co + n_mels);
-    w_len = n_mels * (int)n_bins;
+    a.f_start = sw;
+    a.f_width = sw + n_mels;
+    a.f_w = mel_filters;
+    a.f_stride = (int)n_bins;
   } else {
-    cs = p->dt.csr_start;
-    cw = p->dt.csr_width;
-    co = p->dt.csr_off;
-    w = p->dt.csr_w;
-    w_len = p->dt.nnz;
+    a.f_start = p->dt.csr_start;
+    a.f_width = p->dt.csr_width;
+    a.f_off = p->dt.csr_off;
+    a.f_w = p->dt.csr_w;
   }
-  StftArgs a{reinterpret_cast<const float2 *>(stft), n_clips, n_frames, (int)n_bins, n_mels, tf, (int)tiles,
-             cs, cw, co, w, w_len, out, p->out_dtype == LM_F16, tmin, tmax};
   rc = timed_launch(p, s, 0, "launch(stft kernel)", [&] { return launch_stft(a, s); });
   if (rc != LM_OK) return rc;
   StatLayout st;

@@ -142,21 +142,24 @@ struct StftArgs {
   int64_t n_clips, n_frames;
   int n_bins, n_mels;
   int frames_per_tile, tiles_per_clip;
-  const int32_t *csr_start, *csr_width, *csr_off;
-  const float *csr_w;
-  int w_len;            // floats allocated at csr_w (>= the packed weight count)
+  // band m covers bins [f_start[m], f_start[m] + f_width[m]); its weights are
+  // at f_w + m * f_stride + f_start[m] (f_stride > 0: rows of a dense
+  // matrix) or at f_w + f_off[m] (f_stride == 0: rows packed back to back)
+  const int32_t *f_start, *f_width, *f_off;
+  const float *f_w;
+  int f_stride;
   void *out;
   int out_f16;
   float *tile_min;
   float *tile_max;
+  int n_cu;
 };
 int stft_frames_per_tile(int n_bins, int n_mels);
 hipError_t launch_stft(const StftArgs &a, hipStream_t s);
 
-// Pack a device dense (n_mels, n_bins) filterbank into `ws` laid out as
-// [start n_mels][width n_mels][off n_mels] int32 then [w n_mels*n_bins] f32
-// (rows back to back, row m's weights at w[off[m] + j], j < width[m]).
-hipError_t launch_pack(const float *dense, int n_mels, int n_bins, void *ws, hipStream_t s);
+// First non-zero bin and width of every row of a device dense (n_mels,
+// n_bins) filterbank into start_width[0, n_mels) and [n_mels, 2 n_mels).
+hipError_t launch_pack(const float *dense, int n_mels, int n_bins, int32_t *start_width, hipStream_t s);
 
 struct FixupArgs {
   void *out;

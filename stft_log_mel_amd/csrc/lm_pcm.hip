@@ -224,21 +224,28 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
   // 4. mel sums, log10, rescale, mel-major store
   float vmax = 0.0f, lmin = __builtin_huge_valf();
   OUT *__restrict__ out = reinterpret_cast<OUT *>(a.out) + b * (int64_t)NM * F;
-  for (int o = tid; o < NM * FPB; o += THREADS) {
-    const int fl = o % FPB, m = o / FPB;
-    const int64_t fr = f0 + fl;
-    if (fr >= F) continue;
-    const int st = s_start[m], wd = s_width[m];
-    const float *pr = P + fl * (M + 1) + st;
-    float acc = 0.0f;
-    const float *wr = (w_in_lds ? s_w : a.csr_w) + s_off[m];
-    for (int j = 0; j < wd; ++j) acc = __builtin_fmaf(wr[j], pr[j], acc);
-    const float v = fmaxf(acc * a.mel_scale, 1e-10f);
-    const float L = log10_pos(v);
-    vmax = fmaxf(vmax, v);
-    lmin = fminf(lmin, L);
-    store_out_nt(out + (int64_t)m * F + fr, rescale(L));
-  }
+  // one copy of the loop per weight source, so LDS weights are read with LDS
+  // instructions (a pointer that may point either way would make every
+  // weight load a flat load that waits for all outstanding global loads)
+  auto mel = [&](const float *wsrc) {
+    for (int o = tid; o < NM * FPB; o += THREADS) {
+      const int fl = o % FPB, m = o / FPB;
+      const int64_t fr = f0 + fl;
+      if (fr >= F) continue;
+      const int st = s_start[m], wd = s_width[m];
+      const float *pr = P + fl * (M + 1) + st;
+      float acc = 0.0f;
+      const float *wr = wsrc + s_off[m];
+      for (int j = 0; j < wd; ++j) acc = __builtin_fmaf(wr[j], pr[j], acc);
+      const float v = fmaxf(acc * a.mel_scale, 1e-10f);
+      const float L = log10_pos(v);
+      vmax = fmaxf(vmax, v);
+      lmin = fminf(lmin, L);
+      store_out(out + (int64_t)m * F + fr, rescale(L));
+    }
+  };
+  if (w_in_lds) mel(s_w);
+  else mel(a.csr_w);
 
   // 5. tile statistics
   block_maxmin<THREADS>(vmax, lmin, s_red);

@@ -1,10 +1,11 @@
 // Complex STFT -> log-mel (KBench task page "audio-mel-spectrogram-fused",
 // sections "reference_src", "spec_md", "contract_md", "perf_md").
 //
-// The source is read exactly once.  A workgroup owns TF consecutive frames
-// of one clip; those frames are one contiguous run of TF*NF complex64
-// values, streamed with 16-byte non-temporal loads (two bins per load) and
-// turned into power re^2 + im^2 straight into an LDS tile.  Each (frame,
+// The source is read exactly once.  A tile is TF consecutive frames of one
+// clip; those frames are one contiguous run of TF*NF complex64 values,
+// streamed with 16-byte non-temporal loads (two bins per load) and turned
+// into power re^2 + im^2 straight into an LDS tile.  Workgroups are
+// persistent (a few per compute unit) and take tiles in turn.  Each (frame,
 // band) output is then the packed triangular mel sum over that tile, log10
 // after the 1e-10 floor, (L+4)/4, stored frame-major so a tile's outputs
 // are one contiguous run.  The tile's largest mel value and smallest log
@@ -18,16 +19,19 @@
 namespace lm {
 
 constexpr int kStftThreads = 256;
+constexpr int kStftNW = kStftThreads / 64;
 constexpr int kStftLoadUnroll = 8;
-constexpr int kStftCsrLds = 2048;   // packed weights staged in LDS up to this count
+constexpr int kStftWLds = 2048;     // LDS floats for the staged filter weights
+constexpr int kStftWgPerCu = 4;     // resident workgroups per compute unit
 
 struct StftKernelArgs {
   const float2 *stft;
   int64_t F;
   int NF, NM, TF, tiles_per_clip;
-  const int32_t *csr_start, *csr_width, *csr_off;
-  const float *csr_w;
-  int w_len;
+  int64_t n_tiles;
+  const int32_t *f_start, *f_width, *f_off;
+  const float *f_w;
+  int f_stride;
   void *out;
   float *tile_min, *tile_max;
 };
@@ -36,21 +40,19 @@ __device__ __forceinline__ float pw(float2 v) { return __builtin_fmaf(v.x, v.x, 
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
+// One tile: power of TF frames into P (LDS), then the mel sums, log10,
+// rescale, frame-major store and the tile's statistics.  `wsrc` + s_off[m]
+// is band m's first weight, in LDS or in global memory.
 template <typename OUT, bool VEC16>
-__global__ void __launch_bounds__(kStftThreads) stft_logmel_kernel(StftKernelArgs a) {
-  extern __shared__ float s_dyn[];      // [TF*NF power tile][kStftCsrLds weights]
-  __shared__ int32_t s_start[256], s_width[256], s_off[256];
-  __shared__ float s_red[2 * kStftThreads / 64];
-
+__device__ __forceinline__ void stft_tile(const StftKernelArgs &a, int64_t tile, float *P, const float *wsrc,
+                                          const int32_t *s_start, const int32_t *s_width, const int32_t *s_off,
+                                          float *s_red) {
   const int tid = threadIdx.x;
-  const int64_t tile = blockIdx.x;
   const int64_t b = tile / a.tiles_per_clip;
   const int t = (int)(tile - b * a.tiles_per_clip);
   const int64_t f0 = (int64_t)t * a.TF;
   const int nfr = (int)min((int64_t)a.TF, a.F - f0);
   const int NF = a.NF, NM = a.NM;
-  float *P = s_dyn;
-  float *s_w = s_dyn + a.TF * NF;
 
   // 1. power tile: elements [e0, e0 + n) of the flat complex array
   const int64_t e0 = (b * a.F + f0) * NF;
@@ -80,11 +82,7 @@ __global__ void __launch_bounds__(kStftThreads) stft_logmel_kernel(StftKernelArg
   } else {
     for (int i = tid; i < n; i += kStftThreads) P[i] = pw(a.stft[e0 + i]);
   }
-
-  // packed filterbank -> LDS (ends with a barrier, which also covers the power tile)
-  const int nnz = stage_filters<kStftThreads>(NM, a.csr_start, a.csr_width, a.csr_off, a.csr_w, a.w_len, s_start,
-                                              s_width, s_off, s_w, kStftCsrLds);
-  const bool w_in_lds = nnz <= kStftCsrLds;
+  __syncthreads();
 
   // 2. mel sums, log10, rescale, frame-major store
   OUT *__restrict__ out = reinterpret_cast<OUT *>(a.out) + (b * a.F + f0) * NM;
@@ -94,8 +92,8 @@ __global__ void __launch_bounds__(kStftThreads) stft_logmel_kernel(StftKernelArg
   for (int o = tid; o < nfr * NM; o += kStftThreads) {
     const int st = s_start[m], wd = s_width[m];
     const float *pr = P + f * NF + st;
+    const float *wr = wsrc + s_off[m];
     float acc = 0.0f;
-    const float *wr = (w_in_lds ? s_w : a.csr_w) + s_off[m];
     for (int j = 0; j < wd; ++j) acc = __builtin_fmaf(wr[j], pr[j], acc);
     const float v = fmaxf(acc, 1e-10f);
     const float L = log10_pos(v);
@@ -110,11 +108,69 @@ __global__ void __launch_bounds__(kStftThreads) stft_logmel_kernel(StftKernelArg
     }
   }
 
-  // 3. tile statistics
+  // 3. tile statistics (the barrier inside also ends every read of P)
   block_maxmin<kStftThreads>(vmax, lmin, s_red);
   if (tid == 0) {
     a.tile_max[tile] = vmax;
     a.tile_min[tile] = lmin;
+  }
+  __syncthreads();
+}
+
+// Persistent: each workgroup stages the filter rows once, then takes tiles
+// blockIdx.x, + gridDim.x, ...
+template <typename OUT, bool VEC16>
+__global__ void __launch_bounds__(kStftThreads) stft_logmel_kernel(StftKernelArgs a) {
+  extern __shared__ float s_dyn[];      // [TF*NF power tile][kStftWLds weights]
+  __shared__ int32_t s_start[256], s_width[256], s_off[256];
+  __shared__ int32_t s_scan[kStftNW];
+  __shared__ float s_red[2 * kStftNW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int NM = a.NM;
+  float *P = s_dyn;
+  float *s_w = s_dyn + a.TF * a.NF;
+
+  // filter rows: start, width; offsets by a block scan of the widths (NM <= 256 = threads)
+  int st = 0, wd = 0;
+  if (tid < NM) {
+    st = a.f_start[tid];
+    wd = a.f_width[tid];
+  }
+  int incl = wd;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) s_scan[wv] = incl;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kStftNW; ++w) {
+    const int v = s_scan[w];
+    if (w < wv) base += v;
+    total += v;
+  }
+  const bool in_lds = total <= kStftWLds;
+  if (tid < NM) {
+    const int src = a.f_stride ? tid * a.f_stride + st : a.f_off[tid];
+    const int off = base + incl - wd;
+    s_start[tid] = st;
+    s_width[tid] = wd;
+    s_off[tid] = in_lds ? off : src;
+    if (in_lds)
+      for (int j = 0; j < wd; ++j) s_w[off + j] = a.f_w[src + j];
+  }
+  __syncthreads();
+
+  // one copy of the tile loop per weight source (see stft_tile)
+  if (in_lds) {
+    for (int64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x)
+      stft_tile<OUT, VEC16>(a, tile, P, s_w, s_start, s_width, s_off, s_red);
+  } else {
+    for (int64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x)
+      stft_tile<OUT, VEC16>(a, tile, P, a.f_w, s_start, s_width, s_off, s_red);
   }
 }
 
@@ -134,16 +190,18 @@ hipError_t launch_stft(const StftArgs &a, hipStream_t s) {
   k.NM = a.n_mels;
   k.TF = a.frames_per_tile;
   k.tiles_per_clip = a.tiles_per_clip;
-  k.csr_start = a.csr_start;
-  k.csr_width = a.csr_width;
-  k.csr_off = a.csr_off;
-  k.csr_w = a.csr_w;
-  k.w_len = a.w_len;
+  k.n_tiles = a.n_clips * a.tiles_per_clip;
+  k.f_start = a.f_start;
+  k.f_width = a.f_width;
+  k.f_off = a.f_off;
+  k.f_w = a.f_w;
+  k.f_stride = a.f_stride;
   k.out = a.out;
   k.tile_min = a.tile_min;
   k.tile_max = a.tile_max;
-  const size_t lds = sizeof(float) * ((size_t)a.frames_per_tile * a.n_bins + kStftCsrLds);
-  const dim3 grid((unsigned)(a.n_clips * a.tiles_per_clip)), block(kStftThreads);
+  const size_t lds = sizeof(float) * ((size_t)a.frames_per_tile * a.n_bins + kStftWLds);
+  const int64_t cap = (int64_t)a.n_cu * kStftWgPerCu;
+  const dim3 grid((unsigned)(k.n_tiles < cap ? k.n_tiles : cap)), block(kStftThreads);
   const bool vec16 = (reinterpret_cast<uintptr_t>(a.stft) & 15) == 0;
   if (a.out_f16) {
     if (vec16) hipLaunchKernelGGL((stft_logmel_kernel<__half, true>), grid, block, lds, s, k);
@@ -156,100 +214,46 @@ hipError_t launch_stft(const StftArgs &a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Dense (NM, NF) device filterbank -> packed rows (start, width, off, w),
-// the same layout as a plan's own table.  One workgroup of 16 waves: each
-// wave issues the loads of all its rows at once and reduces each row's
-// first and last non-zero; wave 0 lays out the offsets; then each wave
-// copies its rows' [first, last] weights.
+// Dense (NM, NF) device filterbank -> per-row first non-zero bin and width
+// (0 for an all-zero row).  One wave per row; the weights stay in the dense
+// matrix, which the STFT kernel reads at row m * NF + start[m].
 // ---------------------------------------------------------------------------
 
-constexpr int kPackThreads = 1024;
-constexpr int kPackWaves = kPackThreads / 64;
-constexpr int kPackRowsPerWave = 256 / kPackWaves;   // NM <= 256
-
-__global__ void __launch_bounds__(kPackThreads)
-pack_filters_kernel(const float *__restrict__ dense, int NM, int NF, int32_t *start, int32_t *width,
-                    int32_t *off, float *w) {
-  __shared__ int s_first[256], s_last[256], s_off[256];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int first[kPackRowsPerWave], last[kPackRowsPerWave];
+__global__ void __launch_bounds__(256) filter_rows_kernel(const float *__restrict__ dense, int NM, int NF,
+                                                          int32_t *start, int32_t *width) {
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= NM) return;
+  const float *row = dense + (size_t)m * NF;
+  int first = INT_MAX, last = -1;
+  for (int k0 = 0; k0 < NF; k0 += 256) {
+    float v[4];
 #pragma unroll
-  for (int r = 0; r < kPackRowsPerWave; ++r) {
-    first[r] = INT_MAX;
-    last[r] = -1;
-  }
-  for (int k0 = 0; k0 < NF; k0 += 64) {
-    const int k = k0 + lane;
-    float v[kPackRowsPerWave];
-#pragma unroll
-    for (int r = 0; r < kPackRowsPerWave; ++r) {
-      const int m = wv + r * kPackWaves;
-      v[r] = (m < NM && k < NF) ? dense[(size_t)m * NF + k] : 0.0f;
+    for (int u = 0; u < 4; ++u) {
+      const int k = k0 + 64 * u + lane;
+      v[u] = k < NF ? row[k] : 0.0f;
     }
 #pragma unroll
-    for (int r = 0; r < kPackRowsPerWave; ++r)
-      if (v[r] != 0.0f) {
-        first[r] = min(first[r], k);
-        last[r] = max(last[r], k);
+    for (int u = 0; u < 4; ++u)
+      if (v[u] != 0.0f) {
+        first = min(first, k0 + 64 * u + lane);
+        last = max(last, k0 + 64 * u + lane);
       }
   }
 #pragma unroll
-  for (int r = 0; r < kPackRowsPerWave; ++r) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      first[r] = min(first[r], __shfl_xor(first[r], o, 64));
-      last[r] = max(last[r], __shfl_xor(last[r], o, 64));
-    }
-    const int m = wv + r * kPackWaves;
-    if (lane == 0 && m < NM) {
-      s_first[m] = first[r];
-      s_last[m] = last[r];
-    }
+  for (int o = 32; o > 0; o >>= 1) {
+    first = min(first, __shfl_xor(first, o, 64));
+    last = max(last, __shfl_xor(last, o, 64));
   }
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    const int tid = threadIdx.x;
-    int wd[4], sum = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 4 * tid + i;
-      wd[i] = (m < NM && s_last[m] >= 0) ? s_last[m] - s_first[m] + 1 : 0;
-      sum += wd[i];
-    }
-    int incl = sum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_up(incl, o, 64);
-      if (tid >= o) incl += t;
-    }
-    int run = incl - sum;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 4 * tid + i;
-      if (m < NM) {
-        s_off[m] = run;
-        start[m] = wd[i] ? s_first[m] : 0;
-        width[m] = wd[i];
-        off[m] = run;
-      }
-      run += wd[i];
-    }
-  }
-  __syncthreads();
-  for (int m = wv; m < NM; m += kPackWaves) {
-    if (s_last[m] < 0) continue;
-    const int st = s_first[m], wd = s_last[m] - st + 1, o = s_off[m];
-    for (int j = lane; j < wd; j += 64) w[o + j] = dense[(size_t)m * NF + st + j];
+  if (lane == 0) {
+    start[m] = last >= 0 ? first : 0;
+    width[m] = last >= 0 ? last - first + 1 : 0;
   }
 }
 
-hipError_t launch_pack(const float *dense, int n_mels, int n_bins, void *ws, hipStream_t s) {
-  int32_t *start = reinterpret_cast<int32_t *>(ws);
-  int32_t *width = start + n_mels;
-  int32_t *off = width + n_mels;
-  float *w = reinterpret_cast<float *>(off + n_mels);
-  hipLaunchKernelGGL(pack_filters_kernel, dim3(1), dim3(kPackThreads), 0, s, dense, n_mels, n_bins, start, width,
-                     off, w);
+hipError_t launch_pack(const float *dense, int n_mels, int n_bins, int32_t *start_width, hipStream_t s) {
+  hipLaunchKernelGGL(filter_rows_kernel, dim3((unsigned)((n_mels + 3) / 4)), dim3(256), 0, s, dense, n_mels, n_bins,
+                     start_width, start_width + n_mels);
   return hipGetLastError();
 }
 
