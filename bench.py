@@ -179,21 +179,24 @@ def main():
             run_clip = lambda b: oracle.from_pcm(host_in[b:b + 1], w.n_fft, w.hop, W,    # noqa: E731
                                                  center=w.center, pad_mode=w.pad_mode, power=w.power)
         got = outs[(args.steps - 1) % nbuf].float().cpu().numpy()
+        # clips in order, cycling through the batch again until about
+        # cpu_seconds have passed; each clip's first pass is also a parity check
         t_cpu = time.perf_counter()
         done = 0
         errs = []
-        while done < w.B:
-            ref = run_clip(done)
-            errs.append(float(np.abs(got[done] - ref[0]).max()))
+        while True:
+            ref = run_clip(done % w.B)
+            if done < w.B:
+                errs.append(float(np.abs(got[done] - ref[0]).max()))
             done += 1
             if time.perf_counter() - t_cpu >= args.cpu_seconds:
                 break
         dt = time.perf_counter() - t_cpu
         cpu = {"value": round(done * w.n_frames / dt, 1), "unit": "frames/s", "cores": int(threads),
                "kind": "oracle",
-               "sample": f"{done} of {w.B} clips ({done * w.n_frames} frames) of the same workload, "
-                         f"fp64 numpy oracle, {dt:.1f}s"}
-        parity = {"clips_checked": done, "max_abs_err": max(errs),
+               "sample": f"{done} clips ({done * w.n_frames} frames) of the same workload, taken in order "
+                         f"and cycling through its {w.B} clips, fp64 numpy oracle, {dt:.1f}s"}
+        parity = {"clips_checked": len(errs), "max_abs_err": max(errs),
                   "tol": 2e-3 if w.out_dtype == "f16" else 1e-4}
         print(f"[bench] oracle: {done} clips in {dt:.1f}s, max |err| {max(errs):.2e}", file=sys.stderr,
               flush=True)
@@ -236,6 +239,7 @@ def main():
             "nominal_flop_per_frame": round(fpf, 1),
             "tflops": round(frames * fpf / (main_ms / 1e3) / 1e12, 2),
             "fp32_vector_peak_tflops": FP32_VALU_PEAK_TFLOPS,
+            "fp32_vector_unpacked_peak_tflops": FP32_VALU_PEAK_TFLOPS / 2,
         },
         "fixup_ms": round(fix_ms, 5),
         "pack_ms": round(pack_ms, 5),
