@@ -39,11 +39,8 @@ int upload_tables(lm_plan *p) {
   size_t o_w = align256(o_of + sizeof(int32_t) * NM);
   size_t o_mf = align256(o_w + sizeof(float) * (nnz > 0 ? nnz : 1));
   size_t o_bm = align256(o_mf + sizeof(float) * p->mfma400.size());
-  // meta is read as 16 blocks' worth whatever the block count (zeros past it)
-  size_t o_bw = align256(o_bm + sizeof(int32_t) * std::max<size_t>(48, p->melblk_meta.size()));
-  // blocked weights are followed by one zero batch: the mel loop prefetches
-  // a batch past the last block
-  size_t total = align256(o_bw + sizeof(float) * (p->melblk_w.size() + 64 * kMelBatch) + 16);
+  size_t o_bw = align256(o_bm + sizeof(int32_t) * p->melblk_meta.size());
+  size_t total = align256(o_bw + sizeof(float) * p->melblk_w.size() + 16);
   std::vector<unsigned char> host(total, 0);
   std::memcpy(host.data() + o_win, p->window.data(), sizeof(float) * N);
   std::memcpy(host.data() + o_tw, p->twiddle.data(), sizeof(float) * 2 * M);
@@ -87,7 +84,7 @@ int upload_tables(lm_plan *p) {
   p->dt.mfma400 = p->mfma400.empty() ? nullptr : reinterpret_cast<const float *>(c + o_mf);
   p->dt.melblk_meta = reinterpret_cast<const int32_t *>(c + o_bm);
   p->dt.melblk_w = reinterpret_cast<const float *>(c + o_bw);
-  p->dt.n_melblk = p->have_filters ? (int)(p->melblk_meta.size() / 3) : 0;
+  p->dt.n_melblk = p->have_filters ? (p->n_mels + 15) / 16 : 0;
   p->tables_dirty = false;
   return LM_OK;
 }

@@ -18,9 +18,10 @@
 // then run in registers (5 x 5, Winograd 5-point modules); the 50-point
 // real DFT is the 25-point complex DFT of z[m] = s[2m] + i s[2m+1] followed
 // by its split into real-input bins.  |X|^2 goes to the wave's own power
-// rows in LDS; the mel sums run on the matrix cores over blocks of 16 bands
-// and only the 4-bin chunks their filters touch; log10 after the 1e-10
-// floor, (L+4)/4, mel-major store (16 consecutive frames per band).
+// rows in LDS; the mel sums run on 4x4x1 matrix blocks (4 bands x 4 frames
+// per bin, 16 blocks per instruction) over the bins each quad of bands
+// touches; log10 after the 1e-10 floor, (L+4)/4, mel-major store (16
+// consecutive frames per band).
 //
 // One workgroup of 8 waves per compute unit walks a contiguous range of
 // 16-frame sub-tiles; its waves take every 8th one and never wait for each
@@ -45,7 +46,7 @@ constexpr int kSub = 16;                  // frames per wave step (the matrix-co
 constexpr int kRow = kPcm400Row;          // power row stride
 constexpr int kRegion = kSub * kRow;      // floats of LDS per wave: staged samples, then power rows
 constexpr int kAmat = 4 * 7 * 64;         // first-stage operands (v4f): [j][n1 / 4][lane]
-constexpr int kMelWLds = 6400;            // LDS floats for the blocked filter weights (and one zero batch)
+constexpr int kMelWLds = 6400;            // LDS floats for the mel step weights (and one zero batch)
 constexpr int kPfI16 = 6, kPfF32 = 11;    // 16-byte sample loads per lane held for the next sub-tile
 
 // compile-time cos/sin of 2 pi j / N for N a multiple of 8 (octant reduction
@@ -154,7 +155,7 @@ struct Args {
   int hop, pad, pad_mode;
   float power, pre_scale, mel_scale;
   int n_mels, n_melblk;
-  int melw_n;            // blocked weight count (plus 64 kMelBatch zeros fit kMelWLds)
+  int melw_n;            // mel step weight count (plus 16 kMelBatch zeros fit kMelWLds)
   float *tile_max;
 };
 
@@ -162,20 +163,10 @@ __device__ __forceinline__ float to_f(float v) { return v; }
 __device__ __forceinline__ float to_f(int16_t v) { return (float)(int)v; }
 
 template <typename IN>
-__device__ __forceinline__ float padded(const IN *__restrict__ x, int64_t j, int64_t T, int mode) {
-  if (j < 0 || j >= T) {
-    if (mode == LM_PAD_CONSTANT) return 0.0f;
-    if (mode == LM_PAD_REFLECT) j = j < 0 ? -j : 2 * (T - 1) - j;
-    else if (mode == LM_PAD_REPLICATE) j = j < 0 ? 0 : T - 1;
-    else j = ((j % T) + T) % T;
-  }
-  return to_f(x[j]);
-}
-
-template <typename IN>
 struct Prefetch {
   static constexpr int N = sizeof(IN) == 2 ? kPfI16 : kPfF32;
   u4 v[N];
+  int q_lo, q_hi;   // 16-byte chunks [q_lo, q_hi) of the span were loaded (uniform)
 };
 
 // Where sub-tile gs reads: clip b, samples [s_begin, s_begin + span) of it
@@ -192,59 +183,96 @@ __device__ __forceinline__ SubTile locate(const Args &a, int64_t gs) {
   return t;
 }
 
-// Issue the 16-byte loads of an interior, 16-byte aligned span (the rounded
-// up span must lie inside the clip); false if the span needs the padded path.
+// Issue the 16-byte loads of every chunk of the span that lies inside the
+// clip (the span must start 16-byte aligned); false if it does not, then
+// the whole span takes the padded path.
 template <typename IN>
 __device__ __forceinline__ bool prefetch(const Args &a, const IN *__restrict__ pcm, int64_t gs, int span,
                                          Prefetch<IN> &pf) {
-  constexpr int PER = 16 / sizeof(IN);   // samples per load
+  constexpr int PER = 16 / sizeof(IN);   // samples per chunk
   const int n4 = (span + PER - 1) / PER;
   const SubTile t = locate(a, gs);
   const IN *src = pcm + t.b * a.T + t.s_begin;
-  if (n4 > 64 * Prefetch<IN>::N || t.s_begin < 0 || t.s_begin + (int64_t)n4 * PER > a.T ||
-      (reinterpret_cast<uintptr_t>(src) & 15))
-    return false;
+  if (n4 > 64 * Prefetch<IN>::N || (reinterpret_cast<uintptr_t>(src) & 15)) return false;
+  // chunks q with 0 <= s_begin + PER q and s_begin + PER (q + 1) <= T
+  const int64_t lo = t.s_begin < 0 ? (-t.s_begin + PER - 1) / PER : 0;
+  const int64_t hi = (a.T - t.s_begin) / PER;
+  pf.q_lo = (int)min(lo, (int64_t)n4);
+  pf.q_hi = (int)max((int64_t)pf.q_lo, min(hi, (int64_t)n4));
   const u4 *s4 = reinterpret_cast<const u4 *>(src);
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < Prefetch<IN>::N; ++i)
-    if (lane + 64 * i < n4) pf.v[i] = s4[lane + 64 * i];
+  for (int i = 0; i < Prefetch<IN>::N; ++i) {
+    const int q = lane + 64 * i;
+    if (q >= pf.q_lo && q < pf.q_hi) pf.v[i] = s4[q];
+  }
   return true;
 }
 
-template <typename IN>
-__device__ __forceinline__ void put_prefetch(const Prefetch<IN> &pf, int span, float *R) {
-  constexpr int PER = 16 / sizeof(IN);
-  const int n4 = (span + PER - 1) / PER;
-  const int lane = threadIdx.x & 63;
-  u4 *d4 = reinterpret_cast<u4 *>(R);
-#pragma unroll
-  for (int i = 0; i < Prefetch<IN>::N; ++i)
-    if (lane + 64 * i < n4) d4[lane + 64 * i] = pf.v[i];
+// Source index of padded position j of a clip of T samples (0 <= result <
+// T), or -1 for a constant-mode zero.
+__device__ __forceinline__ int64_t pad_index(int64_t j, int64_t T, int mode) {
+  if (j >= 0 && j < T) return j;
+  if (mode == LM_PAD_CONSTANT) return -1;
+  if (mode == LM_PAD_REFLECT) return j < 0 ? -j : 2 * (T - 1) - j;
+  if (mode == LM_PAD_REPLICATE) return j < 0 ? 0 : T - 1;
+  return ((j % T) + T) % T;
 }
 
-// Padded path: every dword of the span by index arithmetic (positions past
-// the end of the clip's last frame read as 0).
+constexpr int kPadBatch = 8;   // dwords per lane with loads in flight together
+
+// Padded path for span dwords [d_begin, d_end): each by index arithmetic
+// (positions past the end of the clip's last frame read as 0), kPadBatch
+// dwords per lane with all their loads issued before any is used.
 template <typename IN>
-__device__ __forceinline__ void stage_padded(const Args &a, const IN *__restrict__ pcm, int64_t gs, int span,
-                                             float *R) {
+__device__ __forceinline__ void stage_padded(const Args &a, const IN *__restrict__ pcm, int64_t gs, int d_begin,
+                                             int d_end, float *R) {
   constexpr int PER_DW = 4 / sizeof(IN);
   const SubTile t = locate(a, gs);
   const IN *x = pcm + t.b * a.T;
   const int64_t s_limit = (a.F - 1) * (int64_t)a.hop - a.pad + 400;
   uint32_t *d32 = reinterpret_cast<uint32_t *>(R);
   const int lane = threadIdx.x & 63;
-  for (int d = lane; d < span / PER_DW; d += 64) {
-    uint32_t w = 0;
+  for (int d0 = d_begin + lane; d0 < d_end; d0 += 64 * kPadBatch) {
+    float v[kPadBatch][PER_DW];
 #pragma unroll
-    for (int e = 0; e < PER_DW; ++e) {
-      const int64_t j = t.s_begin + (int64_t)d * PER_DW + e;
-      const float v = j < s_limit ? padded(x, j, a.T, a.pad_mode) : 0.0f;
-      if (sizeof(IN) == 2) w |= (uint32_t)(uint16_t)(int16_t)(int)v << (16 * e);
-      else w = __float_as_uint(v);
+    for (int u = 0; u < kPadBatch; ++u)
+#pragma unroll
+      for (int e = 0; e < PER_DW; ++e) {
+        const int64_t j = t.s_begin + (int64_t)(d0 + 64 * u) * PER_DW + e;
+        const int64_t src = (d0 + 64 * u < d_end && j < s_limit) ? pad_index(j, a.T, a.pad_mode) : -1;
+        v[u][e] = src >= 0 ? to_f(x[src]) : 0.0f;
+      }
+#pragma unroll
+    for (int u = 0; u < kPadBatch; ++u) {
+      if (d0 + 64 * u >= d_end) break;
+      uint32_t w = 0;
+#pragma unroll
+      for (int e = 0; e < PER_DW; ++e) {
+        if (sizeof(IN) == 2) w |= (uint32_t)(uint16_t)(int16_t)(int)v[u][e] << (16 * e);
+        else w = __float_as_uint(v[u][e]);
+      }
+      d32[d0 + 64 * u] = w;
     }
-    d32[d] = w;
   }
+}
+
+// The prefetched chunks into the wave's region, then the span's dwords
+// outside them by the padded path.
+template <typename IN>
+__device__ __forceinline__ void put_prefetch(const Args &a, const IN *__restrict__ pcm, int64_t gs,
+                                             const Prefetch<IN> &pf, int span, float *R) {
+  constexpr int PER_DW = 4 / sizeof(IN);
+  const int lane = threadIdx.x & 63;
+  u4 *d4 = reinterpret_cast<u4 *>(R);
+#pragma unroll
+  for (int i = 0; i < Prefetch<IN>::N; ++i) {
+    const int q = lane + 64 * i;
+    if (q >= pf.q_lo && q < pf.q_hi) d4[q] = pf.v[i];
+  }
+  const int ndw = span / PER_DW;
+  if (pf.q_lo > 0) stage_padded<IN>(a, pcm, gs, 0, min(4 * pf.q_lo, ndw), R);
+  if (4 * pf.q_hi < ndw) stage_padded<IN>(a, pcm, gs, 4 * pf.q_hi, ndw, R);
 }
 
 template <typename IN, typename OUT>
@@ -254,14 +282,33 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
   __shared__ v4f s_amat[kAmat];
   __shared__ float s_melw[kMelWLds];
   __shared__ __attribute__((aligned(16))) float s_reg[kWaves * kRegion];
-  __shared__ int s_meta[3 * 16];   // per block: klo, chunks, weight offset
+  __shared__ int s_meta[2 * 16 + 64];   // per block: steps, weight offset; per quad: first bin
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  for (int i = tid; i < kAmat; i += kThreads) s_amat[i] = amat[i];
-  if (tid < 3 * 16) s_meta[tid] = melblk_meta[tid];   // the table holds 16 blocks' worth
-  for (int i = tid; i < a.melw_n + 64 * kMelBatch; i += kThreads)
-    s_melw[i] = i < a.melw_n ? melblk_w[i] * a.mel_scale : 0.0f;
+  {
+    // all loads of the operand table in flight at once
+    constexpr int PER = (kAmat + kThreads - 1) / kThreads;
+    v4f v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      if (tid + u * kThreads < kAmat) v[u] = amat[tid + u * kThreads];
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      if (tid + u * kThreads < kAmat) s_amat[tid + u * kThreads] = v[u];
+  }
+  if (tid < 2 * 16 + 64) s_meta[tid] = melblk_meta[tid];
+  for (int i0 = tid; i0 < a.melw_n + 16 * kMelBatch; i0 += 4 * kThreads) {
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * kThreads;
+      v[u] = i < a.melw_n ? melblk_w[i] * a.mel_scale : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i0 + u * kThreads < a.melw_n + 16 * kMelBatch) s_melw[i0 + u * kThreads] = v[u];
+  }
   __syncthreads();
 
   const IN *__restrict__ pcm = reinterpret_cast<const IN *>(a.pcm);
@@ -282,8 +329,8 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
   for (; gs < wg_end; gs += kWaves) {
     // 1. this sub-tile's samples into the wave's region (LDS operations of
     //    one wave complete in order, so no barrier is needed around them)
-    if (have) put_prefetch<IN>(pf, span, R);
-    else stage_padded<IN>(a, pcm, gs, span, R);
+    if (have) put_prefetch<IN>(a, pcm, gs, pf, span, R);
+    else stage_padded<IN>(a, pcm, gs, 0, span / (4 / (int)sizeof(IN)), R);
     have = gs + kWaves < wg_end && prefetch<IN>(a, pcm, gs + kWaves, span, pf);
 
     // 2. window + 16-point DFT + twiddle on the matrix cores: D[n1] += A[j][n1] x[j][n1].
@@ -389,54 +436,56 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
       for (int i = lane; i < kRegion; i += 64) R[i] = powf(R[i] * a.pre_scale, pe);
     }
 
-    // 5. mel sums on the matrix cores: bands in blocks of 16, each over the
-    //    4-bin chunks its filters touch (a multiple of kMelBatch chunks).  A =
-    //    blocked weights (lane order, pre-scaled, in LDS), B = P[frame c][bin
-    //    klo + 4 ch + g]; lane (c, g) gets bands 16 jb + 4 g + r of frame c.
-    //    Operands go through two register sets: the next batch (or the next
+    // 5. mel sums on 4x4x1 matrix blocks (16 per instruction): block (quad
+    //    g, frame quad c / 4) of step s multiplies the weights of the 4 bands
+    //    of quad 4 jb + g at bin qs + s by the power of 4 frames there, so a
+    //    step advances every quad of the 16-band block jb by one bin.  A =
+    //    weight of band 16 jb + 4 g + c % 4, B = P[frame c][qs_g + s]; lane
+    //    (c, g) gets bands 16 jb + 4 g + r of frame c.  Steps go in batches
+    //    of kMelBatch through two register sets: the next batch (or the next
     //    block's first) is loaded while the current one is multiplied.
     const SubTile t = locate(a, gs);
     const int64_t fr = t.s * kSub + c;
     const bool valid = fr < F;
     OUT *__restrict__ ocol = out + t.b * (int64_t)NM * F + fr;
-    const float *pb0 = Rc + g;
+    const float *wl = s_melw + 4 * g + (c & 3);
     float vmax = 0.0f;
     float wA[kMelBatch], pA[kMelBatch], wB[kMelBatch], pB[kMelBatch];
-    const float *wt = s_melw + s_meta[2] + lane, *pp = pb0 + s_meta[0];
-    int nch = s_meta[1];
+    const float *wt = wl + s_meta[1], *pp = Rc + s_meta[32 + g];
+    int nst = s_meta[0];
 #pragma unroll
     for (int u = 0; u < kMelBatch; ++u) {
-      wA[u] = wt[64 * u];
-      pA[u] = pp[4 * u];
+      wA[u] = wt[16 * u];
+      pA[u] = pp[u];
     }
     for (int jb = 0; jb < NB; ++jb) {
-      const int nb = nch / kMelBatch;
+      const int nb = nst / kMelBatch;
       const int jn = jb + 1 < NB ? jb + 1 : jb;
-      const float *wn = s_melw + s_meta[3 * jn + 2] + lane, *pn = pb0 + s_meta[3 * jn];
-      const int nch_n = s_meta[3 * jn + 1];
+      const float *wn = wl + s_meta[2 * jn + 1], *pn = Rc + s_meta[32 + 4 * jn + g];
+      const int nst_n = s_meta[2 * jn];
       v4f acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
       if (nb == 0) {   // nothing to multiply; the held operands become the next block's
 #pragma unroll
         for (int u = 0; u < kMelBatch; ++u) {
-          wA[u] = wn[64 * u];
-          pA[u] = pn[4 * u];
+          wA[u] = wn[16 * u];
+          pA[u] = pn[u];
         }
       } else {
         for (int k = 0;;) {
           {
             const bool in = k + 1 < nb;
-            const float *wq = in ? wt + 64 * kMelBatch * (k + 1) : wn;
-            const float *pq = in ? pp + 4 * kMelBatch * (k + 1) : pn;
+            const float *wq = in ? wt + 16 * kMelBatch * (k + 1) : wn;
+            const float *pq = in ? pp + kMelBatch * (k + 1) : pn;
 #pragma unroll
             for (int u = 0; u < kMelBatch; ++u) {
-              wB[u] = wq[64 * u];
-              pB[u] = pq[4 * u];
+              wB[u] = wq[16 * u];
+              pB[u] = pq[u];
             }
           }
 #pragma unroll
           for (int u = 0; u < kMelBatch; u += 2) {
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(wA[u], pA[u], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(wA[u + 1], pA[u + 1], acc1, 0, 0, 0);
+            acc0 = __builtin_amdgcn_mfma_f32_4x4x1f32(wA[u], pA[u], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_4x4x1f32(wA[u + 1], pA[u + 1], acc1, 0, 0, 0);
           }
           if (++k >= nb) {
 #pragma unroll
@@ -448,25 +497,25 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
           }
           {
             const bool in = k + 1 < nb;
-            const float *wq = in ? wt + 64 * kMelBatch * (k + 1) : wn;
-            const float *pq = in ? pp + 4 * kMelBatch * (k + 1) : pn;
+            const float *wq = in ? wt + 16 * kMelBatch * (k + 1) : wn;
+            const float *pq = in ? pp + kMelBatch * (k + 1) : pn;
 #pragma unroll
             for (int u = 0; u < kMelBatch; ++u) {
-              wA[u] = wq[64 * u];
-              pA[u] = pq[4 * u];
+              wA[u] = wq[16 * u];
+              pA[u] = pq[u];
             }
           }
 #pragma unroll
           for (int u = 0; u < kMelBatch; u += 2) {
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(wB[u], pB[u], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(wB[u + 1], pB[u + 1], acc1, 0, 0, 0);
+            acc0 = __builtin_amdgcn_mfma_f32_4x4x1f32(wB[u], pB[u], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_4x4x1f32(wB[u + 1], pB[u + 1], acc1, 0, 0, 0);
           }
           if (++k >= nb) break;
         }
       }
       wt = wn;
       pp = pn;
-      nch = nch_n;
+      nst = nst_n;
       float lmn = __builtin_huge_valf();
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -494,7 +543,7 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
 // blocked filter table that fits its LDS share.
 bool pcm400_supported(const lm_plan *p, bool in_i16) {
   if (p->n_fft != 400 || (p->hop & 1) || p->mfma400.empty() || p->n_mels > 256) return false;
-  if (p->melblk_w.size() + 64 * kMelBatch > (size_t)kMelWLds) return false;
+  if (p->melblk_w.size() + 16 * kMelBatch > (size_t)kMelWLds) return false;
   const int span = (kSub - 1) * p->hop + 400;
   const int ndw = in_i16 ? span / 2 : span;
   return ndw + 4 <= kRegion;

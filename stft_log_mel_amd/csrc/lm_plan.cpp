@@ -108,46 +108,48 @@ void build_mfma400(lm_plan *p) {
       }
 }
 
-// Blocked copy of a packed filterbank for the matrix-core mel sum (n_fft =
-// 400 only): bands in blocks of 16; block j covers bins [klo, klo + 4 nch)
-// which contains the union of its bands' supports, nch a multiple of
-// kMelBatch; chunk c of block j is
-// stored in matrix-core lane order, entry [lane] = W[16 j + lane % 16][klo +
-// 4 c + lane / 16] (0 outside a band's support or past the last band).
-// meta holds (klo, nch, offset in floats) per block.
+// Filterbank tables for the n_fft = 400 kernel's mel sum on 4x4x1 matrix
+// blocks.  Bands go in blocks of 16 = 4 quads of 4; a step s of block jb
+// multiplies, for every quad Q = 4 jb + q at once, the weights of its 4
+// bands at bin qs[Q] + s by the power of 16 frames at that bin.  Block jb
+// takes nst steps (the widest of its quads' bin spans, padded to whole
+// batches of kMelBatch); qs[Q] is the quad's first non-zero bin, moved
+// down so that qs[Q] + nst stays inside the kernel's power row.
+// Tables: meta = per block (nst, weight offset) for 16 blocks (zeros past
+// the last), then qs for 64 quads; weights per step as [q][band in quad],
+// 16 floats, zero outside a band's support.
 void build_mel_blocks(lm_plan *p) {
   p->melblk_meta.clear();
   p->melblk_w.clear();
   if (p->n_fft != 400) return;
   const Csr &c = p->csr;
   const int NM = c.n_rows, NB = (NM + 15) / 16;
-  p->melblk_meta.assign(3 * (size_t)NB, 0);
-  p->melblk_w.clear();
-  for (int j = 0; j < NB; ++j) {
-    int klo = 1 << 30, khi = 0;
-    for (int m = 16 * j; m < NM && m < 16 * j + 16; ++m)
-      if (c.width[m] > 0) {
-        klo = std::min(klo, c.start[m]);
-        khi = std::max(khi, c.start[m] + c.width[m]);
-      }
-    if (khi <= klo) {
-      klo = 0;
-      khi = 0;
+  p->melblk_meta.assign(2 * 16 + 64, 0);
+  for (int jb = 0; jb < NB; ++jb) {
+    int lo[4], span[4], nst = 0;
+    for (int q = 0; q < 4; ++q) {
+      int klo = 1 << 30, khi = 0;
+      for (int m = 16 * jb + 4 * q; m < NM && m < 16 * jb + 4 * q + 4; ++m)
+        if (c.width[m] > 0) {
+          klo = std::min(klo, c.start[m]);
+          khi = std::max(khi, c.start[m] + c.width[m]);
+        }
+      lo[q] = khi > klo ? klo : 0;
+      span[q] = khi > klo ? khi - klo : 0;
+      nst = std::max(nst, span[q]);
     }
-    // chunk count padded to whole batches; the padded range starts early
-    // enough to end inside the power row (its extra bins have zero weight)
-    const int nch = (khi - klo + 4 * kMelBatch - 1) / (4 * kMelBatch) * kMelBatch;
-    klo = std::min(klo, kPcm400Row - 4 * nch);
-    p->melblk_meta[3 * j] = klo;
-    p->melblk_meta[3 * j + 1] = nch;
-    p->melblk_meta[3 * j + 2] = (int)p->melblk_w.size();
-    for (int ch = 0; ch < nch; ++ch)
-      for (int lane = 0; lane < 64; ++lane) {
-        const int m = 16 * j + lane % 16, k = klo + 4 * ch + lane / 16;
-        float v = 0.0f;
-        if (m < NM && k >= c.start[m] && k < c.start[m] + c.width[m]) v = c.w[c.off[m] + k - c.start[m]];
-        p->melblk_w.push_back(v);
-      }
+    nst = (nst + kMelBatch - 1) / kMelBatch * kMelBatch;
+    p->melblk_meta[2 * jb] = nst;
+    p->melblk_meta[2 * jb + 1] = (int)p->melblk_w.size();
+    for (int q = 0; q < 4; ++q) p->melblk_meta[32 + 4 * jb + q] = std::min(lo[q], kPcm400Row - nst);
+    for (int s = 0; s < nst; ++s)
+      for (int q = 0; q < 4; ++q)
+        for (int t = 0; t < 4; ++t) {
+          const int m = 16 * jb + 4 * q + t, k = p->melblk_meta[32 + 4 * jb + q] + s;
+          float v = 0.0f;
+          if (m < NM && k >= c.start[m] && k < c.start[m] + c.width[m]) v = c.w[c.off[m] + k - c.start[m]];
+          p->melblk_w.push_back(v);
+        }
   }
 }
 
