@@ -162,6 +162,17 @@ struct Args {
 __device__ __forceinline__ float to_f(float v) { return v; }
 __device__ __forceinline__ float to_f(int16_t v) { return (float)(int)v; }
 
+// LDS layout of the staged span.  With SK (hop = 160 samples), 4 pad dwords
+// follow every hop of samples, so the 16 frame starts of a wave, 84 (int16)
+// or 164 (f32) dwords apart, fall on distinct bank quads; without, the span
+// is dense.  A hop is a multiple of 4 dwords, so 16-byte chunks never
+// straddle a pad.
+template <typename IN, bool SK>
+__device__ __forceinline__ int span_dw(int d) {
+  constexpr int H = sizeof(IN) == 2 ? 80 : 160;   // dwords per 160-sample hop
+  return SK ? d + 4 * (d / H) : d;
+}
+
 template <typename IN>
 struct Prefetch {
   static constexpr int N = sizeof(IN) == 2 ? kPfI16 : kPfF32;
@@ -224,7 +235,7 @@ constexpr int kPadBatch = 8;   // dwords per lane with loads in flight together
 // Padded path for span dwords [d_begin, d_end): each by index arithmetic
 // (positions past the end of the clip's last frame read as 0), kPadBatch
 // dwords per lane with all their loads issued before any is used.
-template <typename IN>
+template <typename IN, bool SK>
 __device__ __forceinline__ void stage_padded(const Args &a, const IN *__restrict__ pcm, int64_t gs, int d_begin,
                                              int d_end, float *R) {
   constexpr int PER_DW = 4 / sizeof(IN);
@@ -252,14 +263,14 @@ __device__ __forceinline__ void stage_padded(const Args &a, const IN *__restrict
         if (sizeof(IN) == 2) w |= (uint32_t)(uint16_t)(int16_t)(int)v[u][e] << (16 * e);
         else w = __float_as_uint(v[u][e]);
       }
-      d32[d0 + 64 * u] = w;
+      d32[span_dw<IN, SK>(d0 + 64 * u)] = w;
     }
   }
 }
 
 // The prefetched chunks into the wave's region, then the span's dwords
 // outside them by the padded path.
-template <typename IN>
+template <typename IN, bool SK>
 __device__ __forceinline__ void put_prefetch(const Args &a, const IN *__restrict__ pcm, int64_t gs,
                                              const Prefetch<IN> &pf, int span, float *R) {
   constexpr int PER_DW = 4 / sizeof(IN);
@@ -268,14 +279,14 @@ __device__ __forceinline__ void put_prefetch(const Args &a, const IN *__restrict
 #pragma unroll
   for (int i = 0; i < Prefetch<IN>::N; ++i) {
     const int q = lane + 64 * i;
-    if (q >= pf.q_lo && q < pf.q_hi) d4[q] = pf.v[i];
+    if (q >= pf.q_lo && q < pf.q_hi) d4[span_dw<IN, SK>(4 * q) / 4] = pf.v[i];
   }
   const int ndw = span / PER_DW;
-  if (pf.q_lo > 0) stage_padded<IN>(a, pcm, gs, 0, min(4 * pf.q_lo, ndw), R);
-  if (4 * pf.q_hi < ndw) stage_padded<IN>(a, pcm, gs, 4 * pf.q_hi, ndw, R);
+  if (pf.q_lo > 0) stage_padded<IN, SK>(a, pcm, gs, 0, min(4 * pf.q_lo, ndw), R);
+  if (4 * pf.q_hi < ndw) stage_padded<IN, SK>(a, pcm, gs, 4 * pf.q_hi, ndw, R);
 }
 
-template <typename IN, typename OUT>
+template <typename IN, typename OUT, bool SK>
 __global__ void __launch_bounds__(kThreads, 1)
 pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ melblk_meta,
               const float *__restrict__ melblk_w, OUT *__restrict__ out, float *__restrict__ tile_min) {
@@ -329,13 +340,17 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
   for (; gs < wg_end; gs += kWaves) {
     // 1. this sub-tile's samples into the wave's region (LDS operations of
     //    one wave complete in order, so no barrier is needed around them)
-    if (have) put_prefetch<IN>(a, pcm, gs, pf, span, R);
-    else stage_padded<IN>(a, pcm, gs, 0, span / (4 / (int)sizeof(IN)), R);
+    if (have) put_prefetch<IN, SK>(a, pcm, gs, pf, span, R);
+    else stage_padded<IN, SK>(a, pcm, gs, 0, span / (4 / (int)sizeof(IN)), R);
     have = gs + kWaves < wg_end && prefetch<IN>(a, pcm, gs + kWaves, span, pf);
 
     // 2. window + 16-point DFT + twiddle on the matrix cores: D[n1] += A[j][n1] x[j][n1].
     //    Lane (c, g) supplies, for step j, the samples n1 + 25 (4 g + j) of frame c:
-    //    a run of 25 consecutive samples starting at c hop + 100 g + 25 j.
+    //    a run of 25 consecutive samples starting at c hop + 100 g + 25 j, read as
+    //    13 dwords (int16 pairs) or float pairs from its first even sample.  In the
+    //    skewed layout two runs cross a pad: j = 0, g = 3 (sample 320, from read
+    //    10) and j = 2, g = 1 (sample 160, from read 5); their later reads are
+    //    4 dwords further on.
     v4f D[25];
 #pragma unroll
     for (int n1 = 0; n1 < 25; ++n1) D[n1] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
@@ -345,12 +360,23 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
 #pragma unroll
       for (int q = 0; q < 7; ++q) A[q] = s_amat[(j * 7 + q) * 64 + lane];
       const int r0 = c * hop + 100 * g + 25 * j;   // even hop: r0 has the parity of j
+      const int relr = (100 * g + 25 * j) & ~1;     // first even sample of the run, within the frame
+      int base, delta = 0;
+      const int ist = j == 0 ? 10 : (j == 2 ? 5 : 13);   // first read past the crossing (unrolled: a constant)
+      if (SK) {
+        base = (sizeof(IN) == 2 ? 84 * c + (relr >> 1) : 164 * c + relr) + 4 * ((relr >= 160) + (relr >= 320));
+        if (j == 0) delta = g == 3 ? 4 : 0;
+        if (j == 2) delta = g == 1 ? 4 : 0;
+      } else {
+        base = sizeof(IN) == 2 ? (r0 >> 1) : (r0 & ~1);
+      }
       float x[25];
       if (sizeof(IN) == 2) {
-        const uint32_t *rd = reinterpret_cast<const uint32_t *>(R) + (r0 >> 1);
+        const uint32_t *rd = reinterpret_cast<const uint32_t *>(R) + base;
+        const uint32_t *rd2 = rd + delta;
         uint32_t w[13];
 #pragma unroll
-        for (int i = 0; i < 13; ++i) w[i] = rd[i];
+        for (int i = 0; i < 13; ++i) w[i] = i < ist ? rd[i] : rd2[i];
 #pragma unroll
         for (int n1 = 0; n1 < 25; ++n1) {
           const int s = n1 + (j & 1);
@@ -358,10 +384,11 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
           x[n1] = (s & 1) ? (float)((int32_t)d >> 16) : (float)(int16_t)(d & 0xffffu);
         }
       } else {
-        const float2 *rf = reinterpret_cast<const float2 *>(R + (r0 & ~1));
+        const float2 *rf = reinterpret_cast<const float2 *>(R + base);
+        const float2 *rf2 = reinterpret_cast<const float2 *>(R + base + delta);
         float2 f[13];
 #pragma unroll
-        for (int i = 0; i < 13; ++i) f[i] = rf[i];
+        for (int i = 0; i < 13; ++i) f[i] = i < ist ? rf[i] : rf2[i];
 #pragma unroll
         for (int n1 = 0; n1 < 25; ++n1) {
           const int s = n1 + (j & 1);
@@ -546,7 +573,8 @@ bool pcm400_supported(const lm_plan *p, bool in_i16) {
   if (p->melblk_w.size() + 16 * kMelBatch > (size_t)kMelWLds) return false;
   const int span = (kSub - 1) * p->hop + 400;
   const int ndw = in_i16 ? span / 2 : span;
-  return ndw + 4 <= kRegion;
+  const int lds_dw = p->hop == 160 ? ndw + 4 * (ndw / (in_i16 ? 80 : 160)) : ndw;   // skewed layout at hop 160
+  return lds_dw + 4 <= kRegion;
 }
 
 StatLayout pcm400_stat_layout(const lm_plan *p) {
@@ -592,14 +620,23 @@ hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &pa, hipStream_t s) {
   const int32_t *bm = p->dt.melblk_meta;
   const float *bw = p->dt.melblk_w;
   float *tm = pa.tile_min;
-  if (!pa.in_i16 && !f16)
-    hipLaunchKernelGGL((pcm400_kernel<float, float>), grid, block, 0, s, k, am, bm, bw, (float *)pa.out, tm);
-  else if (!pa.in_i16 && f16)
-    hipLaunchKernelGGL((pcm400_kernel<float, __half>), grid, block, 0, s, k, am, bm, bw, (__half *)pa.out, tm);
-  else if (pa.in_i16 && !f16)
-    hipLaunchKernelGGL((pcm400_kernel<int16_t, float>), grid, block, 0, s, k, am, bm, bw, (float *)pa.out, tm);
-  else
-    hipLaunchKernelGGL((pcm400_kernel<int16_t, __half>), grid, block, 0, s, k, am, bm, bw, (__half *)pa.out, tm);
+  const bool sk = p->hop == 160;
+#define LM_P400(IN, OUT, SK) \
+  hipLaunchKernelGGL((pcm400_kernel<IN, OUT, SK>), grid, block, 0, s, k, am, bm, bw, (OUT *)pa.out, tm)
+  if (!pa.in_i16 && !f16) {
+    if (sk) LM_P400(float, float, true);
+    else LM_P400(float, float, false);
+  } else if (!pa.in_i16 && f16) {
+    if (sk) LM_P400(float, __half, true);
+    else LM_P400(float, __half, false);
+  } else if (pa.in_i16 && !f16) {
+    if (sk) LM_P400(int16_t, float, true);
+    else LM_P400(int16_t, float, false);
+  } else {
+    if (sk) LM_P400(int16_t, __half, true);
+    else LM_P400(int16_t, __half, false);
+  }
+#undef LM_P400
   return hipGetLastError();
 }
 
