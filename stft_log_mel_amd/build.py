@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblm.so")
 
 SOURCES = ["lm_plan.cpp", "lm_api.cpp", "lm_stft.hip", "lm_pcm.hip", "lm_pcm400.hip", "lm_fixup.hip"]
-HEADERS = ["lm_internal.h", "lm_device.h", os.path.join("..", "..", "include", "lm.h")]
+HEADERS = ["lm_internal.h", "lm_device.h", "lm_fixup.h", os.path.join("..", "..", "include", "lm.h")]
 
 ARCH = "gfx950"
 CFLAGS = [

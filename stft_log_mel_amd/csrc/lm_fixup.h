@@ -1,0 +1,106 @@
+// Per-clip floor (KBench task page "audio-mel-spectrogram-fused", section
+// "spec_md": the floor is per clip, at the clip's largest log value minus
+// 8), applied after the main kernels have written (L + 4) / 4 everywhere.
+//
+// The main kernels record the largest mel value per tile and the smallest L
+// per region of a tile (a frame range times a band range).  Since (x + 4)/4
+// and the cast to the output type are both monotone, max(rescale(L),
+// rescale(hi - 8)) equals rescale(max(L, hi - 8)); so only regions whose
+// smallest L lies below hi - 8 are read, and only values below the floor
+// are rewritten.  hi is log10 of the largest mel value, with the same log10
+// the main kernels use, so the largest output is exactly (hi + 4) / 4.
+//
+// fixup_group is one unit of that work, run by a whole workgroup: it is the
+// body of the stand-alone fix-up kernel and the last phase of the persistent
+// main kernels when they are launched cooperatively.
+#pragma once
+
+#include "lm_device.h"
+#include "lm_internal.h"
+
+namespace lm {
+
+constexpr int kFixEntries = 512;   // regions one group scans
+constexpr int kFixUnroll = 8;      // values per thread with loads in flight together
+
+// Group units of a fix-up: (clip, group) pairs, entries_per_group regions each.
+inline void prepare_fixup(FixupArgs &a) {
+  const int n_ent = a.tiles_per_clip * a.st.min_per_tile();
+  a.entries_per_group = kFixEntries;
+  a.groups_per_clip = (n_ent + kFixEntries - 1) / kFixEntries;
+}
+
+// Unit (clip b, group gi): reduce the clip's maxima to hi (every group of
+// the clip does this itself, so no cross-workgroup atomics or resets are
+// needed), list the regions of the group whose smallest log value lies
+// below hi - 8, then rewrite their values below the floor with all threads.
+// LDS: s_list[kFixEntries], s_n[1], s_red[THREADS / 64].  Every thread of
+// the workgroup must call it; it ends with a barrier.
+template <typename OUT, int THREADS>
+__device__ void fixup_group(const FixupArgs &a, int64_t b, int gi, int *s_list, int *s_n, float *s_red) {
+  constexpr int NW = THREADS / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const StatLayout st = a.st;
+  const int ept = st.min_per_tile();
+  const int n_ent = a.tiles_per_clip * ept, n_max = a.tiles_per_clip * st.max_per_tile;
+  const float *cmax = a.tile_max + b * (int64_t)n_max;
+  const float *cmin = a.tile_min + b * (int64_t)n_ent;
+  if (tid == 0) *s_n = 0;
+  float hi = 0.0f;
+  for (int e = tid; e < n_max; e += THREADS) hi = fmaxf(hi, cmax[e]);
+  hi = wave_max(hi);
+  if (lane == 0) s_red[wv] = hi;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NW; ++i) hi = fmaxf(hi, s_red[i]);
+  const float floorL = log10_pos(fmaxf(hi, 1e-10f)) - 8.0f;
+  const int e0 = gi * a.entries_per_group, e1 = min(n_ent, e0 + a.entries_per_group);
+  for (int e = e0 + tid; e < e1; e += THREADS)
+    if (cmin[e] < floorL) s_list[atomicAdd(s_n, 1)] = e;   // LDS atomic: list order is irrelevant
+  __syncthreads();
+  const int n_flag = *s_n;
+
+  float fo = rescale(floorL);
+  if (sizeof(OUT) == 2) fo = __half2float(__float2half_rn(fo));
+  OUT *out = reinterpret_cast<OUT *>(a.out);
+  const int NM = a.n_mels;
+  const int64_t F = a.n_frames;
+  const int sub_frames = st.frames_per_tile / st.sub_per_tile;
+  const int reg = sub_frames * st.band_h;   // values of a full region
+  const int total = n_flag * reg;
+  for (int k0 = tid; k0 < total; k0 += THREADS * kFixUnroll) {
+    OUT *p[kFixUnroll];
+    float v[kFixUnroll];
+#pragma unroll
+    for (int u = 0; u < kFixUnroll; ++u) {
+      const int k = k0 + u * THREADS;
+      p[u] = nullptr;
+      if (k < total) {
+        const int i = k / reg, el = k - i * reg;
+        const int e = s_list[i];
+        const int t = e / ept, rem = e - t * ept;
+        const int sub = rem / st.blk_per_sub, blk = rem - sub * st.blk_per_sub;
+        int fi, bi;
+        if (a.mel_major) {
+          bi = el / sub_frames;
+          fi = el - bi * sub_frames;
+        } else {
+          fi = el / st.band_h;
+          bi = el - fi * st.band_h;
+        }
+        const int64_t f = (int64_t)t * st.frames_per_tile + (int64_t)sub * sub_frames + fi;
+        const int m = blk * st.band_h + bi;
+        if (f < F && m < NM) {
+          p[u] = out + (a.mel_major ? (b * NM + m) * F + f : (b * F + f) * NM + m);
+          v[u] = load_out(p[u]);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kFixUnroll; ++u)
+      if (p[u] && v[u] < fo) store_out(p[u], fo);
+  }
+  __syncthreads();
+}
+
+}  // namespace lm
