@@ -46,6 +46,16 @@ __device__ void fixup_group(const FixupArgs &a, int64_t b, int gi, int *s_list, 
   const float *cmax = a.tile_max + b * (int64_t)n_max;
   const float *cmin = a.tile_min + b * (int64_t)n_ent;
   if (tid == 0) *s_n = 0;
+  // the group's region minima are loaded together with the maxima (one
+  // round trip): kFixEntries / THREADS of them per thread
+  constexpr int MPT = (kFixEntries + THREADS - 1) / THREADS;
+  const int e0 = gi * a.entries_per_group, e1 = min(n_ent, e0 + a.entries_per_group);
+  float mn[MPT];
+#pragma unroll
+  for (int u = 0; u < MPT; ++u) {
+    const int e = e0 + tid + u * THREADS;
+    mn[u] = e < e1 ? cmin[e] : __builtin_huge_valf();
+  }
   float hi = 0.0f;
   for (int e = tid; e < n_max; e += THREADS) hi = fmaxf(hi, cmax[e]);
   hi = wave_max(hi);
@@ -54,9 +64,9 @@ __device__ void fixup_group(const FixupArgs &a, int64_t b, int gi, int *s_list, 
 #pragma unroll
   for (int i = 0; i < NW; ++i) hi = fmaxf(hi, s_red[i]);
   const float floorL = log10_pos(fmaxf(hi, 1e-10f)) - 8.0f;
-  const int e0 = gi * a.entries_per_group, e1 = min(n_ent, e0 + a.entries_per_group);
-  for (int e = e0 + tid; e < e1; e += THREADS)
-    if (cmin[e] < floorL) s_list[atomicAdd(s_n, 1)] = e;   // LDS atomic: list order is irrelevant
+#pragma unroll
+  for (int u = 0; u < MPT; ++u)
+    if (mn[u] < floorL) s_list[atomicAdd(s_n, 1)] = e0 + tid + u * THREADS;   // LDS atomic: order is irrelevant
   __syncthreads();
   const int n_flag = *s_n;
 
