@@ -30,31 +30,31 @@ struct Radices {};
 
 template <int NFFT>
 struct PcmCfg;
-// FPB frames per tile, THREADS per workgroup, radix sequence of M = NFFT/2.
-template <> struct PcmCfg<400>   { static constexpr int FPB = 16,  THREADS = 256; using Rad = Radices<8, 5, 5>; };
-template <> struct PcmCfg<64>    { static constexpr int FPB = 128, THREADS = 256; using Rad = Radices<16, 2>; };
-template <> struct PcmCfg<128>   { static constexpr int FPB = 64,  THREADS = 256; using Rad = Radices<16, 4>; };
-template <> struct PcmCfg<256>   { static constexpr int FPB = 32,  THREADS = 256; using Rad = Radices<16, 8>; };
-template <> struct PcmCfg<512>   { static constexpr int FPB = 16,  THREADS = 256; using Rad = Radices<16, 16>; };
-template <> struct PcmCfg<1024>  { static constexpr int FPB = 8,   THREADS = 256; using Rad = Radices<8, 8, 8>; };
-template <> struct PcmCfg<2048>  { static constexpr int FPB = 4,   THREADS = 256; using Rad = Radices<16, 16, 4>; };
-template <> struct PcmCfg<4096>  { static constexpr int FPB = 2,   THREADS = 256; using Rad = Radices<16, 16, 8>; };
-template <> struct PcmCfg<8192>  { static constexpr int FPB = 1,   THREADS = 256; using Rad = Radices<16, 16, 16>; };
-template <> struct PcmCfg<16384> { static constexpr int FPB = 1,   THREADS = 512; using Rad = Radices<16, 16, 16, 2>; };
+// FPB frames per tile, THREADS per workgroup, radix sequence of M = NFFT/2,
+// WLDS floats of LDS for staged filter weights (0: weights read from
+// global memory, which leaves room for two workgroups per CU).
+template <> struct PcmCfg<400>   { static constexpr int FPB = 16,  THREADS = 256, WLDS = 4096; using Rad = Radices<8, 5, 5>; };
+template <> struct PcmCfg<64>    { static constexpr int FPB = 128, THREADS = 256, WLDS = 4096; using Rad = Radices<16, 2>; };
+template <> struct PcmCfg<128>   { static constexpr int FPB = 64,  THREADS = 256, WLDS = 4096; using Rad = Radices<16, 4>; };
+template <> struct PcmCfg<256>   { static constexpr int FPB = 32,  THREADS = 256, WLDS = 4096; using Rad = Radices<16, 8>; };
+template <> struct PcmCfg<512>   { static constexpr int FPB = 16,  THREADS = 256, WLDS = 4096; using Rad = Radices<16, 16>; };
+template <> struct PcmCfg<1024>  { static constexpr int FPB = 8,   THREADS = 256, WLDS = 4096; using Rad = Radices<8, 8, 8>; };
+template <> struct PcmCfg<2048>  { static constexpr int FPB = 4,   THREADS = 256, WLDS = 4096; using Rad = Radices<16, 16, 4>; };
+template <> struct PcmCfg<4096>  { static constexpr int FPB = 2,   THREADS = 256, WLDS = 4096; using Rad = Radices<16, 16, 8>; };
+template <> struct PcmCfg<8192>  { static constexpr int FPB = 1,   THREADS = 256, WLDS = 0;    using Rad = Radices<16, 16, 16>; };
+template <> struct PcmCfg<16384> { static constexpr int FPB = 1,   THREADS = 512, WLDS = 0;    using Rad = Radices<16, 16, 16, 2>; };
 
 __device__ __forceinline__ float to_f(float v) { return v; }
 __device__ __forceinline__ float to_f(int16_t v) { return (float)(int)v; }
 
-// Sample j of a clip of T samples, with center padding resolved by index.
-template <typename IN>
-__device__ __forceinline__ float padded_sample(const IN *__restrict__ x, int64_t j, int64_t T, int mode) {
-  if (j < 0 || j >= T) {
-    if (mode == LM_PAD_CONSTANT) return 0.0f;
-    if (mode == LM_PAD_REFLECT) j = j < 0 ? -j : 2 * (T - 1) - j;
-    else if (mode == LM_PAD_REPLICATE) j = j < 0 ? 0 : T - 1;
-    else j = ((j % T) + T) % T;
-  }
-  return to_f(x[j]);
+// Source index of padded position j of a clip of T samples (0 <= result <
+// T), or -1 for a constant-mode zero: the center padding resolved by index.
+__device__ __forceinline__ int64_t pad_source(int64_t j, int64_t T, int mode) {
+  if (j >= 0 && j < T) return j;
+  if (mode == LM_PAD_CONSTANT) return -1;
+  if (mode == LM_PAD_REFLECT) return j < 0 ? -j : 2 * (T - 1) - j;
+  if (mode == LM_PAD_REPLICATE) return j < 0 ? 0 : T - 1;
+  return ((j % T) + T) % T;
 }
 
 // One Stockham radix-R pass over FPB frames of M points held in `buf`.
@@ -129,8 +129,6 @@ struct PcmKernelArgs {
   float *tile_min, *tile_max;
 };
 
-// Packed filter weights are staged in LDS when they fit this many floats.
-constexpr int kCsrLdsMax = 4096;
 
 template <int NFFT, typename IN, typename OUT>
 __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKernelArgs a) {
@@ -139,8 +137,9 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
   constexpr int THREADS = PcmCfg<NFFT>::THREADS;
   constexpr int NW = THREADS / 64;
   __shared__ float2 s_buf[FPB * M];
+  constexpr int WLDS = PcmCfg<NFFT>::WLDS;
   __shared__ int32_t s_start[256], s_width[256], s_off[256];
-  __shared__ float s_w[kCsrLdsMax];
+  __shared__ float s_w[WLDS > 0 ? WLDS : 1];
   __shared__ float s_red[2 * NW];
 
   const int tid = threadIdx.x;
@@ -154,30 +153,36 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
   // packed filterbank -> LDS
   const int NM = a.n_mels;
   const int nnz = stage_filters<THREADS>(NM, a.csr_start, a.csr_width, a.csr_off, a.csr_w, a.nnz, s_start, s_width,
-                                         s_off, s_w, kCsrLdsMax);
-  const bool w_in_lds = nnz <= kCsrLdsMax;
+                                         s_off, s_w, WLDS);
+  const bool w_in_lds = WLDS > 0 && nnz <= WLDS;
 
-  // 1. windowed, padded frame samples as M complex points per frame
+  // 1. windowed, padded frame samples as M complex points per frame; every
+  //    load of the thread is issued before any is used
   const float2 *__restrict__ win2 = reinterpret_cast<const float2 *>(a.window);
-  for (int i = tid; i < FPB * M; i += THREADS) {
+  constexpr int IPT = (FPB * M + THREADS - 1) / THREADS;
+  float xs[IPT][2];
+  float2 ws[IPT];
+#pragma unroll
+  for (int u = 0; u < IPT; ++u) {
+    const int i = tid + u * THREADS;
     const int fl = i / M, n = i - fl * M;
     const int64_t fr = f0 + fl;
-    float2 z = make_float2(0.0f, 0.0f);
-    if (fr < F) {
-      const int64_t s0 = fr * a.hop - a.pad;
-      const int64_t j = s0 + 2 * n;
-      float x0, x1;
-      if (s0 >= 0 && s0 + NFFT <= T) {
-        x0 = to_f(x[j]);
-        x1 = to_f(x[j + 1]);
-      } else {
-        x0 = padded_sample(x, j, T, a.pad_mode);
-        x1 = padded_sample(x, j + 1, T, a.pad_mode);
+    ws[u] = make_float2(0.0f, 0.0f);
+    xs[u][0] = xs[u][1] = 0.0f;
+    if ((FPB * M) % THREADS == 0 || i < FPB * M) {
+      if (fr < F) {
+        const int64_t j = fr * a.hop - a.pad + 2 * n;
+        const int64_t s0 = pad_source(j, T, a.pad_mode), s1 = pad_source(j + 1, T, a.pad_mode);
+        xs[u][0] = s0 >= 0 ? to_f(x[s0]) : 0.0f;
+        xs[u][1] = s1 >= 0 ? to_f(x[s1]) : 0.0f;
+        ws[u] = win2[n];
       }
-      const float2 w = win2[n];
-      z = make_float2(x0 * w.x, x1 * w.y);
     }
-    s_buf[i] = z;
+  }
+#pragma unroll
+  for (int u = 0; u < IPT; ++u) {
+    const int i = tid + u * THREADS;
+    if ((FPB * M) % THREADS == 0 || i < FPB * M) s_buf[i] = make_float2(xs[u][0] * ws[u].x, xs[u][1] * ws[u].y);
   }
   __syncthreads();
 
@@ -228,6 +233,27 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
   // instructions (a pointer that may point either way would make every
   // weight load a flat load that waits for all outstanding global loads)
   auto mel = [&](const float *wsrc) {
+    if (FPB == 1) {
+      // one frame: a wave per band, lanes across the band's bins (wide
+      // bands at large n_fft), then a wave sum
+      const int lane = tid & 63, wv = tid >> 6;
+      const int64_t fr = f0;
+      if (fr >= F) return;
+      for (int m = wv; m < NM; m += NW) {
+        const int st = s_start[m], wd = s_width[m];
+        const float *pr = P + st;
+        const float *wr = wsrc + s_off[m];
+        float acc = 0.0f;
+        for (int j = lane; j < wd; j += 64) acc = __builtin_fmaf(wr[j], pr[j], acc);
+        acc = wave_sum(acc);
+        const float v = fmaxf(acc * a.mel_scale, 1e-10f);
+        const float L = log10_pos(v);
+        vmax = fmaxf(vmax, v);
+        lmin = fminf(lmin, L);
+        if (lane == 0) store_out(out + (int64_t)m * F + fr, rescale(L));
+      }
+      return;
+    }
     for (int o = tid; o < NM * FPB; o += THREADS) {
       const int fl = o % FPB, m = o / FPB;
       const int64_t fr = f0 + fl;
