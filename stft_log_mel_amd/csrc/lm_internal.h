@@ -46,6 +46,7 @@ struct DeviceTables {
   const float *csr_w = nullptr;
   int nnz = 0;
   const float *mfma400 = nullptr;   // n_fft = 400 only
+  const uint16_t *mfma400h = nullptr;
   const int32_t *melblk_meta = nullptr;
   const float *melblk_w = nullptr;
   int n_melblk = 0;
@@ -69,6 +70,7 @@ struct lm_plan {
   std::vector<float> twiddle;     // 2 * M
   std::vector<float> untangle;    // 2 * (M/2 + 1)
   std::vector<float> mfma400;     // n_fft = 400 only: first-stage matrix-core operands (4 x 7 x 64 x 4)
+  std::vector<uint16_t> mfma400h;  // the same as fp16 hi/lo parts for int16 samples (25 x 2 x 2 x 16 x 8)
   std::vector<int32_t> melblk_meta;  // per 16-band block: klo, chunks, offset
   std::vector<float> melblk_w;       // blocked filter weights in matrix-core lane order
 

@@ -39,6 +39,9 @@ namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
@@ -46,6 +49,8 @@ constexpr int kSub = 16;                  // frames per wave step (the matrix-co
 constexpr int kRow = kPcm400Row;          // power row stride
 constexpr int kRegion = kSub * kRow;      // floats of LDS per wave: staged samples, then power rows
 constexpr int kAmat = 4 * 7 * 64;         // first-stage operands (v4f): [j][n1 / 4][lane]
+constexpr int kAmatH = 25 * 2 * 2 * 16;   // the fp16 form for int16 samples (8 halves each): [n1][part][g % 2][row]
+constexpr int kLoff = 1694;               // int16 samples: dword offset of the l / 64 plane in the region
 constexpr int kMelWLds = 6400;            // LDS floats for the mel step weights (and one zero batch)
 constexpr int kPfI16 = 6, kPfF32 = 11;    // 16-byte sample loads per lane held for the next sub-tile
 
@@ -173,6 +178,23 @@ __device__ __forceinline__ int span_dw(int d) {
   return SK ? d + 4 * (d / H) : d;
 }
 
+// int16 samples are staged as two fp16 planes with the dword layout above:
+// H holds h = (x - (x mod 64)) / 64 in [-512, 511] and L holds (x mod 64) /
+// 64, so x / 64 = h + l / 64 exactly.  A dword of two samples converts with
+// integer masks into the fp16 bit patterns 1024 + (h + 512) and 1024 + l
+// (exponent 10, integer mantissa), then one packed fp16 operation each.
+// kLoff is 2 mod 4 dwords, so the two planes' readers use different bank
+// quads.
+__device__ __forceinline__ void split_i16(uint32_t x, uint32_t &H, uint32_t &L) {
+  const uint32_t hb = (((x ^ 0x80008000u) >> 6) & 0x03ff03ffu) | 0x64006400u;
+  const uint32_t lb = (x & 0x003f003fu) | 0x64006400u;
+  const h2 hv = __builtin_bit_cast(h2, hb) + h2{(_Float16)-1536.0f, (_Float16)-1536.0f};
+  const h2 lv = __builtin_bit_cast(h2, lb) * h2{(_Float16)0.015625f, (_Float16)0.015625f} +
+                h2{(_Float16)-16.0f, (_Float16)-16.0f};
+  H = __builtin_bit_cast(uint32_t, hv);
+  L = __builtin_bit_cast(uint32_t, lv);
+}
+
 template <typename IN>
 struct Prefetch {
   static constexpr int N = sizeof(IN) == 2 ? kPfI16 : kPfF32;
@@ -263,7 +285,15 @@ __device__ __forceinline__ void stage_padded(const Args &a, const IN *__restrict
         if (sizeof(IN) == 2) w |= (uint32_t)(uint16_t)(int16_t)(int)v[u][e] << (16 * e);
         else w = __float_as_uint(v[u][e]);
       }
-      d32[span_dw<IN, SK>(d0 + 64 * u)] = w;
+      const int o = span_dw<IN, SK>(d0 + 64 * u);
+      if (sizeof(IN) == 2) {
+        uint32_t H, L;
+        split_i16(w, H, L);
+        d32[o] = H;
+        d32[kLoff + o] = L;
+      } else {
+        d32[o] = w;
+      }
     }
   }
 }
@@ -276,10 +306,28 @@ __device__ __forceinline__ void put_prefetch(const Args &a, const IN *__restrict
   constexpr int PER_DW = 4 / sizeof(IN);
   const int lane = threadIdx.x & 63;
   u4 *d4 = reinterpret_cast<u4 *>(R);
+  u2 *d2 = reinterpret_cast<u2 *>(R + kLoff);
 #pragma unroll
   for (int i = 0; i < Prefetch<IN>::N; ++i) {
     const int q = lane + 64 * i;
-    if (q >= pf.q_lo && q < pf.q_hi) d4[span_dw<IN, SK>(4 * q) / 4] = pf.v[i];
+    if (q >= pf.q_lo && q < pf.q_hi) {
+      const int o = span_dw<IN, SK>(4 * q);
+      if (sizeof(IN) == 2) {
+        u4 H, L;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint32_t hh, ll;
+          split_i16(pf.v[i][e], hh, ll);
+          H[e] = hh;
+          L[e] = ll;
+        }
+        d4[o / 4] = H;
+        d2[o / 2] = u2{L[0], L[1]};
+        d2[o / 2 + 1] = u2{L[2], L[3]};
+      } else {
+        d4[o / 4] = pf.v[i];
+      }
+    }
   }
   const int ndw = span / PER_DW;
   if (pf.q_lo > 0) stage_padded<IN, SK>(a, pcm, gs, 0, min(4 * pf.q_lo, ndw), R);
@@ -290,6 +338,8 @@ template <typename IN, typename OUT, bool SK>
 __global__ void __launch_bounds__(kThreads, 1)
 pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ melblk_meta,
               const float *__restrict__ melblk_w, OUT *__restrict__ out, float *__restrict__ tile_min) {
+  constexpr bool kI16 = sizeof(IN) == 2;
+  constexpr int kTab = kI16 ? kAmatH : kAmat;
   __shared__ v4f s_amat[kAmat];
   __shared__ float s_melw[kMelWLds];
   __shared__ __attribute__((aligned(16))) float s_reg[kWaves * kRegion];
@@ -299,14 +349,14 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   {
     // all loads of the operand table in flight at once
-    constexpr int PER = (kAmat + kThreads - 1) / kThreads;
+    constexpr int PER = (kTab + kThreads - 1) / kThreads;
     v4f v[PER];
 #pragma unroll
     for (int u = 0; u < PER; ++u)
-      if (tid + u * kThreads < kAmat) v[u] = amat[tid + u * kThreads];
+      if (tid + u * kThreads < kTab) v[u] = amat[tid + u * kThreads];
 #pragma unroll
     for (int u = 0; u < PER; ++u)
-      if (tid + u * kThreads < kAmat) s_amat[tid + u * kThreads] = v[u];
+      if (tid + u * kThreads < kTab) s_amat[tid + u * kThreads] = v[u];
   }
   if (tid < 2 * 16 + 64) s_meta[tid] = melblk_meta[tid];
   for (int i0 = tid; i0 < a.melw_n + 16 * kMelBatch; i0 += 4 * kThreads) {
@@ -354,6 +404,34 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
     v4f D[25];
 #pragma unroll
     for (int n1 = 0; n1 < 25; ++n1) D[n1] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (kI16) {
+      // int16: per n1, two fp16 products (matrix hi and lo parts) over
+      // k-slots e of lane (c, g): sample n1 + 25 n2 of frame c, n2 = 4 (e / 2)
+      // + e % 2 + 2 (g % 2), from plane H (groups 0, 3) or L (groups 1, 2).
+      // The run of group g % 2 = 1 starts 50 samples (25 dwords) later; in
+      // the skewed layout it is another 4 dwords later where the samples of
+      // the two groups lie on different sides of a hop boundary.
+      const int h = g & 1;
+      const _Float16 *pl = reinterpret_cast<const _Float16 *>(R + ((g == 0 || g == 3) ? 0 : kLoff));
+      const _Float16 *p0 = pl + 2 * ((SK ? 84 * c : (c * hop) >> 1) + 25 * h);
+      const _Float16 *p1 = p0 + 8 * h;
+      const v8h *tab = reinterpret_cast<const v8h *>(s_amat) + 16 * h + (lane & 15);
+#pragma unroll
+      for (int n1 = 0; n1 < 25; ++n1) {
+        v8h B;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r0 = n1 + 25 * (4 * (e >> 1) + (e & 1));   // sample within the frame for g % 2 = 0
+          const int pad0 = SK ? 4 * ((r0 >= 160) + (r0 >= 320)) : 0;
+          const bool cross = SK && ((r0 < 160 && r0 + 50 >= 160) || (r0 < 320 && r0 + 50 >= 320));
+          const int off = 2 * ((r0 >> 1) + pad0) + (r0 & 1);
+          B[e] = (cross ? p1 : p0)[off];
+        }
+        const v8h Ah = tab[(n1 * 2 + 0) * 32], Al = tab[(n1 * 2 + 1) * 32];
+        D[n1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, B, D[n1], 0, 0, 0);
+        D[n1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, B, D[n1], 0, 0, 0);
+      }
+    } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       v4f A[7];
@@ -398,6 +476,7 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
 #pragma unroll
       for (int n1 = 0; n1 < 25; ++n1)
         D[n1] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[n1 >> 2][n1 & 3], x[n1], D[n1], 0, 0, 0);
+    }
     }
 
     // 3. 25-point DFTs over n1.  Za: class g + 1 (rows 4g, 4g+1).  Zb: class
@@ -574,6 +653,7 @@ bool pcm400_supported(const lm_plan *p, bool in_i16) {
   const int span = (kSub - 1) * p->hop + 400;
   const int ndw = in_i16 ? span / 2 : span;
   const int lds_dw = p->hop == 160 ? ndw + 4 * (ndw / (in_i16 ? 80 : 160)) : ndw;   // skewed layout at hop 160
+  if (in_i16) return lds_dw <= kLoff && kLoff + lds_dw <= kRegion;   // the two fp16 planes
   return lds_dw + 4 <= kRegion;
 }
 
@@ -601,8 +681,9 @@ hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &pa, hipStream_t s) {
   k.pad = p->center ? 200 : 0;
   k.pad_mode = p->pad_mode;
   k.power = p->power;
-  // every power value is 4 |X|^2; int16 samples carry 2^15 per |X|
-  const float in_scale2 = pa.in_i16 ? 1.0f / 1073741824.0f : 1.0f;   // 2^-30
+  // every power value is 4 |X|^2; int16 samples carry 2^15 per |X|, and
+  // their fp16 matrix another 2^12 / 64 = 2^6
+  const float in_scale2 = pa.in_i16 ? 1.0f / 4398046511104.0f : 1.0f;   // 2^-42
   if (p->power == 2.0f) {
     k.mel_scale = 0.25f * in_scale2;
     k.pre_scale = 1.0f;
@@ -616,7 +697,7 @@ hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &pa, hipStream_t s) {
   k.tile_max = pa.tile_max;
   const dim3 grid((unsigned)n_wg), block(kThreads);
   const bool f16 = p->out_dtype == LM_F16;
-  const v4f *am = reinterpret_cast<const v4f *>(p->dt.mfma400);
+  const v4f *am = reinterpret_cast<const v4f *>(pa.in_i16 ? (const void *)p->dt.mfma400h : (const void *)p->dt.mfma400);
   const int32_t *bm = p->dt.melblk_meta;
   const float *bw = p->dt.melblk_w;
   float *tm = pa.tile_min;

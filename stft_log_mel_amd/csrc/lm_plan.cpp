@@ -65,17 +65,8 @@ void build_twiddles(lm_plan *p) {
   }
 }
 
-// Operand tables of the n_fft = 400 kernel's matrix-core stage.  The frame
-// is folded to z[n] = w[2n] x[2n] + i w[2n+1] x[2n+1], n < 200 = 25 * 8, and
-// for each n1 < 25 the eight points z[n1 + 25 n2] go through one real 16x16
-// matrix that applies the window, the 8-point DFT over n2 and the twiddle
-// exp(-2 pi i k2 n1 / 200):
-//   out[k2] = sum_n2 z[n1 + 25 n2] exp(-2 pi i k2 (n1 + 25 n2) / 200).
-// Rows (outputs) are ordered so that lane group g = row / 4 holds the
-// classes (1,7), (2,6), (3,5), (0,4) as (re a, im a, re b, im b); columns
-// (inputs) are r = n2 + 8 e for sample x[2 (n1 + 25 n2) + e].  Stored per
-// n1 in matrix-core lane order: entry [n1][lane][j] = M_n1[lane % 16][4 j +
-// lane / 16].
+// Operand tables of the n_fft = 400 kernel's matrix-core stage (the
+// 16 x 25 split of a 400-point DFT; matrices described below).
 void build_mfma400(lm_plan *p) {
   // Matrix M_n1 (16 x 16) maps the samples y[n1 + 25 n2], n2 < 16, of 16
   // frames to row m: group g = m / 4 holds classes g + 1 (rows 4g, 4g+1,
@@ -89,23 +80,44 @@ void build_mfma400(lm_plan *p) {
   static const int kA[4] = {1, 2, 3, 4}, kB[3] = {7, 6, 5};
   std::vector<double> win(400);
   for (int n = 0; n < 400; ++n) win[n] = 0.5 - 0.5 * std::cos(2.0 * M_PI * (double)n / 400.0);
+  auto entry = [&](int n1, int m, int n2) {
+    const int n = n1 + 25 * n2;
+    const int g = m / 4, sub = m % 4;
+    if (g == 3 && sub >= 2) return ((n2 & 1) == sub - 2) ? win[n] : 0.0;
+    const int k = sub < 2 ? kA[g] : kB[g];
+    const double th = 2.0 * M_PI * (double)(((long)k * n) % 400) / 400.0;
+    return 2.0 * win[n] * ((sub & 1) == 0 ? std::cos(th) : -std::sin(th));
+  };
   p->mfma400.assign(4 * 7 * 64 * 4, 0.0f);
   for (int n1 = 0; n1 < 25; ++n1)
     for (int lane = 0; lane < 64; ++lane)
-      for (int j = 0; j < 4; ++j) {
-        const int m = lane % 16, n2 = 4 * (lane / 16) + j, n = n1 + 25 * n2;
-        const int g = m / 4, sub = m % 4;
-        double v;
-        if (g == 3 && sub >= 2) {
-          v = ((n2 & 1) == sub - 2) ? win[n] : 0.0;
-        } else {
-          const int k = sub < 2 ? kA[g] : kB[g];
-          const double sc = 2.0;
-          const double th = 2.0 * M_PI * (double)(((long)k * n) % 400) / 400.0;
-          v = sc * win[n] * ((sub & 1) == 0 ? std::cos(th) : -std::sin(th));
+      for (int j = 0; j < 4; ++j)
+        p->mfma400[(((size_t)j * 7 + n1 / 4) * 64 + lane) * 4 + n1 % 4] =
+            (float)entry(n1, lane % 16, 4 * (lane / 16) + j);
+  // fp16 form for int16 samples (v_mfma_f32_16x16x32_f16, two per n1): the
+  // samples enter as x / 64 = h + l / 64 with h = (x - (x mod 64)) / 64 and
+  // l = x mod 64, both exact in fp16, and the matrix, scaled by 2^12, as the
+  // sum of two fp16 parts (hi = nearest fp16, lo = nearest fp16 of the
+  // rest), so that hi + lo carries about 22 bits.  Lane (m, g) holds
+  // k-slots e < 8 standing for n2 = 4 (e / 2) + e % 2 + 2 (g % 2); lanes
+  // of groups 0 and 3 supply h, those of groups 1 and 2 supply l / 64, so
+  // both halves of every n2 are present once.  Entry [n1][part][g % 2][m]
+  // holds the 8 values of slots e as fp16 bits.
+  p->mfma400h.assign((size_t)25 * 2 * 2 * 16 * 8, 0);
+  for (int n1 = 0; n1 < 25; ++n1)
+    for (int h = 0; h < 2; ++h)
+      for (int m = 0; m < 16; ++m)
+        for (int e = 0; e < 8; ++e) {
+          const int n2 = 4 * (e / 2) + e % 2 + 2 * h;
+          const double v = 4096.0 * entry(n1, m, n2);
+          const _Float16 hi = (_Float16)v;
+          const _Float16 lo = (_Float16)(v - (double)hi);
+          uint16_t bh, bl;
+          std::memcpy(&bh, &hi, 2);
+          std::memcpy(&bl, &lo, 2);
+          p->mfma400h[((((size_t)n1 * 2 + 0) * 2 + h) * 16 + m) * 8 + e] = bh;
+          p->mfma400h[((((size_t)n1 * 2 + 1) * 2 + h) * 16 + m) * 8 + e] = bl;
         }
-        p->mfma400[(((size_t)j * 7 + n1 / 4) * 64 + lane) * 4 + n1 % 4] = (float)v;
-      }
 }
 
 // Filterbank tables for the n_fft = 400 kernel's mel sum on 4x4x1 matrix
