@@ -138,18 +138,27 @@ __device__ __forceinline__ void dft25(float2 (&a)[25]) {
   }
 }
 
-// min over the 16 lanes of a DPP row (rotations by 1, 2, 4, 8)
+// unsigned min over the 16 lanes of a DPP row (rotations by 1, 2, 4, 8);
+// on the bit patterns of positive floats it is the float min
 template <int N>
-__device__ __forceinline__ float ror_min(float v) {
-  const int r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + N, 0xf, 0xf, false);
-  return fminf(v, __builtin_bit_cast(float, r));
+__device__ __forceinline__ uint32_t ror_min(uint32_t v) {
+  const uint32_t r = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x120 + N, 0xf, 0xf, false);
+  return min(v, r);
 }
-__device__ __forceinline__ float row_min16(float v) {
+__device__ __forceinline__ uint32_t row_min16(uint32_t v) {
   v = ror_min<1>(v);
   v = ror_min<2>(v);
   v = ror_min<4>(v);
   return ror_min<8>(v);
 }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+
+// (log10(v) + 4) / 4 as one fma on the hardware base-2 logarithm
+constexpr float kLog10_2_Q = 0.0752574989159952988f;   // log10(2) / 4
 
 struct Args {
   const void *pcm;
@@ -553,9 +562,12 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
     const SubTile t = locate(a, gs);
     const int64_t fr = t.s * kSub + c;
     const bool valid = fr < F;
+    const bool sub_full = t.s * kSub + kSub <= F;   // uniform: every frame of the sub-tile exists
     OUT *__restrict__ ocol = out + t.b * (int64_t)NM * F + fr;
     const float *wl = s_melw + 4 * g + (c & 3);
-    float vmax = 0.0f;
+    // mel values are >= 1e-10 > 0, so their float order is the order of
+    // their bit patterns: the maximum and the minimum are kept as unsigned
+    uint32_t vmaxb = 0u;
     float wA[kMelBatch], pA[kMelBatch], wB[kMelBatch], pB[kMelBatch];
     const float *wt = wl + s_meta[1], *pp = Rc + s_meta[32 + g];
     int nst = s_meta[0];
@@ -622,23 +634,36 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
       wt = wn;
       pp = pn;
       nst = nst_n;
-      float lmn = __builtin_huge_valf();
+      uint32_t vminb = 0x7f800000u;   // +inf: no value
+      OUT *op = ocol + (int64_t)(16 * jb + 4 * g) * F;
+      if (sub_full && 16 * jb + 16 <= NM) {   // uniform: all 4 bands of every lane exist
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = 16 * jb + 4 * g + r;
-        const float v = fmaxf(acc0[r] + acc1[r], 1e-10f);
-        const float L = log10_pos(v);
-        if (valid && m < NM) {
-          vmax = fmaxf(vmax, v);
-          lmn = fminf(lmn, L);
-          store_out(ocol + (int64_t)m * F, rescale(L));
+        for (int r = 0; r < 4; ++r) {
+          const float v = fmaxf(acc0[r] + acc1[r], 1e-10f);
+          const uint32_t vb = __float_as_uint(v);
+          vmaxb = max(vmaxb, vb);
+          vminb = min(vminb, vb);
+          store_out(op, __builtin_fmaf(__builtin_amdgcn_logf(v), kLog10_2_Q, 1.0f));
+          op += F;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = fmaxf(acc0[r] + acc1[r], 1e-10f);
+          const uint32_t vb = __float_as_uint(v);
+          if (valid && 16 * jb + 4 * g + r < NM) {
+            vmaxb = max(vmaxb, vb);
+            vminb = min(vminb, vb);
+            store_out(op, __builtin_fmaf(__builtin_amdgcn_logf(v), kLog10_2_Q, 1.0f));
+          }
+          op += F;
         }
       }
-      lmn = row_min16(lmn);
-      if (c == 0) tile_min[(gs * NB + jb) * 4 + g] = lmn;
+      vminb = row_min16(vminb);
+      if (c == 0) tile_min[(gs * NB + jb) * 4 + g] = log10_pos(__uint_as_float(vminb));
     }
-    vmax = wave_max(vmax);
-    if (lane == 0) a.tile_max[gs] = vmax;
+    vmaxb = wave_max_u32(vmaxb);
+    if (lane == 0) a.tile_max[gs] = __uint_as_float(vmaxb);
   }
 }
 
