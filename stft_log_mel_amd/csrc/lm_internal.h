@@ -71,7 +71,7 @@ struct lm_plan {
   std::vector<float> untangle;    // 2 * (M/2 + 1)
   std::vector<float> mfma400;     // n_fft = 400 only: first-stage matrix-core operands (4 x 7 x 64 x 4)
   std::vector<uint16_t> mfma400h;  // the same as fp16 hi/lo parts for int16 samples (25 x 2 x 2 x 16 x 8)
-  std::vector<int32_t> melblk_meta;  // per 16-band block: klo, chunks, offset
+  std::vector<int32_t> melblk_meta;  // per batch of mel steps: first bin of each quad, last-batch flag
   std::vector<float> melblk_w;       // blocked filter weights in matrix-core lane order
 
   int device = -1;                // bound at first launch

@@ -27,9 +27,11 @@
 // 16-frame sub-tiles; its waves take every 8th one and never wait for each
 // other (one barrier after the operand tables are staged).  Each wave
 // fetches the next sub-tile's samples into registers while it computes the
-// current one.  Per sub-tile it records the largest mel value and, per
-// 4-band group of every band block, the smallest log value, for the clamp
-// fix-up kernel.
+// current one.  Per sub-tile it records the largest mel value of each of
+// its four lane groups and, per 4-band group of every band block, the
+// smallest log value, for the clamp fix-up kernel.
+#include <type_traits>
+
 #include "lm_device.h"
 #include "lm_internal.h"
 
@@ -51,7 +53,8 @@ constexpr int kRegion = kSub * kRow;      // floats of LDS per wave: staged samp
 constexpr int kAmat = 4 * 7 * 64;         // first-stage operands (v4f): [j][n1 / 4][lane]
 constexpr int kAmatH = 25 * 2 * 2 * 16;   // the fp16 form for int16 samples (8 halves each): [n1][part][g % 2][row]
 constexpr int kLoff = 1694;               // int16 samples: dword offset of the l / 64 plane in the region
-constexpr int kMelWLds = 6400;            // LDS floats for the mel step weights (and one zero batch)
+constexpr int kMelWLds = 5632;            // LDS floats for the mel step weights
+constexpr int kMelBatMax = kMelWLds / (16 * kMelBatch);   // mel batches that fit
 constexpr int kPfI16 = 6, kPfF32 = 11;    // 16-byte sample loads per lane held for the next sub-tile
 
 // compile-time cos/sin of 2 pi j / N for N a multiple of 8 (octant reduction
@@ -151,10 +154,26 @@ __device__ __forceinline__ uint32_t row_min16(uint32_t v) {
   v = ror_min<4>(v);
   return ror_min<8>(v);
 }
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+template <int N>
+__device__ __forceinline__ uint32_t ror_max(uint32_t v) {
+  const uint32_t r = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x120 + N, 0xf, 0xf, false);
+  return max(v, r);
+}
+__device__ __forceinline__ uint32_t row_max16(uint32_t v) {
+  v = ror_max<1>(v);
+  v = ror_max<2>(v);
+  v = ror_max<4>(v);
+  return ror_max<8>(v);
+}
+
+// four consecutive outputs (4-byte alignment suffices for a 16-byte store)
+typedef float v4f_a4 __attribute__((ext_vector_type(4), aligned(4)));
+__device__ __forceinline__ void store_out4(float *p, const float (&o)[4]) {
+  *reinterpret_cast<v4f_a4 *>(p) = v4f_a4{o[0], o[1], o[2], o[3]};
+}
+__device__ __forceinline__ void store_out4(__half *p, const float (&o)[4]) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
-  return v;
+  for (int i = 0; i < 4; ++i) store_out(p + i, o[i]);
 }
 
 // (log10(v) + 4) / 4 as one fma on the hardware base-2 logarithm
@@ -169,7 +188,8 @@ struct Args {
   int hop, pad, pad_mode;
   float power, pre_scale, mel_scale;
   int n_mels, n_melblk;
-  int melw_n;            // mel step weight count (plus 16 kMelBatch zeros fit kMelWLds)
+  int melw_n;            // mel step weight count (at most kMelWLds)
+  int mel_batches;       // batches of kMelBatch steps over all band blocks
   float *tile_max;
 };
 
@@ -350,9 +370,9 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
   constexpr bool kI16 = sizeof(IN) == 2;
   constexpr int kTab = kI16 ? kAmatH : kAmat;
   __shared__ v4f s_amat[kAmat];
-  __shared__ float s_melw[kMelWLds];
+  __shared__ __attribute__((aligned(16))) float s_melw[kMelWLds];
   __shared__ __attribute__((aligned(16))) float s_reg[kWaves * kRegion];
-  __shared__ int s_meta[2 * 16 + 64];   // per block: steps, weight offset; per quad: first bin
+  __shared__ int s_bat[4 * kMelBatMax];   // per mel batch and quad: first bin | last-batch flag << 16
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -367,8 +387,8 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
     for (int u = 0; u < PER; ++u)
       if (tid + u * kThreads < kTab) s_amat[tid + u * kThreads] = v[u];
   }
-  if (tid < 2 * 16 + 64) s_meta[tid] = melblk_meta[tid];
-  for (int i0 = tid; i0 < a.melw_n + 16 * kMelBatch; i0 += 4 * kThreads) {
+  for (int i = tid; i < 4 * a.mel_batches; i += kThreads) s_bat[i] = melblk_meta[i];
+  for (int i0 = tid; i0 < a.melw_n; i0 += 4 * kThreads) {
     float v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -377,7 +397,7 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      if (i0 + u * kThreads < a.melw_n + 16 * kMelBatch) s_melw[i0 + u * kThreads] = v[u];
+      if (i0 + u * kThreads < a.melw_n) s_melw[i0 + u * kThreads] = v[u];
   }
   __syncthreads();
 
@@ -552,118 +572,116 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
     }
 
     // 5. mel sums on 4x4x1 matrix blocks (16 per instruction): block (quad
-    //    g, frame quad c / 4) of step s multiplies the weights of the 4 bands
-    //    of quad 4 jb + g at bin qs + s by the power of 4 frames there, so a
-    //    step advances every quad of the 16-band block jb by one bin.  A =
-    //    weight of band 16 jb + 4 g + c % 4, B = P[frame c][qs_g + s]; lane
-    //    (c, g) gets bands 16 jb + 4 g + r of frame c.  Steps go in batches
-    //    of kMelBatch through two register sets: the next batch (or the next
-    //    block's first) is loaded while the current one is multiplied.
+    //    g, frame quad c / 4) of step s multiplies the power of 4 frames at
+    //    bin qs_g + s by the weights of the 4 bands of quad 4 jb + g there,
+    //    so a step advances every quad of the 16-band block jb by one bin.
+    //    A = P[frame c][qs_g + s], B = weight of band 16 jb + 4 g + c % 4:
+    //    lane (c, g) gets that band for the frames 4 (c / 4) + i, i < 4,
+    //    which are consecutive in the output.  The steps of all blocks run
+    //    as one sequence of batches of kMelBatch steps (every block has at
+    //    least one); a batch's operands are loaded three batches ahead,
+    //    each step reading first the table entry that the load two steps
+    //    later needs (LDS reads complete in order, so a wait for an entry
+    //    never waits for the operand loads issued after it).
+    asm volatile("" ::: "memory");   // keep the table reads below out of the transform's register peak
     const SubTile t = locate(a, gs);
-    const int64_t fr = t.s * kSub + c;
-    const bool valid = fr < F;
+    const int64_t f0 = t.s * kSub + 4 * (c >> 2);
     const bool sub_full = t.s * kSub + kSub <= F;   // uniform: every frame of the sub-tile exists
-    OUT *__restrict__ ocol = out + t.b * (int64_t)NM * F + fr;
-    const float *wl = s_melw + 4 * g + (c & 3);
+    OUT *orow = out + t.b * (int64_t)NM * F + (int64_t)(4 * g + (c & 3)) * F + f0;   // block 0's band
     // mel values are >= 1e-10 > 0, so their float order is the order of
     // their bit patterns: the maximum and the minimum are kept as unsigned
     uint32_t vmaxb = 0u;
-    float wA[kMelBatch], pA[kMelBatch], wB[kMelBatch], pB[kMelBatch];
-    const float *wt = wl + s_meta[1], *pp = Rc + s_meta[32 + g];
-    int nst = s_meta[0];
+    const int NBT = a.mel_batches;
+    const float *wl = s_melw + 16 * g + 4 * (c & 3);
+    float wR[4][kMelBatch], pR[4][kMelBatch];
+    int eR[4];
+    bool endR[4];
+    auto entry = [&](int bt) { return s_bat[4 * min(bt, NBT - 1) + g]; };
+    auto load = [&](auto slot, int bt) {
+      constexpr int S = decltype(slot)::value;
+      const v4f w4 = *reinterpret_cast<const v4f *>(wl + 16 * kMelBatch * min(bt, NBT - 1));
+      const float *pq = Rc + (eR[S] & 0xffff);
 #pragma unroll
-    for (int u = 0; u < kMelBatch; ++u) {
-      wA[u] = wt[16 * u];
-      pA[u] = pp[u];
-    }
-    for (int jb = 0; jb < NB; ++jb) {
-      const int nb = nst / kMelBatch;
-      const int jn = jb + 1 < NB ? jb + 1 : jb;
-      const float *wn = wl + s_meta[2 * jn + 1], *pn = Rc + s_meta[32 + 4 * jn + g];
-      const int nst_n = s_meta[2 * jn];
-      v4f acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (nb == 0) {   // nothing to multiply; the held operands become the next block's
-#pragma unroll
-        for (int u = 0; u < kMelBatch; ++u) {
-          wA[u] = wn[16 * u];
-          pA[u] = pn[u];
-        }
-      } else {
-        for (int k = 0;;) {
-          {
-            const bool in = k + 1 < nb;
-            const float *wq = in ? wt + 16 * kMelBatch * (k + 1) : wn;
-            const float *pq = in ? pp + kMelBatch * (k + 1) : pn;
-#pragma unroll
-            for (int u = 0; u < kMelBatch; ++u) {
-              wB[u] = wq[16 * u];
-              pB[u] = pq[u];
-            }
-          }
-#pragma unroll
-          for (int u = 0; u < kMelBatch; u += 2) {
-            acc0 = __builtin_amdgcn_mfma_f32_4x4x1f32(wA[u], pA[u], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_4x4x1f32(wA[u + 1], pA[u + 1], acc1, 0, 0, 0);
-          }
-          if (++k >= nb) {
-#pragma unroll
-            for (int u = 0; u < kMelBatch; ++u) {
-              wA[u] = wB[u];
-              pA[u] = pB[u];
-            }
-            break;
-          }
-          {
-            const bool in = k + 1 < nb;
-            const float *wq = in ? wt + 16 * kMelBatch * (k + 1) : wn;
-            const float *pq = in ? pp + kMelBatch * (k + 1) : pn;
-#pragma unroll
-            for (int u = 0; u < kMelBatch; ++u) {
-              wA[u] = wq[16 * u];
-              pA[u] = pq[u];
-            }
-          }
-#pragma unroll
-          for (int u = 0; u < kMelBatch; u += 2) {
-            acc0 = __builtin_amdgcn_mfma_f32_4x4x1f32(wB[u], pB[u], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_4x4x1f32(wB[u + 1], pB[u + 1], acc1, 0, 0, 0);
-          }
-          if (++k >= nb) break;
-        }
+      for (int u = 0; u < kMelBatch; ++u) {
+        wR[S][u] = w4[u];
+        pR[S][u] = pq[u];
       }
-      wt = wn;
-      pp = pn;
-      nst = nst_n;
-      uint32_t vminb = 0x7f800000u;   // +inf: no value
-      OUT *op = ocol + (int64_t)(16 * jb + 4 * g) * F;
-      if (sub_full && 16 * jb + 16 <= NM) {   // uniform: all 4 bands of every lane exist
+      endR[S] = (__builtin_amdgcn_readfirstlane(eR[S]) >> 16) != 0;
+    };
+    int cb = 0;
+    v4f acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto compute = [&](auto slot) {
+      constexpr int S = decltype(slot)::value;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float v = fmaxf(acc0[r] + acc1[r], 1e-10f);
+      for (int u = 0; u < kMelBatch; u += 2) {
+        acc0 = __builtin_amdgcn_mfma_f32_4x4x1f32(pR[S][u], wR[S][u], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_4x4x1f32(pR[S][u + 1], wR[S][u + 1], acc1, 0, 0, 0);
+      }
+      if (!endR[S]) return;
+      // block cb complete: log10, rescale, store, statistics
+      uint32_t vminb = 0x7f800000u;   // +inf: no value
+      if (sub_full && 16 * cb + 16 <= NM) {   // uniform: every lane's band and frames exist
+        float o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = fmaxf(acc0[i] + acc1[i], 1e-10f);
           const uint32_t vb = __float_as_uint(v);
           vmaxb = max(vmaxb, vb);
           vminb = min(vminb, vb);
-          store_out(op, __builtin_fmaf(__builtin_amdgcn_logf(v), kLog10_2_Q, 1.0f));
-          op += F;
+          o[i] = __builtin_fmaf(__builtin_amdgcn_logf(v), kLog10_2_Q, 1.0f);
         }
+        store_out4(orow, o);
       } else {
+        const bool band_ok = 16 * cb + 4 * g + (c & 3) < NM;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float v = fmaxf(acc0[r] + acc1[r], 1e-10f);
+        for (int i = 0; i < 4; ++i) {
+          const float v = fmaxf(acc0[i] + acc1[i], 1e-10f);
           const uint32_t vb = __float_as_uint(v);
-          if (valid && 16 * jb + 4 * g + r < NM) {
+          if (band_ok && f0 + i < F) {
             vmaxb = max(vmaxb, vb);
             vminb = min(vminb, vb);
-            store_out(op, __builtin_fmaf(__builtin_amdgcn_logf(v), kLog10_2_Q, 1.0f));
+            store_out(orow + i, __builtin_fmaf(__builtin_amdgcn_logf(v), kLog10_2_Q, 1.0f));
           }
-          op += F;
         }
       }
       vminb = row_min16(vminb);
-      if (c == 0) tile_min[(gs * NB + jb) * 4 + g] = log10_pos(__uint_as_float(vminb));
+      if (c == 0) tile_min[(gs * NB + cb) * 4 + g] = log10_pos(__uint_as_float(vminb));
+      acc0 = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      acc1 = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      ++cb;
+      orow += 16 * F;
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    eR[0] = entry(0);
+    eR[1] = entry(1);
+    eR[2] = entry(2);
+    eR[3] = entry(3);
+    // loads past the last batch repeat it (every wait count stays static)
+    load(I0{}, 0);
+    load(I1{}, 1);
+    load(I2{}, 2);
+    eR[0] = entry(4);
+    // step of batch i in slot S: the entry of batch i + 5 (slot S + 1), the
+    // operands of batch i + 3 (slot S + 3), then the products of batch i
+#define LM_MEL_STEP(S, S1, S3)                \
+  {                                           \
+    eR[S1::value] = entry(i + 5);             \
+    load(S3{}, i + 3);                        \
+    compute(S{});                             \
+    if (++i >= NBT) break;                    \
+  }
+    for (int i = 0; i < NBT;) {
+      LM_MEL_STEP(I0, I1, I3)
+      LM_MEL_STEP(I1, I2, I0)
+      LM_MEL_STEP(I2, I3, I1)
+      LM_MEL_STEP(I3, I0, I2)
     }
-    vmaxb = wave_max_u32(vmaxb);
-    if (lane == 0) a.tile_max[gs] = __uint_as_float(vmaxb);
+#undef LM_MEL_STEP
+    vmaxb = row_max16(vmaxb);
+    if (c == 0) a.tile_max[4 * gs + g] = __uint_as_float(vmaxb);
   }
 }
 
@@ -674,7 +692,7 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
 // blocked filter table that fits its LDS share.
 bool pcm400_supported(const lm_plan *p, bool in_i16) {
   if (p->n_fft != 400 || (p->hop & 1) || p->mfma400.empty() || p->n_mels > 256) return false;
-  if (p->melblk_w.size() + 16 * kMelBatch > (size_t)kMelWLds) return false;
+  if (p->melblk_w.size() > (size_t)kMelWLds) return false;
   const int span = (kSub - 1) * p->hop + 400;
   const int ndw = in_i16 ? span / 2 : span;
   const int lds_dw = p->hop == 160 ? ndw + 4 * (ndw / (in_i16 ? 80 : 160)) : ndw;   // skewed layout at hop 160
@@ -688,7 +706,7 @@ StatLayout pcm400_stat_layout(const lm_plan *p) {
   st.sub_per_tile = 1;
   st.blk_per_sub = 4 * ((p->n_mels + 15) / 16);
   st.band_h = 4;
-  st.max_per_tile = 1;
+  st.max_per_tile = 4;   // one per quad group of lanes
   return st;
 }
 
@@ -719,6 +737,7 @@ hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &pa, hipStream_t s) {
   k.n_mels = p->n_mels;
   k.n_melblk = p->dt.n_melblk;
   k.melw_n = (int)p->melblk_w.size();
+  k.mel_batches = (int)(p->melblk_meta.size() / 4);
   k.tile_max = pa.tile_max;
   const dim3 grid((unsigned)n_wg), block(kThreads);
   const bool f16 = p->out_dtype == LM_F16;

@@ -125,18 +125,18 @@ void build_mfma400(lm_plan *p) {
 // multiplies, for every quad Q = 4 jb + q at once, the weights of its 4
 // bands at bin qs[Q] + s by the power of 16 frames at that bin.  Block jb
 // takes nst steps (the widest of its quads' bin spans, padded to whole
-// batches of kMelBatch); qs[Q] is the quad's first non-zero bin, moved
-// down so that qs[Q] + nst stays inside the kernel's power row.
-// Tables: meta = per block (nst, weight offset) for 16 blocks (zeros past
-// the last), then qs for 64 quads; weights per step as [q][band in quad],
-// 16 floats, zero outside a band's support.
+// batches of kMelBatch steps, at least one batch); qs[Q] is the quad's
+// first non-zero bin, moved down so that qs[Q] + nst stays inside the
+// kernel's power row.  The batches of all blocks form one sequence.  Tables:
+// per batch, for each quad q of its block, the bin of its first step, with
+// bit 16 set on a block's last batch; weights per batch as [q][band in
+// quad][step], 16 kMelBatch floats, zero outside a band's support.
 void build_mel_blocks(lm_plan *p) {
   p->melblk_meta.clear();
   p->melblk_w.clear();
   if (p->n_fft != 400) return;
   const Csr &c = p->csr;
   const int NM = c.n_rows, NB = (NM + 15) / 16;
-  p->melblk_meta.assign(2 * 16 + 64, 0);
   for (int jb = 0; jb < NB; ++jb) {
     int lo[4], span[4], nst = 0;
     for (int q = 0; q < 4; ++q) {
@@ -150,18 +150,20 @@ void build_mel_blocks(lm_plan *p) {
       span[q] = khi > klo ? khi - klo : 0;
       nst = std::max(nst, span[q]);
     }
-    nst = (nst + kMelBatch - 1) / kMelBatch * kMelBatch;
-    p->melblk_meta[2 * jb] = nst;
-    p->melblk_meta[2 * jb + 1] = (int)p->melblk_w.size();
-    for (int q = 0; q < 4; ++q) p->melblk_meta[32 + 4 * jb + q] = std::min(lo[q], kPcm400Row - nst);
-    for (int s = 0; s < nst; ++s)
+    nst = std::max(kMelBatch, (nst + kMelBatch - 1) / kMelBatch * kMelBatch);
+    int qs[4];
+    for (int q = 0; q < 4; ++q) qs[q] = std::min(lo[q], kPcm400Row - nst);
+    for (int s0 = 0; s0 < nst; s0 += kMelBatch) {
+      for (int q = 0; q < 4; ++q) p->melblk_meta.push_back((qs[q] + s0) | (s0 + kMelBatch == nst ? 1 << 16 : 0));
       for (int q = 0; q < 4; ++q)
-        for (int t = 0; t < 4; ++t) {
-          const int m = 16 * jb + 4 * q + t, k = p->melblk_meta[32 + 4 * jb + q] + s;
-          float v = 0.0f;
-          if (m < NM && k >= c.start[m] && k < c.start[m] + c.width[m]) v = c.w[c.off[m] + k - c.start[m]];
-          p->melblk_w.push_back(v);
-        }
+        for (int t = 0; t < 4; ++t)
+          for (int u = 0; u < kMelBatch; ++u) {
+            const int m = 16 * jb + 4 * q + t, k = qs[q] + s0 + u;
+            float v = 0.0f;
+            if (m < NM && k >= c.start[m] && k < c.start[m] + c.width[m]) v = c.w[c.off[m] + k - c.start[m]];
+            p->melblk_w.push_back(v);
+          }
+    }
   }
 }
 
