@@ -109,38 +109,31 @@ int ensure_workspace(lm_plan *p, int64_t n_floats) {
   return LM_OK;
 }
 
-static int prof_begin(lm_plan *p, hipStream_t s, hipEvent_t *beg) {
-  if (!p->profiling) return LM_OK;
-  hipError_t e = hipEventCreate(beg);
-  if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
-  e = hipEventRecord(*beg, s);
-  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-  return LM_OK;
-}
-
-static int prof_end(lm_plan *p, hipStream_t s, hipEvent_t beg, int kind) {
-  if (!p->profiling) return LM_OK;
-  hipEvent_t end;
-  hipError_t e = hipEventCreate(&end);
-  if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
-  e = hipEventRecord(end, s);
-  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-  p->prof.push_back(ProfileRec{beg, end, kind});
-  return LM_OK;
-}
-
-// Launch `fn` bracketed by profiling events when enabled.
+// Launch through `fn(tm)`; when profiling, tm carries two new events that
+// the dispatch stamps at the kernel's start and end.
 template <typename Fn>
 static int timed_launch(lm_plan *p, hipStream_t s, int kind, const char *what, Fn fn) {
-  hipEvent_t beg{};
-  int rc = prof_begin(p, s, &beg);
-  if (rc != LM_OK) return rc;
-  hipError_t e = fn();
+  (void)s;
+  if (!p->profiling) {
+    hipError_t e = fn(nullptr);
+    return e == hipSuccess ? LM_OK : hip_fail(e, what);
+  }
+  LaunchTiming tm{};
+  hipError_t e = hipEventCreate(&tm.beg);
+  if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+  e = hipEventCreate(&tm.end);
   if (e != hipSuccess) {
-    if (p->profiling) (void)hipEventDestroy(beg);
+    (void)hipEventDestroy(tm.beg);
+    return hip_fail(e, "hipEventCreate");
+  }
+  e = fn(&tm);
+  if (e != hipSuccess) {
+    (void)hipEventDestroy(tm.beg);
+    (void)hipEventDestroy(tm.end);
     return hip_fail(e, what);
   }
-  return prof_end(p, s, beg, kind);
+  p->prof.push_back(ProfileRec{tm.beg, tm.end, kind});
+  return LM_OK;
 }
 
 }  // namespace lm
@@ -182,10 +175,10 @@ int lm_from_pcm(lm_plan *p, const void *pcm, int in_dtype, int64_t n_clips, int6
   float *tmin = p->d_stats, *tmax = p->d_stats + n_min;
 
   PcmArgs a{pcm, in_dtype == LM_I16, n_clips, n_samples, F, (int)tiles, out, tmin, tmax};
-  rc = timed_launch(p, s, 0, "launch(pcm kernel)", [&] { return launch_pcm(p, a, s); });
+  rc = timed_launch(p, s, 0, "launch(pcm kernel)", [&](const LaunchTiming *tm) { return launch_pcm(p, a, s, tm); });
   if (rc != LM_OK) return rc;
   FixupArgs fx{out, p->out_dtype == LM_F16, tmin, tmax, n_clips, F, p->n_mels, (int)tiles, st, 1};
-  return timed_launch(p, s, 1, "launch(clamp fix-up)", [&] { return launch_fixup(fx, s); });
+  return timed_launch(p, s, 1, "launch(clamp fix-up)", [&](const LaunchTiming *tm) { return launch_fixup(fx, s, tm); });
 }
 
 int lm_from_stft(lm_plan *p, const void *stft, const float *mel_filters, int64_t n_clips, int64_t n_frames,
@@ -233,7 +226,7 @@ int lm_from_stft(lm_plan *p, const void *stft, const float *mel_filters, int64_t
     }
     int32_t *sw = reinterpret_cast<int32_t *>(p->d_pack);
     rc = timed_launch(p, s, 2, "launch(filter rows)",
-                      [&] { return launch_pack(mel_filters, n_mels, (int)n_bins, sw, s); });
+                      [&](const LaunchTiming *tm) { return launch_pack(mel_filters, n_mels, (int)n_bins, sw, s, tm); });
     if (rc != LM_OK) return rc;
     a.f_start = sw;
     a.f_width = sw + n_mels;
@@ -245,13 +238,13 @@ int lm_from_stft(lm_plan *p, const void *stft, const float *mel_filters, int64_t
     a.f_off = p->dt.csr_off;
     a.f_w = p->dt.csr_w;
   }
-  rc = timed_launch(p, s, 0, "launch(stft kernel)", [&] { return launch_stft(a, s); });
+  rc = timed_launch(p, s, 0, "launch(stft kernel)", [&](const LaunchTiming *tm) { return launch_stft(a, s, tm); });
   if (rc != LM_OK) return rc;
   StatLayout st;
   st.frames_per_tile = tf;
   st.band_h = n_mels;
   FixupArgs fx{out, p->out_dtype == LM_F16, tmin, tmax, n_clips, n_frames, n_mels, (int)tiles, st, 0};
-  return timed_launch(p, s, 1, "launch(clamp fix-up)", [&] { return launch_fixup(fx, s); });
+  return timed_launch(p, s, 1, "launch(clamp fix-up)", [&](const LaunchTiming *tm) { return launch_fixup(fx, s, tm); });
 }
 
 int lm_plan_profile(lm_plan *p, int enable) {

@@ -16,11 +16,11 @@ __global__ void __launch_bounds__(kFixThreads) clamp_fixup_kernel(FixupArgs a) {
   fixup_group<OUT, kFixThreads>(a, b, (int)(blockIdx.x - b * G), s_list, &s_n, s_red);
 }
 
-hipError_t launch_fixup(FixupArgs a, hipStream_t s) {
+hipError_t launch_fixup(FixupArgs a, hipStream_t s, const LaunchTiming *tm) {
   prepare_fixup(a);
   const dim3 grid((unsigned)(a.n_clips * a.groups_per_clip)), block(kFixThreads);
-  if (a.out_f16) hipLaunchKernelGGL(clamp_fixup_kernel<__half>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(clamp_fixup_kernel<float>, grid, block, 0, s, a);
+  if (a.out_f16) LM_LAUNCH(tm, clamp_fixup_kernel<__half>, grid, block, 0, s, a);
+  else LM_LAUNCH(tm, clamp_fixup_kernel<float>, grid, block, 0, s, a);
   return hipGetLastError();
 }
 

@@ -2,6 +2,7 @@
 // kernel launchers.  Not part of the public ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -11,6 +12,18 @@
 #include "lm.h"
 
 namespace lm {
+
+// Optional timing of one kernel launch: events stamped by the dispatch
+// itself at the kernel's start and end (hipExtLaunchKernelGGL), so a
+// profiled duration excludes the launch gap before the kernel.
+struct LaunchTiming {
+  hipEvent_t beg, end;
+};
+#define LM_LAUNCH(tm, K, grid, block, shmem, s, ...)                                           \
+  do {                                                                                         \
+    if (tm) hipExtLaunchKernelGGL(K, grid, block, shmem, s, (tm)->beg, (tm)->end, 0u, __VA_ARGS__); \
+    else hipLaunchKernelGGL(K, grid, block, shmem, s, __VA_ARGS__);                            \
+  } while (0)
 
 // Power row stride (floats) of the n_fft = 400 kernel: bins 0..200 plus
 // zeroed padding that chunked mel reads may touch (20 c mod 64 spreads 16
@@ -134,10 +147,10 @@ struct PcmArgs {
 // input type (the n_fft = 400 matrix-core kernel when it applies, else the
 // generic one).
 StatLayout pcm_stat_layout(const lm_plan *p, bool in_i16);
-hipError_t launch_pcm(const lm_plan *p, const PcmArgs &a, hipStream_t s);
+hipError_t launch_pcm(const lm_plan *p, const PcmArgs &a, hipStream_t s, const LaunchTiming *tm);
 bool pcm400_supported(const lm_plan *p, bool in_i16);
 StatLayout pcm400_stat_layout(const lm_plan *p);
-hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &a, hipStream_t s);
+hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &a, hipStream_t s, const LaunchTiming *tm);
 
 struct StftArgs {
   const float2 *stft;
@@ -157,11 +170,12 @@ struct StftArgs {
   int n_cu;
 };
 int stft_frames_per_tile(int n_bins, int n_mels);
-hipError_t launch_stft(const StftArgs &a, hipStream_t s);
+hipError_t launch_stft(const StftArgs &a, hipStream_t s, const LaunchTiming *tm);
 
 // First non-zero bin and width of every row of a device dense (n_mels,
 // n_bins) filterbank into start_width[0, n_mels) and [n_mels, 2 n_mels).
-hipError_t launch_pack(const float *dense, int n_mels, int n_bins, int32_t *start_width, hipStream_t s);
+hipError_t launch_pack(const float *dense, int n_mels, int n_bins, int32_t *start_width, hipStream_t s,
+                       const LaunchTiming *tm);
 
 struct FixupArgs {
   void *out;
@@ -175,6 +189,6 @@ struct FixupArgs {
   int mel_major;  // 1: (B, NM, F); 0: (B, F, NM)
   int entries_per_group = 0, groups_per_clip = 0;   // set by launch_fixup
 };
-hipError_t launch_fixup(FixupArgs a, hipStream_t s);
+hipError_t launch_fixup(FixupArgs a, hipStream_t s, const LaunchTiming *tm);
 
 }  // namespace lm

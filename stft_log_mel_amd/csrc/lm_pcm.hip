@@ -282,13 +282,14 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
 }
 
 template <int NFFT>
-static hipError_t launch_n(const PcmKernelArgs &k, bool i16, bool f16, int64_t n_tiles, hipStream_t s) {
+static hipError_t launch_n(const PcmKernelArgs &k, bool i16, bool f16, int64_t n_tiles, hipStream_t s,
+                           const LaunchTiming *tm) {
   constexpr int THREADS = PcmCfg<NFFT>::THREADS;
   const dim3 grid((unsigned)n_tiles), block(THREADS);
-  if (!i16 && !f16) hipLaunchKernelGGL((pcm_logmel_kernel<NFFT, float, float>), grid, block, 0, s, k);
-  else if (!i16 && f16) hipLaunchKernelGGL((pcm_logmel_kernel<NFFT, float, __half>), grid, block, 0, s, k);
-  else if (i16 && !f16) hipLaunchKernelGGL((pcm_logmel_kernel<NFFT, int16_t, float>), grid, block, 0, s, k);
-  else hipLaunchKernelGGL((pcm_logmel_kernel<NFFT, int16_t, __half>), grid, block, 0, s, k);
+  if (!i16 && !f16) LM_LAUNCH(tm, (pcm_logmel_kernel<NFFT, float, float>), grid, block, 0, s, k);
+  else if (!i16 && f16) LM_LAUNCH(tm, (pcm_logmel_kernel<NFFT, float, __half>), grid, block, 0, s, k);
+  else if (i16 && !f16) LM_LAUNCH(tm, (pcm_logmel_kernel<NFFT, int16_t, float>), grid, block, 0, s, k);
+  else LM_LAUNCH(tm, (pcm_logmel_kernel<NFFT, int16_t, __half>), grid, block, 0, s, k);
   return hipGetLastError();
 }
 
@@ -318,8 +319,8 @@ StatLayout pcm_stat_layout(const lm_plan *p, bool in_i16) {
   return st;
 }
 
-hipError_t launch_pcm(const lm_plan *p, const PcmArgs &a, hipStream_t s) {
-  if (use_pcm400(p, a.in_i16)) return launch_pcm400(p, a, s);
+hipError_t launch_pcm(const lm_plan *p, const PcmArgs &a, hipStream_t s, const LaunchTiming *tm) {
+  if (use_pcm400(p, a.in_i16)) return launch_pcm400(p, a, s, tm);
   PcmKernelArgs k;
   k.pcm = a.pcm;
   k.T = a.n_samples;
@@ -353,16 +354,16 @@ hipError_t launch_pcm(const lm_plan *p, const PcmArgs &a, hipStream_t s) {
   const int64_t n_tiles = a.n_clips * a.tiles_per_clip;
   const bool f16 = p->out_dtype == LM_F16;
   switch (p->n_fft) {
-    case 400: return launch_n<400>(k, a.in_i16, f16, n_tiles, s);
-    case 64: return launch_n<64>(k, a.in_i16, f16, n_tiles, s);
-    case 128: return launch_n<128>(k, a.in_i16, f16, n_tiles, s);
-    case 256: return launch_n<256>(k, a.in_i16, f16, n_tiles, s);
-    case 512: return launch_n<512>(k, a.in_i16, f16, n_tiles, s);
-    case 1024: return launch_n<1024>(k, a.in_i16, f16, n_tiles, s);
-    case 2048: return launch_n<2048>(k, a.in_i16, f16, n_tiles, s);
-    case 4096: return launch_n<4096>(k, a.in_i16, f16, n_tiles, s);
-    case 8192: return launch_n<8192>(k, a.in_i16, f16, n_tiles, s);
-    case 16384: return launch_n<16384>(k, a.in_i16, f16, n_tiles, s);
+    case 400: return launch_n<400>(k, a.in_i16, f16, n_tiles, s, tm);
+    case 64: return launch_n<64>(k, a.in_i16, f16, n_tiles, s, tm);
+    case 128: return launch_n<128>(k, a.in_i16, f16, n_tiles, s, tm);
+    case 256: return launch_n<256>(k, a.in_i16, f16, n_tiles, s, tm);
+    case 512: return launch_n<512>(k, a.in_i16, f16, n_tiles, s, tm);
+    case 1024: return launch_n<1024>(k, a.in_i16, f16, n_tiles, s, tm);
+    case 2048: return launch_n<2048>(k, a.in_i16, f16, n_tiles, s, tm);
+    case 4096: return launch_n<4096>(k, a.in_i16, f16, n_tiles, s, tm);
+    case 8192: return launch_n<8192>(k, a.in_i16, f16, n_tiles, s, tm);
+    case 16384: return launch_n<16384>(k, a.in_i16, f16, n_tiles, s, tm);
     default: return hipErrorInvalidValue;
   }
 }

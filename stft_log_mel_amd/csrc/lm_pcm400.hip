@@ -710,7 +710,7 @@ StatLayout pcm400_stat_layout(const lm_plan *p) {
   return st;
 }
 
-hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &pa, hipStream_t s) {
+hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &pa, hipStream_t s, const LaunchTiming *tm) {
   Args k;
   k.pcm = pa.pcm;
   k.T = pa.n_samples;
@@ -744,10 +744,10 @@ hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &pa, hipStream_t s) {
   const v4f *am = reinterpret_cast<const v4f *>(pa.in_i16 ? (const void *)p->dt.mfma400h : (const void *)p->dt.mfma400);
   const int32_t *bm = p->dt.melblk_meta;
   const float *bw = p->dt.melblk_w;
-  float *tm = pa.tile_min;
+  float *tmin = pa.tile_min;
   const bool sk = p->hop == 160;
 #define LM_P400(IN, OUT, SK) \
-  hipLaunchKernelGGL((pcm400_kernel<IN, OUT, SK>), grid, block, 0, s, k, am, bm, bw, (OUT *)pa.out, tm)
+  LM_LAUNCH(tm, (pcm400_kernel<IN, OUT, SK>), grid, block, 0, s, k, am, bm, bw, (OUT *)pa.out, tmin)
   if (!pa.in_i16 && !f16) {
     if (sk) LM_P400(float, float, true);
     else LM_P400(float, float, false);

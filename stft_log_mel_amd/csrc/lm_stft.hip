@@ -182,7 +182,7 @@ int stft_frames_per_tile(int n_bins, int n_mels) {
   return tf;
 }
 
-hipError_t launch_stft(const StftArgs &a, hipStream_t s) {
+hipError_t launch_stft(const StftArgs &a, hipStream_t s, const LaunchTiming *tm) {
   StftKernelArgs k;
   k.stft = a.stft;
   k.F = a.n_frames;
@@ -204,11 +204,11 @@ hipError_t launch_stft(const StftArgs &a, hipStream_t s) {
   const dim3 grid((unsigned)(k.n_tiles < cap ? k.n_tiles : cap)), block(kStftThreads);
   const bool vec16 = (reinterpret_cast<uintptr_t>(a.stft) & 15) == 0;
   if (a.out_f16) {
-    if (vec16) hipLaunchKernelGGL((stft_logmel_kernel<__half, true>), grid, block, lds, s, k);
-    else hipLaunchKernelGGL((stft_logmel_kernel<__half, false>), grid, block, lds, s, k);
+    if (vec16) LM_LAUNCH(tm, (stft_logmel_kernel<__half, true>), grid, block, lds, s, k);
+    else LM_LAUNCH(tm, (stft_logmel_kernel<__half, false>), grid, block, lds, s, k);
   } else {
-    if (vec16) hipLaunchKernelGGL((stft_logmel_kernel<float, true>), grid, block, lds, s, k);
-    else hipLaunchKernelGGL((stft_logmel_kernel<float, false>), grid, block, lds, s, k);
+    if (vec16) LM_LAUNCH(tm, (stft_logmel_kernel<float, true>), grid, block, lds, s, k);
+    else LM_LAUNCH(tm, (stft_logmel_kernel<float, false>), grid, block, lds, s, k);
   }
   return hipGetLastError();
 }
@@ -251,8 +251,9 @@ __global__ void __launch_bounds__(256) filter_rows_kernel(const float *__restric
   }
 }
 
-hipError_t launch_pack(const float *dense, int n_mels, int n_bins, int32_t *start_width, hipStream_t s) {
-  hipLaunchKernelGGL(filter_rows_kernel, dim3((unsigned)((n_mels + 3) / 4)), dim3(256), 0, s, dense, n_mels, n_bins,
+hipError_t launch_pack(const float *dense, int n_mels, int n_bins, int32_t *start_width, hipStream_t s,
+                       const LaunchTiming *tm) {
+  LM_LAUNCH(tm, filter_rows_kernel, dim3((unsigned)((n_mels + 3) / 4)), dim3(256), 0, s, dense, n_mels, n_bins,
                      start_width, start_width + n_mels);
   return hipGetLastError();
 }
