@@ -26,9 +26,10 @@ struct LaunchTiming {
   } while (0)
 
 // Power row stride (floats) of the n_fft = 400 kernel: bins 0..200 plus
-// zeroed padding that chunked mel reads may touch (20 c mod 64 spreads 16
-// rows over distinct bank quads).
-constexpr int kPcm400Row = 212;
+// zeroed padding that chunked mel reads may touch; odd, so that the rows
+// of 16 frames read or written by one instruction fall on distinct LDS
+// banks (even strides were measured to serialise LDS accesses).
+constexpr int kPcm400Row = 213;
 // Chunks of 4 bins the n_fft = 400 mel loop takes per step; every band
 // block's chunk count is a multiple of it.
 constexpr int kMelBatch = 4;

@@ -561,10 +561,10 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
       }
     }
     // zero the pad columns 201..211 of the lane's row, which the last chunks read
-    static_assert(kRow == 212, "pad columns below assume 11 of them");
+    static_assert(kRow == 213, "pad columns below assume 12 of them");
     Rc[201 + g] = 0.0f;
     Rc[205 + g] = 0.0f;
-    if (g < 3) Rc[209 + g] = 0.0f;
+    Rc[209 + g] = 0.0f;
     if (a.power != 2.0f) {
       // |X|^p = (|X|^2)^(p/2) in place over the wave's rows
       const float pe = 0.5f * a.power;
