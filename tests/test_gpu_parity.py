@@ -320,3 +320,24 @@ def test_pcm400_fast_and_generic_paths(hop, in_dtype, monkeypatch):
         say("pcm400 path", hop, in_dtype, "force_generic", force)
         out = run_pcm(x, 400, hop, 128, 16000.0)
         check(out, ref, TOL32, f"hop {hop} {in_dtype} generic={force}")
+
+
+def test_pcm400_int16_two_part_fp16_first_stage_precision():
+    """For int16 input the n_fft = 400 first stage runs on fp16 matrix cores,
+    but only as an exact two-part split of every sample (x/64 = h + l/64,
+    both exact in fp16) against a two-part (hi + lo) fp16 matrix, summed in
+    fp32.  Its error against the oracle must stay at the level of the fp32
+    path run on the same samples as float32, and far inside the gate, also
+    on clips with quiet passages and a floor that binds."""
+    B, T = 4, 48000
+    x = lm_synth.speech_pcm(B, T, 16000.0, seed=31, as_int16=True)
+    x[1, 16000:32000] = (x[1, 16000:32000].astype(np.int32) // 256).astype(np.int16)   # about -48 dB
+    x[2] = (x[2].astype(np.int32) // 64).astype(np.int16)                              # quiet clip
+    x[3, 20000:28000] = 0                                                              # digital silence
+    xf = (x.astype(np.float32) / np.float32(32768.0)).astype(np.float32)               # the same samples
+    ref = oracle_pcm(x, 400, 160, 128, 16000.0)
+    say("pcm400 int16 two-part fp16 first stage vs fp32 path")
+    e16 = check(run_pcm(x, 400, 160, 128, 16000.0), ref, TOL32, "int16 (two-part fp16 first stage)")
+    e32 = check(run_pcm(xf, 400, 160, 128, 16000.0), ref, TOL32, "f32 (fp32 first stage)")
+    print(f"[case] max |err| int16 path {e16:.3e}, f32 path {e32:.3e}", flush=True)
+    assert e16 <= max(2.0 * e32, 1e-5), (e16, e32)
