@@ -66,7 +66,7 @@ def lib_path() -> str:
 
 def _load():
     if not os.path.exists(_LIB_PATH):
-        raise ImportError(f"{_LIB_PATH} is not built; run `python -m stft_log_mel_amd.build` "
+        raise ImportError(f"{_LIB_PATH} is not built; run `python stft_log_mel_amd/build.py` "
                           "(there is no fallback implementation)")
     lib = ctypes.CDLL(_LIB_PATH)
     for name, (res, args) in SIGNATURES.items():

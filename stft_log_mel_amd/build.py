@@ -1,6 +1,8 @@
 """Build liblm.so (the HIP library behind include/lm.h) in-tree for gfx950.
 
-    python -m stft_log_mel_amd.build [-v]
+    python stft_log_mel_amd/build.py [-v]
+
+(run as a file: importing the package needs the library this builds)
 
 Every source is compiled with hipcc for gfx950 only.  Packed-FP32 vector
 instructions are switched off for the device code (the host pass warns that
