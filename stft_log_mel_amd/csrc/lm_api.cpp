@@ -41,7 +41,8 @@ int upload_tables(lm_plan *p) {
   size_t o_mh = align256(o_mf + sizeof(float) * p->mfma400.size());
   size_t o_bm = align256(o_mh + sizeof(uint16_t) * p->mfma400h.size());
   size_t o_bw = align256(o_bm + sizeof(int32_t) * p->melblk_meta.size());
-  size_t total = align256(o_bw + sizeof(float) * p->melblk_w.size() + 16);
+  size_t o_t2 = align256(o_bw + sizeof(float) * p->melblk_w.size());
+  size_t total = align256(o_t2 + sizeof(float) * p->twid2.size() + 16);
   std::vector<unsigned char> host(total, 0);
   std::memcpy(host.data() + o_win, p->window.data(), sizeof(float) * N);
   std::memcpy(host.data() + o_tw, p->twiddle.data(), sizeof(float) * 2 * M);
@@ -60,6 +61,7 @@ int upload_tables(lm_plan *p) {
     std::memcpy(host.data() + o_bm, p->melblk_meta.data(), sizeof(int32_t) * p->melblk_meta.size());
     std::memcpy(host.data() + o_bw, p->melblk_w.data(), sizeof(float) * p->melblk_w.size());
   }
+  if (!p->twid2.empty()) std::memcpy(host.data() + o_t2, p->twid2.data(), sizeof(float) * p->twid2.size());
   if (p->dt.base) {
     hipError_t e = hipFree(p->dt.base);
     p->dt.base = nullptr;
@@ -79,6 +81,7 @@ int upload_tables(lm_plan *p) {
   p->dt.window = reinterpret_cast<const float *>(c + o_win);
   p->dt.twiddle = reinterpret_cast<const float2 *>(c + o_tw);
   p->dt.untangle = reinterpret_cast<const float2 *>(c + o_ut);
+  p->dt.tw2 = p->twid2.empty() ? nullptr : reinterpret_cast<const float2 *>(c + o_t2);
   p->dt.csr_start = reinterpret_cast<const int32_t *>(c + o_st);
   p->dt.csr_width = reinterpret_cast<const int32_t *>(c + o_wd);
   p->dt.csr_off = reinterpret_cast<const int32_t *>(c + o_of);

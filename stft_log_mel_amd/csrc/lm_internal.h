@@ -50,12 +50,14 @@ struct Csr {
 // Device copy of the tables one PCM launch reads.  One allocation:
 //   [window n_fft f32][fft twiddles M f32x2][untangle twiddles M/2+1 f32x2]
 //   [csr start n_mels i32][csr width n_mels i32][csr off n_mels i32][csr w nnz f32]
+//   [n_fft = 400 matrix-core operands][blocked filterbank][two-level twiddles]
 struct DeviceTables {
   void *base = nullptr;
   size_t bytes = 0;
   const float *window = nullptr;
   const float2 *twiddle = nullptr;    // exp(-2 pi i j / M), j < M
   const float2 *untangle = nullptr;   // exp(-2 pi i k / n_fft), k <= M/2
+  const float2 *tw2 = nullptr;        // n_fft >= 8192: two-level exp(-2 pi i j / n_fft) table
   const int32_t *csr_start = nullptr, *csr_width = nullptr, *csr_off = nullptr;
   const float *csr_w = nullptr;
   int nnz = 0;
@@ -83,6 +85,7 @@ struct lm_plan {
   std::vector<float> window;      // n_fft
   std::vector<float> twiddle;     // 2 * M
   std::vector<float> untangle;    // 2 * (M/2 + 1)
+  std::vector<float> twid2;       // n_fft >= 8192: 2 * (n_fft / 128 + 128), see build_twiddles
   std::vector<float> mfma400;     // n_fft = 400 only: first-stage matrix-core operands (4 x 7 x 64 x 4)
   std::vector<uint16_t> mfma400h;  // the same as fp16 hi/lo parts for int16 samples (25 x 2 x 2 x 16 x 8)
   std::vector<int32_t> melblk_meta;  // per batch of mel steps: first bin of each quad, last-batch flag

@@ -31,8 +31,8 @@ struct Radices {};
 template <int NFFT>
 struct PcmCfg;
 // FPB frames per tile, THREADS per workgroup, radix sequence of M = NFFT/2,
-// WLDS floats of LDS for staged filter weights (0: weights read from
-// global memory, which leaves room for two workgroups per CU).
+// WLDS floats of LDS for staged filter weights (weights past that count
+// are read from global memory).
 template <> struct PcmCfg<400>   { static constexpr int FPB = 16,  THREADS = 256, WLDS = 4096; using Rad = Radices<8, 5, 5>; };
 template <> struct PcmCfg<64>    { static constexpr int FPB = 128, THREADS = 256, WLDS = 4096; using Rad = Radices<16, 2>; };
 template <> struct PcmCfg<128>   { static constexpr int FPB = 64,  THREADS = 256, WLDS = 4096; using Rad = Radices<16, 4>; };
@@ -41,8 +41,9 @@ template <> struct PcmCfg<512>   { static constexpr int FPB = 16,  THREADS = 256
 template <> struct PcmCfg<1024>  { static constexpr int FPB = 8,   THREADS = 256, WLDS = 4096; using Rad = Radices<8, 8, 8>; };
 template <> struct PcmCfg<2048>  { static constexpr int FPB = 4,   THREADS = 256, WLDS = 4096; using Rad = Radices<16, 16, 4>; };
 template <> struct PcmCfg<4096>  { static constexpr int FPB = 2,   THREADS = 256, WLDS = 4096; using Rad = Radices<16, 16, 8>; };
-template <> struct PcmCfg<8192>  { static constexpr int FPB = 1,   THREADS = 256, WLDS = 0;    using Rad = Radices<16, 16, 16>; };
-template <> struct PcmCfg<16384> { static constexpr int FPB = 1,   THREADS = 512, WLDS = 0;    using Rad = Radices<16, 16, 16, 2>; };
+// n_fft 8192 and 16384 (one frame per tile) run in pcm_big_kernel below
+template <> struct PcmCfg<8192>  { static constexpr int FPB = 1; };
+template <> struct PcmCfg<16384> { static constexpr int FPB = 1; };
 
 __device__ __forceinline__ float to_f(float v) { return v; }
 __device__ __forceinline__ float to_f(int16_t v) { return (float)(int)v; }
@@ -62,8 +63,14 @@ __device__ __forceinline__ int64_t pad_source(int64_t j, int64_t T, int mode) {
 // multiplies a[t] by exp(-2 pi i t k / (Ns R)), transforms, and writes
 // b[s] to ((j / Ns) Ns R + k + s Ns).  After the last pass the frame holds
 // its DFT in natural order.
-template <int R, int M, int FPB, int THREADS, int Ns>
-__device__ __forceinline__ void fft_pass(float2 *buf, const float2 *__restrict__ tw) {
+// LDS position of point i of the FFT buffer: with PAD > 0 one spare
+// float2 follows every 2^PAD points, so that the strided accesses of the
+// early passes fall on distinct banks.
+template <int PAD>
+__device__ __forceinline__ int lds_pos(int i) { return PAD ? i + (i >> PAD) : i; }
+
+template <int R, int M, int FPB, int THREADS, int Ns, int PAD, typename TW>
+__device__ __forceinline__ void fft_pass(float2 *buf, TW tw, int tid) {
   constexpr int NBF = M / R;                 // butterflies per frame
   constexpr int NB = FPB * NBF;
   constexpr int BPT = (NB + THREADS - 1) / THREADS;
@@ -71,16 +78,15 @@ __device__ __forceinline__ void fft_pass(float2 *buf, const float2 *__restrict__
   float2 v[BPT][R];
 #pragma unroll
   for (int i = 0; i < BPT; ++i) {
-    const int q = threadIdx.x + i * THREADS;
+    const int q = tid + i * THREADS;
     if (NB % THREADS == 0 || q < NB) {
       const int f = q / NBF, j = q - f * NBF;
-      const float2 *fb = buf + f * M;
 #pragma unroll
-      for (int t = 0; t < R; ++t) v[i][t] = fb[j + t * NBF];
+      for (int t = 0; t < R; ++t) v[i][t] = buf[lds_pos<PAD>(f * M + j + t * NBF)];
       if (Ns > 1) {
         const int k = j % Ns;
 #pragma unroll
-        for (int t = 1; t < R; ++t) v[i][t] = cmul(v[i][t], tw[t * k * TW_STEP]);
+        for (int t = 1; t < R; ++t) v[i][t] = cmul(v[i][t], tw(t * k * TW_STEP));
       }
       dft<R>(v[i]);
     }
@@ -88,27 +94,29 @@ __device__ __forceinline__ void fft_pass(float2 *buf, const float2 *__restrict__
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < BPT; ++i) {
-    const int q = threadIdx.x + i * THREADS;
+    const int q = tid + i * THREADS;
     if (NB % THREADS == 0 || q < NB) {
       const int f = q / NBF, j = q - f * NBF;
       const int k = j % Ns;
-      float2 *fb = buf + f * M + (j / Ns) * Ns * R + k;
+      const int o = f * M + (j / Ns) * Ns * R + k;
 #pragma unroll
-      for (int s = 0; s < R; ++s) fb[s * Ns] = v[i][s];
+      for (int s = 0; s < R; ++s) buf[lds_pos<PAD>(o + s * Ns)] = v[i][s];
     }
   }
   __syncthreads();
 }
 
-template <int M, int FPB, int THREADS, int Ns, int R, int... Rest>
-__device__ __forceinline__ void fft_passes(float2 *buf, const float2 *__restrict__ tw) {
-  fft_pass<R, M, FPB, THREADS, Ns>(buf, tw);
-  if constexpr (sizeof...(Rest) > 0) fft_passes<M, FPB, THREADS, Ns * R, Rest...>(buf, tw);
+template <int M, int FPB, int THREADS, int Ns, int PAD, typename TW, int R, int... Rest>
+__device__ __forceinline__ void fft_passes(float2 *buf, TW tw, int tid) {
+  fft_pass<R, M, FPB, THREADS, Ns, PAD>(buf, tw, tid);
+  if constexpr (sizeof...(Rest) > 0) fft_passes<M, FPB, THREADS, Ns * R, PAD, TW, Rest...>(buf, tw, tid);
 }
 
-template <int M, int FPB, int THREADS, int... R>
-__device__ __forceinline__ void run_fft(float2 *buf, const float2 *__restrict__ tw, Radices<R...>) {
-  fft_passes<M, FPB, THREADS, 1, R...>(buf, tw);
+// `tw(j)` returns exp(-2 pi i j / M) for 0 <= j < M; `tid` is the thread's
+// index in the workgroup; point i of frame f sits at lds_pos<PAD>(f M + i)
+template <int M, int FPB, int THREADS, int PAD, typename TW, int... R>
+__device__ __forceinline__ void run_fft(float2 *buf, TW tw, Radices<R...>, int tid) {
+  fft_passes<M, FPB, THREADS, 1, PAD, TW, R...>(buf, tw, tid);
 }
 
 struct PcmKernelArgs {
@@ -122,6 +130,7 @@ struct PcmKernelArgs {
   int n_mels;
   const float *window;
   const float2 *twiddle, *untangle;
+  const float2 *tw2;    // n_fft >= 8192: exp(-2 pi i 128 h / n_fft) for h < n_fft / 128, then exp(-2 pi i l / n_fft), l < 128
   const int32_t *csr_start, *csr_width, *csr_off;
   const float *csr_w;
   int nnz;
@@ -187,7 +196,8 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
   __syncthreads();
 
   // 2. M-point complex FFT per frame
-  run_fft<M, FPB, THREADS>(s_buf, a.twiddle, typename PcmCfg<NFFT>::Rad{});
+  const float2 *__restrict__ twt = a.twiddle;
+  run_fft<M, FPB, THREADS, 0>(s_buf, [=](int j) { return twt[j]; }, typename PcmCfg<NFFT>::Rad{}, tid);
 
   // 3. split into the real spectrum; power tile over the same LDS
   constexpr int NU = M / 2 + 1;              // pairs (k, M-k), k = 0..M/2
@@ -233,27 +243,6 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
   // instructions (a pointer that may point either way would make every
   // weight load a flat load that waits for all outstanding global loads)
   auto mel = [&](const float *wsrc) {
-    if (FPB == 1) {
-      // one frame: a wave per band, lanes across the band's bins (wide
-      // bands at large n_fft), then a wave sum
-      const int lane = tid & 63, wv = tid >> 6;
-      const int64_t fr = f0;
-      if (fr >= F) return;
-      for (int m = wv; m < NM; m += NW) {
-        const int st = s_start[m], wd = s_width[m];
-        const float *pr = P + st;
-        const float *wr = wsrc + s_off[m];
-        float acc = 0.0f;
-        for (int j = lane; j < wd; j += 64) acc = __builtin_fmaf(wr[j], pr[j], acc);
-        acc = wave_sum(acc);
-        const float v = fmaxf(acc * a.mel_scale, 1e-10f);
-        const float L = log10_pos(v);
-        vmax = fmaxf(vmax, v);
-        lmin = fminf(lmin, L);
-        if (lane == 0) store_out(out + (int64_t)m * F + fr, rescale(L));
-      }
-      return;
-    }
     for (int o = tid; o < NM * FPB; o += THREADS) {
       const int fl = o % FPB, m = o / FPB;
       const int64_t fr = f0 + fl;
@@ -279,6 +268,208 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
     a.tile_max[tile] = vmax;
     a.tile_min[tile] = lmin;
   }
+}
+
+// ---------------------------------------------------------------------------
+// n_fft >= 8192: one frame fills a workgroup's FFT buffer, so the kernel is
+// persistent instead: one workgroup per compute unit stages the packed
+// filterbank and a two-level twiddle table in LDS once, then walks frames
+// gridDim.x apart.  Per frame the phases are those above (windowed load,
+// folded complex FFT, split and power, mel, statistics), with no global
+// memory access between the load and the store: every twiddle is the
+// product of two LDS entries, exp(-2 pi i j / N) = W[j / 128] W'[j % 128].
+// The next frame's samples are loaded into registers while the mel sums of
+// the current one run.  The mel gives every band L consecutive lanes (L =
+// the largest power of two with L * n_mels <= THREADS, at most 64), which
+// stride over the band's bins and combine their partial sums with xor
+// shuffles, so no band waits on another band's reduction.
+// ---------------------------------------------------------------------------
+template <int NFFT>
+struct BigCfg;
+template <> struct BigCfg<8192>  { static constexpr int THREADS = 512;  using Rad = Radices<16, 16, 16>; };
+template <> struct BigCfg<16384> { static constexpr int THREADS = 1024; using Rad = Radices<16, 8, 8, 8>; };
+
+constexpr int kTwLo = 128;   // entries of the low twiddle table
+constexpr int kBigPad = 5;   // FFT buffer: one spare point per 32
+
+template <int NFFT>
+constexpr int big_wlds() {
+  // LDS floats left for filter weights next to the FFT buffer (M float2),
+  // the twiddle tables and the row tables, within one workgroup's 160 KB
+  return (160 * 1024 - (NFFT / 2 + (NFFT >> (kBigPad + 1))) * 8 - (NFFT / kTwLo + kTwLo) * 8 - 3 * 256 * 4 - 1024) / 4;
+}
+
+template <int NFFT, typename IN, typename OUT>
+__global__ void __launch_bounds__(BigCfg<NFFT>::THREADS) pcm_big_kernel(PcmKernelArgs a, int64_t n_tiles) {
+  constexpr int M = NFFT / 2;
+  constexpr int THREADS = BigCfg<NFFT>::THREADS;
+  constexpr int NW = THREADS / 64;
+  constexpr int WLDS = big_wlds<NFFT>();
+  constexpr int THI = NFFT / kTwLo;
+  __shared__ float2 s_buf[M + (M >> kBigPad)];
+  __shared__ float2 s_tw[THI + kTwLo];   // exp(-2 pi i 128 h / N), then exp(-2 pi i l / N)
+  __shared__ int32_t s_start[256], s_width[256], s_off[256];
+  __shared__ float s_w[WLDS];
+  __shared__ float s_red[2 * NW];
+
+  const int NM = a.n_mels;
+  for (int i = threadIdx.x; i < THI + kTwLo; i += THREADS) s_tw[i] = a.tw2[i];
+  const int nnz = stage_filters<THREADS>(NM, a.csr_start, a.csr_width, a.csr_off, a.csr_w, a.nnz, s_start, s_width,
+                                         s_off, s_w, WLDS);
+  const bool w_in_lds = nnz <= WLDS;
+  int L = 64;   // lanes per band (uniform)
+  while (L > 1 && L * NM > THREADS) L >>= 1;
+  const int64_t T = a.T, F = a.F;
+  constexpr int IPT = M / THREADS;   // complex points per thread
+  static_assert(M % THREADS == 0, "whole points per thread");
+  // exp(-2 pi i j / N), 0 <= j < N
+  auto wN = [&](int j) { return cmul(s_tw[j >> 7], s_tw[THI + (j & (kTwLo - 1))]); };
+
+  // samples of an interior frame (no padding), all loads in flight together;
+  // thread tid takes points n = tid + THREADS u
+  float xs[IPT][2];
+  auto load_interior = [&](int64_t tile, int tid) {
+    const int64_t b = tile / a.tiles_per_clip, fr = tile - b * a.tiles_per_clip;
+    const IN *__restrict__ x = reinterpret_cast<const IN *>(a.pcm) + b * T + (fr * a.hop - a.pad);
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      const int n = tid + u * THREADS;
+      xs[u][0] = to_f(x[2 * n]);
+      xs[u][1] = to_f(x[2 * n + 1]);
+    }
+  };
+  auto interior = [&](int64_t tile) {
+    const int64_t b = tile / a.tiles_per_clip, fr = tile - b * a.tiles_per_clip;
+    const int64_t j0 = fr * a.hop - a.pad;
+    return j0 >= 0 && j0 + NFFT <= T;
+  };
+  bool have = blockIdx.x < n_tiles && interior(blockIdx.x);
+  if (have) load_interior(blockIdx.x, threadIdx.x);
+
+  for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    // the window pointer and the thread index are made opaque per frame so
+    // that per-thread addresses are not kept live across the whole loop
+    const float2 *win2 = reinterpret_cast<const float2 *>(a.window);
+    asm volatile("" : "+s"(win2));
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int64_t b = tile / a.tiles_per_clip;
+    const int64_t fr = tile - b * a.tiles_per_clip;   // one frame per tile
+    // 1. windowed samples z[n] = (w[2n] x[2n], w[2n+1] x[2n+1])
+    if (have) {
+      float2 ws[IPT];
+#pragma unroll
+      for (int u = 0; u < IPT; ++u) ws[u] = win2[tid + u * THREADS];
+#pragma unroll
+      for (int u = 0; u < IPT; ++u)
+        s_buf[lds_pos<kBigPad>(tid + u * THREADS)] = make_float2(xs[u][0] * ws[u].x, xs[u][1] * ws[u].y);
+    } else {
+      // frames that reach into the padding (the first and last few of a
+      // clip): each sample by index arithmetic, one point at a time
+      const IN *__restrict__ x = reinterpret_cast<const IN *>(a.pcm) + b * T;
+      const int64_t j0 = fr * a.hop - a.pad;
+      for (int n = tid; n < M; n += THREADS) {
+        const int64_t s0 = pad_source(j0 + 2 * n, T, a.pad_mode), s1 = pad_source(j0 + 2 * n + 1, T, a.pad_mode);
+        const float2 w = win2[n];
+        s_buf[lds_pos<kBigPad>(n)] = make_float2((s0 >= 0 ? to_f(x[s0]) : 0.0f) * w.x, (s1 >= 0 ? to_f(x[s1]) : 0.0f) * w.y);
+      }
+    }
+    __syncthreads();
+
+    // 2. M-point complex FFT: exp(-2 pi i j / M) = exp(-2 pi i 2j / N)
+    run_fft<M, 1, THREADS, kBigPad>(s_buf, [&](int j) { return wN(2 * j); }, typename BigCfg<NFFT>::Rad{}, tid);
+
+    // 3. split into the real spectrum; power over the same LDS
+    constexpr int NU = M / 2 + 1;
+    constexpr int UPT = (NU + THREADS - 1) / THREADS;
+    float pk[UPT], pmk[UPT];
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int k = tid + u * THREADS;
+      pk[u] = pmk[u] = 0.0f;
+      if (k < NU) {
+        const float2 zk = s_buf[lds_pos<kBigPad>(k)];
+        const float2 zc = cconj(s_buf[lds_pos<kBigPad>(k == 0 ? 0 : M - k)]);
+        const float2 Y = cadd(zk, zc), D = csub(zk, zc);
+        const float2 V = cmul(wN(k), D);
+        pk[u] = (Y.x + V.y) * (Y.x + V.y) + (Y.y - V.x) * (Y.y - V.x);
+        pmk[u] = (Y.x - V.y) * (Y.x - V.y) + (Y.y + V.x) * (Y.y + V.x);
+      }
+    }
+    __syncthreads();
+    float *P = reinterpret_cast<float *>(s_buf);
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int k = tid + u * THREADS;
+      if (k < NU) {
+        P[k] = pk[u];
+        if (k != M / 2) P[M - k] = pmk[u];
+      }
+    }
+    __syncthreads();
+    if (a.power != 2.0f) {
+      const float e = 0.5f * a.power;
+      for (int i = tid; i <= M; i += THREADS) P[i] = powf(P[i] * a.pre_scale, e);
+      __syncthreads();
+    }
+
+    // the next frame's samples, in flight during the mel sums
+    const int64_t nxt = tile + gridDim.x;
+    have = nxt < n_tiles && interior(nxt);
+    if (have) load_interior(nxt, tid);
+
+    // 4. mel: L lanes per band
+    float vmax = 0.0f, lmin = __builtin_huge_valf();
+    OUT *__restrict__ out = reinterpret_cast<OUT *>(a.out) + b * (int64_t)NM * F;
+    const int h = tid & (L - 1);
+    auto mel = [&](const float *wsrc) {
+      for (int m = tid / L; m < NM; m += THREADS / L) {
+        const int st = s_start[m], wd = s_width[m];
+        const float *pr = P + st;
+        const float *wr = wsrc + s_off[m];
+        float acc0 = 0.0f, acc1 = 0.0f;
+        int j = h;
+        for (; j + L < wd; j += 2 * L) {
+          acc0 = __builtin_fmaf(wr[j], pr[j], acc0);
+          acc1 = __builtin_fmaf(wr[j + L], pr[j + L], acc1);
+        }
+        if (j < wd) acc0 = __builtin_fmaf(wr[j], pr[j], acc0);
+        float acc = acc0 + acc1;
+        for (int o = L >> 1; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+        if (h == 0) {
+          const float v = fmaxf(acc * a.mel_scale, 1e-10f);
+          const float Lg = log10_pos(v);
+          vmax = fmaxf(vmax, v);
+          lmin = fminf(lmin, Lg);
+          store_out(out + (int64_t)m * F + fr, rescale(Lg));
+        }
+      }
+    };
+    if (w_in_lds) mel(s_w);
+    else mel(a.csr_w);
+
+    // 5. frame statistics; the barrier inside also keeps the next frame's
+    //    samples out of the power tile until every band has read it
+    block_maxmin<THREADS>(vmax, lmin, s_red);
+    if (tid == 0) {
+      a.tile_max[tile] = vmax;
+      a.tile_min[tile] = lmin;
+    }
+    __syncthreads();
+  }
+}
+
+template <int NFFT>
+static hipError_t launch_big(const PcmKernelArgs &k, bool i16, bool f16, int64_t n_tiles, int n_cu, hipStream_t s,
+                             const LaunchTiming *tm) {
+  constexpr int THREADS = BigCfg<NFFT>::THREADS;
+  const int64_t n_wg = n_tiles < n_cu ? n_tiles : n_cu;
+  const dim3 grid((unsigned)n_wg), block(THREADS);
+  if (!i16 && !f16) LM_LAUNCH(tm, (pcm_big_kernel<NFFT, float, float>), grid, block, 0, s, k, n_tiles);
+  else if (!i16 && f16) LM_LAUNCH(tm, (pcm_big_kernel<NFFT, float, __half>), grid, block, 0, s, k, n_tiles);
+  else if (i16 && !f16) LM_LAUNCH(tm, (pcm_big_kernel<NFFT, int16_t, float>), grid, block, 0, s, k, n_tiles);
+  else LM_LAUNCH(tm, (pcm_big_kernel<NFFT, int16_t, __half>), grid, block, 0, s, k, n_tiles);
+  return hipGetLastError();
 }
 
 template <int NFFT>
@@ -343,6 +534,7 @@ hipError_t launch_pcm(const lm_plan *p, const PcmArgs &a, hipStream_t s, const L
   k.window = p->dt.window;
   k.twiddle = p->dt.twiddle;
   k.untangle = p->dt.untangle;
+  k.tw2 = p->dt.tw2;
   k.csr_start = p->dt.csr_start;
   k.csr_width = p->dt.csr_width;
   k.csr_off = p->dt.csr_off;
@@ -362,8 +554,8 @@ hipError_t launch_pcm(const lm_plan *p, const PcmArgs &a, hipStream_t s, const L
     case 1024: return launch_n<1024>(k, a.in_i16, f16, n_tiles, s, tm);
     case 2048: return launch_n<2048>(k, a.in_i16, f16, n_tiles, s, tm);
     case 4096: return launch_n<4096>(k, a.in_i16, f16, n_tiles, s, tm);
-    case 8192: return launch_n<8192>(k, a.in_i16, f16, n_tiles, s, tm);
-    case 16384: return launch_n<16384>(k, a.in_i16, f16, n_tiles, s, tm);
+    case 8192: return launch_big<8192>(k, a.in_i16, f16, n_tiles, p->n_cu, s, tm);
+    case 16384: return launch_big<16384>(k, a.in_i16, f16, n_tiles, p->n_cu, s, tm);
     default: return hipErrorInvalidValue;
   }
 }

@@ -63,6 +63,19 @@ void build_twiddles(lm_plan *p) {
     p->untangle[2 * k] = (float)std::cos(a);
     p->untangle[2 * k + 1] = (float)-std::sin(a);
   }
+  // two-level table for the one-frame kernels (n_fft >= 8192):
+  // exp(-2 pi i j / N) = hi[j / 128] * lo[j % 128]
+  p->twid2.clear();
+  if (N >= 8192) {
+    const int nhi = N / 128;
+    p->twid2.resize(2 * (size_t)(nhi + 128));
+    for (int i = 0; i < nhi + 128; ++i) {
+      const long j = i < nhi ? 128L * i : (long)(i - nhi);
+      const double a = 2.0 * M_PI * (double)j / (double)N;
+      p->twid2[2 * i] = (float)std::cos(a);
+      p->twid2[2 * i + 1] = (float)-std::sin(a);
+    }
+  }
 }
 
 // Operand tables of the n_fft = 400 kernel's matrix-core stage (the

@@ -198,6 +198,41 @@ def test_pcm_every_size_ragged(n_fft):
     check(out, oracle_pcm(x, n_fft, hop, n_mels, sr), TOL32, f"n_fft {n_fft}")
 
 
+@pytest.mark.parametrize("n_fft,in_dtype,pad_mode,power,n_mels", [
+    (16384, "i16", "constant", 2.0, 256), (16384, "f32", "circular", 1.0, 8),
+    (8192, "i16", "replicate", 2.0, 3), (8192, "f32", "reflect", 3.0, 200)])
+def test_pcm_large_fft_paths(n_fft, in_dtype, pad_mode, power, n_mels):
+    """The persistent one-frame kernel: padded edge frames in every mode,
+    int16 input, general power, 1 to 64 lanes per band."""
+    hop = n_fft // 8
+    B, T = 2, 5 * n_fft + 77
+    sr = 44100.0
+    say("pcm large fft", n_fft, in_dtype, pad_mode, power, n_mels)
+    x = lm_synth.speech_pcm(B, T, sr, seed=n_fft + n_mels, as_int16=(in_dtype == "i16"))
+    out = run_pcm(x, n_fft, hop, n_mels, sr, pad_mode=pad_mode, power=power)
+    ref = oracle_pcm(x, n_fft, hop, n_mels, sr, pad_mode=pad_mode, power=power)
+    check(out, ref, TOL32, f"large fft {n_fft} {in_dtype} {pad_mode}")
+
+
+def test_pcm_large_fft_many_frames_and_global_weights():
+    """More frames than workgroups (each workgroup walks several), and a
+    filterbank too large for the kernel's LDS share (weights from memory)."""
+    n_fft, hop, sr = 8192, 2048, 16000.0
+    x = lm_synth.speech_pcm(1, 300 * hop, sr, seed=21, as_int16=True)
+    say("pcm large fft, 301 frames")
+    out = run_pcm(x, n_fft, hop, 64, sr)
+    check(out, oracle_pcm(x, n_fft, hop, 64, sr), TOL32, "8192 x 301 frames")
+    rng = np.random.default_rng(22)
+    W = rng.random((9, n_fft // 2 + 1)).astype(np.float32)   # dense rows: 36873 weights
+    W[4, :100] = 0.0
+    p = lm().Plan(n_fft, hop, 9).set_filters(W)
+    x2 = lm_synth.speech_pcm(2, 4 * n_fft, sr, seed=23)
+    say("pcm large fft, dense user filters")
+    out2 = p.from_pcm(to_dev(x2))
+    torch.cuda.synchronize()
+    check(out2, oracle.from_pcm(x2, n_fft, hop, W), TOL32, "dense user filters")
+
+
 @pytest.mark.parametrize("pad_mode", ["reflect", "constant", "replicate", "circular"])
 @pytest.mark.parametrize("center", [True, False])
 def test_pcm_pad_modes(pad_mode, center):
