@@ -120,6 +120,42 @@ int lm_plan_set_filters(lm_plan *plan, const float *host_dense, int n_mels, int 
  */
 int lm_plan_get_filters(const lm_plan *plan, float *host_dense, int n_mels, int n_bins);
 
+/* Output of a plan (lm_plan_set_output). */
+enum { LM_OUTPUT_LOGMEL = 0, LM_OUTPUT_MEL = 1 };
+/* Spectrum normalisation of the PCM path (lm_plan_set_output). */
+enum { LM_NORMALIZED_NONE = 0, LM_NORMALIZED_WINDOW = 1, LM_NORMALIZED_FRAME_LENGTH = 2 };
+
+/*
+ * lm_plan_set_output -- what the lm_from_* calls write (flashmel page,
+ * "Usage": a torchaudio-compatible MelSpectrogram, whose output is the mel
+ * power itself; KBench page, "spec_md": the log / clamp / rescale tail).
+ *
+ *  output      LM_OUTPUT_LOGMEL (the default): the normalised log-mel,
+ *              (max(L, hi_b - 8) + 4) / 4 with L = log10(max(mel, 1e-10)).
+ *              LM_OUTPUT_MEL: the mel values themselves, sum_k W[m,k] |X_k|^p,
+ *              with no floor, log, clamp or rescale (torchaudio's
+ *              MelSpectrogram); an LM_F16 plan rounds them to fp16, so
+ *              values beyond 65504 become infinite.
+ *  normalized  LM_NORMALIZED_NONE (the default); LM_NORMALIZED_WINDOW:
+ *              X divided by sqrt(sum_n w[n]^2) before |X|^p (torchaudio's
+ *              normalized=True / "window"); LM_NORMALIZED_FRAME_LENGTH: X
+ *              divided by sqrt(win_length) ("frame_length").  Applies to
+ *              lm_from_pcm only (lm_from_stft takes a finished spectrum).
+ * Host-only.  LM_ERR_INVALID_ARG for an unknown value.
+ */
+int lm_plan_set_output(lm_plan *plan, int output, int normalized);
+
+/*
+ * lm_plan_set_window -- window length of the PCM path (flashmel page,
+ * "Usage": torchaudio's win_length).  The periodic Hann window of
+ * win_length samples, 0.5 - 0.5 cos(2 pi n / win_length), is placed in the
+ * n_fft-point frame starting at (n_fft - win_length) / 2 (integer
+ * division) with zeros around it, as torch.stft pads a shorter window
+ * (win_length 1 gives the window [1], torch's convention).
+ * 1 <= win_length <= n_fft; the default is n_fft.  Host-only.
+ */
+int lm_plan_set_window(lm_plan *plan, int win_length);
+
 /*
  * lm_plan_num_frames -- frames produced for a clip of n_samples:
  * 1 + floor((n_samples + 2*pad - n_fft) / hop), pad = n_fft/2 if center
@@ -139,7 +175,8 @@ int64_t lm_plan_num_frames(const lm_plan *plan, int64_t n_samples);
  *            F = lm_plan_num_frames(plan, n_samples).  Mel-major: each
  *            band's F frames are contiguous.
  *  Each clip is floored at its own maximum: out = (max(L, hi_b - 8) + 4)/4
- *  with L = log10(max(mel, 1e-10)) and hi_b the clip's largest L.
+ *  with L = log10(max(mel, 1e-10)) and hi_b the clip's largest L (or the
+ *  mel values themselves under LM_OUTPUT_MEL, see lm_plan_set_output).
  *
  * Needs n_samples > n_fft/2 for reflect, >= n_fft/2 for circular and
  * >= n_fft for center=0.  n_clips == 0 is a no-op.  Returns
@@ -161,8 +198,9 @@ int lm_from_pcm(lm_plan *plan, const void *pcm, int in_dtype, int64_t n_clips, i
  *              their [first, last] non-zero range; exact for any input).
  *  out         device array (n_clips, n_frames, n_mels) of the plan's
  *              out_dtype.  Frame-major, as the contract fixes.
- *  power = re^2 + im^2 always (the plan's `power`, framing and padding do
- *  not apply to this path).  1 <= n_bins <= 8193, 1 <= n_mels <= 256.
+ *  power = re^2 + im^2 always (the plan's `power`, window, normalisation,
+ *  framing and padding do not apply to this path); the plan's output mode
+ *  does (LM_OUTPUT_MEL writes the mel values without the log tail).  1 <= n_bins <= 8193, 1 <= n_mels <= 256.
  *  n_clips == 0 or n_frames == 0 is a no-op.
  */
 int lm_from_stft(lm_plan *plan, const void *stft, const float *mel_filters, int64_t n_clips,

@@ -48,8 +48,12 @@ __all__ = [
     "mel_to_hz",
     "mel_filterbank",
     "log_mel_tail",
+    "frame_window",
+    "normalization_factor",
     "pcm_power_frames",
+    "mel_from_pcm",
     "from_pcm",
+    "mel_from_stft",
     "from_stft",
 ]
 
@@ -122,6 +126,37 @@ def hann_periodic(N: int) -> np.ndarray:
     """Periodic Hann window: 0.5 - 0.5 cos(2 pi n / N), n = 0..N-1."""
     n = np.arange(N, dtype=np.float64)
     return 0.5 - 0.5 * np.cos(2.0 * np.pi * n / N)
+
+
+def frame_window(n_fft: int, win_length: int | None = None) -> np.ndarray:
+    """The n_fft-point frame window: the periodic Hann of win_length samples
+    (default n_fft) with (n_fft - win_length) // 2 zeros before it and the
+    rest after it (flashmel page, "Usage": torchaudio's win_length, whose
+    shorter window torch.stft centres in the frame; a one-point window is
+    [1], torch's convention)."""
+    W = n_fft if win_length is None else int(win_length)
+    if not 1 <= W <= n_fft:
+        raise ValueError("need 1 <= win_length <= n_fft")
+    w = np.zeros(n_fft, dtype=np.float64)
+    left = (n_fft - W) // 2
+    # a one-point window is [1], as torch.hann_window gives it (the formula
+    # would give [0] and an all-zero spectrum)
+    w[left:left + W] = hann_periodic(W) if W > 1 else 1.0
+    return w
+
+
+def normalization_factor(window: np.ndarray, normalized, win_length: int) -> float:
+    """Factor applied to the complex spectrum before |X|^power (flashmel
+    page, "Usage": torchaudio's ``normalized``): 1 for none,
+    1 / sqrt(sum w^2) for True / "window", 1 / sqrt(win_length) for
+    "frame_length"."""
+    if normalized in (None, False, "none"):
+        return 1.0
+    if normalized in (True, "window"):
+        return 1.0 / math.sqrt(float(np.sum(window * window)))
+    if normalized == "frame_length":
+        return 1.0 / math.sqrt(float(win_length))
+    raise ValueError(normalized)
 
 
 def rdft_direct(y: np.ndarray, chunk: int | None = None) -> np.ndarray:
@@ -246,16 +281,23 @@ def log_mel_tail(mel: np.ndarray) -> np.ndarray:
 # ----------------------------------------------------------------------------
 
 def pcm_power_frames(x_clip: np.ndarray, n_fft: int, hop: int, center: bool = True,
-                     pad_mode: str = "reflect", power: float = 2.0) -> np.ndarray:
-    """One clip (T,) -> (F, n_fft//2 + 1) |X|^power of the windowed frames."""
+                     pad_mode: str = "reflect", power: float = 2.0, win_length: int | None = None,
+                     normalized=None) -> np.ndarray:
+    """One clip (T,) -> (F, n_fft//2 + 1) |c X|^power of the windowed frames,
+    c the normalisation factor (1 unless ``normalized``)."""
     xp = pad_signal(decode_pcm(x_clip), n_fft, center, pad_mode)
-    frames = frame_signal(xp, n_fft, hop) * hann_periodic(n_fft)[None, :]
-    return power_spectrum(rdft_direct(frames), power)
+    w = frame_window(n_fft, win_length)
+    frames = frame_signal(xp, n_fft, hop) * w[None, :]
+    c = normalization_factor(w, normalized, n_fft if win_length is None else win_length)
+    return power_spectrum(c * rdft_direct(frames), power)
 
 
-def from_pcm(x: np.ndarray, n_fft: int, hop: int, filters: np.ndarray, center: bool = True,
-             pad_mode: str = "reflect", power: float = 2.0) -> np.ndarray:
-    """PCM (B, T) float32 or int16 -> (B, n_mels, F) log-mel in float64.
+def mel_from_pcm(x: np.ndarray, n_fft: int, hop: int, filters: np.ndarray, center: bool = True,
+                 pad_mode: str = "reflect", power: float = 2.0, win_length: int | None = None,
+                 normalized=None) -> np.ndarray:
+    """PCM (B, T) float32 or int16 -> (B, n_mels, F) mel values in float64:
+    sum_k W[m, k] |c X_k|^power, the output of a torchaudio-style
+    MelSpectrogram (flashmel page, "Usage").
 
     ``filters`` is the (n_mels, n_fft//2 + 1) filterbank (float64 or the
     float32 weights actually used); the mel sum is dense over all bins.
@@ -266,15 +308,23 @@ def from_pcm(x: np.ndarray, n_fft: int, hop: int, filters: np.ndarray, center: b
     W = np.asarray(filters, dtype=np.float64)
     outs = []
     for b in range(x.shape[0]):
-        P = pcm_power_frames(x[b], n_fft, hop, center, pad_mode, power)
+        P = pcm_power_frames(x[b], n_fft, hop, center, pad_mode, power, win_length, normalized)
         mel = P @ W.T                       # (F, n_mels)
         outs.append(mel.T[None])            # (1, n_mels, F)
-    mel_all = np.concatenate(outs, axis=0)
-    return log_mel_tail(mel_all)
+    return np.concatenate(outs, axis=0)
 
 
-def from_stft(stft: np.ndarray, mel_filters: np.ndarray) -> np.ndarray:
-    """Complex STFT (B, F, NF) -> (B, F, NM) log-mel in float64."""
+def from_pcm(x: np.ndarray, n_fft: int, hop: int, filters: np.ndarray, center: bool = True,
+             pad_mode: str = "reflect", power: float = 2.0, win_length: int | None = None,
+             normalized=None) -> np.ndarray:
+    """PCM (B, T) float32 or int16 -> (B, n_mels, F) log-mel in float64: the
+    mel values of ``mel_from_pcm`` through the per-clip log tail."""
+    return log_mel_tail(mel_from_pcm(x, n_fft, hop, filters, center, pad_mode, power, win_length, normalized))
+
+
+def mel_from_stft(stft: np.ndarray, mel_filters: np.ndarray) -> np.ndarray:
+    """Complex STFT (B, F, NF) -> (B, F, NM) mel values in float64:
+    (re^2 + im^2) @ W^T (task page, "reference_src", before the log)."""
     s = np.asarray(stft)
     if s.ndim == 2:
         s = s[None]
@@ -285,4 +335,9 @@ def from_stft(stft: np.ndarray, mel_filters: np.ndarray) -> np.ndarray:
         im = s[b].imag.astype(np.float64)
         mag = re * re + im * im
         out[b] = (mag @ W.T)
-    return log_mel_tail(out)
+    return out
+
+
+def from_stft(stft: np.ndarray, mel_filters: np.ndarray) -> np.ndarray:
+    """Complex STFT (B, F, NF) -> (B, F, NM) log-mel in float64."""
+    return log_mel_tail(mel_from_stft(stft, mel_filters))

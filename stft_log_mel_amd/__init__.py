@@ -41,6 +41,8 @@ _PAD = {"constant": 0, "reflect": 1, "replicate": 2, "circular": 3}
 _DT = {"f32": 0, "f16": 1, "i16": 2}
 _SCALE = {"slaney": 0, "htk": 1}
 _NORM = {"slaney": 0, None: 1, "none": 1}
+_OUTPUT = {"logmel": 0, "mel": 1}
+_NORMALIZED = {None: 0, False: 0, "none": 0, True: 1, "window": 1, "frame_length": 2}
 
 # Exported symbols and their C signatures (include/lm.h).
 _c_int, _c_i64, _c_p, _c_f, _c_d = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_double
@@ -49,6 +51,8 @@ SIGNATURES = {
     "lm_plan_set_mel": (_c_int, [_c_p, _c_d, _c_d, _c_d, _c_int, _c_int]),
     "lm_plan_set_filters": (_c_int, [_c_p, _c_p, _c_int, _c_int]),
     "lm_plan_get_filters": (_c_int, [_c_p, _c_p, _c_int, _c_int]),
+    "lm_plan_set_output": (_c_int, [_c_p, _c_int, _c_int]),
+    "lm_plan_set_window": (_c_int, [_c_p, _c_int]),
     "lm_plan_num_frames": (_c_i64, [_c_p, _c_i64]),
     "lm_from_pcm": (_c_int, [_c_p, _c_p, _c_int, _c_i64, _c_i64, _c_p, _c_p]),
     "lm_from_stft": (_c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_int, _c_p, _c_p]),
@@ -120,6 +124,7 @@ class Plan:
         self.n_fft, self.hop, self.n_mels = int(n_fft), int(hop), int(n_mels)
         self.center, self.pad_mode, self.power, self.out_dtype = bool(center), pad_mode, float(power), out_dtype
         self.n_bins = self.n_fft // 2 + 1
+        self.output = "logmel"
         self.lock = threading.Lock()
 
     # -- host-side configuration ------------------------------------------
@@ -138,6 +143,20 @@ class Plan:
         if a.ndim != 2:
             raise ValueError("filters must be 2-D (n_mels, n_fft//2 + 1)")
         _check(_lib.lm_plan_set_filters(self._h, a.ctypes.data, a.shape[0], a.shape[1]))
+        return self
+
+    def set_output(self, output: str = "logmel", normalized=None) -> "Plan":
+        """output: "logmel" (normalised log-mel) or "mel" (mel values, no log
+        tail); normalized: None/False, True/"window" or "frame_length"."""
+        if output not in _OUTPUT or normalized not in _NORMALIZED:
+            raise ValueError("output must be 'logmel'|'mel'; normalized None|True|'window'|'frame_length'")
+        _check(_lib.lm_plan_set_output(self._h, _OUTPUT[output], _NORMALIZED[normalized]))
+        self.output = output
+        return self
+
+    def set_window(self, win_length: int) -> "Plan":
+        """Window of win_length samples, centred in the n_fft-point frame."""
+        _check(_lib.lm_plan_set_window(self._h, int(win_length)))
         return self
 
     def get_filters(self) -> np.ndarray:
@@ -230,27 +249,25 @@ class Plan:
 
 
 class MelSpectrogram:
-    """torchaudio-style log-mel transform (flashmel page, "Usage").
+    """torchaudio-style mel transform (flashmel page, "Usage").
 
-    Accepts the torchaudio ``MelSpectrogram`` arguments; those the library
-    does not build yet (``win_length != n_fft``, ``pad != 0``,
-    ``normalized``, ``onesided=False``) raise ``NotImplementedError``.
-    Output: ``(..., n_mels, n_frames)`` normalised log-mel (float32 or
-    float16 per ``dtype``).  Inference only.
+    Accepts the torchaudio ``MelSpectrogram`` arguments (``pad != 0`` and
+    ``onesided=False`` excepted).  ``output="logmel"`` (the default) gives
+    the normalised log-mel; ``output="mel"`` the mel values themselves, as
+    torchaudio does.  Output: ``(..., n_mels, n_frames)`` in float32 or
+    float16 per ``dtype``.  Inference only.
     """
 
     def __init__(self, sample_rate: float = 16000, n_fft: int = 400, win_length: int | None = None,
                  hop_length: int | None = None, f_min: float = 0.0, f_max: float | None = None, pad: int = 0,
-                 n_mels: int = 128, power: float = 2.0, normalized: bool = False, center: bool = True,
+                 n_mels: int = 128, power: float = 2.0, normalized=False, center: bool = True,
                  pad_mode: str = "reflect", onesided: bool = True, norm: str | None = "slaney",
-                 mel_scale: str = "slaney", dtype=None):
+                 mel_scale: str = "slaney", dtype=None, output: str = "logmel"):
         torch = _torch()
-        if win_length is not None and win_length != n_fft:
-            raise NotImplementedError("win_length != n_fft")
         if pad:
             raise NotImplementedError("pad != 0")
-        if normalized:
-            raise NotImplementedError("normalized STFT")
+        if normalized not in _NORMALIZED or output not in _OUTPUT:
+            raise ValueError("normalized must be False|True|'window'|'frame_length'; output 'logmel'|'mel'")
         if not onesided:
             raise ValueError("only onesided=True (the mel projection needs a one-sided spectrum)")
         dtype = torch.float32 if dtype is None else dtype
@@ -258,7 +275,9 @@ class MelSpectrogram:
             raise ValueError("dtype must be torch.float32 or torch.float16")
         self.sample_rate = float(sample_rate)
         self.n_fft = int(n_fft)
-        self.hop_length = int(hop_length) if hop_length is not None else self.n_fft // 2
+        self.win_length = int(win_length) if win_length is not None else self.n_fft
+        self.hop_length = int(hop_length) if hop_length is not None else self.win_length // 2
+        self.normalized, self.output = normalized, output
         self.f_min, self.f_max = float(f_min), (float(f_max) if f_max is not None else self.sample_rate / 2)
         self.n_mels, self.power, self.center, self.pad_mode = int(n_mels), float(power), bool(center), pad_mode
         self.norm, self.mel_scale, self.dtype = norm, mel_scale, dtype
@@ -272,6 +291,8 @@ class MelSpectrogram:
             p = Plan(self.n_fft, self.hop_length, self.n_mels, self.center, self.pad_mode, self.power,
                      "f16" if self.dtype == _torch().float16 else "f32")
             p.set_mel(self.sample_rate, self.f_min, self.f_max, self.mel_scale, self.norm)
+            p.set_window(self.win_length)
+            p.set_output(self.output, self.normalized)
             self._plans[device_index] = p
         return p
 

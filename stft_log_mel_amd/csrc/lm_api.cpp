@@ -180,6 +180,7 @@ int lm_from_pcm(lm_plan *p, const void *pcm, int in_dtype, int64_t n_clips, int6
   PcmArgs a{pcm, in_dtype == LM_I16, n_clips, n_samples, F, (int)tiles, out, tmin, tmax};
   rc = timed_launch(p, s, 0, "launch(pcm kernel)", [&](const LaunchTiming *tm) { return launch_pcm(p, a, s, tm); });
   if (rc != LM_OK) return rc;
+  if (p->output == LM_OUTPUT_MEL) return LM_OK;   // no per-clip tail
   FixupArgs fx{out, p->out_dtype == LM_F16, tmin, tmax, n_clips, F, p->n_mels, (int)tiles, st, 1};
   return timed_launch(p, s, 1, "launch(clamp fix-up)", [&](const LaunchTiming *tm) { return launch_fixup(fx, s, tm); });
 }
@@ -213,7 +214,8 @@ int lm_from_stft(lm_plan *p, const void *stft, const float *mel_filters, int64_t
   float *tmin = p->d_stats, *tmax = p->d_stats + n_clips * tiles;
 
   StftArgs a{reinterpret_cast<const float2 *>(stft), n_clips, n_frames, (int)n_bins, n_mels, tf, (int)tiles,
-             nullptr, nullptr, nullptr, nullptr, 0, out, p->out_dtype == LM_F16, tmin, tmax, p->n_cu};
+             nullptr, nullptr, nullptr, nullptr, 0, out, p->out_dtype == LM_F16, tmin, tmax, p->n_cu,
+             p->output == LM_OUTPUT_MEL};
   if (mel_filters) {
     const size_t need = sizeof(int32_t) * 2 * n_mels;
     if (need > p->pack_cap) {
@@ -243,6 +245,7 @@ int lm_from_stft(lm_plan *p, const void *stft, const float *mel_filters, int64_t
   }
   rc = timed_launch(p, s, 0, "launch(stft kernel)", [&](const LaunchTiming *tm) { return launch_stft(a, s, tm); });
   if (rc != LM_OK) return rc;
+  if (p->output == LM_OUTPUT_MEL) return LM_OK;   // no per-clip tail
   StatLayout st;
   st.frames_per_tile = tf;
   st.band_h = n_mels;

@@ -79,6 +79,9 @@ struct lm_plan {
   int n_fft = 0, hop = 0, n_mels = 0, center = 0, pad_mode = 0, out_dtype = 0;
   float power = 2.0f;
   int n_bins = 0;  // n_fft / 2 + 1
+  int win_length = 0;                   // periodic Hann length, centred in the frame (default n_fft)
+  int output = LM_OUTPUT_LOGMEL;        // LM_OUTPUT_*
+  int normalized = LM_NORMALIZED_NONE;  // LM_NORMALIZED_*
 
   bool have_filters = false;
   lm::Csr csr;
@@ -117,6 +120,8 @@ int ensure_workspace(lm_plan *p, int64_t n_floats);
 int upload_tables(lm_plan *p);
 
 // Host table builders (lm_plan.cpp)
+double window_at(const lm_plan *p, int n);   // the frame window at n (float64)
+double power_scale2(const lm_plan *p);       // factor on |X|^2 from the plan's normalisation
 void build_window(lm_plan *p);
 void build_twiddles(lm_plan *p);
 void build_mfma400(lm_plan *p);
@@ -172,6 +177,7 @@ struct StftArgs {
   float *tile_min;
   float *tile_max;
   int n_cu;
+  int mel_out;   // 1: mel values without the log tail
 };
 int stft_frames_per_tile(int n_bins, int n_mels);
 hipError_t launch_stft(const StftArgs &a, hipStream_t s, const LaunchTiming *tm);

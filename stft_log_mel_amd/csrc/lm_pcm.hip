@@ -127,6 +127,7 @@ struct PcmKernelArgs {
   float power;          // exponent p; 2 takes the fast path
   float mel_scale;      // exact power-of-two scale of the mel sums
   float pre_scale;      // scale of |2X|^2 before a general power
+  int mel_out;          // 1: store the mel values themselves (no log tail)
   int n_mels;
   const float *window;
   const float2 *twiddle, *untangle;
@@ -252,6 +253,10 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
       float acc = 0.0f;
       const float *wr = wsrc + s_off[m];
       for (int j = 0; j < wd; ++j) acc = __builtin_fmaf(wr[j], pr[j], acc);
+      if (a.mel_out) {
+        store_out(out + (int64_t)m * F + fr, acc * a.mel_scale);
+        continue;
+      }
       const float v = fmaxf(acc * a.mel_scale, 1e-10f);
       const float L = log10_pos(v);
       vmax = fmaxf(vmax, v);
@@ -436,7 +441,9 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS) pcm_big_kernel(PcmKerne
         if (j < wd) acc0 = __builtin_fmaf(wr[j], pr[j], acc0);
         float acc = acc0 + acc1;
         for (int o = L >> 1; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-        if (h == 0) {
+        if (h == 0 && a.mel_out) {
+          store_out(out + (int64_t)m * F + fr, acc * a.mel_scale);
+        } else if (h == 0) {
           const float v = fmaxf(acc * a.mel_scale, 1e-10f);
           const float Lg = log10_pos(v);
           vmax = fmaxf(vmax, v);
@@ -522,14 +529,16 @@ hipError_t launch_pcm(const lm_plan *p, const PcmArgs &a, hipStream_t s, const L
   k.pad_mode = p->pad_mode;
   k.power = p->power;
   // |2X|^2 = 4 |X|^2; int16 samples carry a 2^15 factor per |X|
-  const float in_scale2 = a.in_i16 ? 1.0f / 1073741824.0f : 1.0f;   // 2^-30
+  // (the normalisation's factor on |X|^2 joins them)
+  const double in_scale2 = (a.in_i16 ? 1.0 / 1073741824.0 : 1.0) * power_scale2(p);   // 2^-30
   if (p->power == 2.0f) {
-    k.mel_scale = 0.25f * in_scale2;
+    k.mel_scale = (float)(0.25 * in_scale2);
     k.pre_scale = 1.0f;
   } else {
     k.mel_scale = 1.0f;
-    k.pre_scale = 0.25f * in_scale2;
+    k.pre_scale = (float)(0.25 * in_scale2);
   }
+  k.mel_out = p->output == LM_OUTPUT_MEL;
   k.n_mels = p->n_mels;
   k.window = p->dt.window;
   k.twiddle = p->dt.twiddle;

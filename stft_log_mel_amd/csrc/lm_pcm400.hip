@@ -190,6 +190,7 @@ struct Args {
   int n_mels, n_melblk;
   int melw_n;            // mel step weight count (at most kMelWLds)
   int mel_batches;       // batches of kMelBatch steps over all band blocks
+  int mel_out;           // 1: store the mel values themselves (no log tail)
   float *tile_max;
 };
 
@@ -620,7 +621,12 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
       if (!endR[S]) return;
       // block cb complete: log10, rescale, store, statistics
       uint32_t vminb = 0x7f800000u;   // +inf: no value
-      if (sub_full && 16 * cb + 16 <= NM) {   // uniform: every lane's band and frames exist
+      if (a.mel_out) {   // uniform: mel values as they are, no statistics
+        const bool band_ok = 16 * cb + 4 * g + (c & 3) < NM;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (band_ok && f0 + i < F) store_out(orow + i, acc0[i] + acc1[i]);
+      } else if (sub_full && 16 * cb + 16 <= NM) {   // uniform: every lane's band and frames exist
         float o[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -726,14 +732,16 @@ hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &pa, hipStream_t s, con
   k.power = p->power;
   // every power value is 4 |X|^2; int16 samples carry 2^15 per |X|, and
   // their fp16 matrix another 2^12 / 64 = 2^6
-  const float in_scale2 = pa.in_i16 ? 1.0f / 4398046511104.0f : 1.0f;   // 2^-42
+  // (the normalisation's factor on |X|^2 joins them)
+  const double in_scale2 = (pa.in_i16 ? 1.0 / 4398046511104.0 : 1.0) * power_scale2(p);   // 2^-42
   if (p->power == 2.0f) {
-    k.mel_scale = 0.25f * in_scale2;
+    k.mel_scale = (float)(0.25 * in_scale2);
     k.pre_scale = 1.0f;
   } else {
     k.mel_scale = 1.0f;
-    k.pre_scale = 0.25f * in_scale2;
+    k.pre_scale = (float)(0.25 * in_scale2);
   }
+  k.mel_out = p->output == LM_OUTPUT_MEL;
   k.n_mels = p->n_mels;
   k.n_melblk = p->dt.n_melblk;
   k.melw_n = (int)p->melblk_w.size();

@@ -38,13 +38,32 @@ static bool is_supported_nfft(int n) {
   return (n & (n - 1)) == 0;
 }
 
-// Periodic Hann: 0.5 - 0.5 cos(2 pi n / N), n = 0..N-1 (flashmel page,
-// "Usage": the window is always the periodic Hann).
+// Periodic Hann of win_length samples, 0.5 - 0.5 cos(2 pi i / win_length)
+// (flashmel page, "Usage": the window is always the periodic Hann), placed
+// at offset (n_fft - win_length) / 2 of the frame with zeros around it.
+double window_at(const lm_plan *p, int n) {
+  const int W = p->win_length, i = n - (p->n_fft - W) / 2;
+  if (i < 0 || i >= W) return 0.0;
+  if (W == 1) return 1.0;   // a one-point window is [1] (torch.hann_window's convention)
+  return 0.5 - 0.5 * std::cos(2.0 * M_PI * (double)i / (double)W);
+}
+
+// Factor on |X|^2 from the normalisation: 1, 1 / sum_n w[n]^2 (window) or
+// 1 / win_length (frame length).
+double power_scale2(const lm_plan *p) {
+  if (p->normalized == LM_NORMALIZED_WINDOW) {
+    double s = 0.0;
+    for (int n = 0; n < p->n_fft; ++n) s += window_at(p, n) * window_at(p, n);
+    return 1.0 / s;
+  }
+  if (p->normalized == LM_NORMALIZED_FRAME_LENGTH) return 1.0 / (double)p->win_length;
+  return 1.0;
+}
+
 void build_window(lm_plan *p) {
   const int N = p->n_fft;
   p->window.resize(N);
-  for (int n = 0; n < N; ++n)
-    p->window[n] = (float)(0.5 - 0.5 * std::cos(2.0 * M_PI * (double)n / (double)N));
+  for (int n = 0; n < N; ++n) p->window[n] = (float)window_at(p, n);
 }
 
 // exp(-2 pi i j / M) for the M-point complex FFT, and exp(-2 pi i k / N)
@@ -92,7 +111,7 @@ void build_mfma400(lm_plan *p) {
   // for n1 >= 25.
   static const int kA[4] = {1, 2, 3, 4}, kB[3] = {7, 6, 5};
   std::vector<double> win(400);
-  for (int n = 0; n < 400; ++n) win[n] = 0.5 - 0.5 * std::cos(2.0 * M_PI * (double)n / 400.0);
+  for (int n = 0; n < 400; ++n) win[n] = window_at(p, n);
   auto entry = [&](int n1, int m, int n2) {
     const int n = n1 + 25 * n2;
     const int g = m / 4, sub = m % 4;
@@ -266,12 +285,36 @@ int lm_plan_create(lm_plan **plan, int n_fft, int hop, int n_mels, int center, i
   p->power = power;
   p->out_dtype = out_dtype;
   p->n_bins = n_fft / 2 + 1;
+  p->win_length = n_fft;
   const char *fg = std::getenv("LM_FORCE_GENERIC");
   p->force_generic = fg && fg[0] == '1';
   build_window(p);
   build_twiddles(p);
   if (n_fft == 400) build_mfma400(p);
   *plan = p;
+  return LM_OK;
+}
+
+int lm_plan_set_output(lm_plan *p, int output, int normalized) {
+  g_last_error.clear();
+  if (!p) return fail(LM_ERR_INVALID_ARG, "plan is NULL");
+  if (output != LM_OUTPUT_LOGMEL && output != LM_OUTPUT_MEL) return fail(LM_ERR_INVALID_ARG, "unknown output");
+  if (normalized < LM_NORMALIZED_NONE || normalized > LM_NORMALIZED_FRAME_LENGTH)
+    return fail(LM_ERR_INVALID_ARG, "unknown normalized mode");
+  p->output = output;
+  p->normalized = normalized;
+  return LM_OK;
+}
+
+int lm_plan_set_window(lm_plan *p, int win_length) {
+  g_last_error.clear();
+  if (!p) return fail(LM_ERR_INVALID_ARG, "plan is NULL");
+  if (win_length < 1 || win_length > p->n_fft) return fail(LM_ERR_INVALID_ARG, "need 1 <= win_length <= n_fft");
+  if (win_length == p->win_length) return LM_OK;
+  p->win_length = win_length;
+  build_window(p);
+  if (p->n_fft == 400) build_mfma400(p);
+  p->tables_dirty = true;
   return LM_OK;
 }
 

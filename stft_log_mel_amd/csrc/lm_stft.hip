@@ -33,6 +33,7 @@ struct StftKernelArgs {
   const float *f_w;
   int f_stride;
   void *out;
+  int mel_out;   // 1: store the mel values themselves (no log tail)
   float *tile_min, *tile_max;
 };
 
@@ -95,11 +96,15 @@ __device__ __forceinline__ void stft_tile(const StftKernelArgs &a, int64_t tile,
     const float *wr = wsrc + s_off[m];
     float acc = 0.0f;
     for (int j = 0; j < wd; ++j) acc = __builtin_fmaf(wr[j], pr[j], acc);
-    const float v = fmaxf(acc, 1e-10f);
-    const float L = log10_pos(v);
-    vmax = fmaxf(vmax, v);
-    lmin = fminf(lmin, L);
-    store_out_nt(out + o, rescale(L));
+    if (a.mel_out) {
+      store_out_nt(out + o, acc);
+    } else {
+      const float v = fmaxf(acc, 1e-10f);
+      const float L = log10_pos(v);
+      vmax = fmaxf(vmax, v);
+      lmin = fminf(lmin, L);
+      store_out_nt(out + o, rescale(L));
+    }
     m += dm;
     f += df;
     if (m >= NM) {
@@ -197,6 +202,7 @@ hipError_t launch_stft(const StftArgs &a, hipStream_t s, const LaunchTiming *tm)
   k.f_w = a.f_w;
   k.f_stride = a.f_stride;
   k.out = a.out;
+  k.mel_out = a.mel_out;
   k.tile_min = a.tile_min;
   k.tile_max = a.tile_max;
   const size_t lds = sizeof(float) * ((size_t)a.frames_per_tile * a.n_bins + kStftWLds);

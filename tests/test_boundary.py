@@ -192,11 +192,13 @@ def test_from_stft_validation_before_any_hip_call():
 
 def test_python_wrapper_rejects_unbuilt_options():
     with pytest.raises(NotImplementedError):
-        lm.MelSpectrogram(n_fft=400, win_length=300)
-    with pytest.raises(NotImplementedError):
         lm.MelSpectrogram(pad=4)
-    with pytest.raises(NotImplementedError):
-        lm.MelSpectrogram(normalized=True)
+    with pytest.raises(ValueError):
+        lm.MelSpectrogram(normalized="l2")
+    with pytest.raises(ValueError):
+        lm.MelSpectrogram(output="db")
+    with pytest.raises(ValueError):
+        lm.MelSpectrogram(n_fft=400, win_length=401)
     with pytest.raises(ValueError):
         lm.MelSpectrogram(onesided=False)
     with pytest.raises(ValueError):
@@ -214,3 +216,21 @@ def test_binding_has_no_cpu_fallback():
     src = open(os.path.join(ROOT, "stft_log_mel_amd", "__init__.py")).read()
     for word in ["fft", "log10", "hann", "oracle", "einsum", "matmul"]:
         assert word not in src.lower().replace("n_fft", "").replace("rfft", ""), word
+
+
+def test_set_output_and_window_validation():
+    rc, h = _create()
+    assert rc == OK
+    assert _lib.lm_plan_set_output(h, 1, 2) == OK
+    assert _lib.lm_plan_set_output(h, 2, 0) == INVALID
+    assert _lib.lm_plan_set_output(h, 0, 3) == INVALID
+    assert _lib.lm_plan_set_output(h, -1, 0) == INVALID
+    assert _lib.lm_plan_set_window(h, 1) == OK
+    assert _lib.lm_plan_set_window(h, 400) == OK
+    assert _lib.lm_plan_set_window(h, 0) == INVALID
+    assert _lib.lm_plan_set_window(h, 401) == INVALID
+    assert _lib.lm_plan_set_output(None, 0, 0) == INVALID
+    assert _lib.lm_plan_set_window(None, 10) == INVALID
+    _lib.lm_plan_destroy(h)
+    m = lm.MelSpectrogram(sample_rate=16000, n_fft=512, win_length=400, normalized=True, output="mel")
+    assert m.hop_length == 200            # torchaudio's default: win_length // 2

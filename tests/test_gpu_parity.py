@@ -233,6 +233,84 @@ def test_pcm_large_fft_many_frames_and_global_weights():
     check(out2, oracle.from_pcm(x2, n_fft, hop, W), TOL32, "dense user filters")
 
 
+def check_mel(got, ref, rtol, what):
+    """Mel values (no log tail): |got - ref| <= rtol |ref| + 1e-6 max|ref|
+    per clip.  rtol is flashmel's stated agreement with torchaudio (1e-4;
+    1e-3 for fp16 outputs, twice their half-ulp); the absolute part is fp32
+    rounding of the transform, which scales with the clip's energy and
+    dominates only for bands 60 dB or more below the clip's peak."""
+    got = got.detach().float().cpu().numpy().astype(np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.isfinite(got).all(), what
+    peak = np.abs(ref).reshape(ref.shape[0], -1).max(axis=1).reshape((-1,) + (1,) * (ref.ndim - 1))
+    bound = rtol * np.abs(ref) + 1e-6 * peak
+    ratio = np.abs(got - ref) / bound
+    i = np.unravel_index(np.argmax(ratio), ratio.shape)
+    assert ratio.max() <= 1.0, f"{what}: |err| {abs(got[i] - ref[i]):.3e} > bound {bound[i]:.3e} at {i}"
+
+
+@pytest.mark.parametrize("n_fft,hop,in_dtype,out_dtype", [
+    (400, 160, "i16", "f32"), (400, 160, "f32", "f32"), (400, 100, "f32", "f16"), (512, 128, "i16", "f32"),
+    (16384, 4096, "f32", "f16")])
+def test_pcm_mel_output(n_fft, hop, in_dtype, out_dtype):
+    """Mel values without the log tail (torchaudio-style output), on the
+    matrix-core n_fft = 400 kernel, the generic kernel and the one-frame
+    kernel."""
+    sr = 16000.0
+    B, T = 3, max(12000, 4 * n_fft + 33)
+    say("pcm mel output", n_fft, hop, in_dtype, out_dtype)
+    x = lm_synth.speech_pcm(B, T, sr, seed=31 + n_fft, as_int16=(in_dtype == "i16"))
+    p = lm().Plan(n_fft, hop, 64, out_dtype=out_dtype).set_mel(sr).set_output("mel")
+    out = p.from_pcm(to_dev(x))
+    torch.cuda.synchronize()
+    ref = oracle.mel_from_pcm(x, n_fft, hop, oracle.mel_filterbank(sr, n_fft, 64))
+    check_mel(out, ref, 1e-3 if out_dtype == "f16" else 1e-4, f"mel {n_fft} {in_dtype} {out_dtype}")
+
+
+def test_stft_mel_output():
+    B, F, NF, NM = 3, 97, 201, 80
+    say("stft mel output", B, F, NF, NM)
+    s = lm_synth.stft_speechlike(B, F, NF, seed=41)
+    W = lm_synth.lintri_filters(NF, NM)
+    p = lm().Plan(400, 160, NM).set_output("mel")
+    out = p.from_stft(to_dev(s), to_dev(W))
+    torch.cuda.synchronize()
+    check_mel(out, oracle.mel_from_stft(s, W), 1e-4, "stft mel")
+
+
+@pytest.mark.parametrize("n_fft,hop,win_length,normalized,in_dtype,power", [
+    (400, 160, 300, "window", "i16", 2.0), (400, 160, 320, "frame_length", "f32", 2.0),
+    (400, 100, 399, None, "f32", 1.0), (512, 128, 257, "window", "f32", 2.0), (2048, 512, 1500, True, "i16", 2.0)])
+def test_pcm_window_length_and_normalized(n_fft, hop, win_length, normalized, in_dtype, power):
+    """Shorter centred windows and spectrum normalisation (torchaudio's
+    win_length and normalized), on the log-mel output."""
+    sr = 16000.0
+    B, T = 2, max(9000, 3 * n_fft + 5)
+    say("pcm window", n_fft, hop, win_length, normalized, in_dtype, power)
+    x = lm_synth.speech_pcm(B, T, sr, seed=50 + win_length, as_int16=(in_dtype == "i16"))
+    p = lm().Plan(n_fft, hop, 80, power=power).set_mel(sr).set_window(win_length).set_output("logmel", normalized)
+    out = p.from_pcm(to_dev(x))
+    torch.cuda.synchronize()
+    ref = oracle.from_pcm(x, n_fft, hop, oracle.mel_filterbank(sr, n_fft, 80), power=power,
+                          win_length=win_length, normalized=normalized)
+    check(out, ref, TOL32, f"window {n_fft}/{win_length} {normalized}")
+
+
+def test_melspectrogram_wrapper_torchaudio_surface():
+    """MelSpectrogram(output="mel", win_length, normalized) through the wrapper."""
+    sr = 16000.0
+    m = lm().MelSpectrogram(sample_rate=sr, n_fft=512, win_length=400, hop_length=160, n_mels=64,
+                            normalized=True, output="mel")
+    x = lm_synth.speech_pcm(4, 16000, sr, seed=61).reshape(2, 2, 16000)
+    say("MelSpectrogram torchaudio surface")
+    y = m(to_dev(x))
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (2, 2, 64, 101)
+    ref = oracle.mel_from_pcm(x.reshape(4, 16000), 512, 160, oracle.mel_filterbank(sr, 512, 64),
+                              win_length=400, normalized="window")
+    check_mel(y.reshape(4, 64, 101), ref, 1e-4, "wrapper mel")
+
+
 @pytest.mark.parametrize("pad_mode", ["reflect", "constant", "replicate", "circular"])
 @pytest.mark.parametrize("center", [True, False])
 def test_pcm_pad_modes(pad_mode, center):

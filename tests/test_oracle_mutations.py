@@ -129,6 +129,22 @@ def _power_magnitude(X, power=2.0):
     return np.abs(X)
 
 
+def _window_off_by_one(n_fft, win_length=None):
+    W = n_fft if win_length is None else int(win_length)
+    w = np.zeros(n_fft, dtype=np.float64)
+    left = (n_fft - W + 1) // 2            # rounds the offset up instead of down
+    w[left:left + W] = L.hann_periodic(W) if W > 1 else 1.0
+    return w
+
+
+def _normalized_by_sum(window, normalized, win_length):
+    if normalized in (None, False, "none"):
+        return 1.0
+    if normalized in (True, "window"):
+        return 1.0 / float(np.sum(window))     # sum of w, not sqrt of sum of w^2
+    return 1.0 / float(win_length) ** 0.5
+
+
 MUTATIONS = [
     ("log_mel_tail", _tail_per_batch, [pins.test_worked_example_fixture]),
     ("log_mel_tail", _tail_per_frame, [pins.test_worked_example_fixture]),
@@ -153,6 +169,8 @@ MUTATIONS = [
     ("hz_to_mel", _mel_scale_wrong_break, [pins.test_slaney_scale_closed_forms]),
     ("power_spectrum", _power_magnitude, [pins.test_power_general_exponent,
                                           lambda: pins.test_parseval(16)]),
+    ("frame_window", _window_off_by_one, [lambda: pins.test_short_window_matches_torch_stft(512, 257, 128)]),
+    ("normalization_factor", _normalized_by_sum, [lambda: pins.test_normalized_window_closed_form(300)]),
 ]
 
 

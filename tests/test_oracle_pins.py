@@ -348,3 +348,66 @@ def test_brute_force_tiny_stft():
         for f in range(F):
             for n in range(NM):
                 assert abs(got[b, f, n] - (max(logs[f][n], hi - 8) + 4) / 4) < 1e-12
+
+
+# ----------------------------------------------------------------------------
+# torchaudio-style surface: window length, normalisation, mel output
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n_fft,win_length,hop", [(400, 300, 160), (512, 257, 128), (64, 64, 16), (16, 1, 4)])
+def test_short_window_matches_torch_stft(n_fft, win_length, hop):
+    """A window shorter than the frame is centred as torch.stft centres it
+    (an independent library routine, fp64, reflect padding)."""
+    rng = np.random.default_rng(n_fft + win_length)
+    x = rng.standard_normal((2, 9 * n_fft + 7))
+    P = np.stack([oracle.pcm_power_frames(x[b], n_fft, hop, True, "reflect", 2.0, win_length) for b in range(2)])
+    S = torch.stft(torch.from_numpy(x), n_fft, hop, win_length,
+                   torch.hann_window(win_length, periodic=True, dtype=torch.float64),
+                   center=True, pad_mode="reflect", return_complex=True)
+    ref = (S.abs() ** 2).numpy().transpose(0, 2, 1)
+    assert P.shape == ref.shape
+    assert np.max(np.abs(P - ref)) / np.max(ref) < 1e-12
+
+
+@pytest.mark.parametrize("W", [3, 64, 300, 400])
+def test_normalized_window_closed_form(W):
+    """The periodic Hann has sum_n w[n]^2 = 3 W / 8 (W >= 3), so the
+    window-normalised power is the plain power times 8 / (3 W); the
+    frame-length normalisation divides it by W."""
+    n_fft = 400
+    rng = np.random.default_rng(W)
+    x = rng.standard_normal(3000)
+    plain = oracle.pcm_power_frames(x, n_fft, 160, True, "reflect", 2.0, W)
+    win = oracle.pcm_power_frames(x, n_fft, 160, True, "reflect", 2.0, W, normalized="window")
+    fl = oracle.pcm_power_frames(x, n_fft, 160, True, "reflect", 2.0, W, normalized="frame_length")
+    assert np.max(np.abs(win - plain * 8.0 / (3.0 * W))) / np.max(np.abs(win)) < 1e-12
+    assert np.max(np.abs(fl - plain / W)) / np.max(np.abs(fl)) < 1e-12
+    # magnitude (power 1): the factor enters before the exponent
+    m1 = oracle.pcm_power_frames(x, n_fft, 160, True, "reflect", 1.0, W, normalized="window")
+    p1 = oracle.pcm_power_frames(x, n_fft, 160, True, "reflect", 1.0, W)
+    assert np.max(np.abs(m1 - p1 * math.sqrt(8.0 / (3.0 * W)))) / np.max(m1) < 1e-12
+
+
+def test_mel_output_bin_centred_tone_closed_form():
+    """Mel values of a bin-centred tone on interior frames:
+    W[m, k0] (A N / 4)^2 + (W[m, k0-1] + W[m, k0+1]) (A N / 8)^2."""
+    N, hop, A, k0, sr = 400, 160, 0.5, 25, 16000.0
+    n = np.arange(20 * N)
+    x = A * np.cos(2 * np.pi * k0 * n / N + 0.3)
+    W = oracle.mel_filterbank(sr, N, 40)
+    mel = oracle.mel_from_pcm(x[None], N, hop, W)[0]            # (40, F)
+    ref = W[:, k0] * (A * N / 4) ** 2 + (W[:, k0 - 1] + W[:, k0 + 1]) * (A * N / 8) ** 2
+    interior = mel[:, 3:-3]
+    assert np.max(np.abs(interior - ref[:, None])) <= 1e-9 * np.max(ref)
+
+
+def test_log_tail_of_mel_output():
+    """The log-mel is the per-clip tail of the mel values, for both paths."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((2, 5000)).astype(np.float32)
+    W = oracle.mel_filterbank(16000.0, 400, 64)
+    mel = oracle.mel_from_pcm(x, 400, 160, W)
+    assert np.array_equal(oracle.from_pcm(x, 400, 160, W), oracle.log_mel_tail(mel))
+    s = (rng.standard_normal((2, 7, 33)) + 1j * rng.standard_normal((2, 7, 33))).astype(np.complex64)
+    Wl = rng.random((5, 33)).astype(np.float32)
+    assert np.array_equal(oracle.from_stft(s, Wl), oracle.log_mel_tail(oracle.mel_from_stft(s, Wl)))
