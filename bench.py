@@ -74,6 +74,50 @@ def flops_per_frame(w) -> float:
     return 2.5 * N * math.log2(N) + N + 3.0 * (N // 2 + 1) + 2.0 * 2 * (N // 2 + 1)
 
 
+def sweep_one(w, steps: int, warmup: int):
+    """One line of the n_fft sweep: step time, essential-byte rate and the
+    main kernel's dispatch-stamped duration."""
+    import numpy as np  # noqa: F401
+    import torch
+
+    import lm_synth
+    import stft_log_mel_amd as lm
+
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(lm_synth.make_inputs(w)).to(dev)
+    nbuf = max(1, min(8, -(-1_000_000_000 // w.essential_bytes()) + 1))
+    ins = [x.clone() for _ in range(nbuf)]
+    outs = [torch.empty(w.out_shape, dtype=torch.float32, device=dev) for _ in range(nbuf)]
+    plan = lm.Plan(w.n_fft, w.hop, w.n_mels).set_mel(w.sample_rate, w.f_min, w.f_max)
+    for i in range(warmup):
+        plan.from_pcm(ins[i % nbuf], out=outs[i % nbuf])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(steps):
+        plan.from_pcm(ins[i % nbuf], out=outs[i % nbuf])
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    plan.profile(True)
+    for i in range(steps):
+        plan.from_pcm(ins[i % nbuf], out=outs[i % nbuf])
+    torch.cuda.synchronize()
+    plan.profile(False)
+    prof = plan.profile_read()
+    main_ms = prof["main"]["ms"] / max(1, prof["main"]["count"])
+    eb = w.essential_bytes()
+    frames = w.B * w.n_frames
+    print(json.dumps({"workload": w.name, "n_fft": w.n_fft, "hop": w.hop, "n_mels": w.n_mels, "B": w.B,
+                      "T": w.T, "ms_per_step": round(ms, 5), "frames_per_s": round(frames / (ms / 1e3), 1),
+                      "essential_bytes": eb, "essential_gbs_step": round(eb / (ms / 1e3) / 1e9, 1),
+                      "kernel": main_kernel_name(w), "kernel_ms": round(main_ms, 5),
+                      "kernel_gbs": round(eb / (main_ms / 1e3) / 1e9, 1),
+                      "kernel_frac_of_8tbs": round(eb / (main_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "fft_tflops": round(frames * flops_per_frame(w) / (main_ms / 1e3) / 1e12, 2)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -82,6 +126,8 @@ def main():
     ap.add_argument("--workload", default="pcm_i16_b64")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every n_fft of the sweep workloads (one JSON line each, no CPU leg)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (5 times), to scale HBM counters")
     args = ap.parse_args()
@@ -106,6 +152,11 @@ def main():
 
     import lm_synth
     import stft_log_mel_amd as lm
+
+    if args.sweep:
+        for n in lm_synth.SWEEP_SIZES:
+            sweep_one(lm_synth.WORKLOADS[f"sweep_nfft{n}"], args.steps, args.warmup)
+        return
 
     w = lm_synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")

@@ -18,6 +18,9 @@ Workloads
 * ``pcm_f32_nfft16384`` 16 clips x 441000 float32 samples (10 s at 44.1 kHz),
   n_fft 16384, hop 4096, 256 Slaney mels over 0-22.05 kHz, fp16 out.
 
+and adds the n_fft sweep ``sweep_nfft{64..16384}``: 32 clips x 160000
+standard-normal float32 samples, hop n_fft / 4, 128 Slaney mels, fp32 out.
+
 Generators
 ----------
 ``stft_speechlike`` follows the STFT generator of the KBench
@@ -229,6 +232,22 @@ WORKLOADS = {
 }
 
 
+# The flashmel page's n_fft sweep ("Performance": n_fft 64..16384, hop =
+# n_fft / 4, 128 mels, B = 32 clips of T = 160000 samples, randn input);
+# the sample rate is not stated there: 16 kHz, mels over 0..8 kHz.
+SWEEP_SIZES = (64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384)
+for _n in SWEEP_SIZES:
+    WORKLOADS[f"sweep_nfft{_n}"] = Workload(
+        f"sweep_nfft{_n}", "pcm", seed=100 + _n.bit_length(), B=32, T=160000, sample_rate=16000.0,
+        n_fft=_n, hop=_n // 4, n_mels=128, f_min=0.0, f_max=8000.0, in_dtype="f32", out_dtype="f32",
+        signal="noise")
+
+
+def noise_pcm(B: int, T: int, seed: int) -> np.ndarray:
+    """(B, T) float32 standard normal samples (the sweep's randn input)."""
+    return np.random.default_rng(seed).standard_normal((B, T)).astype(np.float32)
+
+
 def make_inputs(w: Workload, B: int | None = None, T: int | None = None, F: int | None = None):
     """Inputs for workload ``w`` (optionally with fewer clips / samples / frames).
 
@@ -242,6 +261,8 @@ def make_inputs(w: Workload, B: int | None = None, T: int | None = None, F: int 
     T = w.T if T is None else T
     if w.signal == "speech":
         return speech_pcm(B, T, w.sample_rate, w.seed, as_int16=(w.in_dtype == "i16"))
+    if w.signal == "noise":
+        return noise_pcm(B, T, w.seed)
     return music_pcm(B, T, w.sample_rate, w.seed)
 
 
@@ -253,5 +274,6 @@ def recipe() -> dict:
         "speech": "f0~U(80,300), h=1..10 amp 1/h phase U(0,2pi), env 0.5(1-cos(2pi*4t+psi)), "
                   "noise RMS -30 dB re tone RMS, peak 0.5; i16=rint(x*32768) clipped",
         "music": "3 sines U(50,15000) Hz amp 0.25 random phase + pink(1/sqrt f) at 0.1x RMS",
+        "noise": "standard normal float32, numpy PCG64(seed) (the n_fft sweep)",
         "seeds": {k: v.seed for k, v in WORKLOADS.items()},
     }

@@ -23,11 +23,18 @@ namespace lm {
 constexpr int kFixEntries = 512;   // regions one group scans
 constexpr int kFixUnroll = 8;      // values per thread with loads in flight together
 
-// Group units of a fix-up: (clip, group) pairs, entries_per_group regions each.
+// Group units of a fix-up: (clip, group) pairs, entries_per_group regions
+// each -- at most kFixEntries, and fewer when regions are large, so that a
+// group never holds more than kFixValues values (a batch whose regions are
+// all flagged then spreads its rewrite over many workgroups).
+constexpr int kFixValues = 65536;
 inline void prepare_fixup(FixupArgs &a) {
   const int n_ent = a.tiles_per_clip * a.st.min_per_tile();
-  a.entries_per_group = kFixEntries;
-  a.groups_per_clip = (n_ent + kFixEntries - 1) / kFixEntries;
+  const int reg = (a.st.frames_per_tile / a.st.sub_per_tile) * a.st.band_h;
+  int per = kFixValues / (reg > 0 ? reg : 1);
+  per = per < 1 ? 1 : (per > kFixEntries ? kFixEntries : per);
+  a.entries_per_group = per;
+  a.groups_per_clip = (n_ent + per - 1) / per;
 }
 
 // Unit (clip b, group gi): reduce the clip's maxima to hi (every group of

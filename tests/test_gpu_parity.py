@@ -311,6 +311,20 @@ def test_melspectrogram_wrapper_torchaudio_surface():
     check_mel(y.reshape(4, 64, 101), ref, 1e-4, "wrapper mel")
 
 
+@pytest.mark.parametrize("n_fft", lm_synth.SWEEP_SIZES)
+def test_pcm_sweep_full_size(n_fft):
+    """The n_fft sweep workloads at full size (32 x 160000, hop n_fft / 4,
+    128 mels); the oracle checks the first and the last clip."""
+    w = lm_synth.WORKLOADS[f"sweep_nfft{n_fft}"]
+    say("pcm sweep full size", w.name)
+    x = lm_synth.make_inputs(w)
+    out = run_pcm(x, w.n_fft, w.hop, w.n_mels, w.sample_rate, fmax=w.f_max)
+    assert tuple(out.shape) == w.out_shape
+    clips = [0, w.B - 1]
+    ref = oracle_pcm(x[clips], w.n_fft, w.hop, w.n_mels, w.sample_rate, fmax=w.f_max)
+    check(out[clips], ref, TOL32, w.name)
+
+
 @pytest.mark.parametrize("pad_mode", ["reflect", "constant", "replicate", "circular"])
 @pytest.mark.parametrize("center", [True, False])
 def test_pcm_pad_modes(pad_mode, center):
