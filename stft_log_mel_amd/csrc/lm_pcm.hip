@@ -279,7 +279,8 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
 // n_fft >= 8192: one frame fills a workgroup's FFT buffer, so the kernel is
 // persistent instead: one workgroup per compute unit stages the packed
 // filterbank and a two-level twiddle table in LDS once, then walks frames
-// gridDim.x apart.  Per frame the phases are those above (windowed load,
+// gridDim.x apart (so the padded first and last frames of the clips, which
+// take the slower index path, spread over the workgroups).  Per frame the phases are those above (windowed load,
 // folded complex FFT, split and power, mel, statistics), with no global
 // memory access between the load and the store: every twiddle is the
 // product of two LDS entries, exp(-2 pi i j / N) = W[j / 128] W'[j % 128].

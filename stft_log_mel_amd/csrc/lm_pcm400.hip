@@ -377,31 +377,6 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  {
-    // all loads of the operand table in flight at once
-    constexpr int PER = (kTab + kThreads - 1) / kThreads;
-    v4f v[PER];
-#pragma unroll
-    for (int u = 0; u < PER; ++u)
-      if (tid + u * kThreads < kTab) v[u] = amat[tid + u * kThreads];
-#pragma unroll
-    for (int u = 0; u < PER; ++u)
-      if (tid + u * kThreads < kTab) s_amat[tid + u * kThreads] = v[u];
-  }
-  for (int i = tid; i < 4 * a.mel_batches; i += kThreads) s_bat[i] = melblk_meta[i];
-  for (int i0 = tid; i0 < a.melw_n; i0 += 4 * kThreads) {
-    float v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * kThreads;
-      v[u] = i < a.melw_n ? melblk_w[i] * a.mel_scale : 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (i0 + u * kThreads < a.melw_n) s_melw[i0 + u * kThreads] = v[u];
-  }
-  __syncthreads();
-
   const IN *__restrict__ pcm = reinterpret_cast<const IN *>(a.pcm);
   float *R = s_reg + wv * kRegion;
   const int hop = a.hop;
@@ -415,7 +390,36 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
   const int64_t wg_end = min(wg0 + a.per_wg, a.n_sub);
   int64_t gs = wg0 + wv;
   Prefetch<IN> pf;
-  bool have = gs < wg_end && prefetch<IN>(a, pcm, gs, span, pf);
+  bool have;
+  {
+    // every table load and the first sub-tile's samples in flight at once
+    // (one round trip before the first barrier)
+    constexpr int PER = (kTab + kThreads - 1) / kThreads;
+    constexpr int WPT = (kMelWLds + kThreads - 1) / kThreads;
+    static_assert(4 * kMelBatMax <= kThreads, "one batch-table entry per thread");
+    v4f v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      if (tid + u * kThreads < kTab) v[u] = amat[tid + u * kThreads];
+    const int bat = tid < 4 * a.mel_batches ? melblk_meta[tid] : 0;
+    float w[WPT];
+#pragma unroll
+    for (int u = 0; u < WPT; ++u) {
+      const int i = tid + u * kThreads;
+      w[u] = i < a.melw_n ? melblk_w[i] : 0.0f;
+    }
+    have = gs < wg_end && prefetch<IN>(a, pcm, gs, span, pf);
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      if (tid + u * kThreads < kTab) s_amat[tid + u * kThreads] = v[u];
+    if (tid < 4 * a.mel_batches) s_bat[tid] = bat;
+#pragma unroll
+    for (int u = 0; u < WPT; ++u) {
+      const int i = tid + u * kThreads;
+      if (i < a.melw_n) s_melw[i] = w[u] * a.mel_scale;
+    }
+    __syncthreads();
+  }
 
   for (; gs < wg_end; gs += kWaves) {
     // 1. this sub-tile's samples into the wave's region (LDS operations of
