@@ -55,7 +55,7 @@ __device__ __forceinline__ int64_t pad_source(int64_t j, int64_t T, int mode) {
   if (mode == LM_PAD_CONSTANT) return -1;
   if (mode == LM_PAD_REFLECT) return j < 0 ? -j : 2 * (T - 1) - j;
   if (mode == LM_PAD_REPLICATE) return j < 0 ? 0 : T - 1;
-  return ((j % T) + T) % T;
+  return j < 0 ? j + T : j - T;   // circular: -T <= j < 2T, as the padding n_fft/2 <= T (checked at entry)
 }
 
 // One Stockham radix-R pass over FPB frames of M points held in `buf`.
@@ -371,14 +371,22 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS) pcm_big_kernel(PcmKerne
         s_buf[lds_pos<kBigPad>(tid + u * THREADS)] = make_float2(xs[u][0] * ws[u].x, xs[u][1] * ws[u].y);
     } else {
       // frames that reach into the padding (the first and last few of a
-      // clip): each sample by index arithmetic, one point at a time
+      // clip): each sample by index arithmetic, all loads in flight together
       const IN *__restrict__ x = reinterpret_cast<const IN *>(a.pcm) + b * T;
       const int64_t j0 = fr * a.hop - a.pad;
-      for (int n = tid; n < M; n += THREADS) {
+      float ys[IPT][2];
+      float2 ws[IPT];
+#pragma unroll
+      for (int u = 0; u < IPT; ++u) {
+        const int n = tid + u * THREADS;
         const int64_t s0 = pad_source(j0 + 2 * n, T, a.pad_mode), s1 = pad_source(j0 + 2 * n + 1, T, a.pad_mode);
-        const float2 w = win2[n];
-        s_buf[lds_pos<kBigPad>(n)] = make_float2((s0 >= 0 ? to_f(x[s0]) : 0.0f) * w.x, (s1 >= 0 ? to_f(x[s1]) : 0.0f) * w.y);
+        ys[u][0] = s0 >= 0 ? to_f(x[s0]) : 0.0f;
+        ys[u][1] = s1 >= 0 ? to_f(x[s1]) : 0.0f;
+        ws[u] = win2[n];
       }
+#pragma unroll
+      for (int u = 0; u < IPT; ++u)
+        s_buf[lds_pos<kBigPad>(tid + u * THREADS)] = make_float2(ys[u][0] * ws[u].x, ys[u][1] * ws[u].y);
     }
     __syncthreads();
 

@@ -279,7 +279,7 @@ __device__ __forceinline__ int64_t pad_index(int64_t j, int64_t T, int mode) {
   if (mode == LM_PAD_CONSTANT) return -1;
   if (mode == LM_PAD_REFLECT) return j < 0 ? -j : 2 * (T - 1) - j;
   if (mode == LM_PAD_REPLICATE) return j < 0 ? 0 : T - 1;
-  return ((j % T) + T) % T;
+  return j < 0 ? j + T : j - T;   // circular: -T <= j < 2T, as the padding n_fft/2 <= T (checked at entry)
 }
 
 constexpr int kPadBatch = 8;   // dwords per lane with loads in flight together
