@@ -158,14 +158,25 @@ __global__ void __launch_bounds__(kStftThreads) stft_logmel_kernel(StftKernelArg
     total += v;
   }
   const bool in_lds = total <= kStftWLds;
+  int src = 0, off = 0;
   if (tid < NM) {
-    const int src = a.f_stride ? tid * a.f_stride + st : a.f_off[tid];
-    const int off = base + incl - wd;
+    src = a.f_stride ? tid * a.f_stride + st : a.f_off[tid];
+    off = base + incl - wd;
     s_start[tid] = st;
     s_width[tid] = wd;
     s_off[tid] = in_lds ? off : src;
-    if (in_lds)
-      for (int j = 0; j < wd; ++j) s_w[off + j] = a.f_w[src + j];
+  }
+  if (in_lds) {
+    // a row's weights kCopy at a time with their loads in flight together
+    constexpr int kCopy = 8;
+    for (int j0 = 0; j0 < wd; j0 += kCopy) {
+      float v[kCopy];
+#pragma unroll
+      for (int u = 0; u < kCopy; ++u) v[u] = j0 + u < wd ? a.f_w[src + j0 + u] : 0.0f;
+#pragma unroll
+      for (int u = 0; u < kCopy; ++u)
+        if (j0 + u < wd) s_w[off + j0 + u] = v[u];
+    }
   }
   __syncthreads();
 
