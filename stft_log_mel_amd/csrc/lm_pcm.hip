@@ -146,7 +146,8 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
   constexpr int FPB = PcmCfg<NFFT>::FPB;
   constexpr int THREADS = PcmCfg<NFFT>::THREADS;
   constexpr int NW = THREADS / 64;
-  __shared__ float2 s_buf[FPB * M];
+  constexpr int PAD = 5;   // one spare point per 32 (lds_pos): the strided first pass stays conflict-free
+  __shared__ float2 s_buf[FPB * M + ((FPB * M) >> PAD)];
   constexpr int WLDS = PcmCfg<NFFT>::WLDS;
   __shared__ int32_t s_start[256], s_width[256], s_off[256];
   __shared__ float s_w[WLDS > 0 ? WLDS : 1];
@@ -192,13 +193,14 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
 #pragma unroll
   for (int u = 0; u < IPT; ++u) {
     const int i = tid + u * THREADS;
-    if ((FPB * M) % THREADS == 0 || i < FPB * M) s_buf[i] = make_float2(xs[u][0] * ws[u].x, xs[u][1] * ws[u].y);
+    if ((FPB * M) % THREADS == 0 || i < FPB * M)
+      s_buf[lds_pos<PAD>(i)] = make_float2(xs[u][0] * ws[u].x, xs[u][1] * ws[u].y);
   }
   __syncthreads();
 
   // 2. M-point complex FFT per frame
   const float2 *__restrict__ twt = a.twiddle;
-  run_fft<M, FPB, THREADS, 0>(s_buf, [=](int j) { return twt[j]; }, typename PcmCfg<NFFT>::Rad{}, tid);
+  run_fft<M, FPB, THREADS, PAD>(s_buf, [=](int j) { return twt[j]; }, typename PcmCfg<NFFT>::Rad{}, tid);
 
   // 3. split into the real spectrum; power tile over the same LDS
   constexpr int NU = M / 2 + 1;              // pairs (k, M-k), k = 0..M/2
@@ -210,8 +212,8 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
     pk[u] = pmk[u] = 0.0f;
     if (q < FPB * NU) {
       const int fl = q / NU, k = q - fl * NU;
-      const float2 zk = s_buf[fl * M + k];
-      const float2 zc = cconj(s_buf[fl * M + (k == 0 ? 0 : M - k)]);
+      const float2 zk = s_buf[lds_pos<PAD>(fl * M + k)];
+      const float2 zc = cconj(s_buf[lds_pos<PAD>(fl * M + (k == 0 ? 0 : M - k))]);
       const float2 Y = cadd(zk, zc), D = csub(zk, zc);
       const float2 V = cmul(a.untangle[k], D);
       pk[u] = (Y.x + V.y) * (Y.x + V.y) + (Y.y - V.x) * (Y.y - V.x);
