@@ -727,8 +727,9 @@ hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &pa, hipStream_t s, con
   k.F = pa.n_frames;
   k.S = pa.tiles_per_clip;
   k.n_sub = pa.n_clips * pa.tiles_per_clip;
-  const int64_t want = (k.n_sub + kWaves - 1) / kWaves;   // workgroups with >= 8 sub-tiles each
-  const int64_t n_wg = want < p->n_cu ? want : p->n_cu;
+  // every CU takes a share, even when there are fewer sub-tiles than waves
+  // (fewer waves per SIMD then finish each sub-tile sooner)
+  const int64_t n_wg = k.n_sub < p->n_cu ? k.n_sub : p->n_cu;
   k.per_wg = (int)((k.n_sub + n_wg - 1) / n_wg);
   k.hop = p->hop;
   k.pad = p->center ? 200 : 0;
