@@ -10,9 +10,9 @@
 // are rewritten.  hi is log10 of the largest mel value, with the same log10
 // the main kernels use, so the largest output is exactly (hi + 4) / 4.
 //
-// fixup_group is one unit of that work, run by a whole workgroup: it is the
-// body of the stand-alone fix-up kernel and the last phase of the persistent
-// main kernels when they are launched cooperatively.
+// fixup_group is one unit of that work, run by a whole workgroup of the
+// fix-up kernel (a second launch after the main kernel; its kernel boundary
+// makes every workgroup's statistics and outputs visible to the fix-up).
 #pragma once
 
 #include "lm_device.h"
