@@ -223,6 +223,19 @@ def main():
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step (wall {wall:.3f}s), "
           f"main kernel {main_ms:.4f} ms, fixup {fix_ms:.4f} ms, pack {pack_ms:.4f} ms", file=sys.stderr, flush=True)
 
+    # context: this GPU's streaming-copy rate (2 GiB read + 2 GiB written)
+    cbuf = torch.empty(1 << 29, dtype=torch.float32, device=dev)
+    cdst = torch.empty_like(cbuf)
+    cdst.copy_(cbuf)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(5):
+        cdst.copy_(cbuf)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * cbuf.numel() * 4 / (ev0.elapsed_time(ev1) / 1e3) / 1e9
+    del cbuf, cdst
+
     # parity spot check of the timed output against the first clip's oracle
     parity = None
     cpu = None
@@ -243,10 +256,14 @@ def main():
         t_cpu = time.perf_counter()
         done = 0
         errs = []
+        sq_err = sq_ref = 0.0
         while True:
             ref = run_clip(done % w.B)
             if done < w.B:
-                errs.append(float(np.abs(got[done] - ref[0]).max()))
+                d = got[done].astype(np.float64) - ref[0]
+                errs.append(float(np.abs(d).max()))
+                sq_err += float((d * d).sum())
+                sq_ref += float((ref[0] * ref[0]).sum())
             done += 1
             if time.perf_counter() - t_cpu >= args.cpu_seconds:
                 break
@@ -256,6 +273,7 @@ def main():
                "sample": f"{done} clips ({done * w.n_frames} frames) of the same workload, taken in order "
                          f"and cycling through its {w.B} clips, fp64 numpy oracle, {dt:.1f}s"}
         parity = {"clips_checked": len(errs), "max_abs_err": max(errs),
+                  "rel_frobenius": (sq_err / sq_ref) ** 0.5 if sq_ref > 0 else 0.0,
                   "tol": 2e-3 if w.out_dtype == "f16" else 1e-4}
         print(f"[bench] oracle: {done} clips in {dt:.1f}s, max |err| {max(errs):.2e}", file=sys.stderr,
               flush=True)
@@ -300,6 +318,9 @@ def main():
             "fp32_vector_peak_tflops": FP32_VALU_PEAK_TFLOPS,
             "fp32_vector_unpacked_peak_tflops": FP32_VALU_PEAK_TFLOPS / 2,
         },
+        "copy_context": {"copy_gbs": round(copy_gbs, 1),
+                         "main_kernel_frac_of_copy": round(achieved / copy_gbs, 4),
+                         "note": "torch copy_ of 2 GiB device to device, read + write bytes per second"},
         "fixup_ms": round(fix_ms, 5),
         "pack_ms": round(pack_ms, 5),
         "cpu_baseline": cpu,

@@ -31,6 +31,12 @@ constexpr int kFixValues = 65536;
 inline void prepare_fixup(FixupArgs &a) {
   const int n_ent = a.tiles_per_clip * a.st.min_per_tile();
   const int reg = (a.st.frames_per_tile / a.st.sub_per_tile) * a.st.band_h;
+  // n / d == umulhi(n, ceil(2^32 / d)) for every n < 2^16 and 2 <= d <= 2^16
+  // (d = 1 is taken apart where they are used): a group's flattened values
+  // number at most kFixValues = 2^16
+  const unsigned inner = (unsigned)(a.mel_major ? a.st.frames_per_tile / a.st.sub_per_tile : a.st.band_h);
+  a.inner_magic = inner > 1 ? (unsigned)((0x100000000ull + inner - 1) / inner) : 0u;
+  a.reg_magic = reg > 1 ? (unsigned)((0x100000000ull + (unsigned)reg - 1) / (unsigned)reg) : 0u;
   int per = kFixValues / (reg > 0 ? reg : 1);
   per = per < 1 ? 1 : (per > kFixEntries ? kFixEntries : per);
   a.entries_per_group = per;
@@ -40,11 +46,12 @@ inline void prepare_fixup(FixupArgs &a) {
 // Unit (clip b, group gi): reduce the clip's maxima to hi (every group of
 // the clip does this itself, so no cross-workgroup atomics or resets are
 // needed), list the regions of the group whose smallest log value lies
-// below hi - 8, then rewrite their values below the floor with all threads.
-// LDS: s_list[kFixEntries], s_n[1], s_red[THREADS / 64].  Every thread of
-// the workgroup must call it; it ends with a barrier.
+// below hi - 8 (as their first frame and first band), then rewrite their
+// values below the floor with all threads.  LDS: s_f0[kFixEntries],
+// s_m0[kFixEntries], s_n[1], s_red[THREADS / 64].  Every thread of the
+// workgroup must call it; it ends with a barrier.
 template <typename OUT, int THREADS>
-__device__ void fixup_group(const FixupArgs &a, int64_t b, int gi, int *s_list, int *s_n, float *s_red) {
+__device__ void fixup_group(const FixupArgs &a, int64_t b, int gi, int *s_f0, int *s_m0, int *s_n, float *s_red) {
   constexpr int NW = THREADS / 64;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const StatLayout st = a.st;
@@ -52,6 +59,7 @@ __device__ void fixup_group(const FixupArgs &a, int64_t b, int gi, int *s_list, 
   const int n_ent = a.tiles_per_clip * ept, n_max = a.tiles_per_clip * st.max_per_tile;
   const float *cmax = a.tile_max + b * (int64_t)n_max;
   const float *cmin = a.tile_min + b * (int64_t)n_ent;
+  const int sub_frames = st.frames_per_tile / st.sub_per_tile;
   if (tid == 0) *s_n = 0;
   // the group's region minima are loaded together with the maxima (one
   // round trip): kFixEntries / THREADS of them per thread
@@ -73,17 +81,27 @@ __device__ void fixup_group(const FixupArgs &a, int64_t b, int gi, int *s_list, 
   const float floorL = log10_pos(fmaxf(hi, 1e-10f)) - 8.0f;
 #pragma unroll
   for (int u = 0; u < MPT; ++u)
-    if (mn[u] < floorL) s_list[atomicAdd(s_n, 1)] = e0 + tid + u * THREADS;   // LDS atomic: order is irrelevant
+    if (mn[u] < floorL) {
+      const int e = e0 + tid + u * THREADS;
+      const int t = e / ept, rem = e - t * ept;
+      const int sub = rem / st.blk_per_sub, blk = rem - sub * st.blk_per_sub;
+      const int k = atomicAdd(s_n, 1);   // LDS atomic: the order of the list is irrelevant
+      s_f0[k] = t * st.frames_per_tile + sub * sub_frames;
+      s_m0[k] = blk * st.band_h;
+    }
   __syncthreads();
   const int n_flag = *s_n;
 
   float fo = rescale(floorL);
   if (sizeof(OUT) == 2) fo = __half2float(__float2half_rn(fo));
+  // rewrite: value k of the flattened list is value el of region i; el
+  // splits into a run index o and the position in the run (contiguous in
+  // the output), both with precomputed multiplies (no division per value)
   OUT *out = reinterpret_cast<OUT *>(a.out);
   const int NM = a.n_mels;
   const int64_t F = a.n_frames;
-  const int sub_frames = st.frames_per_tile / st.sub_per_tile;
-  const int reg = sub_frames * st.band_h;   // values of a full region
+  const int inner = a.mel_major ? sub_frames : st.band_h;   // values of one run
+  const int reg = sub_frames * st.band_h;                    // values of a full region
   const int total = n_flag * reg;
   for (int k0 = tid; k0 < total; k0 += THREADS * kFixUnroll) {
     OUT *p[kFixUnroll];
@@ -93,20 +111,12 @@ __device__ void fixup_group(const FixupArgs &a, int64_t b, int gi, int *s_list, 
       const int k = k0 + u * THREADS;
       p[u] = nullptr;
       if (k < total) {
-        const int i = k / reg, el = k - i * reg;
-        const int e = s_list[i];
-        const int t = e / ept, rem = e - t * ept;
-        const int sub = rem / st.blk_per_sub, blk = rem - sub * st.blk_per_sub;
-        int fi, bi;
-        if (a.mel_major) {
-          bi = el / sub_frames;
-          fi = el - bi * sub_frames;
-        } else {
-          fi = el / st.band_h;
-          bi = el - fi * st.band_h;
-        }
-        const int64_t f = (int64_t)t * st.frames_per_tile + (int64_t)sub * sub_frames + fi;
-        const int m = blk * st.band_h + bi;
+        const int i = reg > 1 ? (int)__umulhi((unsigned)k, a.reg_magic) : k;   // k / reg
+        const int el = k - i * reg;
+        const int o = inner > 1 ? (int)__umulhi((unsigned)el, a.inner_magic) : el;   // el / inner
+        const int in = el - o * inner;
+        const int64_t f = (int64_t)s_f0[i] + (a.mel_major ? in : o);
+        const int m = s_m0[i] + (a.mel_major ? o : in);
         if (f < F && m < NM) {
           p[u] = out + (a.mel_major ? (b * NM + m) * F + f : (b * F + f) * NM + m);
           v[u] = load_out(p[u]);

@@ -9,11 +9,11 @@ constexpr int kFixThreads = 256;
 template <typename OUT>
 __global__ void __launch_bounds__(kFixThreads) clamp_fixup_kernel(FixupArgs a) {
   __shared__ float s_red[kFixThreads / 64];
-  __shared__ int s_list[kFixEntries];
+  __shared__ int s_f0[kFixEntries], s_m0[kFixEntries];
   __shared__ int s_n;
   const int G = a.groups_per_clip;
   const int64_t b = blockIdx.x / G;
-  fixup_group<OUT, kFixThreads>(a, b, (int)(blockIdx.x - b * G), s_list, &s_n, s_red);
+  fixup_group<OUT, kFixThreads>(a, b, (int)(blockIdx.x - b * G), s_f0, s_m0, &s_n, s_red);
 }
 
 hipError_t launch_fixup(FixupArgs a, hipStream_t s, const LaunchTiming *tm) {

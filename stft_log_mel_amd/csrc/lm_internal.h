@@ -198,6 +198,7 @@ struct FixupArgs {
   StatLayout st;
   int mel_major;  // 1: (B, NM, F); 0: (B, F, NM)
   int entries_per_group = 0, groups_per_clip = 0;   // set by launch_fixup
+  unsigned inner_magic = 0, reg_magic = 0;          // set by launch_fixup: divide by a run / a region length
 };
 hipError_t launch_fixup(FixupArgs a, hipStream_t s, const LaunchTiming *tm);
 

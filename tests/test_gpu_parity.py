@@ -401,6 +401,34 @@ def test_pcm_clamp_engaged():
     assert np.abs(out[2].cpu().numpy() + 1.5).max() <= 1e-6     # fp32 1e-10 floor, hardware log2
 
 
+@pytest.mark.parametrize("path", ["pcm16384_one_band", "pcm8192_two_bands", "stft_one_band"])
+def test_clamp_fixup_degenerate_regions(path):
+    """Clamp-engaged batches whose floor regions hold one value, one band
+    or one frame (run lengths of 1 in the fix-up's region walk)."""
+    say("clamp fix-up degenerate regions", path)
+    if path.startswith("pcm"):
+        n_fft = 16384 if "16384" in path else 8192
+        nm = 1 if "one" in path else 2
+        sr = 16000.0
+        x = lm_synth.speech_pcm(2, 12 * n_fft, sr, seed=71)
+        x[0, 3 * n_fft: 9 * n_fft] = 0.0          # silence: the floor binds for whole frames
+        x[1] *= 1e-3
+        p = lm().Plan(n_fft, n_fft // 4, nm).set_mel(sr)
+        out = p.from_pcm(to_dev(x))
+        torch.cuda.synchronize()
+        ref = oracle.from_pcm(x, n_fft, n_fft // 4, oracle.mel_filterbank(sr, n_fft, nm))
+    else:
+        s = lm_synth.stft_speechlike(2, 200, 33, seed=72)
+        s[0, 40:160] = 0.0
+        W = lm_synth.lintri_filters(33, 1)
+        p = lm().Plan(400, 160, 1)
+        out = p.from_stft(to_dev(s), to_dev(W))
+        torch.cuda.synchronize()
+        ref = oracle.from_stft(s, W)
+    assert ref.min() < ref.max() - 1.9           # the floor is engaged
+    check(out, ref, TOL32, path)
+
+
 def test_pcm_invariances():
     sr = 16000.0
     x = lm_synth.speech_pcm(4, 20000, sr, seed=13)
