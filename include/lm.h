@@ -157,8 +157,23 @@ int lm_plan_set_output(lm_plan *plan, int output, int normalized);
 int lm_plan_set_window(lm_plan *plan, int win_length);
 
 /*
+ * lm_plan_set_pad -- two-sided zero padding of the PCM signal (flashmel
+ * page, "Usage": torchaudio's pad argument; "How it works": every padding
+ * applied by index arithmetic).  Each clip of n_samples is read as `pad`
+ * zeros, the clip, `pad` zeros (n_samples + 2 pad samples), and the center
+ * padding of the plan (center=1, pad_mode) then applies to that longer
+ * signal: reflect and circular see the zeros like any other sample.
+ * Nothing padded is stored.  0 <= pad <= 2^30; the default is 0.  A pad
+ * that is not a multiple of 16 bytes of samples (8 int16 or 4 float32
+ * samples) keeps results identical but takes the slower per-sample load
+ * path.  Host-only.  LM_ERR_INVALID_ARG out of range.
+ */
+int lm_plan_set_pad(lm_plan *plan, int64_t pad);
+
+/*
  * lm_plan_num_frames -- frames produced for a clip of n_samples:
- * 1 + floor((n_samples + 2*pad - n_fft) / hop), pad = n_fft/2 if center
+ * 1 + floor((n_samples + 2*sig_pad + 2*pad - n_fft) / hop), with sig_pad
+ * the plan's signal padding (lm_plan_set_pad) and pad = n_fft/2 if center
  * else 0.  Returns a negative lm_status if no frame fits.
  */
 int64_t lm_plan_num_frames(const lm_plan *plan, int64_t n_samples);
@@ -178,8 +193,9 @@ int64_t lm_plan_num_frames(const lm_plan *plan, int64_t n_samples);
  *  with L = log10(max(mel, 1e-10)) and hi_b the clip's largest L (or the
  *  mel values themselves under LM_OUTPUT_MEL, see lm_plan_set_output).
  *
- * Needs n_samples > n_fft/2 for reflect, >= n_fft/2 for circular and
- * >= n_fft for center=0.  n_clips == 0 is a no-op.  Returns
+ * With t = n_samples + 2 sig_pad (lm_plan_set_pad), needs t > n_fft/2 for
+ * reflect, t >= n_fft/2 for circular and t >= n_fft for center=0.
+ * n_clips == 0 is a no-op.  Returns
  * LM_ERR_NO_FILTERS before any filterbank is set.
  */
 int lm_from_pcm(lm_plan *plan, const void *pcm, int in_dtype, int64_t n_clips, int64_t n_samples,

@@ -38,6 +38,7 @@ import numpy as np
 
 __all__ = [
     "decode_pcm",
+    "zero_pad_signal",
     "pad_signal",
     "num_frames",
     "frame_signal",
@@ -75,6 +76,18 @@ def decode_pcm(x: np.ndarray) -> np.ndarray:
     return x.astype(np.float64)
 
 
+def zero_pad_signal(x: np.ndarray, pad: int) -> np.ndarray:
+    """The signal padding ahead of the transform (flashmel page, "Usage":
+    torchaudio's ``pad``): ``pad`` zeros before and after the last axis.
+    The center padding of ``pad_signal`` then applies to the longer signal."""
+    if pad < 0:
+        raise ValueError("pad must be >= 0")
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros(x.shape[:-1] + (x.shape[-1] + 2 * pad,), dtype=np.float64)
+    out[..., pad:pad + x.shape[-1]] = x
+    return out
+
+
 def pad_signal(x: np.ndarray, n_fft: int, center: bool, pad_mode: str) -> np.ndarray:
     """Pad the last axis by n_fft // 2 on both sides when ``center``.
 
@@ -106,9 +119,10 @@ def pad_signal(x: np.ndarray, n_fft: int, center: bool, pad_mode: str) -> np.nda
     return x[..., idx]
 
 
-def num_frames(T: int, n_fft: int, hop: int, center: bool) -> int:
-    """Frame count: 1 + floor((T_padded - n_fft) / hop); no frame is dropped."""
-    t_pad = T + (2 * (n_fft // 2) if center else 0)
+def num_frames(T: int, n_fft: int, hop: int, center: bool, pad: int = 0) -> int:
+    """Frame count: 1 + floor((T_padded - n_fft) / hop); no frame is dropped.
+    T_padded = T + 2 pad (signal padding) + 2 (n_fft // 2) if center."""
+    t_pad = T + 2 * pad + (2 * (n_fft // 2) if center else 0)
     if t_pad < n_fft:
         raise ValueError("signal shorter than one frame")
     return 1 + (t_pad - n_fft) // hop
@@ -282,10 +296,11 @@ def log_mel_tail(mel: np.ndarray) -> np.ndarray:
 
 def pcm_power_frames(x_clip: np.ndarray, n_fft: int, hop: int, center: bool = True,
                      pad_mode: str = "reflect", power: float = 2.0, win_length: int | None = None,
-                     normalized=None) -> np.ndarray:
+                     normalized=None, pad: int = 0) -> np.ndarray:
     """One clip (T,) -> (F, n_fft//2 + 1) |c X|^power of the windowed frames,
-    c the normalisation factor (1 unless ``normalized``)."""
-    xp = pad_signal(decode_pcm(x_clip), n_fft, center, pad_mode)
+    c the normalisation factor (1 unless ``normalized``); the clip is first
+    given ``pad`` zeros on both sides, then the center padding."""
+    xp = pad_signal(zero_pad_signal(decode_pcm(x_clip), pad), n_fft, center, pad_mode)
     w = frame_window(n_fft, win_length)
     frames = frame_signal(xp, n_fft, hop) * w[None, :]
     c = normalization_factor(w, normalized, n_fft if win_length is None else win_length)
@@ -294,7 +309,7 @@ def pcm_power_frames(x_clip: np.ndarray, n_fft: int, hop: int, center: bool = Tr
 
 def mel_from_pcm(x: np.ndarray, n_fft: int, hop: int, filters: np.ndarray, center: bool = True,
                  pad_mode: str = "reflect", power: float = 2.0, win_length: int | None = None,
-                 normalized=None) -> np.ndarray:
+                 normalized=None, pad: int = 0) -> np.ndarray:
     """PCM (B, T) float32 or int16 -> (B, n_mels, F) mel values in float64:
     sum_k W[m, k] |c X_k|^power, the output of a torchaudio-style
     MelSpectrogram (flashmel page, "Usage").
@@ -308,7 +323,7 @@ def mel_from_pcm(x: np.ndarray, n_fft: int, hop: int, filters: np.ndarray, cente
     W = np.asarray(filters, dtype=np.float64)
     outs = []
     for b in range(x.shape[0]):
-        P = pcm_power_frames(x[b], n_fft, hop, center, pad_mode, power, win_length, normalized)
+        P = pcm_power_frames(x[b], n_fft, hop, center, pad_mode, power, win_length, normalized, pad)
         mel = P @ W.T                       # (F, n_mels)
         outs.append(mel.T[None])            # (1, n_mels, F)
     return np.concatenate(outs, axis=0)
@@ -316,10 +331,10 @@ def mel_from_pcm(x: np.ndarray, n_fft: int, hop: int, filters: np.ndarray, cente
 
 def from_pcm(x: np.ndarray, n_fft: int, hop: int, filters: np.ndarray, center: bool = True,
              pad_mode: str = "reflect", power: float = 2.0, win_length: int | None = None,
-             normalized=None) -> np.ndarray:
+             normalized=None, pad: int = 0) -> np.ndarray:
     """PCM (B, T) float32 or int16 -> (B, n_mels, F) log-mel in float64: the
     mel values of ``mel_from_pcm`` through the per-clip log tail."""
-    return log_mel_tail(mel_from_pcm(x, n_fft, hop, filters, center, pad_mode, power, win_length, normalized))
+    return log_mel_tail(mel_from_pcm(x, n_fft, hop, filters, center, pad_mode, power, win_length, normalized, pad))
 
 
 def mel_from_stft(stft: np.ndarray, mel_filters: np.ndarray) -> np.ndarray:

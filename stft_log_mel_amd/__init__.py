@@ -53,6 +53,7 @@ SIGNATURES = {
     "lm_plan_get_filters": (_c_int, [_c_p, _c_p, _c_int, _c_int]),
     "lm_plan_set_output": (_c_int, [_c_p, _c_int, _c_int]),
     "lm_plan_set_window": (_c_int, [_c_p, _c_int]),
+    "lm_plan_set_pad": (_c_int, [_c_p, _c_i64]),
     "lm_plan_num_frames": (_c_i64, [_c_p, _c_i64]),
     "lm_from_pcm": (_c_int, [_c_p, _c_p, _c_int, _c_i64, _c_i64, _c_p, _c_p]),
     "lm_from_stft": (_c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_int, _c_p, _c_p]),
@@ -159,6 +160,11 @@ class Plan:
         _check(_lib.lm_plan_set_window(self._h, int(win_length)))
         return self
 
+    def set_pad(self, pad: int) -> "Plan":
+        """Read each clip with pad zeros before and after it (torchaudio's pad)."""
+        _check(_lib.lm_plan_set_pad(self._h, int(pad)))
+        return self
+
     def get_filters(self) -> np.ndarray:
         a = np.zeros((self.n_mels, self.n_bins), dtype=np.float32)
         _check(_lib.lm_plan_get_filters(self._h, a.ctypes.data, self.n_mels, self.n_bins))
@@ -251,8 +257,8 @@ class Plan:
 class MelSpectrogram:
     """torchaudio-style mel transform (flashmel page, "Usage").
 
-    Accepts the torchaudio ``MelSpectrogram`` arguments (``pad != 0`` and
-    ``onesided=False`` excepted).  ``output="logmel"`` (the default) gives
+    Accepts the torchaudio ``MelSpectrogram`` arguments (``onesided=False``
+    excepted).  ``output="logmel"`` (the default) gives
     the normalised log-mel; ``output="mel"`` the mel values themselves, as
     torchaudio does.  Output: ``(..., n_mels, n_frames)`` in float32 or
     float16 per ``dtype``.  Inference only.
@@ -264,8 +270,6 @@ class MelSpectrogram:
                  pad_mode: str = "reflect", onesided: bool = True, norm: str | None = "slaney",
                  mel_scale: str = "slaney", dtype=None, output: str = "logmel"):
         torch = _torch()
-        if pad:
-            raise NotImplementedError("pad != 0")
         if normalized not in _NORMALIZED or output not in _OUTPUT:
             raise ValueError("normalized must be False|True|'window'|'frame_length'; output 'logmel'|'mel'")
         if not onesided:
@@ -280,6 +284,7 @@ class MelSpectrogram:
         self.normalized, self.output = normalized, output
         self.f_min, self.f_max = float(f_min), (float(f_max) if f_max is not None else self.sample_rate / 2)
         self.n_mels, self.power, self.center, self.pad_mode = int(n_mels), float(power), bool(center), pad_mode
+        self.pad = int(pad)
         self.norm, self.mel_scale, self.dtype = norm, mel_scale, dtype
         self._plans = {}
         # validate now (host-only calls)
@@ -292,6 +297,7 @@ class MelSpectrogram:
                      "f16" if self.dtype == _torch().float16 else "f32")
             p.set_mel(self.sample_rate, self.f_min, self.f_max, self.mel_scale, self.norm)
             p.set_window(self.win_length)
+            p.set_pad(self.pad)
             p.set_output(self.output, self.normalized)
             self._plans[device_index] = p
         return p

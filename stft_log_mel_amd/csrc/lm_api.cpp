@@ -153,11 +153,13 @@ int lm_from_pcm(lm_plan *p, const void *pcm, int in_dtype, int64_t n_clips, int6
   if (n_clips < 0) return fail(LM_ERR_INVALID_ARG, "n_clips < 0");
   if (n_samples < 1) return fail(LM_ERR_INVALID_ARG, "n_samples < 1");
   const int64_t half = p->n_fft / 2;
-  if (!p->center && n_samples < p->n_fft) return fail(LM_ERR_INVALID_ARG, "center=0 needs n_samples >= n_fft");
-  if (p->center && p->pad_mode == LM_PAD_REFLECT && n_samples <= half)
-    return fail(LM_ERR_INVALID_ARG, "reflect padding needs n_samples > n_fft/2");
-  if (p->center && p->pad_mode == LM_PAD_CIRCULAR && n_samples < half)
-    return fail(LM_ERR_INVALID_ARG, "circular padding needs n_samples >= n_fft/2");
+  // the center padding applies to the signal with its zero padding (length t_sig)
+  const int64_t t_sig = n_samples + 2 * p->sig_pad;
+  if (!p->center && t_sig < p->n_fft) return fail(LM_ERR_INVALID_ARG, "center=0 needs n_samples + 2 pad >= n_fft");
+  if (p->center && p->pad_mode == LM_PAD_REFLECT && t_sig <= half)
+    return fail(LM_ERR_INVALID_ARG, "reflect padding needs n_samples + 2 pad > n_fft/2");
+  if (p->center && p->pad_mode == LM_PAD_CIRCULAR && t_sig < half)
+    return fail(LM_ERR_INVALID_ARG, "circular padding needs n_samples + 2 pad >= n_fft/2");
   if (n_clips == 0) return LM_OK;
   if (!pcm || !out) return fail(LM_ERR_INVALID_ARG, "pcm and out must be device pointers");
   const size_t in_align = in_dtype == LM_I16 ? 2 : 4, out_align = p->out_dtype == LM_F16 ? 2 : 4;

@@ -1,11 +1,14 @@
 // Device helpers shared by the kernels: complex arithmetic, small DFT
-// modules, the log10 used by every kernel, wave/block reductions.
+// modules, the log10 used by every kernel, padding by index arithmetic,
+// wave/block reductions.
 #pragma once
 
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+
+#include "lm.h"
 
 namespace lm {
 
@@ -172,6 +175,31 @@ template <>
 __device__ __forceinline__ void dft<8>(float2 (&a)[8]) { dft8(a); }
 template <>
 __device__ __forceinline__ void dft<16>(float2 (&a)[16]) { dft16(a); }
+
+// ---------------------------------------------------------------------------
+// Padding by index arithmetic (flashmel page, "How it works")
+// ---------------------------------------------------------------------------
+
+// Source index, in a clip of T samples, of position j of the signal that is
+// read as P zeros, the clip, P zeros (torchaudio's pad; j counts from the
+// clip's first sample, so those zeros are at -P..-1 and T..T+P-1), with the
+// center padding of `mode` applied beyond that signal; -1 for a zero.  The
+// center padding is at most n_fft/2 < T + 2P samples (reflect) or <= T + 2P
+// (circular), which the entry points check, so one reflection or wrap
+// suffices.
+__device__ __forceinline__ int64_t signal_source(int64_t j, int64_t T, int64_t P, int mode) {
+  if (j >= 0 && j < T) return j;
+  const int64_t Tp = T + 2 * P;
+  int64_t q = j + P;   // position in the zero-padded signal
+  if (q < 0 || q >= Tp) {
+    if (mode == LM_PAD_CONSTANT) return -1;
+    if (mode == LM_PAD_REFLECT) q = q < 0 ? -q : 2 * (Tp - 1) - q;
+    else if (mode == LM_PAD_REPLICATE) q = q < 0 ? 0 : Tp - 1;
+    else q = q < 0 ? q + Tp : q - Tp;
+  }
+  q -= P;
+  return (q >= 0 && q < T) ? q : -1;
+}
 
 // ---------------------------------------------------------------------------
 // Reductions (wave64)

@@ -80,6 +80,7 @@ struct lm_plan {
   float power = 2.0f;
   int n_bins = 0;  // n_fft / 2 + 1
   int win_length = 0;                   // periodic Hann length, centred in the frame (default n_fft)
+  int64_t sig_pad = 0;                  // zeros read before and after each PCM clip (torchaudio's pad)
   int output = LM_OUTPUT_LOGMEL;        // LM_OUTPUT_*
   int normalized = LM_NORMALIZED_NONE;  // LM_NORMALIZED_*
 

@@ -2,8 +2,9 @@
 //
 // A workgroup owns a tile of FPB consecutive frames of one clip and runs
 // the whole chain on it in LDS (flashmel page, "How it works"):
-//   1. frame samples are read straight from the clip with the center
-//      padding done as index arithmetic (nothing padded is stored), paired
+//   1. frame samples are read straight from the clip with the signal's
+//      zero padding and the center padding done as index arithmetic
+//      (nothing padded is stored), paired
 //      as z[n] = w[2n] x[2n] + i w[2n+1] x[2n+1] (periodic Hann);
 //   2. an M = n_fft/2 point complex FFT of z, as Stockham autosort passes
 //      of radix 16/8/5/4/2 through one LDS buffer;
@@ -48,15 +49,6 @@ template <> struct PcmCfg<16384> { static constexpr int FPB = 1; };
 __device__ __forceinline__ float to_f(float v) { return v; }
 __device__ __forceinline__ float to_f(int16_t v) { return (float)(int)v; }
 
-// Source index of padded position j of a clip of T samples (0 <= result <
-// T), or -1 for a constant-mode zero: the center padding resolved by index.
-__device__ __forceinline__ int64_t pad_source(int64_t j, int64_t T, int mode) {
-  if (j >= 0 && j < T) return j;
-  if (mode == LM_PAD_CONSTANT) return -1;
-  if (mode == LM_PAD_REFLECT) return j < 0 ? -j : 2 * (T - 1) - j;
-  if (mode == LM_PAD_REPLICATE) return j < 0 ? 0 : T - 1;
-  return j < 0 ? j + T : j - T;   // circular: -T <= j < 2T, as the padding n_fft/2 <= T (checked at entry)
-}
 
 // One Stockham radix-R pass over FPB frames of M points held in `buf`.
 // Butterfly j of a frame (j < M/R, k = j mod Ns) reads a[t] = in[j + t M/R],
@@ -123,7 +115,8 @@ struct PcmKernelArgs {
   const void *pcm;
   int64_t T, F;
   int tiles_per_clip;
-  int hop, pad, pad_mode;
+  int hop, pad, pad_mode;   // pad: center padding plus the signal's zero padding
+  int64_t sig_pad;         // the signal's zero padding (zeros before and after each clip)
   float power;          // exponent p; 2 takes the fast path
   float mel_scale;      // exact power-of-two scale of the mel sums
   float pre_scale;      // scale of |2X|^2 before a general power
@@ -183,7 +176,7 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
     if ((FPB * M) % THREADS == 0 || i < FPB * M) {
       if (fr < F) {
         const int64_t j = fr * a.hop - a.pad + 2 * n;
-        const int64_t s0 = pad_source(j, T, a.pad_mode), s1 = pad_source(j + 1, T, a.pad_mode);
+        const int64_t s0 = signal_source(j, T, a.sig_pad, a.pad_mode), s1 = signal_source(j + 1, T, a.sig_pad, a.pad_mode);
         xs[u][0] = s0 >= 0 ? to_f(x[s0]) : 0.0f;
         xs[u][1] = s1 >= 0 ? to_f(x[s1]) : 0.0f;
         ws[u] = win2[n];
@@ -381,7 +374,8 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS) pcm_big_kernel(PcmKerne
 #pragma unroll
       for (int u = 0; u < IPT; ++u) {
         const int n = tid + u * THREADS;
-        const int64_t s0 = pad_source(j0 + 2 * n, T, a.pad_mode), s1 = pad_source(j0 + 2 * n + 1, T, a.pad_mode);
+        const int64_t s0 = signal_source(j0 + 2 * n, T, a.sig_pad, a.pad_mode),
+                      s1 = signal_source(j0 + 2 * n + 1, T, a.sig_pad, a.pad_mode);
         ys[u][0] = s0 >= 0 ? to_f(x[s0]) : 0.0f;
         ys[u][1] = s1 >= 0 ? to_f(x[s1]) : 0.0f;
         ws[u] = win2[n];
@@ -536,7 +530,8 @@ hipError_t launch_pcm(const lm_plan *p, const PcmArgs &a, hipStream_t s, const L
   k.F = a.n_frames;
   k.tiles_per_clip = a.tiles_per_clip;
   k.hop = p->hop;
-  k.pad = p->center ? p->n_fft / 2 : 0;
+  k.pad = (p->center ? p->n_fft / 2 : 0) + (int)p->sig_pad;
+  k.sig_pad = p->sig_pad;
   k.pad_mode = p->pad_mode;
   k.power = p->power;
   // |2X|^2 = 4 |X|^2; int16 samples carry a 2^15 factor per |X|

@@ -185,7 +185,8 @@ struct Args {
   int S;                 // 16-frame sub-tiles per clip
   int64_t n_sub;         // sub-tiles of the whole call
   int per_wg;            // sub-tiles per workgroup
-  int hop, pad, pad_mode;
+  int hop, pad, pad_mode;   // pad: center padding plus the signal's zero padding
+  int64_t sig_pad;         // the signal's zero padding (zeros before and after each clip)
   float power, pre_scale, mel_scale;
   int n_mels, n_melblk;
   int melw_n;            // mel step weight count (at most kMelWLds)
@@ -272,16 +273,6 @@ __device__ __forceinline__ bool prefetch(const Args &a, const IN *__restrict__ p
   return true;
 }
 
-// Source index of padded position j of a clip of T samples (0 <= result <
-// T), or -1 for a constant-mode zero.
-__device__ __forceinline__ int64_t pad_index(int64_t j, int64_t T, int mode) {
-  if (j >= 0 && j < T) return j;
-  if (mode == LM_PAD_CONSTANT) return -1;
-  if (mode == LM_PAD_REFLECT) return j < 0 ? -j : 2 * (T - 1) - j;
-  if (mode == LM_PAD_REPLICATE) return j < 0 ? 0 : T - 1;
-  return j < 0 ? j + T : j - T;   // circular: -T <= j < 2T, as the padding n_fft/2 <= T (checked at entry)
-}
-
 constexpr int kPadBatch = 8;   // dwords per lane with loads in flight together
 
 // Padded path for span dwords [d_begin, d_end): each by index arithmetic
@@ -303,7 +294,7 @@ __device__ __forceinline__ void stage_padded(const Args &a, const IN *__restrict
 #pragma unroll
       for (int e = 0; e < PER_DW; ++e) {
         const int64_t j = t.s_begin + (int64_t)(d0 + 64 * u) * PER_DW + e;
-        const int64_t src = (d0 + 64 * u < d_end && j < s_limit) ? pad_index(j, a.T, a.pad_mode) : -1;
+        const int64_t src = (d0 + 64 * u < d_end && j < s_limit) ? signal_source(j, a.T, a.sig_pad, a.pad_mode) : -1;
         v[u][e] = src >= 0 ? to_f(x[src]) : 0.0f;
       }
 #pragma unroll
@@ -732,7 +723,8 @@ hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &pa, hipStream_t s, con
   const int64_t n_wg = k.n_sub < p->n_cu ? k.n_sub : p->n_cu;
   k.per_wg = (int)((k.n_sub + n_wg - 1) / n_wg);
   k.hop = p->hop;
-  k.pad = p->center ? 200 : 0;
+  k.pad = (p->center ? 200 : 0) + (int)p->sig_pad;
+  k.sig_pad = p->sig_pad;
   k.pad_mode = p->pad_mode;
   k.power = p->power;
   // every power value is 4 |X|^2; int16 samples carry 2^15 per |X|, and

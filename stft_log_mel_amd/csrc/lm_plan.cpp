@@ -318,6 +318,14 @@ int lm_plan_set_window(lm_plan *p, int win_length) {
   return LM_OK;
 }
 
+int lm_plan_set_pad(lm_plan *p, int64_t pad) {
+  g_last_error.clear();
+  if (!p) return fail(LM_ERR_INVALID_ARG, "plan is NULL");
+  if (pad < 0 || pad > ((int64_t)1 << 30)) return fail(LM_ERR_INVALID_ARG, "need 0 <= pad <= 2^30");
+  p->sig_pad = pad;
+  return LM_OK;
+}
+
 int lm_plan_set_mel(lm_plan *p, double sr, double f_min, double f_max, int scale, int norm) {
   g_last_error.clear();
   if (!p) return fail(LM_ERR_INVALID_ARG, "plan is NULL");
@@ -382,7 +390,7 @@ int lm_plan_get_filters(const lm_plan *p, float *out, int n_mels, int n_bins) {
 int64_t lm_plan_num_frames(const lm_plan *p, int64_t n_samples) {
   if (!p) return fail(LM_ERR_INVALID_ARG, "plan is NULL");
   if (n_samples < 0) return fail(LM_ERR_INVALID_ARG, "n_samples < 0");
-  const int64_t t_pad = n_samples + (p->center ? 2 * (int64_t)(p->n_fft / 2) : 0);
+  const int64_t t_pad = n_samples + 2 * p->sig_pad + (p->center ? 2 * (int64_t)(p->n_fft / 2) : 0);
   if (t_pad < p->n_fft) return fail(LM_ERR_INVALID_ARG, "signal shorter than one frame");
   return 1 + (t_pad - p->n_fft) / p->hop;
 }

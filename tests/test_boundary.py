@@ -191,8 +191,6 @@ def test_from_stft_validation_before_any_hip_call():
 
 
 def test_python_wrapper_rejects_unbuilt_options():
-    with pytest.raises(NotImplementedError):
-        lm.MelSpectrogram(pad=4)
     with pytest.raises(ValueError):
         lm.MelSpectrogram(normalized="l2")
     with pytest.raises(ValueError):
@@ -234,3 +232,24 @@ def test_set_output_and_window_validation():
     _lib.lm_plan_destroy(h)
     m = lm.MelSpectrogram(sample_rate=16000, n_fft=512, win_length=400, normalized=True, output="mel")
     assert m.hop_length == 200            # torchaudio's default: win_length // 2
+
+
+def test_set_pad_validation_and_frame_counts():
+    rc, h = _create()
+    assert rc == OK
+    assert _lib.lm_plan_set_pad(h, -1) == INVALID
+    assert _lib.lm_plan_set_pad(h, (1 << 30) + 1) == INVALID
+    assert _lib.lm_plan_set_pad(None, 0) == INVALID
+    assert _lib.lm_plan_set_pad(h, 1 << 30) == OK
+    assert _lib.lm_plan_set_pad(h, 100) == OK
+    assert _lib.lm_plan_num_frames(h, 480000) == oracle.num_frames(480000, 400, 160, True, 100) == 3002
+    _lib.lm_plan_destroy(h)
+    rc, h = _create(center=0)
+    assert _lib.lm_plan_set_pad(h, 50) == OK
+    assert _lib.lm_plan_num_frames(h, 300) == 1       # 300 + 2 * 50 = 400 samples: one frame
+    assert _lib.lm_plan_num_frames(h, 299) < 0
+    _lib.lm_plan_destroy(h)
+    m = lm.MelSpectrogram(sample_rate=16000, n_fft=400, hop_length=160, pad=37)
+    assert m.pad == 37 and m._plan_for(None).num_frames(16000) == oracle.num_frames(16000, 400, 160, True, 37)
+    with pytest.raises(Exception):
+        lm.MelSpectrogram(pad=-3)

@@ -311,6 +311,44 @@ def test_melspectrogram_wrapper_torchaudio_surface():
     check_mel(y.reshape(4, 64, 101), ref, 1e-4, "wrapper mel")
 
 
+@pytest.mark.parametrize("n_fft,hop,T,pad,center,pad_mode,in_dtype", [
+    (400, 160, 7001, 8, True, "reflect", "i16"),       # 16-byte multiple: chunked loads stay on
+    (400, 160, 7001, 3, True, "reflect", "i16"),       # odd: every span by index arithmetic
+    (400, 160, 6000, 4, True, "circular", "f32"),
+    (400, 160, 150, 300, True, "reflect", "f32"),      # pad > T: the reflection runs over zeros
+    (400, 160, 300, 60, False, "reflect", "i16"),      # center=0 with T < n_fft: one frame
+    (256, 64, 3001, 37, True, "circular", "f32"),      # generic kernel
+    (1024, 256, 5000, 512, True, "replicate", "i16"),
+    (8192, 2048, 20000, 5000, True, "reflect", "f32"),  # one-frame kernel
+    (16384, 4096, 9000, 4000, True, "constant", "i16")])
+def test_pcm_signal_pad(n_fft, hop, T, pad, center, pad_mode, in_dtype):
+    """torchaudio's pad: zeros read before and after each clip, then the
+    center padding of the longer signal, against the oracle."""
+    sr = 16000.0
+    say("pcm signal pad", n_fft, hop, T, pad, center, pad_mode, in_dtype)
+    x = lm_synth.speech_pcm(2, T, sr, seed=70 + pad, as_int16=(in_dtype == "i16"))
+    p = lm().Plan(n_fft, hop, 64, center, pad_mode).set_mel(sr).set_pad(pad)
+    assert p.num_frames(T) == oracle.num_frames(T, n_fft, hop, center, pad)
+    out = p.from_pcm(to_dev(x))
+    torch.cuda.synchronize()
+    ref = oracle.from_pcm(x, n_fft, hop, oracle.mel_filterbank(sr, n_fft, 64), center=center,
+                          pad_mode=pad_mode, pad=pad)
+    assert tuple(out.shape) == ref.shape
+    check(out, ref, TOL32, f"signal pad {n_fft} {pad} {pad_mode}")
+
+
+def test_melspectrogram_wrapper_pad():
+    sr = 16000.0
+    m = lm().MelSpectrogram(sample_rate=sr, n_fft=400, hop_length=160, n_mels=80, pad=100, output="mel")
+    x = lm_synth.speech_pcm(3, 8000, sr, seed=71)
+    say("MelSpectrogram pad")
+    y = m(to_dev(x))
+    torch.cuda.synchronize()
+    ref = oracle.mel_from_pcm(x, 400, 160, oracle.mel_filterbank(sr, 400, 80), pad=100)
+    assert tuple(y.shape) == ref.shape == (3, 80, 52)
+    check_mel(y, ref, 1e-4, "wrapper pad")
+
+
 @pytest.mark.parametrize("n_fft", lm_synth.SWEEP_SIZES)
 def test_pcm_sweep_full_size(n_fft):
     """The n_fft sweep workloads at full size (32 x 160000, hop n_fft / 4,

@@ -88,8 +88,20 @@ def _frames_hop_slip(xp, n_fft, hop):
     return _orig["frame_signal"](xp, n_fft, hop + 1)
 
 
-def _num_frames_drop_last(T, n_fft, hop, center):
-    return _orig["num_frames"](T, n_fft, hop, center) - 1
+def _num_frames_drop_last(T, n_fft, hop, center, pad=0):
+    return _orig["num_frames"](T, n_fft, hop, center, pad) - 1
+
+
+def _zero_pad_left_only(x, pad):
+    x = np.asarray(x, dtype=np.float64)
+    return np.concatenate([np.zeros(x.shape[:-1] + (2 * pad,)), x], axis=-1)
+
+
+def _zero_pad_reflects(x, pad):
+    x = np.asarray(x, dtype=np.float64)
+    if pad == 0:
+        return x.copy()
+    return np.pad(x, [(0, 0)] * (x.ndim - 1) + [(pad, pad)], mode="reflect")
 
 
 def _fb_wrong_rise(sample_rate, n_fft, n_mels, f_min=0.0, f_max=None, scale="slaney", norm="slaney"):
@@ -161,6 +173,10 @@ MUTATIONS = [
     ("frame_signal", _frames_hop_slip,
      [lambda: pins.test_framing_padding_window_match_torch_stft("constant", 64, 16, 1000)]),
     ("num_frames", _num_frames_drop_last, [pins.test_frame_counts]),
+    ("zero_pad_signal", _zero_pad_left_only,
+     [lambda: pins.test_signal_pad_matches_torch_pad_then_stft("reflect", 400, 160, 1234, 37)]),
+    ("zero_pad_signal", _zero_pad_reflects,
+     [lambda: pins.test_signal_pad_matches_torch_pad_then_stft("constant", 16, 5, 9, 3)]),
     ("mel_filterbank", _fb_wrong_rise,
      [lambda: pins.test_filterbank_invariants(16000, 400, 80, 8000, "slaney")]),
     ("mel_filterbank", _fb_no_norm,

@@ -369,6 +369,35 @@ def test_short_window_matches_torch_stft(n_fft, win_length, hop):
     assert np.max(np.abs(P - ref)) / np.max(ref) < 1e-12
 
 
+@pytest.mark.parametrize("pad_mode", ["reflect", "constant", "replicate", "circular"])
+@pytest.mark.parametrize("n_fft,hop,T,pad", [(400, 160, 1234, 37), (64, 16, 100, 200), (16, 5, 9, 3),
+                                            (256, 64, 1000, 0)])
+def test_signal_pad_matches_torch_pad_then_stft(pad_mode, n_fft, hop, T, pad):
+    """torchaudio's pad: torch.nn.functional.pad with zeros, then torch.stft
+    with its own center padding of the longer signal (both independent
+    library routines, fp64).  pad > T and a tiny clip are included, so the
+    reflection runs over the zeros."""
+    rng = np.random.default_rng(T + pad)
+    x = rng.standard_normal(T)
+    P = oracle.pcm_power_frames(x, n_fft, hop, True, pad_mode, pad=pad)
+    xt = torch.nn.functional.pad(torch.from_numpy(x)[None], (pad, pad), mode="constant", value=0.0)[0]
+    S = torch.stft(xt, n_fft, hop_length=hop, window=torch.hann_window(n_fft, periodic=True, dtype=torch.float64),
+                   center=True, pad_mode=pad_mode, return_complex=True)
+    ref = (S.abs() ** 2).numpy().T
+    assert P.shape == ref.shape
+    assert P.shape[0] == oracle.num_frames(T, n_fft, hop, True, pad)
+    assert np.max(np.abs(P - ref)) / np.max(ref) < 1e-12
+
+
+def test_signal_pad_frame_counts():
+    # T + 2 pad + 2 (n_fft // 2) samples: 480000 + 2 * 100 + 400 -> 3002 frames at hop 160
+    assert oracle.num_frames(480000, 400, 160, True, 100) == 3002
+    assert oracle.num_frames(480000, 400, 160, True, 79) == 3001
+    assert oracle.num_frames(300, 400, 160, False, 50) == 1
+    with pytest.raises(ValueError):
+        oracle.num_frames(298, 400, 160, False, 50)
+
+
 @pytest.mark.parametrize("W", [3, 64, 300, 400])
 def test_normalized_window_closed_form(W):
     """The periodic Hann has sum_n w[n]^2 = 3 W / 8 (W >= 3), so the
