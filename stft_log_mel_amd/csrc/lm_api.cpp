@@ -42,7 +42,12 @@ int upload_tables(lm_plan *p) {
   size_t o_bm = align256(o_mh + sizeof(uint16_t) * p->mfma400h.size());
   size_t o_bw = align256(o_bm + sizeof(int32_t) * p->melblk_meta.size());
   size_t o_t2 = align256(o_bw + sizeof(float) * p->melblk_w.size());
-  size_t total = align256(o_t2 + sizeof(float) * p->twid2.size() + 16);
+  std::vector<int32_t> empty;
+  if (p->have_filters)
+    for (int m = 0; m < NM; ++m)
+      if (p->csr.width[m] == 0) empty.push_back(m);
+  size_t o_eb = align256(o_t2 + sizeof(float) * p->twid2.size());
+  size_t total = align256(o_eb + sizeof(int32_t) * empty.size() + 16);
   std::vector<unsigned char> host(total, 0);
   std::memcpy(host.data() + o_win, p->window.data(), sizeof(float) * N);
   std::memcpy(host.data() + o_tw, p->twiddle.data(), sizeof(float) * 2 * M);
@@ -62,6 +67,7 @@ int upload_tables(lm_plan *p) {
     std::memcpy(host.data() + o_bw, p->melblk_w.data(), sizeof(float) * p->melblk_w.size());
   }
   if (!p->twid2.empty()) std::memcpy(host.data() + o_t2, p->twid2.data(), sizeof(float) * p->twid2.size());
+  if (!empty.empty()) std::memcpy(host.data() + o_eb, empty.data(), sizeof(int32_t) * empty.size());
   if (p->dt.base) {
     hipError_t e = hipFree(p->dt.base);
     p->dt.base = nullptr;
@@ -92,6 +98,8 @@ int upload_tables(lm_plan *p) {
   p->dt.melblk_meta = reinterpret_cast<const int32_t *>(c + o_bm);
   p->dt.melblk_w = reinterpret_cast<const float *>(c + o_bw);
   p->dt.n_melblk = p->have_filters ? (p->n_mels + 15) / 16 : 0;
+  p->dt.empty_bands = reinterpret_cast<const int32_t *>(c + o_eb);
+  p->dt.n_empty = (int)empty.size();
   p->tables_dirty = false;
   return LM_OK;
 }
@@ -184,6 +192,10 @@ int lm_from_pcm(lm_plan *p, const void *pcm, int in_dtype, int64_t n_clips, int6
   if (rc != LM_OK) return rc;
   if (p->output == LM_OUTPUT_MEL) return LM_OK;   // no per-clip tail
   FixupArgs fx{out, p->out_dtype == LM_F16, tmin, tmax, n_clips, F, p->n_mels, (int)tiles, st, 1};
+  if (pcm_skips_empty_bands(p, in_dtype == LM_I16)) {
+    fx.empty_bands = p->dt.empty_bands;
+    fx.n_empty = p->dt.n_empty;
+  }
   return timed_launch(p, s, 1, "launch(clamp fix-up)", [&](const LaunchTiming *tm) { return launch_fixup(fx, s, tm); });
 }
 

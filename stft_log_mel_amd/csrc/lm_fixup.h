@@ -41,6 +41,38 @@ inline void prepare_fixup(FixupArgs &a) {
   per = per < 1 ? 1 : (per > kFixEntries ? kFixEntries : per);
   a.entries_per_group = per;
   a.groups_per_clip = (n_ent + per - 1) / per;
+  a.empty_units = a.n_empty > 0 ? (int)((a.n_frames + kFixValues - 1) / kFixValues) : 0;
+}
+
+// The clip's floor in log10 units, max over its maxima of hi, then log10
+// and minus 8; every thread of the workgroup must call it.
+template <int THREADS>
+__device__ float clip_floor(const FixupArgs &a, int64_t b, float *s_red) {
+  const int n_max = a.tiles_per_clip * a.st.max_per_tile;
+  const float *cmax = a.tile_max + b * (int64_t)n_max;
+  float hi = 0.0f;
+  for (int e = threadIdx.x; e < n_max; e += THREADS) hi = fmaxf(hi, cmax[e]);
+  hi = wave_max(hi);
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = hi;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < THREADS / 64; ++i) hi = fmaxf(hi, s_red[i]);
+  return log10_pos(fmaxf(hi, 1e-10f)) - 8.0f;
+}
+
+// Unit (clip b, empty band row e, segment r): the kFixValues frames from r
+// kFixValues on of band empty_bands[e], which the main kernel left
+// unwritten.  Their log value is log10(1e-10) (no weight, so the mel sum is
+// 0 before the 1e-10 floor), so the result is rescale(max(that, floor)),
+// written without reading.  Mel-major output only.
+template <typename OUT, int THREADS>
+__device__ void fixup_empty_row(const FixupArgs &a, int64_t b, int e, int r, float *s_red) {
+  const float floorL = clip_floor<THREADS>(a, b, s_red);
+  const float v = rescale(fmaxf(log10_pos(1e-10f), floorL));
+  const int64_t F = a.n_frames;
+  OUT *row = reinterpret_cast<OUT *>(a.out) + (b * a.n_mels + a.empty_bands[e]) * F;
+  const int64_t f1 = min(F, (int64_t)(r + 1) * kFixValues);
+  for (int64_t f = (int64_t)r * kFixValues + threadIdx.x; f < f1; f += THREADS) store_out(row + f, v);
 }
 
 // Unit (clip b, group gi): reduce the clip's maxima to hi (every group of
@@ -52,12 +84,10 @@ inline void prepare_fixup(FixupArgs &a) {
 // workgroup must call it; it ends with a barrier.
 template <typename OUT, int THREADS>
 __device__ void fixup_group(const FixupArgs &a, int64_t b, int gi, int *s_f0, int *s_m0, int *s_n, float *s_red) {
-  constexpr int NW = THREADS / 64;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x;
   const StatLayout st = a.st;
   const int ept = st.min_per_tile();
-  const int n_ent = a.tiles_per_clip * ept, n_max = a.tiles_per_clip * st.max_per_tile;
-  const float *cmax = a.tile_max + b * (int64_t)n_max;
+  const int n_ent = a.tiles_per_clip * ept;
   const float *cmin = a.tile_min + b * (int64_t)n_ent;
   const int sub_frames = st.frames_per_tile / st.sub_per_tile;
   if (tid == 0) *s_n = 0;
@@ -71,14 +101,7 @@ __device__ void fixup_group(const FixupArgs &a, int64_t b, int gi, int *s_f0, in
     const int e = e0 + tid + u * THREADS;
     mn[u] = e < e1 ? cmin[e] : __builtin_huge_valf();
   }
-  float hi = 0.0f;
-  for (int e = tid; e < n_max; e += THREADS) hi = fmaxf(hi, cmax[e]);
-  hi = wave_max(hi);
-  if (lane == 0) s_red[wv] = hi;
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < NW; ++i) hi = fmaxf(hi, s_red[i]);
-  const float floorL = log10_pos(fmaxf(hi, 1e-10f)) - 8.0f;
+  const float floorL = clip_floor<THREADS>(a, b, s_red);
 #pragma unroll
   for (int u = 0; u < MPT; ++u)
     if (mn[u] < floorL) {

@@ -66,6 +66,8 @@ struct DeviceTables {
   const int32_t *melblk_meta = nullptr;
   const float *melblk_w = nullptr;
   int n_melblk = 0;
+  const int32_t *empty_bands = nullptr;   // bands with no non-zero weight, ascending
+  int n_empty = 0;
 };
 
 struct ProfileRec {
@@ -158,6 +160,9 @@ struct PcmArgs {
 // generic one).
 StatLayout pcm_stat_layout(const lm_plan *p, bool in_i16);
 hipError_t launch_pcm(const lm_plan *p, const PcmArgs &a, hipStream_t s, const LaunchTiming *tm);
+// True when launch_pcm leaves the plan's empty bands unwritten (the generic
+// kernel, log-mel output, at least one empty band): the fix-up writes them.
+bool pcm_skips_empty_bands(const lm_plan *p, bool in_i16);
 bool pcm400_supported(const lm_plan *p, bool in_i16);
 StatLayout pcm400_stat_layout(const lm_plan *p);
 hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &a, hipStream_t s, const LaunchTiming *tm);
@@ -198,7 +203,13 @@ struct FixupArgs {
   int tiles_per_clip;
   StatLayout st;
   int mel_major;  // 1: (B, NM, F); 0: (B, F, NM)
+  // mel-major only: bands the main kernel left unwritten (no non-zero
+  // weight, so their log value is log10(1e-10) in every frame); the fix-up
+  // writes their floored value without reading them
+  const int32_t *empty_bands = nullptr;
+  int n_empty = 0;
   int entries_per_group = 0, groups_per_clip = 0;   // set by launch_fixup
+  int empty_units = 0;                              // set by launch_fixup: units per empty band row
   unsigned inner_magic = 0, reg_magic = 0;          // set by launch_fixup: divide by a run / a region length
 };
 hipError_t launch_fixup(FixupArgs a, hipStream_t s, const LaunchTiming *tm);

@@ -121,6 +121,7 @@ struct PcmKernelArgs {
   float mel_scale;      // exact power-of-two scale of the mel sums
   float pre_scale;      // scale of |2X|^2 before a general power
   int mel_out;          // 1: store the mel values themselves (no log tail)
+  int skip_empty;       // 1: leave bands without weights unwritten (the fix-up writes them)
   int n_mels;
   const float *window;
   const float2 *twiddle, *untangle;
@@ -244,6 +245,7 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
       const int64_t fr = f0 + fl;
       if (fr >= F) continue;
       const int st = s_start[m], wd = s_width[m];
+      if (wd == 0 && a.skip_empty) continue;   // log10(1e-10) everywhere: written by the fix-up
       const float *pr = P + fl * (M + 1) + st;
       float acc = 0.0f;
       const float *wr = wsrc + s_off[m];
@@ -522,6 +524,10 @@ StatLayout pcm_stat_layout(const lm_plan *p, bool in_i16) {
   return st;
 }
 
+bool pcm_skips_empty_bands(const lm_plan *p, bool in_i16) {
+  return !use_pcm400(p, in_i16) && p->n_fft < 8192 && p->output == LM_OUTPUT_LOGMEL && p->dt.n_empty > 0;
+}
+
 hipError_t launch_pcm(const lm_plan *p, const PcmArgs &a, hipStream_t s, const LaunchTiming *tm) {
   if (use_pcm400(p, a.in_i16)) return launch_pcm400(p, a, s, tm);
   PcmKernelArgs k;
@@ -545,6 +551,7 @@ hipError_t launch_pcm(const lm_plan *p, const PcmArgs &a, hipStream_t s, const L
     k.pre_scale = (float)(0.25 * in_scale2);
   }
   k.mel_out = p->output == LM_OUTPUT_MEL;
+  k.skip_empty = pcm_skips_empty_bands(p, a.in_i16);
   k.n_mels = p->n_mels;
   k.window = p->dt.window;
   k.twiddle = p->dt.twiddle;

@@ -349,6 +349,40 @@ def test_melspectrogram_wrapper_pad():
     check_mel(y, ref, 1e-4, "wrapper pad")
 
 
+@pytest.mark.parametrize("n_fft,hop,T,in_dtype,out_dtype", [
+    (64, 16, 1_100_000, "f32", "f32"),    # 68751 frames: two fix-up segments per empty row
+    (128, 32, 40_000, "i16", "f16"), (256, 64, 30_001, "f32", "f16")])
+def test_pcm_empty_bands_written_by_fixup(n_fft, hop, T, in_dtype, out_dtype):
+    """Bands without any filter weight (most of them at n_fft 64 / 128 mels)
+    are left to the fix-up, which writes rescale(max(log10(1e-10), hi - 8))
+    without reading; a silent clip (hi = -10) keeps -10 there."""
+    sr = 16000.0
+    say("pcm empty bands", n_fft, hop, T, in_dtype, out_dtype)
+    x = lm_synth.speech_pcm(2, T, sr, seed=80 + n_fft, as_int16=(in_dtype == "i16"))
+    x[1] = 0
+    W = oracle.mel_filterbank(sr, n_fft, 128)
+    assert (np.abs(W).sum(1) == 0).sum() > 10
+    p = lm().Plan(n_fft, hop, 128, out_dtype=out_dtype).set_mel(sr)
+    out = p.from_pcm(to_dev(x))
+    torch.cuda.synchronize()
+    ref = oracle.from_pcm(x, n_fft, hop, W)
+    check(out, ref, TOL32 if out_dtype == "f32" else TOL16, f"empty bands {n_fft} {out_dtype}")
+    assert torch.max(torch.abs(out[1].float() + 1.5)).item() < 1e-6
+
+
+def test_pcm_user_filters_with_zero_rows_generic_path():
+    """A caller's filterbank with all-zero rows, interleaved with real ones."""
+    sr = 16000.0
+    W = oracle.mel_filterbank(sr, 512, 40).astype(np.float32)
+    W[::3] = 0.0
+    x = lm_synth.speech_pcm(3, 20_000, sr, seed=81)
+    say("pcm zero filter rows")
+    p = lm().Plan(512, 128, 40).set_filters(W)
+    out = p.from_pcm(to_dev(x))
+    torch.cuda.synchronize()
+    check(out, oracle.from_pcm(x, 512, 128, W), TOL32, "zero filter rows")
+
+
 @pytest.mark.parametrize("n_fft", lm_synth.SWEEP_SIZES)
 def test_pcm_sweep_full_size(n_fft):
     """The n_fft sweep workloads at full size (32 x 160000, hop n_fft / 4,
