@@ -118,6 +118,72 @@ def sweep_one(w, steps: int, warmup: int):
                       "fft_tflops": round(frames * flops_per_frame(w) / (main_ms / 1e3) / 1e12, 2)}), flush=True)
 
 
+def dft_gemm_probe(w, steps: int, warmup: int):
+    """The dense alternative to the fused FFT at n_fft = 400: the windowed
+    frames of the batch (192064 x 400, fp32) times the real DFT matrix
+    (400 x 402: cos and -sin columns for bins 0..200, window folded in), one
+    torch.matmul on the vendor BLAS in fp32.  Times the GEMM alone -- a lower
+    bound for that design, which would still need the power, the mel
+    projection and the log tail -- next to the library's whole fused step on
+    the same batch."""
+    import numpy as np
+    import torch
+
+    import stft_log_mel_amd as lm
+
+    torch.backends.cuda.matmul.allow_tf32 = False
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(lm_synth_inputs(w)).to(dev)
+    N, hop = w.n_fft, w.hop
+    xf = torch.nn.functional.pad(x.float()[:, None, :], (N // 2, N // 2), mode="reflect")[:, 0, :]
+    frames = xf.unfold(-1, N, hop).reshape(-1, N).contiguous()          # (B F, N)
+    n = np.arange(N)[:, None].astype(np.float64)
+    k = np.arange(N // 2 + 1)[None, :].astype(np.float64)
+    win = 0.5 - 0.5 * np.cos(2 * np.pi * np.arange(N) / N)
+    ang = 2 * np.pi * n * k / N
+    D = np.concatenate([np.cos(ang), -np.sin(ang)], axis=1) * win[:, None]   # (N, 2 (N/2 + 1))
+    Dm = torch.from_numpy(D.astype(np.float32)).to(dev)
+    y = torch.empty(frames.shape[0], Dm.shape[1], dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        torch.matmul(frames, Dm, out=y)
+    torch.cuda.synchronize()
+    # sanity: the GEMM is the windowed one-sided DFT (against torch.fft.rfft on a few frames)
+    ref = torch.fft.rfft(frames[:64] * torch.from_numpy(win.astype(np.float32)).to(dev), dim=-1)
+    got = torch.complex(y[:64, :N // 2 + 1], y[:64, N // 2 + 1:])
+    rel = (torch.abs(got - ref).max() / torch.abs(ref).max()).item()
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        torch.matmul(frames, Dm, out=y)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    gemm_ms = ev0.elapsed_time(ev1) / steps
+    flop = 2.0 * frames.shape[0] * N * Dm.shape[1]
+    # the library's fused step on the same batch
+    plan = lm.Plan(N, hop, w.n_mels).set_mel(w.sample_rate, w.f_min, w.f_max)
+    out = torch.empty(w.out_shape, dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        plan.from_pcm(x, out=out)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(steps):
+        plan.from_pcm(x, out=out)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    fused_ms = ev0.elapsed_time(ev1) / steps
+    print(json.dumps({"probe": "dft_as_fp32_gemm", "workload": w.name, "M": frames.shape[0], "K": N,
+                      "N": Dm.shape[1], "gemm_ms": round(gemm_ms, 4), "gemm_tflops": round(flop / gemm_ms / 1e9, 1),
+                      "fp32_matrix_peak_tflops": 157.3, "gemm_rel_err_vs_rfft": rel,
+                      "fused_step_ms": round(fused_ms, 4), "gemm_over_fused_step": round(gemm_ms / fused_ms, 2)}),
+          flush=True)
+
+
+def lm_synth_inputs(w):
+    import lm_synth
+    return lm_synth.make_inputs(w)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,6 +196,9 @@ def main():
                     help="time every n_fft of the sweep workloads (one JSON line each, no CPU leg)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (5 times), to scale HBM counters")
+    ap.add_argument("--dft-gemm", action="store_true",
+                    help="FFT-variant comparison: time the n_fft = 400 transform of the default workload "
+                         "as one dense fp32 GEMM on the vendor BLAS (torch.matmul), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (clips shard across "
@@ -152,6 +221,10 @@ def main():
 
     import lm_synth
     import stft_log_mel_amd as lm
+
+    if args.dft_gemm:
+        dft_gemm_probe(lm_synth.WORKLOADS["pcm_i16_b64"], args.steps, args.warmup)
+        return
 
     if args.sweep:
         for n in lm_synth.SWEEP_SIZES:

@@ -109,7 +109,8 @@ struct lm_plan {
   void *d_pack = nullptr;
   size_t pack_cap = 0;
 
-  bool force_generic = false;    // LM_FORCE_GENERIC=1: skip the specialised PCM kernels
+  int force_generic = 0;         // LM_FORCE_GENERIC: 1 skips the n_fft = 400 matrix-core kernel for the folded
+                                 // generic one; "paired" (2) takes the paired 400-point variant (FFT comparison)
 
   bool profiling = false;
   std::vector<lm::ProfileRec> prof;

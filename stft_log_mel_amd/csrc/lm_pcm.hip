@@ -134,14 +134,24 @@ struct PcmKernelArgs {
 };
 
 
-template <int NFFT, typename IN, typename OUT>
+// exp(-2 pi i / 400): the odd twiddles of the paired 400-point transform
+// come from the 200-point table times this (double-rounded once to fp32)
+constexpr float kW400_1c = 0.99987663248166059f, kW400_1s = -0.015707317311820675f;
+
+// PAIRED (n_fft = 400 only; the FFT-variant comparison): instead of folding
+// each real frame into a 200-point complex sequence, two frames a, b form
+// one 400-point complex sequence z = y_a + i y_b, transformed by radix
+// 16/5/5 passes and split as 2 X_a[k] = Z[k] + Z*[400-k], 2 X_b[k] =
+// -i (Z[k] - Z*[400-k]).
+template <int NFFT, typename IN, typename OUT, bool PAIRED = false>
 __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKernelArgs a) {
+  static_assert(!PAIRED || NFFT == 400, "the paired transform is built for n_fft = 400");
   constexpr int M = NFFT / 2;
   constexpr int FPB = PcmCfg<NFFT>::FPB;
   constexpr int THREADS = PcmCfg<NFFT>::THREADS;
   constexpr int NW = THREADS / 64;
   constexpr int PAD = 5;   // one spare point per 32 (lds_pos): the strided first pass stays conflict-free
-  __shared__ float2 s_buf[FPB * M + ((FPB * M) >> PAD)];
+  __shared__ float2 s_buf[FPB * M + ((FPB * M) >> PAD)];   // also FPB / 2 sequences of NFFT points when PAIRED
   constexpr int WLDS = PcmCfg<NFFT>::WLDS;
   __shared__ int32_t s_start[256], s_width[256], s_off[256];
   __shared__ float s_w[WLDS > 0 ? WLDS : 1];
@@ -161,6 +171,72 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
                                          s_off, s_w, WLDS);
   const bool w_in_lds = WLDS > 0 && nnz <= WLDS;
 
+  if constexpr (PAIRED) {
+    // 1'. frames 2 l and 2 l + 1 of the tile as one complex sequence
+    constexpr int NP = FPB / 2;
+    constexpr int IPT = (NP * NFFT + THREADS - 1) / THREADS;
+    float xa[IPT], xb[IPT], wv[IPT];
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      const int i = tid + u * THREADS;
+      const int pl = i / NFFT, n = i - pl * NFFT;
+      const int64_t fa = f0 + 2 * pl;
+      xa[u] = xb[u] = wv[u] = 0.0f;
+      if (i < NP * NFFT && fa < F) {
+        const int64_t j = fa * a.hop - a.pad + n;
+        const int64_t sa = signal_source(j, T, a.sig_pad, a.pad_mode);
+        const int64_t sb = fa + 1 < F ? signal_source(j + a.hop, T, a.sig_pad, a.pad_mode) : -1;
+        xa[u] = sa >= 0 ? to_f(x[sa]) : 0.0f;
+        xb[u] = sb >= 0 ? to_f(x[sb]) : 0.0f;
+        wv[u] = a.window[n];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      const int i = tid + u * THREADS;
+      if (i < NP * NFFT) s_buf[lds_pos<PAD>(i)] = make_float2(xa[u] * wv[u], xb[u] * wv[u]);
+    }
+    __syncthreads();
+    // 2'. 400-point complex FFT per pair: exp(-2 pi i j / 400) from the
+    //     200-point table, times exp(-2 pi i / 400) for odd j
+    const float2 *__restrict__ twt = a.twiddle;
+    run_fft<NFFT, NP, THREADS, PAD>(
+        s_buf,
+        [=](int j) {
+          const float2 t = twt[j >> 1];
+          return (j & 1) ? cmul(t, make_float2(kW400_1c, kW400_1s)) : t;
+        },
+        Radices<16, 5, 5>{}, tid);
+    // 3'. split into the two frames' spectra, |2 X|^2 in the power tile
+    constexpr int NK = NFFT / 2 + 1;
+    constexpr int UPT = (NP * NK + THREADS - 1) / THREADS;
+    float pa[UPT], pb[UPT];
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int q = tid + u * THREADS;
+      pa[u] = pb[u] = 0.0f;
+      if (q < NP * NK) {
+        const int pl = q / NK, k = q - pl * NK;
+        const float2 zk = s_buf[lds_pos<PAD>(pl * NFFT + k)];
+        const float2 zc = cconj(s_buf[lds_pos<PAD>(pl * NFFT + (k == 0 ? 0 : NFFT - k))]);
+        const float2 A = cadd(zk, zc), Bm = csub(zk, zc);   // 2 X_a, and i 2 X_b
+        pa[u] = A.x * A.x + A.y * A.y;
+        pb[u] = Bm.x * Bm.x + Bm.y * Bm.y;
+      }
+    }
+    __syncthreads();
+    float *P = reinterpret_cast<float *>(s_buf);
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int q = tid + u * THREADS;
+      if (q < NP * NK) {
+        const int pl = q / NK, k = q - pl * NK;
+        P[(2 * pl) * (M + 1) + k] = pa[u];
+        P[(2 * pl + 1) * (M + 1) + k] = pb[u];
+      }
+    }
+    __syncthreads();
+  } else {
   // 1. windowed, padded frame samples as M complex points per frame; every
   //    load of the thread is issued before any is used
   const float2 *__restrict__ win2 = reinterpret_cast<const float2 *>(a.window);
@@ -226,6 +302,8 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
     }
   }
   __syncthreads();
+  }   // folded (not PAIRED)
+  float *P = reinterpret_cast<float *>(s_buf);
   if (a.power != 2.0f) {
     // |X|^p = (|X|^2)^(p/2) in place, outside the unrolled split above
     const float e = 0.5f * a.power;
@@ -486,15 +564,15 @@ static hipError_t launch_big(const PcmKernelArgs &k, bool i16, bool f16, int64_t
   return hipGetLastError();
 }
 
-template <int NFFT>
+template <int NFFT, bool PAIRED = false>
 static hipError_t launch_n(const PcmKernelArgs &k, bool i16, bool f16, int64_t n_tiles, hipStream_t s,
                            const LaunchTiming *tm) {
   constexpr int THREADS = PcmCfg<NFFT>::THREADS;
   const dim3 grid((unsigned)n_tiles), block(THREADS);
-  if (!i16 && !f16) LM_LAUNCH(tm, (pcm_logmel_kernel<NFFT, float, float>), grid, block, 0, s, k);
-  else if (!i16 && f16) LM_LAUNCH(tm, (pcm_logmel_kernel<NFFT, float, __half>), grid, block, 0, s, k);
-  else if (i16 && !f16) LM_LAUNCH(tm, (pcm_logmel_kernel<NFFT, int16_t, float>), grid, block, 0, s, k);
-  else LM_LAUNCH(tm, (pcm_logmel_kernel<NFFT, int16_t, __half>), grid, block, 0, s, k);
+  if (!i16 && !f16) LM_LAUNCH(tm, (pcm_logmel_kernel<NFFT, float, float, PAIRED>), grid, block, 0, s, k);
+  else if (!i16 && f16) LM_LAUNCH(tm, (pcm_logmel_kernel<NFFT, float, __half, PAIRED>), grid, block, 0, s, k);
+  else if (i16 && !f16) LM_LAUNCH(tm, (pcm_logmel_kernel<NFFT, int16_t, float, PAIRED>), grid, block, 0, s, k);
+  else LM_LAUNCH(tm, (pcm_logmel_kernel<NFFT, int16_t, __half, PAIRED>), grid, block, 0, s, k);
   return hipGetLastError();
 }
 
@@ -568,7 +646,9 @@ hipError_t launch_pcm(const lm_plan *p, const PcmArgs &a, hipStream_t s, const L
   const int64_t n_tiles = a.n_clips * a.tiles_per_clip;
   const bool f16 = p->out_dtype == LM_F16;
   switch (p->n_fft) {
-    case 400: return launch_n<400>(k, a.in_i16, f16, n_tiles, s, tm);
+    case 400:
+      if (p->force_generic == 2) return launch_n<400, true>(k, a.in_i16, f16, n_tiles, s, tm);
+      return launch_n<400>(k, a.in_i16, f16, n_tiles, s, tm);
     case 64: return launch_n<64>(k, a.in_i16, f16, n_tiles, s, tm);
     case 128: return launch_n<128>(k, a.in_i16, f16, n_tiles, s, tm);
     case 256: return launch_n<256>(k, a.in_i16, f16, n_tiles, s, tm);

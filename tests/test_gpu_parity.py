@@ -537,16 +537,31 @@ def test_melspectrogram_wrapper_shapes():
 def test_pcm400_fast_and_generic_paths(hop, in_dtype, monkeypatch):
     """n_fft = 400 runs on the matrix-core kernel when the hop is even and the
     tile's span fits in LDS, else on the generic kernel; LM_FORCE_GENERIC=1
-    selects the generic kernel.  Both must match the oracle."""
-    import os
+    selects the generic kernel (folded 200-point transform) and "paired"
+    its paired 400-point variant (two frames per complex transform; the
+    clip's 153 frames leave the last pair with one frame).  All must match
+    the oracle."""
     B, T = 3, 24321
     x = lm_synth.speech_pcm(B, T, 16000.0, seed=hop, as_int16=(in_dtype == "i16"))
     ref = oracle_pcm(x, 400, hop, 128, 16000.0)
-    for force in ("0", "1"):
+    for force in ("0", "1", "paired"):
         monkeypatch.setenv("LM_FORCE_GENERIC", force)
         say("pcm400 path", hop, in_dtype, "force_generic", force)
         out = run_pcm(x, 400, hop, 128, 16000.0)
         check(out, ref, TOL32, f"hop {hop} {in_dtype} generic={force}")
+
+
+@pytest.mark.parametrize("in_dtype,out_dtype,pad_mode,power", [("i16", "f16", "constant", 2.0),
+                                                                ("f32", "f32", "circular", 1.0)])
+def test_pcm400_paired_variant_options(in_dtype, out_dtype, pad_mode, power, monkeypatch):
+    """The paired 400-point variant with fp16 output, other pad modes and a
+    general power."""
+    monkeypatch.setenv("LM_FORCE_GENERIC", "paired")
+    x = lm_synth.speech_pcm(2, 16001, 16000.0, seed=90, as_int16=(in_dtype == "i16"))
+    say("pcm400 paired", in_dtype, out_dtype, pad_mode, power)
+    out = run_pcm(x, 400, 160, 80, 16000.0, pad_mode=pad_mode, power=power, out_dtype=out_dtype)
+    ref = oracle_pcm(x, 400, 160, 80, 16000.0, pad_mode=pad_mode, power=power)
+    check(out, ref, TOL32 if out_dtype == "f32" else TOL16, f"paired {in_dtype} {out_dtype} {pad_mode} {power}")
 
 
 def test_pcm400_int16_two_part_fp16_first_stage_precision():
