@@ -191,6 +191,7 @@ struct Args {
   int n_mels, n_melblk;
   int melw_n;            // mel step weight count (at most kMelWLds)
   int mel_batches;       // batches of kMelBatch steps over all band blocks
+  uint64_t end_mask[2];  // bit b: batch b is the last of its band block
   int mel_out;           // 1: store the mel values themselves (no log tail)
   float *tile_max;
 };
@@ -265,10 +266,21 @@ __device__ __forceinline__ bool prefetch(const Args &a, const IN *__restrict__ p
   pf.q_hi = (int)max((int64_t)pf.q_lo, min(hi, (int64_t)n4));
   const u4 *s4 = reinterpret_cast<const u4 *>(src);
   const int lane = threadIdx.x & 63;
+  // one opaque uniform base per 4 KB of chunks: every load is then that base
+  // plus 16 lane plus an immediate offset below 4 KB, and none needs a
+  // freshly computed address register (which the compiler takes from a
+  // load destination and guards with a wait for all memory accesses)
+  typedef const u4 __attribute__((address_space(1))) *gptr;
+  gptr base[(Prefetch<IN>::N + 3) / 4];
+#pragma unroll
+  for (int h = 0; h < (Prefetch<IN>::N + 3) / 4; ++h) {
+    base[h] = (gptr)(s4 + 256 * h);
+    asm volatile("" : "+s"(base[h]));
+  }
 #pragma unroll
   for (int i = 0; i < Prefetch<IN>::N; ++i) {
     const int q = lane + 64 * i;
-    if (q >= pf.q_lo && q < pf.q_hi) pf.v[i] = s4[q];
+    if (q >= pf.q_lo && q < pf.q_hi) pf.v[i] = base[i >> 2][lane + 64 * (i & 3)];
   }
   return true;
 }
@@ -328,6 +340,10 @@ __device__ __forceinline__ void put_prefetch(const Args &a, const IN *__restrict
   const int lane = threadIdx.x & 63;
   u4 *d4 = reinterpret_cast<u4 *>(R);
   u2 *d2 = reinterpret_cast<u2 *>(R + kLoff);
+  // every prefetch register is retired here, also those the predicated
+  // writes below skip, so no load stays in flight into the next prefetch
+#pragma unroll
+  for (int i = 0; i < Prefetch<IN>::N; ++i) asm volatile("" ::"v"(pf.v[i]));
 #pragma unroll
   for (int i = 0; i < Prefetch<IN>::N; ++i) {
     const int q = lane + 64 * i;
@@ -364,7 +380,7 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
   __shared__ v4f s_amat[kAmat];
   __shared__ __attribute__((aligned(16))) float s_melw[kMelWLds];
   __shared__ __attribute__((aligned(16))) float s_reg[kWaves * kRegion];
-  __shared__ int s_bat[4 * kMelBatMax];   // per mel batch and quad: first bin | last-batch flag << 16
+  __shared__ int s_bat[4 * kMelBatMax];   // per mel batch and quad: first bin
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -403,7 +419,7 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
 #pragma unroll
     for (int u = 0; u < PER; ++u)
       if (tid + u * kThreads < kTab) s_amat[tid + u * kThreads] = v[u];
-    if (tid < 4 * a.mel_batches) s_bat[tid] = bat;
+    if (tid < 4 * a.mel_batches) s_bat[tid] = bat & 0xffff;
 #pragma unroll
     for (int u = 0; u < WPT; ++u) {
       const int i = tid + u * kThreads;
@@ -415,8 +431,15 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
   for (; gs < wg_end; gs += kWaves) {
     // 1. this sub-tile's samples into the wave's region (LDS operations of
     //    one wave complete in order, so no barrier is needed around them)
-    if (have) put_prefetch<IN, SK>(a, pcm, gs, pf, span, R);
-    else stage_padded<IN, SK>(a, pcm, gs, 0, span / (4 / (int)sizeof(IN)), R);
+    if (have) {
+      put_prefetch<IN, SK>(a, pcm, gs, pf, span, R);
+    } else {
+      // no prefetch load is in flight on this path (prefetch returned false),
+      // which the compiler cannot tell: retire the registers here as well
+#pragma unroll
+      for (int i = 0; i < Prefetch<IN>::N; ++i) asm volatile("" ::"v"(pf.v[i]));
+      stage_padded<IN, SK>(a, pcm, gs, 0, span / (4 / (int)sizeof(IN)), R);
+    }
     have = gs + kWaves < wg_end && prefetch<IN>(a, pcm, gs + kWaves, span, pf);
 
     // 2. window + 16-point DFT + twiddle on the matrix cores: D[n1] += A[j][n1] x[j][n1].
@@ -593,26 +616,24 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
     int eR[4];
     bool endR[4];
     auto entry = [&](int bt) { return s_bat[4 * min(bt, NBT - 1) + g]; };
+    const uint64_t endm0 = a.end_mask[0], endm1 = a.end_mask[1];
     auto load = [&](auto slot, int bt) {
       constexpr int S = decltype(slot)::value;
       const v4f w4 = *reinterpret_cast<const v4f *>(wl + 16 * kMelBatch * min(bt, NBT - 1));
-      const float *pq = Rc + (eR[S] & 0xffff);
+      const float *pq = Rc + eR[S];
 #pragma unroll
       for (int u = 0; u < kMelBatch; ++u) {
         wR[S][u] = w4[u];
         pR[S][u] = pq[u];
       }
-      endR[S] = (__builtin_amdgcn_readfirstlane(eR[S]) >> 16) != 0;
+      endR[S] = ((bt < 64 ? endm0 : endm1) >> (bt & 63)) & 1;   // uniform: scalar instructions only
     };
     int cb = 0;
-    v4f acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
     auto compute = [&](auto slot) {
       constexpr int S = decltype(slot)::value;
 #pragma unroll
-      for (int u = 0; u < kMelBatch; u += 2) {
-        acc0 = __builtin_amdgcn_mfma_f32_4x4x1f32(pR[S][u], wR[S][u], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_4x4x1f32(pR[S][u + 1], wR[S][u + 1], acc1, 0, 0, 0);
-      }
+      for (int u = 0; u < kMelBatch; ++u) acc = __builtin_amdgcn_mfma_f32_4x4x1f32(pR[S][u], wR[S][u], acc, 0, 0, 0);
       if (!endR[S]) return;
       // block cb complete: log10, rescale, store, statistics
       uint32_t vminb = 0x7f800000u;   // +inf: no value
@@ -620,12 +641,12 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
         const bool band_ok = 16 * cb + 4 * g + (c & 3) < NM;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (band_ok && f0 + i < F) store_out(orow + i, acc0[i] + acc1[i]);
+          if (band_ok && f0 + i < F) store_out(orow + i, acc[i]);
       } else if (sub_full && 16 * cb + 16 <= NM) {   // uniform: every lane's band and frames exist
         float o[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float v = fmaxf(acc0[i] + acc1[i], 1e-10f);
+          const float v = fmaxf(acc[i], 1e-10f);
           const uint32_t vb = __float_as_uint(v);
           vmaxb = max(vmaxb, vb);
           vminb = min(vminb, vb);
@@ -636,7 +657,7 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
         const bool band_ok = 16 * cb + 4 * g + (c & 3) < NM;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float v = fmaxf(acc0[i] + acc1[i], 1e-10f);
+          const float v = fmaxf(acc[i], 1e-10f);
           const uint32_t vb = __float_as_uint(v);
           if (band_ok && f0 + i < F) {
             vmaxb = max(vmaxb, vb);
@@ -647,8 +668,7 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
       }
       vminb = row_min16(vminb);
       if (c == 0) tile_min[(gs * NB + cb) * 4 + g] = log10_pos(__uint_as_float(vminb));
-      acc0 = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-      acc1 = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
       ++cb;
       orow += 16 * F;
     };
@@ -743,6 +763,10 @@ hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &pa, hipStream_t s, con
   k.n_melblk = p->dt.n_melblk;
   k.melw_n = (int)p->melblk_w.size();
   k.mel_batches = (int)(p->melblk_meta.size() / 4);
+  static_assert(kMelBatMax <= 128, "end flags fit two 64-bit masks");
+  k.end_mask[0] = k.end_mask[1] = 0;
+  for (int bt = 0; bt < k.mel_batches; ++bt)
+    if (p->melblk_meta[4 * (size_t)bt] >> 16) k.end_mask[bt >> 6] |= (uint64_t)1 << (bt & 63);
   k.tile_max = pa.tile_max;
   const dim3 grid((unsigned)n_wg), block(kThreads);
   const bool f16 = p->out_dtype == LM_F16;
