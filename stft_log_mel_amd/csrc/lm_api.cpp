@@ -38,7 +38,7 @@ int upload_tables(lm_plan *p) {
   size_t o_of = align256(o_wd + sizeof(int32_t) * NM);
   size_t o_w = align256(o_of + sizeof(int32_t) * NM);
   size_t o_mf = align256(o_w + sizeof(float) * (nnz > 0 ? nnz : 1));
-  size_t o_mh = align256(o_mf + sizeof(float) * p->mfma400.size());
+  size_t o_mh = o_mf;
   size_t o_bm = align256(o_mh + sizeof(uint16_t) * p->mfma400h.size());
   size_t o_bw = align256(o_bm + sizeof(int32_t) * p->melblk_meta.size());
   size_t o_t2 = align256(o_bw + sizeof(float) * p->melblk_w.size());
@@ -58,8 +58,6 @@ int upload_tables(lm_plan *p) {
     std::memcpy(host.data() + o_of, p->csr.off.data(), sizeof(int32_t) * NM);
     if (nnz) std::memcpy(host.data() + o_w, p->csr.w.data(), sizeof(float) * nnz);
   }
-  if (!p->mfma400.empty())
-    std::memcpy(host.data() + o_mf, p->mfma400.data(), sizeof(float) * p->mfma400.size());
   if (!p->mfma400h.empty())
     std::memcpy(host.data() + o_mh, p->mfma400h.data(), sizeof(uint16_t) * p->mfma400h.size());
   if (p->have_filters) {
@@ -93,7 +91,6 @@ int upload_tables(lm_plan *p) {
   p->dt.csr_off = reinterpret_cast<const int32_t *>(c + o_of);
   p->dt.csr_w = reinterpret_cast<const float *>(c + o_w);
   p->dt.nnz = nnz;
-  p->dt.mfma400 = p->mfma400.empty() ? nullptr : reinterpret_cast<const float *>(c + o_mf);
   p->dt.mfma400h = p->mfma400h.empty() ? nullptr : reinterpret_cast<const uint16_t *>(c + o_mh);
   p->dt.melblk_meta = reinterpret_cast<const int32_t *>(c + o_bm);
   p->dt.melblk_w = reinterpret_cast<const float *>(c + o_bw);

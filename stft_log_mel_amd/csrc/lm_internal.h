@@ -61,7 +61,6 @@ struct DeviceTables {
   const int32_t *csr_start = nullptr, *csr_width = nullptr, *csr_off = nullptr;
   const float *csr_w = nullptr;
   int nnz = 0;
-  const float *mfma400 = nullptr;   // n_fft = 400 only
   const uint16_t *mfma400h = nullptr;
   const int32_t *melblk_meta = nullptr;
   const float *melblk_w = nullptr;
@@ -92,8 +91,7 @@ struct lm_plan {
   std::vector<float> twiddle;     // 2 * M
   std::vector<float> untangle;    // 2 * (M/2 + 1)
   std::vector<float> twid2;       // n_fft >= 8192: 2 * (n_fft / 128 + 128), see build_twiddles
-  std::vector<float> mfma400;     // n_fft = 400 only: first-stage matrix-core operands (4 x 7 x 64 x 4)
-  std::vector<uint16_t> mfma400h;  // the same as fp16 hi/lo parts for int16 samples (25 x 2 x 2 x 16 x 8)
+  std::vector<uint16_t> mfma400h;  // n_fft = 400 only: first-stage matrix as fp16 hi/lo parts (25 x 2 x 2 x 16 x 8)
   std::vector<int32_t> melblk_meta;  // per batch of mel steps: first bin of each quad, last-batch flag
   std::vector<float> melblk_w;       // blocked filter weights in matrix-core lane order
 

@@ -8,7 +8,10 @@
 //   X[16 k1 + k2] = sum_n1 W25^(n1 k1) [ sum_n2 y[n1 + 25 n2] W400^(k2 (n1 + 25 n2)) ].
 // The bracket (window, 16-point DFT and twiddle) is, for each n1, one real
 // 16x16 matrix applied to 16 frames at once on the matrix cores
-// (v_mfma_f32_16x16x4f32, four per n1).  Since y is real, classes k2 and
+// (v_mfma_f32_16x16x32_f16, two per n1: the samples as two fp16 planes
+// whose sum carries them exactly (int16) or to about 22 bits (float, with a
+// per-sub-tile power-of-two scale), against the matrix as fp16 hi + lo
+// parts, accumulated in fp32).  Since y is real, classes k2 and
 // 16 - k2 are conjugate mirrors, so the matrix rows hold classes 1..7
 // (real and imaginary parts) plus the two sums of y over even and over odd
 // n2 -- from which classes 0 and 8, the bins that are multiples of 8, are a
@@ -50,9 +53,8 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kSub = 16;                  // frames per wave step (the matrix-core N)
 constexpr int kRow = kPcm400Row;          // power row stride
 constexpr int kRegion = kSub * kRow;      // floats of LDS per wave: staged samples, then power rows
-constexpr int kAmat = 4 * 7 * 64;         // first-stage operands (v4f): [j][n1 / 4][lane]
-constexpr int kAmatH = 25 * 2 * 2 * 16;   // the fp16 form for int16 samples (8 halves each): [n1][part][g % 2][row]
-constexpr int kLoff = 1694;               // int16 samples: dword offset of the l / 64 plane in the region
+constexpr int kAmatH = 25 * 2 * 2 * 16;   // first-stage operands (8 fp16 each): [n1][part][g % 2][row]
+constexpr int kLoff = 1694;               // dword offset of the second (low) fp16 plane in the region
 constexpr int kMelWLds = 5632;            // LDS floats for the mel step weights
 constexpr int kMelBatMax = kMelWLds / (16 * kMelBatch);   // mel batches that fit
 constexpr int kPfI16 = 6, kPfF32 = 11;    // 16-byte sample loads per lane held for the next sub-tile
@@ -199,15 +201,14 @@ struct Args {
 __device__ __forceinline__ float to_f(float v) { return v; }
 __device__ __forceinline__ float to_f(int16_t v) { return (float)(int)v; }
 
-// LDS layout of the staged span.  With SK (hop = 160 samples), 4 pad dwords
-// follow every hop of samples, so the 16 frame starts of a wave, 84 (int16)
-// or 164 (f32) dwords apart, fall on distinct bank quads; without, the span
-// is dense.  A hop is a multiple of 4 dwords, so 16-byte chunks never
-// straddle a pad.
-template <typename IN, bool SK>
+// LDS layout of the staged span, two fp16 planes (below) in which samples
+// 2d and 2d + 1 share dword d.  With SK (hop = 160 samples = 80 dwords), 4
+// pad dwords follow every hop, so the 16 frame starts of a wave, 84 dwords
+// apart, fall on distinct bank quads; without, the span is dense.  A hop is
+// a multiple of 4 dwords, so 16-byte chunks never straddle a pad.
+template <bool SK>
 __device__ __forceinline__ int span_dw(int d) {
-  constexpr int H = sizeof(IN) == 2 ? 80 : 160;   // dwords per 160-sample hop
-  return SK ? d + 4 * (d / H) : d;
+  return SK ? d + 4 * (d / 80) : d;
 }
 
 // int16 samples are staged as two fp16 planes with the dword layout above:
@@ -225,6 +226,28 @@ __device__ __forceinline__ void split_i16(uint32_t x, uint32_t &H, uint32_t &L) 
                 h2{(_Float16)-16.0f, (_Float16)-16.0f};
   H = __builtin_bit_cast(uint32_t, hv);
   L = __builtin_bit_cast(uint32_t, lv);
+}
+
+// float samples go to the same two planes, scaled per sub-tile by an exact
+// 2^e that puts the span's largest magnitude in [256, 512) (the range of
+// x / 64 for int16): H holds the nearest fp16 of x 2^e and L the nearest
+// fp16 of the remainder, so H + L = x 2^e to about 22 significant bits
+// (2^-24 absolute for the smallest samples).  The mel sums take the exact
+// 2^-2e back.
+__device__ __forceinline__ void split_f32(float x0, float x1, float sc, uint32_t &H, uint32_t &L) {
+  const float a = x0 * sc, b = x1 * sc;
+  const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+  const h2 hv{ha, hb}, lv{(_Float16)(a - (float)ha), (_Float16)(b - (float)hb)};
+  H = __builtin_bit_cast(uint32_t, hv);
+  L = __builtin_bit_cast(uint32_t, lv);
+}
+
+// e with 256 <= m 2^e < 512 for the largest magnitude m of a span (0 for a
+// silent or non-finite span), kept within [-100, 100]
+__device__ __forceinline__ int scale_exponent(float m) {
+  if (!(m > 0.0f) || !(m < __builtin_huge_valf())) return 0;
+  const int ex = __builtin_amdgcn_frexp_expf(m);   // m = f 2^ex, 1/2 <= f < 1
+  return min(100, max(-100, 9 - ex));
 }
 
 template <typename IN>
@@ -287,88 +310,127 @@ __device__ __forceinline__ bool prefetch(const Args &a, const IN *__restrict__ p
 
 constexpr int kPadBatch = 8;   // dwords per lane with loads in flight together
 
-// Padded path for span dwords [d_begin, d_end): each by index arithmetic
-// (positions past the end of the clip's last frame read as 0), kPadBatch
-// dwords per lane with all their loads issued before any is used.
+// Padded path for plane dwords [d_begin, d_end) of the span (samples 2d,
+// 2d + 1): each sample by index arithmetic (positions past the end of the
+// clip's last frame read as 0), kPadBatch dwords per lane with all their
+// loads issued before any is used.  Float samples are scaled by 2^e.
 template <typename IN, bool SK>
 __device__ __forceinline__ void stage_padded(const Args &a, const IN *__restrict__ pcm, int64_t gs, int d_begin,
-                                             int d_end, float *R) {
-  constexpr int PER_DW = 4 / sizeof(IN);
+                                             int d_end, float *R, int e) {
   const SubTile t = locate(a, gs);
   const IN *x = pcm + t.b * a.T;
   const int64_t s_limit = (a.F - 1) * (int64_t)a.hop - a.pad + 400;
   uint32_t *d32 = reinterpret_cast<uint32_t *>(R);
+  const float sc = __builtin_amdgcn_ldexpf(1.0f, e);
   const int lane = threadIdx.x & 63;
   for (int d0 = d_begin + lane; d0 < d_end; d0 += 64 * kPadBatch) {
-    float v[kPadBatch][PER_DW];
+    float v[kPadBatch][2];
 #pragma unroll
     for (int u = 0; u < kPadBatch; ++u)
 #pragma unroll
-      for (int e = 0; e < PER_DW; ++e) {
-        const int64_t j = t.s_begin + (int64_t)(d0 + 64 * u) * PER_DW + e;
+      for (int k = 0; k < 2; ++k) {
+        const int64_t j = t.s_begin + (int64_t)(d0 + 64 * u) * 2 + k;
         const int64_t src = (d0 + 64 * u < d_end && j < s_limit) ? signal_source(j, a.T, a.sig_pad, a.pad_mode) : -1;
-        v[u][e] = src >= 0 ? to_f(x[src]) : 0.0f;
+        v[u][k] = src >= 0 ? to_f(x[src]) : 0.0f;
       }
 #pragma unroll
     for (int u = 0; u < kPadBatch; ++u) {
       if (d0 + 64 * u >= d_end) break;
-      uint32_t w = 0;
-#pragma unroll
-      for (int e = 0; e < PER_DW; ++e) {
-        if (sizeof(IN) == 2) w |= (uint32_t)(uint16_t)(int16_t)(int)v[u][e] << (16 * e);
-        else w = __float_as_uint(v[u][e]);
-      }
-      const int o = span_dw<IN, SK>(d0 + 64 * u);
+      uint32_t H, L;
       if (sizeof(IN) == 2) {
-        uint32_t H, L;
+        const uint32_t w = (uint32_t)(uint16_t)(int16_t)(int)v[u][0] | ((uint32_t)(uint16_t)(int16_t)(int)v[u][1] << 16);
         split_i16(w, H, L);
-        d32[o] = H;
-        d32[kLoff + o] = L;
       } else {
-        d32[o] = w;
+        split_f32(v[u][0], v[u][1], sc, H, L);
       }
+      const int o = span_dw<SK>(d0 + 64 * u);
+      d32[o] = H;
+      d32[kLoff + o] = L;
     }
   }
 }
 
+// Largest magnitude of the lane's samples among plane dwords [d_begin,
+// d_end) of the span, by the padded path's index arithmetic (float input).
+template <typename IN>
+__device__ __forceinline__ float padded_absmax(const Args &a, const IN *__restrict__ pcm, int64_t gs, int d_begin,
+                                               int d_end) {
+  const SubTile t = locate(a, gs);
+  const IN *x = pcm + t.b * a.T;
+  const int64_t s_limit = (a.F - 1) * (int64_t)a.hop - a.pad + 400;
+  float m = 0.0f;
+  for (int d = d_begin + (threadIdx.x & 63); d < d_end; d += 64)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int64_t j = t.s_begin + (int64_t)d * 2 + k;
+      const int64_t src = j < s_limit ? signal_source(j, a.T, a.sig_pad, a.pad_mode) : -1;
+      if (src >= 0) m = fmaxf(m, fabsf(to_f(x[src])));
+    }
+  return m;
+}
+
 // The prefetched chunks into the wave's region, then the span's dwords
-// outside them by the padded path.
+// outside them by the padded path; returns the scale exponent e of float
+// input (0 for int16).
 template <typename IN, bool SK>
-__device__ __forceinline__ void put_prefetch(const Args &a, const IN *__restrict__ pcm, int64_t gs,
-                                             const Prefetch<IN> &pf, int span, float *R) {
-  constexpr int PER_DW = 4 / sizeof(IN);
+__device__ __forceinline__ int put_prefetch(const Args &a, const IN *__restrict__ pcm, int64_t gs,
+                                            const Prefetch<IN> &pf, int span, float *R) {
+  constexpr bool kI16 = sizeof(IN) == 2;
+  constexpr int DPC = 8 / sizeof(IN);   // plane dwords per 16-byte chunk
   const int lane = threadIdx.x & 63;
+  const int ndw = span / 2;
+  const int lo_end = min(DPC * pf.q_lo, ndw), hi_begin = DPC * pf.q_hi;
   u4 *d4 = reinterpret_cast<u4 *>(R);
-  u2 *d2 = reinterpret_cast<u2 *>(R + kLoff);
+  u2 *h2p = reinterpret_cast<u2 *>(R);
+  u2 *l2p = reinterpret_cast<u2 *>(R + kLoff);
   // every prefetch register is retired here, also those the predicated
   // writes below skip, so no load stays in flight into the next prefetch
 #pragma unroll
   for (int i = 0; i < Prefetch<IN>::N; ++i) asm volatile("" ::"v"(pf.v[i]));
+  int e = 0;
+  if constexpr (!kI16) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < Prefetch<IN>::N; ++i) {
+      const int q = lane + 64 * i;
+      if (q >= pf.q_lo && q < pf.q_hi)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) m = fmaxf(m, fabsf(__uint_as_float(pf.v[i][k])));
+    }
+    if (pf.q_lo > 0) m = fmaxf(m, padded_absmax<IN>(a, pcm, gs, 0, lo_end));
+    if (hi_begin < ndw) m = fmaxf(m, padded_absmax<IN>(a, pcm, gs, hi_begin, ndw));
+    e = scale_exponent(wave_max(m));
+  }
+  const float sc = __builtin_amdgcn_ldexpf(1.0f, e);
 #pragma unroll
   for (int i = 0; i < Prefetch<IN>::N; ++i) {
     const int q = lane + 64 * i;
     if (q >= pf.q_lo && q < pf.q_hi) {
-      const int o = span_dw<IN, SK>(4 * q);
-      if (sizeof(IN) == 2) {
+      const int o = span_dw<SK>(DPC * q);
+      if constexpr (kI16) {
         u4 H, L;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int k = 0; k < 4; ++k) {
           uint32_t hh, ll;
-          split_i16(pf.v[i][e], hh, ll);
-          H[e] = hh;
-          L[e] = ll;
+          split_i16(pf.v[i][k], hh, ll);
+          H[k] = hh;
+          L[k] = ll;
         }
         d4[o / 4] = H;
-        d2[o / 2] = u2{L[0], L[1]};
-        d2[o / 2 + 1] = u2{L[2], L[3]};
+        l2p[o / 2] = u2{L[0], L[1]};
+        l2p[o / 2 + 1] = u2{L[2], L[3]};
       } else {
-        d4[o / 4] = pf.v[i];
+        uint32_t H0, L0, H1, L1;
+        split_f32(__uint_as_float(pf.v[i][0]), __uint_as_float(pf.v[i][1]), sc, H0, L0);
+        split_f32(__uint_as_float(pf.v[i][2]), __uint_as_float(pf.v[i][3]), sc, H1, L1);
+        h2p[o / 2] = u2{H0, H1};
+        l2p[o / 2] = u2{L0, L1};
       }
     }
   }
-  const int ndw = span / PER_DW;
-  if (pf.q_lo > 0) stage_padded<IN, SK>(a, pcm, gs, 0, min(4 * pf.q_lo, ndw), R);
-  if (4 * pf.q_hi < ndw) stage_padded<IN, SK>(a, pcm, gs, 4 * pf.q_hi, ndw, R);
+  if (pf.q_lo > 0) stage_padded<IN, SK>(a, pcm, gs, 0, lo_end, R, e);
+  if (hi_begin < ndw) stage_padded<IN, SK>(a, pcm, gs, hi_begin, ndw, R, e);
+  return e;
 }
 
 template <typename IN, typename OUT, bool SK>
@@ -376,8 +438,8 @@ __global__ void __launch_bounds__(kThreads, 1)
 pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ melblk_meta,
               const float *__restrict__ melblk_w, OUT *__restrict__ out, float *__restrict__ tile_min) {
   constexpr bool kI16 = sizeof(IN) == 2;
-  constexpr int kTab = kI16 ? kAmatH : kAmat;
-  __shared__ v4f s_amat[kAmat];
+  constexpr int kTab = kAmatH;
+  __shared__ v4f s_amat[kAmatH];   // fp16 operands, 8 per entry
   __shared__ __attribute__((aligned(16))) float s_melw[kMelWLds];
   __shared__ __attribute__((aligned(16))) float s_reg[kWaves * kRegion];
   __shared__ int s_bat[4 * kMelBatMax];   // per mel batch and quad: first bin
@@ -431,34 +493,31 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
   for (; gs < wg_end; gs += kWaves) {
     // 1. this sub-tile's samples into the wave's region (LDS operations of
     //    one wave complete in order, so no barrier is needed around them)
+    int esc;   // float input: the sub-tile's scale exponent (uniform)
     if (have) {
-      put_prefetch<IN, SK>(a, pcm, gs, pf, span, R);
+      esc = put_prefetch<IN, SK>(a, pcm, gs, pf, span, R);
     } else {
       // no prefetch load is in flight on this path (prefetch returned false),
       // which the compiler cannot tell: retire the registers here as well
 #pragma unroll
       for (int i = 0; i < Prefetch<IN>::N; ++i) asm volatile("" ::"v"(pf.v[i]));
-      stage_padded<IN, SK>(a, pcm, gs, 0, span / (4 / (int)sizeof(IN)), R);
+      esc = kI16 ? 0 : scale_exponent(wave_max(padded_absmax<IN>(a, pcm, gs, 0, span / 2)));
+      stage_padded<IN, SK>(a, pcm, gs, 0, span / 2, R, esc);
     }
+    esc = __builtin_amdgcn_readfirstlane(esc);
     have = gs + kWaves < wg_end && prefetch<IN>(a, pcm, gs + kWaves, span, pf);
 
-    // 2. window + 16-point DFT + twiddle on the matrix cores: D[n1] += A[j][n1] x[j][n1].
-    //    Lane (c, g) supplies, for step j, the samples n1 + 25 (4 g + j) of frame c:
-    //    a run of 25 consecutive samples starting at c hop + 100 g + 25 j, read as
-    //    13 dwords (int16 pairs) or float pairs from its first even sample.  In the
-    //    skewed layout two runs cross a pad: j = 0, g = 3 (sample 320, from read
-    //    10) and j = 2, g = 1 (sample 160, from read 5); their later reads are
-    //    4 dwords further on.
+    // 2. window + 16-point DFT + twiddle on the matrix cores: D[n1] = A[n1] x[n1],
+    //    per n1 two fp16 products (matrix hi and lo parts) over k-slots e of
+    //    lane (c, g): sample n1 + 25 n2 of frame c, n2 = 4 (e / 2) + e % 2 +
+    //    2 (g % 2), from plane H (groups 0, 3) or L (groups 1, 2).  The run of
+    //    group g % 2 = 1 starts 50 samples (25 dwords) later; in the skewed
+    //    layout it is another 4 dwords later where the samples of the two
+    //    groups lie on different sides of a hop boundary.
     v4f D[25];
 #pragma unroll
     for (int n1 = 0; n1 < 25; ++n1) D[n1] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    if constexpr (kI16) {
-      // int16: per n1, two fp16 products (matrix hi and lo parts) over
-      // k-slots e of lane (c, g): sample n1 + 25 n2 of frame c, n2 = 4 (e / 2)
-      // + e % 2 + 2 (g % 2), from plane H (groups 0, 3) or L (groups 1, 2).
-      // The run of group g % 2 = 1 starts 50 samples (25 dwords) later; in
-      // the skewed layout it is another 4 dwords later where the samples of
-      // the two groups lie on different sides of a hop boundary.
+    {
       const int h = g & 1;
       const _Float16 *pl = reinterpret_cast<const _Float16 *>(R + ((g == 0 || g == 3) ? 0 : kLoff));
       const _Float16 *p0 = pl + 2 * ((SK ? 84 * c : (c * hop) >> 1) + 25 * h);
@@ -479,52 +538,6 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
         D[n1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, B, D[n1], 0, 0, 0);
         D[n1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, B, D[n1], 0, 0, 0);
       }
-    } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v4f A[7];
-#pragma unroll
-      for (int q = 0; q < 7; ++q) A[q] = s_amat[(j * 7 + q) * 64 + lane];
-      const int r0 = c * hop + 100 * g + 25 * j;   // even hop: r0 has the parity of j
-      const int relr = (100 * g + 25 * j) & ~1;     // first even sample of the run, within the frame
-      int base, delta = 0;
-      const int ist = j == 0 ? 10 : (j == 2 ? 5 : 13);   // first read past the crossing (unrolled: a constant)
-      if (SK) {
-        base = (sizeof(IN) == 2 ? 84 * c + (relr >> 1) : 164 * c + relr) + 4 * ((relr >= 160) + (relr >= 320));
-        if (j == 0) delta = g == 3 ? 4 : 0;
-        if (j == 2) delta = g == 1 ? 4 : 0;
-      } else {
-        base = sizeof(IN) == 2 ? (r0 >> 1) : (r0 & ~1);
-      }
-      float x[25];
-      if (sizeof(IN) == 2) {
-        const uint32_t *rd = reinterpret_cast<const uint32_t *>(R) + base;
-        const uint32_t *rd2 = rd + delta;
-        uint32_t w[13];
-#pragma unroll
-        for (int i = 0; i < 13; ++i) w[i] = i < ist ? rd[i] : rd2[i];
-#pragma unroll
-        for (int n1 = 0; n1 < 25; ++n1) {
-          const int s = n1 + (j & 1);
-          const uint32_t d = w[s >> 1];
-          x[n1] = (s & 1) ? (float)((int32_t)d >> 16) : (float)(int16_t)(d & 0xffffu);
-        }
-      } else {
-        const float2 *rf = reinterpret_cast<const float2 *>(R + base);
-        const float2 *rf2 = reinterpret_cast<const float2 *>(R + base + delta);
-        float2 f[13];
-#pragma unroll
-        for (int i = 0; i < 13; ++i) f[i] = i < ist ? rf[i] : rf2[i];
-#pragma unroll
-        for (int n1 = 0; n1 < 25; ++n1) {
-          const int s = n1 + (j & 1);
-          x[n1] = (s & 1) ? f[s >> 1].y : f[s >> 1].x;
-        }
-      }
-#pragma unroll
-      for (int n1 = 0; n1 < 25; ++n1)
-        D[n1] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[n1 >> 2][n1 & 3], x[n1], D[n1], 0, 0, 0);
-    }
     }
 
     // 3. 25-point DFTs over n1.  Za: class g + 1 (rows 4g, 4g+1).  Zb: class
@@ -585,10 +598,13 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
     Rc[205 + g] = 0.0f;
     Rc[209 + g] = 0.0f;
     if (a.power != 2.0f) {
-      // |X|^p = (|X|^2)^(p/2) in place over the wave's rows
+      // |X|^p = (|X|^2)^(p/2) in place over the wave's rows (float input:
+      // the sub-tile's 2^-2e first)
       const float pe = 0.5f * a.power;
-      for (int i = lane; i < kRegion; i += 64) R[i] = powf(R[i] * a.pre_scale, pe);
+      for (int i = lane; i < kRegion; i += 64) R[i] = powf(__builtin_amdgcn_ldexpf(R[i] * a.pre_scale, -2 * esc), pe);
     }
+    // float input at power 2: the mel sums carry 2^2e (exact power of two)
+    const int mel_e = (kI16 || a.power != 2.0f) ? 0 : -2 * esc;
 
     // 5. mel sums on 4x4x1 matrix blocks (16 per instruction): block (quad
     //    g, frame quad c / 4) of step s multiplies the power of 4 frames at
@@ -635,6 +651,10 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
 #pragma unroll
       for (int u = 0; u < kMelBatch; ++u) acc = __builtin_amdgcn_mfma_f32_4x4x1f32(pR[S][u], wR[S][u], acc, 0, 0, 0);
       if (!endR[S]) return;
+      if (!kI16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = __builtin_amdgcn_ldexpf(acc[i], mel_e);
+      }
       // block cb complete: log10, rescale, store, statistics
       uint32_t vminb = 0x7f800000u;   // +inf: no value
       if (a.mel_out) {   // uniform: mel values as they are, no statistics
@@ -712,13 +732,13 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
 // known at compile time), a 16-frame span that fits the wave's region and a
 // blocked filter table that fits its LDS share.
 bool pcm400_supported(const lm_plan *p, bool in_i16) {
-  if (p->n_fft != 400 || (p->hop & 1) || p->mfma400.empty() || p->n_mels > 256) return false;
+  (void)in_i16;   // both input types stage the same two fp16 planes
+  if (p->n_fft != 400 || (p->hop & 1) || p->mfma400h.empty() || p->n_mels > 256) return false;
   if (p->melblk_w.size() > (size_t)kMelWLds) return false;
   const int span = (kSub - 1) * p->hop + 400;
-  const int ndw = in_i16 ? span / 2 : span;
-  const int lds_dw = p->hop == 160 ? ndw + 4 * (ndw / (in_i16 ? 80 : 160)) : ndw;   // skewed layout at hop 160
-  if (in_i16) return lds_dw <= kLoff && kLoff + lds_dw <= kRegion;   // the two fp16 planes
-  return lds_dw + 4 <= kRegion;
+  const int ndw = span / 2;
+  const int lds_dw = p->hop == 160 ? ndw + 4 * (ndw / 80) : ndw;   // skewed layout at hop 160
+  return lds_dw <= kLoff && kLoff + lds_dw <= kRegion;
 }
 
 StatLayout pcm400_stat_layout(const lm_plan *p) {
@@ -747,10 +767,12 @@ hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &pa, hipStream_t s, con
   k.sig_pad = p->sig_pad;
   k.pad_mode = p->pad_mode;
   k.power = p->power;
-  // every power value is 4 |X|^2; int16 samples carry 2^15 per |X|, and
-  // their fp16 matrix another 2^12 / 64 = 2^6
-  // (the normalisation's factor on |X|^2 joins them)
-  const double in_scale2 = (pa.in_i16 ? 1.0 / 4398046511104.0 : 1.0) * power_scale2(p);   // 2^-42
+  // every power value is 4 |X|^2 times the fp16 matrix's 2^12 on the
+  // planes' sum squared: int16 planes hold x / 64 with x carrying 2^15, so
+  // 2^12 2^15 / 64 = 2^21 per |X|; float planes hold x 2^e, so 2^12 2^e,
+  // whose 2^e the kernel takes back per sub-tile (the normalisation's factor
+  // on |X|^2 joins them)
+  const double in_scale2 = (pa.in_i16 ? 1.0 / 4398046511104.0 : 1.0 / 16777216.0) * power_scale2(p);   // 2^-42, 2^-24
   if (p->power == 2.0f) {
     k.mel_scale = (float)(0.25 * in_scale2);
     k.pre_scale = 1.0f;
@@ -770,7 +792,7 @@ hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &pa, hipStream_t s, con
   k.tile_max = pa.tile_max;
   const dim3 grid((unsigned)n_wg), block(kThreads);
   const bool f16 = p->out_dtype == LM_F16;
-  const v4f *am = reinterpret_cast<const v4f *>(pa.in_i16 ? (const void *)p->dt.mfma400h : (const void *)p->dt.mfma400);
+  const v4f *am = reinterpret_cast<const v4f *>(p->dt.mfma400h);
   const int32_t *bm = p->dt.melblk_meta;
   const float *bw = p->dt.melblk_w;
   float *tmin = pa.tile_min;

@@ -106,9 +106,7 @@ void build_mfma400(lm_plan *p) {
   // (rows 12, 13) and the sums over even / odd n2 (rows 14, 15).  Class rows
   // are scaled by 2, so that every power value comes out as 4 |X|^2 like
   // the even/odd split's |2 S|^2.  Class k row: w[n] (cos, -sin)(2 pi k n / 400), n = n1 +
-  // 25 n2 (angles reduced exactly in integers).  Operand for step j, lane l:
-  // M_n1[l % 16][4 (l / 16) + j]; stored as [j][n1 / 4][lane][n1 % 4], zero
-  // for n1 >= 25.
+  // 25 n2 (angles reduced exactly in integers).
   static const int kA[4] = {1, 2, 3, 4}, kB[3] = {7, 6, 5};
   std::vector<double> win(400);
   for (int n = 0; n < 400; ++n) win[n] = window_at(p, n);
@@ -120,15 +118,10 @@ void build_mfma400(lm_plan *p) {
     const double th = 2.0 * M_PI * (double)(((long)k * n) % 400) / 400.0;
     return 2.0 * win[n] * ((sub & 1) == 0 ? std::cos(th) : -std::sin(th));
   };
-  p->mfma400.assign(4 * 7 * 64 * 4, 0.0f);
-  for (int n1 = 0; n1 < 25; ++n1)
-    for (int lane = 0; lane < 64; ++lane)
-      for (int j = 0; j < 4; ++j)
-        p->mfma400[(((size_t)j * 7 + n1 / 4) * 64 + lane) * 4 + n1 % 4] =
-            (float)entry(n1, lane % 16, 4 * (lane / 16) + j);
-  // fp16 form for int16 samples (v_mfma_f32_16x16x32_f16, two per n1): the
-  // samples enter as x / 64 = h + l / 64 with h = (x - (x mod 64)) / 64 and
-  // l = x mod 64, both exact in fp16, and the matrix, scaled by 2^12, as the
+  // Operands of v_mfma_f32_16x16x32_f16, two products per n1: the samples
+  // enter as two fp16 planes whose sum is x / 64 (int16: h = (x - (x mod
+  // 64)) / 64 and l = x mod 64, both exact) or x 2^e (float: nearest fp16 and
+  // nearest fp16 of the rest), and the matrix, scaled by 2^12, as the
   // sum of two fp16 parts (hi = nearest fp16, lo = nearest fp16 of the
   // rest), so that hi + lo carries about 22 bits.  Lane (m, g) holds
   // k-slots e < 8 standing for n2 = 4 (e / 2) + e % 2 + 2 (g % 2); lanes

@@ -564,13 +564,13 @@ def test_pcm400_paired_variant_options(in_dtype, out_dtype, pad_mode, power, mon
     check(out, ref, TOL32 if out_dtype == "f32" else TOL16, f"paired {in_dtype} {out_dtype} {pad_mode} {power}")
 
 
-def test_pcm400_int16_two_part_fp16_first_stage_precision():
-    """For int16 input the n_fft = 400 first stage runs on fp16 matrix cores,
-    but only as an exact two-part split of every sample (x/64 = h + l/64,
-    both exact in fp16) against a two-part (hi + lo) fp16 matrix, summed in
-    fp32.  Its error against the oracle must stay at the level of the fp32
-    path run on the same samples as float32, and far inside the gate, also
-    on clips with quiet passages and a floor that binds."""
+def test_pcm400_two_part_fp16_first_stage_precision():
+    """The n_fft = 400 first stage runs on fp16 matrix cores against a
+    two-part (hi + lo) fp16 matrix, summed in fp32.  int16 samples enter as
+    an exact two-part split (x/64 = h + l/64); float samples as the nearest
+    fp16 of x 2^e plus the nearest fp16 of the rest, with 2^e per sub-tile.
+    On the same samples both paths must sit far inside the gate, also on
+    clips with quiet passages, digital silence and a floor that binds."""
     B, T = 4, 48000
     x = lm_synth.speech_pcm(B, T, 16000.0, seed=31, as_int16=True)
     x[1, 16000:32000] = (x[1, 16000:32000].astype(np.int32) // 256).astype(np.int16)   # about -48 dB
@@ -578,8 +578,26 @@ def test_pcm400_int16_two_part_fp16_first_stage_precision():
     x[3, 20000:28000] = 0                                                              # digital silence
     xf = (x.astype(np.float32) / np.float32(32768.0)).astype(np.float32)               # the same samples
     ref = oracle_pcm(x, 400, 160, 128, 16000.0)
-    say("pcm400 int16 two-part fp16 first stage vs fp32 path")
-    e16 = check(run_pcm(x, 400, 160, 128, 16000.0), ref, TOL32, "int16 (two-part fp16 first stage)")
-    e32 = check(run_pcm(xf, 400, 160, 128, 16000.0), ref, TOL32, "f32 (fp32 first stage)")
-    print(f"[case] max |err| int16 path {e16:.3e}, f32 path {e32:.3e}", flush=True)
-    assert e16 <= max(2.0 * e32, 1e-5), (e16, e32)
+    say("pcm400 two-part fp16 first stage: int16 and float on the same samples")
+    e16 = check(run_pcm(x, 400, 160, 128, 16000.0), ref, TOL32, "int16 (exact two-part planes)")
+    e32 = check(run_pcm(xf, 400, 160, 128, 16000.0), ref, TOL32, "float (scaled two-part planes)")
+    print(f"[case] max |err| int16 path {e16:.3e}, float path {e32:.3e}", flush=True)
+    assert max(e16, e32) < 3e-5, (e16, e32)
+
+
+@pytest.mark.parametrize("scale", [3.7e-3, 1.0, 4096.0, 1.5e-9])
+def test_pcm400_float_input_any_amplitude(scale):
+    """Float input is scaled per sub-tile by a power of two chosen from its
+    largest sample, so the result does not depend on the input's overall
+    level (down to where the 1e-10 floor takes over), nor on a loud click
+    next to near-silence in the same sub-tile."""
+    B, T = 3, 40000
+    x = lm_synth.speech_pcm(B, T, 16000.0, seed=32).astype(np.float64)
+    x[1, 8000:16000] *= 1e-5                       # -100 dB passage
+    x[1, 12000] = 0.9                              # a click inside it
+    x[2, :] *= 1e-3
+    xs = (x * scale).astype(np.float32)
+    say("pcm400 float amplitude", scale)
+    out = run_pcm(xs, 400, 160, 80, 16000.0)
+    ref = oracle_pcm(xs, 400, 160, 80, 16000.0)
+    check(out, ref, TOL32, f"float input x {scale}")
