@@ -116,7 +116,7 @@ struct PcmKernelArgs {
   int64_t T, F;
   int tiles_per_clip;
   int hop, pad, pad_mode;   // pad: center padding plus the signal's zero padding
-  int64_t sig_pad;         // the signal's zero padding (zeros before and after each clip)
+  int sig_pad;             // the signal's zero padding (zeros before and after each clip)
   float power;          // exponent p; 2 takes the fast path
   float mel_scale;      // exact power-of-two scale of the mel sums
   float pre_scale;      // scale of |2X|^2 before a general power
@@ -380,6 +380,32 @@ constexpr int big_wlds() {
   return (160 * 1024 - (NFFT / 2 + (NFFT >> (kBigPad + 1))) * 8 - (NFFT / kTwLo + kTwLo) * 8 - 3 * 256 * 4 - 1024) / 4;
 }
 
+// A frame that reaches into the padding (the first and last few of a
+// clip), windowed into the FFT buffer with every sample by index
+// arithmetic, all loads of a thread in flight together.  Kept out of line:
+// inlined, its per-sample padding logic enlarged the frame loop and its
+// scalar register pressure for the few frames that take it.
+template <typename IN, int M, int THREADS>
+__device__ __attribute__((noinline)) void big_padded_frame(const IN *__restrict__ x, const float2 *__restrict__ win2,
+                                                           int64_t j0, int64_t T, int sig_pad, int pad_mode, int tid,
+                                                           float2 *buf) {
+  constexpr int IPT = M / THREADS;
+  float ys[IPT][2];
+  float2 ws[IPT];
+#pragma unroll
+  for (int u = 0; u < IPT; ++u) {
+    const int n = tid + u * THREADS;
+    const int64_t s0 = signal_source(j0 + 2 * n, T, sig_pad, pad_mode),
+                  s1 = signal_source(j0 + 2 * n + 1, T, sig_pad, pad_mode);
+    ys[u][0] = s0 >= 0 ? to_f(x[s0]) : 0.0f;
+    ys[u][1] = s1 >= 0 ? to_f(x[s1]) : 0.0f;
+    ws[u] = win2[n];
+  }
+#pragma unroll
+  for (int u = 0; u < IPT; ++u)
+    buf[lds_pos<kBigPad>(tid + u * THREADS)] = make_float2(ys[u][0] * ws[u].x, ys[u][1] * ws[u].y);
+}
+
 template <int NFFT, typename IN, typename OUT>
 __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS) pcm_big_kernel(PcmKernelArgs a, int64_t n_tiles) {
   constexpr int M = NFFT / 2;
@@ -445,24 +471,8 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS) pcm_big_kernel(PcmKerne
       for (int u = 0; u < IPT; ++u)
         s_buf[lds_pos<kBigPad>(tid + u * THREADS)] = make_float2(xs[u][0] * ws[u].x, xs[u][1] * ws[u].y);
     } else {
-      // frames that reach into the padding (the first and last few of a
-      // clip): each sample by index arithmetic, all loads in flight together
-      const IN *__restrict__ x = reinterpret_cast<const IN *>(a.pcm) + b * T;
-      const int64_t j0 = fr * a.hop - a.pad;
-      float ys[IPT][2];
-      float2 ws[IPT];
-#pragma unroll
-      for (int u = 0; u < IPT; ++u) {
-        const int n = tid + u * THREADS;
-        const int64_t s0 = signal_source(j0 + 2 * n, T, a.sig_pad, a.pad_mode),
-                      s1 = signal_source(j0 + 2 * n + 1, T, a.sig_pad, a.pad_mode);
-        ys[u][0] = s0 >= 0 ? to_f(x[s0]) : 0.0f;
-        ys[u][1] = s1 >= 0 ? to_f(x[s1]) : 0.0f;
-        ws[u] = win2[n];
-      }
-#pragma unroll
-      for (int u = 0; u < IPT; ++u)
-        s_buf[lds_pos<kBigPad>(tid + u * THREADS)] = make_float2(ys[u][0] * ws[u].x, ys[u][1] * ws[u].y);
+      big_padded_frame<IN, M, THREADS>(reinterpret_cast<const IN *>(a.pcm) + b * T, win2, fr * a.hop - a.pad, T,
+                                       a.sig_pad, a.pad_mode, tid, s_buf);
     }
     __syncthreads();
 
@@ -615,7 +625,7 @@ hipError_t launch_pcm(const lm_plan *p, const PcmArgs &a, hipStream_t s, const L
   k.tiles_per_clip = a.tiles_per_clip;
   k.hop = p->hop;
   k.pad = (p->center ? p->n_fft / 2 : 0) + (int)p->sig_pad;
-  k.sig_pad = p->sig_pad;
+  k.sig_pad = (int)p->sig_pad;
   k.pad_mode = p->pad_mode;
   k.power = p->power;
   // |2X|^2 = 4 |X|^2; int16 samples carry a 2^15 factor per |X|

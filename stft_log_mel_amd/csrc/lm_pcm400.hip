@@ -188,7 +188,7 @@ struct Args {
   int64_t n_sub;         // sub-tiles of the whole call
   int per_wg;            // sub-tiles per workgroup
   int hop, pad, pad_mode;   // pad: center padding plus the signal's zero padding
-  int64_t sig_pad;         // the signal's zero padding (zeros before and after each clip)
+  int sig_pad;             // the signal's zero padding (zeros before and after each clip)
   float power, pre_scale, mel_scale;
   int n_mels, n_melblk;
   int melw_n;            // mel step weight count (at most kMelWLds)
@@ -764,7 +764,7 @@ hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &pa, hipStream_t s, con
   k.per_wg = (int)((k.n_sub + n_wg - 1) / n_wg);
   k.hop = p->hop;
   k.pad = (p->center ? 200 : 0) + (int)p->sig_pad;
-  k.sig_pad = p->sig_pad;
+  k.sig_pad = (int)p->sig_pad;
   k.pad_mode = p->pad_mode;
   k.power = p->power;
   // every power value is 4 |X|^2 times the fp16 matrix's 2^12 on the
