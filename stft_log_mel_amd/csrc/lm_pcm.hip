@@ -33,15 +33,17 @@ template <int NFFT>
 struct PcmCfg;
 // FPB frames per tile, THREADS per workgroup, radix sequence of M = NFFT/2,
 // WLDS floats of LDS for staged filter weights (weights past that count
-// are read from global memory).
-template <> struct PcmCfg<400>   { static constexpr int FPB = 16,  THREADS = 256, WLDS = 4096; using Rad = Radices<8, 5, 5>; };
-template <> struct PcmCfg<64>    { static constexpr int FPB = 128, THREADS = 256, WLDS = 4096; using Rad = Radices<16, 2>; };
-template <> struct PcmCfg<128>   { static constexpr int FPB = 64,  THREADS = 256, WLDS = 4096; using Rad = Radices<16, 4>; };
-template <> struct PcmCfg<256>   { static constexpr int FPB = 32,  THREADS = 256, WLDS = 4096; using Rad = Radices<16, 8>; };
-template <> struct PcmCfg<512>   { static constexpr int FPB = 16,  THREADS = 256, WLDS = 4096; using Rad = Radices<16, 16>; };
-template <> struct PcmCfg<1024>  { static constexpr int FPB = 8,   THREADS = 256, WLDS = 4096; using Rad = Radices<8, 8, 8>; };
-template <> struct PcmCfg<2048>  { static constexpr int FPB = 4,   THREADS = 256, WLDS = 4096; using Rad = Radices<16, 16, 4>; };
-template <> struct PcmCfg<4096>  { static constexpr int FPB = 2,   THREADS = 256, WLDS = 4096; using Rad = Radices<16, 16, 8>; };
+// are read from global memory).  512 threads measured 7-27% faster than
+// 256 at every size (more waves to hide each pass's LDS round trips at the
+// same LDS per workgroup); 1024, or twice or half the frames, were slower.
+template <> struct PcmCfg<400>   { static constexpr int FPB = 16,  THREADS = 512, WLDS = 4096; using Rad = Radices<8, 5, 5>; };
+template <> struct PcmCfg<64>    { static constexpr int FPB = 128, THREADS = 512, WLDS = 4096; using Rad = Radices<16, 2>; };
+template <> struct PcmCfg<128>   { static constexpr int FPB = 64,  THREADS = 512, WLDS = 4096; using Rad = Radices<16, 4>; };
+template <> struct PcmCfg<256>   { static constexpr int FPB = 32,  THREADS = 512, WLDS = 4096; using Rad = Radices<16, 8>; };
+template <> struct PcmCfg<512>   { static constexpr int FPB = 16,  THREADS = 512, WLDS = 4096; using Rad = Radices<16, 16>; };
+template <> struct PcmCfg<1024>  { static constexpr int FPB = 8,   THREADS = 512, WLDS = 4096; using Rad = Radices<8, 8, 8>; };
+template <> struct PcmCfg<2048>  { static constexpr int FPB = 4,   THREADS = 512, WLDS = 4096; using Rad = Radices<16, 16, 4>; };
+template <> struct PcmCfg<4096>  { static constexpr int FPB = 2,   THREADS = 512, WLDS = 4096; using Rad = Radices<16, 16, 8>; };
 // n_fft 8192 and 16384 (one frame per tile) run in pcm_big_kernel below
 template <> struct PcmCfg<8192>  { static constexpr int FPB = 1; };
 template <> struct PcmCfg<16384> { static constexpr int FPB = 1; };
