@@ -369,7 +369,7 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
 // ---------------------------------------------------------------------------
 template <int NFFT>
 struct BigCfg;
-template <> struct BigCfg<8192>  { static constexpr int THREADS = 512;  using Rad = Radices<16, 16, 16>; };
+template <> struct BigCfg<8192>  { static constexpr int THREADS = 1024; using Rad = Radices<16, 16, 16>; };
 template <> struct BigCfg<16384> { static constexpr int THREADS = 1024; using Rad = Radices<16, 8, 8, 8>; };
 
 constexpr int kTwLo = 128;   // entries of the low twiddle table

@@ -18,8 +18,12 @@
 
 namespace lm {
 
-constexpr int kStftThreads = 256;
-constexpr int kStftNW = kStftThreads / 64;
+// Workgroup size: 256 threads, four resident per CU, when the call has at
+// least that many tiles (the streaming regime: 300 us at 256 threads
+// against 350 us at 512 on 256 clips); 512 threads when fewer tiles than
+// that (latency-bound: a one-clip call's kernel takes 7.5 us instead of
+// 10 us at 256).
+constexpr int kStftThreadsBig = 256, kStftThreadsSmall = 512;
 constexpr int kStftLoadUnroll = 8;
 constexpr int kStftWLds = 2048;     // LDS floats for the staged filter weights
 constexpr int kStftWgPerCu = 4;     // resident workgroups per compute unit
@@ -44,7 +48,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 // One tile: power of TF frames into P (LDS), then the mel sums, log10,
 // rescale, frame-major store and the tile's statistics.  `wsrc` + s_off[m]
 // is band m's first weight, in LDS or in global memory.
-template <typename OUT, bool VEC16>
+template <typename OUT, bool VEC16, int kStftThreads>
 __device__ __forceinline__ void stft_tile(const StftKernelArgs &a, int64_t tile, float *P, const float *wsrc,
                                           const int32_t *s_start, const int32_t *s_width, const int32_t *s_off,
                                           float *s_red) {
@@ -124,8 +128,9 @@ __device__ __forceinline__ void stft_tile(const StftKernelArgs &a, int64_t tile,
 
 // Persistent: each workgroup stages the filter rows once, then takes tiles
 // blockIdx.x, + gridDim.x, ...
-template <typename OUT, bool VEC16>
+template <typename OUT, bool VEC16, int kStftThreads>
 __global__ void __launch_bounds__(kStftThreads) stft_logmel_kernel(StftKernelArgs a) {
+  constexpr int kStftNW = kStftThreads / 64;
   extern __shared__ float s_dyn[];      // [TF*NF power tile][kStftWLds weights]
   __shared__ int32_t s_start[256], s_width[256], s_off[256];
   __shared__ int32_t s_scan[kStftNW];
@@ -183,10 +188,10 @@ __global__ void __launch_bounds__(kStftThreads) stft_logmel_kernel(StftKernelArg
   // one copy of the tile loop per weight source (see stft_tile)
   if (in_lds) {
     for (int64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x)
-      stft_tile<OUT, VEC16>(a, tile, P, s_w, s_start, s_width, s_off, s_red);
+      stft_tile<OUT, VEC16, kStftThreads>(a, tile, P, s_w, s_start, s_width, s_off, s_red);
   } else {
     for (int64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x)
-      stft_tile<OUT, VEC16>(a, tile, P, a.f_w, s_start, s_width, s_off, s_red);
+      stft_tile<OUT, VEC16, kStftThreads>(a, tile, P, a.f_w, s_start, s_width, s_off, s_red);
   }
 }
 
@@ -218,15 +223,28 @@ hipError_t launch_stft(const StftArgs &a, hipStream_t s, const LaunchTiming *tm)
   k.tile_max = a.tile_max;
   const size_t lds = sizeof(float) * ((size_t)a.frames_per_tile * a.n_bins + kStftWLds);
   const int64_t cap = (int64_t)a.n_cu * kStftWgPerCu;
-  const dim3 grid((unsigned)(k.n_tiles < cap ? k.n_tiles : cap)), block(kStftThreads);
+  const bool small = k.n_tiles < cap;
+  const dim3 grid((unsigned)(small ? k.n_tiles : cap)), block(small ? kStftThreadsSmall : kStftThreadsBig);
   const bool vec16 = (reinterpret_cast<uintptr_t>(a.stft) & 15) == 0;
-  if (a.out_f16) {
-    if (vec16) LM_LAUNCH(tm, (stft_logmel_kernel<__half, true>), grid, block, lds, s, k);
-    else LM_LAUNCH(tm, (stft_logmel_kernel<__half, false>), grid, block, lds, s, k);
+#define LM_STFT(OUT, V, T) LM_LAUNCH(tm, (stft_logmel_kernel<OUT, V, T>), grid, block, lds, s, k)
+  if (small) {
+    if (a.out_f16) {
+      if (vec16) LM_STFT(__half, true, kStftThreadsSmall);
+      else LM_STFT(__half, false, kStftThreadsSmall);
+    } else {
+      if (vec16) LM_STFT(float, true, kStftThreadsSmall);
+      else LM_STFT(float, false, kStftThreadsSmall);
+    }
   } else {
-    if (vec16) LM_LAUNCH(tm, (stft_logmel_kernel<float, true>), grid, block, lds, s, k);
-    else LM_LAUNCH(tm, (stft_logmel_kernel<float, false>), grid, block, lds, s, k);
+    if (a.out_f16) {
+      if (vec16) LM_STFT(__half, true, kStftThreadsBig);
+      else LM_STFT(__half, false, kStftThreadsBig);
+    } else {
+      if (vec16) LM_STFT(float, true, kStftThreadsBig);
+      else LM_STFT(float, false, kStftThreadsBig);
+    }
   }
+#undef LM_STFT
   return hipGetLastError();
 }
 
