@@ -72,6 +72,32 @@ def test_stft_shapes(B, F, NF, NM):
     check(out, oracle.from_stft(s, W), TOL32, f"stft {B,F,NF,NM}")
 
 
+@pytest.mark.parametrize("B", [1, 12])
+def test_stft_caller_filterbank_row_spans(B):
+    """A caller's dense filterbank with an all-zero row, a row whose only
+    weight is the last bin, a row with interior zeros and negative weights
+    (the row-span kernel keeps each row's first to last non-zero weight).
+    One clip runs the 512-thread small-call form of the STFT kernel, 12
+    clips of 3000 frames the 256-thread streaming form."""
+    F, NF, NM = 3000, 201, 80
+    say("stft caller filterbank row spans", B)
+    s = lm_synth.stft_speechlike(B, F, NF, seed=60 + B)
+    W = lm_synth.lintri_filters(NF, NM).astype(np.float32)
+    W[3] = 0.0                                   # no weight at all
+    W[5] = 0.0
+    W[5, NF - 1] = 0.7                           # only the last bin
+    W[9, 20:40] = 0.25
+    W[9, 25:33] = 0.0                            # interior zeros
+    W[11, 50:60] = -0.1                          # negative weights inside the row
+    W[11, 55] = 0.9
+    out = lm().log_mel_spectrogram(to_dev(s), to_dev(W))
+    torch.cuda.synchronize()
+    mel = oracle.mel_from_stft(s, W)
+    ok = np.all(mel > 0, axis=(0, 1))            # log of a non-positive sum: floored on both sides
+    check(out, oracle.from_stft(s, W), TOL32, f"stft filter rows B={B}")
+    assert not ok[3] and ok[5]
+
+
 def test_stft_full_size_large_batch():
     w = lm_synth.WORKLOADS["stft_b256"]
     say("stft full size", w.B, w.F, w.NF, w.NM)
@@ -335,6 +361,32 @@ def test_pcm_signal_pad(n_fft, hop, T, pad, center, pad_mode, in_dtype):
                           pad_mode=pad_mode, pad=pad)
     assert tuple(out.shape) == ref.shape
     check(out, ref, TOL32, f"signal pad {n_fft} {pad} {pad_mode}")
+
+
+def test_calls_follow_the_current_stream():
+    """The library enqueues on torch's current stream: input produced and
+    output consumed on a side stream (default priority), with the default
+    stream busy meanwhile, still gives the oracle's result; a second call
+    into the same output on that stream replaces every value (empty bands
+    included, which only the fix-up writes)."""
+    sr = 16000.0
+    xa = lm_synth.speech_pcm(2, 24000, sr, seed=95)
+    xb = lm_synth.speech_pcm(2, 24000, sr, seed=96)
+    p = lm().Plan(256, 64, 128).set_mel(sr)       # n_fft 256 / 128 mels: has empty bands
+    side = torch.cuda.Stream()
+    say("side-stream ordering")
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        busy = torch.randn(2048, 2048, device=dev())
+        da = torch.from_numpy(xa).to(dev(), non_blocking=False)
+        db = torch.from_numpy(xb).to(dev(), non_blocking=False)
+        out = p.from_pcm(da)
+        for _ in range(4):
+            busy = (busy @ busy) * 1e-3                 # the side stream kept busy between the calls
+        out = p.from_pcm(db, out=out)
+        res = out.clone()
+    side.synchronize()
+    check(res, oracle.from_pcm(xb, 256, 64, oracle.mel_filterbank(sr, 256, 128)), TOL32, "side stream")
 
 
 def test_melspectrogram_wrapper_pad():
