@@ -616,6 +616,86 @@ def test_pcm400_paired_variant_options(in_dtype, out_dtype, pad_mode, power, mon
     check(out, ref, TOL32 if out_dtype == "f32" else TOL16, f"paired {in_dtype} {out_dtype} {pad_mode} {power}")
 
 
+def _random_pcm_config(rng):
+    """One draw of the torchaudio-style surface: n_fft, hop, center, pad
+    mode, power, input and output types, window length, normalisation,
+    signal padding, mel count, range, scale and norm."""
+    n_fft = int(rng.choice([64, 128, 256, 400, 400, 512, 1024, 2048, 4096, 8192]))
+    win = n_fft if rng.random() < 0.6 else int(rng.integers(max(1, n_fft // 3), n_fft + 1))
+    hop = int(rng.choice([160, 160, 100, 161])) if n_fft == 400 else max(1, int(win // rng.choice([2, 3, 4])))
+    sr = float(rng.choice([8000.0, 16000.0, 22050.0]))
+    f_max = sr / 2 if rng.random() < 0.7 else float(sr / 2 * rng.uniform(0.5, 1.0))
+    return dict(n_fft=n_fft, hop=hop, win=win, sr=sr, f_min=float(rng.choice([0.0, 20.0, 60.0])), f_max=f_max,
+                n_mels=int(rng.choice([16, 40, 80, 128])), center=bool(rng.random() < 0.8),
+                pad_mode=str(rng.choice(["reflect", "constant", "replicate", "circular"])),
+                power=float(rng.choice([2.0, 2.0, 1.0, 1.5])), in_dtype=str(rng.choice(["f32", "i16"])),
+                out_dtype=str(rng.choice(["f32", "f32", "f16"])), normalized=rng.choice([None, None, "window", "frame_length"]),
+                sig_pad=int(rng.choice([0, 0, 0, 7, 64])), scale=str(rng.choice(["slaney", "htk"])),
+                norm=rng.choice(["slaney", None]), output=str(rng.choice(["logmel", "logmel", "mel"])))
+
+
+@pytest.mark.parametrize("draw", range(32))
+def test_pcm_random_configurations(draw):
+    """Seeded random draws over the whole PCM surface at small sizes (2 clips,
+    a ragged length), each against the oracle."""
+    rng = np.random.default_rng(1000 + draw)
+    c = _random_pcm_config(rng)
+    if c["output"] == "mel":
+        c["out_dtype"] = "f32"      # raw mel values of any level would leave fp16's range
+    T = int(max(3 * c["n_fft"], 5000) + rng.integers(0, 997))
+    say("pcm random", draw, c, T)
+    x = lm_synth.speech_pcm(2, T, c["sr"], seed=2000 + draw, as_int16=(c["in_dtype"] == "i16"))
+    if c["in_dtype"] == "f32":
+        x = (x * np.float32(rng.choice([1.0, 0.01, 30.0]))).astype(np.float32)
+    p = (lm().Plan(c["n_fft"], c["hop"], c["n_mels"], c["center"], c["pad_mode"], c["power"], c["out_dtype"])
+         .set_mel(c["sr"], c["f_min"], c["f_max"], c["scale"], c["norm"]).set_window(c["win"])
+         .set_pad(c["sig_pad"]).set_output(c["output"], c["normalized"]))
+    out = p.from_pcm(to_dev(x))
+    torch.cuda.synchronize()
+    W = oracle.mel_filterbank(c["sr"], c["n_fft"], c["n_mels"], c["f_min"], c["f_max"], scale=c["scale"], norm=c["norm"])
+    kw = dict(center=c["center"], pad_mode=c["pad_mode"], power=c["power"], win_length=c["win"],
+              normalized=c["normalized"], pad=c["sig_pad"])
+    if c["output"] == "mel":
+        check_mel(out, oracle.mel_from_pcm(x, c["n_fft"], c["hop"], W, **kw), 1e-4, f"random {draw}")
+    else:
+        check(out, oracle.from_pcm(x, c["n_fft"], c["hop"], W, **kw), TOL32 if c["out_dtype"] == "f32" else TOL16,
+              f"random {draw}")
+
+
+@pytest.mark.parametrize("draw", range(12))
+def test_stft_random_configurations(draw):
+    """Seeded random draws over the STFT entry: batch, frames, bins, bands,
+    the caller's dense filterbank or the plan's own, output type and kind."""
+    rng = np.random.default_rng(3000 + draw)
+    B, F = int(rng.integers(1, 6)), int(rng.integers(1, 700))
+    NF = int(rng.choice([65, 129, 201, 257, 401, 513]))
+    NM = int(rng.choice([8, 40, 80, 128, 200]))
+    out_dtype = str(rng.choice(["f32", "f16"]))
+    output = str(rng.choice(["logmel", "logmel", "mel"]))
+    if output == "mel":
+        out_dtype = "f32"
+    own = rng.random() < 0.4
+    say("stft random", draw, B, F, NF, NM, out_dtype, output, "plan filters" if own else "caller filters")
+    s = lm_synth.stft_speechlike(B, F, NF, seed=4000 + draw)
+    if own:
+        n_fft = 2 * (NF - 1)
+        if n_fft not in (64, 128, 256, 512, 1024):
+            n_fft, NF = 256, 129
+            s = lm_synth.stft_speechlike(B, F, NF, seed=4000 + draw)
+        p = lm().Plan(n_fft, n_fft // 4, NM, out_dtype=out_dtype).set_mel(16000.0).set_output(output)
+        W = p.get_filters().astype(np.float64)
+        out = p.from_stft(to_dev(s))
+    else:
+        W = lm_synth.lintri_filters(NF, NM)
+        p = lm().Plan(400, 160, NM, out_dtype=out_dtype).set_output(output)
+        out = p.from_stft(to_dev(s), to_dev(W))
+    torch.cuda.synchronize()
+    if output == "mel":
+        check_mel(out, oracle.mel_from_stft(s, W), 1e-4, f"stft random {draw}")
+    else:
+        check(out, oracle.from_stft(s, W), TOL32 if out_dtype == "f32" else TOL16, f"stft random {draw}")
+
+
 def test_pcm400_two_part_fp16_first_stage_precision():
     """The n_fft = 400 first stage runs on fp16 matrix cores against a
     two-part (hi + lo) fp16 matrix, summed in fp32.  int16 samples enter as
