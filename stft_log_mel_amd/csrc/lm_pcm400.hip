@@ -606,6 +606,11 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
     // float input at power 2: the mel sums carry 2^2e (exact power of two)
     const int mel_e = (kI16 || a.power != 2.0f) ? 0 : -2 * esc;
 
+    // the next sub-tile's samples have arrived by now (their loads went out
+    // before this sub-tile's first stage): retiring the registers here,
+    // before this sub-tile's stores, spares the next staging a wait for them
+#pragma unroll
+    for (int i = 0; i < Prefetch<IN>::N; ++i) asm volatile("" ::"v"(pf.v[i]));
     // 5. mel sums on 4x4x1 matrix blocks (16 per instruction): block (quad
     //    g, frame quad c / 4) of step s multiplies the power of 4 frames at
     //    bin qs_g + s by the weights of the 4 bands of quad 4 jb + g there,
