@@ -33,6 +33,9 @@ constexpr int kPcm400Row = 213;
 // Chunks of 4 bins the n_fft = 400 mel loop takes per step; every band
 // block's chunk count is a multiple of it.
 constexpr int kMelBatch = 4;
+// Accelerator complex dies (XCDs) of the chip, each with its own L2;
+// consecutive workgroup ids are handed to them in turn.
+constexpr int kXcds = 8;
 
 // Set the thread-local error text and return `status`.
 int fail(int status, const std::string &msg);

@@ -452,10 +452,18 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS) pcm_big_kernel(PcmKerne
     const int64_t j0 = fr * a.hop - a.pad;
     return j0 >= 0 && j0 + NFFT <= T;
   };
-  bool have = blockIdx.x < n_tiles && interior(blockIdx.x);
-  if (have) load_interior(blockIdx.x, threadIdx.x);
+  // Neighbouring frames share n_fft - hop samples (three quarters at hop
+  // n_fft/4).  Workgroups go to the chip's 8 XCDs in turn and each XCD has
+  // its own L2, so tiles are dealt such that the workgroups of one XCD take
+  // consecutive frames in each round: the shared samples then come from
+  // that XCD's L2 instead of once more from HBM per XCD.
+  const int G = gridDim.x;
+  const int first = G % kXcds == 0 ? (int)(blockIdx.x % kXcds) * (G / kXcds) + (int)(blockIdx.x / kXcds)
+                                   : (int)blockIdx.x;
+  bool have = first < n_tiles && interior(first);
+  if (have) load_interior(first, threadIdx.x);
 
-  for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+  for (int64_t tile = first; tile < n_tiles; tile += G) {
     // the window pointer and the thread index are made opaque per frame so
     // that per-thread addresses are not kept live across the whole loop
     const float2 *win2 = reinterpret_cast<const float2 *>(a.window);
@@ -516,7 +524,7 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS) pcm_big_kernel(PcmKerne
     }
 
     // the next frame's samples, in flight during the mel sums
-    const int64_t nxt = tile + gridDim.x;
+    const int64_t nxt = tile + G;
     have = nxt < n_tiles && interior(nxt);
     if (have) load_interior(nxt, tid);
 
