@@ -145,6 +145,21 @@ constexpr float kW400_1c = 0.99987663248166059f, kW400_1s = -0.01570731731182067
 // one 400-point complex sequence z = y_a + i y_b, transformed by radix
 // 16/5/5 passes and split as 2 X_a[k] = Z[k] + Z*[400-k], 2 X_b[k] =
 // -i (Z[k] - Z*[400-k]).
+// Tile of workgroup id b in a grid of n workgroups, one tile each.
+// Neighbouring tiles share n_fft - hop input samples, and workgroup ids go
+// to the chip's XCDs (each with its own L2) in turn, so every run of
+// kXcds * K ids is dealt such that each XCD takes K consecutive tiles and
+// the shared samples come from its L2; ids past the last whole run keep
+// their own tile.  A permutation of [0, n).
+template <int K>
+__device__ __forceinline__ int64_t xcd_dealt_tile(int64_t b, int64_t n) {
+  constexpr int64_t C = (int64_t)kXcds * K;
+  if (b >= n / C * C) return b;
+  const int64_t c = b / C;
+  const int r = (int)(b - c * C);
+  return c * C + (int64_t)(r % kXcds) * K + r / kXcds;
+}
+
 template <int NFFT, typename IN, typename OUT, bool PAIRED = false>
 __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKernelArgs a) {
   static_assert(!PAIRED || NFFT == 400, "the paired transform is built for n_fft = 400");
@@ -160,7 +175,7 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
   __shared__ float s_red[2 * NW];
 
   const int tid = threadIdx.x;
-  const int64_t tile = blockIdx.x;
+  const int64_t tile = xcd_dealt_tile<32>(blockIdx.x, gridDim.x);
   const int64_t b = tile / a.tiles_per_clip;
   const int t = (int)(tile - b * a.tiles_per_clip);
   const int64_t f0 = (int64_t)t * FPB;
