@@ -40,11 +40,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def main_kernel_name(w) -> str:
+def main_kernel_name(w, fft_variant: str = "auto") -> str:
     """The kernel lm_from_* launches for this workload (the library's own dispatch rule)."""
     if w.entry == "stft":
         return "stft_logmel_kernel"
-    if w.n_fft == 400 and w.hop % 2 == 0 and not os.environ.get("LM_FORCE_GENERIC"):
+    if w.n_fft == 400 and w.hop % 2 == 0 and fft_variant == "auto":
         return "pcm400_kernel"
     if w.n_fft >= 8192:
         return "pcm_big_kernel"

@@ -24,14 +24,19 @@
  *    The caller owns them.  Inputs are only read; outputs must not alias
  *    inputs.  Arrays are dense and row-major (C order).
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
- *    The lm_from_* calls only enqueue work on it; they never synchronise
- *    with the host, except the first call on a plan (or the first after
- *    its filters change), which uploads the plan's tables with a blocking
- *    copy.
+ *    The lm_from_* calls only enqueue work on it and never wait for the
+ *    device: the plan's tables go up with an asynchronous copy from
+ *    plan-owned pinned host memory, and device tables and workspace are
+ *    allocated, grown (by doubling) and retired in stream order
+ *    (hipMallocAsync / hipFreeAsync on the call's stream).
  *  - A plan binds to the device current at its first lm_from_* call and
- *    must only be used on that device, by one stream at a time (its
- *    workspace is shared between calls).  Do not change or destroy a plan
- *    while work that uses it is in flight.
+ *    must only be used on that device.  It may be used from several
+ *    streams: a call on a stream other than the previous call's makes its
+ *    stream wait (an event) for everything the previous call enqueued, so
+ *    the GPU work of one plan always runs in call order and its shared
+ *    workspace is never used by two calls at once.  Host calls on one plan
+ *    must not run concurrently on several threads.  Do not change or
+ *    destroy a plan while work that uses it is in flight.
  */
 #ifndef LM_H
 #define LM_H
@@ -234,6 +239,26 @@ int lm_from_stft(lm_plan *plan, const void *stft, const float *mel_filters, int6
  */
 int lm_plan_profile(lm_plan *plan, int enable);
 int lm_plan_profile_read(lm_plan *plan, double *ms, int64_t *counts);
+
+/* FFT variants of the n_fft = 400 PCM path (lm_plan_set_fft_variant). */
+enum { LM_FFT_AUTO = 0, LM_FFT_FOLDED = 1, LM_FFT_PAIRED = 2 };
+
+/*
+ * lm_plan_set_fft_variant -- which transform the n_fft = 400 PCM path runs,
+ * for measurement and comparison only (flashmel page, "Performance": the
+ * normal, folded and paired real-input transforms it compared).
+ *
+ *  LM_FFT_AUTO    (the default) the 16 x 25 split with its 16-point stage on
+ *                 the matrix cores wherever it applies (even hop), else the
+ *                 folded form.
+ *  LM_FFT_FOLDED  each frame as a 200-point complex sequence (radix 8, 5, 5),
+ *                 then split into the real spectrum.
+ *  LM_FFT_PAIRED  two frames as one 400-point complex sequence, separated by
+ *                 conjugate symmetry.
+ * Results agree within the same tolerance on every variant.  Other n_fft
+ * ignore the setting.  Host-only.  LM_ERR_INVALID_ARG for an unknown value.
+ */
+int lm_plan_set_fft_variant(lm_plan *plan, int variant);
 
 /* lm_plan_destroy -- free the plan and its device memory (NULL is a no-op). */
 void lm_plan_destroy(lm_plan *plan);

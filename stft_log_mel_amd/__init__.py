@@ -43,6 +43,7 @@ _SCALE = {"slaney": 0, "htk": 1}
 _NORM = {"slaney": 0, None: 1, "none": 1}
 _OUTPUT = {"logmel": 0, "mel": 1}
 _NORMALIZED = {None: 0, False: 0, "none": 0, True: 1, "window": 1, "frame_length": 2}
+_FFT_VARIANT = {"auto": 0, "folded": 1, "paired": 2}
 
 # Exported symbols and their C signatures (include/lm.h).
 _c_int, _c_i64, _c_p, _c_f, _c_d = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_double
@@ -57,6 +58,7 @@ SIGNATURES = {
     "lm_plan_num_frames": (_c_i64, [_c_p, _c_i64]),
     "lm_from_pcm": (_c_int, [_c_p, _c_p, _c_int, _c_i64, _c_i64, _c_p, _c_p]),
     "lm_from_stft": (_c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_int, _c_p, _c_p]),
+    "lm_plan_set_fft_variant": (_c_int, [_c_p, _c_int]),
     "lm_plan_profile": (_c_int, [_c_p, _c_int]),
     "lm_plan_profile_read": (_c_int, [_c_p, ctypes.POINTER(_c_d), ctypes.POINTER(_c_i64)]),
     "lm_plan_destroy": (None, [_c_p]),
@@ -163,6 +165,15 @@ class Plan:
     def set_pad(self, pad: int) -> "Plan":
         """Read each clip with pad zeros before and after it (torchaudio's pad)."""
         _check(_lib.lm_plan_set_pad(self._h, int(pad)))
+        return self
+
+    def set_fft_variant(self, variant: str = "auto") -> "Plan":
+        """n_fft = 400 transform, for comparisons: "auto" (the matrix-core
+        16 x 25 split where it applies), "folded" (200-point complex per
+        frame) or "paired" (two frames per 400-point complex transform)."""
+        if variant not in _FFT_VARIANT:
+            raise ValueError(f"variant must be one of {sorted(_FFT_VARIANT)}")
+        _check(_lib.lm_plan_set_fft_variant(self._h, _FFT_VARIANT[variant]))
         return self
 
     def get_filters(self) -> np.ndarray:

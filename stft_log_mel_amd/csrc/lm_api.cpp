@@ -26,7 +26,34 @@ int ensure_device(lm_plan *p) {
   return LM_OK;
 }
 
-int upload_tables(lm_plan *p) {
+// A pinned staging buffer of at least `bytes` whose previous copy (if any)
+// has finished, reusing the plan's own when possible.
+static int acquire_staging(lm_plan *p, size_t bytes, Staging **out) {
+  for (auto &st : p->staging)
+    if (st.bytes >= bytes && hipEventQuery(st.done) == hipSuccess) {
+      *out = &st;
+      return LM_OK;
+    }
+  Staging st;
+  hipError_t e = hipHostMalloc(&st.host, bytes, hipHostMallocDefault);
+  if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(table staging)");
+  st.bytes = bytes;
+  e = hipEventCreateWithFlags(&st.done, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    (void)hipHostFree(st.host);
+    return hip_fail(e, "hipEventCreate(table staging)");
+  }
+  p->staging.push_back(st);
+  *out = &p->staging.back();
+  return LM_OK;
+}
+
+// Device tables of the plan, refreshed after its host tables change.  The
+// image is assembled in pinned host memory and copied asynchronously into a
+// new stream-ordered allocation; the previous copy is released in stream
+// order behind the work already enqueued (every call on the plan is ordered
+// after the one before, see begin_call), so no call waits for the device.
+int upload_tables(lm_plan *p, hipStream_t s) {
   if (!p->tables_dirty && p->dt.base) return LM_OK;
   const int N = p->n_fft, M = N / 2, NM = p->n_mels;
   const int nnz = (int)p->csr.w.size();
@@ -48,37 +75,38 @@ int upload_tables(lm_plan *p) {
       if (p->csr.width[m] == 0) empty.push_back(m);
   size_t o_eb = align256(o_t2 + sizeof(float) * p->twid2.size());
   size_t total = align256(o_eb + sizeof(int32_t) * empty.size() + 16);
-  std::vector<unsigned char> host(total, 0);
-  std::memcpy(host.data() + o_win, p->window.data(), sizeof(float) * N);
-  std::memcpy(host.data() + o_tw, p->twiddle.data(), sizeof(float) * 2 * M);
-  std::memcpy(host.data() + o_ut, p->untangle.data(), sizeof(float) * 2 * (M / 2 + 1));
+  Staging *stg = nullptr;
+  int rc = acquire_staging(p, total, &stg);
+  if (rc != LM_OK) return rc;
+  unsigned char *host = static_cast<unsigned char *>(stg->host);
+  std::memset(host, 0, total);
+  std::memcpy(host + o_win, p->window.data(), sizeof(float) * N);
+  std::memcpy(host + o_tw, p->twiddle.data(), sizeof(float) * 2 * M);
+  std::memcpy(host + o_ut, p->untangle.data(), sizeof(float) * 2 * (M / 2 + 1));
   if (p->have_filters) {
-    std::memcpy(host.data() + o_st, p->csr.start.data(), sizeof(int32_t) * NM);
-    std::memcpy(host.data() + o_wd, p->csr.width.data(), sizeof(int32_t) * NM);
-    std::memcpy(host.data() + o_of, p->csr.off.data(), sizeof(int32_t) * NM);
-    if (nnz) std::memcpy(host.data() + o_w, p->csr.w.data(), sizeof(float) * nnz);
+    std::memcpy(host + o_st, p->csr.start.data(), sizeof(int32_t) * NM);
+    std::memcpy(host + o_wd, p->csr.width.data(), sizeof(int32_t) * NM);
+    std::memcpy(host + o_of, p->csr.off.data(), sizeof(int32_t) * NM);
+    if (nnz) std::memcpy(host + o_w, p->csr.w.data(), sizeof(float) * nnz);
   }
   if (!p->mfma400h.empty())
-    std::memcpy(host.data() + o_mh, p->mfma400h.data(), sizeof(uint16_t) * p->mfma400h.size());
+    std::memcpy(host + o_mh, p->mfma400h.data(), sizeof(uint16_t) * p->mfma400h.size());
   if (p->have_filters) {
-    std::memcpy(host.data() + o_bm, p->melblk_meta.data(), sizeof(int32_t) * p->melblk_meta.size());
-    std::memcpy(host.data() + o_bw, p->melblk_w.data(), sizeof(float) * p->melblk_w.size());
+    std::memcpy(host + o_bm, p->melblk_meta.data(), sizeof(int32_t) * p->melblk_meta.size());
+    std::memcpy(host + o_bw, p->melblk_w.data(), sizeof(float) * p->melblk_w.size());
   }
-  if (!p->twid2.empty()) std::memcpy(host.data() + o_t2, p->twid2.data(), sizeof(float) * p->twid2.size());
-  if (!empty.empty()) std::memcpy(host.data() + o_eb, empty.data(), sizeof(int32_t) * empty.size());
-  if (p->dt.base) {
-    hipError_t e = hipFree(p->dt.base);
-    p->dt.base = nullptr;
-    if (e != hipSuccess) return hip_fail(e, "hipFree(tables)");
-  }
+  if (!p->twid2.empty()) std::memcpy(host + o_t2, p->twid2.data(), sizeof(float) * p->twid2.size());
+  if (!empty.empty()) std::memcpy(host + o_eb, empty.data(), sizeof(int32_t) * empty.size());
   void *d = nullptr;
-  hipError_t e = hipMalloc(&d, total);
-  if (e != hipSuccess) return hip_fail(e, "hipMalloc(tables)");
-  e = hipMemcpy(d, host.data(), total, hipMemcpyHostToDevice);
+  hipError_t e = hipMallocAsync(&d, total, s);
+  if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(tables)");
+  e = hipMemcpyAsync(d, host, total, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipEventRecord(stg->done, s);
   if (e != hipSuccess) {
-    (void)hipFree(d);
-    return hip_fail(e, "hipMemcpy(tables)");
+    (void)hipFreeAsync(d, s);
+    return hip_fail(e, "hipMemcpyAsync(tables)");
   }
+  if (p->dt.base) (void)hipFreeAsync(p->dt.base, s);
   unsigned char *c = static_cast<unsigned char *>(d);
   p->dt.base = d;
   p->dt.bytes = total;
@@ -101,20 +129,51 @@ int upload_tables(lm_plan *p) {
   return LM_OK;
 }
 
-// Statistics workspace (minima, then maxima), grown on demand.  Every call
-// overwrites all of the entries it reads, so nothing needs clearing.
-int ensure_workspace(lm_plan *p, int64_t n_floats) {
-  if ((size_t)n_floats <= p->stats_cap) return LM_OK;
-  if (p->d_stats) {
-    hipError_t e = hipFree(p->d_stats);
-    p->d_stats = nullptr;
-    p->stats_cap = 0;
-    if (e != hipSuccess) return hip_fail(e, "hipFree(workspace)");
-  }
-  hipError_t e = hipMalloc(reinterpret_cast<void **>(&p->d_stats), sizeof(float) * n_floats);
-  if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
-  p->stats_cap = n_floats;
+// Grow a stream-ordered device buffer to at least `need` bytes (doubling),
+// releasing the old one in stream order behind the work already enqueued.
+static int grow(void **buf, size_t *cap, size_t need, hipStream_t s, const char *what) {
+  if (need <= *cap) return LM_OK;
+  const size_t bytes = std::max(need, 2 * *cap);
+  void *d = nullptr;
+  hipError_t e = hipMallocAsync(&d, bytes, s);
+  if (e != hipSuccess) return hip_fail(e, what);
+  if (*buf) (void)hipFreeAsync(*buf, s);
+  *buf = d;
+  *cap = bytes;
   return LM_OK;
+}
+
+// Statistics workspace (minima, then maxima).  Every call overwrites all of
+// the entries it reads, so nothing needs clearing.
+int ensure_workspace(lm_plan *p, int64_t n_floats, hipStream_t s) {
+  void *buf = p->d_stats;
+  size_t cap = p->stats_cap * sizeof(float);
+  const int rc = grow(&buf, &cap, sizeof(float) * (size_t)n_floats, s, "hipMallocAsync(workspace)");
+  p->d_stats = static_cast<float *>(buf);
+  p->stats_cap = cap / sizeof(float);
+  return rc;
+}
+
+int begin_call(lm_plan *p, hipStream_t s) {
+  int rc = ensure_device(p);
+  if (rc != LM_OK) return rc;
+  if (!p->done_event) {
+    hipError_t e = hipEventCreateWithFlags(&p->done_event, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+  }
+  if (p->has_last && p->last_stream != static_cast<void *>(s)) {
+    hipError_t e = hipStreamWaitEvent(s, p->done_event, 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  }
+  return LM_OK;
+}
+
+int end_call(lm_plan *p, hipStream_t s, int rc) {
+  hipError_t e = hipEventRecord(p->done_event, s);
+  if (e != hipSuccess) return rc != LM_OK ? rc : hip_fail(e, "hipEventRecord");
+  p->last_stream = static_cast<void *>(s);
+  p->has_last = true;
+  return rc;
 }
 
 // Launch through `fn(tm)`; when profiling, tm carries two new events that
@@ -142,6 +201,57 @@ static int timed_launch(lm_plan *p, hipStream_t s, int kind, const char *what, F
   }
   p->prof.push_back(ProfileRec{tm.beg, tm.end, kind});
   return LM_OK;
+}
+
+// The PCM launch sequence (main kernel, then the clamp fix-up) with the
+// statistics workspace at `ws` (n_clips * tiles * (minima + maxima) floats).
+int run_pcm(lm_plan *p, const void *pcm, bool in_i16, int64_t n_clips, int64_t n_samples, int64_t F, int tiles,
+            const StatLayout &st, void *out, float *ws, hipStream_t s) {
+  float *tmin = ws, *tmax = ws + n_clips * tiles * st.min_per_tile();
+  PcmArgs a{pcm, in_i16, n_clips, n_samples, F, tiles, out, tmin, tmax};
+  int rc = timed_launch(p, s, 0, "launch(pcm kernel)", [&](const LaunchTiming *tm) { return launch_pcm(p, a, s, tm); });
+  if (rc != LM_OK) return rc;
+  if (p->output == LM_OUTPUT_MEL) return LM_OK;   // no per-clip tail
+  FixupArgs fx{out, p->out_dtype == LM_F16, tmin, tmax, n_clips, F, p->n_mels, tiles, st, 1};
+  if (pcm_skips_empty_bands(p, in_i16)) {
+    fx.empty_bands = p->dt.empty_bands;
+    fx.n_empty = p->dt.n_empty;
+  }
+  return timed_launch(p, s, 1, "launch(clamp fix-up)", [&](const LaunchTiming *tm) { return launch_fixup(fx, s, tm); });
+}
+
+// The STFT launch sequence: row spans of a device filterbank (if given),
+// main kernel, clamp fix-up.  Uses the plan's workspace and pack buffer.
+static int run_stft(lm_plan *p, const void *stft, const float *mel_filters, int64_t n_clips, int64_t n_frames,
+                    int n_bins, int n_mels, int tf, int tiles, void *out, hipStream_t s) {
+  float *tmin = p->d_stats, *tmax = p->d_stats + n_clips * tiles;
+  StftArgs a{reinterpret_cast<const float2 *>(stft), n_clips, n_frames, n_bins, n_mels, tf, tiles,
+             nullptr, nullptr, nullptr, nullptr, 0, out, p->out_dtype == LM_F16, tmin, tmax, p->n_cu,
+             p->output == LM_OUTPUT_MEL};
+  int rc = LM_OK;
+  if (mel_filters) {
+    int32_t *sw = reinterpret_cast<int32_t *>(p->d_pack);
+    rc = timed_launch(p, s, 2, "launch(filter rows)",
+                      [&](const LaunchTiming *tm) { return launch_pack(mel_filters, n_mels, n_bins, sw, s, tm); });
+    if (rc != LM_OK) return rc;
+    a.f_start = sw;
+    a.f_width = sw + n_mels;
+    a.f_w = mel_filters;
+    a.f_stride = n_bins;
+  } else {
+    a.f_start = p->dt.csr_start;
+    a.f_width = p->dt.csr_width;
+    a.f_off = p->dt.csr_off;
+    a.f_w = p->dt.csr_w;
+  }
+  rc = timed_launch(p, s, 0, "launch(stft kernel)", [&](const LaunchTiming *tm) { return launch_stft(a, s, tm); });
+  if (rc != LM_OK) return rc;
+  if (p->output == LM_OUTPUT_MEL) return LM_OK;   // no per-clip tail
+  StatLayout st;
+  st.frames_per_tile = tf;
+  st.band_h = n_mels;
+  FixupArgs fx{out, p->out_dtype == LM_F16, tmin, tmax, n_clips, n_frames, n_mels, tiles, st, 0};
+  return timed_launch(p, s, 1, "launch(clamp fix-up)", [&](const LaunchTiming *tm) { return launch_fixup(fx, s, tm); });
 }
 
 }  // namespace lm
@@ -172,28 +282,18 @@ int lm_from_pcm(lm_plan *p, const void *pcm, int in_dtype, int64_t n_clips, int6
     return fail(LM_ERR_INVALID_ARG, "misaligned pcm or out pointer");
   const int64_t F = lm_plan_num_frames(p, n_samples);
   if (F < 1) return (int)F;
-  int rc = ensure_device(p);
-  if (rc == LM_OK) rc = upload_tables(p);
-  if (rc != LM_OK) return rc;
   const StatLayout st = pcm_stat_layout(p, in_dtype == LM_I16);
   const int64_t tiles = (F + st.frames_per_tile - 1) / st.frames_per_tile;
   if (tiles > INT32_MAX || n_clips * tiles > INT32_MAX) return fail(LM_ERR_UNSUPPORTED, "input too large");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int rc = begin_call(p, s);
+  if (rc != LM_OK) return rc;
+  rc = upload_tables(p, s);
   const int64_t n_min = n_clips * tiles * st.min_per_tile(), n_max = n_clips * tiles * st.max_per_tile;
-  rc = ensure_workspace(p, n_min + n_max);
-  if (rc != LM_OK) return rc;
-  float *tmin = p->d_stats, *tmax = p->d_stats + n_min;
-
-  PcmArgs a{pcm, in_dtype == LM_I16, n_clips, n_samples, F, (int)tiles, out, tmin, tmax};
-  rc = timed_launch(p, s, 0, "launch(pcm kernel)", [&](const LaunchTiming *tm) { return launch_pcm(p, a, s, tm); });
-  if (rc != LM_OK) return rc;
-  if (p->output == LM_OUTPUT_MEL) return LM_OK;   // no per-clip tail
-  FixupArgs fx{out, p->out_dtype == LM_F16, tmin, tmax, n_clips, F, p->n_mels, (int)tiles, st, 1};
-  if (pcm_skips_empty_bands(p, in_dtype == LM_I16)) {
-    fx.empty_bands = p->dt.empty_bands;
-    fx.n_empty = p->dt.n_empty;
-  }
-  return timed_launch(p, s, 1, "launch(clamp fix-up)", [&](const LaunchTiming *tm) { return launch_fixup(fx, s, tm); });
+  if (rc == LM_OK) rc = ensure_workspace(p, n_min + n_max, s);
+  if (rc == LM_OK) rc = run_pcm(p, pcm, in_dtype == LM_I16, n_clips, n_samples, F, (int)tiles, st, out,
+                                p->d_stats, s);
+  return end_call(p, s, rc);
 }
 
 int lm_from_stft(lm_plan *p, const void *stft, const float *mel_filters, int64_t n_clips, int64_t n_frames,
@@ -218,50 +318,13 @@ int lm_from_stft(lm_plan *p, const void *stft, const float *mel_filters, int64_t
   const int64_t tiles = (n_frames + tf - 1) / tf;
   if (tiles > INT32_MAX || n_clips * tiles > INT32_MAX) return fail(LM_ERR_UNSUPPORTED, "input too large");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  int rc = ensure_device(p);
-  if (rc == LM_OK && !mel_filters) rc = upload_tables(p);
-  if (rc == LM_OK) rc = ensure_workspace(p, 2 * n_clips * tiles);
+  int rc = begin_call(p, s);
   if (rc != LM_OK) return rc;
-  float *tmin = p->d_stats, *tmax = p->d_stats + n_clips * tiles;
-
-  StftArgs a{reinterpret_cast<const float2 *>(stft), n_clips, n_frames, (int)n_bins, n_mels, tf, (int)tiles,
-             nullptr, nullptr, nullptr, nullptr, 0, out, p->out_dtype == LM_F16, tmin, tmax, p->n_cu,
-             p->output == LM_OUTPUT_MEL};
-  if (mel_filters) {
-    const size_t need = sizeof(int32_t) * 2 * n_mels;
-    if (need > p->pack_cap) {
-      if (p->d_pack) {
-        hipError_t e = hipFree(p->d_pack);
-        p->d_pack = nullptr;
-        p->pack_cap = 0;
-        if (e != hipSuccess) return hip_fail(e, "hipFree(pack)");
-      }
-      hipError_t e = hipMalloc(&p->d_pack, need);
-      if (e != hipSuccess) return hip_fail(e, "hipMalloc(pack)");
-      p->pack_cap = need;
-    }
-    int32_t *sw = reinterpret_cast<int32_t *>(p->d_pack);
-    rc = timed_launch(p, s, 2, "launch(filter rows)",
-                      [&](const LaunchTiming *tm) { return launch_pack(mel_filters, n_mels, (int)n_bins, sw, s, tm); });
-    if (rc != LM_OK) return rc;
-    a.f_start = sw;
-    a.f_width = sw + n_mels;
-    a.f_w = mel_filters;
-    a.f_stride = (int)n_bins;
-  } else {
-    a.f_start = p->dt.csr_start;
-    a.f_width = p->dt.csr_width;
-    a.f_off = p->dt.csr_off;
-    a.f_w = p->dt.csr_w;
-  }
-  rc = timed_launch(p, s, 0, "launch(stft kernel)", [&](const LaunchTiming *tm) { return launch_stft(a, s, tm); });
-  if (rc != LM_OK) return rc;
-  if (p->output == LM_OUTPUT_MEL) return LM_OK;   // no per-clip tail
-  StatLayout st;
-  st.frames_per_tile = tf;
-  st.band_h = n_mels;
-  FixupArgs fx{out, p->out_dtype == LM_F16, tmin, tmax, n_clips, n_frames, n_mels, (int)tiles, st, 0};
-  return timed_launch(p, s, 1, "launch(clamp fix-up)", [&](const LaunchTiming *tm) { return launch_fixup(fx, s, tm); });
+  if (!mel_filters) rc = upload_tables(p, s);
+  if (rc == LM_OK) rc = ensure_workspace(p, 2 * n_clips * tiles, s);
+  if (mel_filters && rc == LM_OK) rc = grow(&p->d_pack, &p->pack_cap, sizeof(int32_t) * 2 * n_mels, s, "hipMallocAsync(pack)");
+  if (rc == LM_OK) rc = run_stft(p, stft, mel_filters, n_clips, n_frames, (int)n_bins, n_mels, tf, (int)tiles, out, s);
+  return end_call(p, s, rc);
 }
 
 int lm_plan_profile(lm_plan *p, int enable) {
@@ -302,7 +365,20 @@ void lm_plan_destroy(lm_plan *p) {
   if (p->dt.base) (void)hipFree(p->dt.base);
   if (p->d_stats) (void)hipFree(p->d_stats);
   if (p->d_pack) (void)hipFree(p->d_pack);
+  for (auto &st : p->staging) {
+    (void)hipEventSynchronize(st.done);
+    (void)hipEventDestroy(st.done);
+    (void)hipHostFree(st.host);
+  }
+  if (p->done_event) (void)hipEventDestroy(p->done_event);
   delete p;
+}
+
+int lm_plan_set_fft_variant(lm_plan *p, int variant) {
+  if (!p) return fail(LM_ERR_INVALID_ARG, "plan is NULL");
+  if (variant < LM_FFT_AUTO || variant > LM_FFT_PAIRED) return fail(LM_ERR_INVALID_ARG, "unknown FFT variant");
+  p->fft_variant = variant;
+  return LM_OK;
 }
 
 }  // extern "C"

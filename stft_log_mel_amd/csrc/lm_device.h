@@ -16,16 +16,19 @@ namespace lm {
 // log10 and the output map
 // ---------------------------------------------------------------------------
 
-// log10(v) for normal v > 0, via the hardware base-2 logarithm.  Every
-// kernel (the main passes and the clamp fix-up) uses this one function, so
-// the per-clip maximum maps to the largest output value exactly.
-__device__ __forceinline__ float log10_pos(float v) {
-  return __builtin_amdgcn_logf(v) * 0.301029995663981195f;
-}
+// log10(2) / 4
+constexpr float kLog10_2_Q = 0.0752574989159952988f;
 
-// (L + 4) / 4 written as one fma: scaling by 1/4 is exact, so
-// fma(L, 0.25, 1) rounds the same value as (L + 4) * 0.25.
-__device__ __forceinline__ float rescale(float L) { return __builtin_fmaf(L, 0.25f, 1.0f); }
+// The output value of a mel value v >= 1e-10 (after the floor):
+// (log10 v + 4) / 4, as one fma on the hardware base-2 logarithm.  Every
+// kernel writes exactly this value for every element, the region minima
+// the kernels record are minima of these values, and the clamp fix-up
+// takes the clip's largest output as logmel_of(largest mel value) -- the
+// same function of the same value -- and its floor as that minus 2, i.e.
+// ((hi - 8) + 4) / 4.
+__device__ __forceinline__ float logmel_of(float v) {
+  return __builtin_fmaf(__builtin_amdgcn_logf(v), kLog10_2_Q, 1.0f);
+}
 
 __device__ __forceinline__ void store_out(float *p, float v) { *p = v; }
 __device__ __forceinline__ void store_out(__half *p, float v) { *p = __float2half_rn(v); }
@@ -221,24 +224,24 @@ __device__ __forceinline__ float wave_min(float v) {
   return v;
 }
 
-// Block-wide max of vmax and min of lmin; the result is valid in thread 0.
+// Block-wide max of vmax and min of vmin; the result is valid in thread 0.
 // `red` must hold 2 * (blockDim.x / 64) floats of LDS.
 template <int THREADS>
-__device__ __forceinline__ void block_maxmin(float &vmax, float &lmin, float *red) {
+__device__ __forceinline__ void block_maxmin(float &vmax, float &vmin, float *red) {
   constexpr int NW = THREADS / 64;
   vmax = wave_max(vmax);
-  lmin = wave_min(lmin);
+  vmin = wave_min(vmin);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (lane == 0) {
     red[w] = vmax;
-    red[NW + w] = lmin;
+    red[NW + w] = vmin;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
 #pragma unroll
     for (int i = 1; i < NW; ++i) {
       vmax = fmaxf(vmax, red[i]);
-      lmin = fminf(lmin, red[NW + i]);
+      vmin = fminf(vmin, red[NW + i]);
     }
   }
 }

@@ -2,13 +2,15 @@
 // "spec_md": the floor is per clip, at the clip's largest log value minus
 // 8), applied after the main kernels have written (L + 4) / 4 everywhere.
 //
-// The main kernels record the largest mel value per tile and the smallest L
-// per region of a tile (a frame range times a band range).  Since (x + 4)/4
-// and the cast to the output type are both monotone, max(rescale(L),
-// rescale(hi - 8)) equals rescale(max(L, hi - 8)); so only regions whose
-// smallest L lies below hi - 8 are read, and only values below the floor
-// are rewritten.  hi is log10 of the largest mel value, with the same log10
-// the main kernels use, so the largest output is exactly (hi + 4) / 4.
+// The main kernels write o = logmel_of(v) for every mel value v (after the
+// 1e-10 floor) and record the largest v per tile and the smallest o per
+// region of a tile (a frame range times a band range).  The clip's largest
+// output is logmel_of(hi_v) for its largest mel value hi_v -- the same
+// function of the same value, so that element's output equals it exactly --
+// and its floor in output units is that minus 2, i.e. ((hi - 8) + 4) / 4.
+// Since the cast to the output type is monotone, max(cast(o), cast(floor))
+// equals cast(max(o, floor)); so only regions whose smallest o lies below
+// the floor are read, and only values below it are rewritten.
 //
 // fixup_group is one unit of that work, run by a whole workgroup of the
 // fix-up kernel (a second launch after the main kernel; its kernel boundary
@@ -44,8 +46,8 @@ inline void prepare_fixup(FixupArgs &a) {
   a.empty_units = a.n_empty > 0 ? (int)((a.n_frames + kFixValues - 1) / kFixValues) : 0;
 }
 
-// The clip's floor in log10 units, max over its maxima of hi, then log10
-// and minus 8; every thread of the workgroup must call it.
+// The clip's floor in output units: logmel_of(largest mel value) - 2;
+// every thread of the workgroup must call it.
 template <int THREADS>
 __device__ float clip_floor(const FixupArgs &a, int64_t b, float *s_red) {
   const int n_max = a.tiles_per_clip * a.st.max_per_tile;
@@ -57,29 +59,29 @@ __device__ float clip_floor(const FixupArgs &a, int64_t b, float *s_red) {
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < THREADS / 64; ++i) hi = fmaxf(hi, s_red[i]);
-  return log10_pos(fmaxf(hi, 1e-10f)) - 8.0f;
+  return logmel_of(fmaxf(hi, 1e-10f)) - 2.0f;
 }
 
 // Unit (clip b, empty band row e, segment r): the kFixValues frames from r
 // kFixValues on of band empty_bands[e], which the main kernel left
-// unwritten.  Their log value is log10(1e-10) (no weight, so the mel sum is
-// 0 before the 1e-10 floor), so the result is rescale(max(that, floor)),
-// written without reading.  Mel-major output only.
+// unwritten.  Their mel value is 1e-10 (no weight, so the sum is 0 before
+// the floor), so the result is max(logmel_of(1e-10), floor), written
+// without reading.  Mel-major output only.
 template <typename OUT, int THREADS>
 __device__ void fixup_empty_row(const FixupArgs &a, int64_t b, int e, int r, float *s_red) {
-  const float floorL = clip_floor<THREADS>(a, b, s_red);
-  const float v = rescale(fmaxf(log10_pos(1e-10f), floorL));
+  const float fl = clip_floor<THREADS>(a, b, s_red);
+  const float v = fmaxf(logmel_of(1e-10f), fl);
   const int64_t F = a.n_frames;
   OUT *row = reinterpret_cast<OUT *>(a.out) + (b * a.n_mels + a.empty_bands[e]) * F;
   const int64_t f1 = min(F, (int64_t)(r + 1) * kFixValues);
   for (int64_t f = (int64_t)r * kFixValues + threadIdx.x; f < f1; f += THREADS) store_out(row + f, v);
 }
 
-// Unit (clip b, group gi): reduce the clip's maxima to hi (every group of
-// the clip does this itself, so no cross-workgroup atomics or resets are
-// needed), list the regions of the group whose smallest log value lies
-// below hi - 8 (as their first frame and first band), then rewrite their
-// values below the floor with all threads.  LDS: s_f0[kFixEntries],
+// Unit (clip b, group gi): reduce the clip's maxima to its floor (every
+// group of the clip does this itself, so no cross-workgroup atomics or
+// resets are needed), list the regions of the group whose smallest output
+// lies below the floor (as their first frame and first band), then rewrite
+// their values below the floor with all threads.  LDS: s_f0[kFixEntries],
 // s_m0[kFixEntries], s_n[1], s_red[THREADS / 64].  Every thread of the
 // workgroup must call it; it ends with a barrier.
 template <typename OUT, int THREADS>
@@ -101,10 +103,10 @@ __device__ void fixup_group(const FixupArgs &a, int64_t b, int gi, int *s_f0, in
     const int e = e0 + tid + u * THREADS;
     mn[u] = e < e1 ? cmin[e] : __builtin_huge_valf();
   }
-  const float floorL = clip_floor<THREADS>(a, b, s_red);
+  const float fl = clip_floor<THREADS>(a, b, s_red);
 #pragma unroll
   for (int u = 0; u < MPT; ++u)
-    if (mn[u] < floorL) {
+    if (mn[u] < fl) {
       const int e = e0 + tid + u * THREADS;
       const int t = e / ept, rem = e - t * ept;
       const int sub = rem / st.blk_per_sub, blk = rem - sub * st.blk_per_sub;
@@ -115,7 +117,7 @@ __device__ void fixup_group(const FixupArgs &a, int64_t b, int gi, int *s_f0, in
   __syncthreads();
   const int n_flag = *s_n;
 
-  float fo = rescale(floorL);
+  float fo = fl;
   if (sizeof(OUT) == 2) fo = __half2float(__float2half_rn(fo));
   // rewrite: value k of the flattened list is value el of region i; el
   // splits into a run index o and the position in the run (contiguous in

@@ -77,6 +77,14 @@ struct ProfileRec {
   int kind;
 };
 
+// Pinned host buffer a table upload copies from; `done` is recorded after
+// the copy, so the buffer is reused only once that copy has finished.
+struct Staging {
+  void *host = nullptr;
+  size_t bytes = 0;
+  hipEvent_t done = nullptr;
+};
+
 }  // namespace lm
 
 struct lm_plan {
@@ -103,15 +111,21 @@ struct lm_plan {
   bool tables_dirty = true;
   lm::DeviceTables dt;
 
-  // workspace: per-region smallest log value and per-tile largest mel value
+  // workspace: per-region smallest output value and per-tile largest mel value
   float *d_stats = nullptr;       // [minima][maxima], laid out per call
   size_t stats_cap = 0;           // floats
   // per-call packed copy of a device filterbank (STFT path)
   void *d_pack = nullptr;
   size_t pack_cap = 0;
+  // pinned host buffers of the table uploads
+  std::vector<lm::Staging> staging;
+  // recorded on the stream of the last lm_from_* call after its last launch;
+  // a call on another stream first waits for it
+  hipEvent_t done_event = nullptr;
+  void *last_stream = nullptr;
+  bool has_last = false;
 
-  int force_generic = 0;         // LM_FORCE_GENERIC: 1 skips the n_fft = 400 matrix-core kernel for the folded
-                                 // generic one; "paired" (2) takes the paired 400-point variant (FFT comparison)
+  int fft_variant = LM_FFT_AUTO;   // lm_plan_set_fft_variant (n_fft = 400 only)
 
   bool profiling = false;
   std::vector<lm::ProfileRec> prof;
@@ -119,10 +133,20 @@ struct lm_plan {
 
 namespace lm {
 
-// Workspace helpers (lm_api.cpp)
+// Workspace helpers (lm_api.cpp).  Allocation, upload and release are
+// stream-ordered on `s`, the stream of the call that needs them.
 int ensure_device(lm_plan *p);
-int ensure_workspace(lm_plan *p, int64_t n_floats);
-int upload_tables(lm_plan *p);
+int ensure_workspace(lm_plan *p, int64_t n_floats, hipStream_t s);
+int upload_tables(lm_plan *p, hipStream_t s);
+// Start and end of an lm_from_* call's GPU work on stream s: order it after
+// the plan's previous call, then mark its end.
+int begin_call(lm_plan *p, hipStream_t s);
+int end_call(lm_plan *p, hipStream_t s, int rc);
+struct StatLayout;
+// The PCM launch sequence (main kernel, clamp fix-up) with its statistics
+// workspace at ws.
+int run_pcm(lm_plan *p, const void *pcm, bool in_i16, int64_t n_clips, int64_t n_samples, int64_t F, int tiles,
+            const StatLayout &st, void *out, float *ws, hipStream_t s);
 
 // Host table builders (lm_plan.cpp)
 double window_at(const lm_plan *p, int n);   // the frame window at n (float64)
@@ -137,10 +161,10 @@ Csr pack_dense(const float *dense, int n_rows, int n_bins);
 // Geometry of a main kernel's statistics for the clamp fix-up.  A tile is
 // frames_per_tile consecutive frames of one clip.  Per tile there are
 // sub_per_tile x blk_per_sub minimum entries: entry (sub, blk) holds the
-// smallest log value over frames [sub * frames_per_tile / sub_per_tile,
-// +frames_per_tile / sub_per_tile) of the tile and bands [blk * band_h,
-// (blk + 1) * band_h) (both clipped to the output), or +inf if that region
-// is empty; and max_per_tile maximum entries whose largest value is the
+// smallest output value (float32, before any cast to the output type)
+// over frames [sub * frames_per_tile / sub_per_tile, +frames_per_tile /
+// sub_per_tile) of the tile and bands [blk * band_h, (blk + 1) * band_h)
+// (both clipped to the output), or +inf if that region is empty; and max_per_tile maximum entries whose largest value is the
 // tile's largest mel value (after the 1e-10 floor).  Entries are stored
 // clip-major, tile-major.
 struct StatLayout {

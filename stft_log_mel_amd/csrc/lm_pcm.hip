@@ -329,7 +329,7 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
   }
 
   // 4. mel sums, log10, rescale, mel-major store
-  float vmax = 0.0f, lmin = __builtin_huge_valf();
+  float vmax = 0.0f, omin = __builtin_huge_valf();
   OUT *__restrict__ out = reinterpret_cast<OUT *>(a.out) + b * (int64_t)NM * F;
   // one copy of the loop per weight source, so LDS weights are read with LDS
   // instructions (a pointer that may point either way would make every
@@ -350,20 +350,20 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
         continue;
       }
       const float v = fmaxf(acc * a.mel_scale, 1e-10f);
-      const float L = log10_pos(v);
+      const float ov = logmel_of(v);
       vmax = fmaxf(vmax, v);
-      lmin = fminf(lmin, L);
-      store_out(out + (int64_t)m * F + fr, rescale(L));
+      omin = fminf(omin, ov);
+      store_out(out + (int64_t)m * F + fr, ov);
     }
   };
   if (w_in_lds) mel(s_w);
   else mel(a.csr_w);
 
   // 5. tile statistics
-  block_maxmin<THREADS>(vmax, lmin, s_red);
+  block_maxmin<THREADS>(vmax, omin, s_red);
   if (tid == 0) {
     a.tile_max[tile] = vmax;
-    a.tile_min[tile] = lmin;
+    a.tile_min[tile] = omin;
   }
 }
 
@@ -544,7 +544,7 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS) pcm_big_kernel(PcmKerne
     if (have) load_interior(nxt, tid);
 
     // 4. mel: L lanes per band
-    float vmax = 0.0f, lmin = __builtin_huge_valf();
+    float vmax = 0.0f, omin = __builtin_huge_valf();
     OUT *__restrict__ out = reinterpret_cast<OUT *>(a.out) + b * (int64_t)NM * F;
     const int h = tid & (L - 1);
     auto mel = [&](const float *wsrc) {
@@ -565,10 +565,10 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS) pcm_big_kernel(PcmKerne
           store_out(out + (int64_t)m * F + fr, acc * a.mel_scale);
         } else if (h == 0) {
           const float v = fmaxf(acc * a.mel_scale, 1e-10f);
-          const float Lg = log10_pos(v);
+          const float o = logmel_of(v);
           vmax = fmaxf(vmax, v);
-          lmin = fminf(lmin, Lg);
-          store_out(out + (int64_t)m * F + fr, rescale(Lg));
+          omin = fminf(omin, o);
+          store_out(out + (int64_t)m * F + fr, o);
         }
       }
     };
@@ -577,10 +577,10 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS) pcm_big_kernel(PcmKerne
 
     // 5. frame statistics; the barrier inside also keeps the next frame's
     //    samples out of the power tile until every band has read it
-    block_maxmin<THREADS>(vmax, lmin, s_red);
+    block_maxmin<THREADS>(vmax, omin, s_red);
     if (tid == 0) {
       a.tile_max[tile] = vmax;
-      a.tile_min[tile] = lmin;
+      a.tile_min[tile] = omin;
     }
     __syncthreads();
   }
@@ -627,7 +627,9 @@ static int generic_frames_per_tile(int n_fft) {
   }
 }
 
-static bool use_pcm400(const lm_plan *p, bool in_i16) { return !p->force_generic && pcm400_supported(p, in_i16); }
+static bool use_pcm400(const lm_plan *p, bool in_i16) {
+  return p->fft_variant == LM_FFT_AUTO && pcm400_supported(p, in_i16);
+}
 
 StatLayout pcm_stat_layout(const lm_plan *p, bool in_i16) {
   if (use_pcm400(p, in_i16)) return pcm400_stat_layout(p);
@@ -682,7 +684,7 @@ hipError_t launch_pcm(const lm_plan *p, const PcmArgs &a, hipStream_t s, const L
   const bool f16 = p->out_dtype == LM_F16;
   switch (p->n_fft) {
     case 400:
-      if (p->force_generic == 2) return launch_n<400, true>(k, a.in_i16, f16, n_tiles, s, tm);
+      if (p->fft_variant == LM_FFT_PAIRED) return launch_n<400, true>(k, a.in_i16, f16, n_tiles, s, tm);
       return launch_n<400>(k, a.in_i16, f16, n_tiles, s, tm);
     case 64: return launch_n<64>(k, a.in_i16, f16, n_tiles, s, tm);
     case 128: return launch_n<128>(k, a.in_i16, f16, n_tiles, s, tm);

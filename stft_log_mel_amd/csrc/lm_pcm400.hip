@@ -32,7 +32,7 @@
 // fetches the next sub-tile's samples into registers while it computes the
 // current one.  Per sub-tile it records the largest mel value of each of
 // its four lane groups and, per 4-band group of every band block, the
-// smallest log value, for the clamp fix-up kernel.
+// smallest output value, for the clamp fix-up kernel.
 #include <type_traits>
 
 #include "lm_device.h"
@@ -143,19 +143,20 @@ __device__ __forceinline__ void dft25(float2 (&a)[25]) {
   }
 }
 
-// unsigned min over the 16 lanes of a DPP row (rotations by 1, 2, 4, 8);
-// on the bit patterns of positive floats it is the float min
+// min over the 16 lanes of a DPP row (rotations by 1, 2, 4, 8)
 template <int N>
-__device__ __forceinline__ uint32_t ror_min(uint32_t v) {
-  const uint32_t r = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x120 + N, 0xf, 0xf, false);
-  return min(v, r);
+__device__ __forceinline__ float ror_min(float v) {
+  const float r = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xf, 0xf, false));
+  return fminf(v, r);
 }
-__device__ __forceinline__ uint32_t row_min16(uint32_t v) {
+__device__ __forceinline__ float row_min16(float v) {
   v = ror_min<1>(v);
   v = ror_min<2>(v);
   v = ror_min<4>(v);
   return ror_min<8>(v);
 }
+// unsigned max over the 16 lanes of a DPP row; on the bit patterns of
+// positive floats it is the float max
 template <int N>
 __device__ __forceinline__ uint32_t ror_max(uint32_t v) {
   const uint32_t r = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x120 + N, 0xf, 0xf, false);
@@ -177,9 +178,6 @@ __device__ __forceinline__ void store_out4(__half *p, const float (&o)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) store_out(p + i, o[i]);
 }
-
-// (log10(v) + 4) / 4 as one fma on the hardware base-2 logarithm
-constexpr float kLog10_2_Q = 0.0752574989159952988f;   // log10(2) / 4
 
 struct Args {
   const void *pcm;
@@ -661,7 +659,7 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
         for (int i = 0; i < 4; ++i) acc[i] = __builtin_amdgcn_ldexpf(acc[i], mel_e);
       }
       // block cb complete: log10, rescale, store, statistics
-      uint32_t vminb = 0x7f800000u;   // +inf: no value
+      float omin = __builtin_huge_valf();   // no value
       if (a.mel_out) {   // uniform: mel values as they are, no statistics
         const bool band_ok = 16 * cb + 4 * g + (c & 3) < NM;
 #pragma unroll
@@ -672,10 +670,9 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float v = fmaxf(acc[i], 1e-10f);
-          const uint32_t vb = __float_as_uint(v);
-          vmaxb = max(vmaxb, vb);
-          vminb = min(vminb, vb);
-          o[i] = __builtin_fmaf(__builtin_amdgcn_logf(v), kLog10_2_Q, 1.0f);
+          vmaxb = max(vmaxb, __float_as_uint(v));
+          o[i] = logmel_of(v);
+          omin = fminf(omin, o[i]);
         }
         store_out4(orow, o);
       } else {
@@ -683,16 +680,16 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float v = fmaxf(acc[i], 1e-10f);
-          const uint32_t vb = __float_as_uint(v);
           if (band_ok && f0 + i < F) {
-            vmaxb = max(vmaxb, vb);
-            vminb = min(vminb, vb);
-            store_out(orow + i, __builtin_fmaf(__builtin_amdgcn_logf(v), kLog10_2_Q, 1.0f));
+            const float o = logmel_of(v);
+            vmaxb = max(vmaxb, __float_as_uint(v));
+            omin = fminf(omin, o);
+            store_out(orow + i, o);
           }
         }
       }
-      vminb = row_min16(vminb);
-      if (c == 0) tile_min[(gs * NB + cb) * 4 + g] = log10_pos(__uint_as_float(vminb));
+      omin = row_min16(omin);
+      if (c == 0) tile_min[(gs * NB + cb) * 4 + g] = omin;
       acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
       ++cb;
       orow += 16 * F;

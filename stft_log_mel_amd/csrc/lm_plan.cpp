@@ -279,8 +279,6 @@ int lm_plan_create(lm_plan **plan, int n_fft, int hop, int n_mels, int center, i
   p->out_dtype = out_dtype;
   p->n_bins = n_fft / 2 + 1;
   p->win_length = n_fft;
-  const char *fg = std::getenv("LM_FORCE_GENERIC");
-  p->force_generic = !fg ? 0 : (std::strcmp(fg, "paired") == 0 ? 2 : (fg[0] == '1' ? 1 : 0));
   build_window(p);
   build_twiddles(p);
   if (n_fft == 400) build_mfma400(p);

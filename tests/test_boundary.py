@@ -213,7 +213,21 @@ def test_binding_has_no_cpu_fallback():
     goes through the C library (the binding holds no transform arithmetic)."""
     src = open(os.path.join(ROOT, "stft_log_mel_amd", "__init__.py")).read()
     for word in ["fft", "log10", "hann", "oracle", "einsum", "matmul"]:
-        assert word not in src.lower().replace("n_fft", "").replace("rfft", ""), word
+        text = src.lower().replace("n_fft", "").replace("rfft", "").replace("fft_variant", "")
+        assert word not in text, word
+
+
+def test_fft_variant_validation():
+    rc, h = _create()
+    assert rc == OK
+    for v in (0, 1, 2):
+        assert _lib.lm_plan_set_fft_variant(h, v) == OK
+    for v in (-1, 3):
+        assert _lib.lm_plan_set_fft_variant(h, v) == INVALID
+    assert _lib.lm_plan_set_fft_variant(None, 0) == INVALID
+    _lib.lm_plan_destroy(h)
+    with pytest.raises(ValueError):
+        lm.Plan(400, 160, 80).set_fft_variant("dense")
 
 
 def test_set_output_and_window_validation():

@@ -177,8 +177,9 @@ def test_stft_repeat_calls_and_invariances():
 # ---------------------------------------------------------------------------
 
 def run_pcm(x, n_fft, hop, n_mels, sr, center=True, pad_mode="reflect", power=2.0, out_dtype="f32",
-            fmin=0.0, fmax=None, scale="slaney", norm="slaney"):
+            fmin=0.0, fmax=None, scale="slaney", norm="slaney", fft_variant="auto"):
     p = lm().Plan(n_fft, hop, n_mels, center, pad_mode, power, out_dtype).set_mel(sr, fmin, fmax, scale, norm)
+    p.set_fft_variant(fft_variant)
     out = p.from_pcm(to_dev(x))
     torch.cuda.synchronize()
     return out
@@ -586,32 +587,31 @@ def test_melspectrogram_wrapper_shapes():
 
 
 @pytest.mark.parametrize("hop,in_dtype", [(160, "f32"), (160, "i16"), (161, "f32"), (200, "f32"), (320, "i16")])
-def test_pcm400_fast_and_generic_paths(hop, in_dtype, monkeypatch):
+def test_pcm400_fast_and_generic_paths(hop, in_dtype):
     """n_fft = 400 runs on the matrix-core kernel when the hop is even and the
-    tile's span fits in LDS, else on the generic kernel; LM_FORCE_GENERIC=1
-    selects the generic kernel (folded 200-point transform) and "paired"
-    its paired 400-point variant (two frames per complex transform; the
-    clip's 153 frames leave the last pair with one frame).  All must match
-    the oracle."""
+    tile's span fits in LDS, else on the generic kernel; the "folded" variant
+    selects the generic kernel (folded 200-point transform) and "paired" its
+    paired 400-point variant (two frames per complex transform; the clip's
+    153 frames leave the last pair with one frame).  All must match the
+    oracle."""
     B, T = 3, 24321
     x = lm_synth.speech_pcm(B, T, 16000.0, seed=hop, as_int16=(in_dtype == "i16"))
     ref = oracle_pcm(x, 400, hop, 128, 16000.0)
-    for force in ("0", "1", "paired"):
-        monkeypatch.setenv("LM_FORCE_GENERIC", force)
-        say("pcm400 path", hop, in_dtype, "force_generic", force)
-        out = run_pcm(x, 400, hop, 128, 16000.0)
-        check(out, ref, TOL32, f"hop {hop} {in_dtype} generic={force}")
+    for variant in ("auto", "folded", "paired"):
+        say("pcm400 path", hop, in_dtype, "variant", variant)
+        out = run_pcm(x, 400, hop, 128, 16000.0, fft_variant=variant)
+        check(out, ref, TOL32, f"hop {hop} {in_dtype} variant {variant}")
 
 
 @pytest.mark.parametrize("in_dtype,out_dtype,pad_mode,power", [("i16", "f16", "constant", 2.0),
                                                                 ("f32", "f32", "circular", 1.0)])
-def test_pcm400_paired_variant_options(in_dtype, out_dtype, pad_mode, power, monkeypatch):
+def test_pcm400_paired_variant_options(in_dtype, out_dtype, pad_mode, power):
     """The paired 400-point variant with fp16 output, other pad modes and a
     general power."""
-    monkeypatch.setenv("LM_FORCE_GENERIC", "paired")
     x = lm_synth.speech_pcm(2, 16001, 16000.0, seed=90, as_int16=(in_dtype == "i16"))
     say("pcm400 paired", in_dtype, out_dtype, pad_mode, power)
-    out = run_pcm(x, 400, 160, 80, 16000.0, pad_mode=pad_mode, power=power, out_dtype=out_dtype)
+    out = run_pcm(x, 400, 160, 80, 16000.0, pad_mode=pad_mode, power=power, out_dtype=out_dtype,
+                  fft_variant="paired")
     ref = oracle_pcm(x, 400, 160, 80, 16000.0, pad_mode=pad_mode, power=power)
     check(out, ref, TOL32 if out_dtype == "f32" else TOL16, f"paired {in_dtype} {out_dtype} {pad_mode} {power}")
 
