@@ -240,6 +240,29 @@ int lm_from_stft(lm_plan *plan, const void *stft, const float *mel_filters, int6
 int lm_plan_profile(lm_plan *plan, int enable);
 int lm_plan_profile_read(lm_plan *plan, double *ms, int64_t *counts);
 
+/*
+ * lm_from_pcm_noalloc -- lm_from_pcm for callers that cannot allocate
+ * device memory during a call: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments, kernels and
+ * results as lm_from_pcm; no device or host memory is allocated or freed.
+ *
+ *  - The statistics workspace (per-region output minima and per-tile mel
+ *    maxima that the clamp fix-up reads) is a fixed 8 MiB device array
+ *    (2^21 floats), one per GPU, held until the process ends.  A call
+ *    needing more returns LM_ERR_UNSUPPORTED before any launch (a 30 s clip
+ *    at n_fft 400 / 128 mels needs 6768 floats: about 300 such clips per
+ *    call).  Every entry a call reads is written by that call, so nothing
+ *    needs clearing between calls.
+ *  - Every call on one GPU shares that array: calls that overlap in time on
+ *    one GPU (other streams, other plans, other threads) race on it.
+ *    Calls on one stream, or otherwise ordered, are safe.
+ *  - The plan's device tables must already exist: make one lm_from_pcm call
+ *    with the plan after its last set_mel / set_filters / set_window;
+ *    otherwise LM_ERR_INVALID_ARG.  Profiling (lm_plan_profile) is ignored.
+ */
+int lm_from_pcm_noalloc(lm_plan *plan, const void *pcm, int in_dtype, int64_t n_clips, int64_t n_samples,
+                        void *out, void *stream);
+
 /* FFT variants of the n_fft = 400 PCM path (lm_plan_set_fft_variant). */
 enum { LM_FFT_AUTO = 0, LM_FFT_FOLDED = 1, LM_FFT_PAIRED = 2 };
 

@@ -58,6 +58,7 @@ SIGNATURES = {
     "lm_plan_num_frames": (_c_i64, [_c_p, _c_i64]),
     "lm_from_pcm": (_c_int, [_c_p, _c_p, _c_int, _c_i64, _c_i64, _c_p, _c_p]),
     "lm_from_stft": (_c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_int, _c_p, _c_p]),
+    "lm_from_pcm_noalloc": (_c_int, [_c_p, _c_p, _c_int, _c_i64, _c_i64, _c_p, _c_p]),
     "lm_plan_set_fft_variant": (_c_int, [_c_p, _c_int]),
     "lm_plan_profile": (_c_int, [_c_p, _c_int]),
     "lm_plan_profile_read": (_c_int, [_c_p, ctypes.POINTER(_c_d), ctypes.POINTER(_c_i64)]),

@@ -22,7 +22,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblm.so")
 
-SOURCES = ["lm_plan.cpp", "lm_api.cpp", "lm_stft.hip", "lm_pcm.hip", "lm_pcm400.hip", "lm_fixup.hip"]
+SOURCES = ["lm_plan.cpp", "lm_api.cpp", "lm_stft.hip", "lm_pcm.hip", "lm_pcm400.hip", "lm_fixup.hip",
+           "lm_noalloc.hip"]
 HEADERS = ["lm_internal.h", "lm_device.h", "lm_fixup.h", os.path.join("..", "..", "include", "lm.h")]
 
 ARCH = "gfx950"

@@ -203,10 +203,56 @@ static int timed_launch(lm_plan *p, hipStream_t s, int kind, const char *what, F
   return LM_OK;
 }
 
+static int run_pcm_launches(lm_plan *p, const void *pcm, bool in_i16, int64_t n_clips, int64_t n_samples,
+                            int64_t F, int tiles, const StatLayout &st, void *out, float *ws, hipStream_t s);
+
+// Host-side checks of an lm_from_pcm call (no HIP call); fills the call's
+// geometry.  n_clips == 0 passes and needs no launch.
+int validate_pcm(const lm_plan *p, const void *pcm, int in_dtype, int64_t n_clips, int64_t n_samples,
+                 const void *out, PcmCall *c) {
+  if (!p) return fail(LM_ERR_INVALID_ARG, "plan is NULL");
+  if (!p->have_filters) return fail(LM_ERR_NO_FILTERS, "call lm_plan_set_mel or lm_plan_set_filters first");
+  if (in_dtype != LM_F32 && in_dtype != LM_I16) return fail(LM_ERR_INVALID_ARG, "in_dtype must be LM_F32 or LM_I16");
+  if (n_clips < 0) return fail(LM_ERR_INVALID_ARG, "n_clips < 0");
+  if (n_samples < 1) return fail(LM_ERR_INVALID_ARG, "n_samples < 1");
+  const int64_t half = p->n_fft / 2;
+  // the center padding applies to the signal with its zero padding (length t_sig)
+  const int64_t t_sig = n_samples + 2 * p->sig_pad;
+  if (!p->center && t_sig < p->n_fft) return fail(LM_ERR_INVALID_ARG, "center=0 needs n_samples + 2 pad >= n_fft");
+  if (p->center && p->pad_mode == LM_PAD_REFLECT && t_sig <= half)
+    return fail(LM_ERR_INVALID_ARG, "reflect padding needs n_samples + 2 pad > n_fft/2");
+  if (p->center && p->pad_mode == LM_PAD_CIRCULAR && t_sig < half)
+    return fail(LM_ERR_INVALID_ARG, "circular padding needs n_samples + 2 pad >= n_fft/2");
+  if (n_clips == 0) return LM_OK;
+  if (!pcm || !out) return fail(LM_ERR_INVALID_ARG, "pcm and out must be device pointers");
+  const size_t in_align = in_dtype == LM_I16 ? 2 : 4, out_align = p->out_dtype == LM_F16 ? 2 : 4;
+  if ((reinterpret_cast<uintptr_t>(pcm) % in_align) || (reinterpret_cast<uintptr_t>(out) % out_align))
+    return fail(LM_ERR_INVALID_ARG, "misaligned pcm or out pointer");
+  const int64_t F = lm_plan_num_frames(p, n_samples);
+  if (F < 1) return (int)F;
+  c->F = F;
+  c->st = pcm_stat_layout(p, in_dtype == LM_I16);
+  const int64_t tiles = (F + c->st.frames_per_tile - 1) / c->st.frames_per_tile;
+  if (tiles > INT32_MAX || n_clips * tiles > INT32_MAX) return fail(LM_ERR_UNSUPPORTED, "input too large");
+  c->tiles = (int)tiles;
+  c->ws_floats = n_clips * tiles * (c->st.min_per_tile() + c->st.max_per_tile);
+  return LM_OK;
+}
+
 // The PCM launch sequence (main kernel, then the clamp fix-up) with the
 // statistics workspace at `ws` (n_clips * tiles * (minima + maxima) floats).
+// With allow_profile false no timing events are created (no allocation).
 int run_pcm(lm_plan *p, const void *pcm, bool in_i16, int64_t n_clips, int64_t n_samples, int64_t F, int tiles,
-            const StatLayout &st, void *out, float *ws, hipStream_t s) {
+            const StatLayout &st, void *out, float *ws, hipStream_t s, bool allow_profile) {
+  const bool prof = p->profiling;
+  if (!allow_profile) p->profiling = false;
+  const int rc = run_pcm_launches(p, pcm, in_i16, n_clips, n_samples, F, tiles, st, out, ws, s);
+  p->profiling = prof;
+  return rc;
+}
+
+static int run_pcm_launches(lm_plan *p, const void *pcm, bool in_i16, int64_t n_clips, int64_t n_samples,
+                            int64_t F, int tiles, const StatLayout &st, void *out, float *ws, hipStream_t s) {
   float *tmin = ws, *tmax = ws + n_clips * tiles * st.min_per_tile();
   PcmArgs a{pcm, in_i16, n_clips, n_samples, F, tiles, out, tmin, tmax};
   int rc = timed_launch(p, s, 0, "launch(pcm kernel)", [&](const LaunchTiming *tm) { return launch_pcm(p, a, s, tm); });
@@ -262,37 +308,16 @@ extern "C" {
 
 int lm_from_pcm(lm_plan *p, const void *pcm, int in_dtype, int64_t n_clips, int64_t n_samples, void *out,
                 void *stream) {
-  if (!p) return fail(LM_ERR_INVALID_ARG, "plan is NULL");
-  if (!p->have_filters) return fail(LM_ERR_NO_FILTERS, "call lm_plan_set_mel or lm_plan_set_filters first");
-  if (in_dtype != LM_F32 && in_dtype != LM_I16) return fail(LM_ERR_INVALID_ARG, "in_dtype must be LM_F32 or LM_I16");
-  if (n_clips < 0) return fail(LM_ERR_INVALID_ARG, "n_clips < 0");
-  if (n_samples < 1) return fail(LM_ERR_INVALID_ARG, "n_samples < 1");
-  const int64_t half = p->n_fft / 2;
-  // the center padding applies to the signal with its zero padding (length t_sig)
-  const int64_t t_sig = n_samples + 2 * p->sig_pad;
-  if (!p->center && t_sig < p->n_fft) return fail(LM_ERR_INVALID_ARG, "center=0 needs n_samples + 2 pad >= n_fft");
-  if (p->center && p->pad_mode == LM_PAD_REFLECT && t_sig <= half)
-    return fail(LM_ERR_INVALID_ARG, "reflect padding needs n_samples + 2 pad > n_fft/2");
-  if (p->center && p->pad_mode == LM_PAD_CIRCULAR && t_sig < half)
-    return fail(LM_ERR_INVALID_ARG, "circular padding needs n_samples + 2 pad >= n_fft/2");
-  if (n_clips == 0) return LM_OK;
-  if (!pcm || !out) return fail(LM_ERR_INVALID_ARG, "pcm and out must be device pointers");
-  const size_t in_align = in_dtype == LM_I16 ? 2 : 4, out_align = p->out_dtype == LM_F16 ? 2 : 4;
-  if ((reinterpret_cast<uintptr_t>(pcm) % in_align) || (reinterpret_cast<uintptr_t>(out) % out_align))
-    return fail(LM_ERR_INVALID_ARG, "misaligned pcm or out pointer");
-  const int64_t F = lm_plan_num_frames(p, n_samples);
-  if (F < 1) return (int)F;
-  const StatLayout st = pcm_stat_layout(p, in_dtype == LM_I16);
-  const int64_t tiles = (F + st.frames_per_tile - 1) / st.frames_per_tile;
-  if (tiles > INT32_MAX || n_clips * tiles > INT32_MAX) return fail(LM_ERR_UNSUPPORTED, "input too large");
+  PcmCall c;
+  int rc = validate_pcm(p, pcm, in_dtype, n_clips, n_samples, out, &c);
+  if (rc != LM_OK || n_clips == 0) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  int rc = begin_call(p, s);
+  rc = begin_call(p, s);
   if (rc != LM_OK) return rc;
   rc = upload_tables(p, s);
-  const int64_t n_min = n_clips * tiles * st.min_per_tile(), n_max = n_clips * tiles * st.max_per_tile;
-  if (rc == LM_OK) rc = ensure_workspace(p, n_min + n_max, s);
-  if (rc == LM_OK) rc = run_pcm(p, pcm, in_dtype == LM_I16, n_clips, n_samples, F, (int)tiles, st, out,
-                                p->d_stats, s);
+  if (rc == LM_OK) rc = ensure_workspace(p, c.ws_floats, s);
+  if (rc == LM_OK) rc = run_pcm(p, pcm, in_dtype == LM_I16, n_clips, n_samples, c.F, c.tiles, c.st, out, p->d_stats,
+                                s, true);
   return end_call(p, s, rc);
 }
 

@@ -142,11 +142,6 @@ int upload_tables(lm_plan *p, hipStream_t s);
 // the plan's previous call, then mark its end.
 int begin_call(lm_plan *p, hipStream_t s);
 int end_call(lm_plan *p, hipStream_t s, int rc);
-struct StatLayout;
-// The PCM launch sequence (main kernel, clamp fix-up) with its statistics
-// workspace at ws.
-int run_pcm(lm_plan *p, const void *pcm, bool in_i16, int64_t n_clips, int64_t n_samples, int64_t F, int tiles,
-            const StatLayout &st, void *out, float *ws, hipStream_t s);
 
 // Host table builders (lm_plan.cpp)
 double window_at(const lm_plan *p, int n);   // the frame window at n (float64)
@@ -171,6 +166,22 @@ struct StatLayout {
   int frames_per_tile = 1, sub_per_tile = 1, blk_per_sub = 1, band_h = 1, max_per_tile = 1;
   __host__ __device__ int min_per_tile() const { return sub_per_tile * blk_per_sub; }
 };
+
+// Geometry of one lm_from_pcm call, from validate_pcm.
+struct PcmCall {
+  int64_t F = 0;
+  int tiles = 0;
+  StatLayout st;
+  int64_t ws_floats = 0;   // statistics workspace the call needs
+};
+// Host-side checks of an lm_from_pcm call (no HIP call), filling c; LM_OK
+// with nothing to do for n_clips == 0.
+int validate_pcm(const lm_plan *p, const void *pcm, int in_dtype, int64_t n_clips, int64_t n_samples,
+                 const void *out, PcmCall *c);
+// The PCM launch sequence (main kernel, clamp fix-up) with its statistics
+// workspace at ws; allow_profile false creates no timing events.
+int run_pcm(lm_plan *p, const void *pcm, bool in_i16, int64_t n_clips, int64_t n_samples, int64_t F, int tiles,
+            const StatLayout &st, void *out, float *ws, hipStream_t s, bool allow_profile);
 
 struct PcmArgs {
   const void *pcm;
