@@ -31,12 +31,15 @@
  *    (hipMallocAsync / hipFreeAsync on the call's stream).
  *  - A plan binds to the device current at its first lm_from_* call and
  *    must only be used on that device.  It may be used from several
- *    streams: a call on a stream other than the previous call's makes its
- *    stream wait (an event) for everything the previous call enqueued, so
- *    the GPU work of one plan always runs in call order and its shared
- *    workspace is never used by two calls at once.  Host calls on one plan
- *    must not run concurrently on several threads.  Do not change or
- *    destroy a plan while work that uses it is in flight.
+ *    streams: a call on a stream other than the previous call's records an
+ *    event on the previous call's stream and makes its own stream wait for
+ *    it, so the GPU work of one plan always runs in call order and its
+ *    shared workspace is never used by two calls at once (calls on one
+ *    stream add no event).  A stream a plan was last used on must therefore
+ *    stay valid until the plan's next call on another stream or its
+ *    destruction.  Host calls on one plan must not run concurrently on
+ *    several threads.  Do not change or destroy a plan while work that uses
+ *    it is in flight.
  */
 #ifndef LM_H
 #define LM_H
@@ -246,13 +249,14 @@ int lm_plan_profile_read(lm_plan *plan, double *ms, int64_t *counts);
  * loops, harnesses that forbid allocation.  Same arguments, kernels and
  * results as lm_from_pcm; no device or host memory is allocated or freed.
  *
- *  - The statistics workspace (per-region output minima and per-tile mel
- *    maxima that the clamp fix-up reads) is a fixed 8 MiB device array
- *    (2^21 floats), one per GPU, held until the process ends.  A call
+ *  - The workspace is a fixed 8 MiB device array, one per GPU, held until
+ *    the process ends: 2^21 - 16384 floats of statistics (per-region output
+ *    minima and per-tile mel maxima that the clamp fix-up reads) and 8192
+ *    64-bit slots of the single pass (see lm_plan_set_single_pass).  A call
  *    needing more returns LM_ERR_UNSUPPORTED before any launch (a 30 s clip
  *    at n_fft 400 / 128 mels needs 6768 floats: about 300 such clips per
- *    call).  Every entry a call reads is written by that call, so nothing
- *    needs clearing between calls.
+ *    call).  Every statistic a call reads is written by that call, and the
+ *    slots carry a per-call tag, so nothing needs clearing between calls.
  *  - Every call on one GPU shares that array: calls that overlap in time on
  *    one GPU (other streams, other plans, other threads) race on it.
  *    Calls on one stream, or otherwise ordered, are safe.
@@ -262,6 +266,26 @@ int lm_plan_profile_read(lm_plan *plan, double *ms, int64_t *counts);
  */
 int lm_from_pcm_noalloc(lm_plan *plan, const void *pcm, int in_dtype, int64_t n_clips, int64_t n_samples,
                         void *out, void *stream);
+
+/*
+ * lm_plan_set_single_pass -- use (enable = 1) or not (0, the default) the
+ * single-pass form of the per-clip floor (KBench page, "perf_md": the
+ * clip-resident alternative to a second pass over the output).
+ *
+ * Where it applies, lm_from_pcm runs one cooperative launch instead of the
+ * main kernel plus the clamp fix-up: each wave stores its log-mel values,
+ * publishes its largest mel value on its clip's slot, and all workgroups
+ * meet at a grid barrier (every wait bounded; a wait that runs out writes
+ * NaN); a wave holding a value below its clip's floor then recomputes its
+ * mel sums from the power rows still in its LDS and overwrites them
+ * floored.  It applies at n_fft = 400 (the matrix-core kernel) with log-mel
+ * output and at most one 16-frame sub-tile per resident wave (8 per
+ * compute unit): the launch-bound batches.  Results are bit-identical to
+ * the two-pass form.  It is off by default because it is slower on MI355X:
+ * the cooperative launch alone costs more than the fix-up launch it saves.
+ * Host-only.  LM_ERR_INVALID_ARG unless enable is 0 or 1.
+ */
+int lm_plan_set_single_pass(lm_plan *plan, int enable);
 
 /* FFT variants of the n_fft = 400 PCM path (lm_plan_set_fft_variant). */
 enum { LM_FFT_AUTO = 0, LM_FFT_FOLDED = 1, LM_FFT_PAIRED = 2 };

@@ -60,6 +60,7 @@ SIGNATURES = {
     "lm_from_stft": (_c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_int, _c_p, _c_p]),
     "lm_from_pcm_noalloc": (_c_int, [_c_p, _c_p, _c_int, _c_i64, _c_i64, _c_p, _c_p]),
     "lm_plan_set_fft_variant": (_c_int, [_c_p, _c_int]),
+    "lm_plan_set_single_pass": (_c_int, [_c_p, _c_int]),
     "lm_plan_profile": (_c_int, [_c_p, _c_int]),
     "lm_plan_profile_read": (_c_int, [_c_p, ctypes.POINTER(_c_d), ctypes.POINTER(_c_i64)]),
     "lm_plan_destroy": (None, [_c_p]),
@@ -175,6 +176,12 @@ class Plan:
         if variant not in _FFT_VARIANT:
             raise ValueError(f"variant must be one of {sorted(_FFT_VARIANT)}")
         _check(_lib.lm_plan_set_fft_variant(self._h, _FFT_VARIANT[variant]))
+        return self
+
+    def set_single_pass(self, enable: bool = True) -> "Plan":
+        """Use the one-launch (cooperative, grid-barrier) form of the per-clip
+        floor where it applies; plans start with it off (two launches)."""
+        _check(_lib.lm_plan_set_single_pass(self._h, int(bool(enable))))
         return self
 
     def get_filters(self) -> np.ndarray:

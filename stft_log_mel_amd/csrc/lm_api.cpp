@@ -2,6 +2,7 @@
 // and the launch sequence (main kernel, then the per-clip clamp fix-up) on
 // the caller's stream.
 #include <algorithm>
+#include <atomic>
 #include <cstring>
 
 #include "lm_internal.h"
@@ -18,8 +19,12 @@ int ensure_device(lm_plan *p) {
     int n_cu = 0;
     e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    int coop = 0;
+    e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
     p->device = dev;
     p->n_cu = n_cu > 0 ? n_cu : 1;
+    p->coop_launch = coop != 0;
   } else if (p->device != dev) {
     return fail(LM_ERR_INVALID_ARG, "plan is bound to another device");
   }
@@ -154,6 +159,29 @@ int ensure_workspace(lm_plan *p, int64_t n_floats, hipStream_t s) {
   return rc;
 }
 
+// Single-pass slots of the plan (2 + n_clips words), zeroed when grown
+// (which restarts the barrier parity).
+static int ensure_sync(lm_plan *p, int64_t slots, hipStream_t s) {
+  const size_t need = sizeof(uint64_t) * (size_t)slots;
+  if (need <= p->sync_cap) return LM_OK;
+  p->sync_calls = 0;
+  void *buf = p->d_sync;
+  size_t cap = p->sync_cap;
+  int rc = grow(&buf, &cap, need, s, "hipMallocAsync(single-pass slots)");
+  p->d_sync = static_cast<uint64_t *>(buf);
+  p->sync_cap = cap;
+  if (rc != LM_OK) return rc;
+  const hipError_t e = launch_zero_u64(p->d_sync, cap / sizeof(uint64_t), s);
+  return e == hipSuccess ? LM_OK : hip_fail(e, "launch(zero slots)");
+}
+
+uint32_t next_epoch() {
+  static std::atomic<uint32_t> g_epoch{0};
+  uint32_t e = ++g_epoch;
+  while (e == 0) e = ++g_epoch;   // 0 marks a slot never used
+  return e;
+}
+
 int begin_call(lm_plan *p, hipStream_t s) {
   int rc = ensure_device(p);
   if (rc != LM_OK) return rc;
@@ -162,15 +190,14 @@ int begin_call(lm_plan *p, hipStream_t s) {
     if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
   }
   if (p->has_last && p->last_stream != static_cast<void *>(s)) {
-    hipError_t e = hipStreamWaitEvent(s, p->done_event, 0);
+    hipError_t e = hipEventRecord(p->done_event, reinterpret_cast<hipStream_t>(p->last_stream));
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, p->done_event, 0);
     if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
   }
   return LM_OK;
 }
 
 int end_call(lm_plan *p, hipStream_t s, int rc) {
-  hipError_t e = hipEventRecord(p->done_event, s);
-  if (e != hipSuccess) return rc != LM_OK ? rc : hip_fail(e, "hipEventRecord");
   p->last_stream = static_cast<void *>(s);
   p->has_last = true;
   return rc;
@@ -204,7 +231,8 @@ static int timed_launch(lm_plan *p, hipStream_t s, int kind, const char *what, F
 }
 
 static int run_pcm_launches(lm_plan *p, const void *pcm, bool in_i16, int64_t n_clips, int64_t n_samples,
-                            int64_t F, int tiles, const StatLayout &st, void *out, float *ws, hipStream_t s);
+                            int64_t F, int tiles, const StatLayout &st, void *out, float *ws, uint64_t *sync,
+                            int parity, hipStream_t s);
 
 // Host-side checks of an lm_from_pcm call (no HIP call); fills the call's
 // geometry.  n_clips == 0 passes and needs no launch.
@@ -243,18 +271,27 @@ int validate_pcm(const lm_plan *p, const void *pcm, int in_dtype, int64_t n_clip
 // statistics workspace at `ws` (n_clips * tiles * (minima + maxima) floats).
 // With allow_profile false no timing events are created (no allocation).
 int run_pcm(lm_plan *p, const void *pcm, bool in_i16, int64_t n_clips, int64_t n_samples, int64_t F, int tiles,
-            const StatLayout &st, void *out, float *ws, hipStream_t s, bool allow_profile) {
+            const StatLayout &st, void *out, float *ws, uint64_t *sync, int parity, hipStream_t s,
+            bool allow_profile) {
   const bool prof = p->profiling;
   if (!allow_profile) p->profiling = false;
-  const int rc = run_pcm_launches(p, pcm, in_i16, n_clips, n_samples, F, tiles, st, out, ws, s);
+  const int rc = run_pcm_launches(p, pcm, in_i16, n_clips, n_samples, F, tiles, st, out, ws, sync, parity, s);
   p->profiling = prof;
   return rc;
 }
 
 static int run_pcm_launches(lm_plan *p, const void *pcm, bool in_i16, int64_t n_clips, int64_t n_samples,
-                            int64_t F, int tiles, const StatLayout &st, void *out, float *ws, hipStream_t s) {
-  float *tmin = ws, *tmax = ws + n_clips * tiles * st.min_per_tile();
+                            int64_t F, int tiles, const StatLayout &st, void *out, float *ws, uint64_t *sync,
+                            int parity, hipStream_t s) {
+  float *tmin = ws, *tmax = ws ? ws + n_clips * tiles * st.min_per_tile() : nullptr;
   PcmArgs a{pcm, in_i16, n_clips, n_samples, F, tiles, out, tmin, tmax};
+  if (sync) {   // one pass: the kernel floors each clip itself
+    a.sync = sync;
+    a.epoch = next_epoch();
+    a.parity = parity;
+    return timed_launch(p, s, 0, "launch(pcm kernel, single pass)",
+                        [&](const LaunchTiming *tm) { return launch_pcm(p, a, s, tm); });
+  }
   int rc = timed_launch(p, s, 0, "launch(pcm kernel)", [&](const LaunchTiming *tm) { return launch_pcm(p, a, s, tm); });
   if (rc != LM_OK) return rc;
   if (p->output == LM_OUTPUT_MEL) return LM_OK;   // no per-clip tail
@@ -315,9 +352,11 @@ int lm_from_pcm(lm_plan *p, const void *pcm, int in_dtype, int64_t n_clips, int6
   rc = begin_call(p, s);
   if (rc != LM_OK) return rc;
   rc = upload_tables(p, s);
-  if (rc == LM_OK) rc = ensure_workspace(p, c.ws_floats, s);
-  if (rc == LM_OK) rc = run_pcm(p, pcm, in_dtype == LM_I16, n_clips, n_samples, c.F, c.tiles, c.st, out, p->d_stats,
-                                s, true);
+  const bool one_pass = pcm400_single_pass(p, in_dtype == LM_I16, n_clips * c.tiles);
+  if (rc == LM_OK) rc = one_pass ? ensure_sync(p, 2 + n_clips, s) : ensure_workspace(p, c.ws_floats, s);
+  if (rc == LM_OK)
+    rc = run_pcm(p, pcm, in_dtype == LM_I16, n_clips, n_samples, c.F, c.tiles, c.st, out, one_pass ? nullptr : p->d_stats,
+                 one_pass ? p->d_sync : nullptr, one_pass ? (int)(p->sync_calls++ & 1) : 0, s, true);
   return end_call(p, s, rc);
 }
 
@@ -390,6 +429,7 @@ void lm_plan_destroy(lm_plan *p) {
   if (p->dt.base) (void)hipFree(p->dt.base);
   if (p->d_stats) (void)hipFree(p->d_stats);
   if (p->d_pack) (void)hipFree(p->d_pack);
+  if (p->d_sync) (void)hipFree(p->d_sync);
   for (auto &st : p->staging) {
     (void)hipEventSynchronize(st.done);
     (void)hipEventDestroy(st.done);
@@ -397,6 +437,13 @@ void lm_plan_destroy(lm_plan *p) {
   }
   if (p->done_event) (void)hipEventDestroy(p->done_event);
   delete p;
+}
+
+int lm_plan_set_single_pass(lm_plan *p, int enable) {
+  if (!p) return fail(LM_ERR_INVALID_ARG, "plan is NULL");
+  if (enable != 0 && enable != 1) return fail(LM_ERR_INVALID_ARG, "enable must be 0 or 1");
+  p->single_pass = enable;
+  return LM_OK;
 }
 
 int lm_plan_set_fft_variant(lm_plan *p, int variant) {

@@ -30,13 +30,21 @@ __device__ __forceinline__ float logmel_of(float v) {
   return __builtin_fmaf(__builtin_amdgcn_logf(v), kLog10_2_Q, 1.0f);
 }
 
+// fp16 output is the fp32 value rounded to nearest even.  The empty asm
+// keeps the compiler from fusing the conversion into the fma that produced
+// v (a mixed-precision fma rounds the exact result once, which differs from
+// rounding the fp32 value where that value is a tie in fp16).
+__device__ __forceinline__ float fp32_value(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
 __device__ __forceinline__ void store_out(float *p, float v) { *p = v; }
-__device__ __forceinline__ void store_out(__half *p, float v) { *p = __float2half_rn(v); }
+__device__ __forceinline__ void store_out(__half *p, float v) { *p = __float2half_rn(fp32_value(v)); }
 // Streaming stores for the main kernels: every output is written once and
 // read again only by the fix-up's few flagged regions.
 __device__ __forceinline__ void store_out_nt(float *p, float v) { __builtin_nontemporal_store(v, p); }
 __device__ __forceinline__ void store_out_nt(__half *p, float v) {
-  __builtin_nontemporal_store(__half_as_ushort(__float2half_rn(v)), reinterpret_cast<unsigned short *>(p));
+  __builtin_nontemporal_store(__half_as_ushort(__float2half_rn(fp32_value(v))), reinterpret_cast<unsigned short *>(p));
 }
 __device__ __forceinline__ float load_out(const float *p) { return *p; }
 __device__ __forceinline__ float load_out(const __half *p) { return __half2float(*p); }

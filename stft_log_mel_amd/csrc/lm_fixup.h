@@ -118,7 +118,7 @@ __device__ void fixup_group(const FixupArgs &a, int64_t b, int gi, int *s_f0, in
   const int n_flag = *s_n;
 
   float fo = fl;
-  if (sizeof(OUT) == 2) fo = __half2float(__float2half_rn(fo));
+  if (sizeof(OUT) == 2) fo = __half2float(__float2half_rn(fp32_value(fo)));
   // rewrite: value k of the flattened list is value el of region i; el
   // splits into a run index o and the position in the run (contiguous in
   // the output), both with precomputed multiplies (no division per value)

@@ -119,13 +119,21 @@ struct lm_plan {
   size_t pack_cap = 0;
   // pinned host buffers of the table uploads
   std::vector<lm::Staging> staging;
-  // recorded on the stream of the last lm_from_* call after its last launch;
-  // a call on another stream first waits for it
+  // a call on a stream other than the last call's records this event on the
+  // last call's stream and waits for it
   hipEvent_t done_event = nullptr;
   void *last_stream = nullptr;
   bool has_last = false;
 
   int fft_variant = LM_FFT_AUTO;   // lm_plan_set_fft_variant (n_fft = 400 only)
+  int single_pass = 0;             // lm_plan_set_single_pass
+  bool coop_launch = false;        // the device supports cooperative launches
+  // single-pass slots: [0], [1] grid barrier counters (calls alternate
+  // between them), [2 + b] clip b's maximum as (epoch << 32) | value;
+  // zeroed when allocated
+  uint64_t *d_sync = nullptr;
+  size_t sync_cap = 0;             // bytes
+  uint32_t sync_calls = 0;         // single-pass calls made on d_sync (barrier parity)
 
   bool profiling = false;
   std::vector<lm::ProfileRec> prof;
@@ -139,7 +147,8 @@ int ensure_device(lm_plan *p);
 int ensure_workspace(lm_plan *p, int64_t n_floats, hipStream_t s);
 int upload_tables(lm_plan *p, hipStream_t s);
 // Start and end of an lm_from_* call's GPU work on stream s: order it after
-// the plan's previous call, then mark its end.
+// the plan's previous call (an event, only when the stream changes), then
+// note the stream.
 int begin_call(lm_plan *p, hipStream_t s);
 int end_call(lm_plan *p, hipStream_t s, int rc);
 
@@ -180,8 +189,12 @@ int validate_pcm(const lm_plan *p, const void *pcm, int in_dtype, int64_t n_clip
                  const void *out, PcmCall *c);
 // The PCM launch sequence (main kernel, clamp fix-up) with its statistics
 // workspace at ws; allow_profile false creates no timing events.
+// A non-null sync (2 + n_clips single-pass slots) runs the call as one pass
+// of the main kernel (pcm400_single_pass must hold) with barrier counter
+// `parity`; ws is then unused.
 int run_pcm(lm_plan *p, const void *pcm, bool in_i16, int64_t n_clips, int64_t n_samples, int64_t F, int tiles,
-            const StatLayout &st, void *out, float *ws, hipStream_t s, bool allow_profile);
+            const StatLayout &st, void *out, float *ws, uint64_t *sync, int parity, hipStream_t s,
+            bool allow_profile);
 
 struct PcmArgs {
   const void *pcm;
@@ -191,6 +204,12 @@ struct PcmArgs {
   void *out;
   float *tile_min;
   float *tile_max;
+  // single pass (no fix-up launch): 2 + n_clips slots (two barrier
+  // counters, then the clip maxima), this call's epoch and barrier parity;
+  // nullptr for two passes
+  uint64_t *sync = nullptr;
+  uint32_t epoch = 0;
+  int parity = 0;
 };
 // Statistics geometry of the PCM kernel launch_pcm picks for this plan and
 // input type (the n_fft = 400 matrix-core kernel when it applies, else the
@@ -201,6 +220,12 @@ hipError_t launch_pcm(const lm_plan *p, const PcmArgs &a, hipStream_t s, const L
 // kernel, log-mel output, at least one empty band): the fix-up writes them.
 bool pcm_skips_empty_bands(const lm_plan *p, bool in_i16);
 bool pcm400_supported(const lm_plan *p, bool in_i16);
+// True when a call of n_sub 16-frame sub-tiles runs as one pass of the
+// n_fft = 400 kernel (every wave holds at most one sub-tile and keeps its
+// outputs until the clip's maximum is known; cooperative launch).
+bool pcm400_single_pass(const lm_plan *p, bool in_i16, int64_t n_sub);
+// Next tag of a single-pass call (process-wide, never 0).
+uint32_t next_epoch();
 StatLayout pcm400_stat_layout(const lm_plan *p);
 hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &a, hipStream_t s, const LaunchTiming *tm);
 
@@ -250,5 +275,8 @@ struct FixupArgs {
   unsigned inner_magic = 0, reg_magic = 0;          // set by launch_fixup: divide by a run / a region length
 };
 hipError_t launch_fixup(FixupArgs a, hipStream_t s, const LaunchTiming *tm);
+// Zero n 64-bit words (a fill kernel, not a memset node, so that a captured
+// graph replays it correctly).
+hipError_t launch_zero_u64(uint64_t *p, size_t n, hipStream_t s);
 
 }  // namespace lm

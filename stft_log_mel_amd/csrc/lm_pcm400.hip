@@ -194,7 +194,41 @@ struct Args {
   uint64_t end_mask[2];  // bit b: batch b is the last of its band block
   int mel_out;           // 1: store the mel values themselves (no log tail)
   float *tile_max;
+  // single pass only: this call's tag of the clip maxima, the parity of its
+  // grid barrier counter, and the slots ([0], [1] barrier counters, [2 + b]
+  // clip b's maximum), see grid_barrier
+  uint32_t epoch;
+  int parity;
+  uint64_t *sync;
 };
+
+// Polls of the grid barrier before a workgroup gives up (about 0.1 s):
+// with every workgroup resident (cooperative launch) the last one arrives
+// within microseconds, so this bound only ends a wait that cannot succeed.
+constexpr int kBarrierPolls = 1 << 20;
+
+// Grid barrier of one call; one thread per workgroup.  The plan's calls
+// alternate between two arrival counters (the host passes the parity), and
+// each call zeroes the other counter once every workgroup has arrived, for
+// the call after it (calls on one slot buffer never overlap: they are
+// stream-ordered).  Arrivals are plain atomic adds, which the memory side
+// performs without retries.  Every atomic here is relaxed: no plain store
+// precedes the barrier, and the clip maxima are themselves atomics that
+// have completed (their old values were consumed) before any arrival, so
+// no release fence -- on this chip a write-back of the XCD's L2 -- is
+// needed.  Returns false if the wait ran out of polls.
+__device__ bool grid_barrier(uint64_t *cnt, int parity, uint32_t n) {
+  const uint64_t before = __hip_atomic_fetch_add(cnt + parity, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (before + 1 >= n) {   // the last arrival
+    __hip_atomic_store(cnt + (parity ^ 1), (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+  }
+  for (int i = 0; i < kBarrierPolls; ++i) {
+    if (__hip_atomic_load(cnt + parity, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n) return true;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return false;
+}
 
 __device__ __forceinline__ float to_f(float v) { return v; }
 __device__ __forceinline__ float to_f(int16_t v) { return (float)(int)v; }
@@ -431,7 +465,7 @@ __device__ __forceinline__ int put_prefetch(const Args &a, const IN *__restrict_
   return e;
 }
 
-template <typename IN, typename OUT, bool SK>
+template <typename IN, typename OUT, bool SK, bool RES>
 __global__ void __launch_bounds__(kThreads, 1)
 pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ melblk_meta,
               const float *__restrict__ melblk_w, OUT *__restrict__ out, float *__restrict__ tile_min) {
@@ -488,6 +522,52 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
     __syncthreads();
   }
 
+  // single pass (RES): each wave has at most one sub-tile.  It stores its
+  // log-mel values as they come, publishes its largest mel value and meets
+  // the other workgroups at the grid barrier; its power rows stay in its LDS
+  // region meanwhile, so a wave holding a value below its clip's floor runs
+  // the mel sums again from them and overwrites its values floored.
+  __shared__ int s_ok;
+  __shared__ int64_t s_clip[kWaves];
+  __shared__ uint32_t s_max[kWaves];
+  auto res_sync = [&](uint32_t vmaxb, int64_t b) -> float {
+    // the wave's largest mel value, then one atomic per (workgroup, clip):
+    // the first wave of each run of waves on the same clip (a workgroup's
+    // sub-tiles are consecutive) takes the run's maximum to the clip's slot
+    uint32_t m = 0u;
+    if (b >= 0) {
+      m = row_max16(vmaxb);
+      m = max(max((uint32_t)__builtin_amdgcn_readlane((int)m, 0), (uint32_t)__builtin_amdgcn_readlane((int)m, 16)),
+              max((uint32_t)__builtin_amdgcn_readlane((int)m, 32), (uint32_t)__builtin_amdgcn_readlane((int)m, 48)));
+    }
+    if (lane == 0) {
+      s_clip[wv] = b;
+      s_max[wv] = m;
+    }
+    __syncthreads();
+    if (tid < kWaves) {
+      const int64_t cb_ = s_clip[tid];
+      if (cb_ >= 0 && (tid == 0 || s_clip[tid - 1] != cb_)) {
+        uint32_t mm = s_max[tid];
+        for (int w = tid + 1; w < kWaves && s_clip[w] == cb_; ++w) mm = max(mm, s_max[w]);
+        // (epoch, bits) orders a stale slot of an earlier call below every value of this one
+        const uint64_t prev = __hip_atomic_fetch_max(a.sync + 2 + cb_, ((uint64_t)a.epoch << 32) | mm,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // consuming the old value makes the wave wait until the atomic has
+        // been performed, before the barrier below lets any arrival go out
+        asm volatile("" ::"v"((uint32_t)prev));
+      }
+    }
+    __syncthreads();
+    if (tid == 0) s_ok = grid_barrier(a.sync, a.parity, gridDim.x) ? 1 : 0;
+    __syncthreads();
+    if (b < 0) return 0.0f;
+    const uint64_t w = __hip_atomic_load(a.sync + 2 + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the clip's floor in output units; a barrier that ran out of polls gives NaN
+    return s_ok ? logmel_of(fmaxf(__uint_as_float((uint32_t)w), 1e-10f)) - 2.0f : __builtin_nanf("");
+  };
+  bool res_done = false;
+
   for (; gs < wg_end; gs += kWaves) {
     // 1. this sub-tile's samples into the wave's region (LDS operations of
     //    one wave complete in order, so no barrier is needed around them)
@@ -503,7 +583,9 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
       stage_padded<IN, SK>(a, pcm, gs, 0, span / 2, R, esc);
     }
     esc = __builtin_amdgcn_readfirstlane(esc);
-    have = gs + kWaves < wg_end && prefetch<IN>(a, pcm, gs + kWaves, span, pf);
+    // (the single pass has one sub-tile per wave: nothing to prefetch)
+    if constexpr (RES) have = false;
+    else have = gs + kWaves < wg_end && prefetch<IN>(a, pcm, gs + kWaves, span, pf);
 
     // 2. window + 16-point DFT + twiddle on the matrix cores: D[n1] = A[n1] x[n1],
     //    per n1 two fp16 products (matrix hi and lo parts) over k-slots e of
@@ -649,6 +731,12 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
     };
     int cb = 0;
     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    int res_pass = 0;           // single pass: 1 stores and finds the maximum, 2 floors and stores again
+    float res_fl = 0.0f;        // single pass: the clip's floor in output units
+    bool res_ok = true;         // single pass: the grid barrier completed
+    float res_min = __builtin_huge_valf();   // single pass: the lane's smallest output
+    OUT *const orow0 = orow;
+    (void)orow0;
     auto compute = [&](auto slot) {
       constexpr int S = decltype(slot)::value;
 #pragma unroll
@@ -659,6 +747,37 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
         for (int i = 0; i < 4; ++i) acc[i] = __builtin_amdgcn_ldexpf(acc[i], mel_e);
       }
       // block cb complete: log10, rescale, store, statistics
+      if constexpr (RES) {
+        const bool band_ok = 16 * cb + 4 * g + (c & 3) < NM;
+        float o[4];
+        if (res_pass == 1) {   // uniform: store, and keep the maximum and the lane's minimum
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = fmaxf(acc[i], 1e-10f);
+            o[i] = logmel_of(v);
+            if (band_ok && f0 + i < F) {
+              vmaxb = max(vmaxb, __float_as_uint(v));
+              res_min = fminf(res_min, o[i]);
+            }
+          }
+        } else {               // the floor is known: floor, store again
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = res_ok ? fmaxf(logmel_of(fmaxf(acc[i], 1e-10f)), res_fl) : res_fl;
+        }
+        {
+          if (sub_full && 16 * cb + 16 <= NM) {
+            store_out4(orow, o);
+          } else if (band_ok) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (f0 + i < F) store_out(orow + i, o[i]);
+          }
+        }
+        acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        ++cb;
+        orow += 16 * F;
+        return;
+      }
       float omin = __builtin_huge_valf();   // no value
       if (a.mel_out) {   // uniform: mel values as they are, no statistics
         const bool band_ok = 16 * cb + 4 * g + (c & 3) < NM;
@@ -698,17 +817,7 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
-    eR[0] = entry(0);
-    eR[1] = entry(1);
-    eR[2] = entry(2);
-    eR[3] = entry(3);
-    // loads past the last batch repeat it (every wait count stays static)
-    load(I0{}, 0);
-    load(I1{}, 1);
-    load(I2{}, 2);
-    eR[0] = entry(4);
-    // step of batch i in slot S: the entry of batch i + 5 (slot S + 1), the
-    // operands of batch i + 3 (slot S + 3), then the products of batch i
+    // the mel stage's batch pipeline: operands three batches ahead (see above)
 #define LM_MEL_STEP(S, S1, S3)                \
   {                                           \
     eR[S1::value] = entry(i + 5);             \
@@ -716,15 +825,54 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
     compute(S{});                             \
     if (++i >= NBT) break;                    \
   }
-    for (int i = 0; i < NBT;) {
-      LM_MEL_STEP(I0, I1, I3)
-      LM_MEL_STEP(I1, I2, I0)
-      LM_MEL_STEP(I2, I3, I1)
-      LM_MEL_STEP(I3, I0, I2)
+#define LM_MEL_STAGE()                                                          \
+  {                                                                             \
+    eR[0] = entry(0);                                                           \
+    eR[1] = entry(1);                                                           \
+    eR[2] = entry(2);                                                           \
+    eR[3] = entry(3);                                                           \
+    /* loads past the last batch repeat it (every wait count stays static) */  \
+    load(I0{}, 0);                                                              \
+    load(I1{}, 1);                                                              \
+    load(I2{}, 2);                                                              \
+    eR[0] = entry(4);                                                           \
+    /* step of batch i in slot S: the entry of batch i + 5 (slot S + 1), the */ \
+    /* operands of batch i + 3 (slot S + 3), then the products of batch i    */ \
+    for (int i = 0; i < NBT;) {                                                 \
+      LM_MEL_STEP(I0, I1, I3)                                                   \
+      LM_MEL_STEP(I1, I2, I0)                                                   \
+      LM_MEL_STEP(I2, I3, I1)                                                   \
+      LM_MEL_STEP(I3, I0, I2)                                                   \
+    }                                                                           \
+  }
+    if constexpr (RES) {
+      res_pass = 1;
+      LM_MEL_STAGE()
+      res_fl = res_sync(vmaxb, t.b);
+      res_ok = s_ok != 0;
+      res_done = true;
+      // only a wave holding a value below its clip's floor runs the mel sums
+      // again from its power rows (still in its LDS region) and overwrites
+      // them floored; a barrier that ran out of polls makes every wave
+      // overwrite its values with NaN
+      if (!res_ok || __any(res_min < res_fl)) {
+        res_pass = 2;
+        cb = 0;
+        acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        orow = orow0;
+        LM_MEL_STAGE()
+      }
+    } else {
+      LM_MEL_STAGE()
+      vmaxb = row_max16(vmaxb);
+      if (c == 0) a.tile_max[4 * gs + g] = __uint_as_float(vmaxb);
     }
+#undef LM_MEL_STAGE
 #undef LM_MEL_STEP
-    vmaxb = row_max16(vmaxb);
-    if (c == 0) a.tile_max[4 * gs + g] = __uint_as_float(vmaxb);
+  }
+  // a wave without a sub-tile still takes part in the workgroup's barriers
+  if constexpr (RES) {
+    if (!res_done) (void)res_sync(0u, -1);
   }
 }
 
@@ -751,6 +899,12 @@ StatLayout pcm400_stat_layout(const lm_plan *p) {
   st.band_h = 4;
   st.max_per_tile = 4;   // one per quad group of lanes
   return st;
+}
+
+bool pcm400_single_pass(const lm_plan *p, bool in_i16, int64_t n_sub) {
+  return p->single_pass && p->coop_launch && p->output == LM_OUTPUT_LOGMEL && p->fft_variant == LM_FFT_AUTO &&
+         pcm400_supported(p, in_i16) &&
+         p->n_cu > 0 && n_sub <= (int64_t)p->n_cu * kWaves;
 }
 
 hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &pa, hipStream_t s, const LaunchTiming *tm) {
@@ -792,6 +946,9 @@ hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &pa, hipStream_t s, con
   for (int bt = 0; bt < k.mel_batches; ++bt)
     if (p->melblk_meta[4 * (size_t)bt] >> 16) k.end_mask[bt >> 6] |= (uint64_t)1 << (bt & 63);
   k.tile_max = pa.tile_max;
+  k.epoch = pa.epoch;
+  k.parity = pa.parity;
+  k.sync = pa.sync;
   const dim3 grid((unsigned)n_wg), block(kThreads);
   const bool f16 = p->out_dtype == LM_F16;
   const v4f *am = reinterpret_cast<const v4f *>(p->dt.mfma400h);
@@ -799,8 +956,20 @@ hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &pa, hipStream_t s, con
   const float *bw = p->dt.melblk_w;
   float *tmin = pa.tile_min;
   const bool sk = p->hop == 160;
-#define LM_P400(IN, OUT, SK) \
-  LM_LAUNCH(tm, (pcm400_kernel<IN, OUT, SK>), grid, block, 0, s, k, am, bm, bw, (OUT *)pa.out, tmin)
+#define LM_P400(IN, OUT, SK)                                                                       \
+  do {                                                                                             \
+    if (pa.sync) {                                                                                 \
+      OUT *op = (OUT *)pa.out;                                                                     \
+      void *args[] = {&k, (void *)&am, (void *)&bm, (void *)&bw, (void *)&op, (void *)&tmin};    \
+      if (tm) (void)hipEventRecord(tm->beg, s);                                                    \
+      const hipError_t e = hipLaunchCooperativeKernel(                                             \
+          reinterpret_cast<const void *>(&pcm400_kernel<IN, OUT, SK, true>), grid, block, args, 0, s); \
+      if (e != hipSuccess) return e;                                                               \
+      if (tm) (void)hipEventRecord(tm->end, s);                                                    \
+    } else {                                                                                       \
+      LM_LAUNCH(tm, (pcm400_kernel<IN, OUT, SK, false>), grid, block, 0, s, k, am, bm, bw, (OUT *)pa.out, tmin); \
+    }                                                                                              \
+  } while (0)
   if (!pa.in_i16 && !f16) {
     if (sk) LM_P400(float, float, true);
     else LM_P400(float, float, false);

@@ -217,6 +217,16 @@ def test_binding_has_no_cpu_fallback():
         assert word not in text, word
 
 
+def test_single_pass_validation():
+    rc, h = _create()
+    assert rc == OK
+    assert _lib.lm_plan_set_single_pass(h, 1) == OK
+    assert _lib.lm_plan_set_single_pass(h, 0) == OK
+    assert _lib.lm_plan_set_single_pass(h, 2) == INVALID
+    assert _lib.lm_plan_set_single_pass(None, 1) == INVALID
+    _lib.lm_plan_destroy(h)
+
+
 def test_fft_variant_validation():
     rc, h = _create()
     assert rc == OK

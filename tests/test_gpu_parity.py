@@ -616,6 +616,32 @@ def test_pcm400_paired_variant_options(in_dtype, out_dtype, pad_mode, power):
     check(out, ref, TOL32 if out_dtype == "f32" else TOL16, f"paired {in_dtype} {out_dtype} {pad_mode} {power}")
 
 
+@pytest.mark.parametrize("n_mels", [200, 256])
+@pytest.mark.parametrize("in_dtype", ["f32", "i16"])
+def test_pcm400_many_bands_both_sides_of_the_table_limit(n_mels, in_dtype):
+    """n_fft = 400 with 200 and 256 bands.  Slaney filterbanks of any band
+    count up to 256 fit the matrix-core kernel's blocked weight table (at
+    most 5632 floats of LDS: 1536 for 200 bands, 1472 for 256); a caller's
+    dense filterbank (every bin non-zero in every band: 16 blocks of 201
+    steps, 51456 floats) does not, and runs on the generic kernel.  Both must
+    match the oracle, with a clamp-engaged clip in the batch."""
+    sr = 16000.0
+    B, T = 3, 40000
+    x = lm_synth.speech_pcm(B, T, sr, seed=n_mels + (1 if in_dtype == "i16" else 0), as_int16=(in_dtype == "i16"))
+    x[0, 10000:20000] = 0
+    W = oracle.mel_filterbank(sr, 400, n_mels)
+    say("pcm400", n_mels, "bands", in_dtype, "slaney (fits the table)")
+    out = run_pcm(x, 400, 160, n_mels, sr)
+    check(out, oracle.from_pcm(x, 400, 160, W), TOL32, f"{n_mels} bands slaney {in_dtype}")
+    rng = np.random.default_rng(n_mels)
+    D = (rng.random((n_mels, 201)) * 0.02 + 1e-4).astype(np.float32)   # dense: too wide for the table
+    say("pcm400", n_mels, "bands", in_dtype, "dense caller filterbank (generic kernel)")
+    p = lm().Plan(400, 160, n_mels).set_filters(D)
+    out2 = p.from_pcm(to_dev(x))
+    torch.cuda.synchronize()
+    check(out2, oracle.from_pcm(x, 400, 160, D.astype(np.float64)), TOL32, f"{n_mels} bands dense {in_dtype}")
+
+
 def _random_pcm_config(rng):
     """One draw of the torchaudio-style surface: n_fft, hop, center, pad
     mode, power, input and output types, window length, normalisation,

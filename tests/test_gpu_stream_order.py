@@ -164,3 +164,70 @@ def test_output_map_invariants_exact(path):
         assert o[b].min() >= fl, (b, o[b].min(), fl)
         if b == 0:
             assert (o[b] == fl).sum() > 0, "the floor should bind on clip 0"
+
+
+# ---------------------------------------------------------------------------
+# Single pass (KBench page, perf_md: the clip-resident alternative to a second
+# pass over the output)
+# ---------------------------------------------------------------------------
+
+def _run(x, n_fft, hop, n_mels, sr, single, out_dtype="f32", **kw):
+    p = lm().Plan(n_fft, hop, n_mels, out_dtype=out_dtype, **kw).set_mel(sr).set_single_pass(single)
+    out = p.from_pcm(to_dev(x))
+    torch.cuda.synchronize()
+    return out, p
+
+
+@pytest.mark.parametrize("B,T,n_mels,in_dtype,out_dtype,pad_mode", [
+    (8, 480000, 80, "f32", "f32", "reflect"),       # the 8 x 30 s float batch: 1504 sub-tiles
+    (10, 480000, 128, "i16", "f32", "reflect"),     # 1880 sub-tiles of 128 bands
+    (3, 40001, 200, "f32", "f16", "constant"),      # 200 bands, ragged length, fp16 out
+    (1, 401, 40, "i16", "f32", "replicate"),        # one sub-tile
+    (700, 3000, 64, "f32", "f32", "reflect"),       # many clips of two sub-tiles each
+])
+def test_single_pass_equals_two_pass_and_oracle(B, T, n_mels, in_dtype, out_dtype, pad_mode):
+    sr = 16000.0
+    x = lm_synth.speech_pcm(B, T, sr, seed=230 + B, as_int16=(in_dtype == "i16"))
+    if T > 20000:
+        x[0, T // 3: T // 2] = 0                          # the floor binds on clip 0
+    if B > 1:
+        x[1] = (x[1] // 100) if in_dtype == "i16" else x[1] * np.float32(1e-3)   # a quiet clip
+    say("single pass", B, T, n_mels, in_dtype, out_dtype, pad_mode)
+    one, p1 = _run(x, 400, 160, n_mels, sr, True, out_dtype, pad_mode=pad_mode)
+    two, _ = _run(x, 400, 160, n_mels, sr, False, out_dtype, pad_mode=pad_mode)
+    a, b = one.cpu().numpy(), two.cpu().numpy()
+    # identical also for fp16: both round the same fp32 values to nearest even,
+    # and rounding is monotone, so the fix-up's comparison of stored fp16
+    # values with the floor's rounding decides as the fp32 comparison would
+    assert np.array_equal(a, b), f"single vs two pass: max |diff| {np.abs(a.astype(np.float64) - b).max()}"
+    # the single pass really ran: one launch per call, no fix-up
+    p1.profile(True)
+    p1.from_pcm(to_dev(x))
+    torch.cuda.synchronize()
+    p1.profile(False)
+    prof = p1.profile_read()
+    assert prof["main"]["count"] == 1 and prof["fixup"]["count"] == 0, prof
+    n_check = min(B, 3)
+    ref = oracle.from_pcm(x[:n_check], 400, 160, oracle.mel_filterbank(sr, 400, n_mels), pad_mode=pad_mode)
+    check(one[:n_check], ref, TOL32 if out_dtype == "f32" else 2e-3, "single pass vs oracle")
+
+
+def test_single_pass_repeated_calls_and_silence():
+    """Back-to-back single-pass calls (the barrier and clip slots carry a
+    per-call tag and are never cleared): a loud batch, then a silent one,
+    then the loud one again, then batch sizes that change the grid."""
+    sr = 16000.0
+    loud = lm_synth.speech_pcm(4, 48000, sr, seed=240)
+    silent = np.zeros((4, 48000), dtype=np.float32)
+    p = lm().Plan(400, 160, 80).set_mel(sr).set_single_pass(True)
+    W = oracle.mel_filterbank(sr, 400, 80)
+    ref_loud = oracle.from_pcm(loud, 400, 160, W)
+    say("single pass repeated")
+    for rep in range(3):
+        o1 = p.from_pcm(to_dev(loud))
+        o2 = p.from_pcm(to_dev(silent))
+        o3 = p.from_pcm(to_dev(loud[:1]))
+        torch.cuda.synchronize()
+        check(o1, ref_loud, TOL32, f"loud rep {rep}")
+        assert np.abs(o2.cpu().numpy() + 1.5).max() <= 1e-6, "silence is -1.5 everywhere"
+        check(o3, ref_loud[:1], TOL32, f"one clip rep {rep}")

@@ -30,14 +30,16 @@ def _call(lib, fn, plan, x, out):
                             ctypes.c_void_p(out.data_ptr()), stream)
 
 
-@pytest.mark.parametrize("in_dtype,n_fft,hop,n_mels", [("i16", 400, 160, 128), ("f32", 400, 160, 80),
-                                                       ("f32", 1024, 256, 128)])
-def test_noalloc_matches_lm_from_pcm(in_dtype, n_fft, hop, n_mels):
+@pytest.mark.parametrize("in_dtype,n_fft,hop,n_mels,single", [("i16", 400, 160, 128, False),
+                                                              ("f32", 400, 160, 80, False),
+                                                              ("f32", 400, 160, 80, True),
+                                                              ("f32", 1024, 256, 128, False)])
+def test_noalloc_matches_lm_from_pcm(in_dtype, n_fft, hop, n_mels, single):
     import stft_log_mel_amd as lm
     lib = lm._lib
     sr = 16000.0
     i16 = in_dtype == "i16"
-    plan = lm.Plan(n_fft, hop, n_mels).set_mel(sr)
+    plan = lm.Plan(n_fft, hop, n_mels).set_mel(sr).set_single_pass(single)
     W = oracle.mel_filterbank(sr, n_fft, n_mels)
     # the plan's tables go to the device with one ordinary call
     warm = torch.from_numpy(lm_synth.speech_pcm(1, 8000, sr, seed=300, as_int16=i16)).cuda()
