@@ -19,6 +19,13 @@ namespace lm {
 // log10(2) / 4
 constexpr float kLog10_2_Q = 0.0752574989159952988f;
 
+// max(v, 1e-10f) on the bit patterns, one integer max: the signed-integer
+// order of float bits agrees with the float order whenever one operand is
+// positive (a negative v, or -0, compares below).  Unlike fmaxf it needs no
+// canonicalising of v, and it keeps a NaN (out of contract anyway).
+constexpr int kBits1e10 = 0x2edbe6ff;   // 1e-10f
+__device__ __forceinline__ float floor_1e10(float v) { return __int_as_float(max(__float_as_int(v), kBits1e10)); }
+
 // The output value of a mel value v >= 1e-10 (after the floor):
 // (log10 v + 4) / 4, as one fma on the hardware base-2 logarithm.  Every
 // kernel writes exactly this value for every element, the region minima

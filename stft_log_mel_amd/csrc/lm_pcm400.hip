@@ -302,16 +302,25 @@ __device__ __forceinline__ SubTile locate(const Args &a, int64_t gs) {
   t.s_begin = t.s * kSub * a.hop - a.pad;
   return t;
 }
+// The sub-tile n places after t (uniform; no division: at most n clip steps)
+__device__ __forceinline__ SubTile advance(const Args &a, SubTile t, int n) {
+  t.s += n;
+  while (t.s >= a.S) {
+    t.s -= a.S;
+    ++t.b;
+  }
+  t.s_begin = t.s * kSub * a.hop - a.pad;
+  return t;
+}
 
 // Issue the 16-byte loads of every chunk of the span that lies inside the
 // clip (the span must start 16-byte aligned); false if it does not, then
 // the whole span takes the padded path.
 template <typename IN>
-__device__ __forceinline__ bool prefetch(const Args &a, const IN *__restrict__ pcm, int64_t gs, int span,
+__device__ __forceinline__ bool prefetch(const Args &a, const IN *__restrict__ pcm, const SubTile &t, int span,
                                          Prefetch<IN> &pf) {
   constexpr int PER = 16 / sizeof(IN);   // samples per chunk
   const int n4 = (span + PER - 1) / PER;
-  const SubTile t = locate(a, gs);
   const IN *src = pcm + t.b * a.T + t.s_begin;
   if (n4 > 64 * Prefetch<IN>::N || (reinterpret_cast<uintptr_t>(src) & 15)) return false;
   // chunks q with 0 <= s_begin + PER q and s_begin + PER (q + 1) <= T
@@ -347,9 +356,8 @@ constexpr int kPadBatch = 8;   // dwords per lane with loads in flight together
 // clip's last frame read as 0), kPadBatch dwords per lane with all their
 // loads issued before any is used.  Float samples are scaled by 2^e.
 template <typename IN, bool SK>
-__device__ __forceinline__ void stage_padded(const Args &a, const IN *__restrict__ pcm, int64_t gs, int d_begin,
+__device__ __forceinline__ void stage_padded(const Args &a, const IN *__restrict__ pcm, const SubTile &t, int d_begin,
                                              int d_end, float *R, int e) {
-  const SubTile t = locate(a, gs);
   const IN *x = pcm + t.b * a.T;
   const int64_t s_limit = (a.F - 1) * (int64_t)a.hop - a.pad + 400;
   uint32_t *d32 = reinterpret_cast<uint32_t *>(R);
@@ -385,9 +393,8 @@ __device__ __forceinline__ void stage_padded(const Args &a, const IN *__restrict
 // Largest magnitude of the lane's samples among plane dwords [d_begin,
 // d_end) of the span, by the padded path's index arithmetic (float input).
 template <typename IN>
-__device__ __forceinline__ float padded_absmax(const Args &a, const IN *__restrict__ pcm, int64_t gs, int d_begin,
+__device__ __forceinline__ float padded_absmax(const Args &a, const IN *__restrict__ pcm, const SubTile &t, int d_begin,
                                                int d_end) {
-  const SubTile t = locate(a, gs);
   const IN *x = pcm + t.b * a.T;
   const int64_t s_limit = (a.F - 1) * (int64_t)a.hop - a.pad + 400;
   float m = 0.0f;
@@ -405,7 +412,7 @@ __device__ __forceinline__ float padded_absmax(const Args &a, const IN *__restri
 // outside them by the padded path; returns the scale exponent e of float
 // input (0 for int16).
 template <typename IN, bool SK>
-__device__ __forceinline__ int put_prefetch(const Args &a, const IN *__restrict__ pcm, int64_t gs,
+__device__ __forceinline__ int put_prefetch(const Args &a, const IN *__restrict__ pcm, const SubTile &t,
                                             const Prefetch<IN> &pf, int span, float *R) {
   constexpr bool kI16 = sizeof(IN) == 2;
   constexpr int DPC = 8 / sizeof(IN);   // plane dwords per 16-byte chunk
@@ -429,8 +436,8 @@ __device__ __forceinline__ int put_prefetch(const Args &a, const IN *__restrict_
 #pragma unroll
         for (int k = 0; k < 4; ++k) m = fmaxf(m, fabsf(__uint_as_float(pf.v[i][k])));
     }
-    if (pf.q_lo > 0) m = fmaxf(m, padded_absmax<IN>(a, pcm, gs, 0, lo_end));
-    if (hi_begin < ndw) m = fmaxf(m, padded_absmax<IN>(a, pcm, gs, hi_begin, ndw));
+    if (pf.q_lo > 0) m = fmaxf(m, padded_absmax<IN>(a, pcm, t, 0, lo_end));
+    if (hi_begin < ndw) m = fmaxf(m, padded_absmax<IN>(a, pcm, t, hi_begin, ndw));
     e = scale_exponent(wave_max(m));
   }
   const float sc = __builtin_amdgcn_ldexpf(1.0f, e);
@@ -460,9 +467,18 @@ __device__ __forceinline__ int put_prefetch(const Args &a, const IN *__restrict_
       }
     }
   }
-  if (pf.q_lo > 0) stage_padded<IN, SK>(a, pcm, gs, 0, lo_end, R, e);
-  if (hi_begin < ndw) stage_padded<IN, SK>(a, pcm, gs, hi_begin, ndw, R, e);
+  if (pf.q_lo > 0) stage_padded<IN, SK>(a, pcm, t, 0, lo_end, R, e);
+  if (hi_begin < ndw) stage_padded<IN, SK>(a, pcm, t, hi_begin, ndw, R, e);
   return e;
+}
+
+// Rank of workgroup id w among G workgroups when consecutive ids are dealt
+// to the kXcds XCDs in turn: XCD x = w mod kXcds holds ranks [start_x,
+// start_x + count_x), so each XCD's workgroups take consecutive ranks.
+__device__ __forceinline__ int xcd_rank(int w, int G) {
+  const int x = w % kXcds, j = w / kXcds;
+  const int q = G / kXcds, r = G % kXcds;   // XCDs below r hold q + 1 workgroups
+  return x * q + min(x, r) + j;
 }
 
 template <typename IN, typename OUT, bool SK, bool RES>
@@ -487,9 +503,14 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
   const int NM = a.n_mels, NB = a.n_melblk;
   const int64_t F = a.F;
 
-  const int64_t wg0 = (int64_t)blockIdx.x * a.per_wg;
+  // workgroup ids go to the XCDs in turn (each with its own L2); dealing the
+  // sub-tile ranges so that each XCD's workgroups take consecutive ranges
+  // keeps the output lines shared by neighbouring ranges (a 16-frame run is
+  // 64 bytes of a band row) and the input overlap in one L2
+  const int64_t wg0 = (int64_t)xcd_rank(blockIdx.x, gridDim.x) * a.per_wg;
   const int64_t wg_end = min(wg0 + a.per_wg, a.n_sub);
   int64_t gs = wg0 + wv;
+  SubTile tc = locate(a, gs);   // the sub-tile gs (clip, index, first sample)
   Prefetch<IN> pf;
   bool have;
   {
@@ -509,7 +530,7 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
       const int i = tid + u * kThreads;
       w[u] = i < a.melw_n ? melblk_w[i] : 0.0f;
     }
-    have = gs < wg_end && prefetch<IN>(a, pcm, gs, span, pf);
+    have = gs < wg_end && prefetch<IN>(a, pcm, tc, span, pf);
 #pragma unroll
     for (int u = 0; u < PER; ++u)
       if (tid + u * kThreads < kTab) s_amat[tid + u * kThreads] = v[u];
@@ -573,19 +594,26 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
     //    one wave complete in order, so no barrier is needed around them)
     int esc;   // float input: the sub-tile's scale exponent (uniform)
     if (have) {
-      esc = put_prefetch<IN, SK>(a, pcm, gs, pf, span, R);
+      esc = put_prefetch<IN, SK>(a, pcm, tc, pf, span, R);
     } else {
       // no prefetch load is in flight on this path (prefetch returned false),
       // which the compiler cannot tell: retire the registers here as well
 #pragma unroll
       for (int i = 0; i < Prefetch<IN>::N; ++i) asm volatile("" ::"v"(pf.v[i]));
-      esc = kI16 ? 0 : scale_exponent(wave_max(padded_absmax<IN>(a, pcm, gs, 0, span / 2)));
-      stage_padded<IN, SK>(a, pcm, gs, 0, span / 2, R, esc);
+      esc = kI16 ? 0 : scale_exponent(wave_max(padded_absmax<IN>(a, pcm, tc, 0, span / 2)));
+      stage_padded<IN, SK>(a, pcm, tc, 0, span / 2, R, esc);
     }
     esc = __builtin_amdgcn_readfirstlane(esc);
     // (the single pass has one sub-tile per wave: nothing to prefetch)
-    if constexpr (RES) have = false;
-    else have = gs + kWaves < wg_end && prefetch<IN>(a, pcm, gs + kWaves, span, pf);
+    const SubTile t = tc;
+    if constexpr (RES) {
+      have = false;
+    } else if (gs + kWaves < wg_end) {
+      tc = advance(a, tc, kWaves);
+      have = prefetch<IN>(a, pcm, tc, span, pf);
+    } else {
+      have = false;
+    }
 
     // 2. window + 16-point DFT + twiddle on the matrix cores: D[n1] = A[n1] x[n1],
     //    per n1 two fp16 products (matrix hi and lo parts) over k-slots e of
@@ -704,7 +732,6 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
     //    later needs (LDS reads complete in order, so a wait for an entry
     //    never waits for the operand loads issued after it).
     asm volatile("" ::: "memory");   // keep the table reads below out of the transform's register peak
-    const SubTile t = locate(a, gs);
     const int64_t f0 = t.s * kSub + 4 * (c >> 2);
     const bool sub_full = t.s * kSub + kSub <= F;   // uniform: every frame of the sub-tile exists
     OUT *orow = out + t.b * (int64_t)NM * F + (int64_t)(4 * g + (c & 3)) * F + f0;   // block 0's band
@@ -753,7 +780,7 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
         if (res_pass == 1) {   // uniform: store, and keep the maximum and the lane's minimum
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float v = fmaxf(acc[i], 1e-10f);
+            const float v = floor_1e10(acc[i]);
             o[i] = logmel_of(v);
             if (band_ok && f0 + i < F) {
               vmaxb = max(vmaxb, __float_as_uint(v));
@@ -762,7 +789,7 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
           }
         } else {               // the floor is known: floor, store again
 #pragma unroll
-          for (int i = 0; i < 4; ++i) o[i] = res_ok ? fmaxf(logmel_of(fmaxf(acc[i], 1e-10f)), res_fl) : res_fl;
+          for (int i = 0; i < 4; ++i) o[i] = res_ok ? fmaxf(logmel_of(floor_1e10(acc[i])), res_fl) : res_fl;
         }
         {
           if (sub_full && 16 * cb + 16 <= NM) {
@@ -788,7 +815,7 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
         float o[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float v = fmaxf(acc[i], 1e-10f);
+          const float v = floor_1e10(acc[i]);
           vmaxb = max(vmaxb, __float_as_uint(v));
           o[i] = logmel_of(v);
           omin = fminf(omin, o[i]);
@@ -798,7 +825,7 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
         const bool band_ok = 16 * cb + 4 * g + (c & 3) < NM;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float v = fmaxf(acc[i], 1e-10f);
+          const float v = floor_1e10(acc[i]);
           if (band_ok && f0 + i < F) {
             const float o = logmel_of(v);
             vmaxb = max(vmaxb, __float_as_uint(v));
