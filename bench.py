@@ -184,6 +184,153 @@ def lm_synth_inputs(w):
     return lm_synth.make_inputs(w)
 
 
+PER_CONFIG = ("stft_b1", "pcm_f32_b8", "stft_b256", "pcm_f32_nfft16384")
+
+
+def first_stage_dtype(w, fft_variant: str) -> str:
+    """The arithmetic the workload's transform runs in."""
+    if w.entry == "pcm" and main_kernel_name(w, fft_variant) == "pcm400_kernel":
+        return "f32 (n_fft 400 first stage: two-part fp16 operands, fp32 accumulate)"
+    return "f32"
+
+
+class Run:
+    """One workload resident on the GPU: inputs (several buffer sets, so that
+    every step reads cold input), outputs, plan, and a step that runs the
+    whole path once."""
+
+    def __init__(self, w, dev, fft_variant="auto", single_pass=False, log=True):
+        import torch
+
+        import lm_synth
+        import stft_log_mel_amd as lm
+
+        self.w = w
+        if log:
+            print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
+        t0 = time.time()
+        if w.entry == "stft":
+            self.host_in, self.host_filters = lm_synth.make_inputs(w)
+        else:
+            self.host_in, self.host_filters = lm_synth.make_inputs(w), None
+        if log:
+            print(f"[bench] inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+        self.nbuf = max(1, min(8, -(-1_000_000_000 // w.essential_bytes()) + 1))   # cycle >= ~1 GB of buffers
+        self.ins = [torch.from_numpy(self.host_in).to(dev) for _ in range(self.nbuf)]
+        out_dt = torch.float16 if w.out_dtype == "f16" else torch.float32
+        self.outs = [torch.empty(w.out_shape, dtype=out_dt, device=dev) for _ in range(self.nbuf)]
+        if w.entry == "stft":
+            self.filt = torch.from_numpy(self.host_filters).to(dev)
+            self.plan = lm.Plan(400, 160, w.NM)
+        else:
+            self.plan = lm.Plan(w.n_fft, w.hop, w.n_mels, w.center, w.pad_mode, w.power, w.out_dtype)
+            self.plan.set_mel(w.sample_rate, w.f_min, w.f_max)
+            self.plan.set_fft_variant(fft_variant)
+            self.plan.set_single_pass(single_pass)
+        self.stream = torch.cuda.current_stream(dev)
+
+    def step(self, i):
+        if self.w.entry == "stft":
+            self.plan.from_stft(self.ins[i % self.nbuf], self.filt, out=self.outs[i % self.nbuf])
+        else:
+            self.plan.from_pcm(self.ins[i % self.nbuf], out=self.outs[i % self.nbuf])
+
+    def time(self, steps, warmup):
+        """Mean ms per step over `steps` back-to-back steps (events only
+        around the whole run), then per-step times from a second run with an
+        event between steps, then the same steps with every launch stamped
+        by its own dispatch (per-kernel means)."""
+        import torch
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t_wall = time.perf_counter()
+        ev0.record(self.stream)
+        for i in range(steps):
+            self.step(i)
+        ev1.record(self.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_wall
+        ms = ev0.elapsed_time(ev1) / steps
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        evs[0].record(self.stream)
+        for i in range(steps):
+            self.step(i)
+            evs[i + 1].record(self.stream)
+        torch.cuda.synchronize()
+        per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+        pct = lambda q: per[min(len(per) - 1, int(round(q * (len(per) - 1))))]   # noqa: E731
+        self.plan.profile(True)
+        for i in range(steps):
+            self.step(i)
+        torch.cuda.synchronize()
+        self.plan.profile(False)
+        prof = self.plan.profile_read()
+        kern = {k: prof[k]["ms"] / max(1, prof[k]["count"]) for k in ("main", "fixup", "pack")}
+        return {"ms_per_step": ms, "wall_s": wall, "p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9),
+                "kernel_ms": kern}
+
+    def last_output(self, steps):
+        return self.outs[(steps - 1) % self.nbuf]
+
+    def oracle_clip(self, b):
+        import oracle
+        w = self.w
+        if w.entry == "stft":
+            return oracle.from_stft(self.host_in[b:b + 1], self.host_filters)[0]
+        W = oracle.mel_filterbank(w.sample_rate, w.n_fft, w.n_mels, w.f_min, w.f_max)
+        return oracle.from_pcm(self.host_in[b:b + 1], w.n_fft, w.hop, W, center=w.center,
+                               pad_mode=w.pad_mode, power=w.power)[0]
+
+
+def roofline_of(w, kernel_ms, fft_variant="auto"):
+    """The main kernel against its bounding roofline: HBM bytes for every
+    workload except the n_fft 16384 one, whose bound is the FFT arithmetic
+    (nominal flops against the fp32 vector peak)."""
+    frames = w.B * w.n_frames
+    if w.entry == "pcm" and w.n_fft >= 8192:
+        tf = frames * flops_per_frame(w) / (kernel_ms / 1e3) / 1e12
+        return {"bound": "alu", "achieved": round(tf, 2), "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4),
+                "frac_of_unpacked_fp32": round(tf / (FP32_VALU_PEAK_TFLOPS / 2), 4),
+                "algorithmic_flops_per_launch": round(frames * flops_per_frame(w)),
+                "kernel": main_kernel_name(w, fft_variant), "kernel_ms": round(kernel_ms, 5)}
+    gbs = w.essential_bytes() / (kernel_ms / 1e3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": counter_traffic(w.name),
+            "algorithmic_bytes_per_launch": w.essential_bytes(),
+            "kernel": main_kernel_name(w, fft_variant), "kernel_ms": round(kernel_ms, 5)}
+
+
+def per_config_entry(name, steps, warmup, dev, check_clips):
+    """Time one of the other workloads and check a few of its clips."""
+    import numpy as np
+
+    import lm_synth
+    w = lm_synth.WORKLOADS[name]
+    r = Run(w, dev, log=False)
+    t = r.time(steps, warmup)
+    got = r.last_output(steps).float().cpu().numpy()
+    errs = [float(np.abs(got[b].astype(np.float64) - r.oracle_clip(b)).max()) for b in range(min(w.B, check_clips))]
+    frames = w.B * w.n_frames
+    entry = {
+        "workload": w.name, "entry": f"lm_from_{w.entry}", "shape_in": list(r.host_in.shape),
+        "shape_out": list(w.out_shape), "out": w.out_dtype, "dtype": first_stage_dtype(w, "auto"),
+        "ms_per_step": round(t["ms_per_step"], 5),
+        "ms_per_step_p10_p50_p90": [round(t["p10"], 5), round(t["p50"], 5), round(t["p90"], 5)],
+        "frames_per_s": round(frames / (t["ms_per_step"] / 1e3), 1),
+        "main_kernel_us": round(t["kernel_ms"]["main"] * 1e3, 2),
+        "fixup_us": round(t["kernel_ms"]["fixup"] * 1e3, 2), "pack_us": round(t["kernel_ms"]["pack"] * 1e3, 2),
+        "hbm_gbs_step": round(w.essential_bytes() / (t["ms_per_step"] / 1e3) / 1e9, 1),
+        "roofline": roofline_of(w, t["kernel_ms"]["main"]),
+        "parity": {"clips_checked": len(errs), "max_abs_err": max(errs),
+                   "tol": 2e-3 if w.out_dtype == "f16" else 1e-4},
+    }
+    del r
+    return entry
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -191,7 +338,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="pcm_i16_b64")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-per-config", action="store_true", help="time only the headline workload")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--fft-variant", default="auto", choices=["auto", "folded", "paired"],
+                    help="n_fft = 400 transform (comparison only; auto is the library's choice)")
+    ap.add_argument("--single-pass", action="store_true",
+                    help="use the one-launch (cooperative) form of the per-clip floor where it applies")
     ap.add_argument("--sweep", action="store_true",
                     help="time every n_fft of the sweep workloads (one JSON line each, no CPU leg)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -220,7 +372,6 @@ def main():
         return
 
     import lm_synth
-    import stft_log_mel_amd as lm
 
     if args.dft_gemm:
         dft_gemm_probe(lm_synth.WORKLOADS["pcm_i16_b64"], args.steps, args.warmup)
@@ -234,120 +385,86 @@ def main():
     w = lm_synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
-    t0 = time.time()
-    if w.entry == "stft":
-        host_in, host_filters = lm_synth.make_inputs(w)
-    else:
-        host_in = lm_synth.make_inputs(w)
-    print(f"[bench] inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
-
+    run = Run(w, dev, args.fft_variant, args.single_pass)
+    torch.cuda.synchronize()
+    t = run.time(args.steps, args.warmup)
+    ms_per_step = t["ms_per_step"]
+    main_ms, fix_ms, pack_ms = t["kernel_ms"]["main"], t["kernel_ms"]["fixup"], t["kernel_ms"]["pack"]
     per_step_bytes = w.essential_bytes()
-    nbuf = max(1, min(8, -(-1_000_000_000 // per_step_bytes) + 1))   # cycle >= ~1 GB of buffers
-    ins = [torch.from_numpy(host_in).to(dev) for _ in range(nbuf)]
-    out_dt = torch.float16 if w.out_dtype == "f16" else torch.float32
-    outs = [torch.empty(w.out_shape, dtype=out_dt, device=dev) for _ in range(nbuf)]
-    if w.entry == "stft":
-        filt = torch.from_numpy(host_filters).to(dev)
-        plan = lm.Plan(400, 160, w.NM)
-
-        def step(i):
-            plan.from_stft(ins[i % nbuf], filt, out=outs[i % nbuf])
-    else:
-        plan = lm.Plan(w.n_fft, w.hop, w.n_mels, w.center, w.pad_mode, w.power, w.out_dtype)
-        plan.set_mel(w.sample_rate, w.f_min, w.f_max)
-
-        def step(i):
-            plan.from_pcm(ins[i % nbuf], out=outs[i % nbuf])
-    torch.cuda.synchronize()
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps, {nbuf} buffer sets)", file=sys.stderr, flush=True)
-
-    # timed region: K steps exactly as a caller runs them (no per-launch events)
-    stream = torch.cuda.current_stream(dev)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    ms_total = ev0.elapsed_time(ev1)
-    ms_per_step = ms_total / args.steps
-    # the same K steps again with every launch stamped by its own dispatch
-    # (start and end events on the kernel's stream): per-kernel durations
-    plan.profile(True)
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    plan.profile(False)
-    prof = plan.profile_read()
     frames = w.B * w.n_frames
     value = frames / (ms_per_step / 1e3)
-    main_ms = prof["main"]["ms"] / max(1, prof["main"]["count"])
-    fix_ms = prof["fixup"]["ms"] / max(1, prof["fixup"]["count"])
-    pack_ms = prof["pack"]["ms"] / max(1, prof["pack"]["count"])
-    achieved = per_step_bytes / (main_ms / 1e3) / 1e9
-    print(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step (wall {wall:.3f}s), "
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step (wall {t['wall_s']:.3f}s), "
           f"main kernel {main_ms:.4f} ms, fixup {fix_ms:.4f} ms, pack {pack_ms:.4f} ms", file=sys.stderr, flush=True)
+    got = run.last_output(args.steps).float().cpu().numpy()
+
+    # the same batch through the all-fp32 folded transform (n_fft = 400 only):
+    # the error the two-part fp16 first stage adds is read against it below
+    got_fp32 = None
+    if w.entry == "pcm" and main_kernel_name(w, args.fft_variant) == "pcm400_kernel" and not args.no_cpu:
+        plan32 = __import__("stft_log_mel_amd").Plan(w.n_fft, w.hop, w.n_mels, w.center, w.pad_mode, w.power,
+                                                      w.out_dtype)
+        plan32.set_mel(w.sample_rate, w.f_min, w.f_max).set_fft_variant("folded")
+        got_fp32 = plan32.from_pcm(run.ins[0]).float().cpu().numpy()
+        del plan32
 
     # context: this GPU's streaming-copy rate (2 GiB read + 2 GiB written)
     cbuf = torch.empty(1 << 29, dtype=torch.float32, device=dev)
     cdst = torch.empty_like(cbuf)
     cdst.copy_(cbuf)
     torch.cuda.synchronize()
-    ev0.record(stream)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(run.stream)
     for _ in range(5):
         cdst.copy_(cbuf)
-    ev1.record(stream)
+    ev1.record(run.stream)
     torch.cuda.synchronize()
     copy_gbs = 5 * 2 * cbuf.numel() * 4 / (ev0.elapsed_time(ev1) / 1e3) / 1e9
     del cbuf, cdst
 
-    # parity spot check of the timed output against the first clip's oracle
-    parity = None
-    cpu = None
+    per_config = None
+    if not args.no_per_config and args.workload == "pcm_i16_b64":
+        per_config = {}
+        for name in PER_CONFIG:
+            print(f"[bench] per-config {name}", file=sys.stderr, flush=True)
+            per_config[name] = per_config_entry(name, args.steps, args.warmup, dev,
+                                                check_clips=1 if name != "stft_b256" else 2)
+            torch.cuda.empty_cache()
+
+    # the fp64 oracle on this host's cores, clips in order, cycling through the
+    # batch again until about cpu_seconds have passed; each clip's first pass is
+    # also a parity check of the timed output (and of the all-fp32 path's)
+    parity = cpu = parity32 = None
     if not args.no_cpu:
-        import oracle
         from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-        if w.entry == "stft":
-            W = host_filters
-            run_clip = lambda b: oracle.from_stft(host_in[b:b + 1], W)     # noqa: E731
-        else:
-            W = oracle.mel_filterbank(w.sample_rate, w.n_fft, w.n_mels, w.f_min, w.f_max)
-            run_clip = lambda b: oracle.from_pcm(host_in[b:b + 1], w.n_fft, w.hop, W,    # noqa: E731
-                                                 center=w.center, pad_mode=w.pad_mode, power=w.power)
-        got = outs[(args.steps - 1) % nbuf].float().cpu().numpy()
-        # clips in order, cycling through the batch again until about
-        # cpu_seconds have passed; each clip's first pass is also a parity check
+        blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
         t_cpu = time.perf_counter()
         done = 0
-        errs = []
+        errs, errs32 = [], []
         sq_err = sq_ref = 0.0
         while True:
-            ref = run_clip(done % w.B)
+            ref = run.oracle_clip(done % w.B)
             if done < w.B:
-                d = got[done].astype(np.float64) - ref[0]
+                d = got[done].astype(np.float64) - ref
                 errs.append(float(np.abs(d).max()))
                 sq_err += float((d * d).sum())
-                sq_ref += float((ref[0] * ref[0]).sum())
+                sq_ref += float((ref * ref).sum())
+                if got_fp32 is not None:
+                    errs32.append(float(np.abs(got_fp32[done].astype(np.float64) - ref).max()))
             done += 1
             if time.perf_counter() - t_cpu >= args.cpu_seconds:
                 break
         dt = time.perf_counter() - t_cpu
-        cpu = {"value": round(done * w.n_frames / dt, 1), "unit": "frames/s", "cores": int(threads),
-               "kind": "oracle",
+        cpu = {"value": round(done * w.n_frames / dt, 1), "unit": "frames/s",
+               "cores": len(os.sched_getaffinity(0)), "blas_threads": int(blas_threads), "kind": "oracle",
                "sample": f"{done} clips ({done * w.n_frames} frames) of the same workload, taken in order "
                          f"and cycling through its {w.B} clips, fp64 numpy oracle, {dt:.1f}s"}
         parity = {"clips_checked": len(errs), "max_abs_err": max(errs),
                   "rel_frobenius": (sq_err / sq_ref) ** 0.5 if sq_ref > 0 else 0.0,
                   "tol": 2e-3 if w.out_dtype == "f16" else 1e-4}
+        if errs32:
+            parity32 = {"clips_checked": len(errs32), "max_abs_err": max(errs32),
+                        "path": "folded 200-point transform, all fp32 (lm_plan_set_fft_variant LM_FFT_FOLDED)",
+                        "tol": 1e-4}
         print(f"[bench] oracle: {done} clips in {dt:.1f}s, max |err| {max(errs):.2e}", file=sys.stderr,
               flush=True)
 
@@ -360,31 +477,26 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step_p10_p50_p90": [round(t["p10"], 5), round(t["p50"], 5), round(t["p90"], 5)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": first_stage_dtype(w, args.fft_variant),
         "data": "synthetic (seeded speech-like int16 PCM)" if w.entry == "pcm" else "synthetic (seeded STFT)",
         "config": {
             "workload": w.name, "entry": f"lm_from_{w.entry}", "B": w.B,
             **({"T": w.T, "sample_rate": w.sample_rate, "n_fft": w.n_fft, "hop": w.hop, "n_mels": w.n_mels,
                 "center": w.center, "pad_mode": w.pad_mode, "power": w.power, "in": w.in_dtype,
-                "mel": "slaney/slaney-norm", "f_min": w.f_min, "f_max": w.f_max}
+                "mel": "slaney/slaney-norm", "f_min": w.f_min, "f_max": w.f_max,
+                "fft_variant": args.fft_variant, "single_pass": bool(args.single_pass)}
                if w.entry == "pcm" else {"F": w.F, "NF": w.NF, "NM": w.NM, "in": "complex64",
                                          "filters": "linear triangles (fp32)"}),
             "out": w.out_dtype, "frames_per_step": frames, "essential_bytes_per_step": per_step_bytes,
-            "buffer_sets": nbuf,
+            "buffer_sets": run.nbuf,
         },
         "hbm_gbs_step": round(per_step_bytes / (ms_per_step / 1e3) / 1e9, 1),
         "hbm_frac_step": round(per_step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-        "roofline": {
-            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": counter_traffic(w.name),
-            "kernel": main_kernel_name(w),
-            "kernel_ms": round(main_ms, 5),
-            "algorithmic_bytes_per_launch": per_step_bytes,
-        },
+        "roofline": roofline_of(w, main_ms, args.fft_variant),
         "alu_context": {
             "nominal_flop_per_frame": round(fpf, 1),
             "tflops": round(frames * fpf / (main_ms / 1e3) / 1e12, 2),
@@ -392,12 +504,14 @@ def main():
             "fp32_vector_unpacked_peak_tflops": FP32_VALU_PEAK_TFLOPS / 2,
         },
         "copy_context": {"copy_gbs": round(copy_gbs, 1),
-                         "main_kernel_frac_of_copy": round(achieved / copy_gbs, 4),
+                         "main_kernel_frac_of_copy": round(per_step_bytes / (main_ms / 1e3) / 1e9 / copy_gbs, 4),
                          "note": "torch copy_ of 2 GiB device to device, read + write bytes per second"},
         "fixup_ms": round(fix_ms, 5),
         "pack_ms": round(pack_ms, 5),
         "cpu_baseline": cpu,
         "parity": parity,
+        "parity_fp32_path": parity32,
+        "per_config": per_config,
     }
     print(json.dumps(line), flush=True)
 
