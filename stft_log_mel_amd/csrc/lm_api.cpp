@@ -79,7 +79,8 @@ int upload_tables(lm_plan *p, hipStream_t s) {
     for (int m = 0; m < NM; ++m)
       if (p->csr.width[m] == 0) empty.push_back(m);
   size_t o_eb = align256(o_t2 + sizeof(float) * p->twid2.size());
-  size_t total = align256(o_eb + sizeof(int32_t) * empty.size() + 16);
+  size_t o_ml = align256(o_eb + sizeof(int32_t) * empty.size());
+  size_t total = align256(o_ml + sizeof(int32_t) * p->mel_lanes.size() + 16);
   Staging *stg = nullptr;
   int rc = acquire_staging(p, total, &stg);
   if (rc != LM_OK) return rc;
@@ -102,6 +103,7 @@ int upload_tables(lm_plan *p, hipStream_t s) {
   }
   if (!p->twid2.empty()) std::memcpy(host + o_t2, p->twid2.data(), sizeof(float) * p->twid2.size());
   if (!empty.empty()) std::memcpy(host + o_eb, empty.data(), sizeof(int32_t) * empty.size());
+  if (!p->mel_lanes.empty()) std::memcpy(host + o_ml, p->mel_lanes.data(), sizeof(int32_t) * p->mel_lanes.size());
   void *d = nullptr;
   hipError_t e = hipMallocAsync(&d, total, s);
   if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(tables)");
@@ -130,6 +132,7 @@ int upload_tables(lm_plan *p, hipStream_t s) {
   p->dt.n_melblk = p->have_filters ? (p->n_mels + 15) / 16 : 0;
   p->dt.empty_bands = reinterpret_cast<const int32_t *>(c + o_eb);
   p->dt.n_empty = (int)empty.size();
+  p->dt.mel_lanes = p->mel_lanes.empty() ? nullptr : reinterpret_cast<const int32_t *>(c + o_ml);
   p->tables_dirty = false;
   return LM_OK;
 }

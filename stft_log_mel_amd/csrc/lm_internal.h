@@ -36,6 +36,8 @@ constexpr int kMelBatch = 4;
 // Accelerator complex dies (XCDs) of the chip, each with its own L2;
 // consecutive workgroup ids are handed to them in turn.
 constexpr int kXcds = 8;
+// Threads of the one-frame kernel's workgroup (n_fft 8192 and 16384).
+constexpr int kBigThreads = 1024;
 
 // Set the thread-local error text and return `status`.
 int fail(int status, const std::string &msg);
@@ -70,6 +72,7 @@ struct DeviceTables {
   int n_melblk = 0;
   const int32_t *empty_bands = nullptr;   // bands with no non-zero weight, ascending
   int n_empty = 0;
+  const int32_t *mel_lanes = nullptr;     // n_fft >= 8192: kBigThreads entries (build_mel_lanes)
 };
 
 struct ProfileRec {
@@ -105,6 +108,7 @@ struct lm_plan {
   std::vector<uint16_t> mfma400h;  // n_fft = 400 only: first-stage matrix as fp16 hi/lo parts (25 x 2 x 2 x 16 x 8)
   std::vector<int32_t> melblk_meta;  // per batch of mel steps: first bin of each quad, last-batch flag
   std::vector<float> melblk_w;       // blocked filter weights in matrix-core lane order
+  std::vector<int32_t> mel_lanes;    // n_fft >= 8192: mel lane table of the one-frame kernel (build_mel_lanes)
 
   int device = -1;                // bound at first launch
   int n_cu = 0;                   // compute units of that device
@@ -159,6 +163,7 @@ void build_window(lm_plan *p);
 void build_twiddles(lm_plan *p);
 void build_mfma400(lm_plan *p);
 void build_mel_blocks(lm_plan *p);
+void build_mel_lanes(lm_plan *p, int threads);
 Csr pack_dense(const float *dense, int n_rows, int n_bins);
 
 // Kernel launchers.  Each returns hipSuccess or the launch error.

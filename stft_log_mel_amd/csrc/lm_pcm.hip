@@ -80,7 +80,7 @@ __device__ __forceinline__ void fft_pass(float2 *buf, TW tw, int tid) {
       if (Ns > 1) {
         const int k = j % Ns;
 #pragma unroll
-        for (int t = 1; t < R; ++t) v[i][t] = cmul(v[i][t], tw(t * k * TW_STEP));
+        for (int t = 1; t < R; ++t) v[i][t] = cmul(v[i][t], tw.template at<TW_STEP>(t * k));
       }
       dft<R>(v[i]);
     }
@@ -106,7 +106,18 @@ __device__ __forceinline__ void fft_passes(float2 *buf, TW tw, int tid) {
   if constexpr (sizeof...(Rest) > 0) fft_passes<M, FPB, THREADS, Ns * R, PAD, TW, Rest...>(buf, tw, tid);
 }
 
-// `tw(j)` returns exp(-2 pi i j / M) for 0 <= j < M; `tid` is the thread's
+// A twiddle source for fft_pass: at<STEP>(q) returns exp(-2 pi i q STEP / M)
+// (0 <= q STEP < M) from a function of the table index j = q STEP.
+template <typename F>
+struct TwFn {
+  F f;
+  template <int STEP>
+  __device__ __forceinline__ float2 at(int q) const { return f(q * STEP); }
+};
+template <typename F>
+__device__ __forceinline__ TwFn<F> tw_fn(F f) { return TwFn<F>{f}; }
+
+// `tw.at<STEP>(q)` returns exp(-2 pi i q STEP / M); `tid` is the thread's
 // index in the workgroup; point i of frame f sits at lds_pos<PAD>(f M + i)
 template <int M, int FPB, int THREADS, int PAD, typename TW, int... R>
 __device__ __forceinline__ void run_fft(float2 *buf, TW tw, Radices<R...>, int tid) {
@@ -128,6 +139,8 @@ struct PcmKernelArgs {
   const float *window;
   const float2 *twiddle, *untangle;
   const float2 *tw2;    // n_fft >= 8192: exp(-2 pi i 128 h / n_fft) for h < n_fft / 128, then exp(-2 pi i l / n_fft), l < 128
+  const int32_t *mel_lanes;   // n_fft >= 8192: the mel stage's lane table (band | h << 8 | log2 L << 16, or -1)
+  int hann_tw;          // n_fft >= 8192: 1 if the window is the full-length periodic Hann (derived from tw2)
   const int32_t *csr_start, *csr_width, *csr_off;
   const float *csr_w;
   int nnz;
@@ -219,10 +232,10 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
     const float2 *__restrict__ twt = a.twiddle;
     run_fft<NFFT, NP, THREADS, PAD>(
         s_buf,
-        [=](int j) {
+        tw_fn([=](int j) {
           const float2 t = twt[j >> 1];
           return (j & 1) ? cmul(t, make_float2(kW400_1c, kW400_1s)) : t;
-        },
+        }),
         Radices<16, 5, 5>{}, tid);
     // 3'. split into the two frames' spectra, |2 X|^2 in the power tile
     constexpr int NK = NFFT / 2 + 1;
@@ -287,7 +300,7 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
 
   // 2. M-point complex FFT per frame
   const float2 *__restrict__ twt = a.twiddle;
-  run_fft<M, FPB, THREADS, PAD>(s_buf, [=](int j) { return twt[j]; }, typename PcmCfg<NFFT>::Rad{}, tid);
+  run_fft<M, FPB, THREADS, PAD>(s_buf, tw_fn([=](int j) { return twt[j]; }), typename PcmCfg<NFFT>::Rad{}, tid);
 
   // 3. split into the real spectrum; power tile over the same LDS
   constexpr int NU = M / 2 + 1;              // pairs (k, M-k), k = 0..M/2
@@ -384,11 +397,28 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
 // ---------------------------------------------------------------------------
 template <int NFFT>
 struct BigCfg;
-template <> struct BigCfg<8192>  { static constexpr int THREADS = 1024; using Rad = Radices<16, 16, 16>; };
-template <> struct BigCfg<16384> { static constexpr int THREADS = 1024; using Rad = Radices<16, 8, 8, 8>; };
+template <> struct BigCfg<8192>  { static constexpr int THREADS = kBigThreads; using Rad = Radices<8, 8, 8, 8>; };
+template <> struct BigCfg<16384> { static constexpr int THREADS = kBigThreads; using Rad = Radices<16, 8, 8, 8>; };
 
 constexpr int kTwLo = 128;   // entries of the low twiddle table
 constexpr int kBigPad = 5;   // FFT buffer: one spare point per 32
+
+// Twiddles of the one-frame kernel's M-point FFT from the two-level LDS
+// table: exp(-2 pi i q STEP / M) = exp(-2 pi i j / N) with j = 2 q STEP =
+// 128 h + l, the product of hi[h] and lo[l]; where every j of a pass is a
+// multiple of 128 (the early passes) the low factor is exactly 1 and the
+// twiddle is one table entry.
+template <int THI>
+struct BigTw {
+  const float2 *s_tw;   // THI entries exp(-2 pi i 128 h / N), then kTwLo entries exp(-2 pi i l / N)
+  template <int STEP>
+  __device__ __forceinline__ float2 at(int q) const {
+    constexpr int S = 2 * STEP;
+    const int j = q * S;
+    if constexpr (S % kTwLo == 0) return s_tw[j / kTwLo];
+    else return cmul(s_tw[j >> 7], s_tw[THI + (j & (kTwLo - 1))]);
+  }
+};
 
 template <int NFFT>
 constexpr int big_wlds() {
@@ -441,8 +471,9 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS) pcm_big_kernel(PcmKerne
   const int nnz = stage_filters<THREADS>(NM, a.csr_start, a.csr_width, a.csr_off, a.csr_w, a.nnz, s_start, s_width,
                                          s_off, s_w, WLDS);
   const bool w_in_lds = nnz <= WLDS;
-  int L = 64;   // lanes per band (uniform)
-  while (L > 1 && L * NM > THREADS) L >>= 1;
+  // this thread's place in the mel stage: band, position h in the band's
+  // group of Lb lanes (or none)
+  const int lane_ent = a.mel_lanes[threadIdx.x];
   const int64_t T = a.T, F = a.F;
   constexpr int IPT = M / THREADS;   // complex points per thread
   static_assert(M % THREADS == 0, "whole points per thread");
@@ -488,7 +519,19 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS) pcm_big_kernel(PcmKerne
     const int64_t b = tile / a.tiles_per_clip;
     const int64_t fr = tile - b * a.tiles_per_clip;   // one frame per tile
     // 1. windowed samples z[n] = (w[2n] x[2n], w[2n+1] x[2n+1])
-    if (have) {
+    if (have && a.hann_tw) {
+      // periodic Hann w[n] = 1/2 - 1/2 cos(2 pi n / N), the cosine from the
+      // twiddle table in LDS (no global load at the start of the frame)
+#pragma unroll
+      for (int u = 0; u < IPT; ++u) {
+        const int n = tid + u * THREADS;
+        const float2 h0 = s_tw[(2 * n) >> 7], l0 = s_tw[THI + ((2 * n) & (kTwLo - 1))];
+        const float2 h1 = s_tw[(2 * n + 1) >> 7], l1 = s_tw[THI + ((2 * n + 1) & (kTwLo - 1))];
+        const float c0 = __builtin_fmaf(h0.x, l0.x, -h0.y * l0.y), c1 = __builtin_fmaf(h1.x, l1.x, -h1.y * l1.y);
+        s_buf[lds_pos<kBigPad>(n)] = make_float2(xs[u][0] * __builtin_fmaf(-0.5f, c0, 0.5f),
+                                                 xs[u][1] * __builtin_fmaf(-0.5f, c1, 0.5f));
+      }
+    } else if (have) {
       float2 ws[IPT];
 #pragma unroll
       for (int u = 0; u < IPT; ++u) ws[u] = win2[tid + u * THREADS];
@@ -502,7 +545,7 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS) pcm_big_kernel(PcmKerne
     __syncthreads();
 
     // 2. M-point complex FFT: exp(-2 pi i j / M) = exp(-2 pi i 2j / N)
-    run_fft<M, 1, THREADS, kBigPad>(s_buf, [&](int j) { return wN(2 * j); }, typename BigCfg<NFFT>::Rad{}, tid);
+    run_fft<M, 1, THREADS, kBigPad>(s_buf, BigTw<THI>{s_tw}, typename BigCfg<NFFT>::Rad{}, tid);
 
     // 3. split into the real spectrum; power over the same LDS
     constexpr int NU = M / 2 + 1;
@@ -543,28 +586,35 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS) pcm_big_kernel(PcmKerne
     have = nxt < n_tiles && interior(nxt);
     if (have) load_interior(nxt, tid);
 
-    // 4. mel: L lanes per band
+    // 4. mel: each band's group of Lb lanes strides over its bins; the
+    //    groups' partial sums meet by xor shuffles within the group
     float vmax = 0.0f, omin = __builtin_huge_valf();
     OUT *__restrict__ out = reinterpret_cast<OUT *>(a.out) + b * (int64_t)NM * F;
-    const int h = tid & (L - 1);
     auto mel = [&](const float *wsrc) {
-      for (int m = tid / L; m < NM; m += THREADS / L) {
+      const int m = lane_ent & 255, h = (lane_ent >> 8) & 255, Lb = lane_ent >= 0 ? 1 << (lane_ent >> 16) : 1;
+      float acc0 = 0.0f, acc1 = 0.0f;
+      if (lane_ent >= 0) {
         const int st = s_start[m], wd = s_width[m];
         const float *pr = P + st;
         const float *wr = wsrc + s_off[m];
-        float acc0 = 0.0f, acc1 = 0.0f;
         int j = h;
-        for (; j + L < wd; j += 2 * L) {
+        for (; j + Lb < wd; j += 2 * Lb) {
           acc0 = __builtin_fmaf(wr[j], pr[j], acc0);
-          acc1 = __builtin_fmaf(wr[j + L], pr[j + L], acc1);
+          acc1 = __builtin_fmaf(wr[j + Lb], pr[j + Lb], acc1);
         }
         if (j < wd) acc0 = __builtin_fmaf(wr[j], pr[j], acc0);
-        float acc = acc0 + acc1;
-        for (int o = L >> 1; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-        if (h == 0 && a.mel_out) {
+      }
+      float acc = acc0 + acc1;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {   // uniform shuffles; partners outside the group are not added
+        const float other = __shfl_xor(acc, o, 64);
+        if (o < Lb) acc += other;
+      }
+      if (lane_ent >= 0 && h == 0) {
+        if (a.mel_out) {
           store_out(out + (int64_t)m * F + fr, acc * a.mel_scale);
-        } else if (h == 0) {
-          const float v = fmaxf(acc * a.mel_scale, 1e-10f);
+        } else {
+          const float v = floor_1e10(acc * a.mel_scale);
           const float o = logmel_of(v);
           vmax = fmaxf(vmax, v);
           omin = fminf(omin, o);
@@ -672,6 +722,8 @@ hipError_t launch_pcm(const lm_plan *p, const PcmArgs &a, hipStream_t s, const L
   k.twiddle = p->dt.twiddle;
   k.untangle = p->dt.untangle;
   k.tw2 = p->dt.tw2;
+  k.mel_lanes = p->dt.mel_lanes;
+  k.hann_tw = p->win_length == p->n_fft;
   k.csr_start = p->dt.csr_start;
   k.csr_width = p->dt.csr_width;
   k.csr_off = p->dt.csr_off;

@@ -192,6 +192,48 @@ void build_mel_blocks(lm_plan *p) {
   }
 }
 
+// Lane table of the one-frame kernels' mel stage (n_fft >= 8192, `threads`
+// lanes): every band gets a group of L lanes (a power of two, at most 64,
+// aligned to L within its wave) that stride over its bins and add their
+// partial sums with xor shuffles.  L starts at 1 and doubles for the band
+// with the most bins per lane while lanes remain, so that the widest bands
+// (hundreds of bins) get many lanes and the narrow ones few.  Entry of lane
+// t: band | (position in group << 8) | (log2 L << 16), or -1 (idle).
+void build_mel_lanes(lm_plan *p, int threads) {
+  p->mel_lanes.clear();
+  if (p->n_fft < 8192) return;
+  const Csr &c = p->csr;
+  const int NM = c.n_rows;
+  std::vector<int> L(NM, 1);
+  int used = NM;
+  for (;;) {
+    int best = -1, best_cost = 1;
+    for (int m = 0; m < NM; ++m) {
+      const int cost = (c.width[m] + L[m] - 1) / L[m];
+      if (L[m] < 64 && used + L[m] <= threads && cost > best_cost) {
+        best = m;
+        best_cost = cost;
+      }
+    }
+    if (best < 0) break;
+    used += L[best];
+    L[best] *= 2;
+  }
+  // place groups largest first: every offset is then a multiple of the group
+  // size, so no group straddles a 64-lane wave
+  std::vector<int> order(NM);
+  for (int m = 0; m < NM; ++m) order[m] = m;
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return L[x] > L[y]; });
+  p->mel_lanes.assign(threads, -1);
+  int off = 0;
+  for (int m : order) {
+    int lg = 0;
+    while ((1 << lg) < L[m]) ++lg;
+    for (int h = 0; h < L[m]; ++h) p->mel_lanes[off + h] = m | (h << 8) | (lg << 16);
+    off += L[m];
+  }
+}
+
 Csr pack_dense(const float *dense, int n_rows, int n_bins) {
   Csr c;
   c.n_rows = n_rows;
@@ -345,6 +387,7 @@ int lm_plan_set_mel(lm_plan *p, double sr, double f_min, double f_max, int scale
   }
   p->csr = pack_dense(dense.data(), NM, K);
   build_mel_blocks(p);
+  build_mel_lanes(p, kBigThreads);
   p->have_filters = true;
   p->tables_dirty = true;
   return LM_OK;
@@ -360,6 +403,7 @@ int lm_plan_set_filters(lm_plan *p, const float *host_dense, int n_mels, int n_b
     if (!std::isfinite(host_dense[i])) return fail(LM_ERR_INVALID_ARG, "filters hold a non-finite value");
   p->csr = pack_dense(host_dense, n_mels, n_bins);
   build_mel_blocks(p);
+  build_mel_lanes(p, kBigThreads);
   p->have_filters = true;
   p->tables_dirty = true;
   return LM_OK;
