@@ -21,6 +21,8 @@
 // int16 input is converted to float without its 1/32768 scale; the mel
 // values are scaled by 2^-30 instead (exact), together with the 1/4 of
 // the split above.
+#include <type_traits>
+
 #include "lm_device.h"
 #include "lm_internal.h"
 
@@ -268,25 +270,53 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
     __syncthreads();
   } else {
   // 1. windowed, padded frame samples as M complex points per frame; every
-  //    load of the thread is issued before any is used
+  //    load of the thread is issued before any is used.  A tile whose
+  //    frames all lie inside the clip, with an even first sample (so that a
+  //    sample pair is one aligned 8- or 4-byte word), loads each point's two
+  //    samples with one load and no padding arithmetic.
   const float2 *__restrict__ win2 = reinterpret_cast<const float2 *>(a.window);
   constexpr int IPT = (FPB * M + THREADS - 1) / THREADS;
   float xs[IPT][2];
   float2 ws[IPT];
+  const int64_t j_first = f0 * a.hop - a.pad;
+  const bool direct = j_first >= 0 && f0 + FPB <= F && (f0 + FPB - 1) * a.hop - a.pad + NFFT <= T &&
+                      (((uintptr_t)(x + j_first) | (uintptr_t)(sizeof(IN) * a.hop)) % (2 * sizeof(IN))) == 0;
+  if (direct) {   // uniform
+    typedef typename std::conditional<sizeof(IN) == 2, uint32_t, float2>::type Pair;
 #pragma unroll
-  for (int u = 0; u < IPT; ++u) {
-    const int i = tid + u * THREADS;
-    const int fl = i / M, n = i - fl * M;
-    const int64_t fr = f0 + fl;
-    ws[u] = make_float2(0.0f, 0.0f);
-    xs[u][0] = xs[u][1] = 0.0f;
-    if ((FPB * M) % THREADS == 0 || i < FPB * M) {
-      if (fr < F) {
-        const int64_t j = fr * a.hop - a.pad + 2 * n;
-        const int64_t s0 = signal_source(j, T, a.sig_pad, a.pad_mode), s1 = signal_source(j + 1, T, a.sig_pad, a.pad_mode);
-        xs[u][0] = s0 >= 0 ? to_f(x[s0]) : 0.0f;
-        xs[u][1] = s1 >= 0 ? to_f(x[s1]) : 0.0f;
+    for (int u = 0; u < IPT; ++u) {
+      const int i = tid + u * THREADS;
+      const int fl = i / M, n = i - fl * M;
+      ws[u] = make_float2(0.0f, 0.0f);
+      xs[u][0] = xs[u][1] = 0.0f;
+      if ((FPB * M) % THREADS == 0 || i < FPB * M) {
+        const Pair v = reinterpret_cast<const Pair *>(x + j_first + (int64_t)fl * a.hop)[n];
+        if constexpr (sizeof(IN) == 2) {
+          xs[u][0] = (float)(int16_t)(v & 0xffffu);
+          xs[u][1] = (float)(int16_t)(v >> 16);
+        } else {
+          xs[u][0] = v.x;
+          xs[u][1] = v.y;
+        }
         ws[u] = win2[n];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      const int i = tid + u * THREADS;
+      const int fl = i / M, n = i - fl * M;
+      const int64_t fr = f0 + fl;
+      ws[u] = make_float2(0.0f, 0.0f);
+      xs[u][0] = xs[u][1] = 0.0f;
+      if ((FPB * M) % THREADS == 0 || i < FPB * M) {
+        if (fr < F) {
+          const int64_t j = fr * a.hop - a.pad + 2 * n;
+          const int64_t s0 = signal_source(j, T, a.sig_pad, a.pad_mode), s1 = signal_source(j + 1, T, a.sig_pad, a.pad_mode);
+          xs[u][0] = s0 >= 0 ? to_f(x[s0]) : 0.0f;
+          xs[u][1] = s1 >= 0 ? to_f(x[s1]) : 0.0f;
+          ws[u] = win2[n];
+        }
       }
     }
   }
@@ -347,22 +377,36 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
   // one copy of the loop per weight source, so LDS weights are read with LDS
   // instructions (a pointer that may point either way would make every
   // weight load a flat load that waits for all outstanding global loads)
+  // L lanes per (band, frame) output when the tile has fewer outputs than
+  // threads (L a power of two, at most 16): lane h of a group sums bins h,
+  // h + L, ... in two chains and the group adds its partial sums by xor
+  // shuffles (every lane of a group has the same trip count)
+  int L = 1;
+  while (L < 16 && 2 * L * NM * FPB <= THREADS) L *= 2;
+  const int h = tid & (L - 1);
   auto mel = [&](const float *wsrc) {
-    for (int o = tid; o < NM * FPB; o += THREADS) {
+    for (int o = tid / L; o < NM * FPB; o += THREADS / L) {
       const int fl = o % FPB, m = o / FPB;
       const int64_t fr = f0 + fl;
-      if (fr >= F) continue;
       const int st = s_start[m], wd = s_width[m];
-      if (wd == 0 && a.skip_empty) continue;   // log10(1e-10) everywhere: written by the fix-up
       const float *pr = P + fl * (M + 1) + st;
-      float acc = 0.0f;
       const float *wr = wsrc + s_off[m];
-      for (int j = 0; j < wd; ++j) acc = __builtin_fmaf(wr[j], pr[j], acc);
+      float acc0 = 0.0f, acc1 = 0.0f;
+      int j = h;
+      for (; j + L < wd; j += 2 * L) {
+        acc0 = __builtin_fmaf(wr[j], pr[j], acc0);
+        acc1 = __builtin_fmaf(wr[j + L], pr[j + L], acc1);
+      }
+      if (j < wd) acc0 = __builtin_fmaf(wr[j], pr[j], acc0);
+      float acc = acc0 + acc1;
+      for (int s2 = L >> 1; s2 > 0; s2 >>= 1) acc += __shfl_xor(acc, s2, 64);
+      if (h != 0 || fr >= F) continue;
+      if (wd == 0 && a.skip_empty) continue;   // log10(1e-10) everywhere: written by the fix-up
       if (a.mel_out) {
         store_out(out + (int64_t)m * F + fr, acc * a.mel_scale);
         continue;
       }
-      const float v = fmaxf(acc * a.mel_scale, 1e-10f);
+      const float v = floor_1e10(acc * a.mel_scale);
       const float ov = logmel_of(v);
       vmax = fmaxf(vmax, v);
       omin = fminf(omin, ov);
