@@ -23,16 +23,16 @@ standard-normal float32 samples, hop n_fft / 4, 128 Slaney mels, fp32 out.
 
 Generators
 ----------
-``stft_speechlike`` follows the STFT generator of the KBench
-``audio-mel-spectrogram-fused`` task page (section "make_inputs_src"): a
-spectral tilt exp(-k/(NF/3)) times a per-frame envelope 0.05 + U(0,1)^2,
-times independent standard normals for the real and imaginary parts.  The
-page draws with torch's CUDA generator; here numpy's PCG64 generator draws
-the same distributions on the host, in the order envelope, real, imaginary.
+``stft_speechlike`` draws the STFT workload the KBench
+``audio-mel-spectrogram-fused`` task page describes in words: a speech-like
+spectrum, strong at low frequencies and with about 60 dB of level change
+across frames.  Each bin is a circular complex Gaussian whose amplitude is a
+spectral tilt (falling by a factor e every NF/3 bins) times a per-frame
+level 0.05 + u^2, u uniform on [0, 1).
 
-``lintri_filters`` is the same page's linear triangular filterbank: NM+2
-centres spread linearly over bins 0..NF-1, each row min(rising, falling)
-clamped at zero, with the slope denominators floored at 1e-6, in float32.
+``lintri_filters`` is that page's "NM overlapping triangles spread over the
+NF bins": NM+2 equally spaced points from bin 0 to bin NF-1, triangle m
+peaking (at 1) on point m+1 and reaching 0 on its two neighbours.
 
 ``speech_pcm`` and ``music_pcm`` make the PCM workloads (the pages describe
 only their character; the exact recipe is this module's reading of it and
@@ -62,37 +62,44 @@ __all__ = [
 # ----------------------------------------------------------------------------
 
 def stft_speechlike(B: int, F: int, NF: int, seed: int) -> np.ndarray:
-    """(B, F, NF) complex64 speech-like STFT (tilt x envelope x Gaussian).
+    """(B, F, NF) complex64 speech-like STFT.
 
-    Drawn in float32 throughout: env = 0.05 + U^2 per (clip, frame),
-    tilt[k] = exp(-k / (NF/3)), re and im are standard normals scaled by
-    tilt * env.
+    Bin k of frame f in clip b is ``level[b, f] * tilt[k] * z`` with z a
+    complex normal whose real and imaginary parts are independent N(0, 1),
+    ``tilt[k] = exp(-3 k / NF)`` and ``level = 0.05 + u^2``, u ~ U[0, 1).
+    Levels span 0.05 .. 1.05 (about 26 dB of frame power) and the tilt
+    another 26 dB across the bins, the page's "about 60 dB" in round terms.
+    Draw order: all levels, then the (re, im) pairs of one clip after
+    another, in float32.
     """
     rng = np.random.default_rng(seed)
-    tilt = np.exp(-np.arange(NF, dtype=np.float32) / np.float32(NF / 3.0)).astype(np.float32)
-    env = (np.float32(0.05) + rng.random((B, F, 1), dtype=np.float32) ** 2).astype(np.float32)
-    scale = (tilt.reshape(1, 1, NF) * env).astype(np.float32)
+    u = rng.random((B, F), dtype=np.float32)
+    level = np.float32(0.05) + u * u
+    tilt = np.exp(np.float32(-3.0 / NF) * np.arange(NF, dtype=np.float32)).astype(np.float32)
     out = np.empty((B, F, NF), dtype=np.complex64)
-    view = out.view(np.float32).reshape(B, F, NF, 2)
-    # real parts first, then imaginary parts, one clip at a time to bound memory
+    pairs = out.view(np.float32).reshape(B, F, NF, 2)
     for b in range(B):
-        view[b, :, :, 0] = rng.standard_normal((F, NF), dtype=np.float32) * scale[b]
-    for b in range(B):
-        view[b, :, :, 1] = rng.standard_normal((F, NF), dtype=np.float32) * scale[b]
+        amp = level[b][:, None] * tilt[None, :]
+        pairs[b] = rng.standard_normal((F, NF, 2), dtype=np.float32) * amp[:, :, None]
     return out
 
 
 def lintri_filters(NF: int, NM: int) -> np.ndarray:
-    """(NM, NF) float32 linear triangular filterbank over bin indices."""
-    centres = np.linspace(0.0, NF - 1, NM + 2).astype(np.float32)
-    bins = np.arange(NF, dtype=np.float32).reshape(1, NF)
-    lo = centres[:-2].reshape(NM, 1)
-    mid = centres[1:-1].reshape(NM, 1)
-    hi = centres[2:].reshape(NM, 1)
-    left = (bins - lo) / np.maximum(mid - lo, np.float32(1e-6))
-    right = (hi - bins) / np.maximum(hi - mid, np.float32(1e-6))
-    w = np.maximum(np.minimum(left, right), np.float32(0.0))
-    return np.ascontiguousarray(w.astype(np.float32))
+    """(NM, NF) float32 triangles over bin indices.
+
+    With spacing d = (NF - 1) / (NM + 1), triangle m is the hat
+    max(0, 1 - |k - (m + 1) d| / d): 1 at bin (m + 1) d, 0 from (m + 2) d on
+    and up to m d.  NF = 1 leaves no room for a triangle: all zero.
+    """
+    if NF < 1 or NM < 1:
+        raise ValueError("lintri_filters needs NF >= 1 and NM >= 1")
+    if NF == 1:
+        return np.zeros((NM, 1), dtype=np.float32)
+    d = (NF - 1) / (NM + 1)
+    k = np.arange(NF, dtype=np.float64)
+    peak = d * np.arange(1, NM + 1, dtype=np.float64)
+    hat = 1.0 - np.abs(k[None, :] - peak[:, None]) / d
+    return np.ascontiguousarray(np.maximum(hat, 0.0).astype(np.float32))
 
 
 # ----------------------------------------------------------------------------
@@ -269,8 +276,9 @@ def make_inputs(w: Workload, B: int | None = None, T: int | None = None, F: int 
 def recipe() -> dict:
     """The generator readings, for recording next to results."""
     return {
-        "stft": "env=0.05+U^2 per frame, tilt=exp(-k/(NF/3)), re/im=N(0,1)*tilt*env, numpy PCG64(seed)",
-        "lintri": "NM+2 centres linspace(0,NF-1); min(rise,fall) clamped >=0; denominators >=1e-6; fp32",
+        "stft": "level=0.05+u^2 per frame, tilt=exp(-3k/NF), bin=level*tilt*(N(0,1)+iN(0,1)), "
+                "numpy PCG64(seed): levels, then (re, im) pairs clip by clip",
+        "lintri": "hat max(0, 1-|k-(m+1)d|/d), d=(NF-1)/(NM+1), fp64 then fp32",
         "speech": "f0~U(80,300), h=1..10 amp 1/h phase U(0,2pi), env 0.5(1-cos(2pi*4t+psi)), "
                   "noise RMS -30 dB re tone RMS, peak 0.5; i16=rint(x*32768) clipped",
         "music": "3 sines U(50,15000) Hz amp 0.25 random phase + pink(1/sqrt f) at 0.1x RMS",
