@@ -29,7 +29,7 @@ __device__ __forceinline__ float floor_1e10(float v) { return __int_as_float(max
 // The output value of a mel value v >= 1e-10 (after the floor):
 // (log10 v + 4) / 4, as one fma on the hardware base-2 logarithm.  Every
 // kernel writes exactly this value for every element, the region minima
-// the kernels record are minima of these values, and the clamp fix-up
+// the kernels record are minima of the values v, and the clamp fix-up
 // takes the clip's largest output as logmel_of(largest mel value) -- the
 // same function of the same value -- and its floor as that minus 2, i.e.
 // ((hi - 8) + 4) / 4.

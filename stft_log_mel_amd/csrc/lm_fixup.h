@@ -3,14 +3,18 @@
 // 8), applied after the main kernels have written (L + 4) / 4 everywhere.
 //
 // The main kernels write o = logmel_of(v) for every mel value v (after the
-// 1e-10 floor) and record the largest v per tile and the smallest o per
+// 1e-10 floor) and record the largest v per tile and the smallest v per
 // region of a tile (a frame range times a band range).  The clip's largest
 // output is logmel_of(hi_v) for its largest mel value hi_v -- the same
 // function of the same value, so that element's output equals it exactly --
 // and its floor in output units is that minus 2, i.e. ((hi - 8) + 4) / 4.
 // Since the cast to the output type is monotone, max(cast(o), cast(floor))
-// equals cast(max(o, floor)); so only regions whose smallest o lies below
-// the floor are read, and only values below it are rewritten.
+// equals cast(max(o, floor)); so only regions that may hold an o below the
+// floor are read, and only values below it are rewritten.  A region with
+// smallest mel value m holds no o below logmel_of(m) - kGateSlack: the
+// hardware log2 is within a few ulp (an ulp is at most 2^-16 for results up
+// to 128 in size), so outputs of ordered inputs are out of order by at most
+// a few 1e-6 after the scale by log10(2) / 4; the slack is far above that.
 //
 // fixup_group is one unit of that work, run by a whole workgroup of the
 // fix-up kernel (a second launch after the main kernel; its kernel boundary
@@ -23,6 +27,7 @@
 namespace lm {
 
 constexpr int kFixEntries = 512;   // regions one group scans
+constexpr float kGateSlack = 2.5e-4f;   // see above: regions within it of the floor are read
 constexpr int kFixUnroll = 8;      // values per thread with loads in flight together
 
 // Group units of a fix-up: (clip, group) pairs, entries_per_group regions
@@ -79,8 +84,8 @@ __device__ void fixup_empty_row(const FixupArgs &a, int64_t b, int e, int r, flo
 
 // Unit (clip b, group gi): reduce the clip's maxima to its floor (every
 // group of the clip does this itself, so no cross-workgroup atomics or
-// resets are needed), list the regions of the group whose smallest output
-// lies below the floor (as their first frame and first band), then rewrite
+// resets are needed), list the regions of the group whose smallest mel
+// value maps below the floor plus the slack (as their first frame and first band), then rewrite
 // their values below the floor with all threads.  LDS: s_f0[kFixEntries],
 // s_m0[kFixEntries], s_n[1], s_red[THREADS / 64].  Every thread of the
 // workgroup must call it; it ends with a barrier.
@@ -106,7 +111,7 @@ __device__ void fixup_group(const FixupArgs &a, int64_t b, int gi, int *s_f0, in
   const float fl = clip_floor<THREADS>(a, b, s_red);
 #pragma unroll
   for (int u = 0; u < MPT; ++u)
-    if (mn[u] < fl) {
+    if (logmel_of(mn[u]) < fl + kGateSlack) {   // +inf (an empty region) never is
       const int e = e0 + tid + u * THREADS;
       const int t = e / ept, rem = e - t * ept;
       const int sub = rem / st.blk_per_sub, blk = rem - sub * st.blk_per_sub;

@@ -115,7 +115,7 @@ struct lm_plan {
   bool tables_dirty = true;
   lm::DeviceTables dt;
 
-  // workspace: per-region smallest output value and per-tile largest mel value
+  // workspace: per-region smallest and per-tile largest mel value
   float *d_stats = nullptr;       // [minima][maxima], laid out per call
   size_t stats_cap = 0;           // floats
   // per-call packed copy of a device filterbank (STFT path)
@@ -170,8 +170,7 @@ Csr pack_dense(const float *dense, int n_rows, int n_bins);
 // Geometry of a main kernel's statistics for the clamp fix-up.  A tile is
 // frames_per_tile consecutive frames of one clip.  Per tile there are
 // sub_per_tile x blk_per_sub minimum entries: entry (sub, blk) holds the
-// smallest output value (float32, before any cast to the output type)
-// over frames [sub * frames_per_tile / sub_per_tile, +frames_per_tile /
+// smallest mel value (after the 1e-10 floor, as float32) over frames [sub * frames_per_tile / sub_per_tile, +frames_per_tile /
 // sub_per_tile) of the tile and bands [blk * band_h, (blk + 1) * band_h)
 // (both clipped to the output), or +inf if that region is empty; and max_per_tile maximum entries whose largest value is the
 // tile's largest mel value (after the 1e-10 floor).  Entries are stored

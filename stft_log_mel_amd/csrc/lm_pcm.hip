@@ -15,7 +15,7 @@
 //   4. the packed triangular mel sum per (band, frame), log10 after the
 //      1e-10 floor (KBench task page, "spec_md"), the (L+4)/4 rescale and a
 //      mel-major store (flashmel page, "Usage": (..., n_mels, n_frames));
-//   5. the tile's largest mel value and smallest log value go to per-tile
+//   5. the tile's largest and smallest mel values go to per-tile
 //      slots; the clamp fix-up kernel reduces them per clip and finishes the
 //      per-clip floor.
 // int16 input is converted to float without its 1/32768 scale; the mel
@@ -372,7 +372,7 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
   }
 
   // 4. mel sums, log10, rescale, mel-major store
-  float vmax = 0.0f, omin = __builtin_huge_valf();
+  float vmax = 0.0f, vmin = __builtin_huge_valf();
   OUT *__restrict__ out = reinterpret_cast<OUT *>(a.out) + b * (int64_t)NM * F;
   // one copy of the loop per weight source, so LDS weights are read with LDS
   // instructions (a pointer that may point either way would make every
@@ -409,7 +409,7 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
       const float v = floor_1e10(acc * a.mel_scale);
       const float ov = logmel_of(v);
       vmax = fmaxf(vmax, v);
-      omin = fminf(omin, ov);
+      vmin = fminf(vmin, v);
       store_out(out + (int64_t)m * F + fr, ov);
     }
   };
@@ -417,10 +417,10 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
   else mel(a.csr_w);
 
   // 5. tile statistics
-  block_maxmin<THREADS>(vmax, omin, s_red);
+  block_maxmin<THREADS>(vmax, vmin, s_red);
   if (tid == 0) {
     a.tile_max[tile] = vmax;
-    a.tile_min[tile] = omin;
+    a.tile_min[tile] = vmin;
   }
 }
 
@@ -632,7 +632,7 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS) pcm_big_kernel(PcmKerne
 
     // 4. mel: each band's group of Lb lanes strides over its bins; the
     //    groups' partial sums meet by xor shuffles within the group
-    float vmax = 0.0f, omin = __builtin_huge_valf();
+    float vmax = 0.0f, vmin = __builtin_huge_valf();
     OUT *__restrict__ out = reinterpret_cast<OUT *>(a.out) + b * (int64_t)NM * F;
     auto mel = [&](const float *wsrc) {
       const int m = lane_ent & 255, h = (lane_ent >> 8) & 255, Lb = lane_ent >= 0 ? 1 << (lane_ent >> 16) : 1;
@@ -661,7 +661,7 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS) pcm_big_kernel(PcmKerne
           const float v = floor_1e10(acc * a.mel_scale);
           const float o = logmel_of(v);
           vmax = fmaxf(vmax, v);
-          omin = fminf(omin, o);
+          vmin = fminf(vmin, v);
           store_out(out + (int64_t)m * F + fr, o);
         }
       }
@@ -671,10 +671,10 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS) pcm_big_kernel(PcmKerne
 
     // 5. frame statistics; the barrier inside also keeps the next frame's
     //    samples out of the power tile until every band has read it
-    block_maxmin<THREADS>(vmax, omin, s_red);
+    block_maxmin<THREADS>(vmax, vmin, s_red);
     if (tid == 0) {
       a.tile_max[tile] = vmax;
-      a.tile_min[tile] = omin;
+      a.tile_min[tile] = vmin;
     }
     __syncthreads();
   }

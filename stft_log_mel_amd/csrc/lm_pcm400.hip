@@ -32,7 +32,7 @@
 // fetches the next sub-tile's samples into registers while it computes the
 // current one.  Per sub-tile it records the largest mel value of each of
 // its four lane groups and, per 4-band group of every band block, the
-// smallest output value, for the clamp fix-up kernel.
+// smallest mel value, for the clamp fix-up kernel.
 #include <type_traits>
 
 #include "lm_device.h"
@@ -143,13 +143,14 @@ __device__ __forceinline__ void dft25(float2 (&a)[25]) {
   }
 }
 
-// min over the 16 lanes of a DPP row (rotations by 1, 2, 4, 8)
+// unsigned min over the 16 lanes of a DPP row (rotations by 1, 2, 4, 8);
+// on the bit patterns of positive floats it is the float min
 template <int N>
-__device__ __forceinline__ float ror_min(float v) {
-  const float r = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xf, 0xf, false));
-  return fminf(v, r);
+__device__ __forceinline__ uint32_t ror_min(uint32_t v) {
+  const uint32_t r = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x120 + N, 0xf, 0xf, false);
+  return min(v, r);
 }
-__device__ __forceinline__ float row_min16(float v) {
+__device__ __forceinline__ uint32_t row_min16(uint32_t v) {
   v = ror_min<1>(v);
   v = ror_min<2>(v);
   v = ror_min<4>(v);
@@ -805,7 +806,7 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
         orow += 16 * F;
         return;
       }
-      float omin = __builtin_huge_valf();   // no value
+      uint32_t vminb = 0x7f800000u;   // +inf: no value
       if (a.mel_out) {   // uniform: mel values as they are, no statistics
         const bool band_ok = 16 * cb + 4 * g + (c & 3) < NM;
 #pragma unroll
@@ -817,8 +818,8 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
         for (int i = 0; i < 4; ++i) {
           const float v = floor_1e10(acc[i]);
           vmaxb = max(vmaxb, __float_as_uint(v));
+          vminb = min(vminb, __float_as_uint(v));
           o[i] = logmel_of(v);
-          omin = fminf(omin, o[i]);
         }
         store_out4(orow, o);
       } else {
@@ -827,15 +828,15 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
         for (int i = 0; i < 4; ++i) {
           const float v = floor_1e10(acc[i]);
           if (band_ok && f0 + i < F) {
-            const float o = logmel_of(v);
             vmaxb = max(vmaxb, __float_as_uint(v));
-            omin = fminf(omin, o);
-            store_out(orow + i, o);
+            vminb = min(vminb, __float_as_uint(v));
+            store_out(orow + i, logmel_of(v));
           }
         }
       }
-      omin = row_min16(omin);
-      if (c == 0) tile_min[(gs * NB + cb) * 4 + g] = omin;
+      // the region's smallest mel value (its smallest output is that value's)
+      vminb = row_min16(vminb);
+      if (c == 0) tile_min[(gs * NB + cb) * 4 + g] = __uint_as_float(vminb);
       acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
       ++cb;
       orow += 16 * F;

@@ -8,8 +8,8 @@
 // persistent (a few per compute unit) and take tiles in turn.  Each (frame,
 // band) output is then the packed triangular mel sum over that tile, log10
 // after the 1e-10 floor, (L+4)/4, stored frame-major so a tile's outputs
-// are one contiguous run.  The tile's largest mel value and smallest output
-// value go to per-tile slots; the clamp fix-up kernel reduces them per clip
+// are one contiguous run.  The tile's largest and smallest mel values go to
+// per-tile slots; the clamp fix-up kernel reduces them per clip
 // and completes the per-clip floor.
 #include <climits>
 
@@ -91,7 +91,7 @@ __device__ __forceinline__ void stft_tile(const StftKernelArgs &a, int64_t tile,
 
   // 2. mel sums, log10, rescale, frame-major store
   OUT *__restrict__ out = reinterpret_cast<OUT *>(a.out) + (b * a.F + f0) * NM;
-  float vmax = 0.0f, omin = __builtin_huge_valf();
+  float vmax = 0.0f, vmin = __builtin_huge_valf();
   int m = tid % NM, f = tid / NM;
   const int dm = kStftThreads % NM, df = kStftThreads / NM;
   for (int o = tid; o < nfr * NM; o += kStftThreads) {
@@ -106,7 +106,7 @@ __device__ __forceinline__ void stft_tile(const StftKernelArgs &a, int64_t tile,
       const float v = fmaxf(acc, 1e-10f);
       const float ov = logmel_of(v);
       vmax = fmaxf(vmax, v);
-      omin = fminf(omin, ov);
+      vmin = fminf(vmin, v);
       store_out_nt(out + o, ov);
     }
     m += dm;
@@ -118,10 +118,10 @@ __device__ __forceinline__ void stft_tile(const StftKernelArgs &a, int64_t tile,
   }
 
   // 3. tile statistics (the barrier inside also ends every read of P)
-  block_maxmin<kStftThreads>(vmax, omin, s_red);
+  block_maxmin<kStftThreads>(vmax, vmin, s_red);
   if (tid == 0) {
     a.tile_max[tile] = vmax;
-    a.tile_min[tile] = omin;
+    a.tile_min[tile] = vmin;
   }
   __syncthreads();
 }
