@@ -9,6 +9,9 @@ n_fft 400, hop 160, 128 Slaney mels, float32 out -- the main kernel plus the
 per-clip clamp fix-up.  Inputs are generated on the host, copied to HBM once
 and stay resident; several input/output buffer sets are cycled so that every
 step reads its input from HBM rather than from the 256 MB last-level cache.
+The default warm-up (1000 steps) runs past the ~30 ms the GPU takes to raise
+its clocks under sustained work (``--ramp`` prints that curve), so the 200
+timed steps measure the sustained rate.
 
 Prints ONE JSON line: frames/s for the batch, the main kernel's achieved HBM
 bandwidth against MI355X's 8 TB/s (event-timed on the stream it runs on),
@@ -284,6 +287,36 @@ class Run:
                                pad_mode=w.pad_mode, power=w.power)[0]
 
 
+def ramp_one(w, dev, chunks=30, chunk_ms=3.0):
+    """Step time in consecutive chunks of about chunk_ms of work, starting
+    from an idle GPU (half a second of sleep first): one line per workload."""
+    import torch
+    r = Run(w, dev, log=False)
+    r.step(0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(r.stream)
+    r.step(1)
+    e1.record(r.stream)
+    torch.cuda.synchronize()
+    per = max(1, int(chunk_ms / max(e0.elapsed_time(e1), 1e-3)))
+    time.sleep(0.5)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(chunks + 1)]
+    ev[0].record(r.stream)
+    for c in range(chunks):
+        for i in range(per):
+            r.step(i)
+        ev[c + 1].record(r.stream)
+    torch.cuda.synchronize()
+    t, pts = 0.0, []
+    for c in range(chunks):
+        ms = ev[c].elapsed_time(ev[c + 1])
+        t += ms
+        pts.append([round(t, 2), round(ms / per * 1e3, 2)])
+    print(json.dumps({"ramp": w.name, "steps_per_chunk": per, "elapsed_ms_and_us_per_step": pts}), flush=True)
+    del r
+
+
 def roofline_of(w, kernel_ms, fft_variant="auto"):
     """The main kernel against its bounding roofline: HBM bytes for every
     workload except the n_fft 16384 one, whose bound is the FFT arithmetic
@@ -334,8 +367,11 @@ def per_config_entry(name, steps, warmup, dev, check_clips):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the GPU raises its clocks over the first ~30 ms of sustained work (see
+    # --ramp): the default warm-up covers that, so the timed steps measure the
+    # sustained rate
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="pcm_i16_b64")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-per-config", action="store_true", help="time only the headline workload")
@@ -348,6 +384,9 @@ def main():
                     help="time every n_fft of the sweep workloads (one JSON line each, no CPU leg)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (5 times), to scale HBM counters")
+    ap.add_argument("--ramp", action="store_true",
+                    help="print the step time of every workload in consecutive chunks from an idle GPU "
+                         "(how long the clocks take to settle), then exit")
     ap.add_argument("--dft-gemm", action="store_true",
                     help="FFT-variant comparison: time the n_fft = 400 transform of the default workload "
                          "as one dense fp32 GEMM on the vendor BLAS (torch.matmul), then exit")
@@ -375,6 +414,11 @@ def main():
 
     if args.dft_gemm:
         dft_gemm_probe(lm_synth.WORKLOADS["pcm_i16_b64"], args.steps, args.warmup)
+        return
+
+    if args.ramp:
+        for name in ("pcm_i16_b64",) + PER_CONFIG:
+            ramp_one(lm_synth.WORKLOADS[name], torch.device("cuda:0"))
         return
 
     if args.sweep:
