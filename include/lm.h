@@ -307,6 +307,33 @@ enum { LM_FFT_AUTO = 0, LM_FFT_FOLDED = 1, LM_FFT_PAIRED = 2 };
  */
 int lm_plan_set_fft_variant(lm_plan *plan, int variant);
 
+/*
+ * lm_plan_set_memory_limit -- cap on the device memory the plan holds (its
+ * tables, statistics workspace, filter pack and single-pass slots), for
+ * callers that budget memory on a shared GPU.  0 (the default) is no
+ * limit.  A call that would need more returns LM_ERR_OOM before it
+ * allocates or launches anything, leaving the output untouched and the plan
+ * usable; a buffer grows to the size the call needs rather than by doubling
+ * when doubling would pass the cap.  A cap below what the plan already holds
+ * frees nothing.  Host-only.  LM_ERR_INVALID_ARG if bytes < 0.
+ */
+int lm_plan_set_memory_limit(lm_plan *plan, int64_t bytes);
+
+/* Device bytes the plan holds now (-1 for a NULL plan).  Host-only. */
+int64_t lm_plan_memory_bytes(const lm_plan *plan);
+
+/*
+ * lm_plan_describe -- the plan's choices as text, for logs: its shape and
+ * options, the filterbank it holds, the kernels lm_from_pcm and lm_from_stft
+ * launch for it (n_fft = 400 matrix-core kernel, generic tile kernel or
+ * one-frame kernel, with their tile sizes), the device it is bound to and
+ * the device memory it holds.  Writes at most cap - 1 bytes and a NUL to
+ * buf (nothing if cap is 0) and returns the full length, so a call with
+ * cap = 0 sizes the buffer.  Host-only.  LM_ERR_INVALID_ARG (negative) for
+ * a NULL plan, or a NULL buf with cap > 0.
+ */
+int64_t lm_plan_describe(const lm_plan *plan, char *buf, int64_t cap);
+
 /* lm_plan_destroy -- free the plan and its device memory (NULL is a no-op). */
 void lm_plan_destroy(lm_plan *plan);
 

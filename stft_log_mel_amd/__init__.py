@@ -61,6 +61,9 @@ SIGNATURES = {
     "lm_from_pcm_noalloc": (_c_int, [_c_p, _c_p, _c_int, _c_i64, _c_i64, _c_p, _c_p]),
     "lm_plan_set_fft_variant": (_c_int, [_c_p, _c_int]),
     "lm_plan_set_single_pass": (_c_int, [_c_p, _c_int]),
+    "lm_plan_set_memory_limit": (_c_int, [_c_p, _c_i64]),
+    "lm_plan_memory_bytes": (_c_i64, [_c_p]),
+    "lm_plan_describe": (_c_i64, [_c_p, _c_p, _c_i64]),
     "lm_plan_profile": (_c_int, [_c_p, _c_int]),
     "lm_plan_profile_read": (_c_int, [_c_p, ctypes.POINTER(_c_d), ctypes.POINTER(_c_i64)]),
     "lm_plan_destroy": (None, [_c_p]),
@@ -183,6 +186,25 @@ class Plan:
         floor where it applies; plans start with it off (two launches)."""
         _check(_lib.lm_plan_set_single_pass(self._h, int(bool(enable))))
         return self
+
+    def set_memory_limit(self, n_bytes: int) -> "Plan":
+        """Cap the device memory the plan holds (0: no cap); a call that
+        would need more raises LmError (LM_ERR_OOM) before launching."""
+        _check(_lib.lm_plan_set_memory_limit(self._h, int(n_bytes)))
+        return self
+
+    def memory_bytes(self) -> int:
+        """Device bytes the plan holds now (tables and workspace)."""
+        return int(_lib.lm_plan_memory_bytes(self._h))
+
+    def describe(self) -> str:
+        """The plan's choices as text: shape, filterbank, kernels, device, memory."""
+        n = int(_lib.lm_plan_describe(self._h, None, 0))
+        if n < 0:
+            _check(n)
+        buf = ctypes.create_string_buffer(n + 1)
+        _lib.lm_plan_describe(self._h, buf, n + 1)
+        return buf.value.decode()
 
     def get_filters(self) -> np.ndarray:
         a = np.zeros((self.n_mels, self.n_bins), dtype=np.float32)

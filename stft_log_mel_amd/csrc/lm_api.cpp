@@ -3,6 +3,7 @@
 // the caller's stream.
 #include <algorithm>
 #include <atomic>
+#include <cstdio>
 #include <cstring>
 
 #include "lm_internal.h"
@@ -10,6 +11,30 @@
 namespace lm {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Device bytes the plan holds: tables, statistics, filter pack, single-pass slots.
+size_t plan_device_bytes(const lm_plan *p) {
+  return p->dt.bytes + p->stats_cap * sizeof(float) + p->pack_cap + p->sync_cap;
+}
+
+// Bytes a buffer of `cap` bytes may grow to under the plan's limit, given
+// that it needs `need`: the doubled size if that fits, else `need`, else 0
+// (the limit is exceeded).
+static size_t limited_size(const lm_plan *p, size_t cap, size_t need) {
+  const size_t want = std::max(need, 2 * cap);
+  if (p->mem_limit == 0) return want;
+  const size_t others = plan_device_bytes(p) - cap;
+  if (others + want <= p->mem_limit) return want;
+  if (others + need <= p->mem_limit) return need;
+  return 0;
+}
+
+static int over_limit(const lm_plan *p, size_t need, const char *what) {
+  char buf[192];
+  std::snprintf(buf, sizeof buf, "%s: %zu more bytes would pass the plan's device-memory limit of %zu (%zu held)",
+                what, need, p->mem_limit, plan_device_bytes(p));
+  return fail(LM_ERR_OOM, buf);
+}
 
 int ensure_device(lm_plan *p) {
   int dev = -1;
@@ -81,6 +106,8 @@ int upload_tables(lm_plan *p, hipStream_t s) {
   size_t o_eb = align256(o_t2 + sizeof(float) * p->twid2.size());
   size_t o_ml = align256(o_eb + sizeof(int32_t) * empty.size());
   size_t total = align256(o_ml + sizeof(int32_t) * p->mel_lanes.size() + 16);
+  if (p->mem_limit && plan_device_bytes(p) - p->dt.bytes + total > p->mem_limit)
+    return over_limit(p, total > p->dt.bytes ? total - p->dt.bytes : 0, "device tables");
   Staging *stg = nullptr;
   int rc = acquire_staging(p, total, &stg);
   if (rc != LM_OK) return rc;
@@ -137,11 +164,13 @@ int upload_tables(lm_plan *p, hipStream_t s) {
   return LM_OK;
 }
 
-// Grow a stream-ordered device buffer to at least `need` bytes (doubling),
-// releasing the old one in stream order behind the work already enqueued.
-static int grow(void **buf, size_t *cap, size_t need, hipStream_t s, const char *what) {
+// Grow a stream-ordered device buffer to at least `need` bytes (doubling
+// while the plan's memory limit allows), releasing the old one in stream
+// order behind the work already enqueued.
+static int grow(lm_plan *p, void **buf, size_t *cap, size_t need, hipStream_t s, const char *what) {
   if (need <= *cap) return LM_OK;
-  const size_t bytes = std::max(need, 2 * *cap);
+  const size_t bytes = limited_size(p, *cap, need);
+  if (bytes == 0) return over_limit(p, need - *cap, what);
   void *d = nullptr;
   hipError_t e = hipMallocAsync(&d, bytes, s);
   if (e != hipSuccess) return hip_fail(e, what);
@@ -156,7 +185,7 @@ static int grow(void **buf, size_t *cap, size_t need, hipStream_t s, const char 
 int ensure_workspace(lm_plan *p, int64_t n_floats, hipStream_t s) {
   void *buf = p->d_stats;
   size_t cap = p->stats_cap * sizeof(float);
-  const int rc = grow(&buf, &cap, sizeof(float) * (size_t)n_floats, s, "hipMallocAsync(workspace)");
+  const int rc = grow(p, &buf, &cap, sizeof(float) * (size_t)n_floats, s, "hipMallocAsync(workspace)");
   p->d_stats = static_cast<float *>(buf);
   p->stats_cap = cap / sizeof(float);
   return rc;
@@ -170,7 +199,7 @@ static int ensure_sync(lm_plan *p, int64_t slots, hipStream_t s) {
   p->sync_calls = 0;
   void *buf = p->d_sync;
   size_t cap = p->sync_cap;
-  int rc = grow(&buf, &cap, need, s, "hipMallocAsync(single-pass slots)");
+  int rc = grow(p, &buf, &cap, need, s, "hipMallocAsync(single-pass slots)");
   p->d_sync = static_cast<uint64_t *>(buf);
   p->sync_cap = cap;
   if (rc != LM_OK) return rc;
@@ -389,7 +418,7 @@ int lm_from_stft(lm_plan *p, const void *stft, const float *mel_filters, int64_t
   if (rc != LM_OK) return rc;
   if (!mel_filters) rc = upload_tables(p, s);
   if (rc == LM_OK) rc = ensure_workspace(p, 2 * n_clips * tiles, s);
-  if (mel_filters && rc == LM_OK) rc = grow(&p->d_pack, &p->pack_cap, sizeof(int32_t) * 2 * n_mels, s, "hipMallocAsync(pack)");
+  if (mel_filters && rc == LM_OK) rc = grow(p, &p->d_pack, &p->pack_cap, sizeof(int32_t) * 2 * n_mels, s, "hipMallocAsync(pack)");
   if (rc == LM_OK) rc = run_stft(p, stft, mel_filters, n_clips, n_frames, (int)n_bins, n_mels, tf, (int)tiles, out, s);
   return end_call(p, s, rc);
 }
@@ -454,6 +483,72 @@ int lm_plan_set_fft_variant(lm_plan *p, int variant) {
   if (variant < LM_FFT_AUTO || variant > LM_FFT_PAIRED) return fail(LM_ERR_INVALID_ARG, "unknown FFT variant");
   p->fft_variant = variant;
   return LM_OK;
+}
+
+int lm_plan_set_memory_limit(lm_plan *p, int64_t bytes) {
+  if (!p) return fail(LM_ERR_INVALID_ARG, "plan is null");
+  if (bytes < 0) return fail(LM_ERR_INVALID_ARG, "memory limit must be >= 0 (0: none)");
+  p->mem_limit = (size_t)bytes;
+  return LM_OK;
+}
+
+int64_t lm_plan_memory_bytes(const lm_plan *p) { return p ? (int64_t)plan_device_bytes(p) : -1; }
+
+int64_t lm_plan_describe(const lm_plan *p, char *buf, int64_t cap) {
+  if (!p) return fail(LM_ERR_INVALID_ARG, "plan is null");
+  if (cap < 0 || (cap > 0 && !buf)) return fail(LM_ERR_INVALID_ARG, "buffer is null or cap < 0");
+  static const char *pads[] = {"constant", "reflect", "replicate", "circular"};
+  static const char *outs[] = {"log-mel", "mel"};
+  char line[512];
+  std::string t;
+  std::snprintf(line, sizeof line,
+                "plan: n_fft %d, hop %d, n_mels %d, center %d, pad mode %s, power %g, out %s, window %d, "
+                "signal pad %lld, output %s, normalized %d\n",
+                p->n_fft, p->hop, p->n_mels, p->center,
+                p->pad_mode >= 0 && p->pad_mode < 4 ? pads[p->pad_mode] : "?", (double)p->power,
+                p->out_dtype == LM_F16 ? "f16" : "f32", p->win_length, (long long)p->sig_pad,
+                p->output >= 0 && p->output < 2 ? outs[p->output] : "?", p->normalized);
+  t += line;
+  if (p->have_filters) {
+    int empty = 0;
+    for (int w : p->csr.width) empty += w == 0;
+    std::snprintf(line, sizeof line, "filters: %d bands over %d bins, %zu weights, widest band %d bins, %d empty\n",
+                  p->csr.n_rows, p->csr.n_bins, p->csr.w.size(), p->csr.max_width(), empty);
+  } else {
+    std::snprintf(line, sizeof line, "filters: not set (lm_from_pcm needs lm_plan_set_mel or _set_filters)\n");
+  }
+  t += line;
+  if (p->have_filters) {
+    const std::string k16 = pcm_kernel_summary(p, true), k32 = pcm_kernel_summary(p, false);
+    t += "lm_from_pcm: " + k16 + "\n";
+    if (k32 != k16) t += "lm_from_pcm (float input): " + k32 + "\n";
+    t += "  then clamp_fixup_kernel (per-clip floor; reads only regions whose smallest value may lie below it)\n";
+  }
+  t += "lm_from_stft: filter_rows_kernel (row spans of the caller's filterbank), stft_logmel_kernel, "
+       "clamp_fixup_kernel\n";
+  std::snprintf(line, sizeof line, "options: fft variant %s, single pass %s\n",
+                p->fft_variant == LM_FFT_FOLDED ? "folded" : p->fft_variant == LM_FFT_PAIRED ? "paired" : "auto",
+                p->single_pass ? (p->device < 0 ? "requested" : p->coop_launch ? "requested (cooperative launch)"
+                                                                             : "requested (not available here)")
+                               : "off");
+  t += line;
+  if (p->device < 0)
+    std::snprintf(line, sizeof line, "device: not bound yet (bound at the first lm_from_* call)\n");
+  else
+    std::snprintf(line, sizeof line, "device: %d, %d compute units\n", p->device, p->n_cu);
+  t += line;
+  char lim[32] = "none";
+  if (p->mem_limit) std::snprintf(lim, sizeof lim, "%zu bytes", p->mem_limit);
+  std::snprintf(line, sizeof line, "device memory: %zu bytes held (tables %zu, statistics %zu, filter pack %zu, "
+                "single-pass slots %zu), limit %s\n",
+                plan_device_bytes(p), p->dt.bytes, p->stats_cap * sizeof(float), p->pack_cap, p->sync_cap, lim);
+  t += line;
+  if (cap > 0) {
+    const size_t n = std::min(t.size(), (size_t)(cap - 1));
+    std::memcpy(buf, t.data(), n);
+    buf[n] = 0;
+  }
+  return (int64_t)t.size();
 }
 
 }  // extern "C"

@@ -129,6 +129,7 @@ struct lm_plan {
   void *last_stream = nullptr;
   bool has_last = false;
 
+  size_t mem_limit = 0;            // lm_plan_set_memory_limit (0: none)
   int fft_variant = LM_FFT_AUTO;   // lm_plan_set_fft_variant (n_fft = 400 only)
   int single_pass = 0;             // lm_plan_set_single_pass
   bool coop_launch = false;        // the device supports cooperative launches
@@ -150,6 +151,8 @@ namespace lm {
 int ensure_device(lm_plan *p);
 int ensure_workspace(lm_plan *p, int64_t n_floats, hipStream_t s);
 int upload_tables(lm_plan *p, hipStream_t s);
+// Device bytes the plan holds (tables and workspace).
+size_t plan_device_bytes(const lm_plan *p);
 // Start and end of an lm_from_* call's GPU work on stream s: order it after
 // the plan's previous call (an event, only when the stream changes), then
 // note the stream.
@@ -223,6 +226,9 @@ hipError_t launch_pcm(const lm_plan *p, const PcmArgs &a, hipStream_t s, const L
 // True when launch_pcm leaves the plan's empty bands unwritten (the generic
 // kernel, log-mel output, at least one empty band): the fix-up writes them.
 bool pcm_skips_empty_bands(const lm_plan *p, bool in_i16);
+// One line on the PCM kernel launch_pcm picks for this plan (lm_plan_describe).
+std::string pcm_kernel_summary(const lm_plan *p, bool in_i16);
+std::string pcm400_summary(const lm_plan *p);
 bool pcm400_supported(const lm_plan *p, bool in_i16);
 // True when a call of n_sub 16-frame sub-tiles runs as one pass of the
 // n_fft = 400 kernel (every wave holds at most one sub-tile and keeps its

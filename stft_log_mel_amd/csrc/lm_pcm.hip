@@ -21,6 +21,7 @@
 // int16 input is converted to float without its 1/32768 scale; the mel
 // values are scaled by 2^-30 instead (exact), together with the 1/4 of
 // the split above.
+#include <cstdio>
 #include <type_traits>
 
 #include "lm_device.h"
@@ -723,6 +724,28 @@ static int generic_frames_per_tile(int n_fft) {
 
 static bool use_pcm400(const lm_plan *p, bool in_i16) {
   return p->fft_variant == LM_FFT_AUTO && pcm400_supported(p, in_i16);
+}
+
+std::string pcm_kernel_summary(const lm_plan *p, bool in_i16) {
+  if (use_pcm400(p, in_i16)) return pcm400_summary(p);
+  char buf[256];
+  if (p->n_fft >= 8192) {
+    std::snprintf(buf, sizeof buf,
+                  "pcm_big_kernel<%d>: one frame per step of a %d-thread workgroup, at most one workgroup per "
+                  "compute unit walking a range of frames; mel on lane groups of up to 64 per band",
+                  p->n_fft, kBigThreads);
+  } else if (p->n_fft == 400) {
+    std::snprintf(buf, sizeof buf, "pcm_logmel_kernel<400>%s: %d frames per workgroup of 512 threads, %s",
+                  p->fft_variant == LM_FFT_PAIRED ? " (paired)" : "", PcmCfg<400>::FPB,
+                  p->fft_variant == LM_FFT_PAIRED ? "two frames per 400-point complex FFT"
+                                                  : "200-point complex FFT per frame (8 x 5 x 5) and untangle");
+  } else {
+    std::snprintf(buf, sizeof buf,
+                  "pcm_logmel_kernel<%d>: %d frames per workgroup of 512 threads, %d-point complex FFT per frame "
+                  "in LDS passes and untangle; mel on split lanes",
+                  p->n_fft, generic_frames_per_tile(p->n_fft), p->n_fft / 2);
+  }
+  return buf;
 }
 
 StatLayout pcm_stat_layout(const lm_plan *p, bool in_i16) {

@@ -33,6 +33,7 @@
 // current one.  Per sub-tile it records the largest mel value of each of
 // its four lane groups and, per 4-band group of every band block, the
 // smallest mel value, for the clamp fix-up kernel.
+#include <cstdio>
 #include <type_traits>
 
 #include "lm_device.h"
@@ -917,6 +918,17 @@ bool pcm400_supported(const lm_plan *p, bool in_i16) {
   const int ndw = span / 2;
   const int lds_dw = p->hop == 160 ? ndw + 4 * (ndw / 80) : ndw;   // skewed layout at hop 160
   return lds_dw <= kLoff && kLoff + lds_dw <= kRegion;
+}
+
+std::string pcm400_summary(const lm_plan *p) {
+  char buf[320];
+  std::snprintf(buf, sizeof buf,
+                "pcm400_kernel: first stage on v_mfma_f32_16x16x32_f16 (two-part fp16 operands, fp32 "
+                "accumulate), 25-point DFTs in registers, %d-frame sub-tiles per wave, %d waves per "
+                "workgroup, one workgroup per compute unit; mel on 4x4x1 fp32 matrix blocks: %zu batches "
+                "of %d steps, %zu of %d blocked weights",
+                kSub, kWaves, p->melblk_meta.size() / 4, kMelBatch, p->melblk_w.size(), kMelWLds);
+  return buf;
 }
 
 StatLayout pcm400_stat_layout(const lm_plan *p) {

@@ -277,3 +277,64 @@ def test_set_pad_validation_and_frame_counts():
     assert m.pad == 37 and m._plan_for(None).num_frames(16000) == oracle.num_frames(16000, 400, 160, True, 37)
     with pytest.raises(Exception):
         lm.MelSpectrogram(pad=-3)
+
+
+@pytest.mark.parametrize("n_fft,hop,variant,expect", [
+    (400, 160, "auto", ["pcm400_kernel", "16-frame sub-tiles", "20 batches of 4 steps"]),
+    (400, 160, "folded", ["pcm_logmel_kernel<400>:", "16 frames per workgroup", "(8 x 5 x 5)"]),
+    (400, 160, "paired", ["pcm_logmel_kernel<400> (paired)", "two frames per 400-point"]),
+    (400, 161, "auto", ["pcm_logmel_kernel<400>:"]),           # odd hop: no matrix-core path
+    (1024, 256, "auto", ["pcm_logmel_kernel<1024>: 8 frames per workgroup"]),
+    (16384, 4096, "auto", ["pcm_big_kernel<16384>"]),
+])
+def test_describe_names_the_kernel(n_fft, hop, variant, expect):
+    p = lm.Plan(n_fft, hop, 128).set_mel(16000.0).set_fft_variant(variant)
+    text = p.describe()
+    for e in expect:
+        assert e in text, (e, text)
+    assert "device: not bound yet" in text
+    assert "0 bytes held" in text and "limit none" in text
+
+
+def test_describe_without_filters_and_with_a_wide_caller_filterbank():
+    p = lm.Plan(400, 160, 256)
+    assert "filters: not set" in p.describe()
+    assert "lm_from_pcm:" not in p.describe()
+    # a dense caller filterbank does not fit the matrix-core kernel's blocked table
+    p.set_filters(np.ones((256, 201), dtype=np.float32))
+    text = p.describe()
+    assert "256 bands over 201 bins, 51456 weights, widest band 201 bins, 0 empty" in text
+    assert "pcm_logmel_kernel<400>:" in text and "pcm400_kernel" not in text
+
+
+def test_describe_buffer_sizing_and_truncation():
+    rc, h = _create()
+    assert rc == OK
+    assert _lib.lm_plan_set_mel(h, 16000.0, 0.0, 8000.0, 1, 1) == OK
+    n = _lib.lm_plan_describe(h, None, 0)
+    assert n > 200
+    full = ctypes.create_string_buffer(n + 1)
+    assert _lib.lm_plan_describe(h, full, n + 1) == n
+    assert len(full.value) == n
+    short = ctypes.create_string_buffer(b"\xff" * 16, 16)
+    assert _lib.lm_plan_describe(h, short, 10) == n
+    assert short.raw[:10] == full.value[:9] + b"\0" and short.raw[10:] == b"\xff" * 6
+    assert _lib.lm_plan_describe(h, None, 5) == INVALID
+    assert _lib.lm_plan_describe(h, full, -1) == INVALID
+    assert _lib.lm_plan_describe(None, full, n + 1) == INVALID
+    _lib.lm_plan_destroy(h)
+
+
+def test_memory_limit_validation():
+    rc, h = _create()
+    assert rc == OK
+    assert _lib.lm_plan_memory_bytes(h) == 0
+    assert _lib.lm_plan_memory_bytes(None) == -1
+    assert _lib.lm_plan_set_memory_limit(h, -1) == INVALID
+    assert _lib.lm_plan_set_memory_limit(None, 1) == INVALID
+    assert _lib.lm_plan_set_memory_limit(h, 4096) == OK
+    _lib.lm_plan_destroy(h)
+    p = lm.Plan(400, 160, 80).set_mel(16000.0).set_memory_limit(1 << 20)
+    assert "limit 1048576 bytes" in p.describe()
+    with pytest.raises(ValueError):
+        p.set_memory_limit(-5)
