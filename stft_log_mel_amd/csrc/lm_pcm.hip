@@ -118,11 +118,35 @@ struct TwFn {
   F f;
   template <int STEP>
   __device__ __forceinline__ float2 at(int q) const { return f(q * STEP); }
-  // w[t] = at<STEP>(t k) for 1 <= t < R (one table read each)
+  // w[t] = at<STEP>(t k) for 1 <= t < R: from one table read (R <= 5), two
+  // (R = 8: w and w^4) or three (R = 16: w, w^4, w^8), the other powers as
+  // products of at most four table values
   template <int STEP, int R>
   __device__ __forceinline__ void powers(int k, float2 (&w)[R]) const {
+    if constexpr (R == 2) {
+      w[1] = at<STEP>(k);
+    } else if constexpr (R <= 5) {
+      w[1] = at<STEP>(k);
+      w[2] = cmul(w[1], w[1]);
+      if constexpr (R > 3) w[3] = cmul(w[2], w[1]);
+      if constexpr (R > 4) w[4] = cmul(w[2], w[2]);
+    } else if constexpr (R == 8 || R == 16) {
+      w[1] = at<STEP>(k);
+      w[4] = at<STEP>(4 * k);
+      w[2] = cmul(w[1], w[1]);
+      w[3] = cmul(w[2], w[1]);
+      w[5] = cmul(w[4], w[1]);
+      w[6] = cmul(w[4], w[2]);
+      w[7] = cmul(w[4], w[3]);
+      if constexpr (R == 16) {
+        w[8] = at<STEP>(8 * k);
 #pragma unroll
-    for (int t = 1; t < R; ++t) w[t] = at<STEP>(t * k);
+        for (int t = 9; t < 16; ++t) w[t] = cmul(w[8], w[t - 8]);
+      }
+    } else {
+#pragma unroll
+      for (int t = 1; t < R; ++t) w[t] = at<STEP>(t * k);
+    }
   }
 };
 template <typename F>
