@@ -361,13 +361,27 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
   }
   __syncthreads();
 
+  // the split's twiddles, loaded before the FFT so that their latency
+  // hides behind it (up to n_fft 1024: above, the registers they hold
+  // through the FFT would cost a workgroup of occupancy)
+  constexpr int NU = M / 2 + 1;              // pairs (k, M-k), k = 0..M/2
+  constexpr int UPT = (FPB * NU + THREADS - 1) / THREADS;
+  constexpr bool kPreUt = M <= 512;
+  float2 ut[UPT];
+  if constexpr (kPreUt) {
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int q = tid + u * THREADS;
+      const int fl = q / NU, k = q - fl * NU;
+      ut[u] = q < FPB * NU ? a.untangle[k] : make_float2(0.0f, 0.0f);
+    }
+  }
+
   // 2. M-point complex FFT per frame
   const float2 *__restrict__ twt = a.twiddle;
   run_fft<M, FPB, THREADS, PAD>(s_buf, tw_fn([=](int j) { return twt[j]; }), typename PcmCfg<NFFT>::Rad{}, tid);
 
   // 3. split into the real spectrum; power tile over the same LDS
-  constexpr int NU = M / 2 + 1;              // pairs (k, M-k), k = 0..M/2
-  constexpr int UPT = (FPB * NU + THREADS - 1) / THREADS;
   float pk[UPT], pmk[UPT];
 #pragma unroll
   for (int u = 0; u < UPT; ++u) {
@@ -378,7 +392,7 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
       const float2 zk = s_buf[lds_pos<PAD>(fl * M + k)];
       const float2 zc = cconj(s_buf[lds_pos<PAD>(fl * M + (k == 0 ? 0 : M - k))]);
       const float2 Y = cadd(zk, zc), D = csub(zk, zc);
-      const float2 V = cmul(a.untangle[k], D);
+      const float2 V = cmul(kPreUt ? ut[u] : a.untangle[k], D);
       pk[u] = (Y.x + V.y) * (Y.x + V.y) + (Y.y - V.x) * (Y.y - V.x);
       pmk[u] = (Y.x - V.y) * (Y.x - V.y) + (Y.y + V.x) * (Y.y + V.x);
     }
