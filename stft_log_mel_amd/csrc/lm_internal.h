@@ -36,8 +36,9 @@ constexpr int kMelBatch = 4;
 // Accelerator complex dies (XCDs) of the chip, each with its own L2;
 // consecutive workgroup ids are handed to them in turn.
 constexpr int kXcds = 8;
-// Threads of the one-frame kernel's workgroup (n_fft 8192 and 16384).
-constexpr int kBigThreads = 1024;
+// Threads of the one-frame kernel's workgroup (n_fft 8192 and 16384; also
+// the number of entries of its mel lane table).
+constexpr int big_threads(int n_fft) { return n_fft == 8192 ? 512 : 1024; }
 
 // Set the thread-local error text and return `status`.
 int fail(int status, const std::string &msg);
@@ -72,7 +73,7 @@ struct DeviceTables {
   int n_melblk = 0;
   const int32_t *empty_bands = nullptr;   // bands with no non-zero weight, ascending
   int n_empty = 0;
-  const int32_t *mel_lanes = nullptr;     // n_fft >= 8192: kBigThreads entries (build_mel_lanes)
+  const int32_t *mel_lanes = nullptr;     // n_fft >= 8192: big_threads(n_fft) entries (build_mel_lanes)
 };
 
 struct ProfileRec {

@@ -473,23 +473,37 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
 
 // ---------------------------------------------------------------------------
 // n_fft >= 8192: one frame fills a workgroup's FFT buffer, so the kernel is
-// persistent instead: one workgroup per compute unit stages the packed
-// filterbank and a two-level twiddle table in LDS once, then walks frames
-// gridDim.x apart (so the padded first and last frames of the clips, which
-// take the slower index path, spread over the workgroups).  Per frame the phases are those above (windowed load,
+// persistent instead: WGS workgroups per compute unit stage the packed
+// filterbank (where it fits their LDS share) and a two-level twiddle table
+// in LDS once, then walk frames gridDim.x apart (so the padded first and
+// last frames of the clips, which take the slower index path, spread over
+// the workgroups).  Per frame the phases are those above (windowed load,
 // folded complex FFT, split and power, mel, statistics), with no global
 // memory access between the load and the store: every twiddle is the
 // product of two LDS entries, exp(-2 pi i j / N) = W[j / 128] W'[j % 128].
-// The next frame's samples are loaded into registers while the mel sums of
-// the current one run.  The mel gives every band L consecutive lanes (L =
+// At 16384 (one 1024-thread workgroup per CU) the next frame's samples are
+// loaded into registers while the mel sums of the current one run; at 8192
+// two 512-thread workgroups share a CU, each loading its frame at the
+// frame's start, and either one's barriers and loads overlap the other's
+// work (48 against 69 us per sweep step with one 1024-thread workgroup).  The mel gives every band L consecutive lanes (L =
 // the largest power of two with L * n_mels <= THREADS, at most 64), which
 // stride over the band's bins and combine their partial sums with xor
 // shuffles, so no band waits on another band's reduction.
 // ---------------------------------------------------------------------------
 template <int NFFT>
 struct BigCfg;
-template <> struct BigCfg<8192>  { static constexpr int THREADS = kBigThreads; using Rad = Radices<8, 8, 8, 8>; };
-template <> struct BigCfg<16384> { static constexpr int THREADS = kBigThreads; using Rad = Radices<16, 8, 8, 8>; };
+// THREADS per workgroup, WGS workgroups per CU, PREFETCH: load the next
+// frame's samples during the current frame's mel sums
+template <> struct BigCfg<8192> {
+  static constexpr int THREADS = big_threads(8192), WGS = 2;
+  static constexpr bool PREFETCH = false;
+  using Rad = Radices<8, 8, 8, 8>;
+};
+template <> struct BigCfg<16384> {
+  static constexpr int THREADS = big_threads(16384), WGS = 1;
+  static constexpr bool PREFETCH = true;
+  using Rad = Radices<16, 8, 8, 8>;
+};
 
 constexpr int kTwLo = 128;   // entries of the low twiddle table
 constexpr int kBigPad = 5;   // FFT buffer: one spare point per 32
@@ -534,8 +548,10 @@ struct BigTw {
 template <int NFFT>
 constexpr int big_wlds() {
   // LDS floats left for filter weights next to the FFT buffer (M float2),
-  // the twiddle tables and the row tables, within one workgroup's 160 KB
-  return (160 * 1024 - (NFFT / 2 + (NFFT >> (kBigPad + 1))) * 8 - (NFFT / kTwLo + kTwLo) * 8 - 3 * 256 * 4 - 1024) / 4;
+  // the twiddle tables and the row tables, within one workgroup's share of
+  // the CU's 160 KB
+  return (160 * 1024 / BigCfg<NFFT>::WGS - (NFFT / 2 + (NFFT >> (kBigPad + 1))) * 8 - (NFFT / kTwLo + kTwLo) * 8 -
+          3 * 256 * 4 - 1024) / 4;
 }
 
 // A frame that reaches into the padding (the first and last few of a
@@ -565,7 +581,8 @@ __device__ __attribute__((noinline)) void big_padded_frame(const IN *__restrict_
 }
 
 template <int NFFT, typename IN, typename OUT>
-__global__ void __launch_bounds__(BigCfg<NFFT>::THREADS) pcm_big_kernel(PcmKernelArgs a, int64_t n_tiles) {
+__global__ void __launch_bounds__(BigCfg<NFFT>::THREADS, BigCfg<NFFT>::THREADS / 256 * BigCfg<NFFT>::WGS)
+    pcm_big_kernel(PcmKernelArgs a, int64_t n_tiles) {
   constexpr int M = NFFT / 2;
   constexpr int THREADS = BigCfg<NFFT>::THREADS;
   constexpr int NW = THREADS / 64;
@@ -617,8 +634,12 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS) pcm_big_kernel(PcmKerne
   const int G = gridDim.x;
   const int first = G % kXcds == 0 ? (int)(blockIdx.x % kXcds) * (G / kXcds) + (int)(blockIdx.x / kXcds)
                                    : (int)blockIdx.x;
-  bool have = first < n_tiles && interior(first);
-  if (have) load_interior(first, threadIdx.x);
+  constexpr bool PREFETCH = BigCfg<NFFT>::PREFETCH;
+  bool have = false;
+  if constexpr (PREFETCH) {
+    have = first < n_tiles && interior(first);
+    if (have) load_interior(first, threadIdx.x);
+  }
 
   for (int64_t tile = first; tile < n_tiles; tile += G) {
     // the window pointer and the thread index are made opaque per frame so
@@ -629,6 +650,10 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS) pcm_big_kernel(PcmKerne
     asm volatile("" : "+v"(tid));
     const int64_t b = tile / a.tiles_per_clip;
     const int64_t fr = tile - b * a.tiles_per_clip;   // one frame per tile
+    if constexpr (!PREFETCH) {
+      have = interior(tile);
+      if (have) load_interior(tile, tid);
+    }
     // 1. windowed samples z[n] = (w[2n] x[2n], w[2n+1] x[2n+1])
     if (have && a.hann_tw) {
       // periodic Hann w[n] = 1/2 - 1/2 cos(2 pi n / N), the cosine from the
@@ -693,9 +718,11 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS) pcm_big_kernel(PcmKerne
     }
 
     // the next frame's samples, in flight during the mel sums
-    const int64_t nxt = tile + G;
-    have = nxt < n_tiles && interior(nxt);
-    if (have) load_interior(nxt, tid);
+    if constexpr (PREFETCH) {
+      const int64_t nxt = tile + G;
+      have = nxt < n_tiles && interior(nxt);
+      if (have) load_interior(nxt, tid);
+    }
 
     // 4. mel: each band's group of Lb lanes strides over its bins; the
     //    groups' partial sums meet by xor shuffles within the group
@@ -751,7 +778,8 @@ template <int NFFT>
 static hipError_t launch_big(const PcmKernelArgs &k, bool i16, bool f16, int64_t n_tiles, int n_cu, hipStream_t s,
                              const LaunchTiming *tm) {
   constexpr int THREADS = BigCfg<NFFT>::THREADS;
-  const int64_t n_wg = n_tiles < n_cu ? n_tiles : n_cu;
+  const int64_t slots = (int64_t)n_cu * BigCfg<NFFT>::WGS;
+  const int64_t n_wg = n_tiles < slots ? n_tiles : slots;
   const dim3 grid((unsigned)n_wg), block(THREADS);
   if (!i16 && !f16) LM_LAUNCH(tm, (pcm_big_kernel<NFFT, float, float>), grid, block, 0, s, k, n_tiles);
   else if (!i16 && f16) LM_LAUNCH(tm, (pcm_big_kernel<NFFT, float, __half>), grid, block, 0, s, k, n_tiles);
@@ -797,9 +825,10 @@ std::string pcm_kernel_summary(const lm_plan *p, bool in_i16) {
   char buf[256];
   if (p->n_fft >= 8192) {
     std::snprintf(buf, sizeof buf,
-                  "pcm_big_kernel<%d>: one frame per step of a %d-thread workgroup, at most one workgroup per "
-                  "compute unit walking a range of frames; mel on lane groups of up to 64 per band",
-                  p->n_fft, kBigThreads);
+                  "pcm_big_kernel<%d>: one frame per step of a %d-thread workgroup, %d persistent workgroup%s per "
+                  "compute unit walking frames; mel on lane groups of up to 64 per band",
+                  p->n_fft, big_threads(p->n_fft), p->n_fft == 8192 ? BigCfg<8192>::WGS : BigCfg<16384>::WGS,
+                  (p->n_fft == 8192 ? BigCfg<8192>::WGS : BigCfg<16384>::WGS) > 1 ? "s" : "");
   } else if (p->n_fft == 400) {
     std::snprintf(buf, sizeof buf, "pcm_logmel_kernel<400>%s: %d frames per workgroup of 512 threads, %s",
                   p->fft_variant == LM_FFT_PAIRED ? " (paired)" : "", PcmCfg<400>::FPB,

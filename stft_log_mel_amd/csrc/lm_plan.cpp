@@ -387,7 +387,7 @@ int lm_plan_set_mel(lm_plan *p, double sr, double f_min, double f_max, int scale
   }
   p->csr = pack_dense(dense.data(), NM, K);
   build_mel_blocks(p);
-  build_mel_lanes(p, kBigThreads);
+  build_mel_lanes(p, big_threads(p->n_fft));
   p->have_filters = true;
   p->tables_dirty = true;
   return LM_OK;
@@ -403,7 +403,7 @@ int lm_plan_set_filters(lm_plan *p, const float *host_dense, int n_mels, int n_b
     if (!std::isfinite(host_dense[i])) return fail(LM_ERR_INVALID_ARG, "filters hold a non-finite value");
   p->csr = pack_dense(host_dense, n_mels, n_bins);
   build_mel_blocks(p);
-  build_mel_lanes(p, kBigThreads);
+  build_mel_lanes(p, big_threads(p->n_fft));
   p->have_filters = true;
   p->tables_dirty = true;
   return LM_OK;
