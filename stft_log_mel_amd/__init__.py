@@ -112,8 +112,21 @@ def _torch():
 
 
 def _stream_handle(device):
+    """torch's current stream on `device` as a HIP stream handle."""
     torch = _torch()
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)   # a direct lookup, ~0.3 us
+    if raw is not None:
+        return ctypes.c_void_p(raw(device.index))
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _on_device(device, fn):
+    """Call fn() with `device` current (switching only if it is not)."""
+    torch = _torch()
+    if torch.cuda.current_device() == device.index:
+        return fn()
+    with torch.cuda.device(device):
+        return fn()
 
 
 class Plan:
@@ -239,9 +252,11 @@ class Plan:
         elif (tuple(out.shape) != (B, self.n_mels, F) or out.dtype != odt or not out.is_contiguous()
               or out.device != pcm.device):
             raise ValueError("out has the wrong shape, dtype, layout or device")
-        with torch.cuda.device(pcm.device), self.lock:
-            _check(_lib.lm_from_pcm(self._h, ctypes.c_void_p(pcm.data_ptr()), in_dt, B, T,
-                                    ctypes.c_void_p(out.data_ptr()), _stream_handle(pcm.device)))
+        def call():
+            with self.lock:
+                return _lib.lm_from_pcm(self._h, ctypes.c_void_p(pcm.data_ptr()), in_dt, B, T,
+                                        ctypes.c_void_p(out.data_ptr()), _stream_handle(pcm.device))
+        _check(_on_device(pcm.device, call))
         return out
 
     def from_stft(self, stft, mel_filters=None, out=None):
@@ -267,9 +282,11 @@ class Plan:
         elif (tuple(out.shape) != (B, F, NM) or out.dtype != odt or not out.is_contiguous()
               or out.device != stft.device):
             raise ValueError("out has the wrong shape, dtype, layout or device")
-        with torch.cuda.device(stft.device), self.lock:
-            _check(_lib.lm_from_stft(self._h, ctypes.c_void_p(stft.data_ptr()), fptr, B, F, NF, NM,
-                                     ctypes.c_void_p(out.data_ptr()), _stream_handle(stft.device)))
+        def call():
+            with self.lock:
+                return _lib.lm_from_stft(self._h, ctypes.c_void_p(stft.data_ptr()), fptr, B, F, NF, NM,
+                                         ctypes.c_void_p(out.data_ptr()), _stream_handle(stft.device))
+        _check(_on_device(stft.device, call))
         return out
 
     # -- measurement -----------------------------------------------------------

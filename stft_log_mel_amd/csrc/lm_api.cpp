@@ -410,12 +410,16 @@ int lm_from_stft(lm_plan *p, const void *stft, const float *mel_filters, int64_t
   const size_t out_align = p->out_dtype == LM_F16 ? 2 : 4;
   if ((reinterpret_cast<uintptr_t>(stft) % 8) || (reinterpret_cast<uintptr_t>(out) % out_align))
     return fail(LM_ERR_INVALID_ARG, "misaligned stft or out pointer");
-  const int tf = stft_frames_per_tile((int)n_bins, n_mels);
-  const int64_t tiles = (n_frames + tf - 1) / tf;
-  if (tiles > INT32_MAX || n_clips * tiles > INT32_MAX) return fail(LM_ERR_UNSUPPORTED, "input too large");
+  const int tf0 = stft_frames_per_tile((int)n_bins, n_mels, 0, 0);
+  if ((n_frames + tf0 - 1) / tf0 > INT32_MAX || n_clips * ((n_frames + tf0 - 1) / tf0) > INT32_MAX)
+    return fail(LM_ERR_UNSUPPORTED, "input too large");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   int rc = begin_call(p, s);
   if (rc != LM_OK) return rc;
+  // the tile size of a small call depends on the device's CU count (bound now)
+  const int tf = stft_frames_per_tile((int)n_bins, n_mels, n_clips * n_frames, p->n_cu);
+  const int64_t tiles = (n_frames + tf - 1) / tf;
+  if (tiles > INT32_MAX || n_clips * tiles > INT32_MAX) return end_call(p, s, fail(LM_ERR_UNSUPPORTED, "input too large"));
   if (!mel_filters) rc = upload_tables(p, s);
   if (rc == LM_OK) rc = ensure_workspace(p, 2 * n_clips * tiles, s);
   if (mel_filters && rc == LM_OK) rc = grow(p, &p->d_pack, &p->pack_cap, sizeof(int32_t) * 2 * n_mels, s, "hipMallocAsync(pack)");

@@ -258,7 +258,7 @@ struct StftArgs {
   int n_cu;
   int mel_out;   // 1: mel values without the log tail
 };
-int stft_frames_per_tile(int n_bins, int n_mels);
+int stft_frames_per_tile(int n_bins, int n_mels, int64_t total_frames, int n_cu);
 hipError_t launch_stft(const StftArgs &a, hipStream_t s, const LaunchTiming *tm);
 
 // First non-zero bin and width of every row of a device dense (n_mels,

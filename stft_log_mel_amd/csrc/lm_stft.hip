@@ -27,6 +27,7 @@ constexpr int kStftThreadsBig = 256, kStftThreadsSmall = 512;
 constexpr int kStftLoadUnroll = 8;
 constexpr int kStftWLds = 2048;     // LDS floats for the staged filter weights
 constexpr int kStftWgPerCu = 4;     // resident workgroups per compute unit
+constexpr int kStftMinTile = 4;     // frames per tile at least
 
 struct StftKernelArgs {
   const float2 *stft;
@@ -195,11 +196,18 @@ __global__ void __launch_bounds__(kStftThreads) stft_logmel_kernel(StftKernelArg
   }
 }
 
-int stft_frames_per_tile(int n_bins, int n_mels) {
+int stft_frames_per_tile(int n_bins, int n_mels, int64_t total_frames, int n_cu) {
   (void)n_mels;
   int tf = 6144 / n_bins;
   if (tf > 64) tf = 64;
   if (tf < 1) tf = 1;
+  // a call with fewer tiles than resident workgroups runs one workgroup per
+  // tile and is latency-bound: smaller tiles, about one per CU, spread it
+  // over more of the chip
+  if (n_cu > 0 && (total_frames + tf - 1) / tf < (int64_t)n_cu * kStftWgPerCu) {
+    const int64_t per_cu = (total_frames + n_cu - 1) / n_cu;
+    if (per_cu < tf) tf = (int)(per_cu < kStftMinTile ? kStftMinTile : per_cu);
+  }
   return tf;
 }
 
