@@ -239,13 +239,55 @@ __device__ __forceinline__ float wave_min(float v) {
   return v;
 }
 
-// Block-wide max of vmax and min of vmin; the result is valid in thread 0.
-// `red` must hold 2 * (blockDim.x / 64) floats of LDS.
+// unsigned min over the 16 lanes of a DPP row (rotations by 1, 2, 4, 8);
+// on the bit patterns of positive floats it is the float min
+template <int N>
+__device__ __forceinline__ uint32_t ror_min(uint32_t v) {
+  const uint32_t r = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x120 + N, 0xf, 0xf, false);
+  return min(v, r);
+}
+__device__ __forceinline__ uint32_t row_min16(uint32_t v) {
+  v = ror_min<1>(v);
+  v = ror_min<2>(v);
+  v = ror_min<4>(v);
+  return ror_min<8>(v);
+}
+// unsigned max over the 16 lanes of a DPP row; on the bit patterns of
+// positive floats it is the float max
+template <int N>
+__device__ __forceinline__ uint32_t ror_max(uint32_t v) {
+  const uint32_t r = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x120 + N, 0xf, 0xf, false);
+  return max(v, r);
+}
+__device__ __forceinline__ uint32_t row_max16(uint32_t v) {
+  v = ror_max<1>(v);
+  v = ror_max<2>(v);
+  v = ror_max<4>(v);
+  return ror_max<8>(v);
+}
+
+// unsigned max / min over the whole wave: the DPP row reduction, then the
+// four rows' results by readlane (uniform)
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  v = row_max16(v);
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+__device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
+  v = row_min16(v);
+  return min(min((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+             min((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+
+// Block-wide max of vmax and min of vmin, for non-negative values (mel
+// values after the 1e-10 floor, +inf for none), reduced on their bit
+// patterns; the result is valid in thread 0.  `red` must hold
+// 2 * (blockDim.x / 64) floats of LDS.
 template <int THREADS>
 __device__ __forceinline__ void block_maxmin(float &vmax, float &vmin, float *red) {
   constexpr int NW = THREADS / 64;
-  vmax = wave_max(vmax);
-  vmin = wave_min(vmin);
+  vmax = __uint_as_float(wave_umax(__float_as_uint(vmax)));
+  vmin = __uint_as_float(wave_umin(__float_as_uint(vmin)));
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (lane == 0) {
     red[w] = vmax;

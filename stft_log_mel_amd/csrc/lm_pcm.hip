@@ -725,8 +725,10 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS, BigCfg<NFFT>::THREADS /
     }
 
     // 4. mel: each band's group of Lb lanes strides over its bins; the
-    //    groups' partial sums meet by xor shuffles within the group
-    float vmax = 0.0f, vmin = __builtin_huge_valf();
+    //    groups' partial sums meet by xor shuffles within the group.  The
+    //    frame's largest and smallest mel values are kept on their bit
+    //    patterns (positive floats order as unsigned integers).
+    uint32_t vmaxb = 0u, vminb = 0x7f800000u;
     OUT *__restrict__ out = reinterpret_cast<OUT *>(a.out) + b * (int64_t)NM * F;
     auto mel = [&](const float *wsrc) {
       const int m = lane_ent & 255, h = (lane_ent >> 8) & 255, Lb = lane_ent >= 0 ? 1 << (lane_ent >> 16) : 1;
@@ -754,8 +756,8 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS, BigCfg<NFFT>::THREADS /
         } else {
           const float v = floor_1e10(acc * a.mel_scale);
           const float o = logmel_of(v);
-          vmax = fmaxf(vmax, v);
-          vmin = fminf(vmin, v);
+          vmaxb = max(vmaxb, __float_as_uint(v));
+          vminb = min(vminb, __float_as_uint(v));
           store_out(out + (int64_t)m * F + fr, o);
         }
       }
@@ -763,14 +765,28 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS, BigCfg<NFFT>::THREADS /
     if (w_in_lds) mel(s_w);
     else mel(a.csr_w);
 
-    // 5. frame statistics; the barrier inside also keeps the next frame's
-    //    samples out of the power tile until every band has read it
-    block_maxmin<THREADS>(vmax, vmin, s_red);
-    if (tid == 0) {
-      a.tile_max[tile] = vmax;
-      a.tile_min[tile] = vmin;
+    // 5. frame statistics: each wave's extremes to LDS; the barrier (which
+    //    also keeps the next frame's samples out of the power tile until
+    //    every band has read it) lets thread 0 combine them while the others
+    //    go on to the next frame (s_red is next written at that frame's end)
+    {
+      const uint32_t wmx = wave_umax(vmaxb), wmn = wave_umin(vminb);
+      if ((tid & 63) == 0) {
+        s_red[tid >> 6] = __uint_as_float(wmx);
+        s_red[NW + (tid >> 6)] = __uint_as_float(wmn);
+      }
     }
     __syncthreads();
+    if (tid == 0) {
+      uint32_t mx = 0u, mn = 0x7f800000u;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        mx = max(mx, __float_as_uint(s_red[i]));
+        mn = min(mn, __float_as_uint(s_red[NW + i]));
+      }
+      a.tile_max[tile] = __uint_as_float(mx);
+      a.tile_min[tile] = __uint_as_float(mn);
+    }
   }
 }
 

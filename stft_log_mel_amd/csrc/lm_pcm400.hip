@@ -144,33 +144,6 @@ __device__ __forceinline__ void dft25(float2 (&a)[25]) {
   }
 }
 
-// unsigned min over the 16 lanes of a DPP row (rotations by 1, 2, 4, 8);
-// on the bit patterns of positive floats it is the float min
-template <int N>
-__device__ __forceinline__ uint32_t ror_min(uint32_t v) {
-  const uint32_t r = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x120 + N, 0xf, 0xf, false);
-  return min(v, r);
-}
-__device__ __forceinline__ uint32_t row_min16(uint32_t v) {
-  v = ror_min<1>(v);
-  v = ror_min<2>(v);
-  v = ror_min<4>(v);
-  return ror_min<8>(v);
-}
-// unsigned max over the 16 lanes of a DPP row; on the bit patterns of
-// positive floats it is the float max
-template <int N>
-__device__ __forceinline__ uint32_t ror_max(uint32_t v) {
-  const uint32_t r = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x120 + N, 0xf, 0xf, false);
-  return max(v, r);
-}
-__device__ __forceinline__ uint32_t row_max16(uint32_t v) {
-  v = ror_max<1>(v);
-  v = ror_max<2>(v);
-  v = ror_max<4>(v);
-  return ror_max<8>(v);
-}
-
 // four consecutive outputs (4-byte alignment suffices for a 16-byte store)
 typedef float v4f_a4 __attribute__((ext_vector_type(4), aligned(4)));
 __device__ __forceinline__ void store_out4(float *p, const float (&o)[4]) {
