@@ -59,7 +59,7 @@ __device__ float clip_floor(const FixupArgs &a, int64_t b, float *s_red) {
   const float *cmax = a.tile_max + b * (int64_t)n_max;
   float hi = 0.0f;
   for (int e = threadIdx.x; e < n_max; e += THREADS) hi = fmaxf(hi, cmax[e]);
-  hi = wave_max(hi);
+  hi = __uint_as_float(wave_umax(__float_as_uint(hi)));   // maxima are >= 0
   if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = hi;
   __syncthreads();
 #pragma unroll
