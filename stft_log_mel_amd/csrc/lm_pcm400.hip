@@ -413,7 +413,7 @@ __device__ __forceinline__ int put_prefetch(const Args &a, const IN *__restrict_
     }
     if (pf.q_lo > 0) m = fmaxf(m, padded_absmax<IN>(a, pcm, t, 0, lo_end));
     if (hi_begin < ndw) m = fmaxf(m, padded_absmax<IN>(a, pcm, t, hi_begin, ndw));
-    e = scale_exponent(wave_max(m));
+    e = scale_exponent(__uint_as_float(wave_umax(__float_as_uint(m))));   // m >= 0
   }
   const float sc = __builtin_amdgcn_ldexpf(1.0f, e);
 #pragma unroll
@@ -575,7 +575,7 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
       // which the compiler cannot tell: retire the registers here as well
 #pragma unroll
       for (int i = 0; i < Prefetch<IN>::N; ++i) asm volatile("" ::"v"(pf.v[i]));
-      esc = kI16 ? 0 : scale_exponent(wave_max(padded_absmax<IN>(a, pcm, tc, 0, span / 2)));
+      esc = kI16 ? 0 : scale_exponent(__uint_as_float(wave_umax(__float_as_uint(padded_absmax<IN>(a, pcm, tc, 0, span / 2)))));
       stage_padded<IN, SK>(a, pcm, tc, 0, span / 2, R, esc);
     }
     esc = __builtin_amdgcn_readfirstlane(esc);
