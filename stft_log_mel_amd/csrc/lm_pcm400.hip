@@ -484,6 +484,11 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
   // 64 bytes of a band row) and the input overlap in one L2
   const int64_t wg0 = (int64_t)xcd_rank(blockIdx.x, gridDim.x) * a.per_wg;
   const int64_t wg_end = min(wg0 + a.per_wg, a.n_sub);
+  // the waves start on sub-tiles wg0 + wv and then claim the range's next
+  // ones from one LDS counter, so that a wave that runs ahead (the older wave
+  // of a SIMD wins the issue slots both want) takes more of them and the
+  // waves of a compute unit end together
+  __shared__ int s_next;
   int64_t gs = wg0 + wv;
   SubTile tc = locate(a, gs);   // the sub-tile gs (clip, index, first sample)
   Prefetch<IN> pf;
@@ -510,6 +515,7 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
     for (int u = 0; u < PER; ++u)
       if (tid + u * kThreads < kTab) s_amat[tid + u * kThreads] = v[u];
     if (tid < 4 * a.mel_batches) s_bat[tid] = bat & 0xffff;
+    if (tid == 0) s_next = kWaves;
 #pragma unroll
     for (int u = 0; u < WPT; ++u) {
       const int i = tid + u * kThreads;
@@ -564,7 +570,14 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
   };
   bool res_done = false;
 
-  for (; gs < wg_end; gs += kWaves) {
+  int64_t gs_next = wg_end;
+  for (; gs < wg_end; gs = gs_next) {
+    // 0. claim the wave's next sub-tile (the LDS atomic's return overlaps the
+    //    staging below); the single pass keeps one sub-tile per wave
+    int claim = 0;
+    if constexpr (!RES) {
+      if (lane == 0) claim = atomicAdd(&s_next, 1);
+    }
     // 1. this sub-tile's samples into the wave's region (LDS operations of
     //    one wave complete in order, so no barrier is needed around them)
     int esc;   // float input: the sub-tile's scale exponent (uniform)
@@ -581,10 +594,10 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
     esc = __builtin_amdgcn_readfirstlane(esc);
     // (the single pass has one sub-tile per wave: nothing to prefetch)
     const SubTile t = tc;
-    if constexpr (RES) {
-      have = false;
-    } else if (gs + kWaves < wg_end) {
-      tc = advance(a, tc, kWaves);
+    gs_next = RES ? wg_end : wg0 + __builtin_amdgcn_readfirstlane(claim);
+    if (gs_next < wg_end) {
+      const int64_t n = gs_next - gs;   // >= 1 (uniform)
+      tc = n <= a.S ? advance(a, tc, (int)n) : locate(a, gs_next);
       have = prefetch<IN>(a, pcm, tc, span, pf);
     } else {
       have = false;
