@@ -47,7 +47,7 @@ def main_kernel_name(w, fft_variant: str = "auto") -> str:
     """The kernel lm_from_* launches for this workload (the library's own dispatch rule)."""
     if w.entry == "stft":
         return "stft_logmel_kernel"
-    if w.n_fft == 400 and w.hop % 2 == 0 and fft_variant == "auto":
+    if w.n_fft == 400 and w.hop % 2 == 0 and fft_variant in ("auto", "split_mfma"):
         return "pcm400_kernel"
     if w.n_fft >= 8192:
         return "pcm_big_kernel"
@@ -193,6 +193,8 @@ PER_CONFIG = ("stft_b1", "pcm_f32_b8", "stft_b256", "pcm_f32_nfft16384")
 def first_stage_dtype(w, fft_variant: str) -> str:
     """The arithmetic the workload's transform runs in."""
     if w.entry == "pcm" and main_kernel_name(w, fft_variant) == "pcm400_kernel":
+        if fft_variant == "split_mfma":
+            return "f32 (n_fft 400 16-point and 25-point stages: two-part fp16 operands, fp32 accumulate)"
         return "f32 (n_fft 400 first stage: two-part fp16 operands, fp32 accumulate)"
     return "f32"
 
@@ -376,7 +378,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-per-config", action="store_true", help="time only the headline workload")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--fft-variant", default="auto", choices=["auto", "folded", "paired"],
+    ap.add_argument("--fft-variant", default="auto", choices=["auto", "split_mfma", "folded", "paired"],
                     help="n_fft = 400 transform (comparison only; auto is the library's choice)")
     ap.add_argument("--single-pass", action="store_true",
                     help="use the one-launch (cooperative) form of the per-clip floor where it applies")

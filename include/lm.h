@@ -288,7 +288,7 @@ int lm_from_pcm_noalloc(lm_plan *plan, const void *pcm, int in_dtype, int64_t n_
 int lm_plan_set_single_pass(lm_plan *plan, int enable);
 
 /* FFT variants of the n_fft = 400 PCM path (lm_plan_set_fft_variant). */
-enum { LM_FFT_AUTO = 0, LM_FFT_FOLDED = 1, LM_FFT_PAIRED = 2 };
+enum { LM_FFT_AUTO = 0, LM_FFT_FOLDED = 1, LM_FFT_PAIRED = 2, LM_FFT_SPLIT_MFMA = 3 };
 
 /*
  * lm_plan_set_fft_variant -- which transform the n_fft = 400 PCM path runs,
@@ -296,8 +296,13 @@ enum { LM_FFT_AUTO = 0, LM_FFT_FOLDED = 1, LM_FFT_PAIRED = 2 };
  * normal, folded and paired real-input transforms it compared).
  *
  *  LM_FFT_AUTO    (the default) the 16 x 25 split with its 16-point stage on
- *                 the matrix cores wherever it applies (even hop), else the
- *                 folded form.
+ *                 the matrix cores and its 25-point DFTs in registers
+ *                 wherever it applies (even hop), else the folded form.
+ *  LM_FFT_SPLIT_MFMA  the 16 x 25 split with the 25-point stage on the
+ *                 matrix cores as well (two-part fp16 operands, three
+ *                 products), where the blocked filterbank leaves room for
+ *                 that stage's operands (up to 1920 blocked weights: 128
+ *                 Slaney bands over 0-8 kHz take 1280); else as AUTO.
  *  LM_FFT_FOLDED  each frame as a 200-point complex sequence (radix 8, 5, 5),
  *                 then split into the real spectrum.
  *  LM_FFT_PAIRED  two frames as one 400-point complex sequence, separated by

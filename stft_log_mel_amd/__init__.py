@@ -43,7 +43,7 @@ _SCALE = {"slaney": 0, "htk": 1}
 _NORM = {"slaney": 0, None: 1, "none": 1}
 _OUTPUT = {"logmel": 0, "mel": 1}
 _NORMALIZED = {None: 0, False: 0, "none": 0, True: 1, "window": 1, "frame_length": 2}
-_FFT_VARIANT = {"auto": 0, "folded": 1, "paired": 2}
+_FFT_VARIANT = {"auto": 0, "folded": 1, "paired": 2, "split_mfma": 3}
 
 # Exported symbols and their C signatures (include/lm.h).
 _c_int, _c_i64, _c_p, _c_f, _c_d = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_double

@@ -96,7 +96,8 @@ int upload_tables(lm_plan *p, hipStream_t s) {
   size_t o_w = align256(o_of + sizeof(int32_t) * NM);
   size_t o_mf = align256(o_w + sizeof(float) * (nnz > 0 ? nnz : 1));
   size_t o_mh = o_mf;
-  size_t o_bm = align256(o_mh + sizeof(uint16_t) * p->mfma400h.size());
+  size_t o_mt = align256(o_mh + sizeof(uint16_t) * p->mfma400h.size());
+  size_t o_bm = align256(o_mt + sizeof(uint16_t) * p->mfma400t.size());
   size_t o_bw = align256(o_bm + sizeof(int32_t) * p->melblk_meta.size());
   size_t o_t2 = align256(o_bw + sizeof(float) * p->melblk_w.size());
   std::vector<int32_t> empty;
@@ -124,6 +125,8 @@ int upload_tables(lm_plan *p, hipStream_t s) {
   }
   if (!p->mfma400h.empty())
     std::memcpy(host + o_mh, p->mfma400h.data(), sizeof(uint16_t) * p->mfma400h.size());
+  if (!p->mfma400t.empty())
+    std::memcpy(host + o_mt, p->mfma400t.data(), sizeof(uint16_t) * p->mfma400t.size());
   if (p->have_filters) {
     std::memcpy(host + o_bm, p->melblk_meta.data(), sizeof(int32_t) * p->melblk_meta.size());
     std::memcpy(host + o_bw, p->melblk_w.data(), sizeof(float) * p->melblk_w.size());
@@ -154,6 +157,7 @@ int upload_tables(lm_plan *p, hipStream_t s) {
   p->dt.csr_w = reinterpret_cast<const float *>(c + o_w);
   p->dt.nnz = nnz;
   p->dt.mfma400h = p->mfma400h.empty() ? nullptr : reinterpret_cast<const uint16_t *>(c + o_mh);
+  p->dt.mfma400t = p->mfma400t.empty() ? nullptr : reinterpret_cast<const uint16_t *>(c + o_mt);
   p->dt.melblk_meta = reinterpret_cast<const int32_t *>(c + o_bm);
   p->dt.melblk_w = reinterpret_cast<const float *>(c + o_bw);
   p->dt.n_melblk = p->have_filters ? (p->n_mels + 15) / 16 : 0;
@@ -484,7 +488,7 @@ int lm_plan_set_single_pass(lm_plan *p, int enable) {
 
 int lm_plan_set_fft_variant(lm_plan *p, int variant) {
   if (!p) return fail(LM_ERR_INVALID_ARG, "plan is NULL");
-  if (variant < LM_FFT_AUTO || variant > LM_FFT_PAIRED) return fail(LM_ERR_INVALID_ARG, "unknown FFT variant");
+  if (variant < LM_FFT_AUTO || variant > LM_FFT_SPLIT_MFMA) return fail(LM_ERR_INVALID_ARG, "unknown FFT variant");
   p->fft_variant = variant;
   return LM_OK;
 }
@@ -531,7 +535,10 @@ int64_t lm_plan_describe(const lm_plan *p, char *buf, int64_t cap) {
   t += "lm_from_stft: filter_rows_kernel (row spans of the caller's filterbank), stft_logmel_kernel, "
        "clamp_fixup_kernel\n";
   std::snprintf(line, sizeof line, "options: fft variant %s, single pass %s\n",
-                p->fft_variant == LM_FFT_FOLDED ? "folded" : p->fft_variant == LM_FFT_PAIRED ? "paired" : "auto",
+                p->fft_variant == LM_FFT_FOLDED   ? "folded"
+                : p->fft_variant == LM_FFT_PAIRED ? "paired"
+                : p->fft_variant == LM_FFT_SPLIT_MFMA ? "split_mfma"
+                                                      : "auto",
                 p->single_pass ? (p->device < 0 ? "requested" : p->coop_launch ? "requested (cooperative launch)"
                                                                              : "requested (not available here)")
                                : "off");

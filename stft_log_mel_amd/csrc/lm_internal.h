@@ -68,6 +68,7 @@ struct DeviceTables {
   const float *csr_w = nullptr;
   int nnz = 0;
   const uint16_t *mfma400h = nullptr;
+  const uint16_t *mfma400t = nullptr;   // n_fft = 400: second-stage (25-point DFT) operands
   const int32_t *melblk_meta = nullptr;
   const float *melblk_w = nullptr;
   int n_melblk = 0;
@@ -107,6 +108,8 @@ struct lm_plan {
   std::vector<float> untangle;    // 2 * (M/2 + 1)
   std::vector<float> twid2;       // n_fft >= 8192: 2 * (n_fft / 128 + 128), see build_twiddles
   std::vector<uint16_t> mfma400h;  // n_fft = 400 only: first-stage matrix as fp16 hi/lo parts (25 x 2 x 2 x 16 x 8)
+  std::vector<uint16_t> mfma400t;  // n_fft = 400 only: 25-point DFT as fp16 hi/lo operands (4 x 5 x 64 x 8)
+  bool mfma400t_fits = false;      // the window keeps every first-stage value in the second stage's fp16 range
   std::vector<int32_t> melblk_meta;  // per batch of mel steps: first bin of each quad, last-batch flag
   std::vector<float> melblk_w;       // blocked filter weights in matrix-core lane order
   std::vector<int32_t> mel_lanes;    // n_fft >= 8192: mel lane table of the one-frame kernel (build_mel_lanes)

@@ -834,7 +834,7 @@ static int generic_frames_per_tile(int n_fft) {
 }
 
 static bool use_pcm400(const lm_plan *p, bool in_i16) {
-  return p->fft_variant == LM_FFT_AUTO && pcm400_supported(p, in_i16);
+  return (p->fft_variant == LM_FFT_AUTO || p->fft_variant == LM_FFT_SPLIT_MFMA) && pcm400_supported(p, in_i16);
 }
 
 std::string pcm_kernel_summary(const lm_plan *p, bool in_i16) {

@@ -58,6 +58,13 @@ constexpr int kAmatH = 25 * 2 * 2 * 16;   // first-stage operands (8 fp16 each):
 constexpr int kLoff = 1694;               // dword offset of the second (low) fp16 plane in the region
 constexpr int kMelWLds = 5632;            // LDS floats for the mel step weights
 constexpr int kMelBatMax = kMelWLds / (16 * kMelBatch);   // mel batches that fit
+// With the 25-point stage on the matrix cores its operand table (20 KB)
+// takes LDS from the mel weights: up to 1920 of them (128 Slaney bands
+// over 0-8 kHz need 1280).
+constexpr int kA2Tab = 4 * 5 * 64;         // second-stage operands (8 fp16 each): [mt][step][lane]
+constexpr int kMelWLds2 = 1920;
+constexpr float kS2In = 0.0009765625f;     // 2^-10: first-stage values into fp16 range
+constexpr int kStoreChunks = 13;           // 16-byte chunks of one (class, frame) second-stage input
 constexpr int kPfI16 = 6, kPfF32 = 11;    // 16-byte sample loads per lane held for the next sub-tile
 
 // compile-time cos/sin of 2 pi j / N for N a multiple of 8 (octant reduction
@@ -168,6 +175,7 @@ struct Args {
   int mel_batches;       // batches of kMelBatch steps over all band blocks
   uint64_t end_mask[2];  // bit b: batch b is the last of its band block
   int mel_out;           // 1: store the mel values themselves (no log tail)
+  const v4f *a2;         // second-stage operands (the matrix-core 25-point form only)
   float *tile_max;
   // single pass only: this call's tag of the clip maxima, the parity of its
   // grid barrier counter, and the slots ([0], [1] barrier counters, [2 + b]
@@ -456,16 +464,22 @@ __device__ __forceinline__ int xcd_rank(int w, int G) {
   return x * q + min(x, r) + j;
 }
 
-template <typename IN, typename OUT, bool SK, bool RES>
+template <typename IN, typename OUT, bool SK, bool RES, bool S2>
 __global__ void __launch_bounds__(kThreads, 1)
 pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ melblk_meta,
               const float *__restrict__ melblk_w, OUT *__restrict__ out, float *__restrict__ tile_min) {
+  static_assert(!(S2 && RES), "the single pass keeps the register 25-point form");
   constexpr bool kI16 = sizeof(IN) == 2;
   constexpr int kTab = kAmatH;
+  constexpr int kMelW = S2 ? kMelWLds2 : kMelWLds;
+  constexpr int kBatMax = kMelW / (16 * kMelBatch);
+  constexpr int kTab2 = S2 ? kA2Tab : 0;
   __shared__ v4f s_amat[kAmatH];   // fp16 operands, 8 per entry
-  __shared__ __attribute__((aligned(16))) float s_melw[kMelWLds];
+  __shared__ v4f s_a2[S2 ? kA2Tab : 1];   // second-stage fp16 operands
+  __shared__ float2 s_w50[16];            // W50^q, q < 16 (the 50-point split)
+  __shared__ __attribute__((aligned(16))) float s_melw[kMelW];
   __shared__ __attribute__((aligned(16))) float s_reg[kWaves * kRegion];
-  __shared__ int s_bat[4 * kMelBatMax];   // per mel batch and quad: first bin
+  __shared__ int s_bat[4 * kBatMax];   // per mel batch and quad: first bin
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -497,12 +511,16 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
     // every table load and the first sub-tile's samples in flight at once
     // (one round trip before the first barrier)
     constexpr int PER = (kTab + kThreads - 1) / kThreads;
-    constexpr int WPT = (kMelWLds + kThreads - 1) / kThreads;
-    static_assert(4 * kMelBatMax <= kThreads, "one batch-table entry per thread");
-    v4f v[PER];
+    constexpr int PER2 = (kTab2 + kThreads - 1) / kThreads;
+    constexpr int WPT = (kMelW + kThreads - 1) / kThreads;
+    static_assert(4 * kBatMax <= kThreads, "one batch-table entry per thread");
+    v4f v[PER], v2[PER2 > 0 ? PER2 : 1];
 #pragma unroll
     for (int u = 0; u < PER; ++u)
       if (tid + u * kThreads < kTab) v[u] = amat[tid + u * kThreads];
+#pragma unroll
+    for (int u = 0; u < PER2; ++u)
+      if (tid + u * kThreads < kTab2) v2[u] = a.a2[tid + u * kThreads];
     const int bat = tid < 4 * a.mel_batches ? melblk_meta[tid] : 0;
     float w[WPT];
 #pragma unroll
@@ -514,6 +532,12 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
 #pragma unroll
     for (int u = 0; u < PER; ++u)
       if (tid + u * kThreads < kTab) s_amat[tid + u * kThreads] = v[u];
+    if constexpr (S2) {
+#pragma unroll
+      for (int u = 0; u < PER2; ++u)
+        if (tid + u * kThreads < kTab2) s_a2[tid + u * kThreads] = v2[u];
+      if (tid < 16) s_w50[tid] = w400(8 * tid);
+    }
     if (tid < 4 * a.mel_batches) s_bat[tid] = bat & 0xffff;
     if (tid == 0) s_next = kWaves;
 #pragma unroll
@@ -595,13 +619,19 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
     // (the single pass has one sub-tile per wave: nothing to prefetch)
     const SubTile t = tc;
     gs_next = RES ? wg_end : wg0 + __builtin_amdgcn_readfirstlane(claim);
-    if (gs_next < wg_end) {
-      const int64_t n = gs_next - gs;   // >= 1 (uniform)
-      tc = n <= a.S ? advance(a, tc, (int)n) : locate(a, gs_next);
-      have = prefetch<IN>(a, pcm, tc, span, pf);
-    } else {
-      have = false;
-    }
+    // the next sub-tile's samples: loads issued here, before the transform
+    // (the matrix-core 25-point form issues them after its second stage,
+    // where its registers are free again)
+    auto issue_prefetch = [&]() {
+      if (gs_next < wg_end) {
+        const int64_t n = gs_next - gs;   // >= 1 (uniform)
+        tc = n <= a.S ? advance(a, tc, (int)n) : locate(a, gs_next);
+        have = prefetch<IN>(a, pcm, tc, span, pf);
+      } else {
+        have = false;
+      }
+    };
+    issue_prefetch();
 
     // 2. window + 16-point DFT + twiddle on the matrix cores: D[n1] = A[n1] x[n1],
     //    per n1 two fp16 products (matrix hi and lo parts) over k-slots e of
@@ -636,56 +666,197 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
       }
     }
 
-    // 3. 25-point DFTs over n1.  Za: class g + 1 (rows 4g, 4g+1).  Zb: class
-    //    7 - g (rows 4g+2, 4g+3) for g < 3; for g = 3, z[m] = s[2m] + i s[2m+1]
-    //    with s[n1 + 25 e] the sum over n2 of parity e (rows 14, 15).
-    float2 Za[25], Zb[25];
-#pragma unroll
-    for (int n1 = 0; n1 < 25; ++n1) Za[n1] = make_float2(D[n1][0], D[n1][1]);
-#pragma unroll
-    for (int m = 0; m < 25; ++m) {
-      const int e = 2 * m, o = 2 * m + 1;
-      const float se = e < 25 ? D[e][2] : D[e - 25][3];
-      const float so = o < 25 ? D[o][2] : D[o - 25][3];
-      Zb[m] = make_float2(g3 ? se : D[m][2], g3 ? so : D[m][3]);
-    }
-    dft25(Za);
-    dft25(Zb);
-
-    // 4. power rows (every value is 4 |X[k]|^2: the class rows are scaled by
-    //    2 in the matrix).  Za output k1 is bin 16 k1 + (g+1), or its mirror
-    //    400 - that for k1 > 12.  Zb outputs of groups 0..2 are bins 16 k1 +
-    //    7 - g and mirrors alike; they are taken in pairs (j, 25 - j), bins
-    //    16 j + 7 - g and 16 j - 7 + g, so that group 3 can share the loop:
-    //    there, with u = Zb[j], v = Zb[25 - j], A = u + v*, B = u - v* and W =
-    //    W50^j, the 50-point real DFT gives 2 S[j] = A - i W B (bin 8 j) and
-    //    conj(2 S[25 - j]) = A + i W B (bin 200 - 8 j).  The complex values
-    //    are formed before squaring, so a weak bin is not the difference of
-    //    two large squares.
     float *Rc = R + c * kRow;
-    {
-      float *pa = Rc + (g + 1), *pb = Rc + (15 - g);
+    if constexpr (S2) {
+      // 3'. The 25-point DFTs over n1 on the matrix cores, in two rounds.
+      //     Round 0 takes each lane's rows 4g, 4g+1 (class g + 1), round 1
+      //     its rows 4g+2, 4g+3 (class 7 - g), or for g = 3 the sequence
+      //     s[i] = s[n1 + 25 e] (rows 14, 15) in natural order, so that
+      //     z[m] = s[2m] + i s[2m+1].  A lane stores its class's 50 inputs
+      //     (times 2^-10, into fp16 range) as fp16 hi and lo parts, 13
+      //     chunks of 16 bytes, in the wave's region; the region's staged
+      //     span has been read by then (one wave's LDS operations complete
+      //     in order).  Then each of the round's four class jobs runs as
+      //     products with the (job, frame) chunks as B operand (column =
+      //     frame) against the DFT matrix (64 rows x five 32-wide steps,
+      //     see the plan's table): lane (c, g) ends with quad q = 4 mt + g,
+      //     i.e. Z[q] and Z[25 - q], of every job for frame c.
+      asm volatile("" ::: "memory");
+      const u4 *st = reinterpret_cast<const u4 *>(R);
+      u4 *mine = reinterpret_cast<u4 *>(R) + (g * 16 + c) * kStoreChunks;
+      const int cbase = c * kStoreChunks;
+      const int f4 = g < 2 ? 4 + g : (g == 2 ? 12 : 0);   // the last step's chunk (g = 3: any, A is zero)
+      float *rq = Rc + 16 * g, *rs = Rc + 8 * g, *rm = Rc - 8 * g;
+      auto put_quad = [&](int r, int jb, int mt, float p0, float p1) {
+        if (mt == 3 && g != 0) return;   // quads 13..15 hold nothing
+        if (r == 1 && jb == 3) {
+          rs[32 * mt] = p0;
+          rm[200 - 32 * mt] = p1;
+        } else {
+          const int k = r == 0 ? jb + 1 : 7 - jb;
+          rq[64 * mt + k] = p0;
+          if (mt > 0 || g > 0) rq[64 * mt - k] = p1;
+        }
+      };
+      // the lane's class values of round r in K order, as fp16 hi / lo
+      // dwords, stored chunk by chunk (few of them live at a time)
+      auto convert_store = [&](int r) {
+        auto pair = [&](int n, uint32_t &H, uint32_t &L) {
+          float x0, x1;
+          if (r == 0) {
+            x0 = D[n][0];
+            x1 = D[n][1];
+          } else {
+            const int i0 = 2 * n, i1 = 2 * n + 1;
+            const float s0 = i0 < 25 ? D[i0][2] : D[i0 - 25][3];
+            const float s1 = i1 < 25 ? D[i1][2] : D[i1 - 25][3];
+            x0 = g3 ? s0 : D[n][2];
+            x1 = g3 ? s1 : D[n][3];
+          }
+          split_f32(x0, x1, kS2In, H, L);
+        };
 #pragma unroll
-      for (int k1 = 0; k1 < 25; ++k1) {
-        const float p = __builtin_fmaf(Za[k1].x, Za[k1].x, Za[k1].y * Za[k1].y);
-        if (k1 <= 12) pa[16 * k1] = p;
-        else pb[16 * (24 - k1)] = p;
+        for (int j = 0; j < 6; ++j) {
+          uint32_t H[4], L[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) pair(4 * j + k, H[k], L[k]);
+          mine[j] = u4{H[0], H[1], H[2], H[3]};
+          mine[6 + j] = u4{L[0], L[1], L[2], L[3]};
+        }
+        uint32_t H, L;
+        pair(24, H, L);
+        mine[12] = u4{H, L, H, 0u};
+      };
+      // The products of round r in two halves of the output rows (mt 0, 1
+      // and 2, 3), operands one step ahead; `done` takes each (job, mt)
+      // result.
+      auto products = [&](int r, auto done) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          v4f acc[4][2];
+#pragma unroll
+          for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) acc[jb][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+          v8h Bv[1][4], Av[1][2];
+          auto load_step = [&](int t, v8h (&B)[4], v8h (&A)[2]) {
+            // B chunk of lane group g at step t (the plan's pairing): hi
+            // 0..5, lo 6..11, the inputs-48/49 tail 12
+            const int f = t < 3 ? 4 * t + g : (t == 3 ? g : f4);
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) B[jb] = __builtin_bit_cast(v8h, st[jb * 16 * kStoreChunks + cbase + f]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) A[i] = __builtin_bit_cast(v8h, s_a2[((2 * hf + i) * 5 + t) * 64 + lane]);
+          };
+#pragma unroll
+          for (int t = 0; t < 5; ++t) {
+            load_step(t, Bv[0], Av[0]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+              for (int jb = 0; jb < 4; ++jb)
+                acc[jb][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Av[0][i], Bv[0][jb], acc[jb][i], 0, 0, 0);
+            asm volatile("" ::: "memory");   // at most two steps' operands in registers
+          }
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) done(jb, 2 * hf + i, i, acc[jb][i]);
+        }
+      };
+      // 4'. |X|^2 of the lane's quads (4 |X|^2 as in the register form: the
+      //     class rows carry a factor 2, the split gives 2 S).  Job 3 of
+      //     round 1 is the 50-point real split: with u = Z[q], v = Z[25 - q],
+      //     A = u + v*, B = u - v* and W = W50^q, 2 S[q] = A - i W B (bin 8 q)
+      //     and conj(2 S[25 - q]) = A + i W B (bin 200 - 8 q).
+      auto power2 = [&](bool split, int mt, const v4f &z, float &p0, float &p1) {
+        if (split) {
+          const float2 W = s_w50[4 * mt + g];
+          const float Ax = z[0] + z[2], Ay = z[1] - z[3], Bx = z[0] - z[2], By = z[1] + z[3];
+          const float p = __builtin_fmaf(W.x, Bx, -W.y * By), q = __builtin_fmaf(W.x, By, W.y * Bx);
+          const float X1x = Ax + q, X1y = Ay - p, X2x = Ax - q, X2y = Ay + p;
+          p0 = __builtin_fmaf(X1x, X1x, X1y * X1y);
+          p1 = __builtin_fmaf(X2x, X2x, X2y * X2y);
+        } else {
+          p0 = __builtin_fmaf(z[0], z[0], z[1] * z[1]);
+          p1 = __builtin_fmaf(z[2], z[2], z[3] * z[3]);
+        }
+      };
+      convert_store(0);
+      asm volatile("" ::: "memory");
+      // round 0's power values wait in registers until round 1's operand
+      // reads are done, since the power rows overwrite the operand chunks
+      float pw0[4][4][2];
+      products(0, [&](int jb, int mt, int, const v4f &z) { power2(false, mt, z, pw0[jb][mt][0], pw0[jb][mt][1]); });
+      asm volatile("" ::: "memory");
+      convert_store(1);
+      asm volatile("" ::: "memory");
+      float pw1[4][2][2];   // round 1's first half, written after the second half's reads
+      products(1, [&](int jb, int mt, int i, const v4f &z) {
+        float p0, p1;
+        power2(jb == 3, mt, z, p0, p1);
+        if (mt < 2) {
+          pw1[jb][i][0] = p0;
+          pw1[jb][i][1] = p1;
+        } else {
+          put_quad(1, jb, mt, p0, p1);
+          put_quad(1, jb, i, pw1[jb][i][0], pw1[jb][i][1]);
+          put_quad(0, jb, mt, pw0[jb][mt][0], pw0[jb][mt][1]);
+          put_quad(0, jb, i, pw0[jb][i][0], pw0[jb][i][1]);
+        }
+      });
+      asm volatile("" ::: "memory");
+    } else {
+      // 3. 25-point DFTs over n1.  Za: class g + 1 (rows 4g, 4g+1).  Zb: class
+      //    7 - g (rows 4g+2, 4g+3) for g < 3; for g = 3, z[m] = s[2m] + i s[2m+1]
+      //    with s[n1 + 25 e] the sum over n2 of parity e (rows 14, 15).
+      float2 Za[25], Zb[25];
+#pragma unroll
+      for (int n1 = 0; n1 < 25; ++n1) Za[n1] = make_float2(D[n1][0], D[n1][1]);
+#pragma unroll
+      for (int m = 0; m < 25; ++m) {
+        const int e = 2 * m, o = 2 * m + 1;
+        const float se = e < 25 ? D[e][2] : D[e - 25][3];
+        const float so = o < 25 ? D[o][2] : D[o - 25][3];
+        Zb[m] = make_float2(g3 ? se : D[m][2], g3 ? so : D[m][3]);
       }
-      const int kb = 7 - g;
-      float *q1 = Rc + (g3 ? 0 : kb), *q2 = Rc + (g3 ? 200 : -kb);
-      const int st1 = g3 ? 8 : 16, st2 = g3 ? -8 : 16;
+      dft25(Za);
+      dft25(Zb);
+
+      // 4. power rows (every value is 4 |X[k]|^2: the class rows are scaled by
+      //    2 in the matrix).  Za output k1 is bin 16 k1 + (g+1), or its mirror
+      //    400 - that for k1 > 12.  Zb outputs of groups 0..2 are bins 16 k1 +
+      //    7 - g and mirrors alike; they are taken in pairs (j, 25 - j), bins
+      //    16 j + 7 - g and 16 j - 7 + g, so that group 3 can share the loop:
+      //    there, with u = Zb[j], v = Zb[25 - j], A = u + v*, B = u - v* and W =
+      //    W50^j, the 50-point real DFT gives 2 S[j] = A - i W B (bin 8 j) and
+      //    conj(2 S[25 - j]) = A + i W B (bin 200 - 8 j).  The complex values
+      //    are formed before squaring, so a weak bin is not the difference of
+      //    two large squares.
+      {
+        float *pa = Rc + (g + 1), *pb = Rc + (15 - g);
 #pragma unroll
-      for (int j = 0; j < 13; ++j) {
-        const float2 u = Zb[j], v = Zb[(25 - j) % 25];
-        const float2 A = make_float2(u.x + v.x, u.y - v.y), B = make_float2(u.x - v.x, u.y + v.y);
-        const float wx = kW400.c[8 * j], wy = kW400.s[8 * j];
-        const float p = __builtin_fmaf(wx, B.x, -wy * B.y), q = __builtin_fmaf(wx, B.y, wy * B.x);   // W B
-        const float2 X1 = g3 ? make_float2(A.x + q, A.y - p) : u;
-        const float2 X2 = g3 ? make_float2(A.x - q, A.y + p) : v;
-        q1[st1 * j] = __builtin_fmaf(X1.x, X1.x, X1.y * X1.y);
-        const float p2 = __builtin_fmaf(X2.x, X2.x, X2.y * X2.y);
-        if (j == 0) Rc[g3 ? 200 : kb] = p2;
-        else q2[st2 * j] = p2;
+        for (int k1 = 0; k1 < 25; ++k1) {
+          const float p = __builtin_fmaf(Za[k1].x, Za[k1].x, Za[k1].y * Za[k1].y);
+          if (k1 <= 12) pa[16 * k1] = p;
+          else pb[16 * (24 - k1)] = p;
+        }
+        const int kb = 7 - g;
+        float *q1 = Rc + (g3 ? 0 : kb), *q2 = Rc + (g3 ? 200 : -kb);
+        const int st1 = g3 ? 8 : 16, st2 = g3 ? -8 : 16;
+#pragma unroll
+        for (int j = 0; j < 13; ++j) {
+          const float2 u = Zb[j], v = Zb[(25 - j) % 25];
+          const float2 A = make_float2(u.x + v.x, u.y - v.y), B = make_float2(u.x - v.x, u.y + v.y);
+          const float wx = kW400.c[8 * j], wy = kW400.s[8 * j];
+          const float p = __builtin_fmaf(wx, B.x, -wy * B.y), q = __builtin_fmaf(wx, B.y, wy * B.x);   // W B
+          const float2 X1 = g3 ? make_float2(A.x + q, A.y - p) : u;
+          const float2 X2 = g3 ? make_float2(A.x - q, A.y + p) : v;
+          q1[st1 * j] = __builtin_fmaf(X1.x, X1.x, X1.y * X1.y);
+          const float p2 = __builtin_fmaf(X2.x, X2.x, X2.y * X2.y);
+          if (j == 0) Rc[g3 ? 200 : kb] = p2;
+          else q2[st2 * j] = p2;
+        }
       }
     }
     // zero the pad columns 201..211 of the lane's row, which the last chunks read
@@ -702,11 +873,14 @@ pcm400_kernel(Args a, const v4f *__restrict__ amat, const int32_t *__restrict__ 
     // float input at power 2: the mel sums carry 2^2e (exact power of two)
     const int mel_e = (kI16 || a.power != 2.0f) ? 0 : -2 * esc;
 
-    // the next sub-tile's samples have arrived by now (their loads went out
-    // before this sub-tile's first stage): retiring the registers here,
-    // before this sub-tile's stores, spares the next staging a wait for them
+    {
+      // the next sub-tile's samples have arrived by now (their loads went
+      // out before this sub-tile's first stage): retiring the registers
+      // here, before this sub-tile's stores, spares the next staging a wait
+      // for them
 #pragma unroll
-    for (int i = 0; i < Prefetch<IN>::N; ++i) asm volatile("" ::"v"(pf.v[i]));
+      for (int i = 0; i < Prefetch<IN>::N; ++i) asm volatile("" ::"v"(pf.v[i]));
+    }
     // 5. mel sums on 4x4x1 matrix blocks (16 per instruction): block (quad
     //    g, frame quad c / 4) of step s multiplies the power of 4 frames at
     //    bin qs_g + s by the weights of the 4 bands of quad 4 jb + g there,
@@ -906,14 +1080,24 @@ bool pcm400_supported(const lm_plan *p, bool in_i16) {
   return lds_dw <= kLoff && kLoff + lds_dw <= kRegion;
 }
 
+// The 25-point stage runs on the matrix cores when that form is asked for,
+// the blocked weights fit next to its operand table and the window keeps
+// every first-stage value in fp16 range.
+bool pcm400_matrix25(const lm_plan *p) {
+  return p->fft_variant == LM_FFT_SPLIT_MFMA && p->mfma400t_fits && !p->mfma400t.empty() &&
+         p->melblk_w.size() <= (size_t)kMelWLds2 && p->melblk_meta.size() / 4 <= (size_t)(kMelWLds2 / (16 * kMelBatch));
+}
+
 std::string pcm400_summary(const lm_plan *p) {
-  char buf[320];
+  char buf[400];
+  const bool m25 = pcm400_matrix25(p);
   std::snprintf(buf, sizeof buf,
                 "pcm400_kernel: first stage on v_mfma_f32_16x16x32_f16 (two-part fp16 operands, fp32 "
-                "accumulate), 25-point DFTs in registers, %d-frame sub-tiles per wave, %d waves per "
+                "accumulate), 25-point DFTs %s, %d-frame sub-tiles per wave, %d waves per "
                 "workgroup, one workgroup per compute unit; mel on 4x4x1 fp32 matrix blocks: %zu batches "
                 "of %d steps, %zu of %d blocked weights",
-                kSub, kWaves, p->melblk_meta.size() / 4, kMelBatch, p->melblk_w.size(), kMelWLds);
+                m25 ? "on v_mfma_f32_16x16x32_f16 (two-part fp16 operands, three products)" : "in registers",
+                kSub, kWaves, p->melblk_meta.size() / 4, kMelBatch, p->melblk_w.size(), m25 ? kMelWLds2 : kMelWLds);
   return buf;
 }
 
@@ -928,7 +1112,8 @@ StatLayout pcm400_stat_layout(const lm_plan *p) {
 }
 
 bool pcm400_single_pass(const lm_plan *p, bool in_i16, int64_t n_sub) {
-  return p->single_pass && p->coop_launch && p->output == LM_OUTPUT_LOGMEL && p->fft_variant == LM_FFT_AUTO &&
+  return p->single_pass && p->coop_launch && p->output == LM_OUTPUT_LOGMEL &&
+         (p->fft_variant == LM_FFT_AUTO || p->fft_variant == LM_FFT_SPLIT_MFMA) &&
          pcm400_supported(p, in_i16) &&
          p->n_cu > 0 && n_sub <= (int64_t)p->n_cu * kWaves;
 }
@@ -954,7 +1139,11 @@ hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &pa, hipStream_t s, con
   // 2^12 2^15 / 64 = 2^21 per |X|; float planes hold x 2^e, so 2^12 2^e,
   // whose 2^e the kernel takes back per sub-tile (the normalisation's factor
   // on |X|^2 joins them)
-  const double in_scale2 = (pa.in_i16 ? 1.0 / 4398046511104.0 : 1.0 / 16777216.0) * power_scale2(p);   // 2^-42, 2^-24
+  // The matrix-core 25-point stage takes the values times 2^-10 and its
+  // matrix carries 2^8: 2^-2 per |X|, 2^-4 on every power value.
+  const bool m25 = !pa.sync && pcm400_matrix25(p);
+  const double in_scale2 = (pa.in_i16 ? 1.0 / 4398046511104.0 : 1.0 / 16777216.0) * power_scale2(p) *
+                           (m25 ? 16.0 : 1.0);   // 2^-42, 2^-24 (times 2^4)
   if (p->power == 2.0f) {
     k.mel_scale = (float)(0.25 * in_scale2);
     k.pre_scale = 1.0f;
@@ -975,6 +1164,7 @@ hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &pa, hipStream_t s, con
   k.epoch = pa.epoch;
   k.parity = pa.parity;
   k.sync = pa.sync;
+  k.a2 = reinterpret_cast<const v4f *>(p->dt.mfma400t);
   const dim3 grid((unsigned)n_wg), block(kThreads);
   const bool f16 = p->out_dtype == LM_F16;
   const v4f *am = reinterpret_cast<const v4f *>(p->dt.mfma400h);
@@ -989,11 +1179,13 @@ hipError_t launch_pcm400(const lm_plan *p, const PcmArgs &pa, hipStream_t s, con
       void *args[] = {&k, (void *)&am, (void *)&bm, (void *)&bw, (void *)&op, (void *)&tmin};    \
       if (tm) (void)hipEventRecord(tm->beg, s);                                                    \
       const hipError_t e = hipLaunchCooperativeKernel(                                             \
-          reinterpret_cast<const void *>(&pcm400_kernel<IN, OUT, SK, true>), grid, block, args, 0, s); \
+          reinterpret_cast<const void *>(&pcm400_kernel<IN, OUT, SK, true, false>), grid, block, args, 0, s); \
       if (e != hipSuccess) return e;                                                               \
       if (tm) (void)hipEventRecord(tm->end, s);                                                    \
+    } else if (m25) {                                                                              \
+      LM_LAUNCH(tm, (pcm400_kernel<IN, OUT, SK, false, true>), grid, block, 0, s, k, am, bm, bw, (OUT *)pa.out, tmin); \
     } else {                                                                                       \
-      LM_LAUNCH(tm, (pcm400_kernel<IN, OUT, SK, false>), grid, block, 0, s, k, am, bm, bw, (OUT *)pa.out, tmin); \
+      LM_LAUNCH(tm, (pcm400_kernel<IN, OUT, SK, false, false>), grid, block, 0, s, k, am, bm, bw, (OUT *)pa.out, tmin); \
     }                                                                                              \
   } while (0)
   if (!pa.in_i16 && !f16) {

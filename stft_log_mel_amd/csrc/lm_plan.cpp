@@ -143,6 +143,77 @@ void build_mfma400(lm_plan *p) {
           p->mfma400h[((((size_t)n1 * 2 + 0) * 2 + h) * 16 + m) * 8 + e] = bh;
           p->mfma400h[((((size_t)n1 * 2 + 1) * 2 + h) * 16 + m) * 8 + e] = bl;
         }
+
+  // Second stage: the 25-point DFT over n1, Z[k] = sum_n W25^(n k) z[n], as
+  // a real 64 x 50 matrix (scaled by 2^8) on v_mfma_f32_16x16x32_f16.
+  // Input index i = 2 n + (0: real, 1: imaginary part of z[n]).  Output rows
+  // come in quads q = row / 4 < 13: Re Z[q], Im Z[q], Re Z[25 - q], Im
+  // Z[25 - q] (q = 0 repeats Z[0]), so a lane holds the pair (q, 25 - q)
+  // that a conjugate-mirror class or the 50-point real split needs; rows of
+  // quads 13..15 are zero.  Both operands carry about 22 bits as fp16 hi +
+  // lo parts, and the product keeps hi.hi, hi.lo and lo.hi: the K slots of
+  // the five 32-wide steps pair, per 8-slot chunk of lane group gq,
+  //   step 0: A hi, inputs 8 gq..          with B hi of the same inputs
+  //   step 1: A hi, inputs 8 (4 + gq) (gq < 2) or 8 (gq - 2) (gq >= 2) with B hi / B lo
+  //   step 2: A hi, inputs 8 (2 + gq)      with B lo
+  //   step 3: A lo, inputs 8 gq            with B hi
+  //   step 4: A lo, inputs 8 (4 + gq) (gq < 2); gq = 2: inputs 48, 49 as
+  //           (hi.hi, hi.lo, lo.hi) and two zero slots; gq = 3: zero
+  // (the kernel reads the matching B chunk).  Entry [mt][step][lane] holds
+  // lane (row 16 mt + lane % 16, group lane / 16)'s 8 slots as fp16 bits.
+  constexpr double kS2Scale = 256.0;
+  // The second stage takes the first stage's values times 2^-10 as fp16:
+  // with samples of magnitude at most 512 (both input forms) and the matrix
+  // scaled by 2^12, every value stays below fp16's largest finite value when
+  // each row's absolute sum over n2 keeps 2^12 * 512 * sum * 2^-10 under
+  // 65504 (the periodic Hann gives sum <= 16 on a class row: 32768).
+  double row_abs = 0.0;
+  for (int n1 = 0; n1 < 25; ++n1)
+    for (int m = 0; m < 16; ++m) {
+      double sum = 0.0;
+      for (int n2 = 0; n2 < 16; ++n2) sum += std::fabs(entry(n1, m, n2));
+      row_abs = std::max(row_abs, sum);
+    }
+  p->mfma400t_fits = 4096.0 * 512.0 * row_abs / 1024.0 <= 60000.0;
+  auto dft_coef = [](int row, int in) -> double {
+    const int q = row / 4, r = row % 4;
+    if (q > 12) return 0.0;
+    const int k = r < 2 ? q : (25 - q) % 25;
+    const int n = in / 2;
+    const double th = 2.0 * M_PI * (double)((n * k) % 25) / 25.0;
+    const double c = std::cos(th), s = std::sin(th);
+    if ((r & 1) == 0) return (in & 1) == 0 ? c : s;   // Re Z[k] = sum cos re + sin im
+    return (in & 1) == 0 ? -s : c;                     // Im Z[k] = sum -sin re + cos im
+  };
+  p->mfma400t.assign((size_t)4 * 5 * 64 * 8, 0);
+  for (int mt = 0; mt < 4; ++mt)
+    for (int t = 0; t < 5; ++t)
+      for (int lane = 0; lane < 64; ++lane)
+        for (int e = 0; e < 8; ++e) {
+          const int row = 16 * mt + lane % 16, gq = lane / 16;
+          int part = 0, in = -1;   // part 0: hi, 1: lo; in < 0: zero slot
+          switch (t) {
+            case 0: in = 8 * gq + e; break;
+            case 1: in = 8 * (gq < 2 ? 4 + gq : gq - 2) + e; break;
+            case 2: in = 8 * (2 + gq) + e; break;
+            case 3: part = 1; in = 8 * gq + e; break;
+            default:
+              if (gq < 2) {
+                part = 1;
+                in = 8 * (4 + gq) + e;
+              } else if (gq == 2 && e < 6) {
+                part = e < 4 ? 0 : 1;
+                in = 48 + e % 2;
+              }
+          }
+          if (in < 0) continue;
+          const double v = kS2Scale * dft_coef(row, in);
+          const _Float16 hi = (_Float16)v;
+          const _Float16 lo = (_Float16)(v - (double)hi);
+          uint16_t b;
+          std::memcpy(&b, part == 0 ? &hi : &lo, 2);
+          p->mfma400t[(((size_t)mt * 5 + t) * 64 + lane) * 8 + e] = b;
+        }
 }
 
 // Filterbank tables for the n_fft = 400 kernel's mel sum on 4x4x1 matrix

@@ -230,9 +230,9 @@ def test_single_pass_validation():
 def test_fft_variant_validation():
     rc, h = _create()
     assert rc == OK
-    for v in (0, 1, 2):
+    for v in (0, 1, 2, 3):
         assert _lib.lm_plan_set_fft_variant(h, v) == OK
-    for v in (-1, 3):
+    for v in (-1, 4):
         assert _lib.lm_plan_set_fft_variant(h, v) == INVALID
     assert _lib.lm_plan_set_fft_variant(None, 0) == INVALID
     _lib.lm_plan_destroy(h)

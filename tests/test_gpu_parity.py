@@ -597,7 +597,7 @@ def test_pcm400_fast_and_generic_paths(hop, in_dtype):
     B, T = 3, 24321
     x = lm_synth.speech_pcm(B, T, 16000.0, seed=hop, as_int16=(in_dtype == "i16"))
     ref = oracle_pcm(x, 400, hop, 128, 16000.0)
-    for variant in ("auto", "folded", "paired"):
+    for variant in ("auto", "split_mfma", "folded", "paired"):
         say("pcm400 path", hop, in_dtype, "variant", variant)
         out = run_pcm(x, 400, hop, 128, 16000.0, fft_variant=variant)
         check(out, ref, TOL32, f"hop {hop} {in_dtype} variant {variant}")
@@ -621,10 +621,12 @@ def test_pcm400_paired_variant_options(in_dtype, out_dtype, pad_mode, power):
 def test_pcm400_many_bands_both_sides_of_the_table_limit(n_mels, in_dtype):
     """n_fft = 400 with 200 and 256 bands.  Slaney filterbanks of any band
     count up to 256 fit the matrix-core kernel's blocked weight table (at
-    most 5632 floats of LDS: 1536 for 200 bands, 1472 for 256); a caller's
-    dense filterbank (every bin non-zero in every band: 16 blocks of 201
-    steps, 51456 floats) does not, and runs on the generic kernel.  Both must
-    match the oracle, with a clamp-engaged clip in the batch."""
+    most 5632 floats of LDS: 1536 for 200 bands, 1472 for 256; also within
+    the 1920 left beside the matrix-core 25-point stage's operands, which
+    runs them too); a caller's dense filterbank (every bin non-zero in every
+    band: 16 blocks of 201 steps, 51456 floats) does not fit, and runs on
+    the generic kernel.  All must match the oracle, with a clamp-engaged
+    clip in the batch."""
     sr = 16000.0
     B, T = 3, 40000
     x = lm_synth.speech_pcm(B, T, sr, seed=n_mels + (1 if in_dtype == "i16" else 0), as_int16=(in_dtype == "i16"))
@@ -633,6 +635,9 @@ def test_pcm400_many_bands_both_sides_of_the_table_limit(n_mels, in_dtype):
     say("pcm400", n_mels, "bands", in_dtype, "slaney (fits the table)")
     out = run_pcm(x, 400, 160, n_mels, sr)
     check(out, oracle.from_pcm(x, 400, 160, W), TOL32, f"{n_mels} bands slaney {in_dtype}")
+    say("pcm400", n_mels, "bands", in_dtype, "slaney, 25-point stage on the matrix cores")
+    out = run_pcm(x, 400, 160, n_mels, sr, fft_variant="split_mfma")
+    check(out, oracle.from_pcm(x, 400, 160, W), TOL32, f"{n_mels} bands slaney {in_dtype} split_mfma")
     rng = np.random.default_rng(n_mels)
     D = (rng.random((n_mels, 201)) * 0.02 + 1e-4).astype(np.float32)   # dense: too wide for the table
     say("pcm400", n_mels, "bands", in_dtype, "dense caller filterbank (generic kernel)")
@@ -640,6 +645,26 @@ def test_pcm400_many_bands_both_sides_of_the_table_limit(n_mels, in_dtype):
     out2 = p.from_pcm(to_dev(x))
     torch.cuda.synchronize()
     check(out2, oracle.from_pcm(x, 400, 160, D.astype(np.float64)), TOL32, f"{n_mels} bands dense {in_dtype}")
+
+
+@pytest.mark.parametrize("in_dtype,out_dtype", [("i16", "f32"), ("f32", "f16")])
+def test_pcm400_wide_caller_bands_take_the_register_form(in_dtype, out_dtype):
+    """A caller's filterbank of 128 bands 40 bins wide needs 5504 blocked
+    weights: more than fit next to the matrix-core 25-point stage's operands
+    (1920), within the register form's 5632, so asking for the matrix-core
+    form gets the register form.  The plan description names the form, and
+    the result must match the oracle."""
+    x = lm_synth.speech_pcm(2, 24000, 16000.0, seed=77, as_int16=(in_dtype == "i16"))
+    W = np.zeros((128, 201), dtype=np.float32)
+    for m in range(128):
+        W[m, max(0, m - 20):m + 20] = 0.01 + 0.001 * m
+    p = lm().Plan(400, 160, 128, out_dtype=out_dtype).set_filters(W).set_fft_variant("split_mfma")
+    assert "25-point DFTs in registers" in p.describe()
+    say("pcm400 register 25-point form, wide caller bands", in_dtype, out_dtype)
+    out = p.from_pcm(to_dev(x))
+    torch.cuda.synchronize()
+    check(out, oracle.from_pcm(x, 400, 160, W.astype(np.float64)), TOL32 if out_dtype == "f32" else TOL16,
+          f"wide caller bands {in_dtype} {out_dtype}")
 
 
 def _random_pcm_config(rng):
@@ -744,9 +769,13 @@ def test_pcm400_two_part_fp16_first_stage_precision(in_dtype):
     ref = oracle_pcm(x, 400, 160, 128, 16000.0)
     say("pcm400 two-part fp16 first stage vs the all-fp32 transform, full clips", in_dtype)
     e_split = check(run_pcm(x, 400, 160, 128, 16000.0), ref, TOL32, f"{in_dtype} two-part fp16 first stage")
+    e_both = check(run_pcm(x, 400, 160, 128, 16000.0, fft_variant="split_mfma"), ref, TOL32,
+                   f"{in_dtype} two-part fp16 16-point and 25-point stages")
     e_fp32 = check(run_pcm(x, 400, 160, 128, 16000.0, fft_variant="folded"), ref, TOL32, f"{in_dtype} all-fp32")
-    print(f"[case] max |err| two-part fp16 {e_split:.3e}, all-fp32 {e_fp32:.3e}", flush=True)
+    print(f"[case] max |err| two-part fp16 first stage {e_split:.3e}, both stages {e_both:.3e}, "
+          f"all-fp32 {e_fp32:.3e}", flush=True)
     assert e_split <= 2.0 * e_fp32, (e_split, e_fp32)
+    assert e_both <= 2.0 * e_fp32, (e_both, e_fp32)
 
 
 @pytest.mark.parametrize("scale", [3.7e-3, 1.0, 4096.0, 1.5e-9])
