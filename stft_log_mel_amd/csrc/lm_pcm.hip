@@ -65,6 +65,11 @@ __device__ __forceinline__ float to_f(int16_t v) { return (float)(int)v; }
 // early passes fall on distinct banks.
 template <int PAD>
 __device__ __forceinline__ int lds_pos(int i) { return PAD ? i + (i >> PAD) : i; }
+// lds_pos(b + d) - lds_pos(b) for a compile-time step d, valid wherever b
+// and b + d lie in the same 2^PAD block or d is a multiple of 2^PAD
+template <int PAD>
+constexpr int lds_step(int d) { return PAD ? d + (d >> PAD) : d; }
+constexpr bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
 template <int R, int M, int FPB, int THREADS, int Ns, int PAD, typename TW>
 __device__ __forceinline__ void fft_pass(float2 *buf, TW tw, int tid) {
@@ -72,14 +77,29 @@ __device__ __forceinline__ void fft_pass(float2 *buf, TW tw, int tid) {
   constexpr int NB = FPB * NBF;
   constexpr int BPT = (NB + THREADS - 1) / THREADS;
   constexpr int TW_STEP = M / (Ns * R);
+  // Padded positions from one base per butterfly and compile-time steps
+  // where that is exact: reads b + t NBF with NBF a multiple of 2^PAD;
+  // writes o + s Ns with everything a power of two (then either Ns is a
+  // multiple of 2^PAD, or o's offset in its 2^PAD block is below Ns and
+  // the butterfly's outputs cross blocks only at multiples of 2^PAD)
+  constexpr int P2 = 1 << PAD;
+  constexpr bool kReadStep = PAD == 0 || NBF % P2 == 0 || (is_pow2(M) && M <= P2);
+  constexpr bool kWriteStep =
+      PAD == 0 || (is_pow2(M) && M % P2 == 0 && is_pow2(Ns) && is_pow2(R) && (Ns % P2 == 0 || P2 % Ns == 0));
   float2 v[BPT][R];
 #pragma unroll
   for (int i = 0; i < BPT; ++i) {
     const int q = tid + i * THREADS;
     if (NB % THREADS == 0 || q < NB) {
       const int f = q / NBF, j = q - f * NBF;
+      if constexpr (kReadStep) {
+        const float2 *rb = buf + lds_pos<PAD>(f * M + j);
 #pragma unroll
-      for (int t = 0; t < R; ++t) v[i][t] = buf[lds_pos<PAD>(f * M + j + t * NBF)];
+        for (int t = 0; t < R; ++t) v[i][t] = rb[lds_step<PAD>(t * NBF)];
+      } else {
+#pragma unroll
+        for (int t = 0; t < R; ++t) v[i][t] = buf[lds_pos<PAD>(f * M + j + t * NBF)];
+      }
       if (Ns > 1) {
         const int k = j % Ns;
         float2 w[R];
@@ -98,8 +118,14 @@ __device__ __forceinline__ void fft_pass(float2 *buf, TW tw, int tid) {
       const int f = q / NBF, j = q - f * NBF;
       const int k = j % Ns;
       const int o = f * M + (j / Ns) * Ns * R + k;
+      if constexpr (kWriteStep) {
+        float2 *wb = buf + lds_pos<PAD>(o);
 #pragma unroll
-      for (int s = 0; s < R; ++s) buf[lds_pos<PAD>(o + s * Ns)] = v[i][s];
+        for (int s = 0; s < R; ++s) wb[lds_step<PAD>(s * Ns)] = v[i][s];
+      } else {
+#pragma unroll
+        for (int s = 0; s < R; ++s) buf[lds_pos<PAD>(o + s * Ns)] = v[i][s];
+      }
     }
   }
   __syncthreads();
@@ -353,11 +379,13 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
       }
     }
   }
+  static_assert(THREADS % (1 << PAD) == 0, "whole 2^PAD blocks per thread stride");
+  float2 *const wb = s_buf + lds_pos<PAD>(tid);
 #pragma unroll
   for (int u = 0; u < IPT; ++u) {
     const int i = tid + u * THREADS;
     if ((FPB * M) % THREADS == 0 || i < FPB * M)
-      s_buf[lds_pos<PAD>(i)] = make_float2(xs[u][0] * ws[u].x, xs[u][1] * ws[u].y);
+      wb[lds_step<PAD>(u * THREADS)] = make_float2(xs[u][0] * ws[u].x, xs[u][1] * ws[u].y);
   }
   __syncthreads();
 
@@ -576,9 +604,9 @@ __device__ __attribute__((noinline)) void big_padded_frame(const IN *__restrict_
     ys[u][1] = s1 >= 0 ? to_f(x[s1]) : 0.0f;
     ws[u] = win2[n];
   }
+  float2 *const wb = buf + lds_pos<kBigPad>(tid);
 #pragma unroll
-  for (int u = 0; u < IPT; ++u)
-    buf[lds_pos<kBigPad>(tid + u * THREADS)] = make_float2(ys[u][0] * ws[u].x, ys[u][1] * ws[u].y);
+  for (int u = 0; u < IPT; ++u) wb[lds_step<kBigPad>(u * THREADS)] = make_float2(ys[u][0] * ws[u].x, ys[u][1] * ws[u].y);
 }
 
 template <int NFFT, typename IN, typename OUT>
@@ -659,22 +687,23 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS, BigCfg<NFFT>::THREADS /
     if (have && a.hann_tw) {
       // periodic Hann w[n] = 1/2 - 1/2 cos(2 pi n / N), the cosine from the
       // twiddle table in LDS (no global load at the start of the frame)
+      float2 *const wb = s_buf + lds_pos<kBigPad>(tid);
 #pragma unroll
       for (int u = 0; u < IPT; ++u) {
         const int n = tid + u * THREADS;
         const float2 h0 = s_tw[(2 * n) >> 7], l0 = s_tw[THI + ((2 * n) & (kTwLo - 1))];
         const float2 h1 = s_tw[(2 * n + 1) >> 7], l1 = s_tw[THI + ((2 * n + 1) & (kTwLo - 1))];
         const float c0 = __builtin_fmaf(h0.x, l0.x, -h0.y * l0.y), c1 = __builtin_fmaf(h1.x, l1.x, -h1.y * l1.y);
-        s_buf[lds_pos<kBigPad>(n)] = make_float2(xs[u][0] * __builtin_fmaf(-0.5f, c0, 0.5f),
-                                                 xs[u][1] * __builtin_fmaf(-0.5f, c1, 0.5f));
+        wb[lds_step<kBigPad>(u * THREADS)] = make_float2(xs[u][0] * __builtin_fmaf(-0.5f, c0, 0.5f),
+                                                         xs[u][1] * __builtin_fmaf(-0.5f, c1, 0.5f));
       }
     } else if (have) {
       float2 ws[IPT];
 #pragma unroll
       for (int u = 0; u < IPT; ++u) ws[u] = win2[tid + u * THREADS];
+      float2 *const wb = s_buf + lds_pos<kBigPad>(tid);
 #pragma unroll
-      for (int u = 0; u < IPT; ++u)
-        s_buf[lds_pos<kBigPad>(tid + u * THREADS)] = make_float2(xs[u][0] * ws[u].x, xs[u][1] * ws[u].y);
+      for (int u = 0; u < IPT; ++u) wb[lds_step<kBigPad>(u * THREADS)] = make_float2(xs[u][0] * ws[u].x, xs[u][1] * ws[u].y);
     } else {
       big_padded_frame<IN, M, THREADS>(reinterpret_cast<const IN *>(a.pcm) + b * T, win2, fr * a.hop - a.pad, T,
                                        a.sig_pad, a.pad_mode, tid, s_buf);
