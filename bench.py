@@ -10,10 +10,12 @@ per-clip clamp fix-up.  Inputs are generated on the host, copied to HBM once
 and stay resident; several input/output buffer sets are cycled so that every
 step reads its input from HBM rather than from the 256 MB last-level cache.
 The GPU raises its clocks over the first ~30 ms of sustained work (``--ramp``
-prints that curve).  Before the warm-up steps, 60 ms of plain device copies
-(``--clock-ramp-ms``; unrelated to the transform) bring it there, so that
-short runs with few warm-up steps are timed at the sustained clocks too; the
-default warm-up (1000 steps) and the 200 timed steps follow unchanged.
+prints that curve).  Before the warm-up steps of each workload, 500 ms of
+fp32 matrix products (``--clock-ramp-ms``, ``--clock-ramp-kind``; unrelated
+to the transform) bring it there, so that short runs with few warm-up steps
+are timed at the sustained clocks too (plain copies, the other kind, leave
+the compute clock where it was); the default warm-up (1000 steps) and the
+200 timed steps follow unchanged.
 
 Prints ONE JSON line: frames/s for the batch, the main kernel's achieved HBM
 bandwidth against MI355X's 8 TB/s (event-timed on the stream it runs on),
@@ -374,13 +376,16 @@ def clock_ramp(dev, ms: float, kind: str = "copy") -> dict:
     return {"ms": round(spent, 1), "ops": n, "kind": kind}
 
 
-def per_config_entry(name, steps, warmup, dev, check_clips):
+def per_config_entry(name, steps, warmup, dev, check_clips, ramp_ms, ramp_kind):
     """Time one of the other workloads and check a few of its clips."""
     import numpy as np
+    import torch
 
     import lm_synth
     w = lm_synth.WORKLOADS[name]
     r = Run(w, dev, log=False)
+    torch.cuda.synchronize()
+    clock_ramp(dev, ramp_ms, ramp_kind)
     t = r.time(steps, warmup)
     got = r.last_output(steps).float().cpu().numpy()
     errs = [float(np.abs(got[b].astype(np.float64) - r.oracle_clip(b)).max()) for b in range(min(w.B, check_clips))]
@@ -422,10 +427,10 @@ def main():
                     help="time every n_fft of the sweep workloads (one JSON line each, no CPU leg)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (5 times), to scale HBM counters")
-    ap.add_argument("--clock-ramp-kind", default="copy", choices=["copy", "gemm"])
-    ap.add_argument("--clock-ramp-ms", type=float, default=60.0,
-                    help="device time of plain copies before the warm-up steps, so that short runs "
-                         "(few warm-up steps) are timed at the sustained clocks; 0 turns it off")
+    ap.add_argument("--clock-ramp-kind", default="gemm", choices=["copy", "gemm"])
+    ap.add_argument("--clock-ramp-ms", type=float, default=500.0,
+                    help="device time of unrelated work before each workload's warm-up steps, so that "
+                         "short runs (few warm-up steps) are timed at the sustained clocks; 0 turns it off")
     ap.add_argument("--ramp", action="store_true",
                     help="print the step time of every workload in consecutive chunks from an idle GPU "
                          "(how long the clocks take to settle), then exit")
@@ -514,7 +519,8 @@ def main():
         for name in PER_CONFIG:
             print(f"[bench] per-config {name}", file=sys.stderr, flush=True)
             per_config[name] = per_config_entry(name, args.steps, args.warmup, dev,
-                                                check_clips=1 if name != "stft_b256" else 2)
+                                                check_clips=1 if name != "stft_b256" else 2,
+                                                ramp_ms=args.clock_ramp_ms, ramp_kind=args.clock_ramp_kind)
             torch.cuda.empty_cache()
 
     # the fp64 oracle on this host's cores, clips in order, cycling through the
@@ -564,7 +570,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "clock_ramp": {"device_ms": ramp["ms"], "what": f"{ramp['ops']} {ramp['kind']} operations unrelated to the "
-                       "transform before the warm-up steps (clocks to their sustained level)"},
+                       "transform before the warm-up steps of each workload (clocks to their sustained level)"},
         "ms_per_step": round(ms_per_step, 5),
         "ms_per_step_p10_p50_p90": [round(t["p10"], 5), round(t["p50"], 5), round(t["p90"], 5)],
         "higher_is_better": True,
