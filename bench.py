@@ -376,6 +376,84 @@ def clock_ramp(dev, ms: float, kind: str = "copy") -> dict:
     return {"ms": round(spent, 1), "ops": n, "kind": kind}
 
 
+def floored_share(w, got):
+    """How much of an output the per-clip floor decided: the share of values
+    at the clip's floor (the largest output minus 2, i.e. log10 at hi - 8)
+    and, where the main kernel's statistics regions are known (n_fft 400:
+    16 frames x 4 bands; n_fft >= 8192: one frame x all bands), the share of
+    regions holding such a value -- the regions the clamp fix-up rewrites
+    (its gate, on region minima with a small slack, may take a few more)."""
+    import numpy as np
+    tol = 2e-3 if w.out_dtype == "f16" else 1e-6
+    g = got.astype(np.float32)
+    hi = g.reshape(g.shape[0], -1).max(axis=1)
+    at = g <= (hi - 2.0 + tol)[:, None, None]
+    res = {"values_at_floor": round(float(at.mean()), 7)}
+    if w.entry == "pcm" and (w.n_fft == 400 or w.n_fft >= 8192):
+        fr, bd = (16, 4) if w.n_fft == 400 else (1, at.shape[1])
+        B, NM, F = at.shape
+        nf, nb = -(-F // fr), -(-NM // bd)
+        pad = np.zeros((B, nb * bd, nf * fr), dtype=bool)
+        pad[:, :NM, :F] = at
+        reg = pad.reshape(B, nb, bd, nf, fr).any(axis=(2, 4))
+        res["regions"] = int(reg.size)
+        res["region_shape"] = f"{fr} frames x {bd} bands"
+        res["regions_holding_floored_values"] = round(float(reg.mean()), 7)
+    return res
+
+
+def torch_eager(run, steps, got, last):
+    """Context only: the same chain composed from PyTorch's own GPU
+    operators (torch.stft, squared magnitude, matmul, log10, amax, clamp)
+    on the same GPU and the same resident inputs, with the library plan's
+    filterbank; timed with events like the library's steps.  Returns its
+    ms per step and its largest difference from `got`, the library's output
+    of step `last`."""
+    import numpy as np
+    import torch
+    w, dev = run.w, run.ins[0].device
+    if w.entry == "pcm":
+        fb = torch.from_numpy(run.plan.get_filters()).to(dev)               # (n_mels, n_fft/2 + 1)
+        win = torch.hann_window(w.n_fft, periodic=True, dtype=torch.float32, device=dev)
+        scale = 1.0 / 32768.0 if w.in_dtype == "i16" else 1.0
+
+        def chain(i):
+            x = run.ins[i % run.nbuf].to(torch.float32) * scale
+            S = torch.stft(x, w.n_fft, hop_length=w.hop, window=win, center=w.center, pad_mode=w.pad_mode,
+                           return_complex=True)
+            P = (S.real.square() + S.imag.square()).contiguous()            # (B, NF, F)
+            L = torch.log10(torch.clamp(torch.matmul(fb, P), min=1e-10))    # (B, n_mels, F)
+            hi = L.amax(dim=(1, 2), keepdim=True)
+            return (torch.maximum(L, hi - 8.0) + 4.0) / 4.0
+    else:
+        fb = run.filt.t().contiguous()                                      # (NF, NM)
+
+        def chain(i):
+            S = run.ins[i % run.nbuf]
+            P = (S.real.square() + S.imag.square()).contiguous()            # (B, F, NF)
+            L = torch.log10(torch.clamp(torch.matmul(P, fb), min=1e-10))    # (B, F, NM)
+            hi = L.amax(dim=(1, 2), keepdim=True)
+            return (torch.maximum(L, hi - 8.0) + 4.0) / 4.0
+    n = max(1, min(steps, 50))
+    for i in range(3):
+        o = chain(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        o = chain(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    o = chain(last).cpu().numpy()   # the input buffer set that step read
+    diff = float(np.abs(o.astype(np.float64) - got.astype(np.float64)).max())
+    del o
+    torch.cuda.empty_cache()
+    return {"ms_per_step": round(ms, 5), "steps": n, "max_abs_diff_vs_library": diff,
+            "what": "torch.stft + squared magnitude + torch.matmul with the plan's filterbank + log10 / amax / "
+                    "clamp, PyTorch's own GPU operators (fp32), same GPU and resident inputs; context only"}
+
+
 def per_config_entry(name, steps, warmup, dev, check_clips, ramp_ms, ramp_kind):
     """Time one of the other workloads and check a few of its clips."""
     import numpy as np
@@ -388,6 +466,7 @@ def per_config_entry(name, steps, warmup, dev, check_clips, ramp_ms, ramp_kind):
     clock_ramp(dev, ramp_ms, ramp_kind)
     t = r.time(steps, warmup)
     got = r.last_output(steps).float().cpu().numpy()
+    eager = torch_eager(r, steps, got, steps - 1)
     errs = [float(np.abs(got[b].astype(np.float64) - r.oracle_clip(b)).max()) for b in range(min(w.B, check_clips))]
     frames = w.B * w.n_frames
     entry = {
@@ -402,6 +481,8 @@ def per_config_entry(name, steps, warmup, dev, check_clips, ramp_ms, ramp_kind):
         "roofline": roofline_of(w, t["kernel_ms"]["main"]),
         "parity": {"clips_checked": len(errs), "max_abs_err": max(errs),
                    "tol": 2e-3 if w.out_dtype == "f16" else 1e-4},
+        "floor": floored_share(w, got),
+        "torch_eager": {**eager, "library_speedup": round(eager["ms_per_step"] / t["ms_per_step"], 2)},
     }
     del r
     return entry
@@ -488,6 +569,8 @@ def main():
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step (wall {t['wall_s']:.3f}s), "
           f"main kernel {main_ms:.4f} ms, fixup {fix_ms:.4f} ms, pack {pack_ms:.4f} ms", file=sys.stderr, flush=True)
     got = run.last_output(args.steps).float().cpu().numpy()
+    eager = torch_eager(run, args.steps, got, args.steps - 1)
+    print(f"[bench] PyTorch operators, same chain: {eager['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
 
     # the same batch through the all-fp32 folded transform (n_fft = 400 only):
     # the error the two-part fp16 first stage adds is read against it below
@@ -602,6 +685,8 @@ def main():
                          "main_kernel_frac_of_copy": round(per_step_bytes / (main_ms / 1e3) / 1e9 / copy_gbs, 4),
                          "note": "torch copy_ of 2 GiB device to device, read + write bytes per second"},
         "fixup_ms": round(fix_ms, 5),
+        "floor": floored_share(w, got),
+        "torch_eager": {**eager, "library_speedup": round(eager["ms_per_step"] / ms_per_step, 2)},
         "pack_ms": round(pack_ms, 5),
         "cpu_baseline": cpu,
         "parity": parity,

@@ -75,3 +75,21 @@ def test_committed_counter_records_name_their_kernel():
         assert r["kernel"] == bench.main_kernel_name(lm_synth.WORKLOADS[name])
         assert r["bytes_per_launch"] == r["fetch_bytes"] + r["write_bytes"]
         assert len(r["source_hash"]) == 16
+
+
+def test_floored_share_counts_values_and_regions_at_the_clip_floor():
+    import numpy as np
+    w = lm_synth.WORKLOADS["pcm_f32_b8"]          # n_fft 400: regions of 16 frames x 4 bands
+    got = np.full((2, 8, 40), 1.0, dtype=np.float32)
+    got[0, 0, 0] = 3.0                             # clip 0: largest output 3, floor 1
+    got[1, 0, 0] = 2.5                             # clip 1: floor 0.5, nothing at it
+    got[0, 5, 33] = 1.5
+    r = bench.floored_share(w, got)
+    assert r["values_at_floor"] == round((8 * 40 - 2) / (2 * 8 * 40), 7)
+    # clip 0: 2 band groups x 3 frame groups, all hold a floored value; clip 1: none
+    assert r["regions"] == 12 and r["regions_holding_floored_values"] == 0.5
+    big = lm_synth.WORKLOADS["pcm_f32_nfft16384"]  # one frame x all bands
+    g2 = np.zeros((1, 4, 3), dtype=np.float32)
+    g2[0, :, 1] = 2.0
+    r2 = bench.floored_share(big, g2)
+    assert r2["regions"] == 3 and abs(r2["regions_holding_floored_values"] - 2 / 3) < 1e-6
