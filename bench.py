@@ -499,6 +499,8 @@ def main():
     ap.add_argument("--workload", default="pcm_i16_b64")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-per-config", action="store_true", help="time only the headline workload")
+    ap.add_argument("--no-torch", action="store_true",
+                    help="skip the PyTorch-operator composition of the same chain (context only)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--fft-variant", default="auto", choices=["auto", "split_mfma", "folded", "paired"],
                     help="n_fft = 400 transform (comparison only; auto is the library's choice)")
@@ -569,8 +571,11 @@ def main():
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step (wall {t['wall_s']:.3f}s), "
           f"main kernel {main_ms:.4f} ms, fixup {fix_ms:.4f} ms, pack {pack_ms:.4f} ms", file=sys.stderr, flush=True)
     got = run.last_output(args.steps).float().cpu().numpy()
-    eager = torch_eager(run, args.steps, got, args.steps - 1)
-    print(f"[bench] PyTorch operators, same chain: {eager['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
+    eager = None
+    if not args.no_torch:
+        eager = torch_eager(run, args.steps, got, args.steps - 1)
+        print(f"[bench] PyTorch operators, same chain: {eager['ms_per_step']:.4f} ms/step", file=sys.stderr,
+              flush=True)
 
     # the same batch through the all-fp32 folded transform (n_fft = 400 only):
     # the error the two-part fp16 first stage adds is read against it below
@@ -686,7 +691,8 @@ def main():
                          "note": "torch copy_ of 2 GiB device to device, read + write bytes per second"},
         "fixup_ms": round(fix_ms, 5),
         "floor": floored_share(w, got),
-        "torch_eager": {**eager, "library_speedup": round(eager["ms_per_step"] / ms_per_step, 2)},
+        "torch_eager": ({**eager, "library_speedup": round(eager["ms_per_step"] / ms_per_step, 2)}
+                        if eager else None),
         "pack_ms": round(pack_ms, 5),
         "cpu_baseline": cpu,
         "parity": parity,
