@@ -634,15 +634,17 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS, BigCfg<NFFT>::THREADS /
   const int64_t T = a.T, F = a.F;
   constexpr int IPT = M / THREADS;   // complex points per thread
   static_assert(M % THREADS == 0, "whole points per thread");
-  // exp(-2 pi i j / N), 0 <= j < N
-  auto wN = [&](int j) { return cmul(s_tw[j >> 7], s_tw[THI + (j & (kTwLo - 1))]); };
+  // A thread's points n = tid + THREADS u share their low table entries:
+  // 2 THREADS and THREADS are multiples of kTwLo, so for every u the index j
+  // = 2n (window) or n (split) has the same j mod kTwLo and its high index
+  // advances by a compile-time step.
+  static_assert(THREADS % kTwLo == 0, "low twiddle entry shared by a thread's points");
 
-  // samples of an interior frame (no padding), all loads in flight together;
-  // thread tid takes points n = tid + THREADS u
+  // samples of an interior frame (no padding) of clip b at frame fr, all
+  // loads in flight together; thread tid takes points n = tid + THREADS u
   float xs[IPT][2];
-  auto load_interior = [&](int64_t tile, int tid) {
-    const int64_t b = tile / a.tiles_per_clip, fr = tile - b * a.tiles_per_clip;
-    const IN *__restrict__ x = reinterpret_cast<const IN *>(a.pcm) + b * T + (fr * a.hop - a.pad);
+  auto load_interior = [&](int b, int fr, int tid) {
+    const IN *__restrict__ x = reinterpret_cast<const IN *>(a.pcm) + b * T + ((int64_t)fr * a.hop - a.pad);
 #pragma unroll
     for (int u = 0; u < IPT; ++u) {
       const int n = tid + u * THREADS;
@@ -650,9 +652,8 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS, BigCfg<NFFT>::THREADS /
       xs[u][1] = to_f(x[2 * n + 1]);
     }
   };
-  auto interior = [&](int64_t tile) {
-    const int64_t b = tile / a.tiles_per_clip, fr = tile - b * a.tiles_per_clip;
-    const int64_t j0 = fr * a.hop - a.pad;
+  auto interior = [&](int fr) {
+    const int64_t j0 = (int64_t)fr * a.hop - a.pad;
     return j0 >= 0 && j0 + NFFT <= T;
   };
   // Neighbouring frames share n_fft - hop samples (three quarters at hop
@@ -664,10 +665,15 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS, BigCfg<NFFT>::THREADS /
   const int first = G % kXcds == 0 ? (int)(blockIdx.x % kXcds) * (G / kXcds) + (int)(blockIdx.x / kXcds)
                                    : (int)blockIdx.x;
   constexpr bool PREFETCH = BigCfg<NFFT>::PREFETCH;
+  // (clip, frame) of the tile, stepped by G tiles per frame without a
+  // division: G = gq clips + gr frames
+  const int tpc = a.tiles_per_clip;
+  const int gq = G / tpc, gr = G - gq * tpc;
+  int cb = first / tpc, cfr = first - cb * tpc;
   bool have = false;
   if constexpr (PREFETCH) {
-    have = first < n_tiles && interior(first);
-    if (have) load_interior(first, threadIdx.x);
+    have = first < n_tiles && interior(cfr);
+    if (have) load_interior(cb, cfr, threadIdx.x);
   }
 
   for (int64_t tile = first; tile < n_tiles; tile += G) {
@@ -677,11 +683,16 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS, BigCfg<NFFT>::THREADS /
     asm volatile("" : "+s"(win2));
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
-    const int64_t b = tile / a.tiles_per_clip;
-    const int64_t fr = tile - b * a.tiles_per_clip;   // one frame per tile
+    const int64_t b = cb;
+    const int fr = cfr;   // one frame per tile
+    int nb = cb + gq, nfr = cfr + gr;   // the tile G further on
+    if (nfr >= tpc) {
+      nfr -= tpc;
+      ++nb;
+    }
     if constexpr (!PREFETCH) {
-      have = interior(tile);
-      if (have) load_interior(tile, tid);
+      have = interior(fr);
+      if (have) load_interior(cb, fr, tid);
     }
     // wave priorities: the frame's load and window and its mel sums at 1,
     // the FFT passes at 0, so that where two workgroups share a CU (n_fft
@@ -693,13 +704,16 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS, BigCfg<NFFT>::THREADS /
     if (have && a.hann_tw) {
       // periodic Hann w[n] = 1/2 - 1/2 cos(2 pi n / N), the cosine from the
       // twiddle table in LDS (no global load at the start of the frame)
+      // (samples 2n and 2n + 1 share the high entry of index (2n) >> 7, which
+      // advances by 2 THREADS / kTwLo per u; their low entries are those of
+      // 2 tid and 2 tid + 1 for every u)
       float2 *const wb = s_buf + lds_pos<kBigPad>(tid);
+      const float2 *const hb = s_tw + ((2 * tid) >> 7);
+      const float2 l0 = s_tw[THI + ((2 * tid) & (kTwLo - 1))], l1 = s_tw[THI + ((2 * tid + 1) & (kTwLo - 1))];
 #pragma unroll
       for (int u = 0; u < IPT; ++u) {
-        const int n = tid + u * THREADS;
-        const float2 h0 = s_tw[(2 * n) >> 7], l0 = s_tw[THI + ((2 * n) & (kTwLo - 1))];
-        const float2 h1 = s_tw[(2 * n + 1) >> 7], l1 = s_tw[THI + ((2 * n + 1) & (kTwLo - 1))];
-        const float c0 = __builtin_fmaf(h0.x, l0.x, -h0.y * l0.y), c1 = __builtin_fmaf(h1.x, l1.x, -h1.y * l1.y);
+        const float2 h = hb[u * (2 * THREADS / kTwLo)];
+        const float c0 = __builtin_fmaf(h.x, l0.x, -h.y * l0.y), c1 = __builtin_fmaf(h.x, l1.x, -h.y * l1.y);
         wb[lds_step<kBigPad>(u * THREADS)] = make_float2(xs[u][0] * __builtin_fmaf(-0.5f, c0, 0.5f),
                                                          xs[u][1] * __builtin_fmaf(-0.5f, c1, 0.5f));
       }
@@ -711,7 +725,7 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS, BigCfg<NFFT>::THREADS /
 #pragma unroll
       for (int u = 0; u < IPT; ++u) wb[lds_step<kBigPad>(u * THREADS)] = make_float2(xs[u][0] * ws[u].x, xs[u][1] * ws[u].y);
     } else {
-      big_padded_frame<IN, M, THREADS>(reinterpret_cast<const IN *>(a.pcm) + b * T, win2, fr * a.hop - a.pad, T,
+      big_padded_frame<IN, M, THREADS>(reinterpret_cast<const IN *>(a.pcm) + b * T, win2, (int64_t)fr * a.hop - a.pad, T,
                                        a.sig_pad, a.pad_mode, tid, s_buf);
     }
     __syncthreads();
@@ -723,16 +737,23 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS, BigCfg<NFFT>::THREADS /
     // 3. split into the real spectrum; power over the same LDS
     constexpr int NU = M / 2 + 1;
     constexpr int UPT = (NU + THREADS - 1) / THREADS;
+    // point k = tid + THREADS u: Z[k] and Z[M - k] at one base each plus a
+    // compile-time step (THREADS is a multiple of 2^kBigPad); the twiddle
+    // exp(-2 pi i k / N) is hi[k >> 7] lo[tid mod kTwLo]
     float pk[UPT], pmk[UPT];
+    const float2 *const zkb = s_buf + lds_pos<kBigPad>(tid);
+    const float2 *const zcb = s_buf + lds_pos<kBigPad>(M - tid);   // one past the buffer's points for tid = 0
+    const float2 *const wh = s_tw + (tid >> 7);
+    const float2 wl = s_tw[THI + (tid & (kTwLo - 1))];
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       const int k = tid + u * THREADS;
       pk[u] = pmk[u] = 0.0f;
       if (k < NU) {
-        const float2 zk = s_buf[lds_pos<kBigPad>(k)];
-        const float2 zc = cconj(s_buf[lds_pos<kBigPad>(k == 0 ? 0 : M - k)]);
+        const float2 zk = zkb[lds_step<kBigPad>(u * THREADS)];
+        const float2 zc = cconj(k == 0 ? s_buf[0] : zcb[-lds_step<kBigPad>(u * THREADS)]);
         const float2 Y = cadd(zk, zc), D = csub(zk, zc);
-        const float2 V = cmul(wN(k), D);
+        const float2 V = cmul(cmul(wh[u * (THREADS / kTwLo)], wl), D);
         pk[u] = (Y.x + V.y) * (Y.x + V.y) + (Y.y - V.x) * (Y.y - V.x);
         pmk[u] = (Y.x - V.y) * (Y.x - V.y) + (Y.y + V.x) * (Y.y + V.x);
       }
@@ -757,9 +778,8 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS, BigCfg<NFFT>::THREADS /
     __builtin_amdgcn_s_setprio(1);
     // the next frame's samples, in flight during the mel sums
     if constexpr (PREFETCH) {
-      const int64_t nxt = tile + G;
-      have = nxt < n_tiles && interior(nxt);
-      if (have) load_interior(nxt, tid);
+      have = tile + G < n_tiles && interior(nfr);
+      if (have) load_interior(nb, nfr, tid);
     }
 
     // 4. mel: each band's group of Lb lanes strides over its bins; the
@@ -825,6 +845,8 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS, BigCfg<NFFT>::THREADS /
       a.tile_max[tile] = __uint_as_float(mx);
       a.tile_min[tile] = __uint_as_float(mn);
     }
+    cb = nb;
+    cfr = nfr;
   }
 }
 
