@@ -631,6 +631,7 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS, BigCfg<NFFT>::THREADS /
   // this thread's place in the mel stage: band, position h in the band's
   // group of Lb lanes (or none)
   const int lane_ent = a.mel_lanes[threadIdx.x];
+  const int perm32 = (((int)threadIdx.x + 32) & 63) << 2;   // ds_bpermute address of lane + 32 in the wave
   const int64_t T = a.T, F = a.F;
   constexpr int IPT = M / THREADS;   // complex points per thread
   static_assert(M % THREADS == 0, "whole points per thread");
@@ -792,21 +793,45 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS, BigCfg<NFFT>::THREADS /
       const int m = lane_ent & 255, h = (lane_ent >> 8) & 255, Lb = lane_ent >= 0 ? 1 << (lane_ent >> 16) : 1;
       float acc0 = 0.0f, acc1 = 0.0f;
       if (lane_ent >= 0) {
-        const int st = s_start[m], wd = s_width[m];
-        const float *pr = P + st;
-        const float *wr = wsrc + s_off[m];
-        int j = h;
-        for (; j + Lb < wd; j += 2 * Lb) {
-          acc0 = __builtin_fmaf(wr[j], pr[j], acc0);
-          acc1 = __builtin_fmaf(wr[j + Lb], pr[j + Lb], acc1);
+        // pairs of adjacent bins 2h + 2 Lb t and the next one, in two
+        // chains: both reads of a chain's step come off one pointer (an
+        // immediate offset for the second), and the pointers step by 2 Lb;
+        // an odd band's last bin is the single one at the end
+        const int wd = s_width[m];
+        const float *pr = P + s_start[m] + 2 * h;
+        const float *wr = wsrc + s_off[m] + 2 * h;
+        int j = 2 * h;
+        for (; j + 1 < wd; j += 2 * Lb) {
+          acc0 = __builtin_fmaf(wr[0], pr[0], acc0);
+          acc1 = __builtin_fmaf(wr[1], pr[1], acc1);
+          wr += 2 * Lb;
+          pr += 2 * Lb;
         }
-        if (j < wd) acc0 = __builtin_fmaf(wr[j], pr[j], acc0);
+        if (j < wd) acc0 = __builtin_fmaf(wr[0], pr[0], acc0);
       }
+      // the group's partial sums meet at its first lane (h = 0): step o
+      // adds the partial sum of lane + o -- a DPP row shift within the
+      // 16-lane row for o <= 8, a swizzle within 32 lanes for 16, a permute
+      // across the wave for 32 -- and adds nothing where o >= Lb (the
+      // partner belongs to another group)
       float acc = acc0 + acc1;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {   // uniform shuffles; partners outside the group are not added
-        const float other = __shfl_xor(acc, o, 64);
-        if (o < Lb) acc += other;
+      auto from_plus = [&](float v, auto ctrl) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xf, 0xf, true));
+      };
+      {
+        float t;
+        t = from_plus(acc, std::integral_constant<int, 0x101>{});   // row_shl:1
+        acc = 1 < Lb ? acc + t : acc;
+        t = from_plus(acc, std::integral_constant<int, 0x102>{});   // row_shl:2
+        acc = 2 < Lb ? acc + t : acc;
+        t = from_plus(acc, std::integral_constant<int, 0x104>{});   // row_shl:4
+        acc = 4 < Lb ? acc + t : acc;
+        t = from_plus(acc, std::integral_constant<int, 0x108>{});   // row_shl:8
+        acc = 8 < Lb ? acc + t : acc;
+        t = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(acc), (16 << 10) | 0x1f));   // lane ^ 16
+        acc = 16 < Lb ? acc + t : acc;
+        t = __int_as_float(__builtin_amdgcn_ds_bpermute(perm32, __float_as_int(acc)));   // lane + 32
+        acc = 32 < Lb ? acc + t : acc;
       }
       if (lane_ent >= 0 && h == 0) {
         if (a.mel_out) {
