@@ -523,14 +523,19 @@ template <int NFFT>
 struct BigCfg;
 // THREADS per workgroup, WGS workgroups per CU, PREFETCH: load the next
 // frame's samples during the current frame's mel sums
+// TAB_STEP, TAB_NS: the radix-8 pass whose twiddles come from an LDS table
+// of their seven powers (its twiddle step and its Ns; 0 for none), where the
+// workgroup's LDS has room for it
 template <> struct BigCfg<8192> {
   static constexpr int THREADS = big_threads(8192), WGS = 2;
   static constexpr bool PREFETCH = false;
+  static constexpr int TAB_STEP = 0, TAB_NS = 0;
   using Rad = Radices<8, 8, 8, 8>;
 };
 template <> struct BigCfg<16384> {
   static constexpr int THREADS = big_threads(16384), WGS = 1;
   static constexpr bool PREFETCH = true;
+  static constexpr int TAB_STEP = 8, TAB_NS = 128;   // the third pass: 8192 / (128 * 8)
   using Rad = Radices<16, 8, 8, 8>;
 };
 
@@ -542,9 +547,10 @@ constexpr int kBigPad = 5;   // FFT buffer: one spare point per 32
 // 128 h + l, the product of hi[h] and lo[l]; where every j of a pass is a
 // multiple of 128 (the early passes) the low factor is exactly 1 and the
 // twiddle is one table entry.
-template <int THI>
+template <int THI, int TSTEP = 0, int TNS = 0>
 struct BigTw {
   const float2 *s_tw;   // THI entries exp(-2 pi i 128 h / N), then kTwLo entries exp(-2 pi i l / N)
+  const float2 *s_tab;  // TSTEP > 0: at<TSTEP>(t k) for 1 <= t < 8, k < TNS, at [(t - 1) TNS + k]
   template <int STEP>
   __device__ __forceinline__ float2 at(int q) const {
     constexpr int S = 2 * STEP;
@@ -559,7 +565,12 @@ struct BigTw {
   // products as before and 4 instead of 14 LDS reads.
   template <int STEP, int R>
   __device__ __forceinline__ void powers(int k, float2 (&w)[R]) const {
-    if constexpr ((2 * STEP) % kTwLo == 0 || R != 8) {
+    if constexpr (TSTEP > 0 && STEP == TSTEP && R == 8) {
+      // seven table reads, no products (the table holds each power as one
+      // product of two entries of s_tw)
+#pragma unroll
+      for (int t = 1; t < R; ++t) w[t] = s_tab[(t - 1) * TNS + k];
+    } else if constexpr ((2 * STEP) % kTwLo == 0 || R != 8) {
 #pragma unroll
       for (int t = 1; t < R; ++t) w[t] = at<STEP>(t * k);
     } else {
@@ -580,7 +591,7 @@ constexpr int big_wlds() {
   // the twiddle tables and the row tables, within one workgroup's share of
   // the CU's 160 KB
   return (160 * 1024 / BigCfg<NFFT>::WGS - (NFFT / 2 + (NFFT >> (kBigPad + 1))) * 8 - (NFFT / kTwLo + kTwLo) * 8 -
-          3 * 256 * 4 - 1024) / 4;
+          7 * BigCfg<NFFT>::TAB_NS * 8 - 3 * 256 * 4 - 1024) / 4;
 }
 
 // A frame that reaches into the padding (the first and last few of a
@@ -619,12 +630,25 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS, BigCfg<NFFT>::THREADS /
   constexpr int THI = NFFT / kTwLo;
   __shared__ float2 s_buf[M + (M >> kBigPad)];
   __shared__ float2 s_tw[THI + kTwLo];   // exp(-2 pi i 128 h / N), then exp(-2 pi i l / N)
+  constexpr int TSTEP = BigCfg<NFFT>::TAB_STEP, TNS = BigCfg<NFFT>::TAB_NS;
+  __shared__ float2 s_tab[TNS > 0 ? 7 * TNS : 1];
   __shared__ int32_t s_start[256], s_width[256], s_off[256];
   __shared__ float s_w[WLDS];
   __shared__ float s_red[2 * NW];
 
   const int NM = a.n_mels;
   for (int i = threadIdx.x; i < THI + kTwLo; i += THREADS) s_tw[i] = a.tw2[i];
+  if constexpr (TNS > 0) {
+    // the tabulated pass's twiddle powers at<TSTEP>(t k) = exp(-2 pi i j / N),
+    // j = 2 TSTEP t k, each the product of its two entries of the two-level
+    // table (read here from global memory; the barrier in stage_filters
+    // orders these stores before the first frame)
+    static_assert((TNS & (TNS - 1)) == 0 && 2 * TSTEP * 7 * (TNS - 1) < NFFT, "table within one turn");
+    for (int i = threadIdx.x; i < 7 * TNS; i += THREADS) {
+      const int j = 2 * TSTEP * (i / TNS + 1) * (i & (TNS - 1));
+      s_tab[i] = cmul(a.tw2[j >> 7], a.tw2[THI + (j & (kTwLo - 1))]);
+    }
+  }
   const int nnz = stage_filters<THREADS>(NM, a.csr_start, a.csr_width, a.csr_off, a.csr_w, a.nnz, s_start, s_width,
                                          s_off, s_w, WLDS);
   const bool w_in_lds = nnz <= WLDS;
@@ -645,12 +669,22 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS, BigCfg<NFFT>::THREADS /
   // loads in flight together; thread tid takes points n = tid + THREADS u
   float xs[IPT][2];
   auto load_interior = [&](int b, int fr, int tid) {
-    const IN *__restrict__ x = reinterpret_cast<const IN *>(a.pcm) + b * T + ((int64_t)fr * a.hop - a.pad);
+    // one uniform base per u and the thread's 32-bit byte offset, so that
+    // the loads take a scalar base and a vector offset (no 64-bit address
+    // arithmetic per load)
+    const char *__restrict__ xb =
+        reinterpret_cast<const char *>(reinterpret_cast<const IN *>(a.pcm) + b * T + ((int64_t)fr * a.hop - a.pad));
+    const uint32_t o = (uint32_t)tid * (uint32_t)(2 * sizeof(IN));
 #pragma unroll
     for (int u = 0; u < IPT; ++u) {
-      const int n = tid + u * THREADS;
-      xs[u][0] = to_f(x[2 * n]);
-      xs[u][1] = to_f(x[2 * n + 1]);
+      // opaque, so that the compiler keeps it a scalar base; global address
+      // space, so that the loads stay global loads
+      uint64_t bu = reinterpret_cast<uint64_t>(xb) + (uint64_t)u * (THREADS * 2 * sizeof(IN));
+      asm volatile("" : "+s"(bu));
+      const __attribute__((address_space(1))) IN *p =
+          reinterpret_cast<const __attribute__((address_space(1))) IN *>(bu + o);
+      xs[u][0] = to_f(p[0]);
+      xs[u][1] = to_f(p[1]);
     }
   };
   auto interior = [&](int fr) {
@@ -721,7 +755,11 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS, BigCfg<NFFT>::THREADS /
     } else if (have) {
       float2 ws[IPT];
 #pragma unroll
-      for (int u = 0; u < IPT; ++u) ws[u] = win2[tid + u * THREADS];
+      for (int u = 0; u < IPT; ++u) {   // global loads (win2 is opaque, so its address space is restated)
+        const __attribute__((address_space(1))) float *wf =
+            reinterpret_cast<const __attribute__((address_space(1))) float *>(reinterpret_cast<uint64_t>(win2));
+        ws[u] = make_float2(wf[2 * (tid + u * THREADS)], wf[2 * (tid + u * THREADS) + 1]);
+      }
       float2 *const wb = s_buf + lds_pos<kBigPad>(tid);
 #pragma unroll
       for (int u = 0; u < IPT; ++u) wb[lds_step<kBigPad>(u * THREADS)] = make_float2(xs[u][0] * ws[u].x, xs[u][1] * ws[u].y);
@@ -733,7 +771,7 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS, BigCfg<NFFT>::THREADS /
 
     // 2. M-point complex FFT: exp(-2 pi i j / M) = exp(-2 pi i 2j / N)
     __builtin_amdgcn_s_setprio(0);
-    run_fft<M, 1, THREADS, kBigPad>(s_buf, BigTw<THI>{s_tw}, typename BigCfg<NFFT>::Rad{}, tid);
+    run_fft<M, 1, THREADS, kBigPad>(s_buf, BigTw<THI, TSTEP, TNS>{s_tw, s_tab}, typename BigCfg<NFFT>::Rad{}, tid);
 
     // 3. split into the real spectrum; power over the same LDS
     constexpr int NU = M / 2 + 1;
