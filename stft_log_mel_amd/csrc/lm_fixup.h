@@ -53,12 +53,19 @@ inline void prepare_fixup(FixupArgs &a) {
 
 // The clip's floor in output units: logmel_of(largest mel value) - 2;
 // every thread of the workgroup must call it.
+constexpr int kFixMaxUnroll = 8;   // maxima per thread with their loads in flight together
 template <int THREADS>
 __device__ float clip_floor(const FixupArgs &a, int64_t b, float *s_red) {
   const int n_max = a.tiles_per_clip * a.st.max_per_tile;
   const float *cmax = a.tile_max + b * (int64_t)n_max;
   float hi = 0.0f;
-  for (int e = threadIdx.x; e < n_max; e += THREADS) hi = fmaxf(hi, cmax[e]);
+  for (int e0 = threadIdx.x; e0 < n_max; e0 += kFixMaxUnroll * THREADS) {
+    float v[kFixMaxUnroll];
+#pragma unroll
+    for (int u = 0; u < kFixMaxUnroll; ++u) v[u] = e0 + u * THREADS < n_max ? cmax[e0 + u * THREADS] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < kFixMaxUnroll; ++u) hi = fmaxf(hi, v[u]);
+  }
   hi = __uint_as_float(wave_umax(__float_as_uint(hi)));   // maxima are >= 0
   if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = hi;
   __syncthreads();
