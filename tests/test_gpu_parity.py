@@ -307,10 +307,13 @@ def test_stft_mel_output():
 
 @pytest.mark.parametrize("n_fft,hop,win_length,normalized,in_dtype,power", [
     (400, 160, 300, "window", "i16", 2.0), (400, 160, 320, "frame_length", "f32", 2.0),
-    (400, 100, 399, None, "f32", 1.0), (512, 128, 257, "window", "f32", 2.0), (2048, 512, 1500, True, "i16", 2.0)])
+    (400, 100, 399, None, "f32", 1.0), (512, 128, 257, "window", "f32", 2.0), (2048, 512, 1500, True, "i16", 2.0),
+    (8192, 2048, 6000, None, "f32", 2.0), (16384, 4096, 12001, "window", "i16", 2.0)])
 def test_pcm_window_length_and_normalized(n_fft, hop, win_length, normalized, in_dtype, power):
     """Shorter centred windows and spectrum normalisation (torchaudio's
-    win_length and normalized), on the log-mel output."""
+    win_length and normalized), on the log-mel output; at 8192 and 16384 the
+    one-frame kernel's window-table path instead of its Hann-from-twiddles
+    path."""
     sr = 16000.0
     B, T = 2, max(9000, 3 * n_fft + 5)
     say("pcm window", n_fft, hop, win_length, normalized, in_dtype, power)
