@@ -79,14 +79,37 @@ __device__ float clip_floor(const FixupArgs &a, int64_t b, float *s_red) {
 // unwritten.  Their mel value is 1e-10 (no weight, so the sum is 0 before
 // the floor), so the result is max(logmel_of(1e-10), floor), written
 // without reading.  Mel-major output only.
+// The segment is written with 16-byte stores between a scalar head (up to
+// the first 16-byte boundary) and a scalar tail; every element of it gets
+// the same value.
 template <typename OUT, int THREADS>
 __device__ void fixup_empty_row(const FixupArgs &a, int64_t b, int e, int r, float *s_red) {
   const float fl = clip_floor<THREADS>(a, b, s_red);
   const float v = fmaxf(logmel_of(1e-10f), fl);
   const int64_t F = a.n_frames;
   OUT *row = reinterpret_cast<OUT *>(a.out) + (b * a.n_mels + a.empty_bands[e]) * F;
-  const int64_t f1 = min(F, (int64_t)(r + 1) * kFixValues);
-  for (int64_t f = (int64_t)r * kFixValues + threadIdx.x; f < f1; f += THREADS) store_out(row + f, v);
+  const int64_t f0 = (int64_t)r * kFixValues, f1 = min(F, f0 + kFixValues);
+  OUT *const p = row + f0;
+  const int n = (int)(f1 - f0);   // <= kFixValues
+  constexpr int VE = 16 / (int)sizeof(OUT);   // elements per 16 bytes
+  const int mis = (int)((reinterpret_cast<uintptr_t>(p) & 15) / sizeof(OUT));   // elements past a boundary
+  const int head = min(n, (VE - mis) % VE);
+  const int nv = (n - head) / VE;
+  const int tid = threadIdx.x;
+  if (tid < head) store_out(p + tid, v);
+  // the value's bit pattern in the output type, four 32-bit words
+  uint32_t w;
+  if constexpr (sizeof(OUT) == 2) {
+    const uint32_t hb = __half_as_ushort(__float2half_rn(fp32_value(v)));
+    w = hb | (hb << 16);
+  } else {
+    w = __float_as_uint(v);
+  }
+  const uint4 q = make_uint4(w, w, w, w);
+  uint4 *const pv = reinterpret_cast<uint4 *>(p + head);   // 16-byte aligned
+  for (int i = tid; i < nv; i += THREADS) pv[i] = q;
+  const int t0 = head + nv * VE;
+  if (t0 + tid < n) store_out(p + t0 + tid, v);   // fewer than VE <= THREADS elements
 }
 
 // Unit (clip b, group gi): reduce the clip's maxima to its floor (every
