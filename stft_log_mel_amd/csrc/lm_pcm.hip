@@ -514,10 +514,13 @@ __global__ void __launch_bounds__(PcmCfg<NFFT>::THREADS) pcm_logmel_kernel(PcmKe
 // loaded into registers while the mel sums of the current one run; at 8192
 // two 512-thread workgroups share a CU, each loading its frame at the
 // frame's start, and either one's barriers and loads overlap the other's
-// work (48 against 69 us per sweep step with one 1024-thread workgroup).  The mel gives every band L consecutive lanes (L =
-// the largest power of two with L * n_mels <= THREADS, at most 64), which
-// stride over the band's bins and combine their partial sums with xor
-// shuffles, so no band waits on another band's reduction.
+// work (48 against 69 us per sweep step with one 1024-thread workgroup).
+// The mel gives every band a group of L consecutive lanes (a power of two,
+// at most 64, from the plan's lane table, which widens the groups of the
+// bands with the most bins per lane), which stride over the band's bins in
+// pairs of adjacent bins and add their partial sums at the group's first
+// lane (DPP row shifts, one swizzle, one permute), so no band waits on
+// another band's reduction.
 // ---------------------------------------------------------------------------
 template <int NFFT>
 struct BigCfg;
@@ -821,9 +824,9 @@ __global__ void __launch_bounds__(BigCfg<NFFT>::THREADS, BigCfg<NFFT>::THREADS /
       if (have) load_interior(nb, nfr, tid);
     }
 
-    // 4. mel: each band's group of Lb lanes strides over its bins; the
-    //    groups' partial sums meet by xor shuffles within the group.  The
-    //    frame's largest and smallest mel values are kept on their bit
+    // 4. mel: each band's group of Lb lanes strides over its bins in pairs
+    //    of adjacent bins; the group's partial sums meet at its first lane.
+    //    The frame's largest and smallest mel values are kept on their bit
     //    patterns (positive floats order as unsigned integers).
     uint32_t vmaxb = 0u, vminb = 0x7f800000u;
     OUT *__restrict__ out = reinterpret_cast<OUT *>(a.out) + b * (int64_t)NM * F;
