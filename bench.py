@@ -522,7 +522,7 @@ def main():
                          "as one dense fp32 GEMM on the vendor BLAS (torch.matmul), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (clips shard across "
+        print("bench.py measures one GPU: the library has no multi-GPU path (clips shard across "
               "GPUs with no communication; see the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
