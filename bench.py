@@ -337,6 +337,9 @@ def roofline_of(w, kernel_ms, fft_variant="auto"):
                 "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4),
                 "frac_of_unpacked_fp32": round(tf / (FP32_VALU_PEAK_TFLOPS / 2), 4),
                 "algorithmic_flops_per_launch": round(frames * flops_per_frame(w)),
+                # HBM bytes per launch from the counters, for context (this
+                # kernel's bound is its arithmetic)
+                "traffic": counter_traffic(w.name), "algorithmic_bytes_per_launch": w.essential_bytes(),
                 "kernel": main_kernel_name(w, fft_variant), "kernel_ms": round(kernel_ms, 5)}
     gbs = w.essential_bytes() / (kernel_ms / 1e3) / 1e9
     return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
